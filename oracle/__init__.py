@@ -1,0 +1,185 @@
+"""CPU oracle for N:M masking, compression and sparse x dense products.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py`` may import this package.  The GPU
+library never loads it and shares no code with it.
+
+The arithmetic lives in ``nm_oracle.c`` (plain C99, compiled with gcc); this
+module only builds that file and marshals numpy arrays into it.  Functions
+follow the definitions cited in ``nm_oracle.h``:
+
+* ``mask`` / ``compress``: ASP's exhaustive best-pattern search
+  ("量化友好的SR-STE稀疏化训练", section "NVIDA Apex内的静态掩码稀疏"), exact
+  scores, first (lexicographically smallest) best pattern on ties.
+* ``compress`` / ``decompress``: value array plus b-bit position fields
+  ("[리뷰] Accelerating Sparse Deep Neural Networks", section
+  "2:4 Sparsity의 benefits").
+* ``spmm``: dense product of the decompressed operand with X in double
+  (same review, section "Tensor Scores 상에서 구조적인 sparse GEMM").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "nm_oracle.c")
+_LIB = os.path.join(_HERE, "libnm_oracle.so")
+
+F32, F16, BF16 = 0, 1, 2
+_DT_CODE = {"f32": F32, "f16": F16, "bf16": BF16}
+_ELEM = {F32: np.uint32, F16: np.uint16, BF16: np.uint16}
+
+
+def build(force: bool = True) -> str:
+    """Compile nm_oracle.c into libnm_oracle.so with gcc."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
+        )
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        L = ctypes.CDLL(_LIB)
+        i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        L.nmo_meta_bits.argtypes = [i32]
+        L.nmo_meta_bits.restype = i32
+        L.nmo_meta_words_per_row.argtypes = [i64, i32, i32]
+        L.nmo_meta_words_per_row.restype = i64
+        L.nmo_mask.argtypes = [vp, i32, i64, i64, i32, i32, vp]
+        L.nmo_compress.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp]
+        L.nmo_decompress.argtypes = [vp, vp, i32, i64, i64, i32, i32, vp]
+        L.nmo_spmm.argtypes = [vp, vp, i64, i64, i32, i32, vp, i64, i32, vp]
+        L.nmo_spmm_rows.argtypes = [vp, vp, i64, i64, i32, i32, vp, i64, i32, i64, i64, vp]
+        L.nmo_spmm_sample.argtypes = [vp, vp, i64, i64, i32, i32, vp, i64, i32, vp, vp, i64, vp]
+        L.nmo_to_double.argtypes = [vp, i32, i64]
+        L.nmo_to_double.restype = ctypes.c_double
+        for f in ("nmo_mask", "nmo_compress", "nmo_decompress", "nmo_spmm", "nmo_spmm_rows",
+                  "nmo_spmm_sample"):
+            getattr(L, f).restype = i32
+        _lib = L
+    return _lib
+
+
+def _code(dt) -> int:
+    return _DT_CODE[dt] if isinstance(dt, str) else int(dt)
+
+
+def _ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise ValueError(f"oracle {what} rejected its arguments (code {rc})")
+
+
+def meta_bits(m: int) -> int:
+    return lib().nmo_meta_bits(m)
+
+
+def meta_words_per_row(K: int, n: int, m: int) -> int:
+    return lib().nmo_meta_words_per_row(K, n, m)
+
+
+def _as_bits(W: np.ndarray, dt: int) -> np.ndarray:
+    want = _ELEM[dt]
+    if W.dtype != want:
+        W = W.view(want)
+    return np.ascontiguousarray(W)
+
+
+def mask(W: np.ndarray, dt, n: int, m: int) -> np.ndarray:
+    """uint8 R x K: 1 where the weight is kept."""
+    dt = _code(dt)
+    W = _as_bits(W, dt)
+    R, K = W.shape
+    out = np.empty((R, K), dtype=np.uint8)
+    _check(lib().nmo_mask(_ptr(W), dt, R, K, n, m, _ptr(out)), "mask")
+    return out
+
+
+def compress(W: np.ndarray, dt, n: int, m: int):
+    """(values R x K*n/m as raw bits, meta R x words_per_row uint32)."""
+    dt = _code(dt)
+    W = _as_bits(W, dt)
+    R, K = W.shape
+    if K % m:
+        raise ValueError("K must be a multiple of m")
+    vals = np.empty((R, K // m * n), dtype=_ELEM[dt])
+    wpr = meta_words_per_row(K, n, m)
+    meta = np.empty((R, max(wpr, 0)), dtype=np.uint32)
+    _check(lib().nmo_compress(_ptr(W), dt, R, K, n, m, _ptr(vals), _ptr(meta)), "compress")
+    return vals, meta
+
+
+def decompress(values: np.ndarray, meta: np.ndarray, dt, R: int, K: int, n: int, m: int) -> np.ndarray:
+    dt = _code(dt)
+    values = _as_bits(values, dt)
+    meta = np.ascontiguousarray(meta, dtype=np.uint32)
+    out = np.empty((R, K), dtype=_ELEM[dt])
+    _check(lib().nmo_decompress(_ptr(values), _ptr(meta), dt, R, K, n, m, _ptr(out)), "decompress")
+    return out
+
+
+def spmm(values, meta, R: int, K: int, n: int, m: int, X: np.ndarray, dt) -> np.ndarray:
+    """Y (R x T, float64) = decompress(values, meta) @ X."""
+    dt = _code(dt)
+    values = _as_bits(values, dt)
+    meta = np.ascontiguousarray(meta, dtype=np.uint32)
+    X = _as_bits(X, dt)
+    T = X.shape[1]
+    Y = np.empty((R, T), dtype=np.float64)
+    _check(lib().nmo_spmm(_ptr(values), _ptr(meta), R, K, n, m, _ptr(X), T, dt, _ptr(Y)), "spmm")
+    return Y
+
+
+def spmm_rows(values, meta, R, K, n, m, X, dt, r0: int, r1: int, Y: np.ndarray) -> None:
+    """Fill rows [r0, r1) of the R x T float64 array Y (other rows untouched)."""
+    dt = _code(dt)
+    assert Y.dtype == np.float64 and Y.flags["C_CONTIGUOUS"]
+    rc = lib().nmo_spmm_rows(_ptr(values), _ptr(meta), R, K, n, m, _ptr(X), X.shape[1], dt, r0, r1,
+                             _ptr(Y))
+    _check(rc, "spmm_rows")
+
+
+def spmm_sample(values, meta, R, K, n, m, X, dt, rs, ts) -> np.ndarray:
+    """Y[rs[i], ts[i]] of the product, one exact dot product per sample."""
+    dt = _code(dt)
+    values = _as_bits(values, dt)
+    meta = np.ascontiguousarray(meta, dtype=np.uint32)
+    X = _as_bits(X, dt)
+    rs = np.ascontiguousarray(rs, dtype=np.int64)
+    ts = np.ascontiguousarray(ts, dtype=np.int64)
+    out = np.empty(len(rs), dtype=np.float64)
+    rc = lib().nmo_spmm_sample(_ptr(values), _ptr(meta), R, K, n, m, _ptr(X), X.shape[1], dt,
+                               _ptr(rs), _ptr(ts), len(rs), _ptr(out))
+    _check(rc, "spmm_sample")
+    return out
+
+
+def to_double(a: np.ndarray, dt) -> np.ndarray:
+    """Exact float64 value of every element (raw bits in, doubles out)."""
+    dt = _code(dt)
+    a = _as_bits(a, dt)
+    flat = a.reshape(-1)
+    L = lib()
+    out = np.empty(flat.shape[0], dtype=np.float64)
+    p = _ptr(flat)
+    for i in range(flat.shape[0]):
+        out[i] = L.nmo_to_double(p, dt, i)
+    return out.reshape(a.shape)

@@ -1,0 +1,343 @@
+/*
+ * nm_oracle.c -- CPU oracle (test infrastructure only; see nm_oracle.h).
+ *
+ * Plain, slow and deliberately literal.  Every step follows a definition
+ * stated on the source pages; where the pages leave a step open the reading
+ * is named at that step.
+ */
+#include "nm_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* Exact magnitudes.                                                         */
+/*                                                                           */
+/* ASP's mn_1d_best ([SRSTE] "NVIDA Apex内的静态掩码稀疏") scores a pattern by the */
+/* sum of |w| over the kept positions.  A floating-point sum can round two    */
+/* different scores to the same number, so the oracle sums exactly: every     */
+/* finite float of a binary format is an integer multiple of that format's   */
+/* smallest subnormal, and that integer is                                   */
+/*     e == 0 :  f                      (subnormal or zero)                   */
+/*     e >  0 :  (2^p + f) << (e - 1)   (normal)                              */
+/* for exponent field e and p-bit fraction field f.  The same formula applied */
+/* to the all-ones exponent gives Inf/NaN an integer larger than every finite */
+/* value, which is the order of the sign-cleared bit pattern.                */
+/* fp32 needs up to 2^24 << 254 < 2^278; five 64-bit limbs hold sums of up to */
+/* 2^42 such terms, far more than any group.                                  */
+/* ------------------------------------------------------------------------ */
+
+#define LIMBS 5
+typedef struct {
+  uint64_t w[LIMBS]; /* little-endian limbs */
+} big_t;
+
+static void big_zero(big_t* a) { memset(a, 0, sizeof(*a)); }
+
+static void big_add(big_t* acc, const big_t* x) {
+  uint64_t carry = 0;
+  for (int i = 0; i < LIMBS; i++) {
+    uint64_t s = acc->w[i] + x->w[i];
+    uint64_t c1 = s < acc->w[i];
+    uint64_t s2 = s + carry;
+    uint64_t c2 = s2 < s;
+    acc->w[i] = s2;
+    carry = c1 | c2;
+  }
+}
+
+/* -1, 0, +1 as a <, ==, > b */
+static int big_cmp(const big_t* a, const big_t* b) {
+  for (int i = LIMBS - 1; i >= 0; i--) {
+    if (a->w[i] < b->w[i]) return -1;
+    if (a->w[i] > b->w[i]) return 1;
+  }
+  return 0;
+}
+
+/* value << shift into a big_t; value < 2^25, shift < 256 */
+static void big_from_shifted(big_t* out, uint64_t value, int shift) {
+  big_zero(out);
+  int limb = shift / 64, off = shift % 64;
+  out->w[limb] = value << off;
+  if (off != 0 && limb + 1 < LIMBS) out->w[limb + 1] = value >> (64 - off);
+}
+
+static uint32_t raw_bits(const void* p, int dt, int64_t i) {
+  if (dt == NMO_F32) return ((const uint32_t*)p)[i];
+  return ((const uint16_t*)p)[i];
+}
+
+/* exact |w| of element i, as an integer multiple of the smallest subnormal */
+static void exact_magnitude(const void* W, int dt, int64_t i, big_t* out) {
+  uint32_t bits = raw_bits(W, dt, i);
+  uint32_t e, f;
+  int p;
+  if (dt == NMO_F32) {
+    e = (bits >> 23) & 0xFFu;
+    f = bits & 0x7FFFFFu;
+    p = 23;
+  } else if (dt == NMO_BF16) { /* bf16 = upper half of an fp32 */
+    e = (bits >> 7) & 0xFFu;
+    f = (bits & 0x7Fu) << 16;
+    p = 23;
+  } else { /* fp16 */
+    e = (bits >> 10) & 0x1Fu;
+    f = bits & 0x3FFu;
+    p = 10;
+  }
+  if (e == 0)
+    big_from_shifted(out, f, 0);
+  else
+    big_from_shifted(out, ((uint64_t)1 << p) + f, (int)e - 1);
+}
+
+double nmo_to_double(const void* p, int dt, int64_t i) {
+  uint32_t bits = raw_bits(p, dt, i);
+  if (dt == NMO_F32) {
+    float v;
+    memcpy(&v, &bits, 4);
+    return (double)v;
+  }
+  if (dt == NMO_BF16) {
+    uint32_t b32 = bits << 16;
+    float v;
+    memcpy(&v, &b32, 4);
+    return (double)v;
+  }
+  /* fp16: 1 sign, 5 exponent (bias 15), 10 fraction bits */
+  int s = (bits >> 15) & 1;
+  int e = (bits >> 10) & 0x1F;
+  int f = bits & 0x3FF;
+  double v;
+  if (e == 0)
+    v = ldexp((double)f, -24);
+  else if (e == 31)
+    v = f ? NAN : INFINITY;
+  else
+    v = ldexp((double)(1024 + f), e - 25);
+  return s ? -v : v;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Argument checks and metadata geometry                                     */
+/* ------------------------------------------------------------------------ */
+
+int nmo_meta_bits(int m) {
+  switch (m) {
+    case 2: return 1;
+    case 4: return 2;
+    case 8: return 3;
+    case 16: return 4;
+    default: return -1;
+  }
+}
+
+int64_t nmo_meta_words_per_row(int64_t K, int n, int m) {
+  int b = nmo_meta_bits(m);
+  if (b < 0 || n < 1 || n > m || K < 0 || K % m != 0) return -1;
+  int64_t bits = (K / m) * n * b;
+  return (bits + 31) / 32;
+}
+
+static int check_args(int dt, int64_t R, int64_t K, int n, int m) {
+  if (dt != NMO_F32 && dt != NMO_F16 && dt != NMO_BF16) return -1;
+  if (R < 0 || K < 0) return -2;
+  if (nmo_meta_bits(m) < 0 || n < 1 || n > m) return -3;
+  if (K % m != 0) return -4;
+  return 0;
+}
+
+static void put_field(uint32_t* row, int64_t field, int b, uint32_t v) {
+  int64_t bit = field * b;
+  int64_t w = bit / 32;
+  int off = (int)(bit % 32);
+  row[w] |= (uint32_t)((uint64_t)v << off);
+  if (off + b > 32) row[w + 1] |= v >> (32 - off);
+}
+
+static uint32_t get_field(const uint32_t* row, int64_t field, int b) {
+  int64_t bit = field * b;
+  int64_t w = bit / 32;
+  int off = (int)(bit % 32);
+  uint64_t window = row[w] >> off;
+  if (off + b > 32) window |= (uint64_t)row[w + 1] << (32 - off);
+  return (uint32_t)(window & ((1u << b) - 1u));
+}
+
+/* ------------------------------------------------------------------------ */
+/* Group selection: ASP's exhaustive search ([SRSTE] "NVIDA Apex内的静态掩码稀疏"). */
+/* Enumerate every set of n positions out of m (all valid N:M patterns) in   */
+/* lexicographic order of the ascending index tuple, score each by the exact */
+/* sum of the kept magnitudes, and keep the first pattern with the largest   */
+/* score (a later pattern replaces it only when strictly larger).            */
+/* ------------------------------------------------------------------------ */
+static void best_pattern(const void* W, int dt, int64_t base, int n, int m, int* kept) {
+  int idx[16];
+  big_t mag[16], best, score;
+  for (int i = 0; i < m; i++) exact_magnitude(W, dt, base + i, &mag[i]);
+  for (int j = 0; j < n; j++) idx[j] = j;
+  int have_best = 0;
+  for (;;) {
+    big_zero(&score);
+    for (int j = 0; j < n; j++) big_add(&score, &mag[idx[j]]);
+    if (!have_best || big_cmp(&score, &best) > 0) {
+      best = score;
+      for (int j = 0; j < n; j++) kept[j] = idx[j];
+      have_best = 1;
+    }
+    /* next combination in lexicographic order */
+    int j = n - 1;
+    while (j >= 0 && idx[j] == m - n + j) j--;
+    if (j < 0) break;
+    idx[j]++;
+    for (int k = j + 1; k < n; k++) idx[k] = idx[k - 1] + 1;
+  }
+}
+
+int nmo_mask(const void* W, int dt, int64_t R, int64_t K, int n, int m, uint8_t* mask) {
+  int rc = check_args(dt, R, K, n, m);
+  if (rc) return rc;
+  int kept[16];
+  for (int64_t r = 0; r < R; r++) {
+    for (int64_t g = 0; g < K / m; g++) {
+      int64_t base = r * K + g * m;
+      best_pattern(W, dt, base, n, m, kept);
+      for (int i = 0; i < m; i++) mask[base + i] = 0;
+      for (int j = 0; j < n; j++) mask[base + kept[j]] = 1;
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Compression ([ASDNN] "2:4 Sparsity의 benefits"): the kept values of each   */
+/* group, in ascending position order, form the value array (K*n/m per row,  */
+/* always n per group even if the group holds more zeros); each kept value's */
+/* position inside its group is written as a b-bit metadata field.           */
+/* ------------------------------------------------------------------------ */
+int nmo_compress(const void* W, int dt, int64_t R, int64_t K, int n, int m, void* values,
+                 uint32_t* meta) {
+  int rc = check_args(dt, R, K, n, m);
+  if (rc) return rc;
+  int b = nmo_meta_bits(m);
+  int64_t wpr = nmo_meta_words_per_row(K, n, m);
+  int64_t kv = K / m * n; /* values per row */
+  int kept[16];
+  for (int64_t r = 0; r < R; r++) {
+    uint32_t* mrow = meta + r * wpr;
+    for (int64_t w = 0; w < wpr; w++) mrow[w] = 0;
+    for (int64_t g = 0; g < K / m; g++) {
+      int64_t base = r * K + g * m;
+      best_pattern(W, dt, base, n, m, kept);
+      for (int j = 0; j < n; j++) {
+        int64_t dst = r * kv + g * n + j;
+        if (dt == NMO_F32)
+          ((uint32_t*)values)[dst] = ((const uint32_t*)W)[base + kept[j]];
+        else
+          ((uint16_t*)values)[dst] = ((const uint16_t*)W)[base + kept[j]];
+        put_field(mrow, g * n + j, b, (uint32_t)kept[j]);
+      }
+    }
+  }
+  return 0;
+}
+
+/* Decompression: stored values back at their recorded positions, +0 elsewhere. */
+int nmo_decompress(const void* values, const uint32_t* meta, int dt, int64_t R, int64_t K, int n,
+                   int m, void* W_out) {
+  int rc = check_args(dt, R, K, n, m);
+  if (rc) return rc;
+  int b = nmo_meta_bits(m);
+  int64_t wpr = nmo_meta_words_per_row(K, n, m);
+  int64_t kv = K / m * n;
+  int s = dt == NMO_F32 ? 4 : 2;
+  memset(W_out, 0, (size_t)(R * K * s));
+  for (int64_t r = 0; r < R; r++) {
+    const uint32_t* mrow = meta + r * wpr;
+    for (int64_t g = 0; g < K / m; g++) {
+      for (int j = 0; j < n; j++) {
+        int64_t pos = r * K + g * m + get_field(mrow, g * n + j, b);
+        int64_t src = r * kv + g * n + j;
+        if (dt == NMO_F32)
+          ((uint32_t*)W_out)[pos] = ((const uint32_t*)values)[src];
+        else
+          ((uint16_t*)W_out)[pos] = ((const uint16_t*)values)[src];
+      }
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Sparse x dense product ([ASDNN] "Tensor Scores 상에서 구조적인 sparse GEMM"): */
+/* the result is the ordinary dense product of the decompressed first operand */
+/* with the dense second operand.  Inputs are converted to double exactly;   */
+/* every product of two 16-bit or two fp32 inputs is exact in double, and the */
+/* sum runs over ascending k.                                                */
+/* ------------------------------------------------------------------------ */
+static void decompress_row_double(const void* values, const uint32_t* meta, int dt, int64_t r,
+                                  int64_t K, int n, int m, double* wd) {
+  int b = nmo_meta_bits(m);
+  int64_t wpr = nmo_meta_words_per_row(K, n, m);
+  int64_t kv = K / m * n;
+  const uint32_t* mrow = meta + r * wpr;
+  for (int64_t k = 0; k < K; k++) wd[k] = 0.0;
+  for (int64_t g = 0; g < K / m; g++)
+    for (int j = 0; j < n; j++)
+      wd[g * m + get_field(mrow, g * n + j, b)] = nmo_to_double(values, dt, r * kv + g * n + j);
+}
+
+int nmo_spmm_rows(const void* values, const uint32_t* meta, int64_t R, int64_t K, int n, int m,
+                  const void* X, int64_t T, int dt, int64_t r0, int64_t r1, double* Y) {
+  int rc = check_args(dt, R, K, n, m);
+  if (rc) return rc;
+  if (T < 0 || r0 < 0 || r1 > R || r0 > r1) return -2;
+  double* wd = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+  double* xrow = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+  if (!wd || !xrow) {
+    free(wd);
+    free(xrow);
+    return -5;
+  }
+  for (int64_t r = r0; r < r1; r++) {
+    double* y = Y + r * T;
+    for (int64_t t = 0; t < T; t++) y[t] = 0.0;
+    decompress_row_double(values, meta, dt, r, K, n, m, wd);
+    for (int64_t k = 0; k < K; k++) {
+      for (int64_t t = 0; t < T; t++) xrow[t] = nmo_to_double(X, dt, k * T + t);
+      for (int64_t t = 0; t < T; t++) y[t] += wd[k] * xrow[t];
+    }
+  }
+  free(wd);
+  free(xrow);
+  return 0;
+}
+
+int nmo_spmm(const void* values, const uint32_t* meta, int64_t R, int64_t K, int n, int m,
+             const void* X, int64_t T, int dt, double* Y) {
+  return nmo_spmm_rows(values, meta, R, K, n, m, X, T, dt, 0, R, Y);
+}
+
+int nmo_spmm_sample(const void* values, const uint32_t* meta, int64_t R, int64_t K, int n, int m,
+                    const void* X, int64_t T, int dt, const int64_t* rs, const int64_t* ts,
+                    int64_t count, double* out) {
+  int rc = check_args(dt, R, K, n, m);
+  if (rc) return rc;
+  double* wd = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+  if (!wd) return -5;
+  for (int64_t i = 0; i < count; i++) {
+    int64_t r = rs[i], t = ts[i];
+    if (r < 0 || r >= R || t < 0 || t >= T) {
+      free(wd);
+      return -2;
+    }
+    decompress_row_double(values, meta, dt, r, K, n, m, wd);
+    double acc = 0.0;
+    for (int64_t k = 0; k < K; k++) acc += wd[k] * nmo_to_double(X, dt, k * T + t);
+    out[i] = acc;
+  }
+  free(wd);
+  return 0;
+}

@@ -1,0 +1,91 @@
+/*
+ * nm_oracle.h -- CPU oracle for N:M magnitude masking, compression and the
+ * compressed-sparse x dense product.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is a plain, slow, single-threaded C99
+ * implementation written from the definitions on the source pages.  It shares
+ * no code, header, table or constant with the GPU library; only the test
+ * suite, the smoke check and the benchmark's CPU-baseline leg may load it.
+ *
+ * Sources (cited by page title and section):
+ *   [SRSTE]  "量化友好的SR-STE稀疏化训练" (blog.bakeneko-kuro.com)
+ *            - section "概念": N:M means N non-zero among every M consecutive weights.
+ *            - section "NVIDA Apex内的静态掩码稀疏": ASP's m4n2_1d / mn_1d_best
+ *              scores every valid N-of-M pattern by the L1 norm of the weights it
+ *              keeps and takes the best pattern per group of M along the last,
+ *              contiguous dimension.
+ *   [ASDNN]  "[리뷰] Accelerating Sparse Deep Neural Networks" (moon-walker.medium.com)
+ *            - section "2:4 Sparsity의 benefits": compressed matrix of R*C/2 values,
+ *              2-bit position metadata per kept value, always N values stored per
+ *              group; 4 fp16 values take 36 bits instead of 64.
+ *            - section "Tensor Scores 상에서 구조적인 sparse GEMM": sparse (first,
+ *              compressed) operand times dense operand gives a dense result.
+ *            - section "Step-2: Weight Pruning": drop the two smallest of each four.
+ *
+ * Readings where the pages are silent (each also listed in the design doc):
+ *   - N counts KEPT elements; exactly N values are stored per group.
+ *   - Ties between equally good patterns go to the lexicographically first
+ *     ascending index tuple (lower index wins).
+ *   - Pattern scores are summed EXACTLY (integer arithmetic), not in fp32.
+ *   - |w| is ordered by the format's bits with the sign cleared; the exact
+ *     magnitude of an Inf/NaN bit pattern continues that integer order
+ *     (so NaN ranks above Inf, Inf above every finite value).
+ *   - Metadata: b = log2(M) bits per kept value; field f = g*N + j of a row
+ *     (j-th kept index of group g, ascending) sits at bit f*b of the row's
+ *     uint32 bitstream, least significant bit first; every row starts on a
+ *     word boundary; pad bits are zero.
+ *   - Decompression writes +0 (all-zero bits) at pruned positions.
+ *
+ * Conventions: every matrix is dense row-major; W is R x K with groups along
+ * K; values R x (K*N/M); meta R x words_per_row uint32; X K x T; Y R x T.
+ * Element types: dt = 0 (fp32), 1 (fp16), 2 (bf16); 16-bit types are passed
+ * as raw uint16 bit patterns.  Return value 0 = success, negative = bad args.
+ */
+#ifndef NM_ORACLE_H
+#define NM_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NMO_F32 0
+#define NMO_F16 1
+#define NMO_BF16 2
+
+/* metadata bits per kept value, log2(m); -1 if m is not a power of two in [2,16] */
+int nmo_meta_bits(int m);
+/* uint32 words of metadata per row: ceil(K/m * n * b / 32) */
+int64_t nmo_meta_words_per_row(int64_t K, int n, int m);
+
+/* mask[r*K+k] = 1 if W[r,k] is kept, else 0 (exhaustive search over all patterns) */
+int nmo_mask(const void* W, int dt, int64_t R, int64_t K, int n, int m, uint8_t* mask);
+
+/* values (R x K*n/m, dtype dt) and meta (R x words_per_row) of W */
+int nmo_compress(const void* W, int dt, int64_t R, int64_t K, int n, int m, void* values,
+                 uint32_t* meta);
+
+/* dense R x K matrix with the stored values at their positions and +0 elsewhere */
+int nmo_decompress(const void* values, const uint32_t* meta, int dt, int64_t R, int64_t K, int n,
+                   int m, void* W_out);
+
+/* Y (R x T, double) = decompress(values, meta) * X, summed in double over ascending k */
+int nmo_spmm(const void* values, const uint32_t* meta, int64_t R, int64_t K, int n, int m,
+             const void* X, int64_t T, int dt, double* Y);
+
+/* rows [r0, r1) of the product above, written to Y (R x T layout, only those rows touched) */
+int nmo_spmm_rows(const void* values, const uint32_t* meta, int64_t R, int64_t K, int n, int m,
+                  const void* X, int64_t T, int dt, int64_t r0, int64_t r1, double* Y);
+
+/* out[i] = Y[rs[i], ts[i]] of the product above, one dot product per sample */
+int nmo_spmm_sample(const void* values, const uint32_t* meta, int64_t R, int64_t K, int n, int m,
+                    const void* X, int64_t T, int dt, const int64_t* rs, const int64_t* ts,
+                    int64_t count, double* out);
+
+/* exact value of one element as a double (helper used by the Python side of the oracle) */
+double nmo_to_double(const void* p, int dt, int64_t i);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
