@@ -1,0 +1,311 @@
+#!/usr/bin/env python3
+"""Benchmark of the N:M hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input: for each weight
+matrix of the workload, nm_mask, nm_compress (mask + values + metadata),
+nm_decompress and nm_spmm (Y = W_sparse X).  Inputs are resident in HBM before
+the timed region.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload llama_mlp]
+
+`value` is the whole step's effective throughput: dense-equivalent product
+flops (2 R K T per matrix) divided by the step time.  Per-kernel figures,
+the roofline of the dominant kernel, the dense GEMM on the same shapes and the
+CPU oracle timed on the host are reported alongside.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "2:4 spmm effective TFLOP/s + mask/compress GB/s (% of MI355X roofline)"
+PEAK_HBM_GBS = 8000.0
+PEAK_MFMA_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+# workload name -> (synthetic matrices, N:M pattern)
+WORKLOADS = {
+    "llama_mlp": (["llama_up", "llama_down"], (2, 4)),
+    "bert_ffn": (["bert_ffn"], (2, 4)),
+    "resnet_conv3x3": (["resnet_conv3x3"], (2, 4)),
+    "sweep_f16_2_4": (["sweep_f16"], (2, 4)),
+    "sweep_f16_1_2": (["sweep_f16"], (1, 2)),
+    "sweep_f16_4_8": (["sweep_f16"], (4, 8)),
+    "toy_f32": (["toy_f32"], (2, 4)),
+}
+
+
+def meta_bits(m: int) -> int:
+    return {2: 1, 4: 2, 8: 3}[m]
+
+
+def algorithmic_bytes(R, K, T, n, m, s):
+    """Bytes each kernel must move at minimum (one read of inputs, one write of outputs)."""
+    e = R * K
+    kept = e * n // m
+    meta = R * ((K // m * n * meta_bits(m) + 31) // 32) * 4
+    return {
+        "mask": e * s + e,
+        "compress": e * s + kept * s + meta,
+        "decompress": kept * s + meta + e * s,
+        "spmm": kept * s + meta + K * T * s + R * T * s,
+    }
+
+
+def cpu_baseline(mats, n, m, threads: int, budget_s: float = 12.0):
+    """The oracle as it stands, on the host: mask + compress + decompress + product of a
+    bounded slice of rows of every matrix, rows spread over `threads` threads."""
+    import oracle
+
+    oracle.lib()
+    F = 0.0
+    rows_done = {}
+    t0 = time.perf_counter()
+    block = 4  # rows per thread per round
+    rounds = 0
+    while True:
+        for w in mats:
+            r0 = rows_done.get(w["name"], 0)
+            r1 = min(w["R"], r0 + block * threads)
+            if r1 <= r0:
+                continue
+            Wsl = np.ascontiguousarray(w["W"][r0:r1])
+            R = r1 - r0
+
+            def work(k, Wsl=Wsl, R=R, w=w):
+                a = k * R // threads
+                b = (k + 1) * R // threads
+                if b <= a:
+                    return
+                part = np.ascontiguousarray(Wsl[a:b])
+                oracle.mask(part, w["dtype"], n, m)
+                vals, meta = oracle.compress(part, w["dtype"], n, m)
+                oracle.decompress(vals, meta, w["dtype"], b - a, w["K"], n, m)
+                Y = np.empty((b - a, w["T"]), dtype=np.float64)
+                oracle.spmm_rows(vals, meta, b - a, w["K"], n, m, w["X"], w["dtype"], 0, b - a, Y)
+
+            with ThreadPoolExecutor(max_workers=threads) as ex:
+                list(ex.map(work, range(threads)))
+            rows_done[w["name"]] = r1
+            F += 2.0 * R * w["K"] * w["T"]
+        rounds += 1
+        if time.perf_counter() - t0 >= budget_s or all(rows_done.get(w["name"], 0) >= w["R"]
+                                                       for w in mats):
+            break
+    dt = time.perf_counter() - t0
+    sample = ", ".join(f"{k}: rows 0..{v} of {next(w['R'] for w in mats if w['name'] == k)}"
+                       for k, v in rows_done.items())
+    return {"value": F / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"mask+compress+decompress+product of {sample} (fp64 product, all T columns)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama_mlp", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense GEMM baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the kernels shard by rows of W with no exchange, but this build measures one GPU)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import masking_sparse_gemm_amd as nm
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    names, (n, m) = WORKLOADS[args.workload]
+
+    # ---- inputs, resident in HBM before timing ----
+    mats = []
+    for name in names:
+        w = synth.WORKLOADS[name]
+        W, X = w.W(), w.X()
+        tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
+
+        def to_dev(a, tdt=tdt):
+            if a.dtype == np.float32:
+                return torch.from_numpy(a).to(dev)
+            return torch.from_numpy(a.view(np.int16)).view(tdt).to(dev)
+
+        s = 4 if w.dtype == "f32" else 2
+        d = dict(name=name, R=w.R, K=w.K, T=w.T, dtype=w.dtype, s=s, W=W, X=X, Wd=to_dev(W),
+                 Xd=to_dev(X))
+        d["vals"] = torch.empty((w.R, w.K // m * n), dtype=tdt, device=dev)
+        d["meta"] = torch.empty((w.R, nm.meta_words_per_row(w.K, n, m)), dtype=torch.int32,
+                                device=dev)
+        d["mask"] = torch.empty((w.R, w.K), dtype=torch.bool, device=dev)
+        d["dec"] = torch.empty((w.R, w.K), dtype=tdt, device=dev)
+        d["Y"] = torch.empty((w.R, w.T), dtype=tdt, device=dev)
+        mats.append(d)
+    dtype = mats[0]["dtype"]
+    L = nm.lib()
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    DT = {"f32": 0, "f16": 1, "bf16": 2}[dtype]
+    kinds = ["mask", "compress", "decompress", "spmm"]
+
+    def launch(d, kind):
+        if kind == "mask":
+            rc = L.nm_mask(d["Wd"].data_ptr(), DT, d["R"], d["K"], n, m, d["mask"].data_ptr(), sp)
+        elif kind == "compress":
+            rc = L.nm_compress(d["Wd"].data_ptr(), DT, d["R"], d["K"], n, m, d["vals"].data_ptr(),
+                               d["meta"].data_ptr(), sp)
+        elif kind == "decompress":
+            rc = L.nm_decompress(d["vals"].data_ptr(), d["meta"].data_ptr(), DT, d["R"], d["K"],
+                                 n, m, d["dec"].data_ptr(), sp)
+        else:
+            rc = L.nm_spmm(d["vals"].data_ptr(), d["meta"].data_ptr(), d["R"], d["K"], n, m,
+                           d["Xd"].data_ptr(), d["T"], DT, d["Y"].data_ptr(), DT, sp)
+        if rc != 0:
+            raise RuntimeError(f"{kind} failed: {nm.status_str(rc)}")
+
+    def step(events=None):
+        for d in mats:
+            for kind in kinds:
+                if events is not None:
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    launch(d, kind)
+                    e1.record(stream)
+                    events.append((d["name"], kind, e0, e1))
+                else:
+                    launch(d, kind)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` steps, synchronised on both sides ----
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # ---- per-kernel durations, HIP events on the launch stream (separate pass) ----
+    events = []
+    for _ in range(args.steps):
+        step(events)
+    torch.cuda.synchronize()
+    per = {}
+    for name, kind, e0, e1 in events:
+        per.setdefault((name, kind), []).append(e0.elapsed_time(e1))
+
+    F_eff = sum(2.0 * d["R"] * d["K"] * d["T"] for d in mats)
+    F_alg = F_eff * n / m
+    value = F_eff / (ms_per_step * 1e-3) / 1e12
+
+    kernels = {}
+    tot = {k: [0.0, 0.0] for k in kinds}  # [seconds per step, algorithmic bytes per step]
+    for d in mats:
+        ab = algorithmic_bytes(d["R"], d["K"], d["T"], n, m, d["s"])
+        for kind in kinds:
+            t = float(np.mean(per[(d["name"], kind)])) * 1e-3
+            entry = {"us": round(t * 1e6, 2), "alg_bytes": ab[kind],
+                     "gbps": round(ab[kind] / t / 1e9, 1)}
+            if kind == "spmm":
+                f_alg = 2.0 * d["R"] * d["K"] * d["T"] * n / m
+                entry["eff_tflops"] = round(2.0 * d["R"] * d["K"] * d["T"] / t / 1e12, 1)
+                entry["alg_tflops"] = round(f_alg / t / 1e12, 1)
+            else:
+                entry["frac_hbm"] = round(ab[kind] / t / 1e9 / PEAK_HBM_GBS, 3)
+            kernels[f"{d['name']}.{kind}"] = entry
+            tot[kind][0] += t
+            tot[kind][1] += ab[kind]
+
+    spmm_t = tot["spmm"][0]
+    achieved = F_alg / spmm_t / 1e12
+    peak = PEAK_MFMA_TFLOPS[dtype]
+    roofline = {"bound": "mfma", "kernel": "nm_spmm (smfmac 16x16x64)" if n * 2 == m else "nm_spmm",
+                "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None,
+                "note": "achieved = algorithmic flops 2*R*(K*N/M)*T per launch / mean launch time"}
+
+    mc_bytes = tot["mask"][1] + tot["compress"][1]
+    mc_time = tot["mask"][0] + tot["compress"][0]
+    mask_compress = {"gbps": round(mc_bytes / mc_time / 1e9, 1),
+                     "frac_hbm": round(mc_bytes / mc_time / 1e9 / PEAK_HBM_GBS, 3),
+                     "compress_gbps": round(tot["compress"][1] / tot["compress"][0] / 1e9, 1),
+                     "compress_frac_hbm": round(tot["compress"][1] / tot["compress"][0] / 1e9
+                                                / PEAK_HBM_GBS, 3)}
+
+    dense = None
+    if not args.no_dense:
+        # hipBLASLt through torch.matmul on the decompressed weight, same dtype and shapes
+        ts = []
+        for d in mats:
+            if d["dtype"] == "f32":
+                continue
+            A, B = d["dec"], d["Xd"]
+            for _ in range(3):
+                torch.matmul(A, B)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(args.steps):
+                torch.matmul(A, B)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / args.steps * 1e-3)
+        if ts:
+            dense_t = sum(ts)
+            dense = {"tflops": round(F_eff / dense_t / 1e12, 1), "us_total": round(dense_t * 1e6, 1),
+                     "spmm_speedup": round(dense_t / spmm_t, 3),
+                     "how": "torch.matmul (hipBLASLt) on the decompressed weight, same dtype"}
+
+    cpu = None
+    if not args.no_cpu:
+        threads = max(1, min(16, os.cpu_count() or 1))
+        cpu = cpu_baseline(mats, n, m, threads)
+
+    w0 = mats[0]
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload,
+                   "matrices": [f"{d['name']} {d['R']}x{d['K']} X {d['K']}x{d['T']}" for d in mats],
+                   "pattern": f"{n}:{m}", "global_batch": w0["T"], "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "spmm_eff_tflops": round(F_eff / spmm_t / 1e12, 1),
+        "mask_compress": mask_compress,
+        "dense_gemm": dense,
+        "kernels": kernels,
+        "context": "pages: up to 2x dense math throughput on A100 sparse Tensor Cores (not a target)",
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,112 @@
+/*
+ * nm.h -- C ABI of libnm: N:M magnitude masking, compression and the
+ * compressed-sparse x dense product on AMD Instinct MI355X (gfx950).
+ *
+ * Plain C; no HIP or PyTorch types appear in the signatures.  Every pointer
+ * argument is a DEVICE pointer to memory the caller owns; the library
+ * allocates nothing and keeps no state besides a once-initialised record of
+ * which devices it has checked.  Calls are asynchronous on `stream` (a
+ * hipStream_t passed as void*, NULL = the default stream): NM_OK means the
+ * work was enqueued, and a fault inside a kernel surfaces at the caller's next
+ * synchronisation.  Arguments are validated before anything is launched; on
+ * any error nothing is written.  Outputs must not alias inputs.
+ *
+ * Layouts (all dense, row-major, no padding between rows):
+ *   W      R x K            elements of `dt`; groups are M consecutive elements along K
+ *   mask   R x K            uint8, 1 = kept, 0 = pruned
+ *   values R x (K*N/M)      elements of `dt`; the N kept values of each group, in
+ *                           ascending position order
+ *   meta   R x words(K,N,M) uint32; see nm_meta_words_per_row
+ *   X      K x T            elements of `dt`
+ *   Y      R x T            elements of `y_dt`
+ *
+ * Sources, cited by page title and section:
+ *   "量化友好的SR-STE稀疏化训练" (blog.bakeneko-kuro.com), section "概念" (N:M keeps
+ *   N non-zero weights in every M consecutive ones) and section "NVIDA Apex内的静态
+ *   掩码稀疏" (ASP's exhaustive search: score every N-of-M pattern by the L1 norm of
+ *   the weights it keeps, take the best per group of M along the contiguous dim).
+ *   "[리뷰] Accelerating Sparse Deep Neural Networks" (moon-walker.medium.com),
+ *   section "2:4 Sparsity의 benefits" (R*C/2 value array plus 2 bits of position
+ *   per value; N values stored per group even when it holds more zeros) and
+ *   section "Tensor Scores 상에서 구조적인 sparse GEMM" (sparse first operand,
+ *   compressed by the application, times a dense operand gives a dense result;
+ *   16-bit inputs and outputs, fp32 only in a reduced mode).
+ */
+#ifndef NM_H
+#define NM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NM_ABI_VERSION 1
+
+typedef enum {
+  NM_OK = 0,
+  NM_ERR_NULL = 1,        /* a required pointer is NULL                              */
+  NM_ERR_SHAPE = 2,       /* negative size, or K not a multiple of M                 */
+  NM_ERR_PATTERN = 3,     /* N:M outside 1 <= N <= M, M in {2, 4, 8}                 */
+  NM_ERR_DTYPE = 4,       /* unknown dtype, or y_dt neither dt nor NM_F32            */
+  NM_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned                        */
+  NM_ERR_UNSUPPORTED = 6, /* valid arguments this build has no kernel for            */
+  NM_ERR_DEVICE = 7       /* no usable gfx950 device, or the launch failed           */
+} nm_status;
+
+typedef enum { NM_F32 = 0, NM_F16 = 1, NM_BF16 = 2 } nm_dtype;
+
+typedef void* nm_stream_t; /* a hipStream_t; NULL selects the default stream */
+
+/* NM_ABI_VERSION of the loaded library. */
+int nm_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* nm_status_str(nm_status s);
+
+/* Bytes of the value array: R * (K / m * n) * sizeof(dt); 0 for invalid arguments. */
+size_t nm_values_bytes(int64_t R, int64_t K, int n, int m, nm_dtype dt);
+
+/* Metadata words per row: ceil((K / m) * n * b / 32) with b = log2(m) bits per kept
+ * value (1 for 1:2, 2 for 2:4, 3 for 4:8).  Field f = g*n + j of a row holds the
+ * position (0..m-1) of the j-th kept value of group g at bit offset f*b of the
+ * row's bitstream, least significant bit first (word f*b/32, bit f*b%32; a 3-bit
+ * field may straddle two words).  Every row starts on a word boundary and unused
+ * high bits are zero.  For 2:4 this makes each group one nibble i0 | i1 << 2.
+ * Returns -1 for invalid arguments. */
+int64_t nm_meta_words_per_row(int64_t K, int n, int m);
+
+/* Magnitude-best N:M mask of W ("NVIDA Apex内的静态掩码稀疏"): in every group of m
+ * consecutive elements along K the n positions with the largest sum of |w| are
+ * kept; equal sums go to the lexicographically first position tuple (lower
+ * index wins).  |w| is compared exactly (as the sign-cleared bit pattern, which
+ * also ranks NaN above Inf above every finite value).  Writes mask (R x K). */
+nm_status nm_mask(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m, uint8_t* mask,
+                  nm_stream_t stream);
+
+/* Mask and compress in one pass ("2:4 Sparsity의 benefits"): the kept values of
+ * each group in ascending position order go to `values` (bitwise copies, so -0
+ * stays -0) and their positions to `meta` (layout above). */
+nm_status nm_compress(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m,
+                      void* values, uint32_t* meta, nm_stream_t stream);
+
+/* Inverse of nm_compress: W_out (R x K) gets each stored value at its recorded
+ * position and +0 (all-zero bits) everywhere else.  The metadata is trusted: a
+ * field that repeats a position within a group leaves the later value there. */
+nm_status nm_decompress(const void* values, const uint32_t* meta, nm_dtype dt, int64_t R,
+                        int64_t K, int n, int m, void* W_out, nm_stream_t stream);
+
+/* Y = W_sparse * X ("Tensor Scores 상에서 구조적인 sparse GEMM"): W_sparse is the
+ * R x K matrix that (values, meta) encode, X is K x T, Y is R x T.  Products are
+ * accumulated in fp32 and rounded once to y_dt (round to nearest even); y_dt
+ * must be dt or NM_F32.  The metadata is trusted (well-formedness is the
+ * caller's responsibility, as for any compressed operand). */
+nm_status nm_spmm(const void* values, const uint32_t* meta, int64_t R, int64_t K, int n, int m,
+                  const void* X, int64_t T, nm_dtype dt, void* Y, nm_dtype y_dt,
+                  nm_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NM_H */

@@ -1,0 +1,147 @@
+// nm_api.hip -- the C ABI declared in include/nm.h: argument checks and dispatch.
+//
+// Every check runs on the host before any HIP call, so a rejected call touches
+// neither the device nor the outputs.  The only global state is a per-device
+// record of whether the device is a gfx950, filled on first use.
+#include <atomic>
+#include <cstring>
+
+#include "../../include/nm.h"
+#include "nm_launch.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, 2 = unsupported device
+std::atomic<int> g_device_ok[kMaxDevices];
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// A pointer may be NULL only when the array it addresses is empty.
+bool missing(const void* p, int64_t count) { return p == nullptr && count > 0; }
+
+int meta_bits_of(int m) { return m == 2 ? 1 : m == 4 ? 2 : m == 8 ? 3 : -1; }
+
+int elem_bytes(nm_dtype dt) { return dt == NM_F32 ? 4 : 2; }
+
+bool valid_dtype(int dt) { return dt == NM_F32 || dt == NM_F16 || dt == NM_BF16; }
+
+nm_status check_pattern(int n, int m) {
+  if (meta_bits_of(m) < 0 || n < 1 || n > m) return NM_ERR_PATTERN;
+  return NM_OK;
+}
+
+nm_status check_shape(int64_t R, int64_t K, int m) {
+  if (R < 0 || K < 0 || K % m != 0) return NM_ERR_SHAPE;
+  // element counts must fit the kernels' 64-bit index arithmetic comfortably
+  if (R > 0 && K > ((int64_t)1 << 40) / R) return NM_ERR_SHAPE;
+  return NM_OK;
+}
+
+nm_status check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return NM_ERR_DEVICE;
+  int state = g_device_ok[dev].load(std::memory_order_acquire);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return NM_ERR_DEVICE;
+    state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_device_ok[dev].store(state, std::memory_order_release);
+  }
+  return state == 1 ? NM_OK : NM_ERR_DEVICE;
+}
+
+nm_status from_hip(hipError_t e) { return e == hipSuccess ? NM_OK : NM_ERR_DEVICE; }
+
+}  // namespace
+
+extern "C" {
+
+int nm_abi_version(void) { return NM_ABI_VERSION; }
+
+const char* nm_status_str(nm_status s) {
+  switch (s) {
+    case NM_OK: return "ok";
+    case NM_ERR_NULL: return "null pointer";
+    case NM_ERR_SHAPE: return "bad shape (negative size or K not a multiple of M)";
+    case NM_ERR_PATTERN: return "bad N:M pattern (need 1 <= N <= M, M in {2,4,8})";
+    case NM_ERR_DTYPE: return "bad dtype (unknown, or output neither input dtype nor fp32)";
+    case NM_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case NM_ERR_UNSUPPORTED: return "unsupported combination";
+    case NM_ERR_DEVICE: return "device error (no gfx950 device, or launch failed)";
+  }
+  return "unknown status";
+}
+
+size_t nm_values_bytes(int64_t R, int64_t K, int n, int m, nm_dtype dt) {
+  if (!valid_dtype(dt) || check_pattern(n, m) != NM_OK || check_shape(R, K, m) != NM_OK) return 0;
+  return (size_t)(R * (K / m * n) * elem_bytes(dt));
+}
+
+int64_t nm_meta_words_per_row(int64_t K, int n, int m) {
+  if (check_pattern(n, m) != NM_OK || K < 0 || K % m != 0) return -1;
+  return ((K / m) * n * meta_bits_of(m) + 31) / 32;
+}
+
+nm_status nm_mask(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m, uint8_t* mask,
+                  nm_stream_t stream) {
+  if (!valid_dtype(dt)) return NM_ERR_DTYPE;
+  nm_status st = check_pattern(n, m);
+  if (st != NM_OK) return st;
+  if ((st = check_shape(R, K, m)) != NM_OK) return st;
+  if (missing(W, R * K) || missing(mask, R * K)) return NM_ERR_NULL;
+  if (R * K == 0) return NM_OK;
+  if (!aligned16(W) || !aligned16(mask)) return NM_ERR_ALIGN;
+  if ((st = check_device()) != NM_OK) return st;
+  return from_hip(nm::launch_select(W, elem_bytes(dt), R, K, n, m, nullptr, nullptr, mask,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+nm_status nm_compress(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m,
+                      void* values, uint32_t* meta, nm_stream_t stream) {
+  if (!valid_dtype(dt)) return NM_ERR_DTYPE;
+  nm_status st = check_pattern(n, m);
+  if (st != NM_OK) return st;
+  if ((st = check_shape(R, K, m)) != NM_OK) return st;
+  if (missing(W, R * K) || missing(values, R * K) || missing(meta, R * K)) return NM_ERR_NULL;
+  if (R * K == 0) return NM_OK;
+  if (!aligned16(W) || !aligned16(values) || !aligned16(meta)) return NM_ERR_ALIGN;
+  if ((st = check_device()) != NM_OK) return st;
+  return from_hip(nm::launch_select(W, elem_bytes(dt), R, K, n, m, values, meta, nullptr,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+nm_status nm_decompress(const void* values, const uint32_t* meta, nm_dtype dt, int64_t R,
+                        int64_t K, int n, int m, void* W_out, nm_stream_t stream) {
+  if (!valid_dtype(dt)) return NM_ERR_DTYPE;
+  nm_status st = check_pattern(n, m);
+  if (st != NM_OK) return st;
+  if ((st = check_shape(R, K, m)) != NM_OK) return st;
+  if (missing(values, R * K) || missing(meta, R * K) || missing(W_out, R * K)) return NM_ERR_NULL;
+  if (R * K == 0) return NM_OK;
+  if (!aligned16(values) || !aligned16(meta) || !aligned16(W_out)) return NM_ERR_ALIGN;
+  if ((st = check_device()) != NM_OK) return st;
+  return from_hip(nm::launch_decompress(values, meta, elem_bytes(dt), R, K, n, m, W_out,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+nm_status nm_spmm(const void* values, const uint32_t* meta, int64_t R, int64_t K, int n, int m,
+                  const void* X, int64_t T, nm_dtype dt, void* Y, nm_dtype y_dt,
+                  nm_stream_t stream) {
+  if (!valid_dtype(dt) || !valid_dtype(y_dt) || (y_dt != dt && y_dt != NM_F32))
+    return NM_ERR_DTYPE;
+  nm_status st = check_pattern(n, m);
+  if (st != NM_OK) return st;
+  if ((st = check_shape(R, K, m)) != NM_OK) return st;
+  if (T < 0 || (K > 0 && T > ((int64_t)1 << 40) / K) || (R > 0 && T > ((int64_t)1 << 40) / R))
+    return NM_ERR_SHAPE;
+  if (missing(values, R * K) || missing(meta, R * K) || missing(X, K * T) || missing(Y, R * T))
+    return NM_ERR_NULL;
+  if (R * T == 0) return NM_OK;
+  if (!aligned16(values) || !aligned16(meta) || !aligned16(X) || !aligned16(Y)) return NM_ERR_ALIGN;
+  if ((st = check_device()) != NM_OK) return st;
+  return from_hip(nm::launch_spmm(values, meta, R, K, n, m, X, T, (int)dt, Y, (int)y_dt,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

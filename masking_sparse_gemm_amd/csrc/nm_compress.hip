@@ -1,0 +1,476 @@
+// nm_compress.hip -- mask, compress and decompress kernels (gfx950).
+//
+// These passes move bytes and compare integers; they are bound by HBM bandwidth,
+// not by arithmetic.  The fast ("flat") kernels treat W as one stream of 16-byte
+// units: a lane loads one unit (8 x 16-bit or 4 x fp32 elements, or 8 fp32 for
+// M = 8) with a single coalesced 16-byte load, selects its groups in registers,
+// writes its kept values with one 4/8/16-byte store and packs its metadata bits
+// into 32-bit words together with its neighbours: wave shuffles when a whole
+// number of lanes fills a word, a per-wave LDS bit buffer otherwise.  The flat
+// kernels need every row to hold a whole number of units and of metadata words,
+// so that rows concatenate into one stream; any other shape uses the simple
+// per-group / per-word kernels at the bottom, which make no such assumption.
+//
+// Formats ("[리뷰] Accelerating Sparse Deep Neural Networks", section
+// "2:4 Sparsity의 benefits"): values hold the N kept elements of each group in
+// ascending position order; metadata field f = g*N + j of a row holds position
+// j of group g in b = log2(M) bits at bit f*b of the row, least significant first.
+#include "nm_device.h"
+#include "nm_launch.h"
+
+namespace nm {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnitsPerThread = 4;
+
+template <typename E, int M>
+struct UnitShape {
+  static constexpr int kElems = (16 / (int)sizeof(E)) > M ? (16 / (int)sizeof(E)) : M;
+  static constexpr int kWords = kElems * (int)sizeof(E) / 4;  // 32-bit words loaded
+  static constexpr int kGroups = kElems / M;
+};
+
+template <int NW>
+__device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&w)[NW]) {
+  static_assert(NW % 4 == 0, "units are whole 16-byte vectors");
+#pragma unroll
+  for (int i = 0; i < NW / 4; ++i) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p) + i);
+    w[4 * i + 0] = v[0];
+    w[4 * i + 1] = v[1];
+    w[4 * i + 2] = v[2];
+    w[4 * i + 3] = v[3];
+  }
+}
+
+template <int NW>
+__device__ __forceinline__ void store_words(uint32_t* p, const uint32_t (&w)[NW]) {
+  if constexpr (NW == 4) {
+    __builtin_nontemporal_store(u32x4_t{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4_t*>(p));
+  } else if constexpr (NW == 2) {
+    __builtin_nontemporal_store(u32x2_t{w[0], w[1]}, reinterpret_cast<u32x2_t*>(p));
+  } else if constexpr (NW == 1) {
+    __builtin_nontemporal_store(w[0], p);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) p[i] = w[i];
+  }
+}
+
+// Selection for every group of one unit: kept positions and the unit's metadata bits.
+template <typename E, int N, int M>
+struct UnitSelection {
+  using S = UnitShape<E, M>;
+  int pos[S::kGroups][N];
+  uint32_t keep[S::kGroups];
+
+  __device__ __forceinline__ void run(const uint32_t (&w)[S::kWords]) {
+#pragma unroll
+    for (int g = 0; g < S::kGroups; ++g) {
+      uint32_t key[M];
+#pragma unroll
+      for (int i = 0; i < M; ++i) key[i] = word_elem<E>(w, g * M + i) & Elem<E>::kKeyMask;
+      keep[g] = keep_bits<N, M>(key);
+      kept_positions<N>(keep[g], pos[g]);
+    }
+  }
+  // this unit's metadata: S::kGroups * N fields of b bits, first field in the low bits
+  __device__ __forceinline__ uint32_t meta_bits_of_unit() const {
+    constexpr int b = meta_bits(M);
+    uint32_t bits = 0;
+#pragma unroll
+    for (int g = 0; g < S::kGroups; ++g)
+#pragma unroll
+      for (int j = 0; j < N; ++j) bits |= (uint32_t)pos[g][j] << ((g * N + j) * b);
+    return bits;
+  }
+};
+
+// OR-reduce `v` over aligned runs of L lanes (L a power of two <= 32).
+template <int L>
+__device__ __forceinline__ uint32_t or_reduce_lanes(uint32_t v) {
+#pragma unroll
+  for (int s = 1; s < L; s <<= 1) v |= __shfl_xor(v, s);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Flat mask / compress kernel.
+// ---------------------------------------------------------------------------
+template <typename E, int N, int M, bool kMask, bool kCompress>
+__global__ void __launch_bounds__(kThreads) flat_select_kernel(const uint32_t* __restrict__ W,
+                                                               int64_t units,
+                                                               uint32_t* __restrict__ values,
+                                                               uint32_t* __restrict__ meta,
+                                                               uint8_t* __restrict__ mask) {
+  using S = UnitShape<E, M>;
+  constexpr int b = meta_bits(M);
+  constexpr int kUnitBits = S::kGroups * N * b;       // metadata bits per unit
+  constexpr int kValWords = S::kGroups * N * (int)sizeof(E) / 4;
+  constexpr bool kShuffle = (32 % kUnitBits) == 0;   // a whole number of units per word
+  constexpr int kWaveWords = 64 * kUnitBits / 32;    // words one wave-step writes
+  __shared__ uint32_t lds_bits[kThreads / 64][kShuffle ? 1 : kWaveWords];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t block_first = (int64_t)blockIdx.x * kThreads * kUnitsPerThread;
+
+#pragma unroll
+  for (int it = 0; it < kUnitsPerThread; ++it) {
+    const int64_t wave_first = block_first + (int64_t)it * kThreads + wave * 64;
+    const int64_t u = wave_first + lane;
+    const bool live = u < units;
+    uint32_t w[S::kWords];
+    if (live) {
+      load_words<S::kWords>(W + u * S::kWords, w);
+    } else {
+#pragma unroll
+      for (int i = 0; i < S::kWords; ++i) w[i] = 0;
+    }
+    UnitSelection<E, N, M> sel;
+    sel.run(w);
+
+    if constexpr (kMask) {
+      if (live) {
+        // one byte per element, 1 = kept
+        uint32_t mb[S::kElems / 4];
+#pragma unroll
+        for (int i = 0; i < S::kElems / 4; ++i) mb[i] = 0;
+#pragma unroll
+        for (int g = 0; g < S::kGroups; ++g)
+#pragma unroll
+          for (int i = 0; i < M; ++i) {
+            const int e = g * M + i;
+            mb[e / 4] |= ((sel.keep[g] >> i) & 1u) << (8 * (e % 4));
+          }
+        store_words<S::kElems / 4>(reinterpret_cast<uint32_t*>(mask + u * S::kElems), mb);
+      }
+    }
+    if constexpr (kCompress) {
+      if (live) {
+        uint32_t vw[kValWords];
+#pragma unroll
+        for (int i = 0; i < kValWords; ++i) vw[i] = 0;
+#pragma unroll
+        for (int g = 0; g < S::kGroups; ++g)
+#pragma unroll
+          for (int j = 0; j < N; ++j) {
+            const uint32_t v = group_elem<E, M>(w + g * M * (int)sizeof(E) / 4, sel.pos[g][j]);
+            const int k = g * N + j;  // value index inside the unit
+            if constexpr (sizeof(E) == 2)
+              vw[k / 2] |= v << (16 * (k % 2));
+            else
+              vw[k] = v;
+          }
+        store_words<kValWords>(values + u * kValWords, vw);
+      }
+      const uint32_t bits = live ? sel.meta_bits_of_unit() : 0u;
+      if constexpr (kShuffle) {
+        constexpr int L = 32 / kUnitBits;  // lanes per metadata word
+        const uint32_t word = or_reduce_lanes<L>(bits << ((lane % L) * kUnitBits));
+        const int64_t widx = u / L;
+        if ((lane % L) == 0 && live) meta[widx] = word;
+      } else {
+        // bits of lane l start at bit l*kUnitBits of this wave-step's kWaveWords words
+        uint32_t* buf = lds_bits[wave];
+        for (int i = lane; i < kWaveWords; i += 64) buf[i] = 0;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        const int bit = lane * kUnitBits;
+        atomicOr(&buf[bit / 32], bits << (bit % 32));
+        if ((bit % 32) + kUnitBits > 32) atomicOr(&buf[bit / 32 + 1], bits >> (32 - bit % 32));
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        const int64_t total_words = units * kUnitBits / 32;
+        const int64_t first_word = wave_first * kUnitBits / 32;
+        for (int i = lane; i < kWaveWords; i += 64)
+          if (first_word + i < total_words) meta[first_word + i] = buf[i];
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Flat decompress kernel: one unit of output per lane.
+// ---------------------------------------------------------------------------
+template <typename E, int N, int M>
+__global__ void __launch_bounds__(kThreads) flat_decompress_kernel(
+    const uint32_t* __restrict__ values, const uint32_t* __restrict__ meta, int64_t units,
+    uint32_t* __restrict__ out) {
+  using S = UnitShape<E, M>;
+  constexpr int b = meta_bits(M);
+  constexpr int kUnitBits = S::kGroups * N * b;
+  constexpr int kValWords = S::kGroups * N * (int)sizeof(E) / 4;
+  const int64_t block_first = (int64_t)blockIdx.x * kThreads * kUnitsPerThread;
+#pragma unroll
+  for (int it = 0; it < kUnitsPerThread; ++it) {
+    const int64_t u = block_first + (int64_t)it * kThreads + threadIdx.x;
+    if (u >= units) continue;
+    uint32_t vw[kValWords];
+    if constexpr (kValWords == 4) {
+      const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(values) + u);
+      vw[0] = v[0]; vw[1] = v[1]; vw[2] = v[2]; vw[3] = v[3];
+    } else if constexpr (kValWords == 2) {
+      const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(values) + u);
+      vw[0] = v[0]; vw[1] = v[1];
+    } else {
+#pragma unroll
+      for (int i = 0; i < kValWords; ++i) vw[i] = values[u * kValWords + i];
+    }
+    const int64_t bit = u * kUnitBits;
+    uint64_t window = meta[bit / 32];
+    if ((bit % 32) + kUnitBits > 32) window |= (uint64_t)meta[bit / 32 + 1] << 32;
+    const uint32_t bits = (uint32_t)(window >> (bit % 32));
+    uint32_t ow[S::kWords];
+#pragma unroll
+    for (int i = 0; i < S::kWords; ++i) ow[i] = 0;
+#pragma unroll
+    for (int g = 0; g < S::kGroups; ++g) {
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        const int k = g * N + j;
+        const int p = (bits >> (k * b)) & ((1u << b) - 1u);
+        const uint32_t v = word_elem<E>(vw, k);
+        // out[g*M + p] = v, as selects over the M compile-time positions
+#pragma unroll
+        for (int i = 0; i < M; ++i) {
+          const int e = g * M + i;
+          if constexpr (sizeof(E) == 2) {
+            const uint32_t sh = 16 * (e % 2);
+            const uint32_t cur = ow[e / 2];
+            ow[e / 2] = (p == i) ? ((cur & ~(0xFFFFu << sh)) | (v << sh)) : cur;
+          } else {
+            ow[e] = (p == i) ? v : ow[e];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < S::kWords / 4; ++i)
+      __builtin_nontemporal_store(u32x4_t{ow[4 * i], ow[4 * i + 1], ow[4 * i + 2], ow[4 * i + 3]},
+                                  reinterpret_cast<u32x4_t*>(out + u * S::kWords) + i);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Shape-agnostic kernels (any R, K with K % M == 0).
+// ---------------------------------------------------------------------------
+template <typename E, int N, int M>
+__device__ __forceinline__ void select_group(const E* W, int64_t base, int (&pos)[N],
+                                             uint32_t& keep) {
+  uint32_t key[M];
+#pragma unroll
+  for (int i = 0; i < M; ++i) key[i] = (uint32_t)W[base + i] & Elem<E>::kKeyMask;
+  keep = keep_bits<N, M>(key);
+  kept_positions<N>(keep, pos);
+}
+
+// one thread per group: mask bytes and/or values
+template <typename E, int N, int M, bool kMask, bool kValues>
+__global__ void __launch_bounds__(kThreads) group_kernel(const E* __restrict__ W, int64_t groups,
+                                                         E* __restrict__ values,
+                                                         uint8_t* __restrict__ mask) {
+  const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (g >= groups) return;
+  int pos[N];
+  uint32_t keep;
+  select_group<E, N, M>(W, g * M, pos, keep);
+  if constexpr (kMask)
+#pragma unroll
+    for (int i = 0; i < M; ++i) mask[g * M + i] = (keep >> i) & 1u;
+  if constexpr (kValues)
+#pragma unroll
+    for (int j = 0; j < N; ++j) values[g * N + j] = W[g * M + pos[j]];
+}
+
+// one thread per metadata word
+template <typename E, int N, int M>
+__global__ void __launch_bounds__(kThreads) meta_word_kernel(const E* __restrict__ W, int64_t R,
+                                                             int64_t K, int64_t wpr,
+                                                             uint32_t* __restrict__ meta) {
+  constexpr int b = meta_bits(M);
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= R * wpr) return;
+  const int64_t r = idx / wpr, w = idx % wpr;
+  const int64_t fields = K / M * N;
+  const int64_t f0 = (32 * w) / b;
+  int64_t f1 = (32 * w + 31) / b;
+  if (f1 > fields - 1) f1 = fields - 1;
+  uint32_t word = 0;
+  for (int64_t g = f0 / N; g <= f1 / N; ++g) {
+    int pos[N];
+    uint32_t keep;
+    select_group<E, N, M>(W, r * K + g * M, pos, keep);
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int64_t f = g * N + j;
+      if (f < f0 || f > f1) continue;
+      const int64_t off = f * b - 32 * w;  // may be negative for a field straddling in
+      word |= off >= 0 ? (uint32_t)pos[j] << off : (uint32_t)pos[j] >> (-off);
+    }
+  }
+  meta[idx] = word;
+}
+
+// one thread per group of the output
+template <typename E, int N, int M>
+__global__ void __launch_bounds__(kThreads) group_decompress_kernel(
+    const E* __restrict__ values, const uint32_t* __restrict__ meta, int64_t R, int64_t K,
+    int64_t wpr, E* __restrict__ out) {
+  constexpr int b = meta_bits(M);
+  const int64_t gpr = K / M;
+  const int64_t gi = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (gi >= R * gpr) return;
+  const int64_t r = gi / gpr, g = gi % gpr;
+  const uint32_t* mrow = meta + r * wpr;
+  E o[M];
+#pragma unroll
+  for (int i = 0; i < M; ++i) o[i] = 0;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const int64_t bit = (g * N + j) * b;
+    uint64_t window = mrow[bit / 32];
+    if ((bit % 32) + b > 32) window |= (uint64_t)mrow[bit / 32 + 1] << 32;
+    const int p = (int)((window >> (bit % 32)) & ((1u << b) - 1u));
+    const E v = values[r * (gpr * N) + g * N + j];
+#pragma unroll
+    for (int i = 0; i < M; ++i) o[i] = (p == i) ? v : o[i];
+  }
+#pragma unroll
+  for (int i = 0; i < M; ++i) out[r * K + g * M + i] = o[i];
+}
+
+inline unsigned blocks_for(int64_t work, int64_t per_block) {
+  return (unsigned)((work + per_block - 1) / per_block);
+}
+
+// Does one unit's value output fill a 4-, 8- or 16-byte store?
+template <typename E, int N, int M>
+constexpr bool flat_kernel_exists() {
+  constexpr int kValBytes = UnitShape<E, M>::kGroups * N * (int)sizeof(E);
+  return kValBytes == 4 || kValBytes == 8 || kValBytes == 16;
+}
+
+// Can rows be concatenated into one stream of whole units and whole metadata words?
+template <typename E, int N, int M>
+bool flat_ok(int64_t K) {
+  using S = UnitShape<E, M>;
+  constexpr int kUnitBits = S::kGroups * N * meta_bits(M);
+  if (!flat_kernel_exists<E, N, M>()) return false;
+  if (K % S::kElems != 0) return false;
+  const int64_t row_bits = (K / S::kElems) * kUnitBits;
+  if (row_bits % 32 != 0) return false;
+  // the LDS packing path writes whole 64-lane wave-steps; rows must hold whole words
+  return true;
+}
+
+template <typename E, int N, int M>
+hipError_t run_select(const void* W, int64_t R, int64_t K, void* values, uint32_t* meta,
+                      uint8_t* mask, hipStream_t s) {
+  using S = UnitShape<E, M>;
+  const int64_t elems = R * K;
+  if (elems == 0) return hipSuccess;
+  const bool want_mask = mask != nullptr, want_compress = values != nullptr;
+  if constexpr (flat_kernel_exists<E, N, M>()) {
+   if (flat_ok<E, N, M>(K)) {
+    const int64_t units = elems / S::kElems;
+    const unsigned grid = blocks_for(units, (int64_t)kThreads * kUnitsPerThread);
+    const uint32_t* w = static_cast<const uint32_t*>(W);
+    uint32_t* v = static_cast<uint32_t*>(values);
+    if (want_mask && want_compress)
+      flat_select_kernel<E, N, M, true, true><<<grid, kThreads, 0, s>>>(w, units, v, meta, mask);
+    else if (want_mask)
+      flat_select_kernel<E, N, M, true, false><<<grid, kThreads, 0, s>>>(w, units, v, meta, mask);
+    else
+      flat_select_kernel<E, N, M, false, true><<<grid, kThreads, 0, s>>>(w, units, v, meta, mask);
+    return hipGetLastError();
+   }
+  }
+  const int64_t groups = elems / M;
+  const unsigned grid = blocks_for(groups, kThreads);
+  const E* w = static_cast<const E*>(W);
+  E* v = static_cast<E*>(values);
+  if (want_mask && want_compress)
+    group_kernel<E, N, M, true, true><<<grid, kThreads, 0, s>>>(w, groups, v, mask);
+  else if (want_mask)
+    group_kernel<E, N, M, true, false><<<grid, kThreads, 0, s>>>(w, groups, v, mask);
+  else
+    group_kernel<E, N, M, false, true><<<grid, kThreads, 0, s>>>(w, groups, v, mask);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !want_compress) return e;
+  const int64_t wpr = ((K / M) * N * meta_bits(M) + 31) / 32;
+  if (R * wpr > 0)
+    meta_word_kernel<E, N, M><<<blocks_for(R * wpr, kThreads), kThreads, 0, s>>>(w, R, K, wpr, meta);
+  return hipGetLastError();
+}
+
+template <typename E, int N, int M>
+hipError_t run_decompress(const void* values, const uint32_t* meta, int64_t R, int64_t K,
+                          void* out, hipStream_t s) {
+  using S = UnitShape<E, M>;
+  const int64_t elems = R * K;
+  if (elems == 0) return hipSuccess;
+  if constexpr (flat_kernel_exists<E, N, M>()) {
+    if (flat_ok<E, N, M>(K)) {
+      const int64_t units = elems / S::kElems;
+      flat_decompress_kernel<E, N, M>
+          <<<blocks_for(units, (int64_t)kThreads * kUnitsPerThread), kThreads, 0, s>>>(
+              static_cast<const uint32_t*>(values), meta, units, static_cast<uint32_t*>(out));
+      return hipGetLastError();
+    }
+  }
+  const int64_t wpr = ((K / M) * N * meta_bits(M) + 31) / 32;
+  group_decompress_kernel<E, N, M><<<blocks_for(elems / M, kThreads), kThreads, 0, s>>>(
+      static_cast<const E*>(values), meta, R, K, wpr, static_cast<E*>(out));
+  return hipGetLastError();
+}
+
+// Compile-time dispatch over the supported N:M patterns.
+template <typename E, template <typename, int, int> class F, typename... A>
+hipError_t dispatch_nm(int n, int m, A... args) {
+#define NM_CASE(NN, MM) \
+  if (n == NN && m == MM) return F<E, NN, MM>::run(args...);
+  NM_CASE(1, 2) NM_CASE(2, 2)
+  NM_CASE(1, 4) NM_CASE(2, 4) NM_CASE(3, 4) NM_CASE(4, 4)
+  NM_CASE(1, 8) NM_CASE(2, 8) NM_CASE(3, 8) NM_CASE(4, 8)
+  NM_CASE(5, 8) NM_CASE(6, 8) NM_CASE(7, 8) NM_CASE(8, 8)
+#undef NM_CASE
+  return hipErrorInvalidValue;
+}
+
+template <typename E, int N, int M>
+struct SelectOp {
+  static hipError_t run(const void* W, int64_t R, int64_t K, void* values, uint32_t* meta,
+                        uint8_t* mask, hipStream_t s) {
+    return run_select<E, N, M>(W, R, K, values, meta, mask, s);
+  }
+};
+template <typename E, int N, int M>
+struct DecompressOp {
+  static hipError_t run(const void* values, const uint32_t* meta, int64_t R, int64_t K, void* out,
+                        hipStream_t s) {
+    return run_decompress<E, N, M>(values, meta, R, K, out, s);
+  }
+};
+
+}  // namespace
+
+hipError_t launch_select(const void* W, int elem_bytes, int64_t R, int64_t K, int n, int m,
+                         void* values, uint32_t* meta, uint8_t* mask, hipStream_t s) {
+  if (elem_bytes == 2)
+    return dispatch_nm<uint16_t, SelectOp>(n, m, W, R, K, values, meta, mask, s);
+  return dispatch_nm<uint32_t, SelectOp>(n, m, W, R, K, values, meta, mask, s);
+}
+
+hipError_t launch_decompress(const void* values, const uint32_t* meta, int elem_bytes, int64_t R,
+                             int64_t K, int n, int m, void* out, hipStream_t s) {
+  if (elem_bytes == 2)
+    return dispatch_nm<uint16_t, DecompressOp>(n, m, values, meta, R, K, out, s);
+  return dispatch_nm<uint32_t, DecompressOp>(n, m, values, meta, R, K, out, s);
+}
+
+}  // namespace nm

@@ -1,0 +1,106 @@
+// nm_device.h -- device-side building blocks shared by the libnm kernels (gfx950).
+//
+// Group selection.  ASP's exhaustive search ("量化友好的SR-STE稀疏化训练", section
+// "NVIDA Apex内的静态掩码稀疏") keeps, in each group of M, the N positions whose
+// magnitudes have the largest sum, the first such tuple on ties.  The kernels reach
+// the same set without enumerating patterns: element i is kept iff fewer than N
+// elements beat it, where j beats i when |w_j| > |w_i|, or |w_j| == |w_i| and j < i.
+// Every optimal pattern holds all elements above the N-th largest magnitude plus
+// enough elements equal to it; taking the lowest-index equal ones gives the
+// lexicographically first optimal tuple, and the count rule takes exactly those
+// (it is also the "drop the smallest of each group" reading of "[리뷰] Accelerating
+// Sparse Deep Neural Networks", section "Step-2: Weight Pruning").
+//
+// Magnitudes are compared as integers: the bit pattern with the sign cleared orders
+// exactly as |w| for every finite value and infinity (and puts NaN above Inf).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nm {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Raw storage of one element: uint16_t for bf16 / fp16, uint32_t for fp32.
+template <typename E>
+struct Elem;
+template <>
+struct Elem<uint16_t> {
+  static constexpr uint32_t kKeyMask = 0x7FFFu;
+  static constexpr int kBytes = 2;
+};
+template <>
+struct Elem<uint32_t> {
+  static constexpr uint32_t kKeyMask = 0x7FFFFFFFu;
+  static constexpr int kBytes = 4;
+};
+
+constexpr int meta_bits(int m) { return m == 2 ? 1 : m == 4 ? 2 : m == 8 ? 3 : m == 16 ? 4 : 0; }
+
+// Bit i of the result is set iff element i of the group is kept (count rule above).
+template <int N, int M>
+__device__ __forceinline__ uint32_t keep_bits(const uint32_t (&key)[M]) {
+  int beaten[M];
+#pragma unroll
+  for (int i = 0; i < M; ++i) beaten[i] = 0;
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+#pragma unroll
+    for (int j = i + 1; j < M; ++j) {
+      const int i_wins = key[i] >= key[j];  // equal magnitudes: the lower index wins
+      beaten[j] += i_wins;
+      beaten[i] += 1 - i_wins;
+    }
+  }
+  uint32_t keep = 0;
+#pragma unroll
+  for (int i = 0; i < M; ++i) keep |= (beaten[i] < N ? 1u : 0u) << i;
+  return keep;
+}
+
+// Positions of the N set bits of `keep`, ascending.
+template <int N>
+__device__ __forceinline__ void kept_positions(uint32_t keep, int (&pos)[N]) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    pos[j] = __builtin_ctz(keep);
+    keep &= keep - 1u;
+  }
+}
+
+// w[idx] for a compile-time-sized register array and a run-time idx, as a select tree
+// (no dynamic register indexing, so nothing spills to scratch).
+template <int NW>
+__device__ __forceinline__ uint32_t pick_word(const uint32_t* w, int idx) {
+  if constexpr (NW == 1) {
+    return w[0];
+  } else {
+    const uint32_t lo = pick_word<NW / 2>(w, idx & (NW / 2 - 1));
+    const uint32_t hi = pick_word<NW / 2>(w + NW / 2, idx & (NW / 2 - 1));
+    return (idx & (NW / 2)) ? hi : lo;
+  }
+}
+
+// Element `pos` of a group of M elements stored little-endian in 32-bit words.
+template <typename E, int M>
+__device__ __forceinline__ uint32_t group_elem(const uint32_t* gw, int pos) {
+  if constexpr (sizeof(E) == 2) {
+    const uint32_t w = pick_word<(M / 2 > 0 ? M / 2 : 1)>(gw, pos >> 1);
+    return (w >> ((pos & 1) * 16)) & 0xFFFFu;
+  } else {
+    return pick_word<M>(gw, pos);
+  }
+}
+
+// Element e of a register array of words.
+template <typename E>
+__device__ __forceinline__ uint32_t word_elem(const uint32_t* w, int e) {
+  if constexpr (sizeof(E) == 2)
+    return (w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+  else
+    return w[e];
+}
+
+}  // namespace nm

@@ -1,0 +1,140 @@
+"""Host-only checks of the C ABI: it loads, exports what include/nm.h declares,
+computes its size helpers, and rejects bad arguments before touching a device.
+No kernel is launched here."""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+import masking_sparse_gemm_amd as nm
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nm.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(nm.LIB_PATH), reason="libnm.so not built")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nm_[a-z_]+)\s*\(", text)))
+
+
+def test_header_lists_the_binding_exports():
+    assert header_functions() == sorted(nm.EXPORTS)
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    L = nm.lib()
+    for name in header_functions():
+        assert hasattr(L, name), name
+    assert L.nm_abi_version() == 1
+
+
+@needs_lib
+def test_status_strings():
+    for code in range(8):
+        s = nm.status_str(code)
+        assert s and s != "unknown status"
+    assert nm.status_str(99) == "unknown status"
+
+
+@needs_lib
+@pytest.mark.parametrize("K,n,m", [(128, 2, 4), (768, 2, 4), (4096, 1, 2), (4096, 4, 8),
+                                    (11008, 2, 4), (8, 4, 8), (12, 2, 4), (40, 2, 4), (0, 2, 4),
+                                    (96, 3, 8), (64, 8, 8), (16, 1, 4)])
+def test_meta_words_per_row_matches_oracle(K, n, m):
+    assert nm.meta_words_per_row(K, n, m) == oracle.meta_words_per_row(K, n, m)
+
+
+@needs_lib
+def test_size_helpers_reject_bad_arguments():
+    L = nm.lib()
+    assert L.nm_meta_words_per_row(6, 2, 4) == -1
+    assert L.nm_meta_words_per_row(16, 2, 16) == -1  # M = 16 is not a GPU pattern
+    assert L.nm_meta_words_per_row(16, 0, 4) == -1
+    assert L.nm_values_bytes(3072, 768, 2, 4, nm.NM_BF16) == 3072 * 384 * 2
+    assert L.nm_values_bytes(64, 128, 2, 4, nm.NM_F32) == 64 * 64 * 4
+    assert L.nm_values_bytes(64, 130, 2, 4, nm.NM_F32) == 0
+    assert L.nm_values_bytes(64, 128, 2, 4, 7) == 0
+
+
+FAKE = 0x10000  # aligned, never dereferenced: validation fails before any device access
+
+
+@needs_lib
+@pytest.mark.parametrize("case,expect", [
+    (dict(W=0), "null"),
+    (dict(out=0), "null"),
+    (dict(dt=5), "dtype"),
+    (dict(n=3, m=3), "pattern"),
+    (dict(n=0), "pattern"),
+    (dict(n=5), "pattern"),
+    (dict(m=16, n=2), "pattern"),
+    (dict(K=130), "shape"),
+    (dict(R=-1), "shape"),
+    (dict(W=FAKE + 8), "align"),
+    (dict(out=FAKE + 4), "align"),
+])
+def test_mask_compress_argument_errors(case, expect):
+    L = nm.lib()
+    a = dict(W=FAKE, dt=nm.NM_BF16, R=64, K=128, n=2, m=4, out=FAKE)
+    a.update(case)
+    code = L.nm_mask(a["W"], a["dt"], a["R"], a["K"], a["n"], a["m"], a["out"], None)
+    assert nm.STATUS[code] == expect
+    code = L.nm_compress(a["W"], a["dt"], a["R"], a["K"], a["n"], a["m"], a["out"], FAKE, None)
+    assert nm.STATUS[code] == expect
+    code = L.nm_decompress(a["W"], FAKE, a["dt"], a["R"], a["K"], a["n"], a["m"], a["out"], None)
+    assert nm.STATUS[code] == expect
+
+
+@needs_lib
+@pytest.mark.parametrize("case,expect", [
+    (dict(X=0), "null"),
+    (dict(meta=0), "null"),
+    (dict(y_dt=nm.NM_F16), "dtype"),   # bf16 in, fp16 out is not offered
+    (dict(dt=9), "dtype"),
+    (dict(T=-3), "shape"),
+    (dict(K=126), "shape"),
+    (dict(n=3, m=5), "pattern"),
+    (dict(Y=FAKE + 2), "align"),
+    (dict(meta=FAKE + 4), "align"),
+])
+def test_spmm_argument_errors(case, expect):
+    L = nm.lib()
+    a = dict(values=FAKE, meta=FAKE, R=64, K=128, n=2, m=4, X=FAKE, T=32, dt=nm.NM_BF16,
+             Y=FAKE, y_dt=nm.NM_BF16)
+    a.update(case)
+    code = L.nm_spmm(a["values"], a["meta"], a["R"], a["K"], a["n"], a["m"], a["X"], a["T"],
+                     a["dt"], a["Y"], a["y_dt"], None)
+    assert nm.STATUS[code] == expect
+
+
+@needs_lib
+def test_empty_arrays_may_be_null():
+    L = nm.lib()
+    assert L.nm_mask(None, nm.NM_BF16, 0, 128, 2, 4, None, None) == 0
+    assert L.nm_compress(None, nm.NM_F16, 16, 0, 2, 4, None, None, None) == 0
+    assert L.nm_spmm(FAKE, FAKE, 8, 128, 2, 4, FAKE, 0, nm.NM_BF16, None, nm.NM_BF16, None) == 0
+
+
+def test_product_path_does_not_load_the_oracle():
+    """Importing and using the binding never pulls in the CPU oracle."""
+    code = ("import sys, masking_sparse_gemm_amd as nm; "
+            "assert not any(k == 'oracle' or k.startswith('oracle.') for k in sys.modules); "
+            "print('clean')")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
+    assert out.returncode == 0 and "clean" in out.stdout, out.stderr
+
+
+def test_binding_has_no_cpu_fallback():
+    src = open(os.path.join(ROOT, "masking_sparse_gemm_amd", "__init__.py")).read()
+    assert "import oracle" not in src and "from oracle" not in src
+    for f in os.listdir(os.path.join(ROOT, "masking_sparse_gemm_amd", "csrc")):
+        text = open(os.path.join(ROOT, "masking_sparse_gemm_amd", "csrc", f)).read()
+        assert "nm_oracle" not in text and "nmo_" not in text, f
