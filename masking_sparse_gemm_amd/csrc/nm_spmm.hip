@@ -29,6 +29,8 @@
 // Every other pattern, fp32, and shapes the tiled kernel does not take (K not a
 // multiple of 128, T not a multiple of 8) use a plain LDS-tiled kernel that
 // expands the compressed rows to fp32 and accumulates with fp32 FMAs.
+#include <type_traits>
+
 #include "nm_device.h"
 #include "nm_launch.h"
 
@@ -76,121 +78,258 @@ __device__ __forceinline__ void store_from_f32(void* p, int64_t i, float v) {
 // ===========================================================================
 // Structured-sparse matrix-core kernel (2:4, or 1:2 widened to 2:4).
 // ===========================================================================
-constexpr int kKStep = 128;  // K per main-loop step (two smfmac instructions)
+constexpr int kKStep = 64;  // K per pipeline step: one smfmac per fragment pair
 
-template <int BM, int BN, int WAVES_M, int WAVES_N>
+// STAGES: LDS ring depth (the step being computed + STAGES - 1 in flight)
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
 struct SmfmacTile {
+  static constexpr int kStages = STAGES;
   static constexpr int kThreads = 64 * WAVES_M * WAVES_N;
+  static constexpr int kWaves = WAVES_M * WAVES_N;
   static constexpr int kWM = BM / WAVES_M;
   static constexpr int kWN = BN / WAVES_N;
   static constexpr int kFM = kWM / 16;
   static constexpr int kFN = kWN / 16;
-  static constexpr int kLdsStride = BN + 8;  // halves per LDS row (16-byte pad)
-  static constexpr int kLdsStage = kKStep * kLdsStride;
-  static constexpr int kXChunks = kKStep * BN / 8 / kThreads;  // 16-byte X loads per thread
+  // one stage of the LDS ring: X tile (64 K rows x BN), A values (BM rows x 64 bytes),
+  // metadata (BM rows x 8 bytes: four 16-bit 2:4 units, or 1:2 bytes in the first half)
+  static constexpr int kXRowBytes = BN * 2;
+  static constexpr int kXChunks = BN / 8;
+  static constexpr int kXBytes = kKStep * kXRowBytes;
+  static constexpr int kABytes = BM * 64;
+  static constexpr int kMBytes = BM * 8;
+  static constexpr int kStageBytes = kXBytes + kABytes + kMBytes;
+  // direct loads per wave and step (each moves 1 KB; metadata ones move 256 bytes)
+  static constexpr int kXLoads = kXBytes / 1024 / kWaves;
+  static constexpr int kALoads = kABytes / 1024 / kWaves;
+  static constexpr int kMLoads = kMBytes / 256 / kWaves;
+  static constexpr int kLoads = kXLoads + kALoads + kMLoads;
   static_assert(kWM % 16 == 0 && kWN % 16 == 0, "wave tile must be whole 16x16 fragments");
-  static_assert((kKStep * BN / 8) % kThreads == 0, "X tile must split evenly over threads");
+  static_assert(kXBytes % (1024 * kWaves) == 0 && kABytes % (1024 * kWaves) == 0 &&
+                    kMBytes % (256 * kWaves) == 0,
+                "every wave issues the same number of direct loads per step");
+  static_assert(kXChunks >= 16, "the X swizzle needs at least 16 chunks per row");
+  static_assert(kFM % 4 == 0, "A fragments are read four at a time");
+  static_assert(kStages >= 2 && (kStages - 2) * kLoads <= 63, "vmcnt budget");
+  static_assert(kStages * kStageBytes <= 160 * 1024, "LDS budget");
 };
 
-// 1:2 metadata bits (one per value) of 32 K positions -> eight 2:4 nibbles.
-__device__ __forceinline__ uint32_t widen_1_2(uint32_t x16) {
-  uint32_t x = x16 & 0xFFFFu;  // bit i -> bit 2i
-  x = (x | (x << 8)) & 0x00FF00FFu;
-  x = (x | (x << 4)) & 0x0F0F0F0Fu;
-  x = (x | (x << 2)) & 0x33333333u;
-  x = (x | (x << 1)) & 0x55555555u;
-  return x | 0x88888888u;  // second value of each pair sits in the upper half (2 + bit)
+// 1:2 metadata bits (one per value) of 16 K positions -> four 2:4 nibbles.
+__device__ __forceinline__ uint32_t widen_1_2(uint32_t x8) {
+  uint32_t x = x8 & 0xFFu;  // bit i -> bit 2i
+  x = (x | (x << 4)) & 0x0F0Fu;
+  x = (x | (x << 2)) & 0x3333u;
+  x = (x | (x << 1)) & 0x5555u;
+  return x | 0x8888u;  // the second value of each pair sits in the upper half (2 + bit)
 }
 
 template <bool BF16>
-__device__ __forceinline__ float4_t smfmac(const uint4& a, const short16_t& b, const float4_t& c,
-                                           uint32_t idx, int half) {
+__device__ __forceinline__ float4_t smfmac(const u32x4_t& a, const short16_t& b, const float4_t& c,
+                                           uint32_t idx) {
   if constexpr (BF16) {
-    const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
-    const bf16x16_t bv = __builtin_bit_cast(bf16x16_t, b);
-    return half == 0 ? __builtin_amdgcn_smfmac_f32_16x16x64_bf16(av, bv, c, (int)idx, 0, 0)
-                     : __builtin_amdgcn_smfmac_f32_16x16x64_bf16(av, bv, c, (int)idx, 0, 1);
+    return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                     __builtin_bit_cast(bf16x16_t, b), c,
+                                                     (int)idx, 0, 0);
   } else {
-    const f16x8_t av = __builtin_bit_cast(f16x8_t, a);
-    const f16x16_t bv = __builtin_bit_cast(f16x16_t, b);
-    return half == 0 ? __builtin_amdgcn_smfmac_f32_16x16x64_f16(av, bv, c, (int)idx, 0, 0)
-                     : __builtin_amdgcn_smfmac_f32_16x16x64_f16(av, bv, c, (int)idx, 0, 1);
+    return __builtin_amdgcn_smfmac_f32_16x16x64_f16(__builtin_bit_cast(f16x8_t, a),
+                                                    __builtin_bit_cast(f16x16_t, b), c, (int)idx,
+                                                    0, 0);
   }
 }
 
-__device__ __forceinline__ short4_t lds_tr_read(const uint16_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(p));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Direct global -> LDS loads (global_load_lds_dword / _dwordx4): lane l of the wave
+// writes its bytes at lds_wave_base + size * l.  The builtin is device-only; keeping it
+// out of the host pass keeps the host-side launch stubs of the kernels that use it.
+template <int kSize>
+__device__ __forceinline__ void global_to_lds(const void* src, uint8_t* lds_wave_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  static_assert(kSize == 4 || kSize == 16, "dword or dwordx4");
+  if constexpr (kSize == 16)
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_wave_base, 16, 0, 0);
+  else
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_wave_base, 4, 0, 0);
+#endif
 }
 
-template <bool BF16, bool kPat12, int YT, int BM, int BN, int WAVES_M, int WAVES_N>
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)(p);
+}
+
+// All LDS reads go through asm blocks that also wait for them: the compiler then sees no
+// LDS read that might alias the in-flight direct loads (it would answer with a wait for
+// every outstanding load), and no register that a pending load might still write.
+
+// One B fragment (16 K rows x 16 columns, K-major per lane): four transposing reads at
+// rows kb, kb + 4 (addresses a0, a1) and kb + 32, kb + 36 (the same + kFar bytes).
+template <int kFar>
+__device__ __forceinline__ short16_t lds_b_fragment(uint32_t a0, uint32_t a1) {
+  short4_t b0, b1, b2, b3;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %5\n\t"
+      "ds_read_b64_tr_b16 %2, %4 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %3, %5 offset:%6\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3)
+      : "v"(a0), "v"(a1), "n"(kFar)
+      : "memory");
+  const short8_t lo = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+  const short8_t hi = __builtin_shufflevector(b2, b3, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+}
+
+// Four A fragments (16 bytes each, 1 KB apart) and their metadata (128 bytes apart).
+// kPat12 reads one byte of 1:2 metadata, otherwise a 16-bit 2:4 unit.
+template <bool kPat12>
+__device__ __forceinline__ void lds_a_fragments4(uint32_t va, uint32_t ma, u32x4_t& a0,
+                                                 u32x4_t& a1, u32x4_t& a2, u32x4_t& a3,
+                                                 uint32_t& m0, uint32_t& m1, uint32_t& m2,
+                                                 uint32_t& m3) {
+  if constexpr (kPat12) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:1024\n\t"
+        "ds_read_b128 %2, %8 offset:2048\n\t"
+        "ds_read_b128 %3, %8 offset:3072\n\t"
+        "ds_read_u8 %4, %9\n\t"
+        "ds_read_u8 %5, %9 offset:128\n\t"
+        "ds_read_u8 %6, %9 offset:256\n\t"
+        "ds_read_u8 %7, %9 offset:384\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(m0), "=&v"(m1), "=&v"(m2), "=&v"(m3)
+        : "v"(va), "v"(ma)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:1024\n\t"
+        "ds_read_b128 %2, %8 offset:2048\n\t"
+        "ds_read_b128 %3, %8 offset:3072\n\t"
+        "ds_read_u16 %4, %9\n\t"
+        "ds_read_u16 %5, %9 offset:128\n\t"
+        "ds_read_u16 %6, %9 offset:256\n\t"
+        "ds_read_u16 %7, %9 offset:384\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(m0), "=&v"(m1), "=&v"(m2), "=&v"(m3)
+        : "v"(va), "v"(ma)
+        : "memory");
+  }
+}
+
+// Wait until at most N direct loads of this wave are outstanding, then meet the other
+// waves: the step whose loads completed is then visible in LDS for every wave.
+template <int N>
+__device__ __forceinline__ void wait_loads_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Pipeline: K steps of 64 through a ring of kStages LDS stages, every operand brought in
+// by direct global -> LDS loads issued kStages - 1 steps ahead (loads for steps past
+// the end re-read the last step, so every step issues the same loads and the loop has no
+// branches).  Per step each wave reads its A fragments and metadata once, then for each
+// 16-column B fragment issues FM smfmac.
+//
+// LDS layouts within a stage (all conflict-free for the reads that follow):
+//   X: K row r holds BN columns as 16-byte chunks, logical chunk c at physical chunk
+//      c ^ (r & 15); a direct load of 1 KB fills 1024 / (2 BN) consecutive rows.
+//   A: tile row i holds the 64 value bytes of this step (K/2 values per row of W in
+//      global memory, 32 per step); 16-byte chunk c at physical chunk c ^ ((i >> 2) & 3).
+//      One direct load fills rows 16 j .. 16 j + 15: exactly one fragment's rows.
+//   meta: tile row i holds 8 bytes (2:4: four 16-bit units; 1:2: four bytes + pad).
+template <bool BF16, bool kPat12, int YT, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
     smfmac_spmm_kernel(const uint16_t* __restrict__ values, const uint32_t* __restrict__ meta,
                        const uint16_t* __restrict__ X, void* __restrict__ Y, int R, int K, int T,
                        int tiles_n) {
-  using TL = SmfmacTile<BM, BN, WAVES_M, WAVES_N>;
-  constexpr int FM = TL::kFM, FN = TL::kFN, NT = TL::kThreads;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2 * TL::kLdsStage];
+  using TL = SmfmacTile<BM, BN, WAVES_M, WAVES_N, STAGES>;
+  constexpr int FM = TL::kFM, FN = TL::kFN, kStages = STAGES;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int tile_m = blockIdx.x / tiles_n, tile_n = blockIdx.x % tiles_n;
   const int m0 = tile_m * BM, t0 = tile_n * BN;
   const int l16 = lane & 15, q = lane >> 4;
+  const int nsteps = K / kKStep;
+  const int last_step = nsteps - 1;
 
-  const int64_t vals_per_row = K / 2;
-  // metadata words per row: 2:4 -> K/32, 1:2 -> K/64
-  const int64_t meta_per_row = kPat12 ? K / 64 : K / 32;
-
-  // ---- per-lane A pointers (one row per fragment; rows past R are clamped) ----
-  const uint16_t* a_ptr[FM];
-  const uint32_t* m_ptr[FM];
+  // ---- direct-load sources (byte offsets for step 0) and LDS destinations ----
+  const uint8_t* xg = reinterpret_cast<const uint8_t*>(X);
+  const uint8_t* vg = reinterpret_cast<const uint8_t*>(values);
+  const uint8_t* mg = reinterpret_cast<const uint8_t*>(meta);
+  const int64_t meta_row_bytes = K / (kPat12 ? 16 : 8);
+  int64_t x_src[TL::kXLoads];
+  uint32_t x_dst[TL::kXLoads];
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
-    int row = m0 + wm * TL::kWM + fm * 16 + l16;
-    row = row < R ? row : R - 1;
-    a_ptr[fm] = values + (int64_t)row * vals_per_row + 16 * q;
-    m_ptr[fm] = meta + (int64_t)row * meta_per_row + (kPat12 ? (q >> 1) : q);
+  for (int j = 0; j < TL::kXLoads; ++j) {
+    const int w1k = j * TL::kWaves + wave;  // 1 KB window of the X tile
+    const int slot = w1k * 64 + lane;       // 16-byte slot
+    const int r = slot / TL::kXChunks, pc = slot % TL::kXChunks;
+    const int lc = pc ^ (r & 15);
+    int col = t0 + 8 * lc;
+    col = col < T ? col : 0;  // columns past T: any valid address (outputs past T only)
+    x_src[j] = ((int64_t)r * T + col) * 2;
+    x_dst[j] = (uint32_t)(w1k * 1024);
   }
+  int64_t a_src[TL::kALoads];
+  uint32_t a_dst[TL::kALoads];
+#pragma unroll
+  for (int j = 0; j < TL::kALoads; ++j) {
+    const int blk = j * TL::kWaves + wave;  // rows 16 blk .. 16 blk + 15 of the tile
+    const int i = 16 * blk + (lane >> 2), pc = lane & 3;
+    const int lc = pc ^ ((i >> 2) & 3);
+    int row = m0 + i;
+    row = row < R ? row : R - 1;  // rows past R: any valid row (their outputs are dropped)
+    a_src[j] = (int64_t)row * K + 16 * lc;
+    a_dst[j] = (uint32_t)(TL::kXBytes + blk * 1024);
+  }
+  int64_t m_src[TL::kMLoads];
+  uint32_t m_dst[TL::kMLoads];
+#pragma unroll
+  for (int j = 0; j < TL::kMLoads; ++j) {
+    const int blk = j * TL::kWaves + wave;  // rows 32 blk .. 32 blk + 31
+    const int i = 32 * blk + (lane >> 1);
+    int row = m0 + i;
+    row = row < R ? row : R - 1;
+    // 1:2 rows carry 4 bytes per step: the second half-lane reads the same word
+    m_src[j] = (int64_t)row * meta_row_bytes + (kPat12 ? 0 : 4 * (lane & 1));
+    m_dst[j] = (uint32_t)(TL::kXBytes + TL::kABytes + blk * 256);
+  }
+  auto issue_step = [&](int step) {
+    step = step < last_step ? step : last_step;
+    uint8_t* st = smem + (step % kStages) * TL::kStageBytes;
+    const int64_t kx = (int64_t)step * kKStep * T * 2;    // X rows
+    const int64_t ka = (int64_t)step * 64;                // A value bytes
+    const int64_t km = (int64_t)step * (kPat12 ? 4 : 8);  // metadata bytes
+#pragma unroll
+    for (int j = 0; j < TL::kXLoads; ++j) global_to_lds<16>(xg + x_src[j] + kx, st + x_dst[j]);
+#pragma unroll
+    for (int j = 0; j < TL::kALoads; ++j) global_to_lds<16>(vg + a_src[j] + ka, st + a_dst[j]);
+#pragma unroll
+    for (int j = 0; j < TL::kMLoads; ++j) global_to_lds<4>(mg + m_src[j] + km, st + m_dst[j]);
+  };
 
-  // ---- X tile loader: chunk c -> (row c / (BN/8), 8 columns at 8*(c % (BN/8))) ----
-  uint4 xr[TL::kXChunks];
-  auto load_x = [&](int k0) {
+  // ---- per-lane LDS read offsets within a stage ----
+  // A fragment fm: tile row i = wm*kWM + 16 fm + l16, logical chunk q
+  const int ia = wm * TL::kWM + l16;
+  const uint32_t a_rd = (uint32_t)(TL::kXBytes + ia * 64 + ((q ^ ((ia >> 2) & 3)) << 4));
+  const uint32_t m_rd = (uint32_t)(TL::kXBytes + TL::kABytes + ia * 8 + (kPat12 ? q : 2 * q));
+  // B fragment fn: K rows {8q..8q+7} and {32+8q..32+8q+7}; lane i of a 16-lane block
+  // reads K row kb + (i >> 2), logical columns 4 (i & 3) .. +3
+  const int sw0 = 8 * (q & 1) | (l16 >> 2);  // (row & 15) for kb = 8q and 8q + 32
+  const int sw1 = sw0 | 4;                   // (row & 15) for kb = 8q + 4 and 8q + 36
+  const int rb = 8 * q + (l16 >> 2);
+  const int half8 = 8 * (l16 & 1);
+  uint32_t b_rd[FN][2];
 #pragma unroll
-    for (int i = 0; i < TL::kXChunks; ++i) {
-      const int c = tid + i * NT;
-      const int r = c / (BN / 8), col = t0 + 8 * (c % (BN / 8));
-      if (col < T)
-        xr[i] = *reinterpret_cast<const uint4*>(X + (int64_t)(k0 + r) * T + col);
-      else
-        xr[i] = make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto store_x = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < TL::kXChunks; ++i) {
-      const int c = tid + i * NT;
-      const int r = c / (BN / 8), col = 8 * (c % (BN / 8));
-      *reinterpret_cast<uint4*>(&xs[buf * TL::kLdsStage + r * TL::kLdsStride + col]) = xr[i];
-    }
-  };
-
-  uint4 a_cur[FM][2], a_nxt[FM][2];
-  uint32_t i_cur[FM], i_nxt[FM];
-  auto load_a = [&](int k0, uint4 (&a)[FM][2], uint32_t (&ix)[FM]) {
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      const uint4* p = reinterpret_cast<const uint4*>(a_ptr[fm] + k0 / 2);
-      a[fm][0] = p[0];
-      a[fm][1] = p[1];
-      if constexpr (kPat12) {
-        const uint32_t w = m_ptr[fm][k0 / 64];
-        ix[fm] = widen_1_2(w >> (16 * (q & 1)));
-      } else {
-        ix[fm] = m_ptr[fm][k0 / 32];
-      }
-    }
-  };
+  for (int fn = 0; fn < FN; ++fn) {
+    const int lc = (wn * TL::kWN + fn * 16) / 8 + ((l16 & 3) >> 1);
+    b_rd[fn][0] = (uint32_t)(rb * TL::kXRowBytes + ((lc ^ sw0) << 4) + half8);
+    b_rd[fn][1] = (uint32_t)((rb + 4) * TL::kXRowBytes + ((lc ^ sw1) << 4) + half8);
+  }
 
   float4_t acc[FM][FN];
 #pragma unroll
@@ -198,55 +337,43 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int nsteps = K / kKStep;
-  load_x(0);
-  load_a(0, a_cur, i_cur);
-  store_x(0);
-  __syncthreads();
+  // ---- prologue: steps 0 .. kStages-2 in flight ----
+#pragma unroll
+  for (int k = 0; k < kStages - 1; ++k) issue_step(k);
 
-  // LDS read offsets of this lane for the transposing loads (see the layout note above):
-  // lane i' of a 16-lane block reads row kb + (i' >> 2), columns 4 * (i' & 3) .. +3.
-  const int tr_row = l16 >> 2, tr_col = 4 * (l16 & 3);
-
+  const uint32_t smem_base = lds_addr(smem);
   for (int s = 0; s < nsteps; ++s) {
-    const int cur = s & 1;
-    const bool more = s + 1 < nsteps;
-    if (more) {
-      load_x((s + 1) * kKStep);
-      load_a((s + 1) * kKStep, a_nxt, i_nxt);
+    // step s landed (steps s+1 .. s+kStages-2 may still be in flight); after the barrier
+    // no wave reads stage (s-1) % kStages any more, which the next issue overwrites
+    wait_loads_and_barrier<(kStages - 2) * TL::kLoads>();
+    issue_step(s + kStages - 1);
+    const uint32_t st = smem_base + (uint32_t)((s % kStages) * TL::kStageBytes);
+
+    u32x4_t a[FM];
+    uint32_t ix[FM];
+#pragma unroll
+    for (int f = 0; f < FM; f += 4)
+      lds_a_fragments4<kPat12>(st + a_rd + f * 1024, st + m_rd + f * 128, a[f], a[f + 1],
+                               a[f + 2], a[f + 3], ix[f], ix[f + 1], ix[f + 2], ix[f + 3]);
+    if constexpr (kPat12) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) ix[fm] = widen_1_2(ix[fm]);
     }
-    const uint16_t* xb = xs + cur * TL::kLdsStage;
+    short16_t b = lds_b_fragment<32 * TL::kXRowBytes>(st + b_rd[0][0], st + b_rd[0][1]);
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      // K rows (within the step) holding B elements 0..7 and 8..15 of lane group q
-      const int kb0 = 32 * (q >> 1) + 16 * half + 8 * (q & 1);
+    for (int fn = 0; fn < FN; ++fn) {
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const uint16_t* base = xb + tr_row * TL::kLdsStride + wn * TL::kWN + fn * 16 + tr_col;
-        const short4_t b0 = lds_tr_read(base + (kb0 + 0) * TL::kLdsStride);
-        const short4_t b1 = lds_tr_read(base + (kb0 + 4) * TL::kLdsStride);
-        const short4_t b2 = lds_tr_read(base + (kb0 + 64) * TL::kLdsStride);
-        const short4_t b3 = lds_tr_read(base + (kb0 + 68) * TL::kLdsStride);
-        const short8_t lo = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
-        const short8_t hi = __builtin_shufflevector(b2, b3, 0, 1, 2, 3, 4, 5, 6, 7);
-        const short16_t bfrag =
-            __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
-          acc[fm][fn] = smfmac<BF16>(a_cur[fm][half], bfrag, acc[fm][fn], i_cur[fm], half);
+      for (int fm = 0; fm < FM; ++fm) acc[fm][fn] = smfmac<BF16>(a[fm], b, acc[fm][fn], ix[fm]);
+      if (fn + 1 < FN) {
+        // the smfmacs above are queued before the next fragment's reads are issued, so
+        // the matrix cores work through them while this wave waits for LDS
+        __builtin_amdgcn_sched_barrier(0);
+        b = lds_b_fragment<32 * TL::kXRowBytes>(st + b_rd[fn + 1][0], st + b_rd[fn + 1][1]);
       }
     }
-    if (more) {
-      store_x(cur ^ 1);
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm) {
-        a_cur[fm][0] = a_nxt[fm][0];
-        a_cur[fm][1] = a_nxt[fm][1];
-        i_cur[fm] = i_nxt[fm];
-      }
-    }
-    __syncthreads();
   }
+  // drain the loads issued for steps past the end before the wave exits
+  wait_loads_and_barrier<0>();
 
   // ---- epilogue: lane holds rows 4q..4q+3, column l16 of each 16x16 fragment ----
 #pragma unroll
@@ -365,19 +492,28 @@ hipError_t run_generic(const void* values, const uint32_t* meta, int64_t R, int6
   return hipErrorInvalidValue;
 }
 
-// Tile configuration of the matrix-core kernel.
-constexpr int kBM = 128, kBN = 128, kWavesM = 2, kWavesN = 2;
+// Tile configurations of the matrix-core kernel, and the choice between them.
+template <bool BF16, bool kPat12, int YT, int BM, int BN, int WM_, int WN_, int ST_>
+hipError_t launch_tile(const void* values, const uint32_t* meta, int64_t R, int64_t K,
+                       const void* X, int64_t T, void* Y, hipStream_t s) {
+  using TL = SmfmacTile<BM, BN, WM_, WN_, ST_>;
+  const int tiles_m = (int)((R + BM - 1) / BM), tiles_n = (int)((T + BN - 1) / BN);
+  auto kernel = smfmac_spmm_kernel<BF16, kPat12, YT, BM, BN, WM_, WN_, ST_>;
+  const size_t lds = (size_t)ST_ * TL::kStageBytes;
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
+  kernel<<<tiles_m * tiles_n, TL::kThreads, lds, s>>>(
+      static_cast<const uint16_t*>(values), meta, static_cast<const uint16_t*>(X), Y, (int)R,
+      (int)K, (int)T, tiles_n);
+  return hipGetLastError();
+}
 
 template <bool BF16, bool kPat12, int YT>
 hipError_t run_smfmac(const void* values, const uint32_t* meta, int64_t R, int64_t K,
                       const void* X, int64_t T, void* Y, hipStream_t s) {
-  using TL = SmfmacTile<kBM, kBN, kWavesM, kWavesN>;
-  const int tiles_m = (int)((R + kBM - 1) / kBM), tiles_n = (int)((T + kBN - 1) / kBN);
-  smfmac_spmm_kernel<BF16, kPat12, YT, kBM, kBN, kWavesM, kWavesN>
-      <<<tiles_m * tiles_n, TL::kThreads, 0, s>>>(
-          static_cast<const uint16_t*>(values), meta, static_cast<const uint16_t*>(X), Y, (int)R,
-          (int)K, (int)T, tiles_n);
-  return hipGetLastError();
+  return launch_tile<BF16, kPat12, YT, 256, 128, 2, 2, 4>(values, meta, R, K, X, T, Y, s);
 }
 
 }  // namespace
@@ -386,6 +522,7 @@ hipError_t launch_spmm(const void* values, const uint32_t* meta, int64_t R, int6
                        int m, const void* X, int64_t T, int dt, void* Y, int y_dt, hipStream_t s) {
   if (R == 0 || T == 0) return hipSuccess;
   const bool pat24 = (n == 2 && m == 4), pat12 = (n == 1 && m == 2);
+  // the matrix-core kernel addresses A, its metadata and X with 32-bit byte offsets
   const bool tiled_shape = K > 0 && K % kKStep == 0 && T % 8 == 0 && R < (1 << 30) &&
                            T < (1 << 30) && K < (1 << 30);
   if (dt != kF32 && (pat24 || pat12) && tiled_shape) {

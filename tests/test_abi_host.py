@@ -37,6 +37,16 @@ def test_library_exports_every_declared_symbol():
 
 
 @needs_lib
+def test_library_has_no_undefined_symbols_of_its_own():
+    """Every kernel launch stub and internal function is defined inside libnm.so."""
+    out = subprocess.run(["nm", "-D", "--undefined-only", nm.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    names = [l.split()[-1] for l in out.splitlines() if l.strip()]
+    own = [s for s in names if s.startswith(("_ZN2nm", "nm_")) or "device_stub" in s]
+    assert not own, own
+
+
+@needs_lib
 def test_status_strings():
     for code in range(8):
         s = nm.status_str(code)
