@@ -16,6 +16,7 @@ CPU oracle timed on the host are reported alongside.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -57,6 +58,24 @@ def algorithmic_bytes(R, K, T, n, m, s):
         "decompress": kept * s + meta + e * s,
         "spmm": kept * s + meta + K * T * s + R * T * s,
     }
+
+
+def profiled_traffic(workload: str):
+    """HBM bytes per nm_spmm dispatch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary (already scaled by the copy-kernel calibration), or None when that summary is
+    missing or was taken on a different version of the kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
+    src = os.path.join(ROOT, "masking_sparse_gemm_amd", "csrc", "nm_spmm.hip")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        prof = json.load(f)
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != prof.get("nm_spmm_hip_sha256"):
+            return None
+    per = [v["read_bytes"] + v["write_bytes"] for k, v in prof["per_dispatch_bytes"].items()
+           if k.startswith("smfmac_spmm_kernel")]
+    return sum(per) / len(per) if per else None
 
 
 def cpu_baseline(mats, n, m, threads: int, budget_s: float = 12.0):
@@ -115,6 +134,9 @@ def main() -> int:
     ap.add_argument("--workload", default="llama_mlp", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense GEMM baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one 512 MiB device-to-device copy (a kernel of known traffic "
+                         "for scaling FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -155,6 +177,13 @@ def main() -> int:
         d["Y"] = torch.empty((w.R, w.T), dtype=tdt, device=dev)
         mats.append(d)
     dtype = mats[0]["dtype"]
+    if args.copy_calibration:
+        src = torch.empty(1 << 29, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     L = nm.lib()
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
@@ -239,7 +268,14 @@ def main() -> int:
     roofline = {"bound": "mfma", "kernel": "nm_spmm (smfmac 16x16x64)" if n * 2 == m else "nm_spmm",
                 "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": None,
-                "note": "achieved = algorithmic flops 2*R*(K*N/M)*T per launch / mean launch time"}
+                "alg_bytes_per_launch": sum(algorithmic_bytes(d["R"], d["K"], d["T"], n, m,
+                                                              d["s"])["spmm"] for d in mats) / len(mats),
+                "note": "achieved = algorithmic flops 2*R*(K*N/M)*T per launch / mean launch time; "
+                        "traffic = profiled HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, "
+                        "calibrated on a copy kernel)"}
+    traffic = profiled_traffic(args.workload)
+    if traffic is not None:
+        roofline["traffic"] = round(traffic)
 
     mc_bytes = tot["mask"][1] + tot["compress"][1]
     mc_time = tot["mask"][0] + tot["compress"][0]

@@ -29,6 +29,8 @@
 // Every other pattern, fp32, and shapes the tiled kernel does not take (K not a
 // multiple of 128, T not a multiple of 8) use a plain LDS-tiled kernel that
 // expands the compressed rows to fp32 and accumulates with fp32 FMAs.
+#include <atomic>
+#include <cstdlib>
 #include <type_traits>
 
 #include "nm_device.h"
@@ -224,6 +226,30 @@ __device__ __forceinline__ void wait_loads_and_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// Which output tile a workgroup computes.  Workgroups are dispatched round-robin over
+// the XCDs (each with its own L2), so workgroup b runs on XCD b % xcds.  Each XCD gets
+// a contiguous run of `per_xcd` tiles of an order that walks groups of gm x gn tiles
+// (row tiles x column tiles; column-major inside a group): the workgroups an XCD runs
+// at the same time then cover a compact block of the output and share both their rows
+// of A and their columns of X in that XCD's L2.
+struct TileMap {
+  int tiles_m, tiles_n, xcds, per_xcd, gm, gn;
+  __device__ __forceinline__ bool tile_of(int b, int& tm, int& tn) const {
+    const int t = (b % xcds) * per_xcd + b / xcds;
+    if (t >= tiles_m * tiles_n) return false;
+    // row-groups of gm row tiles (the last may be shorter), every earlier one full
+    const int g_m = t / (gm * tiles_n);
+    const int rows = min(gm, tiles_m - g_m * gm);
+    const int u = t - g_m * gm * tiles_n;
+    // inside it, column-groups of gn column tiles (the last may be narrower)
+    const int g_n = u / (rows * gn);
+    const int v = u - g_n * rows * gn;
+    tm = g_m * gm + v % rows;
+    tn = g_n * gn + v / rows;
+    return true;
+  }
+};
+
 // Pipeline: K steps of 64 through a ring of kStages LDS stages, every operand brought in
 // by direct global -> LDS loads issued kStages - 1 steps ahead (loads for steps past
 // the end re-read the last step, so every step issues the same loads and the loop has no
@@ -241,16 +267,17 @@ template <bool BF16, bool kPat12, int YT, int BM, int BN, int WAVES_M, int WAVES
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
     smfmac_spmm_kernel(const uint16_t* __restrict__ values, const uint32_t* __restrict__ meta,
                        const uint16_t* __restrict__ X, void* __restrict__ Y, int R, int K, int T,
-                       int tiles_n) {
+                       TileMap map) {
   using TL = SmfmacTile<BM, BN, WAVES_M, WAVES_N, STAGES>;
   constexpr int FM = TL::kFM, FN = TL::kFN, kStages = STAGES;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
+  int tile_m, tile_n;
+  if (!map.tile_of(blockIdx.x, tile_m, tile_n)) return;  // whole workgroup, before any load
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  const int tile_m = blockIdx.x / tiles_n, tile_n = blockIdx.x % tiles_n;
   const int m0 = tile_m * BM, t0 = tile_n * BN;
   const int l16 = lane & 15, q = lane >> 4;
   const int nsteps = K / kKStep;
@@ -492,6 +519,23 @@ hipError_t run_generic(const void* values, const uint32_t* meta, int64_t R, int6
   return hipErrorInvalidValue;
 }
 
+// XCDs of the current device: MI355X (gfx950) has 8, with 32 compute units each.
+// Looked up once per device.
+int xcd_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 1;
+    v = cus % 8 == 0 ? 8 : 1;
+    cached[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
 // Tile configurations of the matrix-core kernel, and the choice between them.
 template <bool BF16, bool kPat12, int YT, int BM, int BN, int WM_, int WN_, int ST_>
 hipError_t launch_tile(const void* values, const uint32_t* meta, int64_t R, int64_t K,
@@ -504,16 +548,58 @@ hipError_t launch_tile(const void* values, const uint32_t* meta, int64_t R, int6
       hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
-  kernel<<<tiles_m * tiles_n, TL::kThreads, lds, s>>>(
+  TileMap map;
+  map.tiles_m = tiles_m;
+  map.tiles_n = tiles_n;
+  map.xcds = xcd_count();
+  map.per_xcd = (tiles_m * tiles_n + map.xcds - 1) / map.xcds;
+  map.gn = tiles_n < 4 ? tiles_n : 4;
+  map.gm = 32 / map.gn;
+  kernel<<<map.xcds * map.per_xcd, TL::kThreads, lds, s>>>(
       static_cast<const uint16_t*>(values), meta, static_cast<const uint16_t*>(X), Y, (int)R,
-      (int)K, (int)T, tiles_n);
+      (int)K, (int)T, map);
   return hipGetLastError();
+}
+
+// Three tile shapes; the launch picks the one with the smallest estimated time: waves of
+// workgroups over the device (ceil(tiles / CUs)) times the tile's work divided by the
+// rate that shape sustains on long K loops (measured on MI355X, effective TFLOP/s).
+struct TileChoice {
+  int bm, bn;
+  double rate;
+};
+constexpr TileChoice kTiles[3] = {{256, 256, 1300.0}, {256, 128, 1030.0}, {128, 128, 800.0}};
+
+int pick_tile(int64_t R, int64_t T) {
+  // NM_SPMM_TILE=0/1/2 pins one shape (used by the tests to cover every shape)
+  if (const char* e = getenv("NM_SPMM_TILE")) {
+    if (e[0] >= '0' && e[0] <= '2' && e[1] == 0) return e[0] - '0';
+  }
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (cus <= 0) cus = 256;
+  int best = 0;
+  double best_t = 0;
+  for (int i = 0; i < 3; ++i) {
+    const int64_t tiles = ((R + kTiles[i].bm - 1) / kTiles[i].bm) * ((T + kTiles[i].bn - 1) / kTiles[i].bn);
+    const double t = (double)((tiles + cus - 1) / cus) * kTiles[i].bm * kTiles[i].bn / kTiles[i].rate;
+    if (i == 0 || t < best_t) {
+      best = i;
+      best_t = t;
+    }
+  }
+  return best;
 }
 
 template <bool BF16, bool kPat12, int YT>
 hipError_t run_smfmac(const void* values, const uint32_t* meta, int64_t R, int64_t K,
                       const void* X, int64_t T, void* Y, hipStream_t s) {
-  return launch_tile<BF16, kPat12, YT, 256, 128, 2, 2, 4>(values, meta, R, K, X, T, Y, s);
+  switch (pick_tile(R, T)) {
+    case 0: return launch_tile<BF16, kPat12, YT, 256, 256, 2, 4, 3>(values, meta, R, K, X, T, Y, s);
+    case 1: return launch_tile<BF16, kPat12, YT, 256, 128, 4, 2, 4>(values, meta, R, K, X, T, Y, s);
+    default: return launch_tile<BF16, kPat12, YT, 128, 128, 2, 2, 4>(values, meta, R, K, X, T, Y, s);
+  }
 }
 
 }  // namespace

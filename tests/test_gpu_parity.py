@@ -169,8 +169,8 @@ def test_select_empty():
 # sparse x dense product
 # ---------------------------------------------------------------------------
 
-# (R, K, T): several 128 x 128 tiles with ragged row and column tails; K multiples of
-# 128 take the matrix-core kernel, the others the generic one.
+# (R, K, T): several tiles with ragged row and column tails; 2:4 and 1:2 with K a multiple
+# of 64 and T of 8 take the matrix-core kernel, everything else the generic one.
 PRODUCT_SHAPES = [(200, 384, 264), (130, 256, 136), (16, 128, 8), (257, 128, 520), (64, 96, 40),
                   (33, 40, 13)]
 
@@ -190,6 +190,21 @@ def test_spmm_elementwise(dtype, n, m, yf32):
         Y = nm.spmm(vals, meta, dev(X, dtype), n, m, out_dtype=TORCH_DT[y_dtype])
         y_ref, s = reference_product(vals_o, meta_o, R, K, n, m, X, dtype)
         check_product(Y, y_ref, s, K // m * n, dtype, y_dtype, f"{R}x{K}x{T} {n}:{m}")
+
+
+@pytest.mark.parametrize("tile", ["0", "1", "2"])
+@pytest.mark.parametrize("dtype,n,m", [("bf16", 2, 4), ("f16", 1, 2)])
+def test_spmm_every_tile_shape(tile, dtype, n, m, monkeypatch):
+    """Each matrix-core tile shape, pinned, on shapes with ragged row and column tiles."""
+    monkeypatch.setenv("NM_SPMM_TILE", tile)
+    rng = np.random.default_rng(61)
+    for R, K, T in [(300, 192, 264), (520, 128, 136), (16, 64, 8)]:
+        W = encode(rng.standard_normal((R, K)), dtype)
+        X = encode(rng.standard_normal((K, T)), dtype)
+        vals, meta, vals_o, meta_o = check_select(W, dtype, n, m)
+        Y = nm.spmm(vals, meta, dev(X, dtype), n, m, out_dtype=torch.float32)
+        y_ref, s = reference_product(vals_o, meta_o, R, K, n, m, X, dtype)
+        check_product(Y, y_ref, s, K // m * n, dtype, "f32", f"tile {tile} {R}x{K}x{T}")
 
 
 @pytest.mark.parametrize("n,m", [(2, 4), (1, 2), (4, 8), (1, 4)])
