@@ -74,7 +74,7 @@ def profiled_traffic(workload: str):
         if hashlib.sha256(f.read()).hexdigest() != prof.get("nm_spmm_hip_sha256"):
             return None
     per = [v["read_bytes"] + v["write_bytes"] for k, v in prof["per_dispatch_bytes"].items()
-           if k.startswith("smfmac_spmm_kernel")]
+           if "spmm_kernel" in k]
     return sum(per) / len(per) if per else None
 
 
@@ -132,6 +132,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama_mlp", choices=sorted(WORKLOADS))
+    ap.add_argument("--layout", default="blocked", choices=["blocked", "rows"],
+                    help="storage layout of the compressed weight (include/nm.h)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense GEMM baseline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -169,9 +171,9 @@ def main() -> int:
         s = 4 if w.dtype == "f32" else 2
         d = dict(name=name, R=w.R, K=w.K, T=w.T, dtype=w.dtype, s=s, W=W, X=X, Wd=to_dev(W),
                  Xd=to_dev(X))
-        d["vals"] = torch.empty((w.R, w.K // m * n), dtype=tdt, device=dev)
-        d["meta"] = torch.empty((w.R, nm.meta_words_per_row(w.K, n, m)), dtype=torch.int32,
-                                device=dev)
+        vshape, mshape = nm.compressed_shapes(w.R, w.K, n, m, args.layout)
+        d["vals"] = torch.empty(vshape, dtype=tdt, device=dev)
+        d["meta"] = torch.empty(mshape, dtype=torch.int32, device=dev)
         d["mask"] = torch.empty((w.R, w.K), dtype=torch.bool, device=dev)
         d["dec"] = torch.empty((w.R, w.K), dtype=tdt, device=dev)
         d["Y"] = torch.empty((w.R, w.T), dtype=tdt, device=dev)
@@ -188,19 +190,20 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
     DT = {"f32": 0, "f16": 1, "bf16": 2}[dtype]
+    LAY = nm.LAYOUTS[args.layout]
     kinds = ["mask", "compress", "decompress", "spmm"]
 
     def launch(d, kind):
         if kind == "mask":
             rc = L.nm_mask(d["Wd"].data_ptr(), DT, d["R"], d["K"], n, m, d["mask"].data_ptr(), sp)
         elif kind == "compress":
-            rc = L.nm_compress(d["Wd"].data_ptr(), DT, d["R"], d["K"], n, m, d["vals"].data_ptr(),
-                               d["meta"].data_ptr(), sp)
+            rc = L.nm_compress(d["Wd"].data_ptr(), DT, d["R"], d["K"], n, m, LAY,
+                               d["vals"].data_ptr(), d["meta"].data_ptr(), sp)
         elif kind == "decompress":
             rc = L.nm_decompress(d["vals"].data_ptr(), d["meta"].data_ptr(), DT, d["R"], d["K"],
-                                 n, m, d["dec"].data_ptr(), sp)
+                                 n, m, LAY, d["dec"].data_ptr(), sp)
         else:
-            rc = L.nm_spmm(d["vals"].data_ptr(), d["meta"].data_ptr(), d["R"], d["K"], n, m,
+            rc = L.nm_spmm(d["vals"].data_ptr(), d["meta"].data_ptr(), d["R"], d["K"], n, m, LAY,
                            d["Xd"].data_ptr(), d["T"], DT, d["Y"].data_ptr(), DT, sp)
         if rc != 0:
             raise RuntimeError(f"{kind} failed: {nm.status_str(rc)}")
@@ -265,7 +268,8 @@ def main() -> int:
     spmm_t = tot["spmm"][0]
     achieved = F_alg / spmm_t / 1e12
     peak = PEAK_MFMA_TFLOPS[dtype]
-    roofline = {"bound": "mfma", "kernel": "nm_spmm (smfmac 16x16x64)" if n * 2 == m else "nm_spmm",
+    roofline = {"bound": "mfma",
+                "kernel": "nm_spmm (structured-sparse matrix cores)" if n * 2 == m else "nm_spmm",
                 "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": None,
                 "alg_bytes_per_launch": sum(algorithmic_bytes(d["R"], d["K"], d["T"], n, m,
@@ -330,7 +334,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": args.workload,
                    "matrices": [f"{d['name']} {d['R']}x{d['K']} X {d['K']}x{d['T']}" for d in mats],
-                   "pattern": f"{n}:{m}", "global_batch": w0["T"], "parallelism": "single GPU"},
+                   "pattern": f"{n}:{m}", "layout": args.layout, "global_batch": w0["T"],
+                   "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "spmm_eff_tflops": round(F_eff / spmm_t / 1e12, 1),

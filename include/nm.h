@@ -11,14 +11,34 @@
  * synchronisation.  Arguments are validated before anything is launched; on
  * any error nothing is written.  Outputs must not alias inputs.
  *
- * Layouts (all dense, row-major, no padding between rows):
+ * Dense arrays (row-major, no padding between rows):
  *   W      R x K            elements of `dt`; groups are M consecutive elements along K
  *   mask   R x K            uint8, 1 = kept, 0 = pruned
- *   values R x (K*N/M)      elements of `dt`; the N kept values of each group, in
- *                           ascending position order
- *   meta   R x words(K,N,M) uint32; see nm_meta_words_per_row
  *   X      K x T            elements of `dt`
  *   Y      R x T            elements of `y_dt`
+ *
+ * The compressed pair (values, meta) is stored in one of two layouts:
+ *
+ *   NM_LAYOUT_ROWS -- the plain format.
+ *     values R x (K*N/M)    elements of `dt`; the N kept values of each group, in
+ *                           ascending position order, groups in order along the row
+ *     meta   R x words      uint32; see nm_meta_words_per_row
+ *
+ *   NM_LAYOUT_BLOCKED -- the same bytes regrouped in the order the sparse product
+ *     streams them (K must be a multiple of 64).  Rows are taken in groups of 16
+ *     (G = ceil(R / 16); rows R .. 16G-1 are stored as zeros) and K in steps of
+ *     64 (S = K / 64).  Per row and step there are V = 64*N/M values and
+ *     B = V*b/8 metadata bytes (b bits per field as below; B is always whole).
+ *     Block (g, s) holds rows 16g .. 16g+15 of step s, row after row:
+ *       value j (0 <= j < V) of row 16g+r, step s, is element
+ *         ((g*S + s)*16 + r)*V + j        of values
+ *         = element (16g+r)*(K*N/M) + s*V + j of the ROWS values;
+ *       metadata byte i (0 <= i < B) of row 16g+r, step s, is byte
+ *         ((g*S + s)*16 + r)*B + i        of meta
+ *         = byte s*B + i of row 16g+r's ROWS bitstream (bits 8(s*B+i) .. +7).
+ *     values has G*16*(K*N/M) elements, meta G*16*S*B bytes (a multiple of 4).
+ *     With 16-bit values and N/M = 1/2 one block of values is 1 KB and one block
+ *     of metadata 128 (2:4) or 64 (1:2) bytes, each a single contiguous read.
  *
  * Sources, cited by page title and section:
  *   "量化友好的SR-STE稀疏化训练" (blog.bakeneko-kuro.com), section "概念" (N:M keeps
@@ -42,7 +62,7 @@
 extern "C" {
 #endif
 
-#define NM_ABI_VERSION 1
+#define NM_ABI_VERSION 2
 
 typedef enum {
   NM_OK = 0,
@@ -52,10 +72,13 @@ typedef enum {
   NM_ERR_DTYPE = 4,       /* unknown dtype, or y_dt neither dt nor NM_F32            */
   NM_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned                        */
   NM_ERR_UNSUPPORTED = 6, /* valid arguments this build has no kernel for            */
-  NM_ERR_DEVICE = 7       /* no usable gfx950 device, or the launch failed           */
+  NM_ERR_DEVICE = 7,      /* no usable gfx950 device, or the launch failed           */
+  NM_ERR_LAYOUT = 8       /* unknown layout, or NM_LAYOUT_BLOCKED with K % 64 != 0   */
 } nm_status;
 
 typedef enum { NM_F32 = 0, NM_F16 = 1, NM_BF16 = 2 } nm_dtype;
+
+typedef enum { NM_LAYOUT_ROWS = 0, NM_LAYOUT_BLOCKED = 1 } nm_layout;
 
 typedef void* nm_stream_t; /* a hipStream_t; NULL selects the default stream */
 
@@ -65,8 +88,15 @@ int nm_abi_version(void);
 /* Static, human-readable name of a status code (never NULL). */
 const char* nm_status_str(nm_status s);
 
-/* Bytes of the value array: R * (K / m * n) * sizeof(dt); 0 for invalid arguments. */
-size_t nm_values_bytes(int64_t R, int64_t K, int n, int m, nm_dtype dt);
+/* Bytes of the value array: R * (K / m * n) * sizeof(dt) for NM_LAYOUT_ROWS,
+ * 16 * ceil(R / 16) * (K / m * n) * sizeof(dt) for NM_LAYOUT_BLOCKED; 0 for invalid
+ * arguments. */
+size_t nm_values_bytes(int64_t R, int64_t K, int n, int m, nm_dtype dt, nm_layout layout);
+
+/* Bytes of the metadata array: R * 4 * nm_meta_words_per_row(K, n, m) for
+ * NM_LAYOUT_ROWS, 16 * ceil(R / 16) * (K / 64) * B for NM_LAYOUT_BLOCKED; 0 for
+ * invalid arguments. */
+size_t nm_meta_bytes(int64_t R, int64_t K, int n, int m, nm_layout layout);
 
 /* Metadata words per row: ceil((K / m) * n * b / 32) with b = log2(m) bits per kept
  * value (1 for 1:2, 2 for 2:4, 3 for 4:8).  Field f = g*n + j of a row holds the
@@ -87,24 +117,28 @@ nm_status nm_mask(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m
 
 /* Mask and compress in one pass ("2:4 Sparsity의 benefits"): the kept values of
  * each group in ascending position order go to `values` (bitwise copies, so -0
- * stays -0) and their positions to `meta` (layout above). */
+ * stays -0) and their positions to `meta`, in `layout` (see above; the padding
+ * rows of NM_LAYOUT_BLOCKED are written as zeros). */
 nm_status nm_compress(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m,
-                      void* values, uint32_t* meta, nm_stream_t stream);
+                      nm_layout layout, void* values, uint32_t* meta, nm_stream_t stream);
 
 /* Inverse of nm_compress: W_out (R x K) gets each stored value at its recorded
  * position and +0 (all-zero bits) everywhere else.  The metadata is trusted: a
  * field that repeats a position within a group leaves the later value there. */
 nm_status nm_decompress(const void* values, const uint32_t* meta, nm_dtype dt, int64_t R,
-                        int64_t K, int n, int m, void* W_out, nm_stream_t stream);
+                        int64_t K, int n, int m, nm_layout layout, void* W_out,
+                        nm_stream_t stream);
 
 /* Y = W_sparse * X ("Tensor Scores 상에서 구조적인 sparse GEMM"): W_sparse is the
  * R x K matrix that (values, meta) encode, X is K x T, Y is R x T.  Products are
  * accumulated in fp32 and rounded once to y_dt (round to nearest even); y_dt
  * must be dt or NM_F32.  The metadata is trusted (well-formedness is the
- * caller's responsibility, as for any compressed operand). */
+ * caller's responsibility, as for any compressed operand).  Both layouts are
+ * accepted; the matrix-core kernels (2:4 and 1:2, 16-bit dt) stream
+ * NM_LAYOUT_BLOCKED at full speed and NM_LAYOUT_ROWS at a lower rate. */
 nm_status nm_spmm(const void* values, const uint32_t* meta, int64_t R, int64_t K, int n, int m,
-                  const void* X, int64_t T, nm_dtype dt, void* Y, nm_dtype y_dt,
-                  nm_stream_t stream);
+                  nm_layout layout, const void* X, int64_t T, nm_dtype dt, void* Y,
+                  nm_dtype y_dt, nm_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -9,6 +9,12 @@ library functions raises.
     Y = spmm(values, meta, X, 2, 4)           # X: (K, T), Y: (R, T)
     keep = mask(W, 2, 4)                      # bool (R, K)
     Wd = decompress(values, meta, 2, 4, K)    # dense (R, K), +0 where pruned
+
+The compressed pair comes in two layouts (defined in include/nm.h): "rows"
+(values (R, K*n/m), meta (R, words)) and "blocked" (blocks of 16 rows x 64
+columns, the order the sparse product streams; values (G, S, 16, 64*n/m), meta
+(G, S, words per block) with G = ceil(R/16), S = K/64).  A blocked pair does not
+record R, so decompress and spmm take it as ``rows=``.
 """
 from __future__ import annotations
 
@@ -23,11 +29,13 @@ LIB_PATH = os.path.join(HERE, "libnm.so")
 NM_F32, NM_F16, NM_BF16 = 0, 1, 2
 _DT = {torch.float32: NM_F32, torch.float16: NM_F16, torch.bfloat16: NM_BF16}
 _TORCH_DT = {v: k for k, v in _DT.items()}
-STATUS = ["ok", "null", "shape", "pattern", "dtype", "align", "unsupported", "device"]
+STATUS = ["ok", "null", "shape", "pattern", "dtype", "align", "unsupported", "device", "layout"]
+LAYOUTS = {"rows": 0, "blocked": 1}
+ABI_VERSION = 2
 
 # every function the C header declares
-EXPORTS = ("nm_abi_version", "nm_status_str", "nm_values_bytes", "nm_meta_words_per_row",
-           "nm_mask", "nm_compress", "nm_decompress", "nm_spmm")
+EXPORTS = ("nm_abi_version", "nm_status_str", "nm_values_bytes", "nm_meta_bytes",
+           "nm_meta_words_per_row", "nm_mask", "nm_compress", "nm_decompress", "nm_spmm")
 
 
 class NMError(RuntimeError):
@@ -51,16 +59,21 @@ def lib() -> ctypes.CDLL:
         L.nm_abi_version.restype = i32
         L.nm_status_str.argtypes = [i32]
         L.nm_status_str.restype = ctypes.c_char_p
-        L.nm_values_bytes.argtypes = [i64, i64, i32, i32, i32]
+        L.nm_values_bytes.argtypes = [i64, i64, i32, i32, i32, i32]
         L.nm_values_bytes.restype = ctypes.c_size_t
+        L.nm_meta_bytes.argtypes = [i64, i64, i32, i32, i32]
+        L.nm_meta_bytes.restype = ctypes.c_size_t
         L.nm_meta_words_per_row.argtypes = [i64, i32, i32]
         L.nm_meta_words_per_row.restype = i64
         L.nm_mask.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp]
-        L.nm_compress.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, vp]
-        L.nm_decompress.argtypes = [vp, vp, i32, i64, i64, i32, i32, vp, vp]
-        L.nm_spmm.argtypes = [vp, vp, i64, i64, i32, i32, vp, i64, i32, vp, i32, vp]
+        L.nm_compress.argtypes = [vp, i32, i64, i64, i32, i32, i32, vp, vp, vp]
+        L.nm_decompress.argtypes = [vp, vp, i32, i64, i64, i32, i32, i32, vp, vp]
+        L.nm_spmm.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, i64, i32, vp, i32, vp]
         for f in ("nm_mask", "nm_compress", "nm_decompress", "nm_spmm"):
             getattr(L, f).restype = i32
+        if L.nm_abi_version() != ABI_VERSION:
+            raise ImportError(f"{LIB_PATH} has ABI {L.nm_abi_version()}, expected {ABI_VERSION}: "
+                              "rebuild it")
         _lib = L
     return _lib
 
@@ -98,6 +111,27 @@ def meta_words_per_row(K: int, n: int, m: int) -> int:
     return int(lib().nm_meta_words_per_row(K, n, m))
 
 
+def _layout(layout: str) -> int:
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
+    return LAYOUTS[layout]
+
+
+def compressed_shapes(R: int, K: int, n: int, m: int, layout: str = "rows"):
+    """Shapes of (values, meta) for an R x K matrix: meta is int32 holding uint32 words."""
+    lay = _layout(layout)
+    words = meta_words_per_row(K, n, m)  # -1 for a bad pattern or K % m != 0
+    if words < 0:
+        _check("nm_compress", 2 if (m in (2, 4, 8) and 1 <= n <= m) else 3)
+    if lay == 0:
+        return (R, K // m * n), (R, words)
+    if K % 64:
+        _check("nm_compress", 8)
+    V = 64 // m * n                      # values per row and 64-wide step
+    B = V * {2: 1, 4: 2, 8: 3}[m] // 8   # metadata bytes per row and step
+    return ((R + 15) // 16, K // 64, 16, V), ((R + 15) // 16, K // 64, 4 * B)
+
+
 def mask(W: torch.Tensor, n: int = 2, m: int = 4) -> torch.Tensor:
     """Bool (R, K): True where the weight is kept by the magnitude-best N:M pattern."""
     dt = _dense_input(W, "W")
@@ -107,56 +141,63 @@ def mask(W: torch.Tensor, n: int = 2, m: int = 4) -> torch.Tensor:
     return out
 
 
-def compress(W: torch.Tensor, n: int = 2, m: int = 4):
-    """(values (R, K*n/m) in W's dtype, meta (R, words) int32 holding the uint32 bit fields)."""
+def compress(W: torch.Tensor, n: int = 2, m: int = 4, layout: str = "rows"):
+    """(values in W's dtype, meta int32 holding the uint32 bit fields) in `layout`."""
     dt = _dense_input(W, "W")
     R, K = W.shape
-    if K % m:
-        raise ValueError("K must be a multiple of m")
-    words = meta_words_per_row(K, n, m)
-    if words < 0:
-        _check("nm_compress", 3)
-    values = torch.empty((R, K // m * n), dtype=W.dtype, device=W.device)
-    meta = torch.empty((R, words), dtype=torch.int32, device=W.device)
-    _check("nm_compress", lib().nm_compress(_ptr(W), dt, R, K, n, m, _ptr(values), _ptr(meta),
-                                            _stream(W)))
+    lay = _layout(layout)
+    vshape, mshape = compressed_shapes(R, K, n, m, layout)
+    values = torch.empty(vshape, dtype=W.dtype, device=W.device)
+    meta = torch.empty(mshape, dtype=torch.int32, device=W.device)
+    _check("nm_compress", lib().nm_compress(_ptr(W), dt, R, K, n, m, lay, _ptr(values),
+                                            _ptr(meta), _stream(W)))
     return values, meta
 
 
-def _check_compressed(values: torch.Tensor, meta: torch.Tensor, n: int, m: int, K: int) -> int:
-    dt = _dense_input(values, "values")
-    R = values.shape[0]
-    words = meta_words_per_row(K, n, m)
-    if words < 0:
-        _check("nm_decompress", 3)
-    if values.shape != (R, K // m * n):
-        raise ValueError(f"values must be ({R}, {K // m * n}) for K={K}, {n}:{m}")
-    if meta.dtype != torch.int32 or meta.shape != (R, words) or not meta.is_contiguous():
-        raise ValueError(f"meta must be a contiguous int32 ({R}, {words}) tensor")
+def _check_compressed(values: torch.Tensor, meta: torch.Tensor, n: int, m: int, K: int,
+                      layout: str, rows: int | None) -> tuple[int, int]:
+    """(dtype code, R) of a compressed pair, after checking its shapes against K and n:m."""
+    if values.dtype not in _DT or not values.is_cuda or not values.is_contiguous():
+        raise ValueError("values must be a contiguous float32/float16/bfloat16 GPU tensor")
+    if _layout(layout) == 0:
+        R = values.shape[0] if values.dim() == 2 else -1
+        if rows is not None and rows != R:
+            raise ValueError(f"rows={rows} does not match values ({R} rows)")
+    else:
+        if rows is None:
+            raise ValueError("the blocked layout needs rows= (the matrix's row count)")
+        R = rows
+        if values.dim() != 4 or values.shape[0] != (R + 15) // 16:
+            raise ValueError(f"blocked values must be ({(R + 15) // 16}, S, 16, V) for R={R}")
+    vshape, mshape = compressed_shapes(R, K, n, m, layout)
+    if tuple(values.shape) != tuple(vshape):
+        raise ValueError(f"values must be {tuple(vshape)} for K={K}, {n}:{m}, {layout}")
+    if meta.dtype != torch.int32 or tuple(meta.shape) != tuple(mshape) or not meta.is_contiguous():
+        raise ValueError(f"meta must be a contiguous int32 {tuple(mshape)} tensor")
     if meta.device != values.device:
         raise ValueError("values and meta must be on the same device")
-    return dt
+    return _DT[values.dtype], R
 
 
-def decompress(values: torch.Tensor, meta: torch.Tensor, n: int, m: int, K: int) -> torch.Tensor:
+def decompress(values: torch.Tensor, meta: torch.Tensor, n: int, m: int, K: int,
+               layout: str = "rows", rows: int | None = None) -> torch.Tensor:
     """Dense (R, K): stored values at their positions, +0 elsewhere."""
-    dt = _check_compressed(values, meta, n, m, K)
-    R = values.shape[0]
+    dt, R = _check_compressed(values, meta, n, m, K, layout, rows)
     out = torch.empty((R, K), dtype=values.dtype, device=values.device)
     _check("nm_decompress", lib().nm_decompress(_ptr(values), _ptr(meta), dt, R, K, n, m,
-                                                _ptr(out), _stream(values)))
+                                                _layout(layout), _ptr(out), _stream(values)))
     return out
 
 
 def spmm(values: torch.Tensor, meta: torch.Tensor, X: torch.Tensor, n: int = 2, m: int = 4,
-         out_dtype: torch.dtype | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+         out_dtype: torch.dtype | None = None, out: torch.Tensor | None = None,
+         layout: str = "rows", rows: int | None = None) -> torch.Tensor:
     """Y (R, T) = W_sparse @ X with fp32 accumulation; out_dtype is X's dtype or float32."""
     xdt = _dense_input(X, "X")
     K, T = X.shape
-    dt = _check_compressed(values, meta, n, m, K)
+    dt, R = _check_compressed(values, meta, n, m, K, layout, rows)
     if dt != xdt:
         raise ValueError("values and X must have the same dtype")
-    R = values.shape[0]
     y_dtype = out_dtype or X.dtype
     if out is None:
         out = torch.empty((R, T), dtype=y_dtype, device=X.device)
@@ -164,6 +205,6 @@ def spmm(values: torch.Tensor, meta: torch.Tensor, X: torch.Tensor, n: int = 2, 
         raise ValueError("out has the wrong shape, dtype or layout")
     if y_dtype not in _DT:
         raise ValueError("out_dtype must be float32, float16 or bfloat16")
-    _check("nm_spmm", lib().nm_spmm(_ptr(values), _ptr(meta), R, K, n, m, _ptr(X), T, dt,
-                                    _ptr(out), _DT[y_dtype], _stream(X)))
+    _check("nm_spmm", lib().nm_spmm(_ptr(values), _ptr(meta), R, K, n, m, _layout(layout),
+                                    _ptr(X), T, dt, _ptr(out), _DT[y_dtype], _stream(X)))
     return out

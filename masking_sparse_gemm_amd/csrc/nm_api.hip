@@ -53,6 +53,22 @@ nm_status check_device() {
 
 nm_status from_hip(hipError_t e) { return e == hipSuccess ? NM_OK : NM_ERR_DEVICE; }
 
+// NM_LAYOUT_BLOCKED cuts K into steps of 64: each step then holds a whole number of
+// groups (M divides 64) and of metadata bytes (64 N / M fields of log2(M) bits).
+nm_status check_layout(int layout, int64_t K) {
+  if (layout == NM_LAYOUT_ROWS) return NM_OK;
+  if (layout == NM_LAYOUT_BLOCKED && K % 64 == 0) return NM_OK;
+  return NM_ERR_LAYOUT;
+}
+
+int64_t padded_rows(int64_t R, int layout) { return layout == NM_LAYOUT_BLOCKED ? (R + 15) / 16 * 16 : R; }
+
+// Bytes of metadata per row: the row's whole words (ROWS) or its K/64 step slices (BLOCKED).
+int64_t meta_row_bytes(int64_t K, int n, int m, int layout) {
+  const int64_t bits = (K / m) * n * meta_bits_of(m);
+  return layout == NM_LAYOUT_BLOCKED ? bits / 8 : (bits + 31) / 32 * 4;
+}
+
 }  // namespace
 
 extern "C" {
@@ -69,13 +85,23 @@ const char* nm_status_str(nm_status s) {
     case NM_ERR_ALIGN: return "pointer not 16-byte aligned";
     case NM_ERR_UNSUPPORTED: return "unsupported combination";
     case NM_ERR_DEVICE: return "device error (no gfx950 device, or launch failed)";
+    case NM_ERR_LAYOUT: return "bad layout (unknown, or blocked layout with K not a multiple of 64)";
   }
   return "unknown status";
 }
 
-size_t nm_values_bytes(int64_t R, int64_t K, int n, int m, nm_dtype dt) {
-  if (!valid_dtype(dt) || check_pattern(n, m) != NM_OK || check_shape(R, K, m) != NM_OK) return 0;
-  return (size_t)(R * (K / m * n) * elem_bytes(dt));
+size_t nm_values_bytes(int64_t R, int64_t K, int n, int m, nm_dtype dt, nm_layout layout) {
+  if (!valid_dtype(dt) || check_pattern(n, m) != NM_OK || check_shape(R, K, m) != NM_OK ||
+      check_layout(layout, K) != NM_OK)
+    return 0;
+  return (size_t)(padded_rows(R, layout) * (K / m * n) * elem_bytes(dt));
+}
+
+size_t nm_meta_bytes(int64_t R, int64_t K, int n, int m, nm_layout layout) {
+  if (check_pattern(n, m) != NM_OK || check_shape(R, K, m) != NM_OK ||
+      check_layout(layout, K) != NM_OK)
+    return 0;
+  return (size_t)(padded_rows(R, layout) * meta_row_bytes(K, n, m, layout));
 }
 
 int64_t nm_meta_words_per_row(int64_t K, int n, int m) {
@@ -93,46 +119,51 @@ nm_status nm_mask(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m
   if (R * K == 0) return NM_OK;
   if (!aligned16(W) || !aligned16(mask)) return NM_ERR_ALIGN;
   if ((st = check_device()) != NM_OK) return st;
-  return from_hip(nm::launch_select(W, elem_bytes(dt), R, K, n, m, nullptr, nullptr, mask,
+  return from_hip(nm::launch_select(W, elem_bytes(dt), R, K, n, m, false, nullptr, nullptr, mask,
                                     static_cast<hipStream_t>(stream)));
 }
 
 nm_status nm_compress(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m,
-                      void* values, uint32_t* meta, nm_stream_t stream) {
+                      nm_layout layout, void* values, uint32_t* meta, nm_stream_t stream) {
   if (!valid_dtype(dt)) return NM_ERR_DTYPE;
   nm_status st = check_pattern(n, m);
   if (st != NM_OK) return st;
   if ((st = check_shape(R, K, m)) != NM_OK) return st;
+  if ((st = check_layout(layout, K)) != NM_OK) return st;
   if (missing(W, R * K) || missing(values, R * K) || missing(meta, R * K)) return NM_ERR_NULL;
   if (R * K == 0) return NM_OK;
   if (!aligned16(W) || !aligned16(values) || !aligned16(meta)) return NM_ERR_ALIGN;
   if ((st = check_device()) != NM_OK) return st;
-  return from_hip(nm::launch_select(W, elem_bytes(dt), R, K, n, m, values, meta, nullptr,
-                                    static_cast<hipStream_t>(stream)));
+  return from_hip(nm::launch_select(W, elem_bytes(dt), R, K, n, m, layout == NM_LAYOUT_BLOCKED,
+                                    values, meta, nullptr, static_cast<hipStream_t>(stream)));
 }
 
 nm_status nm_decompress(const void* values, const uint32_t* meta, nm_dtype dt, int64_t R,
-                        int64_t K, int n, int m, void* W_out, nm_stream_t stream) {
+                        int64_t K, int n, int m, nm_layout layout, void* W_out,
+                        nm_stream_t stream) {
   if (!valid_dtype(dt)) return NM_ERR_DTYPE;
   nm_status st = check_pattern(n, m);
   if (st != NM_OK) return st;
   if ((st = check_shape(R, K, m)) != NM_OK) return st;
+  if ((st = check_layout(layout, K)) != NM_OK) return st;
   if (missing(values, R * K) || missing(meta, R * K) || missing(W_out, R * K)) return NM_ERR_NULL;
   if (R * K == 0) return NM_OK;
   if (!aligned16(values) || !aligned16(meta) || !aligned16(W_out)) return NM_ERR_ALIGN;
   if ((st = check_device()) != NM_OK) return st;
-  return from_hip(nm::launch_decompress(values, meta, elem_bytes(dt), R, K, n, m, W_out,
+  return from_hip(nm::launch_decompress(values, meta, elem_bytes(dt), R, K, n, m,
+                                        layout == NM_LAYOUT_BLOCKED, W_out,
                                         static_cast<hipStream_t>(stream)));
 }
 
 nm_status nm_spmm(const void* values, const uint32_t* meta, int64_t R, int64_t K, int n, int m,
-                  const void* X, int64_t T, nm_dtype dt, void* Y, nm_dtype y_dt,
-                  nm_stream_t stream) {
+                  nm_layout layout, const void* X, int64_t T, nm_dtype dt, void* Y,
+                  nm_dtype y_dt, nm_stream_t stream) {
   if (!valid_dtype(dt) || !valid_dtype(y_dt) || (y_dt != dt && y_dt != NM_F32))
     return NM_ERR_DTYPE;
   nm_status st = check_pattern(n, m);
   if (st != NM_OK) return st;
   if ((st = check_shape(R, K, m)) != NM_OK) return st;
+  if ((st = check_layout(layout, K)) != NM_OK) return st;
   if (T < 0 || (K > 0 && T > ((int64_t)1 << 40) / K) || (R > 0 && T > ((int64_t)1 << 40) / R))
     return NM_ERR_SHAPE;
   if (missing(values, R * K) || missing(meta, R * K) || missing(X, K * T) || missing(Y, R * T))
@@ -140,8 +171,8 @@ nm_status nm_spmm(const void* values, const uint32_t* meta, int64_t R, int64_t K
   if (R * T == 0) return NM_OK;
   if (!aligned16(values) || !aligned16(meta) || !aligned16(X) || !aligned16(Y)) return NM_ERR_ALIGN;
   if ((st = check_device()) != NM_OK) return st;
-  return from_hip(nm::launch_spmm(values, meta, R, K, n, m, X, T, (int)dt, Y, (int)y_dt,
-                                  static_cast<hipStream_t>(stream)));
+  return from_hip(nm::launch_spmm(values, meta, R, K, n, m, layout == NM_LAYOUT_BLOCKED, X, T,
+                                  (int)dt, Y, (int)y_dt, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

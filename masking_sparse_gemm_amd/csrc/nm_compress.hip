@@ -15,6 +15,8 @@
 // "2:4 Sparsity의 benefits"): values hold the N kept elements of each group in
 // ascending position order; metadata field f = g*N + j of a row holds position
 // j of group g in b = log2(M) bits at bit f*b of the row, least significant first.
+// The blocked layout stores the same values and bits in blocks of 16 rows x 64
+// columns (include/nm.h); its kernels take one block per wave.
 #include "nm_device.h"
 #include "nm_launch.h"
 
@@ -257,6 +259,143 @@ __global__ void __launch_bounds__(kThreads) flat_decompress_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Blocked layout (see include/nm.h): one wave per block of 16 rows x one 64-wide K
+// step.  Lane l takes row l / 4 of the block and elements 16 (l % 4) .. +15 of the
+// step; its kept values and its metadata bits then sit at lane-linear offsets of the
+// block (value l * 16N/M, bit l * 16Nb/M), so a wave writes the block's values and its
+// metadata as two contiguous runs.  Rows past R are stored as zeros.
+// ---------------------------------------------------------------------------
+template <typename E, int N, int M>
+struct LaneShape {
+  static constexpr int kWords = 16 * (int)sizeof(E) / 4;      // 16 elements of W
+  static constexpr int kGroups = 16 / M;
+  static constexpr int kVals = kGroups * N;                   // kept values per lane
+  static constexpr int kValWords = kVals * (int)sizeof(E) / 4;
+  static constexpr int kBits = kVals * meta_bits(M);          // metadata bits per lane
+  static constexpr int kBlockMetaWords = 64 * kBits / 32;
+  static constexpr bool kShuffle = 32 % kBits == 0;           // whole lanes per word
+};
+
+template <typename E, int N, int M>
+__global__ void __launch_bounds__(kThreads) blocked_select_kernel(const uint32_t* __restrict__ W,
+                                                                  int64_t R, int64_t K,
+                                                                  int64_t blocks,
+                                                                  uint32_t* __restrict__ values,
+                                                                  uint32_t* __restrict__ meta) {
+  using L = LaneShape<E, N, M>;
+  constexpr int b = meta_bits(M);
+  __shared__ uint32_t lds_bits[kThreads / 64][L::kShuffle ? 1 : L::kBlockMetaWords];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t blk = (int64_t)blockIdx.x * (kThreads / 64) + wave;
+  if (blk >= blocks) return;  // the whole wave
+  const int64_t steps = K / 64;
+  const int64_t row = 16 * (blk / steps) + (lane >> 2);
+  const bool live = row < R;
+  uint32_t w[L::kWords];
+  if (live) {
+    load_words<L::kWords>(W + (row * K + 64 * (blk % steps) + 16 * (lane & 3)) * sizeof(E) / 4, w);
+  } else {
+#pragma unroll
+    for (int i = 0; i < L::kWords; ++i) w[i] = 0;
+  }
+  uint32_t vw[L::kValWords];
+#pragma unroll
+  for (int i = 0; i < L::kValWords; ++i) vw[i] = 0;
+  uint64_t bits = 0;
+#pragma unroll
+  for (int gi = 0; gi < L::kGroups; ++gi) {
+    uint32_t key[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) key[i] = word_elem<E>(w, gi * M + i) & Elem<E>::kKeyMask;
+    int pos[N];
+    kept_positions<N>(keep_bits<N, M>(key), pos);
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int k = gi * N + j;
+      const uint32_t v = group_elem<E, M>(w + gi * M * (int)sizeof(E) / 4, pos[j]);
+      if constexpr (sizeof(E) == 2)
+        vw[k / 2] |= v << (16 * (k % 2));
+      else
+        vw[k] = v;
+      bits |= (uint64_t)pos[j] << (k * b);
+    }
+  }
+  if (!live) bits = 0;  // padding rows: zero values (w = 0) and zero metadata
+  store_words<L::kValWords>(values + blk * (64 * L::kValWords) + lane * L::kValWords, vw);
+
+  uint32_t* mblk = meta + blk * L::kBlockMetaWords;
+  if constexpr (L::kShuffle) {
+    constexpr int LPW = 32 / L::kBits;  // lanes per metadata word
+    const uint32_t word = or_reduce_lanes<LPW>((uint32_t)bits << ((lane % LPW) * L::kBits));
+    if (lane % LPW == 0) mblk[lane / LPW] = word;
+  } else {
+    uint32_t* buf = lds_bits[wave];
+    for (int i = lane; i < L::kBlockMetaWords; i += 64) buf[i] = 0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    const int o = lane * L::kBits, wi = o / 32, sh = o % 32;
+    atomicOr(&buf[wi], (uint32_t)(bits << sh));
+    if (sh + L::kBits > 32) atomicOr(&buf[wi + 1], (uint32_t)(bits >> (32 - sh)));
+    if (sh + L::kBits > 64) atomicOr(&buf[wi + 2], (uint32_t)(bits >> (64 - sh)));
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    for (int i = lane; i < L::kBlockMetaWords; i += 64) mblk[i] = buf[i];
+  }
+}
+
+template <typename E, int N, int M>
+__global__ void __launch_bounds__(kThreads) blocked_decompress_kernel(
+    const uint32_t* __restrict__ values, const uint32_t* __restrict__ meta, int64_t R, int64_t K,
+    int64_t blocks, uint32_t* __restrict__ out) {
+  using L = LaneShape<E, N, M>;
+  constexpr int b = meta_bits(M);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t blk = (int64_t)blockIdx.x * (kThreads / 64) + wave;
+  if (blk >= blocks) return;
+  const int64_t steps = K / 64;
+  const int64_t row = 16 * (blk / steps) + (lane >> 2);
+  if (row >= R) return;  // padding rows have no output
+  const uint32_t* vsrc = values + blk * (64 * L::kValWords) + lane * L::kValWords;
+  uint32_t vw[L::kValWords];
+#pragma unroll
+  for (int i = 0; i < L::kValWords; ++i) vw[i] = vsrc[i];
+  const uint32_t* mblk = meta + blk * L::kBlockMetaWords;
+  const int o = lane * L::kBits, wi = o / 32, sh = o % 32;
+  uint64_t window = mblk[wi];
+  if (sh + L::kBits > 32) window |= (uint64_t)mblk[wi + 1] << 32;
+  uint64_t bits = window >> sh;
+  if (sh + L::kBits > 64) bits |= (uint64_t)mblk[wi + 2] << (64 - sh);
+  uint32_t ow[L::kWords];
+#pragma unroll
+  for (int i = 0; i < L::kWords; ++i) ow[i] = 0;
+#pragma unroll
+  for (int gi = 0; gi < L::kGroups; ++gi) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int k = gi * N + j;
+      const int p = (int)((bits >> (k * b)) & ((1u << b) - 1u));
+      const uint32_t v = word_elem<E>(vw, k);
+#pragma unroll
+      for (int i = 0; i < M; ++i) {
+        const int e = gi * M + i;
+        if constexpr (sizeof(E) == 2) {
+          const uint32_t sh16 = 16 * (e % 2);
+          const uint32_t cur = ow[e / 2];
+          ow[e / 2] = (p == i) ? ((cur & ~(0xFFFFu << sh16)) | (v << sh16)) : cur;
+        } else {
+          ow[e] = (p == i) ? v : ow[e];
+        }
+      }
+    }
+  }
+  uint32_t* dst = out + (row * K + 64 * (blk % steps) + 16 * (lane & 3)) * sizeof(E) / 4;
+#pragma unroll
+  for (int i = 0; i < L::kWords / 4; ++i)
+    __builtin_nontemporal_store(u32x4_t{ow[4 * i], ow[4 * i + 1], ow[4 * i + 2], ow[4 * i + 3]},
+                                reinterpret_cast<u32x4_t*>(dst) + i);
+}
+
+// ---------------------------------------------------------------------------
 // Shape-agnostic kernels (any R, K with K % M == 0).
 // ---------------------------------------------------------------------------
 template <typename E, int N, int M>
@@ -369,12 +508,18 @@ bool flat_ok(int64_t K) {
 }
 
 template <typename E, int N, int M>
-hipError_t run_select(const void* W, int64_t R, int64_t K, void* values, uint32_t* meta,
-                      uint8_t* mask, hipStream_t s) {
+hipError_t run_select(const void* W, int64_t R, int64_t K, bool blocked, void* values,
+                      uint32_t* meta, uint8_t* mask, hipStream_t s) {
   using S = UnitShape<E, M>;
   const int64_t elems = R * K;
   if (elems == 0) return hipSuccess;
   const bool want_mask = mask != nullptr, want_compress = values != nullptr;
+  if (blocked) {  // compress only (the mask is a dense array in either layout)
+    const int64_t blocks = (R + 15) / 16 * (K / 64);
+    blocked_select_kernel<E, N, M><<<blocks_for(blocks, kThreads / 64), kThreads, 0, s>>>(
+        static_cast<const uint32_t*>(W), R, K, blocks, static_cast<uint32_t*>(values), meta);
+    return hipGetLastError();
+  }
   if constexpr (flat_kernel_exists<E, N, M>()) {
    if (flat_ok<E, N, M>(K)) {
     const int64_t units = elems / S::kElems;
@@ -410,10 +555,16 @@ hipError_t run_select(const void* W, int64_t R, int64_t K, void* values, uint32_
 
 template <typename E, int N, int M>
 hipError_t run_decompress(const void* values, const uint32_t* meta, int64_t R, int64_t K,
-                          void* out, hipStream_t s) {
+                          bool blocked, void* out, hipStream_t s) {
   using S = UnitShape<E, M>;
   const int64_t elems = R * K;
   if (elems == 0) return hipSuccess;
+  if (blocked) {
+    const int64_t blocks = (R + 15) / 16 * (K / 64);
+    blocked_decompress_kernel<E, N, M><<<blocks_for(blocks, kThreads / 64), kThreads, 0, s>>>(
+        static_cast<const uint32_t*>(values), meta, R, K, blocks, static_cast<uint32_t*>(out));
+    return hipGetLastError();
+  }
   if constexpr (flat_kernel_exists<E, N, M>()) {
     if (flat_ok<E, N, M>(K)) {
       const int64_t units = elems / S::kElems;
@@ -444,33 +595,34 @@ hipError_t dispatch_nm(int n, int m, A... args) {
 
 template <typename E, int N, int M>
 struct SelectOp {
-  static hipError_t run(const void* W, int64_t R, int64_t K, void* values, uint32_t* meta,
-                        uint8_t* mask, hipStream_t s) {
-    return run_select<E, N, M>(W, R, K, values, meta, mask, s);
+  static hipError_t run(const void* W, int64_t R, int64_t K, bool blocked, void* values,
+                        uint32_t* meta, uint8_t* mask, hipStream_t s) {
+    return run_select<E, N, M>(W, R, K, blocked, values, meta, mask, s);
   }
 };
 template <typename E, int N, int M>
 struct DecompressOp {
-  static hipError_t run(const void* values, const uint32_t* meta, int64_t R, int64_t K, void* out,
-                        hipStream_t s) {
-    return run_decompress<E, N, M>(values, meta, R, K, out, s);
+  static hipError_t run(const void* values, const uint32_t* meta, int64_t R, int64_t K,
+                        bool blocked, void* out, hipStream_t s) {
+    return run_decompress<E, N, M>(values, meta, R, K, blocked, out, s);
   }
 };
 
 }  // namespace
 
 hipError_t launch_select(const void* W, int elem_bytes, int64_t R, int64_t K, int n, int m,
-                         void* values, uint32_t* meta, uint8_t* mask, hipStream_t s) {
+                         bool blocked, void* values, uint32_t* meta, uint8_t* mask,
+                         hipStream_t s) {
   if (elem_bytes == 2)
-    return dispatch_nm<uint16_t, SelectOp>(n, m, W, R, K, values, meta, mask, s);
-  return dispatch_nm<uint32_t, SelectOp>(n, m, W, R, K, values, meta, mask, s);
+    return dispatch_nm<uint16_t, SelectOp>(n, m, W, R, K, blocked, values, meta, mask, s);
+  return dispatch_nm<uint32_t, SelectOp>(n, m, W, R, K, blocked, values, meta, mask, s);
 }
 
 hipError_t launch_decompress(const void* values, const uint32_t* meta, int elem_bytes, int64_t R,
-                             int64_t K, int n, int m, void* out, hipStream_t s) {
+                             int64_t K, int n, int m, bool blocked, void* out, hipStream_t s) {
   if (elem_bytes == 2)
-    return dispatch_nm<uint16_t, DecompressOp>(n, m, values, meta, R, K, out, s);
-  return dispatch_nm<uint32_t, DecompressOp>(n, m, values, meta, R, K, out, s);
+    return dispatch_nm<uint16_t, DecompressOp>(n, m, values, meta, R, K, blocked, out, s);
+  return dispatch_nm<uint32_t, DecompressOp>(n, m, values, meta, R, K, blocked, out, s);
 }
 
 }  // namespace nm

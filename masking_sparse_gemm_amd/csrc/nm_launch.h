@@ -5,15 +5,19 @@
 
 namespace nm {
 
+// `blocked` selects NM_LAYOUT_BLOCKED for the compressed pair (K % 64 == 0 checked).
+
 // Mask and/or compress: mask may be null (compress only); values/meta may be null (mask only).
 hipError_t launch_select(const void* W, int elem_bytes, int64_t R, int64_t K, int n, int m,
-                         void* values, uint32_t* meta, uint8_t* mask, hipStream_t s);
+                         bool blocked, void* values, uint32_t* meta, uint8_t* mask,
+                         hipStream_t s);
 
 hipError_t launch_decompress(const void* values, const uint32_t* meta, int elem_bytes, int64_t R,
-                             int64_t K, int n, int m, void* out, hipStream_t s);
+                             int64_t K, int n, int m, bool blocked, void* out, hipStream_t s);
 
 // dt / y_dt use the nm_dtype codes: 0 fp32, 1 fp16, 2 bf16.
 hipError_t launch_spmm(const void* values, const uint32_t* meta, int64_t R, int64_t K, int n,
-                       int m, const void* X, int64_t T, int dt, void* Y, int y_dt, hipStream_t s);
+                       int m, bool blocked, const void* X, int64_t T, int dt, void* Y, int y_dt,
+                       hipStream_t s);
 
 }  // namespace nm

@@ -183,7 +183,7 @@ __device__ __forceinline__ short16_t lds_b_fragment(uint32_t a0, uint32_t a1) {
 
 // Four A fragments (16 bytes each, 1 KB apart) and their metadata (128 bytes apart).
 // kPat12 reads one byte of 1:2 metadata, otherwise a 16-bit 2:4 unit.
-template <bool kPat12>
+template <bool kPat12, int kAStride = 1024, int kMStride = 128>
 __device__ __forceinline__ void lds_a_fragments4(uint32_t va, uint32_t ma, u32x4_t& a0,
                                                  u32x4_t& a1, u32x4_t& a2, u32x4_t& a3,
                                                  uint32_t& m0, uint32_t& m1, uint32_t& m2,
@@ -191,30 +191,32 @@ __device__ __forceinline__ void lds_a_fragments4(uint32_t va, uint32_t ma, u32x4
   if constexpr (kPat12) {
     asm volatile(
         "ds_read_b128 %0, %8\n\t"
-        "ds_read_b128 %1, %8 offset:1024\n\t"
-        "ds_read_b128 %2, %8 offset:2048\n\t"
-        "ds_read_b128 %3, %8 offset:3072\n\t"
+        "ds_read_b128 %1, %8 offset:%10\n\t"
+        "ds_read_b128 %2, %8 offset:%11\n\t"
+        "ds_read_b128 %3, %8 offset:%12\n\t"
         "ds_read_u8 %4, %9\n\t"
-        "ds_read_u8 %5, %9 offset:128\n\t"
-        "ds_read_u8 %6, %9 offset:256\n\t"
-        "ds_read_u8 %7, %9 offset:384\n\t"
+        "ds_read_u8 %5, %9 offset:%13\n\t"
+        "ds_read_u8 %6, %9 offset:%14\n\t"
+        "ds_read_u8 %7, %9 offset:%15\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(m0), "=&v"(m1), "=&v"(m2), "=&v"(m3)
-        : "v"(va), "v"(ma)
+        : "v"(va), "v"(ma), "n"(kAStride), "n"(2 * kAStride), "n"(3 * kAStride), "n"(kMStride),
+          "n"(2 * kMStride), "n"(3 * kMStride)
         : "memory");
   } else {
     asm volatile(
         "ds_read_b128 %0, %8\n\t"
-        "ds_read_b128 %1, %8 offset:1024\n\t"
-        "ds_read_b128 %2, %8 offset:2048\n\t"
-        "ds_read_b128 %3, %8 offset:3072\n\t"
+        "ds_read_b128 %1, %8 offset:%10\n\t"
+        "ds_read_b128 %2, %8 offset:%11\n\t"
+        "ds_read_b128 %3, %8 offset:%12\n\t"
         "ds_read_u16 %4, %9\n\t"
-        "ds_read_u16 %5, %9 offset:128\n\t"
-        "ds_read_u16 %6, %9 offset:256\n\t"
-        "ds_read_u16 %7, %9 offset:384\n\t"
+        "ds_read_u16 %5, %9 offset:%13\n\t"
+        "ds_read_u16 %6, %9 offset:%14\n\t"
+        "ds_read_u16 %7, %9 offset:%15\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(a0), "=&v"(a1), "=&v"(a2), "=&v"(a3), "=&v"(m0), "=&v"(m1), "=&v"(m2), "=&v"(m3)
-        : "v"(va), "v"(ma)
+        : "v"(va), "v"(ma), "n"(kAStride), "n"(2 * kAStride), "n"(3 * kAStride), "n"(kMStride),
+          "n"(2 * kMStride), "n"(3 * kMStride)
         : "memory");
   }
 }
@@ -225,6 +227,52 @@ template <int N>
 __device__ __forceinline__ void wait_loads_and_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
+
+// Byte offset, for step 0, of one lane's direct load of compressed values: the load
+// fills tile rows i0 .. i0+15 (64 value bytes per row and step), lane l taking row
+// i0 + l/4 and the 16-byte chunk that lands at physical chunk l % 4 of that LDS row
+// (logical chunk (l % 4) ^ ((row >> 2) & 3)).  Rows past the matrix read any valid row
+// (their outputs are dropped).
+template <bool kBlocked>
+__device__ __forceinline__ int64_t values_source(int m0, int i0, int lane, int R, int K,
+                                                 int nsteps) {
+  const int i = i0 + (lane >> 2);
+  const int lc = (lane & 3) ^ ((i >> 2) & 3);
+  if constexpr (kBlocked) {  // one contiguous 1 KB block per 16 rows and step
+    const int last = ((R + 15) >> 4) - 1;
+    int g = (m0 + i0) >> 4;
+    g = g < last ? g : last;
+    return (int64_t)g * nsteps * 1024 + (lane >> 2) * 64 + 16 * lc;
+  } else {  // row-major: 64 bytes per row and step
+    int row = m0 + i;
+    row = row < R ? row : R - 1;
+    return (int64_t)row * K + 16 * lc;
+  }
+}
+template <bool kBlocked>
+constexpr int64_t values_step_bytes() { return kBlocked ? 1024 : 64; }
+
+// The same for metadata: a load fills tile rows i0 .. i0+31 with 8 bytes each, two lanes
+// per row (1:2 rows hold 4 bytes per step, which both lanes read).
+template <bool kBlocked, bool kPat12>
+__device__ __forceinline__ int64_t meta_source(int m0, int i0, int lane, int R, int K,
+                                               int nsteps) {
+  constexpr int kRowStep = kPat12 ? 4 : 8;  // metadata bytes per row and step
+  const int i = i0 + (lane >> 1);
+  const int half = kPat12 ? 0 : 4 * (lane & 1);
+  if constexpr (kBlocked) {
+    const int last = ((R + 15) >> 4) - 1;
+    int g = (m0 + i) >> 4;
+    g = g < last ? g : last;
+    return (int64_t)g * nsteps * (16 * kRowStep) + (i & 15) * kRowStep + half;
+  } else {
+    int row = m0 + i;
+    row = row < R ? row : R - 1;
+    return (int64_t)row * (K / 64 * kRowStep) + half;
+  }
+}
+template <bool kBlocked, bool kPat12>
+constexpr int64_t meta_step_bytes() { return (kPat12 ? 4 : 8) * (kBlocked ? 16 : 1); }
 
 // Which output tile a workgroup computes.  Workgroups are dispatched round-robin over
 // the XCDs (each with its own L2), so workgroup b runs on XCD b % xcds.  Each XCD gets
@@ -263,7 +311,8 @@ struct TileMap {
 //      global memory, 32 per step); 16-byte chunk c at physical chunk c ^ ((i >> 2) & 3).
 //      One direct load fills rows 16 j .. 16 j + 15: exactly one fragment's rows.
 //   meta: tile row i holds 8 bytes (2:4: four 16-bit units; 1:2: four bytes + pad).
-template <bool BF16, bool kPat12, int YT, int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
+template <bool BF16, bool kPat12, bool kBlocked, int YT, int BM, int BN, int WAVES_M, int WAVES_N,
+          int STAGES>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
     smfmac_spmm_kernel(const uint16_t* __restrict__ values, const uint32_t* __restrict__ meta,
                        const uint16_t* __restrict__ X, void* __restrict__ Y, int R, int K, int T,
@@ -287,7 +336,6 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
   const uint8_t* xg = reinterpret_cast<const uint8_t*>(X);
   const uint8_t* vg = reinterpret_cast<const uint8_t*>(values);
   const uint8_t* mg = reinterpret_cast<const uint8_t*>(meta);
-  const int64_t meta_row_bytes = K / (kPat12 ? 16 : 8);
   int64_t x_src[TL::kXLoads];
   uint32_t x_dst[TL::kXLoads];
 #pragma unroll
@@ -306,11 +354,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 #pragma unroll
   for (int j = 0; j < TL::kALoads; ++j) {
     const int blk = j * TL::kWaves + wave;  // rows 16 blk .. 16 blk + 15 of the tile
-    const int i = 16 * blk + (lane >> 2), pc = lane & 3;
-    const int lc = pc ^ ((i >> 2) & 3);
-    int row = m0 + i;
-    row = row < R ? row : R - 1;  // rows past R: any valid row (their outputs are dropped)
-    a_src[j] = (int64_t)row * K + 16 * lc;
+    a_src[j] = values_source<kBlocked>(m0, 16 * blk, lane, R, K, nsteps);
     a_dst[j] = (uint32_t)(TL::kXBytes + blk * 1024);
   }
   int64_t m_src[TL::kMLoads];
@@ -318,19 +362,15 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 #pragma unroll
   for (int j = 0; j < TL::kMLoads; ++j) {
     const int blk = j * TL::kWaves + wave;  // rows 32 blk .. 32 blk + 31
-    const int i = 32 * blk + (lane >> 1);
-    int row = m0 + i;
-    row = row < R ? row : R - 1;
-    // 1:2 rows carry 4 bytes per step: the second half-lane reads the same word
-    m_src[j] = (int64_t)row * meta_row_bytes + (kPat12 ? 0 : 4 * (lane & 1));
+    m_src[j] = meta_source<kBlocked, kPat12>(m0, 32 * blk, lane, R, K, nsteps);
     m_dst[j] = (uint32_t)(TL::kXBytes + TL::kABytes + blk * 256);
   }
   auto issue_step = [&](int step) {
     step = step < last_step ? step : last_step;
     uint8_t* st = smem + (step % kStages) * TL::kStageBytes;
-    const int64_t kx = (int64_t)step * kKStep * T * 2;    // X rows
-    const int64_t ka = (int64_t)step * 64;                // A value bytes
-    const int64_t km = (int64_t)step * (kPat12 ? 4 : 8);  // metadata bytes
+    const int64_t kx = (int64_t)step * kKStep * T * 2;                      // X rows
+    const int64_t ka = (int64_t)step * values_step_bytes<kBlocked>();       // values
+    const int64_t km = (int64_t)step * meta_step_bytes<kBlocked, kPat12>();  // metadata
 #pragma unroll
     for (int j = 0; j < TL::kXLoads; ++j) global_to_lds<16>(xg + x_src[j] + kx, st + x_dst[j]);
 #pragma unroll
@@ -419,12 +459,592 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 }
 
 // ===========================================================================
+// Structured-sparse matrix-core kernel, 32x32x32 form with hand-scheduled blocks.
+//
+// A wave owns 128 rows x 64 columns of the tile: four 32-row A fragments and two
+// 32-column B fragments per 32-wide K substep (two substeps per 64-wide step).  The work
+// of a step is cut into four blocks, one per (substep t, B fragment f); each block is one
+// asm statement that first issues LDS reads of fragments needed later, then the four
+// v_smfmac_f32_32x32x32 of this block (~130 matrix-core cycles), then waits for its
+// reads, so the matrix cores work while the reads are in flight.  Each block reads the
+// next block's B fragment; block (0,1) also reads this step's substep-1 A fragments and
+// block (1,1) next step's substep-0 A fragments.  A register is thus rewritten only
+// when the last smfmac that read it is at least one whole block back, and the B fragment
+// of the previous block is passed in as a dummy input so that no read lands in it while
+// that block's smfmac may still be reading it.  Accumulators live in AGPRs.
+// ===========================================================================
+typedef float float16v_t __attribute__((ext_vector_type(16)));
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
+struct Smfmac32Tile {
+  static constexpr int kThreads = 64 * WAVES_M * WAVES_N;
+  static constexpr int kWaves = WAVES_M * WAVES_N;
+  static constexpr int kStages = STAGES;
+  static constexpr int kWM = BM / WAVES_M;
+  static constexpr int kWN = BN / WAVES_N;
+  static constexpr int kXRowBytes = BN * 2;
+  static constexpr int kXChunks = BN / 8;
+  static constexpr int kXBytes = kKStep * kXRowBytes;
+  static constexpr int kABytes = BM * 64;
+  static constexpr int kMBytes = BM * 8;
+  static constexpr int kStageBytes = kXBytes + kABytes + kMBytes;
+  static constexpr int kXLoads = kXBytes / 1024 / kWaves;
+  static constexpr int kALoads = kABytes / 1024 / kWaves;
+  static constexpr int kMLoads = kMBytes / 256 / kWaves;
+  static constexpr int kLoads = kXLoads + kALoads + kMLoads;
+  static_assert(kWM == 128, "a wave owns four 32-row A fragments");
+  static_assert(kWN == 64, "a wave owns two 32-column B fragments");
+  static_assert(kXBytes % (1024 * kWaves) == 0 && kABytes % (1024 * kWaves) == 0 &&
+                    kMBytes % (256 * kWaves) == 0,
+                "every wave issues the same number of direct loads per step");
+  static_assert(BN >= 128, "the X swizzle needs at least 8 column pairs per row");
+  static_assert(kStages >= 3 && (kStages - 2) * kLoads <= 63, "vmcnt budget");
+  static_assert(kStages * kStageBytes <= 160 * 1024, "LDS budget");
+};
+
+struct AFrags {
+  u32x4_t v[4];
+  uint32_t ix[4];
+};
+
+// One block: read the next B fragment (rows kb, kb + 4 at b0, b1 and kb + 16, kb + 20 at
+// + kFar); with kReadA also four A fragments (kAStride apart) and their index words
+// (kMStride apart); then the four smfmac of this block on accumulators c[0..3] (AGPRs).
+#define NM_SMFMAC32_OPS(OP)                                                                \
+  OP " %[c0], %[a0], %[b], %[i0]\n\t" OP " %[c1], %[a1], %[b], %[i1]\n\t" OP               \
+     " %[c2], %[a2], %[b], %[i2]\n\t" OP " %[c3], %[a3], %[b], %[i3]\n\t"                  \
+     "s_waitcnt lgkmcnt(0)"
+#define NM_SMFMAC32_BREADS                                                                 \
+  "s_nop 2\n\t"                                                                            \
+  "ds_read_b64_tr_b16 %[n0], %[b0]\n\t"                                                    \
+  "ds_read_b64_tr_b16 %[n1], %[b1]\n\t"                                                    \
+  "ds_read_b64_tr_b16 %[n2], %[b0] offset:%[far]\n\t"                                      \
+  "ds_read_b64_tr_b16 %[n3], %[b1] offset:%[far]\n\t"
+#define NM_SMFMAC32_AREADS(MREAD)                                                          \
+  "ds_read_b128 %[na0], %[aa]\n\t"                                                         \
+  "ds_read_b128 %[na1], %[aa] offset:%[as1]\n\t"                                           \
+  "ds_read_b128 %[na2], %[aa] offset:%[as2]\n\t"                                           \
+  "ds_read_b128 %[na3], %[aa] offset:%[as3]\n\t"                                           \
+  MREAD " %[ni0], %[ma]\n\t"                                                               \
+  MREAD " %[ni1], %[ma] offset:%[ms1]\n\t"                                                 \
+  MREAD " %[ni2], %[ma] offset:%[ms2]\n\t"                                                 \
+  MREAD " %[ni3], %[ma] offset:%[ms3]\n\t"
+#define NM_SMFMAC32_BOUTS                                                                  \
+  [n0] "=&v"(n[0]), [n1] "=&v"(n[1]), [n2] "=&v"(n[2]), [n3] "=&v"(n[3])
+#define NM_SMFMAC32_COUTS                                                                  \
+  [c0] "+a"(c0), [c1] "+a"(c1), [c2] "+a"(c2), [c3] "+a"(c3)
+#define NM_SMFMAC32_INS                                                                    \
+  [a0] "v"(a.v[0]), [a1] "v"(a.v[1]), [a2] "v"(a.v[2]), [a3] "v"(a.v[3]),                  \
+      [i0] "v"(a.ix[0]), [i1] "v"(a.ix[1]), [i2] "v"(a.ix[2]), [i3] "v"(a.ix[3]),          \
+      [b] "v"(b), [keep] "v"(keep), [b0] "v"(b0), [b1] "v"(b1), [far] "n"(kFar)
+
+template <bool BF16, int kFar>
+__device__ __forceinline__ void smfmac32_block(float16v_t& c0, float16v_t& c1, float16v_t& c2,
+                                               float16v_t& c3, const AFrags& a,
+                                               const short16_t& b, const short16_t& keep,
+                                               uint32_t b0, uint32_t b1, short4_t (&n)[4]) {
+  if constexpr (BF16)
+    asm volatile(NM_SMFMAC32_BREADS NM_SMFMAC32_OPS("v_smfmac_f32_32x32x32_bf16")
+                 : NM_SMFMAC32_BOUTS, NM_SMFMAC32_COUTS
+                 : NM_SMFMAC32_INS
+                 : "memory");
+  else
+    asm volatile(NM_SMFMAC32_BREADS NM_SMFMAC32_OPS("v_smfmac_f32_32x32x32_f16")
+                 : NM_SMFMAC32_BOUTS, NM_SMFMAC32_COUTS
+                 : NM_SMFMAC32_INS
+                 : "memory");
+}
+
+template <bool BF16, bool kPat12, int kFar, int kAStride, int kMStride>
+__device__ __forceinline__ void smfmac32_block_a(float16v_t& c0, float16v_t& c1, float16v_t& c2,
+                                                 float16v_t& c3, const AFrags& a,
+                                                 const short16_t& b, const short16_t& keep,
+                                                 uint32_t b0, uint32_t b1, short4_t (&n)[4],
+                                                 uint32_t aa, uint32_t ma, AFrags& na) {
+#define NM_SMFMAC32_A(OP, MREAD)                                                           \
+  asm volatile(NM_SMFMAC32_BREADS NM_SMFMAC32_AREADS(MREAD) NM_SMFMAC32_OPS(OP)            \
+               : NM_SMFMAC32_BOUTS, [na0] "=&v"(na.v[0]), [na1] "=&v"(na.v[1]),            \
+                 [na2] "=&v"(na.v[2]), [na3] "=&v"(na.v[3]), [ni0] "=&v"(na.ix[0]),        \
+                 [ni1] "=&v"(na.ix[1]), [ni2] "=&v"(na.ix[2]), [ni3] "=&v"(na.ix[3]),      \
+                 NM_SMFMAC32_COUTS                                                         \
+               : NM_SMFMAC32_INS, [aa] "v"(aa), [ma] "v"(ma), [as1] "n"(kAStride),         \
+                 [as2] "n"(2 * kAStride), [as3] "n"(3 * kAStride), [ms1] "n"(kMStride),    \
+                 [ms2] "n"(2 * kMStride), [ms3] "n"(3 * kMStride)                          \
+               : "memory")
+  if constexpr (BF16) {
+    if constexpr (kPat12)
+      NM_SMFMAC32_A("v_smfmac_f32_32x32x32_bf16", "ds_read_u8");
+    else
+      NM_SMFMAC32_A("v_smfmac_f32_32x32x32_bf16", "ds_read_u16");
+  } else {
+    if constexpr (kPat12)
+      NM_SMFMAC32_A("v_smfmac_f32_32x32x32_f16", "ds_read_u8");
+    else
+      NM_SMFMAC32_A("v_smfmac_f32_32x32x32_f16", "ds_read_u16");
+  }
+#undef NM_SMFMAC32_A
+}
+#undef NM_SMFMAC32_OPS
+#undef NM_SMFMAC32_BREADS
+#undef NM_SMFMAC32_AREADS
+#undef NM_SMFMAC32_BOUTS
+#undef NM_SMFMAC32_COUTS
+#undef NM_SMFMAC32_INS
+
+__device__ __forceinline__ short16_t join_b(const short4_t (&n)[4]) {
+  return __builtin_shufflevector(__builtin_shufflevector(n[0], n[1], 0, 1, 2, 3, 4, 5, 6, 7),
+                                 __builtin_shufflevector(n[2], n[3], 0, 1, 2, 3, 4, 5, 6, 7),
+                                 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+}
+
+template <bool kPat12>
+__device__ __forceinline__ void widen_frags(AFrags& a) {
+  if constexpr (kPat12) {
+#pragma unroll
+    for (int fm = 0; fm < 4; ++fm) a.ix[fm] = widen_1_2(a.ix[fm]);
+  }
+}
+
+// Stores one wave's 128 x 64 block of fp32 accumulators (32x32 fragments: fm = 0..3 down,
+// f = 0..1 across; lane l holds column 32f + l % 32 and rows 8(i/4) + 4(l/32) + i%4 of
+// fragment fm) to Y as YT.  Each 32-row slab passes through `lds` (this wave's own
+// kEpilogueBytes, row-major) so that Y is written in 16-byte pieces of one row -- eight
+// 16-bit or four fp32 outputs -- instead of one output per store.  T % 8 == 0, so a piece
+// is either wholly inside the matrix or wholly outside.  A wave's LDS accesses complete in
+// order, so the reads see this slab's writes and the next slab's writes follow the reads.
+constexpr int kEpilogueBytes = 32 * (64 * 4 + 16);
+template <int YT>
+__device__ __forceinline__ void store_block_128x64(const float16v_t (&acc)[4][2], uint8_t* lds,
+                                                   void* Y, int row0, int col0, int R, int T,
+                                                   int lane) {
+  constexpr int kEB = YT == kF32 ? 4 : 2;   // bytes per output
+  constexpr int kPitch = 64 * kEB + 16;     // LDS row pitch, padded against bank conflicts
+  constexpr int kPer16 = 16 / kEB;          // outputs per 16-byte piece
+  constexpr int kRowPieces = 64 / kPer16;
+  static_assert(32 * kPitch <= kEpilogueBytes, "slab fits the wave's LDS region");
+  const int l32 = lane & 31, q = lane >> 5;
+  uint8_t* y = static_cast<uint8_t*>(Y);
+#pragma unroll
+  for (int fm = 0; fm < 4; ++fm) {
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        uint8_t* d = lds + (8 * (i / 4) + 4 * q + (i % 4)) * kPitch + (32 * f + l32) * kEB;
+        const float v = acc[fm][f][i];
+        if constexpr (YT == kF32)
+          *reinterpret_cast<float*>(d) = v;
+        else if constexpr (YT == kBF16)
+          *reinterpret_cast<uint16_t*>(d) = (uint16_t)f32_to_bf16(v);
+        else
+          *reinterpret_cast<uint16_t*>(d) = (uint16_t)f32_to_f16(v);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 32 * kRowPieces / 64; ++k) {
+      const int pc = k * 64 + lane, r = pc / kRowPieces, cp = pc % kRowPieces;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds + r * kPitch + cp * 16);
+      const int row = row0 + 32 * fm + r, col = col0 + cp * kPer16;
+      if (row < R && col < T)
+        *reinterpret_cast<u32x4_t*>(y + ((int64_t)row * T + col) * kEB) = v;
+    }
+  }
+}
+
+template <bool BF16, bool kPat12, bool kBlocked, int YT, int BM, int BN, int WAVES_M, int WAVES_N,
+          int STAGES>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
+    smfmac32_spmm_kernel(const uint16_t* __restrict__ values, const uint32_t* __restrict__ meta,
+                         const uint16_t* __restrict__ X, void* __restrict__ Y, int R, int K,
+                         int T, TileMap map) {
+  using TL = Smfmac32Tile<BM, BN, WAVES_M, WAVES_N, STAGES>;
+  constexpr int kStages = STAGES;
+  constexpr int kRB = TL::kXRowBytes;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+
+  int tile_m, tile_n;
+  if (!map.tile_of(blockIdx.x, tile_m, tile_n)) return;  // whole workgroup, before any load
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int m0 = tile_m * BM, t0 = tile_n * BN;
+  const int l32 = lane & 31, q = lane >> 5, l16 = lane & 15, blk = lane >> 4;
+  const int nsteps = K / kKStep;
+  const int last_step = nsteps - 1;
+
+  // ---- direct-load sources and LDS destinations (as in smfmac_spmm_kernel, except that
+  // X chunks are swizzled in 32-byte pairs: logical pair p of K row r sits at p ^ (r & 7))
+  const uint8_t* xg = reinterpret_cast<const uint8_t*>(X);
+  const uint8_t* vg = reinterpret_cast<const uint8_t*>(values);
+  const uint8_t* mg = reinterpret_cast<const uint8_t*>(meta);
+  int64_t x_src[TL::kXLoads];
+  uint32_t x_dst[TL::kXLoads];
+#pragma unroll
+  for (int j = 0; j < TL::kXLoads; ++j) {
+    const int w1k = j * TL::kWaves + wave;
+    const int slot = w1k * 64 + lane;
+    const int r = slot / TL::kXChunks, pc = slot % TL::kXChunks;
+    const int lc = 2 * ((pc >> 1) ^ (r & 7)) + (pc & 1);
+    int col = t0 + 8 * lc;
+    col = col < T ? col : 0;  // columns past T: any valid address (outputs past T only)
+    x_src[j] = ((int64_t)r * T + col) * 2;
+    x_dst[j] = (uint32_t)(w1k * 1024);
+  }
+  int64_t a_src[TL::kALoads];
+  uint32_t a_dst[TL::kALoads];
+#pragma unroll
+  for (int j = 0; j < TL::kALoads; ++j) {
+    const int b16 = j * TL::kWaves + wave;
+    a_src[j] = values_source<kBlocked>(m0, 16 * b16, lane, R, K, nsteps);
+    a_dst[j] = (uint32_t)(TL::kXBytes + b16 * 1024);
+  }
+  int64_t m_src[TL::kMLoads];
+  uint32_t m_dst[TL::kMLoads];
+#pragma unroll
+  for (int j = 0; j < TL::kMLoads; ++j) {
+    const int b32 = j * TL::kWaves + wave;
+    m_src[j] = meta_source<kBlocked, kPat12>(m0, 32 * b32, lane, R, K, nsteps);
+    m_dst[j] = (uint32_t)(TL::kXBytes + TL::kABytes + b32 * 256);
+  }
+  // The direct loads of one step, numbered 0 .. kLoads-1 (X, then values, then
+  // metadata); issue_part<P> issues the P-th quarter of them.  The main loop spreads a
+  // step's loads over its four smfmac blocks: issued all at once, right after the
+  // barrier, they would hold every wave in the load-issue queue while the matrix cores
+  // sit idle.
+  auto issue_part = [&](auto part, int step) {
+    constexpr int P = decltype(part)::value;
+    constexpr int j0 = P * TL::kLoads / 4, j1 = (P + 1) * TL::kLoads / 4;
+    step = step < last_step ? step : last_step;
+    uint8_t* st = smem + (step % kStages) * TL::kStageBytes;
+    const int64_t kx = (int64_t)step * kKStep * T * 2;
+    const int64_t ka = (int64_t)step * values_step_bytes<kBlocked>();
+    const int64_t km = (int64_t)step * meta_step_bytes<kBlocked, kPat12>();
+#pragma unroll
+    for (int j = 0; j < TL::kLoads; ++j) {
+      if (j < j0 || j >= j1) continue;
+      if (j < TL::kXLoads) {
+        global_to_lds<16>(xg + x_src[j] + kx, st + x_dst[j]);
+      } else if (j < TL::kXLoads + TL::kALoads) {
+        const int a = j - TL::kXLoads;
+        global_to_lds<16>(vg + a_src[a] + ka, st + a_dst[a]);
+      } else {
+        const int mi = j - TL::kXLoads - TL::kALoads;
+        global_to_lds<4>(mg + m_src[mi] + km, st + m_dst[mi]);
+      }
+    }
+  };
+  auto issue_step = [&](int step) {
+    issue_part(std::integral_constant<int, 0>{}, step);
+    issue_part(std::integral_constant<int, 1>{}, step);
+    issue_part(std::integral_constant<int, 2>{}, step);
+    issue_part(std::integral_constant<int, 3>{}, step);
+  };
+
+  // ---- per-lane LDS read offsets within a stage ----
+  // A fragment fm of substep t: tile row ia + 32 fm, 16-byte chunk (2t + q) ^ ((ia >> 2) & 3)
+  const int ia = wm * TL::kWM + l32;
+  const int aswz = (ia >> 2) & 3;
+  const uint32_t a_rd0 = (uint32_t)(TL::kXBytes + ia * 64 + (((0 + q) ^ aswz) << 4));
+  const uint32_t a_rd1 = (uint32_t)(TL::kXBytes + ia * 64 + (((2 + q) ^ aswz) << 4));
+  // index word of substep t: unit 2t + q of the row's step (2:4: 16-bit units; 1:2: bytes)
+  constexpr int kMT = kPat12 ? 2 : 4;  // byte distance from substep 0 to substep 1
+  const uint32_t m_rd0 = (uint32_t)(TL::kXBytes + TL::kABytes + ia * 8 + (kPat12 ? q : 2 * q));
+  const uint32_t m_rd1 = m_rd0 + kMT;
+  // B fragment (t, f): K rows 32t + {8q..8q+7, 16+8q..16+8q+7}; lane i of a 16-lane block
+  // reads K row kb + (i >> 2), columns 4 (i & 3) .. +3 of the block's 16 columns
+  const int rb = 8 * q + (l16 >> 2);
+  uint32_t b_rd[2][2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const int lp = (wn * TL::kWN + 32 * f + 16 * (blk & 1)) / 16;  // logical 32-byte pair
+    b_rd[f][0] = (uint32_t)(rb * kRB + ((lp ^ (l16 >> 2)) << 5) + 8 * (l16 & 3));
+    b_rd[f][1] = (uint32_t)((rb + 4) * kRB + ((lp ^ (4 + (l16 >> 2))) << 5) + 8 * (l16 & 3));
+  }
+  constexpr int kFar = 16 * kRB;  // K rows +16
+  constexpr int kSub = 32 * kRB;  // K rows +32 (substep 1)
+  constexpr int kAS = 32 * 64;    // next 32-row A fragment
+  constexpr int kMS = 32 * 8;     // its index words
+
+  float16v_t acc[4][2];
+#pragma unroll
+  for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+    for (int f = 0; f < 2; ++f) acc[fm][f] = float16v_t{};
+
+  // ---- prologue: steps 0 .. kStages-2 in flight; substep-0 A and the first B fragment of
+  // step 0 in registers; step 1 landed and visible ----
+#pragma unroll
+  for (int k = 0; k < kStages - 1; ++k) issue_step(k);
+  const uint32_t smem_base = lds_addr(smem);
+  auto stage_of = [&](int step) {
+    return smem_base + (uint32_t)((step % kStages) * TL::kStageBytes);
+  };
+  AFrags a0, a1;
+  short16_t b, bk = short16_t{};
+  short4_t n[4];
+  wait_loads_and_barrier<(kStages - 2) * TL::kLoads>();  // step 0 landed
+  {
+    const uint32_t st = stage_of(0);
+    lds_a_fragments4<kPat12, kAS, kMS>(st + a_rd0, st + m_rd0, a0.v[0], a0.v[1], a0.v[2],
+                                       a0.v[3], a0.ix[0], a0.ix[1], a0.ix[2], a0.ix[3]);
+    b = lds_b_fragment<kFar>(st + b_rd[0][0], st + b_rd[0][1]);
+    widen_frags<kPat12>(a0);
+  }
+  wait_loads_and_barrier<(kStages - 3) * TL::kLoads>();  // step 1 landed
+
+  for (int s = 0; s < nsteps; ++s) {
+    // invariant: steps s and s+1 are in LDS and visible; a0 holds substep-0 A of step s;
+    // b holds B(0,0) of step s; no wave reads stage (s-1) % kStages any more
+    const int ahead = s + kStages - 1;  // the step whose loads this iteration issues
+    const uint32_t st = stage_of(s), sn = stage_of(s + 1);
+    // block (0,0): reads B(0,1)
+    smfmac32_block<BF16, kFar>(acc[0][0], acc[1][0], acc[2][0], acc[3][0], a0, b, bk,
+                               st + b_rd[1][0], st + b_rd[1][1], n);
+    bk = b;
+    b = join_b(n);
+    issue_part(std::integral_constant<int, 0>{}, ahead);
+    // block (0,1): reads B(1,0) and substep-1 A of this step
+    smfmac32_block_a<BF16, kPat12, kFar, kAS, kMS>(
+        acc[0][1], acc[1][1], acc[2][1], acc[3][1], a0, b, bk, st + b_rd[0][0] + kSub,
+        st + b_rd[0][1] + kSub, n, st + a_rd1, st + m_rd1, a1);
+    bk = b;
+    b = join_b(n);
+    widen_frags<kPat12>(a1);
+    issue_part(std::integral_constant<int, 1>{}, ahead);
+    // block (1,0): reads B(1,1)
+    smfmac32_block<BF16, kFar>(acc[0][0], acc[1][0], acc[2][0], acc[3][0], a1, b, bk,
+                               st + b_rd[1][0] + kSub, st + b_rd[1][1] + kSub, n);
+    bk = b;
+    b = join_b(n);
+    issue_part(std::integral_constant<int, 2>{}, ahead);
+    // block (1,1): reads next step's B(0,0) and substep-0 A (the last step reads a stage
+    // that holds no useful data; the values are never used)
+    smfmac32_block_a<BF16, kPat12, kFar, kAS, kMS>(
+        acc[0][1], acc[1][1], acc[2][1], acc[3][1], a1, b, bk, sn + b_rd[0][0],
+        sn + b_rd[0][1], n, sn + a_rd0, sn + m_rd0, a0);
+    bk = b;
+    b = join_b(n);
+    widen_frags<kPat12>(a0);
+    issue_part(std::integral_constant<int, 3>{}, ahead);
+    // step s+2 landed (s+3 .. s+kStages-1 may still be in flight); after the barrier no
+    // wave reads stage s % kStages any more
+    wait_loads_and_barrier<(kStages - 3) * TL::kLoads>();
+  }
+  // drain the loads issued for steps past the end (every wave, then the barrier: no direct
+  // load or fragment read touches LDS afterwards), and give the last smfmac results time
+  // to land before plain instructions read the accumulators
+  wait_loads_and_barrier<0>();
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  static_assert(TL::kWaves * kEpilogueBytes <= kStages * TL::kStageBytes, "epilogue LDS");
+  store_block_128x64<YT>(acc, smem + wave * kEpilogueBytes, Y, m0 + wm * TL::kWM,
+                         t0 + wn * TL::kWN, R, T, lane);
+}
+
+// ===========================================================================
+// Wave-specialised form of the 32x32x32 kernel.  Each SIMD runs one consumer wave (LDS
+// fragment reads and smfmac blocks, exactly as in smfmac32_spmm_kernel) and one producer
+// wave (direct global -> LDS loads only).  A wave that issues direct loads stalls whenever
+// the load queue is full; with the loads in their own waves those stalls no longer hold up
+// a matrix core.  One barrier per step hands the stages over:
+//   producer, iteration s: load step s+S-1 into the stage step s-1 used, then wait until
+//     step s+2 has landed, then the barrier;
+//   consumer, iteration s: compute step s (the last block also reads the first fragments
+//     of step s+1), then the barrier.
+// After barrier s, steps s+1 and s+2 are in LDS and visible, and no wave reads the stage
+// of step s any more.  Both kinds of wave pass the same nsteps + 1 barriers.
+// ===========================================================================
+template <int BM, int BN, int CWAVES_M, int CWAVES_N, int PWAVES, int STAGES>
+struct WsTile {
+  static constexpr int kConsumers = CWAVES_M * CWAVES_N;
+  static constexpr int kProducers = PWAVES;
+  static constexpr int kThreads = 64 * (kConsumers + kProducers);
+  static constexpr int kStages = STAGES;
+  static constexpr int kWM = BM / CWAVES_M;
+  static constexpr int kWN = BN / CWAVES_N;
+  static constexpr int kXRowBytes = BN * 2;
+  static constexpr int kXChunks = BN / 8;
+  static constexpr int kXBytes = kKStep * kXRowBytes;
+  static constexpr int kABytes = BM * 64;
+  static constexpr int kMBytes = BM * 8;
+  static constexpr int kStageBytes = kXBytes + kABytes + kMBytes;
+  static constexpr int kXLoads = kXBytes / 1024 / kProducers;  // per producer wave and step
+  static constexpr int kALoads = kABytes / 1024 / kProducers;
+  static constexpr int kMLoads = kMBytes / 256 / kProducers;
+  static constexpr int kLoads = kXLoads + kALoads + kMLoads;
+  static_assert(kWM == 128 && kWN == 64, "a consumer owns 128 x 64 outputs");
+  static_assert(kXBytes % (1024 * kProducers) == 0 && kABytes % (1024 * kProducers) == 0 &&
+                    kMBytes % (256 * kProducers) == 0,
+                "every producer issues the same number of direct loads per step");
+  static_assert(BN >= 128, "the X swizzle needs at least 8 column pairs per row");
+  static_assert(kStages >= 3 && (kStages - 2) * kLoads <= 63, "vmcnt budget");
+  static_assert(kStages * kStageBytes <= 160 * 1024, "LDS budget");
+};
+
+template <bool BF16, bool kPat12, bool kBlocked, int YT, int BM, int BN, int CWAVES_M,
+          int CWAVES_N, int PWAVES, int STAGES>
+__global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
+    smfmac_ws_spmm_kernel(const uint16_t* __restrict__ values, const uint32_t* __restrict__ meta,
+                          const uint16_t* __restrict__ X, void* __restrict__ Y, int R, int K,
+                          int T, TileMap map) {
+  using TL = WsTile<BM, BN, CWAVES_M, CWAVES_N, PWAVES, STAGES>;
+  constexpr int kStages = STAGES;
+  constexpr int kRB = TL::kXRowBytes;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+
+  int tile_m, tile_n;
+  if (!map.tile_of(blockIdx.x, tile_m, tile_n)) return;  // whole workgroup, before any load
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m0 = tile_m * BM, t0 = tile_n * BN;
+  const int nsteps = K / kKStep;
+  const int last_step = nsteps - 1;
+
+  if (wave >= TL::kConsumers) {
+    // ---------------- producer ----------------
+    const int pw = wave - TL::kConsumers;
+    const uint8_t* xg = reinterpret_cast<const uint8_t*>(X);
+    const uint8_t* vg = reinterpret_cast<const uint8_t*>(values);
+    const uint8_t* mg = reinterpret_cast<const uint8_t*>(meta);
+    int64_t x_src[TL::kXLoads];
+    uint32_t x_dst[TL::kXLoads];
+#pragma unroll
+    for (int j = 0; j < TL::kXLoads; ++j) {
+      const int w1k = j * TL::kProducers + pw;  // 1 KB window of the X tile
+      const int slot = w1k * 64 + lane;
+      const int r = slot / TL::kXChunks, pc = slot % TL::kXChunks;
+      const int lc = 2 * ((pc >> 1) ^ (r & 7)) + (pc & 1);  // 32-byte pair swizzle
+      int col = t0 + 8 * lc;
+      col = col < T ? col : 0;  // columns past T: any valid address (outputs past T only)
+      x_src[j] = ((int64_t)r * T + col) * 2;
+      x_dst[j] = (uint32_t)(w1k * 1024);
+    }
+    int64_t a_src[TL::kALoads];
+    uint32_t a_dst[TL::kALoads];
+#pragma unroll
+    for (int j = 0; j < TL::kALoads; ++j) {
+      const int b16 = j * TL::kProducers + pw;
+      a_src[j] = values_source<kBlocked>(m0, 16 * b16, lane, R, K, nsteps);
+      a_dst[j] = (uint32_t)(TL::kXBytes + b16 * 1024);
+    }
+    int64_t m_src[TL::kMLoads];
+    uint32_t m_dst[TL::kMLoads];
+#pragma unroll
+    for (int j = 0; j < TL::kMLoads; ++j) {
+      const int b32 = j * TL::kProducers + pw;
+      m_src[j] = meta_source<kBlocked, kPat12>(m0, 32 * b32, lane, R, K, nsteps);
+      m_dst[j] = (uint32_t)(TL::kXBytes + TL::kABytes + b32 * 256);
+    }
+    auto issue_step = [&](int step) {
+      step = step < last_step ? step : last_step;  // past the end: re-read the last step
+      uint8_t* st = smem + (step % kStages) * TL::kStageBytes;
+      const int64_t kx = (int64_t)step * kKStep * T * 2;
+      const int64_t ka = (int64_t)step * values_step_bytes<kBlocked>();
+      const int64_t km = (int64_t)step * meta_step_bytes<kBlocked, kPat12>();
+#pragma unroll
+      for (int j = 0; j < TL::kXLoads; ++j) global_to_lds<16>(xg + x_src[j] + kx, st + x_dst[j]);
+#pragma unroll
+      for (int j = 0; j < TL::kALoads; ++j) global_to_lds<16>(vg + a_src[j] + ka, st + a_dst[j]);
+#pragma unroll
+      for (int j = 0; j < TL::kMLoads; ++j) global_to_lds<4>(mg + m_src[j] + km, st + m_dst[j]);
+    };
+#pragma unroll
+    for (int k = 0; k < kStages - 1; ++k) issue_step(k);
+    wait_loads_and_barrier<(kStages - 3) * TL::kLoads>();  // steps 0 and 1 landed
+    for (int s = 0; s < nsteps; ++s) {
+      issue_step(s + kStages - 1);
+      wait_loads_and_barrier<(kStages - 3) * TL::kLoads>();  // step s+2 landed
+    }
+    // loads past the end have landed before the consumers reuse LDS for the epilogue
+    wait_loads_and_barrier<0>();
+    return;
+  }
+
+  // ---------------- consumer ----------------
+  const int wm = wave / CWAVES_N, wn = wave % CWAVES_N;
+  const int l32 = lane & 31, q = lane >> 5, l16 = lane & 15, blk = lane >> 4;
+  const int ia = wm * TL::kWM + l32;
+  const int aswz = (ia >> 2) & 3;
+  const uint32_t a_rd0 = (uint32_t)(TL::kXBytes + ia * 64 + (((0 + q) ^ aswz) << 4));
+  const uint32_t a_rd1 = (uint32_t)(TL::kXBytes + ia * 64 + (((2 + q) ^ aswz) << 4));
+  constexpr int kMT = kPat12 ? 2 : 4;
+  const uint32_t m_rd0 = (uint32_t)(TL::kXBytes + TL::kABytes + ia * 8 + (kPat12 ? q : 2 * q));
+  const uint32_t m_rd1 = m_rd0 + kMT;
+  const int rb = 8 * q + (l16 >> 2);
+  uint32_t b_rd[2][2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const int lp = (wn * TL::kWN + 32 * f + 16 * (blk & 1)) / 16;
+    b_rd[f][0] = (uint32_t)(rb * kRB + ((lp ^ (l16 >> 2)) << 5) + 8 * (l16 & 3));
+    b_rd[f][1] = (uint32_t)((rb + 4) * kRB + ((lp ^ (4 + (l16 >> 2))) << 5) + 8 * (l16 & 3));
+  }
+  constexpr int kFar = 16 * kRB;
+  constexpr int kSub = 32 * kRB;
+  constexpr int kAS = 32 * 64;
+  constexpr int kMS = 32 * 8;
+
+  float16v_t acc[4][2];
+#pragma unroll
+  for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+    for (int f = 0; f < 2; ++f) acc[fm][f] = float16v_t{};
+
+  const uint32_t smem_base = lds_addr(smem);
+  auto stage_of = [&](int step) {
+    return smem_base + (uint32_t)((step % kStages) * TL::kStageBytes);
+  };
+  AFrags a0, a1;
+  short16_t b, bk = short16_t{};
+  short4_t n[4];
+  asm volatile("s_barrier" ::: "memory");  // steps 0 and 1 landed
+  {
+    const uint32_t st = stage_of(0);
+    lds_a_fragments4<kPat12, kAS, kMS>(st + a_rd0, st + m_rd0, a0.v[0], a0.v[1], a0.v[2],
+                                       a0.v[3], a0.ix[0], a0.ix[1], a0.ix[2], a0.ix[3]);
+    b = lds_b_fragment<kFar>(st + b_rd[0][0], st + b_rd[0][1]);
+    widen_frags<kPat12>(a0);
+  }
+  for (int s = 0; s < nsteps; ++s) {
+    const uint32_t st = stage_of(s), sn = stage_of(s + 1);
+    smfmac32_block<BF16, kFar>(acc[0][0], acc[1][0], acc[2][0], acc[3][0], a0, b, bk,
+                               st + b_rd[1][0], st + b_rd[1][1], n);
+    bk = b;
+    b = join_b(n);
+    smfmac32_block_a<BF16, kPat12, kFar, kAS, kMS>(
+        acc[0][1], acc[1][1], acc[2][1], acc[3][1], a0, b, bk, st + b_rd[0][0] + kSub,
+        st + b_rd[0][1] + kSub, n, st + a_rd1, st + m_rd1, a1);
+    bk = b;
+    b = join_b(n);
+    widen_frags<kPat12>(a1);
+    smfmac32_block<BF16, kFar>(acc[0][0], acc[1][0], acc[2][0], acc[3][0], a1, b, bk,
+                               st + b_rd[1][0] + kSub, st + b_rd[1][1] + kSub, n);
+    bk = b;
+    b = join_b(n);
+    // the last step reads a stage that holds no useful data; the values are never used
+    smfmac32_block_a<BF16, kPat12, kFar, kAS, kMS>(
+        acc[0][1], acc[1][1], acc[2][1], acc[3][1], a1, b, bk, sn + b_rd[0][0],
+        sn + b_rd[0][1], n, sn + a_rd0, sn + m_rd0, a0);
+    bk = b;
+    b = join_b(n);
+    widen_frags<kPat12>(a0);
+    asm volatile("s_barrier" ::: "memory");  // step s+2 landed; stage of step s released
+  }
+  // the producers' last loads have landed (final barrier), and the last smfmac results
+  // get time to land before plain instructions read the accumulators
+  asm volatile("s_barrier\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  static_assert(TL::kConsumers * kEpilogueBytes <= kStages * TL::kStageBytes, "epilogue LDS");
+  store_block_128x64<YT>(acc, smem + wave * kEpilogueBytes, Y, m0 + wm * TL::kWM,
+                         t0 + wn * TL::kWN, R, T, lane);
+}
+
+// ===========================================================================
 // Shape-agnostic kernel: any N:M, any dtype, any shape with K % M == 0.
 // ===========================================================================
 constexpr int kGT = 64;   // tile rows and columns
 constexpr int kGK = 32;   // K per step (a multiple of every supported M)
 
-template <int DT, int YT, int N, int M>
+template <int DT, int YT, int N, int M, bool kBlocked>
 __global__ void __launch_bounds__(256) generic_spmm_kernel(const void* __restrict__ values,
                                                            const uint32_t* __restrict__ meta,
                                                            const void* __restrict__ X,
@@ -449,14 +1069,24 @@ __global__ void __launch_bounds__(256) generic_spmm_kernel(const void* __restric
 #pragma unroll
       for (int e = 0; e < M; ++e) o[e] = 0.f;
       if (row < R && g < gpr) {
-        const uint32_t* mrow = meta + row * wpr;
 #pragma unroll
         for (int j = 0; j < N; ++j) {
-          const int64_t bit = (g * N + j) * b;
-          uint64_t window = mrow[bit / 32];
-          if ((bit % 32) + b > 32) window |= (uint64_t)mrow[bit / 32 + 1] << 32;
+          // field f of the row: value index and metadata bit in the chosen layout
+          const int64_t f = g * N + j;
+          int64_t vi, bit;
+          if constexpr (kBlocked) {
+            constexpr int64_t V = 64 / M * N;  // values per row and 64-wide step
+            const int64_t rr = ((row >> 4) * (K / 64) + f / V) * 16 + (row & 15);
+            vi = rr * V + f % V;
+            bit = rr * V * b + (f % V) * b;
+          } else {
+            vi = row * (gpr * N) + f;
+            bit = row * wpr * 32 + f * b;
+          }
+          uint64_t window = meta[bit / 32];
+          if ((bit % 32) + b > 32) window |= (uint64_t)meta[bit / 32 + 1] << 32;
           const int p = (int)((window >> (bit % 32)) & ((1u << b) - 1u));
-          const float v = load_as_f32<DT>(values, row * (gpr * N) + g * N + j);
+          const float v = load_as_f32<DT>(values, vi);
 #pragma unroll
           for (int e = 0; e < M; ++e) o[e] = (p == e) ? v : o[e];
         }
@@ -502,14 +1132,15 @@ __global__ void zero_fill_kernel(uint32_t* __restrict__ p, int64_t words, int64_
   if (i == words && tail_halves) reinterpret_cast<uint16_t*>(p + words)[0] = 0;
 }
 
-template <int DT, int YT>
+template <int DT, int YT, bool kBlocked>
 hipError_t run_generic(const void* values, const uint32_t* meta, int64_t R, int64_t K, int n,
                        int m, const void* X, int64_t T, void* Y, hipStream_t s) {
   const dim3 grid((unsigned)((T + kGT - 1) / kGT), (unsigned)((R + kGT - 1) / kGT));
-#define NM_G(NN, MM)                                                                         \
-  if (n == NN && m == MM) {                                                                  \
-    generic_spmm_kernel<DT, YT, NN, MM><<<grid, 256, 0, s>>>(values, meta, X, Y, R, K, T); \
-    return hipGetLastError();                                                                \
+#define NM_G(NN, MM)                                                                        \
+  if (n == NN && m == MM) {                                                                 \
+    generic_spmm_kernel<DT, YT, NN, MM, kBlocked><<<grid, 256, 0, s>>>(values, meta, X, Y, R, \
+                                                                       K, T);               \
+    return hipGetLastError();                                                               \
   }
   NM_G(1, 2) NM_G(2, 2)
   NM_G(1, 4) NM_G(2, 4) NM_G(3, 4) NM_G(4, 4)
@@ -517,6 +1148,14 @@ hipError_t run_generic(const void* values, const uint32_t* meta, int64_t R, int6
   NM_G(5, 8) NM_G(6, 8) NM_G(7, 8) NM_G(8, 8)
 #undef NM_G
   return hipErrorInvalidValue;
+}
+
+template <int DT, int YT>
+hipError_t run_generic_layout(const void* values, const uint32_t* meta, int64_t R, int64_t K,
+                              int n, int m, bool blocked, const void* X, int64_t T, void* Y,
+                              hipStream_t s) {
+  return blocked ? run_generic<DT, YT, true>(values, meta, R, K, n, m, X, T, Y, s)
+                 : run_generic<DT, YT, false>(values, meta, R, K, n, m, X, T, Y, s);
 }
 
 // XCDs of the current device: MI355X (gfx950) has 8, with 32 compute units each.
@@ -536,13 +1175,29 @@ int xcd_count() {
   return v;
 }
 
-// Tile configurations of the matrix-core kernel, and the choice between them.
-template <bool BF16, bool kPat12, int YT, int BM, int BN, int WM_, int WN_, int ST_>
+// One matrix-core launch: kernel K32 (32x32x32 blocks) or the 16x16x64 kernel, with the
+// XCD-aware tile order.
+// Kernel forms: 0 = 16x16x64 smfmac kernel, 1 = 32x32x32 blocks, 2 = 32x32x32 blocks with
+// producer waves (PW of them).
+template <int KIND, int BM, int BN, int WM_, int WN_, int PW, int ST_>
+using TileOf = std::conditional_t<
+    KIND == 0, SmfmacTile<BM, BN, WM_, WN_, ST_>,
+    std::conditional_t<KIND == 1, Smfmac32Tile<BM, BN, WM_, WN_, ST_>,
+                       WsTile<BM, BN, WM_, WN_, PW, ST_>>>;
+
+template <bool BF16, bool kPat12, bool kBlocked, int YT, int KIND, int BM, int BN, int WM_,
+          int WN_, int PW, int ST_>
 hipError_t launch_tile(const void* values, const uint32_t* meta, int64_t R, int64_t K,
                        const void* X, int64_t T, void* Y, hipStream_t s) {
-  using TL = SmfmacTile<BM, BN, WM_, WN_, ST_>;
+  using TL = TileOf<KIND, BM, BN, WM_, WN_, PW, ST_>;
   const int tiles_m = (int)((R + BM - 1) / BM), tiles_n = (int)((T + BN - 1) / BN);
-  auto kernel = smfmac_spmm_kernel<BF16, kPat12, YT, BM, BN, WM_, WN_, ST_>;
+  void (*kernel)(const uint16_t*, const uint32_t*, const uint16_t*, void*, int, int, int, TileMap);
+  if constexpr (KIND == 0)
+    kernel = smfmac_spmm_kernel<BF16, kPat12, kBlocked, YT, BM, BN, WM_, WN_, ST_>;
+  else if constexpr (KIND == 1)
+    kernel = smfmac32_spmm_kernel<BF16, kPat12, kBlocked, YT, BM, BN, WM_, WN_, ST_>;
+  else
+    kernel = smfmac_ws_spmm_kernel<BF16, kPat12, kBlocked, YT, BM, BN, WM_, WN_, PW, ST_>;
   const size_t lds = (size_t)ST_ * TL::kStageBytes;
   static const hipError_t attr =
       hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
@@ -561,29 +1216,36 @@ hipError_t launch_tile(const void* values, const uint32_t* meta, int64_t R, int6
   return hipGetLastError();
 }
 
-// Three tile shapes; the launch picks the one with the smallest estimated time: waves of
-// workgroups over the device (ceil(tiles / CUs)) times the tile's work divided by the
-// rate that shape sustains on long K loops (measured on MI355X, effective TFLOP/s).
+// Three tile shapes; the launch picks the one with the smallest estimated time: rounds of
+// workgroups over the device (ceil(tiles / CUs)) times the time of one tile, which is its
+// work at the rate that shape sustains on long K loops (measured on MI355X with normally
+// distributed data, effective TFLOP/s over the whole device) plus a fixed per-tile cost
+// (pipeline fill and the epilogue).
 struct TileChoice {
   int bm, bn;
   double rate;
 };
-constexpr TileChoice kTiles[3] = {{256, 256, 1300.0}, {256, 128, 1030.0}, {128, 128, 800.0}};
+constexpr int kNumTiles = 3;
+constexpr TileChoice kTiles[kNumTiles] = {{256, 256, 1300.0}, {256, 128, 1450.0},
+                                          {128, 128, 850.0}};
+constexpr double kTileFixedUs = 3.0;
 
-int pick_tile(int64_t R, int64_t T) {
+int pick_tile(int64_t R, int64_t K, int64_t T) {
   // NM_SPMM_TILE=0/1/2 pins one shape (used by the tests to cover every shape)
   if (const char* e = getenv("NM_SPMM_TILE")) {
-    if (e[0] >= '0' && e[0] <= '2' && e[1] == 0) return e[0] - '0';
+    if (e[0] >= '0' && e[0] < '0' + kNumTiles && e[1] == 0) return e[0] - '0';
   }
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess)
-    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (cus <= 0) cus = 256;
   int best = 0;
   double best_t = 0;
-  for (int i = 0; i < 3; ++i) {
-    const int64_t tiles = ((R + kTiles[i].bm - 1) / kTiles[i].bm) * ((T + kTiles[i].bn - 1) / kTiles[i].bn);
-    const double t = (double)((tiles + cus - 1) / cus) * kTiles[i].bm * kTiles[i].bn / kTiles[i].rate;
+  for (int i = 0; i < kNumTiles; ++i) {
+    const TileChoice& c = kTiles[i];
+    const int64_t tiles = ((R + c.bm - 1) / c.bm) * ((T + c.bn - 1) / c.bn);
+    const double tile_us = 2.0 * c.bm * c.bn * (double)K / (c.rate * 1e6 / cus) + kTileFixedUs;
+    const double t = (double)((tiles + cus - 1) / cus) * tile_us;
     if (i == 0 || t < best_t) {
       best = i;
       best_t = t;
@@ -592,20 +1254,34 @@ int pick_tile(int64_t R, int64_t T) {
   return best;
 }
 
-template <bool BF16, bool kPat12, int YT>
+template <bool BF16, bool kPat12, bool kBlocked, int YT>
 hipError_t run_smfmac(const void* values, const uint32_t* meta, int64_t R, int64_t K,
                       const void* X, int64_t T, void* Y, hipStream_t s) {
-  switch (pick_tile(R, T)) {
-    case 0: return launch_tile<BF16, kPat12, YT, 256, 256, 2, 4, 3>(values, meta, R, K, X, T, Y, s);
-    case 1: return launch_tile<BF16, kPat12, YT, 256, 128, 4, 2, 4>(values, meta, R, K, X, T, Y, s);
-    default: return launch_tile<BF16, kPat12, YT, 128, 128, 2, 2, 4>(values, meta, R, K, X, T, Y, s);
+  switch (pick_tile(R, K, T)) {
+    case 0:
+      return launch_tile<BF16, kPat12, kBlocked, YT, 1, 256, 256, 2, 4, 0, 3>(values, meta, R, K,
+                                                                             X, T, Y, s);
+    case 1:
+      return launch_tile<BF16, kPat12, kBlocked, YT, 2, 256, 128, 2, 2, 4, 4>(values, meta, R, K,
+                                                                             X, T, Y, s);
+    default:
+      return launch_tile<BF16, kPat12, kBlocked, YT, 0, 128, 128, 2, 2, 0, 4>(values, meta, R, K,
+                                                                             X, T, Y, s);
   }
+}
+
+template <bool BF16, bool kPat12, int YT>
+hipError_t run_smfmac_layout(const void* values, const uint32_t* meta, int64_t R, int64_t K,
+                             bool blocked, const void* X, int64_t T, void* Y, hipStream_t s) {
+  return blocked ? run_smfmac<BF16, kPat12, true, YT>(values, meta, R, K, X, T, Y, s)
+                 : run_smfmac<BF16, kPat12, false, YT>(values, meta, R, K, X, T, Y, s);
 }
 
 }  // namespace
 
 hipError_t launch_spmm(const void* values, const uint32_t* meta, int64_t R, int64_t K, int n,
-                       int m, const void* X, int64_t T, int dt, void* Y, int y_dt, hipStream_t s) {
+                       int m, bool blocked, const void* X, int64_t T, int dt, void* Y, int y_dt,
+                       hipStream_t s) {
   if (R == 0 || T == 0) return hipSuccess;
   const bool pat24 = (n == 2 && m == 4), pat12 = (n == 1 && m == 2);
   // the matrix-core kernel addresses A, its metadata and X with 32-bit byte offsets
@@ -613,9 +1289,10 @@ hipError_t launch_spmm(const void* values, const uint32_t* meta, int64_t R, int6
                            T < (1 << 30) && K < (1 << 30);
   if (dt != kF32 && (pat24 || pat12) && tiled_shape) {
     const bool yf32 = y_dt == kF32;
-#define NM_S(BF, P12)                                                                        \
-  return yf32 ? run_smfmac<BF, P12, kF32>(values, meta, R, K, X, T, Y, s)                    \
-              : run_smfmac<BF, P12, (BF ? kBF16 : kF16)>(values, meta, R, K, X, T, Y, s);
+#define NM_S(BF, P12)                                                                       \
+  return yf32 ? run_smfmac_layout<BF, P12, kF32>(values, meta, R, K, blocked, X, T, Y, s)   \
+              : run_smfmac_layout<BF, P12, (BF ? kBF16 : kF16)>(values, meta, R, K, blocked, X, \
+                                                                T, Y, s);
     if (dt == kBF16) {
       if (pat24) { NM_S(true, false) } else { NM_S(true, true) }
     } else {
@@ -631,12 +1308,15 @@ hipError_t launch_spmm(const void* values, const uint32_t* meta, int64_t R, int6
         static_cast<uint32_t*>(Y), words, tail_halves);
     return hipGetLastError();
   }
-  if (dt == kF32) return run_generic<kF32, kF32>(values, meta, R, K, n, m, X, T, Y, s);
+  if (dt == kF32)
+    return run_generic_layout<kF32, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s);
   if (dt == kBF16)
-    return y_dt == kF32 ? run_generic<kBF16, kF32>(values, meta, R, K, n, m, X, T, Y, s)
-                        : run_generic<kBF16, kBF16>(values, meta, R, K, n, m, X, T, Y, s);
-  return y_dt == kF32 ? run_generic<kF16, kF32>(values, meta, R, K, n, m, X, T, Y, s)
-                      : run_generic<kF16, kF16>(values, meta, R, K, n, m, X, T, Y, s);
+    return y_dt == kF32
+               ? run_generic_layout<kBF16, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s)
+               : run_generic_layout<kBF16, kBF16>(values, meta, R, K, n, m, blocked, X, T, Y, s);
+  return y_dt == kF32
+             ? run_generic_layout<kF16, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s)
+             : run_generic_layout<kF16, kF16>(values, meta, R, K, n, m, blocked, X, T, Y, s);
 }
 
 }  // namespace nm

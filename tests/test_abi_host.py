@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     L = nm.lib()
     for name in header_functions():
         assert hasattr(L, name), name
-    assert L.nm_abi_version() == 1
+    assert L.nm_abi_version() == nm.ABI_VERSION == 2
 
 
 @needs_lib
@@ -48,7 +48,7 @@ def test_library_has_no_undefined_symbols_of_its_own():
 
 @needs_lib
 def test_status_strings():
-    for code in range(8):
+    for code in range(9):
         s = nm.status_str(code)
         assert s and s != "unknown status"
     assert nm.status_str(99) == "unknown status"
@@ -68,10 +68,21 @@ def test_size_helpers_reject_bad_arguments():
     assert L.nm_meta_words_per_row(6, 2, 4) == -1
     assert L.nm_meta_words_per_row(16, 2, 16) == -1  # M = 16 is not a GPU pattern
     assert L.nm_meta_words_per_row(16, 0, 4) == -1
-    assert L.nm_values_bytes(3072, 768, 2, 4, nm.NM_BF16) == 3072 * 384 * 2
-    assert L.nm_values_bytes(64, 128, 2, 4, nm.NM_F32) == 64 * 64 * 4
-    assert L.nm_values_bytes(64, 130, 2, 4, nm.NM_F32) == 0
-    assert L.nm_values_bytes(64, 128, 2, 4, 7) == 0
+    ROWS, BLOCKED = nm.LAYOUTS["rows"], nm.LAYOUTS["blocked"]
+    assert L.nm_values_bytes(3072, 768, 2, 4, nm.NM_BF16, ROWS) == 3072 * 384 * 2
+    assert L.nm_values_bytes(64, 128, 2, 4, nm.NM_F32, ROWS) == 64 * 64 * 4
+    assert L.nm_values_bytes(64, 130, 2, 4, nm.NM_F32, ROWS) == 0
+    assert L.nm_values_bytes(64, 128, 2, 4, 7, ROWS) == 0
+    assert L.nm_values_bytes(64, 128, 2, 4, nm.NM_BF16, 2) == 0
+    # blocked: rows padded to 16, K in steps of 64
+    assert L.nm_values_bytes(17, 128, 2, 4, nm.NM_BF16, BLOCKED) == 32 * 64 * 2
+    assert L.nm_values_bytes(17, 96, 2, 4, nm.NM_BF16, BLOCKED) == 0
+    assert L.nm_meta_bytes(17, 128, 2, 4, ROWS) == 17 * 4 * 4
+    assert L.nm_meta_bytes(17, 128, 2, 4, BLOCKED) == 32 * 2 * 8
+    assert L.nm_meta_bytes(17, 128, 4, 8, BLOCKED) == 32 * 2 * 12
+    assert L.nm_meta_bytes(17, 128, 1, 2, BLOCKED) == 32 * 2 * 4
+    assert L.nm_meta_bytes(17, 128, 3, 8, BLOCKED) == 32 * 2 * 9
+    assert L.nm_meta_bytes(17, 96, 2, 4, BLOCKED) == 0
 
 
 FAKE = 0x10000  # aligned, never dereferenced: validation fails before any device access
@@ -90,16 +101,21 @@ FAKE = 0x10000  # aligned, never dereferenced: validation fails before any devic
     (dict(R=-1), "shape"),
     (dict(W=FAKE + 8), "align"),
     (dict(out=FAKE + 4), "align"),
+    (dict(layout=2), "layout"),
+    (dict(layout=1, K=96), "layout"),
 ])
 def test_mask_compress_argument_errors(case, expect):
     L = nm.lib()
-    a = dict(W=FAKE, dt=nm.NM_BF16, R=64, K=128, n=2, m=4, out=FAKE)
+    a = dict(W=FAKE, dt=nm.NM_BF16, R=64, K=128, n=2, m=4, out=FAKE, layout=0)
     a.update(case)
-    code = L.nm_mask(a["W"], a["dt"], a["R"], a["K"], a["n"], a["m"], a["out"], None)
+    if "layout" not in case:  # nm_mask has no layout argument
+        code = L.nm_mask(a["W"], a["dt"], a["R"], a["K"], a["n"], a["m"], a["out"], None)
+        assert nm.STATUS[code] == expect
+    code = L.nm_compress(a["W"], a["dt"], a["R"], a["K"], a["n"], a["m"], a["layout"], a["out"],
+                         FAKE, None)
     assert nm.STATUS[code] == expect
-    code = L.nm_compress(a["W"], a["dt"], a["R"], a["K"], a["n"], a["m"], a["out"], FAKE, None)
-    assert nm.STATUS[code] == expect
-    code = L.nm_decompress(a["W"], FAKE, a["dt"], a["R"], a["K"], a["n"], a["m"], a["out"], None)
+    code = L.nm_decompress(a["W"], FAKE, a["dt"], a["R"], a["K"], a["n"], a["m"], a["layout"],
+                           a["out"], None)
     assert nm.STATUS[code] == expect
 
 
@@ -114,14 +130,16 @@ def test_mask_compress_argument_errors(case, expect):
     (dict(n=3, m=5), "pattern"),
     (dict(Y=FAKE + 2), "align"),
     (dict(meta=FAKE + 4), "align"),
+    (dict(layout=7), "layout"),
+    (dict(layout=1, K=96), "layout"),
 ])
 def test_spmm_argument_errors(case, expect):
     L = nm.lib()
-    a = dict(values=FAKE, meta=FAKE, R=64, K=128, n=2, m=4, X=FAKE, T=32, dt=nm.NM_BF16,
-             Y=FAKE, y_dt=nm.NM_BF16)
+    a = dict(values=FAKE, meta=FAKE, R=64, K=128, n=2, m=4, layout=0, X=FAKE, T=32,
+             dt=nm.NM_BF16, Y=FAKE, y_dt=nm.NM_BF16)
     a.update(case)
-    code = L.nm_spmm(a["values"], a["meta"], a["R"], a["K"], a["n"], a["m"], a["X"], a["T"],
-                     a["dt"], a["Y"], a["y_dt"], None)
+    code = L.nm_spmm(a["values"], a["meta"], a["R"], a["K"], a["n"], a["m"], a["layout"], a["X"],
+                     a["T"], a["dt"], a["Y"], a["y_dt"], None)
     assert nm.STATUS[code] == expect
 
 
@@ -129,8 +147,22 @@ def test_spmm_argument_errors(case, expect):
 def test_empty_arrays_may_be_null():
     L = nm.lib()
     assert L.nm_mask(None, nm.NM_BF16, 0, 128, 2, 4, None, None) == 0
-    assert L.nm_compress(None, nm.NM_F16, 16, 0, 2, 4, None, None, None) == 0
-    assert L.nm_spmm(FAKE, FAKE, 8, 128, 2, 4, FAKE, 0, nm.NM_BF16, None, nm.NM_BF16, None) == 0
+    for layout in (0, 1):
+        assert L.nm_compress(None, nm.NM_F16, 16, 0, 2, 4, layout, None, None, None) == 0
+        assert L.nm_compress(None, nm.NM_F16, 0, 64, 2, 4, layout, None, None, None) == 0
+        assert L.nm_spmm(FAKE, FAKE, 8, 128, 2, 4, layout, FAKE, 0, nm.NM_BF16, None, nm.NM_BF16,
+                         None) == 0
+
+
+def test_binding_shapes_follow_the_layout_definition():
+    """compressed_shapes() agrees with the header's byte counts (no GPU needed)."""
+    if not os.path.exists(nm.LIB_PATH):
+        pytest.skip("libnm.so not built")
+    for R, K, n, m in [(17, 128, 2, 4), (300, 256, 4, 8), (16, 64, 1, 2), (5, 192, 3, 8)]:
+        (G, S, r16, V), (G2, S2, words) = nm.compressed_shapes(R, K, n, m, "blocked")
+        assert (G, S, r16, V) == ((R + 15) // 16, K // 64, 16, 64 // m * n) and (G2, S2) == (G, S)
+        b = {2: 1, 4: 2, 8: 3}[m]
+        assert 4 * words == 16 * V * b // 8
 
 
 def test_product_path_does_not_load_the_oracle():

@@ -20,7 +20,7 @@ import torch
 import masking_sparse_gemm_amd as nm
 import oracle
 import synth
-from tests.helpers import as_bits, encode, normwise_rel_err
+from tests.helpers import as_bits, blocked_from_rows, encode, normwise_rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -80,6 +80,30 @@ def check_select(W: np.ndarray, dtype: str, n: int, m: int, label: str = ""):
     dec = nm.decompress(vals, meta, n, m, K)
     dec_o = oracle.decompress(vals_o, meta_o, dtype, R, K, n, m)
     assert np.array_equal(host_bits(dec), as_bits(dec_o)), f"decompress {label}"
+    if K % 64 == 0:
+        check_select_blocked(W, dtype, n, m, vals_o, meta_o, dec_o, label)
+    return vals, meta, vals_o, meta_o
+
+
+def check_select_blocked(W, dtype, n, m, vals_o, meta_o, dec_o=None, label=""):
+    """compress / decompress in the blocked layout == the oracle's arrays regrouped, bitwise."""
+    R, K = W.shape
+    vb, mb = nm.compress(dev(W, dtype), n, m, layout="blocked")
+    vb_o, mb_o = blocked_from_rows(as_bits(vals_o), meta_o, R, K, n, m)
+    assert np.array_equal(host_bits(vb), vb_o), f"blocked values {label}"
+    assert np.array_equal(host_bits(mb), mb_o), f"blocked meta {label}"
+    if dec_o is None:
+        dec_o = oracle.decompress(vals_o, meta_o, dtype, R, K, n, m)
+    dec = nm.decompress(vb, mb, n, m, K, layout="blocked", rows=R)
+    assert np.array_equal(host_bits(dec), as_bits(dec_o)), f"blocked decompress {label}"
+    return vb, mb
+
+
+def compressed(W, dtype, n, m, layout):
+    """The checked compressed pair in `layout` and the oracle's (rows) pair."""
+    vals, meta, vals_o, meta_o = check_select(W, dtype, n, m)
+    if layout == "blocked":
+        vals, meta = check_select_blocked(W, dtype, n, m, vals_o, meta_o)
     return vals, meta, vals_o, meta_o
 
 
@@ -114,7 +138,8 @@ def tie_heavy(rng, shape, dtype, scale=1.0):
 
 SELECT_PATTERNS = [(1, 2), (2, 2), (1, 4), (2, 4), (3, 4), (4, 4), (1, 8), (2, 8), (3, 8), (4, 8),
                    (7, 8), (8, 8)]
-SELECT_SHAPES = [(7, 128), (33, 96), (5, 24), (64, 8), (3, 1024), (1, 64 * 8)]
+SELECT_SHAPES = [(7, 128), (33, 96), (5, 24), (64, 8), (3, 1024), (1, 64 * 8), (33, 192),
+                 (17, 64)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
@@ -163,6 +188,8 @@ def test_select_empty():
         assert vals.shape == (R, K // 2) and meta.shape == (R, K // 32)
         assert nm.mask(W, 2, 4).shape == (R, K)
         assert nm.decompress(vals, meta, 2, 4, K).shape == (R, K)
+        vb, mb = nm.compress(W, 2, 4, layout="blocked")
+        assert nm.decompress(vb, mb, 2, 4, K, layout="blocked", rows=R).shape == (R, K)
 
 
 # ---------------------------------------------------------------------------
@@ -178,70 +205,79 @@ PRODUCT_SHAPES = [(200, 384, 264), (130, 256, 136), (16, 128, 8), (257, 128, 520
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("n,m", [(2, 4), (1, 2), (4, 8), (3, 4), (1, 8)])
 @pytest.mark.parametrize("yf32", [False, True])
-def test_spmm_elementwise(dtype, n, m, yf32):
+@pytest.mark.parametrize("layout", ["rows", "blocked"])
+def test_spmm_elementwise(dtype, n, m, yf32, layout):
     rng = np.random.default_rng(7 + n + 3 * m)
     for R, K, T in PRODUCT_SHAPES:
-        if K % m:
+        if K % m or (layout == "blocked" and K % 64):
             continue
         W = encode(rng.standard_normal((R, K)), dtype)
         X = encode(rng.standard_normal((K, T)), dtype)
-        vals, meta, vals_o, meta_o = check_select(W, dtype, n, m)
+        vals, meta, vals_o, meta_o = compressed(W, dtype, n, m, layout)
         y_dtype = "f32" if yf32 else dtype
-        Y = nm.spmm(vals, meta, dev(X, dtype), n, m, out_dtype=TORCH_DT[y_dtype])
+        Y = nm.spmm(vals, meta, dev(X, dtype), n, m, out_dtype=TORCH_DT[y_dtype], layout=layout,
+                    rows=R)
         y_ref, s = reference_product(vals_o, meta_o, R, K, n, m, X, dtype)
-        check_product(Y, y_ref, s, K // m * n, dtype, y_dtype, f"{R}x{K}x{T} {n}:{m}")
+        check_product(Y, y_ref, s, K // m * n, dtype, y_dtype, f"{R}x{K}x{T} {n}:{m} {layout}")
 
 
 @pytest.mark.parametrize("tile", ["0", "1", "2"])
 @pytest.mark.parametrize("dtype,n,m", [("bf16", 2, 4), ("f16", 1, 2)])
-def test_spmm_every_tile_shape(tile, dtype, n, m, monkeypatch):
+@pytest.mark.parametrize("layout", ["rows", "blocked"])
+def test_spmm_every_tile_shape(tile, dtype, n, m, layout, monkeypatch):
     """Each matrix-core tile shape, pinned, on shapes with ragged row and column tiles."""
     monkeypatch.setenv("NM_SPMM_TILE", tile)
     rng = np.random.default_rng(61)
-    for R, K, T in [(300, 192, 264), (520, 128, 136), (16, 64, 8)]:
+    for R, K, T in [(300, 192, 264), (520, 128, 136), (16, 64, 8), (33, 640, 392)]:
         W = encode(rng.standard_normal((R, K)), dtype)
         X = encode(rng.standard_normal((K, T)), dtype)
-        vals, meta, vals_o, meta_o = check_select(W, dtype, n, m)
-        Y = nm.spmm(vals, meta, dev(X, dtype), n, m, out_dtype=torch.float32)
+        vals, meta, vals_o, meta_o = compressed(W, dtype, n, m, layout)
+        Y = nm.spmm(vals, meta, dev(X, dtype), n, m, out_dtype=torch.float32, layout=layout,
+                    rows=R)
         y_ref, s = reference_product(vals_o, meta_o, R, K, n, m, X, dtype)
-        check_product(Y, y_ref, s, K // m * n, dtype, "f32", f"tile {tile} {R}x{K}x{T}")
+        check_product(Y, y_ref, s, K // m * n, dtype, "f32", f"tile {tile} {R}x{K}x{T} {layout}")
 
 
 @pytest.mark.parametrize("n,m", [(2, 4), (1, 2), (4, 8), (1, 4)])
-def test_spmm_f32_elementwise(n, m):
+@pytest.mark.parametrize("layout", ["rows", "blocked"])
+def test_spmm_f32_elementwise(n, m, layout):
     rng = np.random.default_rng(31)
     for R, K, T in PRODUCT_SHAPES:
-        if K % m:
+        if K % m or (layout == "blocked" and K % 64):
             continue
         W = rng.standard_normal((R, K)).astype(np.float32)
         X = rng.standard_normal((K, T)).astype(np.float32)
-        vals, meta, vals_o, meta_o = check_select(W, "f32", n, m)
-        Y = nm.spmm(vals, meta, dev(X, "f32"), n, m)
+        vals, meta, vals_o, meta_o = compressed(W, "f32", n, m, layout)
+        Y = nm.spmm(vals, meta, dev(X, "f32"), n, m, layout=layout, rows=R)
         y_ref, s = reference_product(vals_o, meta_o, R, K, n, m, X, "f32")
-        check_product(Y, y_ref, s, K // m * n, "f32", "f32", f"{R}x{K}x{T}")
+        check_product(Y, y_ref, s, K // m * n, "f32", "f32", f"{R}x{K}x{T} {layout}")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("n,m", [(2, 4), (1, 2)])
-def test_spmm_identity_is_exact(dtype, n, m):
+@pytest.mark.parametrize("layout", ["rows", "blocked"])
+def test_spmm_identity_is_exact(dtype, n, m, layout):
     """X = I: every output is one product by 1, so Y equals the masked weight bitwise."""
     rng = np.random.default_rng(41)
-    K = 256
-    W = encode(rng.standard_normal((72, K)), dtype)
-    vals, meta = nm.compress(dev(W, dtype), n, m)
-    Y = nm.spmm(vals, meta, dev(encode(np.eye(K), dtype), dtype), n, m)
-    assert np.array_equal(host_bits(Y), host_bits(nm.decompress(vals, meta, n, m, K)))
+    R, K = 72, 256
+    W = encode(rng.standard_normal((R, K)), dtype)
+    vals, meta = nm.compress(dev(W, dtype), n, m, layout=layout)
+    Y = nm.spmm(vals, meta, dev(encode(np.eye(K), dtype), dtype), n, m, layout=layout, rows=R)
+    dec = nm.decompress(vals, meta, n, m, K, layout=layout, rows=R)
+    assert np.array_equal(host_bits(Y), host_bits(dec))
 
 
-def test_spmm_integers_are_exact():
+@pytest.mark.parametrize("layout", ["rows", "blocked"])
+def test_spmm_integers_are_exact(layout):
     """Small integers: every partial sum is exact in fp32, so any order gives the oracle's value."""
     rng = np.random.default_rng(43)
     R, K, T = 96, 512, 72
     for dtype in ["bf16", "f16", "f32"]:
         W = encode(rng.integers(-8, 9, (R, K)).astype(np.float64), dtype)
         X = encode(rng.integers(-8, 9, (K, T)).astype(np.float64), dtype)
-        vals, meta = nm.compress(dev(W, dtype), 2, 4)
-        Y = nm.spmm(vals, meta, dev(X, dtype), 2, 4, out_dtype=torch.float32)
+        vals, meta = nm.compress(dev(W, dtype), 2, 4, layout=layout)
+        Y = nm.spmm(vals, meta, dev(X, dtype), 2, 4, out_dtype=torch.float32, layout=layout,
+                    rows=R)
         vals_o, meta_o = oracle.compress(W, dtype, 2, 4)
         assert np.array_equal(host_f64(Y), oracle.spmm(vals_o, meta_o, R, K, 2, 4, X, dtype))
 
@@ -258,6 +294,20 @@ def test_spmm_empty():
     me = torch.zeros((4, 0), dtype=torch.int32, device="cuda")
     y = nm.spmm(ve, me, torch.zeros((0, 10), dtype=torch.bfloat16, device="cuda"))
     assert y.shape == (4, 10) and not y.float().abs().sum().item()
+    # blocked: no rows, no columns, and an empty contraction (K = 0)
+    vb, mb = nm.compress(torch.zeros((0, 128), dtype=torch.bfloat16, device="cuda"), 2, 4,
+                         layout="blocked")
+    assert nm.spmm(vb, mb, x, layout="blocked", rows=0).shape == (0, 16)
+    vb, mb = nm.compress(torch.ones((20, 128), dtype=torch.bfloat16, device="cuda"), 2, 4,
+                         layout="blocked")
+    y = nm.spmm(vb, mb, torch.zeros((128, 0), dtype=torch.bfloat16, device="cuda"),
+                layout="blocked", rows=20)
+    assert y.shape == (20, 0)
+    vb, mb = nm.compress(torch.zeros((20, 0), dtype=torch.bfloat16, device="cuda"), 2, 4,
+                         layout="blocked")
+    y = nm.spmm(vb, mb, torch.zeros((0, 10), dtype=torch.bfloat16, device="cuda"),
+                layout="blocked", rows=20)
+    assert y.shape == (20, 10) and not y.float().abs().sum().item()
 
 
 def sample_points(rng, R, T, count=1500):
@@ -277,18 +327,24 @@ def test_spmm_full_workloads_sampled(name):
     Xd = dev(X, w.dtype)
     rng = np.random.default_rng(55)
     for n, m in w.patterns:
-        print(f"[spmm] {name} {w.R}x{w.K}x{w.T} {n}:{m}", flush=True)
-        vals, meta = nm.compress(dev(W, w.dtype), n, m)
         vals_o, meta_o = oracle.compress(W, w.dtype, n, m)
-        assert np.array_equal(host_bits(vals), as_bits(vals_o))
-        assert np.array_equal(host_bits(meta), meta_o)
-        Y = nm.spmm(vals, meta, Xd, n, m)
         rs, ts = sample_points(rng, w.R, w.T)
         y_ref = oracle.spmm_sample(vals_o, meta_o, w.R, w.K, n, m, X, w.dtype, rs, ts)
         s = oracle.spmm_sample(abs_bits(vals_o, w.dtype), meta_o, w.R, w.K, n, m,
                                abs_bits(X, w.dtype), w.dtype, rs, ts)
-        y = Y[torch.from_numpy(rs).cuda(), torch.from_numpy(ts).cuda()]
-        check_product(y, y_ref, s, w.K // m * n, w.dtype, w.dtype, f"{name} {n}:{m}")
-        if name == "toy_f32":  # small enough to compare every output
-            y_full, s_full = reference_product(vals_o, meta_o, w.R, w.K, n, m, X, w.dtype)
-            check_product(Y, y_full, s_full, w.K // m * n, w.dtype, w.dtype, "toy full")
+        for layout in ["blocked", "rows"]:
+            print(f"[spmm] {name} {w.R}x{w.K}x{w.T} {n}:{m} {layout}", flush=True)
+            vals, meta = nm.compress(dev(W, w.dtype), n, m, layout=layout)
+            if layout == "rows":
+                assert np.array_equal(host_bits(vals), as_bits(vals_o))
+                assert np.array_equal(host_bits(meta), meta_o)
+            else:
+                vb_o, mb_o = blocked_from_rows(as_bits(vals_o), meta_o, w.R, w.K, n, m)
+                assert np.array_equal(host_bits(vals), vb_o)
+                assert np.array_equal(host_bits(meta), mb_o)
+            Y = nm.spmm(vals, meta, Xd, n, m, layout=layout, rows=w.R)
+            y = Y[torch.from_numpy(rs).cuda(), torch.from_numpy(ts).cuda()]
+            check_product(y, y_ref, s, w.K // m * n, w.dtype, w.dtype, f"{name} {n}:{m} {layout}")
+            if name == "toy_f32":  # small enough to compare every output
+                y_full, s_full = reference_product(vals_o, meta_o, w.R, w.K, n, m, X, w.dtype)
+                check_product(Y, y_full, s_full, w.K // m * n, w.dtype, w.dtype, "toy full")
