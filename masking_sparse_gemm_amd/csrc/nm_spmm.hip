@@ -1039,6 +1039,237 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
 }
 
 // ===========================================================================
+// 4:8 on dense matrix cores (no structured-sparse instruction takes 4:8).  The blocked
+// layout's values and metadata reach LDS exactly as for 2:4 (4:8 also keeps half the
+// values; its metadata is 12 bytes per row and 64-wide step), and each consumer lane
+// expands one 4:8 group into the dense A operand of v_mfma_f32_32x32x16: the A operand of a
+// lane is 8 consecutive K of one row, i.e. exactly one group.  The 4 stored values become
+// 8 slots with four v_perm_b32 byte selects whose selectors come from a 256-entry table
+// indexed by the group's keep mask (one bit per kept position).  Inside a 64-wide step the
+// contraction order is permuted so that lane half q of substep t takes group 4q + t (K
+// 32q + 8t .. +7): a lane's four groups of a step are then one contiguous 32-byte run of
+// values and 48 contiguous metadata bits, and B is read at the matching K rows.
+// Wave-specialised like smfmac_ws_spmm_kernel: producer waves load, consumer waves expand
+// and multiply, one barrier per step.
+// ===========================================================================
+template <int BM, int BN, int CWAVES_M, int CWAVES_N, int PWAVES, int STAGES>
+struct Ws48Tile {
+  static constexpr int kConsumers = CWAVES_M * CWAVES_N;
+  static constexpr int kProducers = PWAVES;
+  static constexpr int kThreads = 64 * (kConsumers + kProducers);
+  static constexpr int kStages = STAGES;
+  static constexpr int kWM = BM / CWAVES_M;
+  static constexpr int kWN = BN / CWAVES_N;
+  static constexpr int kXRowBytes = BN * 2;
+  static constexpr int kXChunks = BN / 8;
+  static constexpr int kXBytes = kKStep * kXRowBytes;
+  static constexpr int kABytes = BM * 64;
+  static constexpr int kMRow = 12;  // metadata bytes per row and step
+  static constexpr int kMBytes = BM * kMRow;
+  static constexpr int kStageBytes = kXBytes + kABytes + kMBytes;
+  static constexpr int kLutBytes = 256 * 16;
+  static constexpr int kXLoads = kXBytes / 1024 / kProducers;
+  static constexpr int kALoads = kABytes / 1024 / kProducers;
+  static constexpr int kMLoads = kMBytes / 256 / kProducers;
+  static constexpr int kLoads = kXLoads + kALoads + kMLoads;
+  static_assert(kWM == 128 && kWN == 64, "a consumer owns 128 x 64 outputs");
+  static_assert(kXBytes % (1024 * kProducers) == 0 && kABytes % (1024 * kProducers) == 0 &&
+                    kMBytes % (256 * kProducers) == 0,
+                "every producer issues the same number of direct loads per step");
+  static_assert(BN >= 128, "the X swizzle needs at least 8 column pairs per row");
+  static_assert(kStages >= 3 && (kStages - 2) * kLoads <= 63, "vmcnt budget");
+  static_assert(kStages * kStageBytes + kLutBytes <= 160 * 1024, "LDS budget");
+};
+
+template <bool BF16>
+__device__ __forceinline__ float16v_t mfma32x32x16(const u32x4_t& a, const u32x4_t& b,
+                                                   const float16v_t& c) {
+  if constexpr (BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+template <bool BF16, int YT, int BM, int BN, int CWAVES_M, int CWAVES_N, int PWAVES, int STAGES>
+__global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
+    mfma48_ws_spmm_kernel(const uint16_t* __restrict__ values, const uint32_t* __restrict__ meta,
+                          const uint16_t* __restrict__ X, void* __restrict__ Y, int R, int K,
+                          int T, TileMap map) {
+  using TL = Ws48Tile<BM, BN, CWAVES_M, CWAVES_N, PWAVES, STAGES>;
+  constexpr int kStages = STAGES;
+  constexpr int kRB = TL::kXRowBytes;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+
+  int tile_m, tile_n;
+  if (!map.tile_of(blockIdx.x, tile_m, tile_n)) return;  // whole workgroup, before any load
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m0 = tile_m * BM, t0 = tile_n * BN;
+  const int nsteps = K / kKStep;
+  const int last_step = nsteps - 1;
+  const int last_group = ((R + 15) >> 4) - 1;
+
+  if (wave >= TL::kConsumers) {
+    // ---------------- producer ----------------
+    const int pw = wave - TL::kConsumers;
+    const uint8_t* xg = reinterpret_cast<const uint8_t*>(X);
+    const uint8_t* vg = reinterpret_cast<const uint8_t*>(values);
+    const uint8_t* mg = reinterpret_cast<const uint8_t*>(meta);
+    int64_t x_src[TL::kXLoads];
+    uint32_t x_dst[TL::kXLoads];
+#pragma unroll
+    for (int j = 0; j < TL::kXLoads; ++j) {
+      const int w1k = j * TL::kProducers + pw;
+      const int slot = w1k * 64 + lane;
+      const int r = slot / TL::kXChunks, pc = slot % TL::kXChunks;
+      const int lc = 2 * ((pc >> 1) ^ (r & 7)) + (pc & 1);
+      int col = t0 + 8 * lc;
+      col = col < T ? col : 0;
+      x_src[j] = ((int64_t)r * T + col) * 2;
+      x_dst[j] = (uint32_t)(w1k * 1024);
+    }
+    int64_t a_src[TL::kALoads];
+    uint32_t a_dst[TL::kALoads];
+#pragma unroll
+    for (int j = 0; j < TL::kALoads; ++j) {
+      const int b16 = j * TL::kProducers + pw;
+      a_src[j] = values_source<true>(m0, 16 * b16, lane, R, K, nsteps);
+      a_dst[j] = (uint32_t)(TL::kXBytes + b16 * 1024);
+    }
+    // metadata: the tile's 16 blocks of 16 rows x 12 bytes (192 bytes each, nsteps * 192
+    // bytes apart) land back to back, so tile row i sits at 12 i; load j covers bytes
+    // 256 j .. 256 j + 255 of that run, four per lane
+    int64_t m_src[TL::kMLoads];
+    uint32_t m_dst[TL::kMLoads];
+#pragma unroll
+    for (int j = 0; j < TL::kMLoads; ++j) {
+      const int w256 = j * TL::kProducers + pw;
+      const int o = w256 * 256 + 4 * lane;
+      int g = m0 / 16 + o / 192;
+      g = g < last_group ? g : last_group;
+      m_src[j] = (int64_t)g * nsteps * 192 + o % 192;
+      m_dst[j] = (uint32_t)(TL::kXBytes + TL::kABytes + w256 * 256);
+    }
+    auto issue_step = [&](int step) {
+      step = step < last_step ? step : last_step;
+      uint8_t* st = smem + (step % kStages) * TL::kStageBytes;
+      const int64_t kx = (int64_t)step * kKStep * T * 2;
+      const int64_t ka = (int64_t)step * 1024;
+      const int64_t km = (int64_t)step * 192;
+#pragma unroll
+      for (int j = 0; j < TL::kXLoads; ++j) global_to_lds<16>(xg + x_src[j] + kx, st + x_dst[j]);
+#pragma unroll
+      for (int j = 0; j < TL::kALoads; ++j) global_to_lds<16>(vg + a_src[j] + ka, st + a_dst[j]);
+#pragma unroll
+      for (int j = 0; j < TL::kMLoads; ++j) global_to_lds<4>(mg + m_src[j] + km, st + m_dst[j]);
+    };
+#pragma unroll
+    for (int k = 0; k < kStages - 1; ++k) issue_step(k);
+    wait_loads_and_barrier<(kStages - 3) * TL::kLoads>();  // steps 0 and 1 landed
+    for (int s = 0; s < nsteps; ++s) {
+      issue_step(s + kStages - 1);
+      wait_loads_and_barrier<(kStages - 3) * TL::kLoads>();  // step s+2 landed
+    }
+    wait_loads_and_barrier<0>();  // loads past the end landed before the epilogue
+    return;
+  }
+
+  // ---------------- consumer ----------------
+  // expansion table: entry m (a keep mask) holds the v_perm_b32 selectors of output dwords
+  // 0..3 (slots 2k, 2k+1): slot i kept -> bytes 2j, 2j+1 of the group's 8 value bytes, j the
+  // rank of i among the kept positions; not kept -> 0x0c (a zero byte)
+  uint8_t* lut = smem + kStages * TL::kStageBytes;
+  {
+    const int m = tid;  // 256 consumer threads, one entry each
+    u32x4_t e;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t sel = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int i = 2 * k + h;
+        const uint32_t j = __builtin_popcount(m & ((1u << i) - 1u));
+        const uint32_t pair = ((m >> i) & 1) ? (2 * j) | ((2 * j + 1) << 8) : 0x0c0cu;
+        sel |= pair << (16 * h);
+      }
+      e[k] = sel;
+    }
+    *reinterpret_cast<u32x4_t*>(lut + 16 * m) = e;
+  }
+  const int wm = wave / CWAVES_N, wn = wave % CWAVES_N;
+  const int l32 = lane & 31, q = lane >> 5, l16 = lane & 15, blk = lane >> 4;
+  const int ia = wm * TL::kWM + l32;
+  const int aswz = (ia >> 2) & 3;
+  // values: chunks 2q and 2q+1 of the row (groups 4q .. 4q+3)
+  const uint32_t a_rd0 = (uint32_t)(TL::kXBytes + ia * 64 + (((2 * q) ^ aswz) << 4));
+  const uint32_t a_rd1 = (uint32_t)(TL::kXBytes + ia * 64 + (((2 * q + 1) ^ aswz) << 4));
+  // metadata: bytes 6q .. 6q+5 of the row's 12, read as the dwords at 4q and 4q + 4
+  const uint32_t m_rd = (uint32_t)(TL::kXBytes + TL::kABytes + ia * TL::kMRow + 4 * q);
+  // B of substep t: K rows 32q + 8t + {0..3} and {4..7}
+  const int rb = 32 * q + (l16 >> 2);
+  uint32_t b_rd[2][2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const int lp = (wn * TL::kWN + 32 * f + 16 * (blk & 1)) / 16;
+    b_rd[f][0] = (uint32_t)(rb * kRB + ((lp ^ (l16 >> 2)) << 5) + 8 * (l16 & 3));
+    b_rd[f][1] = (uint32_t)((rb + 4) * kRB + ((lp ^ (4 + (l16 >> 2))) << 5) + 8 * (l16 & 3));
+  }
+  float16v_t acc[4][2];
+#pragma unroll
+  for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+    for (int f = 0; f < 2; ++f) acc[fm][f] = float16v_t{};
+
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // table written; steps 0, 1 landed
+  for (int s = 0; s < nsteps; ++s) {
+    const uint8_t* st = smem + (s % kStages) * TL::kStageBytes;
+    u32x4_t v[4][2];
+    uint64_t mb[4];
+#pragma unroll
+    for (int fm = 0; fm < 4; ++fm) {
+      v[fm][0] = *reinterpret_cast<const u32x4_t*>(st + a_rd0 + fm * 32 * 64);
+      v[fm][1] = *reinterpret_cast<const u32x4_t*>(st + a_rd1 + fm * 32 * 64);
+      const uint32_t* mp = reinterpret_cast<const uint32_t*>(st + m_rd + fm * 32 * TL::kMRow);
+      mb[fm] = ((uint64_t)mp[0] | ((uint64_t)mp[1] << 32)) >> (16 * q);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      u32x4_t a[4];
+#pragma unroll
+      for (int fm = 0; fm < 4; ++fm) {
+        const uint32_t bits = (uint32_t)(mb[fm] >> (12 * t)) & 0xfffu;
+        const uint32_t keep = (1u << (bits & 7)) | (1u << ((bits >> 3) & 7)) |
+                              (1u << ((bits >> 6) & 7)) | (1u << ((bits >> 9) & 7));
+        const u32x4_t sel = *reinterpret_cast<const u32x4_t*>(lut + 16 * keep);
+        const u32x4_t& vv = v[fm][t >> 1];
+        const uint32_t d0 = vv[2 * (t & 1)], d1 = vv[2 * (t & 1) + 1];
+        a[fm] = u32x4_t{__builtin_amdgcn_perm(d1, d0, sel[0]), __builtin_amdgcn_perm(d1, d0, sel[1]),
+                        __builtin_amdgcn_perm(d1, d0, sel[2]), __builtin_amdgcn_perm(d1, d0, sel[3])};
+      }
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_short4_t*)(st + b_rd[f][0] + 8 * t * kRB));
+        const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_short4_t*)(st + b_rd[f][1] + 8 * t * kRB));
+        const u32x4_t b = __builtin_bit_cast(
+            u32x4_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int fm = 0; fm < 4; ++fm) acc[fm][f] = mfma32x32x16<BF16>(a[fm], b, acc[fm][f]);
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // stage of step s released
+  }
+  asm volatile("s_barrier" ::: "memory");  // the producers' last loads have landed
+  static_assert(TL::kConsumers * kEpilogueBytes <= kStages * TL::kStageBytes, "epilogue LDS");
+  store_block_128x64<YT>(acc, smem + wave * kEpilogueBytes, Y, m0 + wm * TL::kWM,
+                         t0 + wn * TL::kWN, R, T, lane);
+}
+
+// ===========================================================================
 // Shape-agnostic kernel: any N:M, any dtype, any shape with K % M == 0.
 // ===========================================================================
 constexpr int kGT = 64;   // tile rows and columns
@@ -1270,6 +1501,32 @@ hipError_t run_smfmac(const void* values, const uint32_t* meta, int64_t R, int64
   }
 }
 
+// 4:8, 16-bit, blocked layout: dense matrix cores on expanded groups, 256 x 128 tiles.
+template <bool BF16, int YT>
+hipError_t run_mfma48(const void* values, const uint32_t* meta, int64_t R, int64_t K,
+                      const void* X, int64_t T, void* Y, hipStream_t s) {
+  constexpr int BM = 256, BN = 128, ST = 4;
+  using TL = Ws48Tile<BM, BN, 2, 2, 4, ST>;
+  const int tiles_m = (int)((R + BM - 1) / BM), tiles_n = (int)((T + BN - 1) / BN);
+  auto kernel = mfma48_ws_spmm_kernel<BF16, YT, BM, BN, 2, 2, 4, ST>;
+  const size_t lds = (size_t)ST * TL::kStageBytes + TL::kLutBytes;
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
+  TileMap map;
+  map.tiles_m = tiles_m;
+  map.tiles_n = tiles_n;
+  map.xcds = xcd_count();
+  map.per_xcd = (tiles_m * tiles_n + map.xcds - 1) / map.xcds;
+  map.gn = tiles_n < 4 ? tiles_n : 4;
+  map.gm = 32 / map.gn;
+  kernel<<<map.xcds * map.per_xcd, TL::kThreads, lds, s>>>(
+      static_cast<const uint16_t*>(values), meta, static_cast<const uint16_t*>(X), Y, (int)R,
+      (int)K, (int)T, map);
+  return hipGetLastError();
+}
+
 template <bool BF16, bool kPat12, int YT>
 hipError_t run_smfmac_layout(const void* values, const uint32_t* meta, int64_t R, int64_t K,
                              bool blocked, const void* X, int64_t T, void* Y, hipStream_t s) {
@@ -1287,6 +1544,13 @@ hipError_t launch_spmm(const void* values, const uint32_t* meta, int64_t R, int6
   // the matrix-core kernel addresses A, its metadata and X with 32-bit byte offsets
   const bool tiled_shape = K > 0 && K % kKStep == 0 && T % 8 == 0 && R < (1 << 30) &&
                            T < (1 << 30) && K < (1 << 30);
+  if (dt != kF32 && n == 4 && m == 8 && blocked && tiled_shape) {
+    if (dt == kBF16)
+      return y_dt == kF32 ? run_mfma48<true, kF32>(values, meta, R, K, X, T, Y, s)
+                          : run_mfma48<true, kBF16>(values, meta, R, K, X, T, Y, s);
+    return y_dt == kF32 ? run_mfma48<false, kF32>(values, meta, R, K, X, T, Y, s)
+                        : run_mfma48<false, kF16>(values, meta, R, K, X, T, Y, s);
+  }
   if (dt != kF32 && (pat24 || pat12) && tiled_shape) {
     const bool yf32 = y_dt == kF32;
 #define NM_S(BF, P12)                                                                       \
