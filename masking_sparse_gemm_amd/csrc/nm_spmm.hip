@@ -1050,7 +1050,11 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
 // 32q + 8t .. +7): a lane's four groups of a step are then one contiguous 32-byte run of
 // values and 48 contiguous metadata bits, and B is read at the matching K rows.
 // Wave-specialised like smfmac_ws_spmm_kernel: producer waves load, consumer waves expand
-// and multiply, one barrier per step.
+// and multiply, one barrier per step.  The producers, otherwise idle, also turn each
+// landed step's 3-bit positions into one keep-mask byte per group (their own LDS region
+// of the stage), which takes the mask building off the consumers' instruction stream.
+// Producer, iteration s: load step s+3, wait for step s+2, build its keep masks, barrier;
+// consumer, iteration s: step s (reading step s+1's keep masks for the next fragments).
 // ===========================================================================
 template <int BM, int BN, int CWAVES_M, int CWAVES_N, int PWAVES, int STAGES>
 struct Ws48Tile {
@@ -1066,7 +1070,8 @@ struct Ws48Tile {
   static constexpr int kABytes = BM * 64;
   static constexpr int kMRow = 12;  // metadata bytes per row and step
   static constexpr int kMBytes = BM * kMRow;
-  static constexpr int kStageBytes = kXBytes + kABytes + kMBytes;
+  static constexpr int kKmBytes = BM * 8;  // keep masks: one byte per group, 8 per row
+  static constexpr int kStageBytes = kXBytes + kABytes + kMBytes + kKmBytes;
   static constexpr int kLutBytes = 256 * 16;
   static constexpr int kXLoads = kXBytes / 1024 / kProducers;
   static constexpr int kALoads = kABytes / 1024 / kProducers;
@@ -1076,8 +1081,9 @@ struct Ws48Tile {
   static_assert(kXBytes % (1024 * kProducers) == 0 && kABytes % (1024 * kProducers) == 0 &&
                     kMBytes % (256 * kProducers) == 0,
                 "every producer issues the same number of direct loads per step");
+  static_assert(BM == 64 * kProducers, "one producer lane per tile row builds its keep masks");
   static_assert(BN >= 128, "the X swizzle needs at least 8 column pairs per row");
-  static_assert(kStages >= 3 && (kStages - 2) * kLoads <= 63, "vmcnt budget");
+  static_assert(kStages >= 4 && (kStages - 2) * kLoads <= 63, "vmcnt budget");
   static_assert(kStages * kStageBytes + kLutBytes <= 160 * 1024, "LDS budget");
 };
 
@@ -1140,13 +1146,15 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
       a_dst[j] = (uint32_t)(TL::kXBytes + b16 * 1024);
     }
     // metadata: the tile's 16 blocks of 16 rows x 12 bytes (192 bytes each, nsteps * 192
-    // bytes apart) land back to back, so tile row i sits at 12 i; load j covers bytes
-    // 256 j .. 256 j + 255 of that run, four per lane
+    // bytes apart) land back to back, so tile row i sits at 12 i; a load covers 256 bytes
+    // of that run, four per lane.  Producer pw loads the bytes of rows 64 pw .. 64 pw + 63
+    // itself, so its own wait covers the rows whose keep masks it builds.
+    static_assert(64 * TL::kMRow == 256 * TL::kMLoads, "a producer's rows are whole loads");
     int64_t m_src[TL::kMLoads];
     uint32_t m_dst[TL::kMLoads];
 #pragma unroll
     for (int j = 0; j < TL::kMLoads; ++j) {
-      const int w256 = j * TL::kProducers + pw;
+      const int w256 = pw * TL::kMLoads + j;
       const int o = w256 * 256 + 4 * lane;
       int g = m0 / 16 + o / 192;
       g = g < last_group ? g : last_group;
@@ -1166,12 +1174,49 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
 #pragma unroll
       for (int j = 0; j < TL::kMLoads; ++j) global_to_lds<4>(mg + m_src[j] + km, st + m_dst[j]);
     };
+    // keep masks of a landed step: lane l of producer pw takes tile row 64 pw + l (its 12
+    // metadata bytes = eight 12-bit groups of four 3-bit positions).  LDS accesses go
+    // through asm that waits for itself, so the compiler sees no LDS access that the
+    // in-flight direct loads might alias.
+    const uint32_t smem_base = lds_addr(smem);
+    const int krow = 64 * pw + lane;
+    auto build_keep_masks = [&](int step) {
+      const uint32_t st = smem_base + (uint32_t)((step % kStages) * TL::kStageBytes);
+      const uint32_t src = st + TL::kXBytes + TL::kABytes + krow * TL::kMRow;
+      const uint32_t dst = st + TL::kXBytes + TL::kABytes + TL::kMBytes + krow * 8;
+      uint32_t m0, m1, m2;
+      asm volatile(
+          "ds_read_b32 %0, %3\n\tds_read_b32 %1, %3 offset:4\n\tds_read_b32 %2, %3 offset:8\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(m0), "=&v"(m1), "=&v"(m2)
+          : "v"(src)
+          : "memory");
+      const uint64_t lo = (uint64_t)m0 | ((uint64_t)m1 << 32);   // groups 0 .. 4
+      const uint64_t hi = (uint64_t)m1 | ((uint64_t)m2 << 32);   // groups 5 .. 7 (from bit 32)
+      uint32_t k[2] = {0u, 0u};
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const uint32_t bits = (uint32_t)(g < 5 ? lo >> (12 * g) : hi >> (12 * g - 32)) & 0xfffu;
+        const uint32_t keep = (1u << (bits & 7)) | (1u << ((bits >> 3) & 7)) |
+                              (1u << ((bits >> 6) & 7)) | (1u << ((bits >> 9) & 7));
+        k[g >> 2] |= keep << (8 * (g & 3));
+      }
+      asm volatile("ds_write_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                   :
+                   : "v"(dst), "v"(u32x2_t{k[0], k[1]})
+                   : "memory");
+    };
 #pragma unroll
     for (int k = 0; k < kStages - 1; ++k) issue_step(k);
-    wait_loads_and_barrier<(kStages - 3) * TL::kLoads>();  // steps 0 and 1 landed
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kStages - 3) * TL::kLoads) : "memory");
+    build_keep_masks(0);
+    build_keep_masks(1);
+    asm volatile("s_barrier" ::: "memory");  // steps 0 and 1 landed, their masks built
     for (int s = 0; s < nsteps; ++s) {
       issue_step(s + kStages - 1);
-      wait_loads_and_barrier<(kStages - 3) * TL::kLoads>();  // step s+2 landed
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kStages - 3) * TL::kLoads) : "memory");
+      build_keep_masks(s + 2);  // past the end: stale data of an unused stage, never read
+      asm volatile("s_barrier" ::: "memory");  // step s+2 landed and its masks built
     }
     wait_loads_and_barrier<0>();  // loads past the end landed before the epilogue
     return;
@@ -1206,8 +1251,8 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
   // values: chunks 2q and 2q+1 of the row (groups 4q .. 4q+3)
   const uint32_t a_rd0 = (uint32_t)(TL::kXBytes + ia * 64 + (((2 * q) ^ aswz) << 4));
   const uint32_t a_rd1 = (uint32_t)(TL::kXBytes + ia * 64 + (((2 * q + 1) ^ aswz) << 4));
-  // metadata: bytes 6q .. 6q+5 of the row's 12, read as the dwords at 4q and 4q + 4
-  const uint32_t m_rd = (uint32_t)(TL::kXBytes + TL::kABytes + ia * TL::kMRow + 4 * q);
+  // keep masks of groups 4q .. 4q+3 of the row: one dword
+  const uint32_t km_rd = (uint32_t)(TL::kXBytes + TL::kABytes + TL::kMBytes + ia * 8 + 4 * q);
   // B of substep t: K rows 32q + 8t + {0..3} and {4..7}
   const int rb = 32 * q + (l16 >> 2);
   uint32_t b_rd[2][2];
@@ -1223,44 +1268,94 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
 #pragma unroll
     for (int f = 0; f < 2; ++f) acc[fm][f] = float16v_t{};
 
+  // Software pipeline over substeps u = 4 s + t: while substep u runs its eight matrix
+  // instructions, the value dwords and expansion selectors of substep u+2 and the B
+  // fragments of substep u+1 are being read (the selector reads index a table at random
+  // and meet bank conflicts, so they get two substeps); step s+1's keep masks are read
+  // at t = 1.
+  auto vals_of = [&](const uint8_t* stg, int fm, int t) {  // group 4q + t of row ia + 32 fm
+    return *reinterpret_cast<const u32x2_t*>(stg + (t < 2 ? a_rd0 : a_rd1) + fm * 32 * 64 +
+                                             8 * (t & 1));
+  };
+  auto meta_of = [&](const uint8_t* stg, int fm) {  // keep masks of this lane's 4 groups
+    return *reinterpret_cast<const uint32_t*>(stg + km_rd + fm * 32 * 8);
+  };
+  auto sel_of = [&](uint32_t masks, int t) {  // expansion selectors of group t
+    return *reinterpret_cast<const u32x4_t*>(lut + 16 * ((masks >> (8 * t)) & 0xffu));
+  };
+  auto b_of = [&](const uint8_t* stg, int f, int t) {
+    const short4_t lo =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(stg + b_rd[f][0] + 8 * t * kRB));
+    const short4_t hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(stg + b_rd[f][1] + 8 * t * kRB));
+    return __builtin_bit_cast(u32x4_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // table written; steps 0, 1 landed
-  for (int s = 0; s < nsteps; ++s) {
-    const uint8_t* st = smem + (s % kStages) * TL::kStageBytes;
-    u32x4_t v[4][2];
-    uint64_t mb[4];
+  uint32_t mcur[4], mnext[4];
+  u32x2_t vcur[4], vnext[4];
+  u32x4_t scur[4], snext[4], bcur[2];
+  {
+    const uint8_t* st0 = smem;
 #pragma unroll
     for (int fm = 0; fm < 4; ++fm) {
-      v[fm][0] = *reinterpret_cast<const u32x4_t*>(st + a_rd0 + fm * 32 * 64);
-      v[fm][1] = *reinterpret_cast<const u32x4_t*>(st + a_rd1 + fm * 32 * 64);
-      const uint32_t* mp = reinterpret_cast<const uint32_t*>(st + m_rd + fm * 32 * TL::kMRow);
-      mb[fm] = ((uint64_t)mp[0] | ((uint64_t)mp[1] << 32)) >> (16 * q);
+      mcur[fm] = meta_of(st0, fm);
+      vcur[fm] = vals_of(st0, fm, 0);
+      scur[fm] = sel_of(mcur[fm], 0);
+      vnext[fm] = vals_of(st0, fm, 1);
+      snext[fm] = sel_of(mcur[fm], 1);
     }
 #pragma unroll
+    for (int f = 0; f < 2; ++f) bcur[f] = b_of(st0, f, 0);
+  }
+  for (int s = 0; s < nsteps; ++s) {
+    const uint8_t* st = smem + (s % kStages) * TL::kStageBytes;
+    const uint8_t* sn = smem + ((s + 1) % kStages) * TL::kStageBytes;  // landed; the last
+    // step reads a stage that holds no useful data, and the values are never used
+#pragma unroll
     for (int t = 0; t < 4; ++t) {
+      if (t == 1) {
+#pragma unroll
+        for (int fm = 0; fm < 4; ++fm) mnext[fm] = meta_of(sn, fm);
+      }
+      const int t1 = (t + 1) & 3, t2 = (t + 2) & 3;
+      const uint8_t* stg1 = t < 3 ? st : sn;  // substep u+1
+      const uint8_t* stg2 = t < 2 ? st : sn;  // substep u+2
+      u32x2_t vnn[4];
+      u32x4_t snn[4], bnext[2];
+#pragma unroll
+      for (int fm = 0; fm < 4; ++fm) {
+        vnn[fm] = vals_of(stg2, fm, t2);
+        snn[fm] = sel_of(t < 2 ? mcur[fm] : mnext[fm], t2);
+      }
+#pragma unroll
+      for (int f = 0; f < 2; ++f) bnext[f] = b_of(stg1, f, t1);
+      // expand substep u and run its matrix instructions
       u32x4_t a[4];
 #pragma unroll
       for (int fm = 0; fm < 4; ++fm) {
-        const uint32_t bits = (uint32_t)(mb[fm] >> (12 * t)) & 0xfffu;
-        const uint32_t keep = (1u << (bits & 7)) | (1u << ((bits >> 3) & 7)) |
-                              (1u << ((bits >> 6) & 7)) | (1u << ((bits >> 9) & 7));
-        const u32x4_t sel = *reinterpret_cast<const u32x4_t*>(lut + 16 * keep);
-        const u32x4_t& vv = v[fm][t >> 1];
-        const uint32_t d0 = vv[2 * (t & 1)], d1 = vv[2 * (t & 1) + 1];
-        a[fm] = u32x4_t{__builtin_amdgcn_perm(d1, d0, sel[0]), __builtin_amdgcn_perm(d1, d0, sel[1]),
-                        __builtin_amdgcn_perm(d1, d0, sel[2]), __builtin_amdgcn_perm(d1, d0, sel[3])};
+        const uint32_t d0 = vcur[fm][0], d1 = vcur[fm][1];
+        a[fm] = u32x4_t{__builtin_amdgcn_perm(d1, d0, scur[fm][0]),
+                        __builtin_amdgcn_perm(d1, d0, scur[fm][1]),
+                        __builtin_amdgcn_perm(d1, d0, scur[fm][2]),
+                        __builtin_amdgcn_perm(d1, d0, scur[fm][3])};
       }
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_short4_t*)(st + b_rd[f][0] + 8 * t * kRB));
-        const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_short4_t*)(st + b_rd[f][1] + 8 * t * kRB));
-        const u32x4_t b = __builtin_bit_cast(
-            u32x4_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      for (int f = 0; f < 2; ++f)
 #pragma unroll
-        for (int fm = 0; fm < 4; ++fm) acc[fm][f] = mfma32x32x16<BF16>(a[fm], b, acc[fm][f]);
+        for (int fm = 0; fm < 4; ++fm) acc[fm][f] = mfma32x32x16<BF16>(a[fm], bcur[f], acc[fm][f]);
+#pragma unroll
+      for (int fm = 0; fm < 4; ++fm) {
+        vcur[fm] = vnext[fm];
+        scur[fm] = snext[fm];
+        vnext[fm] = vnn[fm];
+        snext[fm] = snn[fm];
       }
+      bcur[0] = bnext[0];
+      bcur[1] = bnext[1];
     }
+#pragma unroll
+    for (int fm = 0; fm < 4; ++fm) mcur[fm] = mnext[fm];
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // stage of step s released
   }
   asm volatile("s_barrier" ::: "memory");  // the producers' last loads have landed
