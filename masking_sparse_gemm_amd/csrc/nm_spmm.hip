@@ -475,6 +475,13 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 // ===========================================================================
 typedef float float16v_t __attribute__((ext_vector_type(16)));
 
+// LDS layout of an X stage for the 32x32 kernels: K row r holds BN columns as 32-byte
+// pairs (16 columns each), logical pair p at physical pair p ^ xpair_swizzle(r).  A
+// transposing B read has its two 16-lane column halves (adjacent logical pairs) on four
+// rows r..r+3; the swizzle 2 (r & 3) puts one half on even and the other on odd pairs,
+// so the 32 lanes of a pass touch all 64 banks exactly once.
+__device__ __forceinline__ int xpair_swizzle(int r) { return (r & 3) << 1; }
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES>
 struct Smfmac32Tile {
   static constexpr int kThreads = 64 * WAVES_M * WAVES_N;
@@ -674,7 +681,8 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
   const int last_step = nsteps - 1;
 
   // ---- direct-load sources and LDS destinations (as in smfmac_spmm_kernel, except that
-  // X chunks are swizzled in 32-byte pairs: logical pair p of K row r sits at p ^ (r & 7))
+  // X chunks are swizzled in 32-byte pairs: logical pair p of K row r sits at
+  // p ^ xpair_swizzle(r))
   const uint8_t* xg = reinterpret_cast<const uint8_t*>(X);
   const uint8_t* vg = reinterpret_cast<const uint8_t*>(values);
   const uint8_t* mg = reinterpret_cast<const uint8_t*>(meta);
@@ -685,7 +693,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
     const int w1k = j * TL::kWaves + wave;
     const int slot = w1k * 64 + lane;
     const int r = slot / TL::kXChunks, pc = slot % TL::kXChunks;
-    const int lc = 2 * ((pc >> 1) ^ (r & 7)) + (pc & 1);
+    const int lc = 2 * ((pc >> 1) ^ xpair_swizzle(r)) + (pc & 1);
     int col = t0 + 8 * lc;
     col = col < T ? col : 0;  // columns past T: any valid address (outputs past T only)
     x_src[j] = ((int64_t)r * T + col) * 2;
@@ -758,8 +766,9 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 #pragma unroll
   for (int f = 0; f < 2; ++f) {
     const int lp = (wn * TL::kWN + 32 * f + 16 * (blk & 1)) / 16;  // logical 32-byte pair
-    b_rd[f][0] = (uint32_t)(rb * kRB + ((lp ^ (l16 >> 2)) << 5) + 8 * (l16 & 3));
-    b_rd[f][1] = (uint32_t)((rb + 4) * kRB + ((lp ^ (4 + (l16 >> 2))) << 5) + 8 * (l16 & 3));
+    b_rd[f][0] = (uint32_t)(rb * kRB + ((lp ^ xpair_swizzle(rb)) << 5) + 8 * (l16 & 3));
+    b_rd[f][1] =
+        (uint32_t)((rb + 4) * kRB + ((lp ^ xpair_swizzle(rb + 4)) << 5) + 8 * (l16 & 3));
   }
   constexpr int kFar = 16 * kRB;  // K rows +16
   constexpr int kSub = 32 * kRB;  // K rows +32 (substep 1)
@@ -914,7 +923,7 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
       const int w1k = j * TL::kProducers + pw;  // 1 KB window of the X tile
       const int slot = w1k * 64 + lane;
       const int r = slot / TL::kXChunks, pc = slot % TL::kXChunks;
-      const int lc = 2 * ((pc >> 1) ^ (r & 7)) + (pc & 1);  // 32-byte pair swizzle
+      const int lc = 2 * ((pc >> 1) ^ xpair_swizzle(r)) + (pc & 1);
       int col = t0 + 8 * lc;
       col = col < T ? col : 0;  // columns past T: any valid address (outputs past T only)
       x_src[j] = ((int64_t)r * T + col) * 2;
@@ -976,8 +985,9 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
 #pragma unroll
   for (int f = 0; f < 2; ++f) {
     const int lp = (wn * TL::kWN + 32 * f + 16 * (blk & 1)) / 16;
-    b_rd[f][0] = (uint32_t)(rb * kRB + ((lp ^ (l16 >> 2)) << 5) + 8 * (l16 & 3));
-    b_rd[f][1] = (uint32_t)((rb + 4) * kRB + ((lp ^ (4 + (l16 >> 2))) << 5) + 8 * (l16 & 3));
+    b_rd[f][0] = (uint32_t)(rb * kRB + ((lp ^ xpair_swizzle(rb)) << 5) + 8 * (l16 & 3));
+    b_rd[f][1] =
+        (uint32_t)((rb + 4) * kRB + ((lp ^ xpair_swizzle(rb + 4)) << 5) + 8 * (l16 & 3));
   }
   constexpr int kFar = 16 * kRB;
   constexpr int kSub = 32 * kRB;
@@ -1131,7 +1141,7 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
       const int w1k = j * TL::kProducers + pw;
       const int slot = w1k * 64 + lane;
       const int r = slot / TL::kXChunks, pc = slot % TL::kXChunks;
-      const int lc = 2 * ((pc >> 1) ^ (r & 7)) + (pc & 1);
+      const int lc = 2 * ((pc >> 1) ^ xpair_swizzle(r)) + (pc & 1);
       int col = t0 + 8 * lc;
       col = col < T ? col : 0;
       x_src[j] = ((int64_t)r * T + col) * 2;
@@ -1259,8 +1269,9 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
 #pragma unroll
   for (int f = 0; f < 2; ++f) {
     const int lp = (wn * TL::kWN + 32 * f + 16 * (blk & 1)) / 16;
-    b_rd[f][0] = (uint32_t)(rb * kRB + ((lp ^ (l16 >> 2)) << 5) + 8 * (l16 & 3));
-    b_rd[f][1] = (uint32_t)((rb + 4) * kRB + ((lp ^ (4 + (l16 >> 2))) << 5) + 8 * (l16 & 3));
+    b_rd[f][0] = (uint32_t)(rb * kRB + ((lp ^ xpair_swizzle(rb)) << 5) + 8 * (l16 & 3));
+    b_rd[f][1] =
+        (uint32_t)((rb + 4) * kRB + ((lp ^ xpair_swizzle(rb + 4)) << 5) + 8 * (l16 & 3));
   }
   float16v_t acc[4][2];
 #pragma unroll
@@ -1552,7 +1563,7 @@ struct TileChoice {
   double rate;
 };
 constexpr int kNumTiles = 3;
-constexpr TileChoice kTiles[kNumTiles] = {{256, 256, 1300.0}, {256, 128, 1450.0},
+constexpr TileChoice kTiles[kNumTiles] = {{256, 256, 1300.0}, {256, 128, 1300.0},
                                           {128, 128, 850.0}};
 constexpr double kTileFixedUs = 3.0;
 
