@@ -16,6 +16,11 @@ follow the definitions cited in ``nm_oracle.h``:
   "2:4 Sparsity의 benefits").
 * ``spmm``: dense product of the decompressed operand with X in double
   (same review, section "Tensor Scores 상에서 구조적인 sparse GEMM").
+* ``prune`` / ``srste_grad``: SR-STE's masked forward weight and its backward
+  gradient ("量化友好的SR-STE稀疏化训练", section
+  "基于直通估计的动态掩码精炼化稀疏(SR-STE)"), the gradient in the printed
+  backward's fp32 order; ``round_from_f32`` is its final rounding to the
+  element type, exposed for the pins.
 """
 from __future__ import annotations
 
@@ -39,7 +44,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp"
         subprocess.check_call(
-            ["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
+            ["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-Wall", "-Wextra", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
         )
         os.replace(tmp, _LIB)
     return _LIB
@@ -65,10 +70,13 @@ def lib():
         L.nmo_spmm.argtypes = [vp, vp, i64, i64, i32, i32, vp, i64, i32, vp]
         L.nmo_spmm_rows.argtypes = [vp, vp, i64, i64, i32, i32, vp, i64, i32, i64, i64, vp]
         L.nmo_spmm_sample.argtypes = [vp, vp, i64, i64, i32, i32, vp, i64, i32, vp, vp, i64, vp]
+        L.nmo_prune.argtypes = [vp, i32, i64, i64, i32, i32, vp]
+        L.nmo_srste_grad.argtypes = [vp, vp, i32, i64, i64, i32, i32, ctypes.c_float, vp]
+        L.nmo_round_from_f32.argtypes = [vp, i32, i64, vp]
         L.nmo_to_double.argtypes = [vp, i32, i64]
         L.nmo_to_double.restype = ctypes.c_double
         for f in ("nmo_mask", "nmo_compress", "nmo_decompress", "nmo_spmm", "nmo_spmm_rows",
-                  "nmo_spmm_sample"):
+                  "nmo_spmm_sample", "nmo_prune", "nmo_srste_grad", "nmo_round_from_f32"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -170,6 +178,41 @@ def spmm_sample(values, meta, R, K, n, m, X, dt, rs, ts) -> np.ndarray:
                                _ptr(rs), _ptr(ts), len(rs), _ptr(out))
     _check(rc, "spmm_sample")
     return out
+
+
+def prune(W: np.ndarray, dt, n: int, m: int) -> np.ndarray:
+    """SR-STE forward weight (raw bits): W where kept, +0 where pruned."""
+    dt = _code(dt)
+    W = _as_bits(W, dt)
+    R, K = W.shape
+    out = np.empty((R, K), dtype=_ELEM[dt])
+    _check(lib().nmo_prune(_ptr(W), dt, R, K, n, m, _ptr(out)), "prune")
+    return out
+
+
+def srste_grad(W: np.ndarray, G: np.ndarray, dt, n: int, m: int, decay: float) -> np.ndarray:
+    """SR-STE backward gradient (raw bits): G where W is kept, else G + decay * W
+    in fp32 (product, then sum), rounded to the element type."""
+    dt = _code(dt)
+    W = _as_bits(W, dt)
+    G = _as_bits(G, dt)
+    if W.shape != G.shape:
+        raise ValueError("W and G must have the same shape")
+    R, K = W.shape
+    out = np.empty((R, K), dtype=_ELEM[dt])
+    _check(lib().nmo_srste_grad(_ptr(W), _ptr(G), dt, R, K, n, m, float(decay), _ptr(out)),
+           "srste_grad")
+    return out
+
+
+def round_from_f32(x: np.ndarray, dt) -> np.ndarray:
+    """Raw bits of every float32 of x rounded to dt (nearest, ties to even)."""
+    dt = _code(dt)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    flat = x.reshape(-1)
+    out = np.empty(flat.shape[0], dtype=_ELEM[dt])
+    _check(lib().nmo_round_from_f32(_ptr(flat), dt, flat.shape[0], _ptr(out)), "round_from_f32")
+    return out.reshape(x.shape)
 
 
 def to_double(a: np.ndarray, dt) -> np.ndarray:

@@ -341,3 +341,146 @@ int nmo_spmm_sample(const void* values, const uint32_t* meta, int64_t R, int64_t
   free(wd);
   return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* SR-STE ([SRSTE] "基于直通估计的动态掩码精炼化稀疏(SR-STE)").                */
+/*                                                                           */
+/* Forward: the mask is searched again from the current weights at every    */
+/* step and the layer uses the weights times that mask.  Backward: the      */
+/* gradient passes straight through where the mask keeps the weight and     */
+/* gains decay * weight where it prunes it.                                  */
+/* ------------------------------------------------------------------------ */
+
+/* exact value of element i as a float (every fp16 and bf16 value is an fp32 value) */
+static float elem_to_float(const void* p, int dt, int64_t i) {
+  uint32_t bits = raw_bits(p, dt, i);
+  float v;
+  if (dt == NMO_F32) {
+    memcpy(&v, &bits, 4);
+    return v;
+  }
+  if (dt == NMO_BF16) {
+    uint32_t b32 = bits << 16;
+    memcpy(&v, &b32, 4);
+    return v;
+  }
+  return (float)nmo_to_double(p, dt, i);
+}
+
+/* Round a float to the nearest bf16, ties to even.  bf16 is the upper half of   */
+/* the fp32 encoding (same sign, exponent and leading 7 fraction bits), so the   */
+/* discarded low 16 bits decide: above half an ulp rounds up, exactly half rounds */
+/* to the even neighbour; a carry into the exponent (or into Inf) is the correct */
+/* next value.  NaN stays NaN (quiet bit set).                                   */
+static uint16_t float_to_bf16(float x) {
+  uint32_t u;
+  memcpy(&u, &x, 4);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  uint32_t keep = u >> 16, rest = u & 0xFFFFu;
+  if (rest > 0x8000u || (rest == 0x8000u && (keep & 1u))) keep += 1u;
+  return (uint16_t)keep;
+}
+
+/* Round a float to the nearest IEEE binary16, ties to even: 1 sign, 5 exponent  */
+/* (bias 15) and 10 fraction bits.  |x| is scaled (exactly, in double) to units  */
+/* of its binade's quantum and rounded to an integer with rint (the default      */
+/* rounding mode is to nearest, ties to even).  Magnitudes from 65520 (half way  */
+/* between the largest finite value 65504 and 2^16) up become Inf.               */
+static uint16_t float_to_f16(float x) {
+  uint16_t sign = signbit(x) ? 0x8000u : 0u;
+  double a = fabs((double)x);
+  if (isnan(x)) return (uint16_t)(sign | 0x7E00u);
+  if (a >= 65520.0) return (uint16_t)(sign | 0x7C00u);
+  if (a < ldexp(1.0, -14)) { /* subnormal binade: quantum 2^-24 */
+    double q = rint(ldexp(a, 24)); /* 0 .. 1024; 1024 is the smallest normal's code */
+    return (uint16_t)(sign | (uint16_t)q);
+  }
+  int ex;
+  frexp(a, &ex);                   /* a = f * 2^ex, 0.5 <= f < 1 */
+  int E = ex - 1;                  /* 2^E <= a < 2^(E+1), -14 <= E <= 15 */
+  double q = rint(ldexp(a, 10 - E)); /* 1024 .. 2048 */
+  if (q == 2048.0) {
+    q = 1024.0;
+    E += 1;
+  }
+  return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | (uint16_t)(q - 1024.0));
+}
+
+static void store_rounded(void* out, int dt, int64_t i, float v) {
+  if (dt == NMO_F32)
+    memcpy((uint32_t*)out + i, &v, 4);
+  else if (dt == NMO_BF16)
+    ((uint16_t*)out)[i] = float_to_bf16(v);
+  else
+    ((uint16_t*)out)[i] = float_to_f16(v);
+}
+
+int nmo_round_from_f32(const float* in, int dt, int64_t count, void* out) {
+  if (dt != NMO_F32 && dt != NMO_F16 && dt != NMO_BF16) return -1;
+  if (count < 0) return -2;
+  for (int64_t i = 0; i < count; i++) store_rounded(out, dt, i, in[i]);
+  return 0;
+}
+
+static void copy_elem(void* dst, const void* src, int dt, int64_t i) {
+  if (dt == NMO_F32)
+    ((uint32_t*)dst)[i] = ((const uint32_t*)src)[i];
+  else
+    ((uint16_t*)dst)[i] = ((const uint16_t*)src)[i];
+}
+
+static void zero_elem(void* dst, int dt, int64_t i) {
+  if (dt == NMO_F32)
+    ((uint32_t*)dst)[i] = 0u;
+  else
+    ((uint16_t*)dst)[i] = 0u;
+}
+
+/* Forward weight: kept elements unchanged (bit for bit), pruned ones +0. */
+int nmo_prune(const void* W, int dt, int64_t R, int64_t K, int n, int m, void* W_out) {
+  int rc = check_args(dt, R, K, n, m);
+  if (rc) return rc;
+  int kept[16];
+  for (int64_t r = 0; r < R; r++) {
+    for (int64_t g = 0; g < K / m; g++) {
+      int64_t base = r * K + g * m;
+      best_pattern(W, dt, base, n, m, kept);
+      for (int i = 0; i < m; i++) zero_elem(W_out, dt, base + i);
+      for (int j = 0; j < n; j++) copy_elem(W_out, W, dt, base + kept[j]);
+    }
+  }
+  return 0;
+}
+
+/* Backward: out = G where the weight is kept (bit for bit); where it is pruned,  */
+/* out = G + decay * W evaluated as the printed backward does for a float32       */
+/* decay: p = decay * w rounded to fp32, s = g + p rounded to fp32, then s       */
+/* rounded once to dt.  The operands w and g are the exact fp32 values of the    */
+/* stored elements.  Each operation is its own IEEE single operation (this file  */
+/* is compiled with -ffp-contract=off, so no fused multiply-add).                */
+int nmo_srste_grad(const void* W, const void* G, int dt, int64_t R, int64_t K, int n, int m,
+                   float decay, void* G_out) {
+  int rc = check_args(dt, R, K, n, m);
+  if (rc) return rc;
+  int kept[16];
+  for (int64_t r = 0; r < R; r++) {
+    for (int64_t g = 0; g < K / m; g++) {
+      int64_t base = r * K + g * m;
+      int is_kept[16] = {0};
+      best_pattern(W, dt, base, n, m, kept);
+      for (int j = 0; j < n; j++) is_kept[kept[j]] = 1;
+      for (int i = 0; i < m; i++) {
+        if (is_kept[i]) {
+          copy_elem(G_out, G, dt, base + i);
+        } else {
+          float w = elem_to_float(W, dt, base + i);
+          float gr = elem_to_float(G, dt, base + i);
+          float p = decay * w;
+          float s = gr + p;
+          store_rounded(G_out, dt, base + i, s);
+        }
+      }
+    }
+  }
+  return 0;
+}

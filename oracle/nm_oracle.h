@@ -14,6 +14,10 @@
  *              scores every valid N-of-M pattern by the L1 norm of the weights it
  *              keeps and takes the best pattern per group of M along the last,
  *              contiguous dimension.
+ *            - section "基于直通估计的动态掩码精炼化稀疏(SR-STE)": the mask is
+ *              recomputed from |w| at every forward step, the layer uses weight
+ *              times mask, and the backward returns grad + decay*(1-mask)*weight
+ *              (decay 0.0002 by default).
  *   [ASDNN]  "[리뷰] Accelerating Sparse Deep Neural Networks" (moon-walker.medium.com)
  *            - section "2:4 Sparsity의 benefits": compressed matrix of R*C/2 values,
  *              2-bit position metadata per kept value, always N values stored per
@@ -35,6 +39,12 @@
  *     uint32 bitstream, least significant bit first; every row starts on a
  *     word boundary; pad bits are zero.
  *   - Decompression writes +0 (all-zero bits) at pruned positions.
+ *   - SR-STE's masked weight (weight times mask) is a selection: kept elements
+ *     bit for bit, +0 at pruned ones (the decompression rule).  Its mask is the
+ *     same best-pattern mask (the printed argsort leaves ties open).
+ *   - SR-STE's gradient is G bit for bit where the weight is kept (the decay
+ *     term is zero there); where it is pruned it is fl32(fl32(decay*w) + g),
+ *     rounded once more to the element type, in the printed backward's order.
  *
  * Conventions: every matrix is dense row-major; W is R x K with groups along
  * K; values R x (K*N/M); meta R x words_per_row uint32; X K x T; Y R x T.
@@ -81,6 +91,17 @@ int nmo_spmm_rows(const void* values, const uint32_t* meta, int64_t R, int64_t K
 int nmo_spmm_sample(const void* values, const uint32_t* meta, int64_t R, int64_t K, int n, int m,
                     const void* X, int64_t T, int dt, const int64_t* rs, const int64_t* ts,
                     int64_t count, double* out);
+
+/* W_out = W where kept, +0 where pruned (SR-STE forward weight) */
+int nmo_prune(const void* W, int dt, int64_t R, int64_t K, int n, int m, void* W_out);
+
+/* G_out = G where W is kept; fl32(g + fl32(decay * w)) rounded to dt where pruned
+ * (SR-STE backward) */
+int nmo_srste_grad(const void* W, const void* G, int dt, int64_t R, int64_t K, int n, int m,
+                   float decay, void* G_out);
+
+/* out[i] = in[i] rounded to dt (round to nearest, ties to even; fp32 copies) */
+int nmo_round_from_f32(const float* in, int dt, int64_t count, void* out);
 
 /* exact value of one element as a double (helper used by the Python side of the oracle) */
 double nmo_to_double(const void* p, int dt, int64_t i);
