@@ -51,6 +51,9 @@
  *   section "Tensor Scores 상에서 구조적인 sparse GEMM" (sparse first operand,
  *   compressed by the application, times a dense operand gives a dense result;
  *   16-bit inputs and outputs, fp32 only in a reduced mode).
+ *   "量化友好的SR-STE稀疏化训练", section "基于直通估计的动态掩码精炼化稀疏(SR-STE)"
+ *   (the mask is searched again from the weights at every training step; the
+ *   backward adds decay * w to the gradient where the mask prunes w).
  */
 #ifndef NM_H
 #define NM_H
@@ -62,7 +65,7 @@
 extern "C" {
 #endif
 
-#define NM_ABI_VERSION 2
+#define NM_ABI_VERSION 3
 
 typedef enum {
   NM_OK = 0,
@@ -73,7 +76,8 @@ typedef enum {
   NM_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned                        */
   NM_ERR_UNSUPPORTED = 6, /* valid arguments this build has no kernel for            */
   NM_ERR_DEVICE = 7,      /* no usable gfx950 device, or the launch failed           */
-  NM_ERR_LAYOUT = 8       /* unknown layout, or NM_LAYOUT_BLOCKED with K % 64 != 0   */
+  NM_ERR_LAYOUT = 8,      /* unknown layout, or NM_LAYOUT_BLOCKED with K % 64 != 0   */
+  NM_ERR_ALIAS = 9        /* an output overlaps an input it may not replace          */
 } nm_status;
 
 typedef enum { NM_F32 = 0, NM_F16 = 1, NM_BF16 = 2 } nm_dtype;
@@ -139,6 +143,28 @@ nm_status nm_decompress(const void* values, const uint32_t* meta, nm_dtype dt, i
 nm_status nm_spmm(const void* values, const uint32_t* meta, int64_t R, int64_t K, int n, int m,
                   nm_layout layout, const void* X, int64_t T, nm_dtype dt, void* Y,
                   nm_dtype y_dt, nm_stream_t stream);
+
+/* SR-STE forward weight ("基于直通估计的动态掩码精炼化稀疏(SR-STE)"): the mask is
+ * searched from W on every call (the nm_mask rule) and W_out (R x K, dt) gets W
+ * where it is kept, bit for bit, and +0 where it is pruned -- the dense masked
+ * weight of the forward step (nm_compress gives the same step in compressed form).
+ * W_out may be W itself (in place); any other overlap returns NM_ERR_ALIAS.
+ * W and W_out must be 16-byte aligned. */
+nm_status nm_prune(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m, void* W_out,
+                   nm_stream_t stream);
+
+/* SR-STE backward for the dense weights ("基于直通估计的动态掩码精炼化稀疏(SR-STE)"):
+ * G (R x K, dt) is the gradient with respect to the masked weight; G_out gets
+ *   G                      where W is kept (bit for bit),
+ *   G + decay * W          where W is pruned,
+ * the latter evaluated as one fp32 product decay * w, one fp32 sum with g (never
+ * fused into one rounding), then one rounding to dt (nearest, ties to even).  The
+ * mask is recomputed from W (the nm_mask rule), so W must be the weight of the
+ * same step's forward.  The page's default decay is 0.0002.  G_out may be G
+ * itself (in place); an output overlapping W, or G partially, returns
+ * NM_ERR_ALIAS.  W, G and G_out must be 16-byte aligned. */
+nm_status nm_srste_grad(const void* W, const void* G, nm_dtype dt, int64_t R, int64_t K, int n,
+                        int m, float decay, void* G_out, nm_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -9,6 +9,8 @@ library functions raises.
     Y = spmm(values, meta, X, 2, 4)           # X: (K, T), Y: (R, T)
     keep = mask(W, 2, 4)                      # bool (R, K)
     Wd = decompress(values, meta, 2, 4, K)    # dense (R, K), +0 where pruned
+    Wp = prune(W, 2, 4)                       # SR-STE forward weight: W where kept, +0 else
+    srste_grad(W, G, 2, 4, out=G)             # SR-STE backward, in place on G
 
 The compressed pair comes in two layouts (defined in include/nm.h): "rows"
 (values (R, K*n/m), meta (R, words)) and "blocked" (blocks of 16 rows x 64
@@ -29,13 +31,16 @@ LIB_PATH = os.path.join(HERE, "libnm.so")
 NM_F32, NM_F16, NM_BF16 = 0, 1, 2
 _DT = {torch.float32: NM_F32, torch.float16: NM_F16, torch.bfloat16: NM_BF16}
 _TORCH_DT = {v: k for k, v in _DT.items()}
-STATUS = ["ok", "null", "shape", "pattern", "dtype", "align", "unsupported", "device", "layout"]
+STATUS = ["ok", "null", "shape", "pattern", "dtype", "align", "unsupported", "device", "layout",
+          "alias"]
 LAYOUTS = {"rows": 0, "blocked": 1}
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 # every function the C header declares
 EXPORTS = ("nm_abi_version", "nm_status_str", "nm_values_bytes", "nm_meta_bytes",
-           "nm_meta_words_per_row", "nm_mask", "nm_compress", "nm_decompress", "nm_spmm")
+           "nm_meta_words_per_row", "nm_mask", "nm_compress", "nm_decompress", "nm_spmm",
+           "nm_prune", "nm_srste_grad")
+SRSTE_DECAY = 0.0002  # the SR-STE page's default decay
 
 
 class NMError(RuntimeError):
@@ -69,7 +74,10 @@ def lib() -> ctypes.CDLL:
         L.nm_compress.argtypes = [vp, i32, i64, i64, i32, i32, i32, vp, vp, vp]
         L.nm_decompress.argtypes = [vp, vp, i32, i64, i64, i32, i32, i32, vp, vp]
         L.nm_spmm.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, i64, i32, vp, i32, vp]
-        for f in ("nm_mask", "nm_compress", "nm_decompress", "nm_spmm"):
+        L.nm_prune.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp]
+        L.nm_srste_grad.argtypes = [vp, vp, i32, i64, i64, i32, i32, ctypes.c_float, vp, vp]
+        for f in ("nm_mask", "nm_compress", "nm_decompress", "nm_spmm", "nm_prune",
+                  "nm_srste_grad"):
             getattr(L, f).restype = i32
         if L.nm_abi_version() != ABI_VERSION:
             raise ImportError(f"{LIB_PATH} has ABI {L.nm_abi_version()}, expected {ABI_VERSION}: "
@@ -207,4 +215,38 @@ def spmm(values: torch.Tensor, meta: torch.Tensor, X: torch.Tensor, n: int = 2, 
         raise ValueError("out_dtype must be float32, float16 or bfloat16")
     _check("nm_spmm", lib().nm_spmm(_ptr(values), _ptr(meta), R, K, n, m, _layout(layout),
                                     _ptr(X), T, dt, _ptr(out), _DT[y_dtype], _stream(X)))
+    return out
+
+
+def _same_dense(t: torch.Tensor, like: torch.Tensor, name: str) -> None:
+    if t.shape != like.shape or t.dtype != like.dtype or t.device != like.device:
+        raise ValueError(f"{name} must match W's shape, dtype and device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major)")
+
+
+def prune(W: torch.Tensor, n: int = 2, m: int = 4, out: torch.Tensor | None = None) -> torch.Tensor:
+    """SR-STE forward weight: W where the N:M mask keeps it, +0 elsewhere (out may be W)."""
+    dt = _dense_input(W, "W")
+    R, K = W.shape
+    if out is None:
+        out = torch.empty_like(W)
+    else:
+        _same_dense(out, W, "out")
+    _check("nm_prune", lib().nm_prune(_ptr(W), dt, R, K, n, m, _ptr(out), _stream(W)))
+    return out
+
+
+def srste_grad(W: torch.Tensor, G: torch.Tensor, n: int = 2, m: int = 4,
+               decay: float = SRSTE_DECAY, out: torch.Tensor | None = None) -> torch.Tensor:
+    """SR-STE backward: G where W is kept, G + decay*W where pruned (out may be G)."""
+    dt = _dense_input(W, "W")
+    _same_dense(G, W, "G")
+    R, K = W.shape
+    if out is None:
+        out = torch.empty_like(G)
+    else:
+        _same_dense(out, W, "out")
+    _check("nm_srste_grad", lib().nm_srste_grad(_ptr(W), _ptr(G), dt, R, K, n, m, float(decay),
+                                                _ptr(out), _stream(W)))
     return out

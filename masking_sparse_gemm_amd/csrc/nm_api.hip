@@ -51,6 +51,12 @@ nm_status check_device() {
   return state == 1 ? NM_OK : NM_ERR_DEVICE;
 }
 
+// Do the byte ranges [a, a + n) and [b, b + n) share a byte?
+bool overlaps(const void* a, const void* b, int64_t bytes) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return bytes > 0 && x < y + (uintptr_t)bytes && y < x + (uintptr_t)bytes;
+}
+
 nm_status from_hip(hipError_t e) { return e == hipSuccess ? NM_OK : NM_ERR_DEVICE; }
 
 // NM_LAYOUT_BLOCKED cuts K into steps of 64: each step then holds a whole number of
@@ -86,6 +92,7 @@ const char* nm_status_str(nm_status s) {
     case NM_ERR_UNSUPPORTED: return "unsupported combination";
     case NM_ERR_DEVICE: return "device error (no gfx950 device, or launch failed)";
     case NM_ERR_LAYOUT: return "bad layout (unknown, or blocked layout with K not a multiple of 64)";
+    case NM_ERR_ALIAS: return "an output overlaps an input it may not replace";
   }
   return "unknown status";
 }
@@ -173,6 +180,37 @@ nm_status nm_spmm(const void* values, const uint32_t* meta, int64_t R, int64_t K
   if ((st = check_device()) != NM_OK) return st;
   return from_hip(nm::launch_spmm(values, meta, R, K, n, m, layout == NM_LAYOUT_BLOCKED, X, T,
                                   (int)dt, Y, (int)y_dt, static_cast<hipStream_t>(stream)));
+}
+
+nm_status nm_prune(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m, void* W_out,
+                   nm_stream_t stream) {
+  if (!valid_dtype(dt)) return NM_ERR_DTYPE;
+  nm_status st = check_pattern(n, m);
+  if (st != NM_OK) return st;
+  if ((st = check_shape(R, K, m)) != NM_OK) return st;
+  if (missing(W, R * K) || missing(W_out, R * K)) return NM_ERR_NULL;
+  if (R * K == 0) return NM_OK;
+  if (W_out != W && overlaps(W, W_out, R * K * elem_bytes(dt))) return NM_ERR_ALIAS;
+  if (!aligned16(W) || !aligned16(W_out)) return NM_ERR_ALIGN;
+  if ((st = check_device()) != NM_OK) return st;
+  return from_hip(nm::launch_prune(W, (int)dt, R, K, n, m, W_out,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+nm_status nm_srste_grad(const void* W, const void* G, nm_dtype dt, int64_t R, int64_t K, int n,
+                        int m, float decay, void* G_out, nm_stream_t stream) {
+  if (!valid_dtype(dt)) return NM_ERR_DTYPE;
+  nm_status st = check_pattern(n, m);
+  if (st != NM_OK) return st;
+  if ((st = check_shape(R, K, m)) != NM_OK) return st;
+  if (missing(W, R * K) || missing(G, R * K) || missing(G_out, R * K)) return NM_ERR_NULL;
+  if (R * K == 0) return NM_OK;
+  const int64_t bytes = R * K * elem_bytes(dt);
+  if (overlaps(W, G_out, bytes) || (G_out != G && overlaps(G, G_out, bytes))) return NM_ERR_ALIAS;
+  if (!aligned16(W) || !aligned16(G) || !aligned16(G_out)) return NM_ERR_ALIGN;
+  if ((st = check_device()) != NM_OK) return st;
+  return from_hip(nm::launch_srste_grad(W, G, (int)dt, R, K, n, m, decay, G_out,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

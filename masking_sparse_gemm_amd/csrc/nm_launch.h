@@ -20,4 +20,10 @@ hipError_t launch_spmm(const void* values, const uint32_t* meta, int64_t R, int6
                        int m, bool blocked, const void* X, int64_t T, int dt, void* Y, int y_dt,
                        hipStream_t s);
 
+// SR-STE passes (dt in nm_dtype codes); `out` may be W (prune) or G (grad).
+hipError_t launch_prune(const void* W, int dt, int64_t R, int64_t K, int n, int m, void* out,
+                        hipStream_t s);
+hipError_t launch_srste_grad(const void* W, const void* G, int dt, int64_t R, int64_t K, int n,
+                             int m, float decay, void* out, hipStream_t s);
+
 }  // namespace nm

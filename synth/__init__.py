@@ -173,6 +173,14 @@ class Workload:
     def X(self) -> np.ndarray:
         return generate(self.x, (self.K, self.T), self.dtype)
 
+    def G(self) -> np.ndarray:
+        """A weight gradient of W's shape: N(0, 1e-3^2), seed 3 (the SR-STE backward's input)."""
+        return generate(GRAD_DIST, (self.R, self.K), self.dtype)
+
+
+# Weight gradients for the SR-STE backward: i.i.d. normal, small next to the weights.
+GRAD_DIST = Dist("normal", seed=3, scale=1e-3)
+
 
 def _llama(R, K, name):
     return Workload(

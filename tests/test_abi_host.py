@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     L = nm.lib()
     for name in header_functions():
         assert hasattr(L, name), name
-    assert L.nm_abi_version() == nm.ABI_VERSION == 2
+    assert L.nm_abi_version() == nm.ABI_VERSION == 3
 
 
 @needs_lib
@@ -48,7 +48,7 @@ def test_library_has_no_undefined_symbols_of_its_own():
 
 @needs_lib
 def test_status_strings():
-    for code in range(9):
+    for code in range(10):
         s = nm.status_str(code)
         assert s and s != "unknown status"
     assert nm.status_str(99) == "unknown status"
@@ -152,6 +152,61 @@ def test_empty_arrays_may_be_null():
         assert L.nm_compress(None, nm.NM_F16, 0, 64, 2, 4, layout, None, None, None) == 0
         assert L.nm_spmm(FAKE, FAKE, 8, 128, 2, 4, layout, FAKE, 0, nm.NM_BF16, None, nm.NM_BF16,
                          None) == 0
+
+
+@needs_lib
+@pytest.mark.parametrize("case,expect", [
+    (dict(W=0), "null"),
+    (dict(G=0), "null"),
+    (dict(out=0), "null"),
+    (dict(dt=4), "dtype"),
+    (dict(n=0), "pattern"),
+    (dict(m=16, n=2), "pattern"),
+    (dict(K=130), "shape"),
+    (dict(R=-2), "shape"),
+    (dict(W=FAKE + 8, out=FAKE + 0x100000), "align"),
+    (dict(G=FAKE + 2), "align"),
+    (dict(out=FAKE + 0x100008), "align"),
+    (dict(out=FAKE), "alias"),                     # G_out on top of W
+    (dict(out=FAKE + 0x2000), "alias"),            # G_out overlapping W's second half
+    # G_out just past W does not overlap it: the alias check passes and the
+    # (later) alignment check of G reports instead
+    (dict(out=FAKE + 0x4000, G=FAKE + 0x80002), "align"),
+    (dict(out=FAKE + 0x80000 + 64), "alias"),      # G_out partly over G
+])
+def test_srste_argument_errors(case, expect):
+    """W at FAKE (64 x 128 bf16 = 16 KiB), G at FAKE + 512 KiB, G_out at FAKE + 1 MiB."""
+    L = nm.lib()
+    a = dict(W=FAKE, G=FAKE + 0x80000, out=FAKE + 0x100000, dt=nm.NM_BF16, R=64, K=128, n=2, m=4)
+    a.update(case)
+    code = L.nm_srste_grad(a["W"], a["G"], a["dt"], a["R"], a["K"], a["n"], a["m"], 2e-4,
+                           a["out"], None)
+    assert nm.STATUS[code] == expect
+
+
+@needs_lib
+@pytest.mark.parametrize("case,expect", [
+    (dict(W=0), "null"),
+    (dict(out=0), "null"),
+    (dict(dt=3), "dtype"),
+    (dict(n=9, m=8), "pattern"),
+    (dict(K=6), "shape"),
+    (dict(W=FAKE + 4), "align"),
+    (dict(out=FAKE + 0x2000), "alias"),            # half way into W
+])
+def test_prune_argument_errors(case, expect):
+    L = nm.lib()
+    a = dict(W=FAKE, out=FAKE + 0x100000, dt=nm.NM_F16, R=64, K=128, n=2, m=4)
+    a.update(case)
+    code = L.nm_prune(a["W"], a["dt"], a["R"], a["K"], a["n"], a["m"], a["out"], None)
+    assert nm.STATUS[code] == expect
+
+
+@needs_lib
+def test_srste_empty_arrays_may_be_null():
+    L = nm.lib()
+    assert L.nm_prune(None, nm.NM_BF16, 0, 128, 2, 4, None, None) == 0
+    assert L.nm_srste_grad(None, None, nm.NM_F32, 16, 0, 2, 4, 2e-4, None, None) == 0
 
 
 def test_binding_shapes_follow_the_layout_definition():
