@@ -12,6 +12,11 @@ the timed region.  Prints one JSON line.
 flops (2 R K T per matrix) divided by the step time.  Per-kernel figures,
 the roofline of the dominant kernel, the dense GEMM on the same shapes and the
 CPU oracle timed on the host are reported alongside.
+
+The SR-STE passes of a training step on the same weights (nm_prune, the
+forward's masked weight, and nm_srste_grad, the backward's gradient) are timed
+in a separate pass after the step and reported under "srste" with their HBM
+roofline; they are not part of `value`.
 """
 from __future__ import annotations
 
@@ -76,6 +81,35 @@ def profiled_traffic(workload: str):
     per = [v["read_bytes"] + v["write_bytes"] for k, v in prof["per_dispatch_bytes"].items()
            if "spmm_kernel" in k]
     return sum(per) / len(per) if per else None
+
+
+def srste_cpu_sample(mats, n, m, budget_s: float = 3.0):
+    """The oracle's SR-STE forward weight + gradient on leading rows of each matrix,
+    one thread, for about budget_s seconds: elements per second."""
+    import oracle
+
+    oracle.lib()
+    done, elems = {}, 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        progressed = False
+        for w in mats:
+            r0 = done.get(w["name"], 0)
+            r1 = min(w["R"], r0 + 64)
+            if r1 <= r0:
+                continue
+            Wsl, Gsl = np.ascontiguousarray(w["W"][r0:r1]), np.ascontiguousarray(w["G"][r0:r1])
+            oracle.prune(Wsl, w["dtype"], n, m)
+            oracle.srste_grad(Wsl, Gsl, w["dtype"], n, m, 2e-4)
+            done[w["name"]] = r1
+            elems += (r1 - r0) * w["K"]
+            progressed = True
+        if not progressed:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(elems / dt / 1e6, 2), "unit": "Melem/s (forward weight + gradient)",
+            "cores": 1, "kind": "oracle", "seconds": round(dt, 2),
+            "sample": ", ".join(f"{k}: rows 0..{v}" for k, v in done.items())}
 
 
 def cpu_baseline(mats, n, m, threads: int, budget_s: float = 12.0):
@@ -169,14 +203,17 @@ def main() -> int:
             return torch.from_numpy(a.view(np.int16)).view(tdt).to(dev)
 
         s = 4 if w.dtype == "f32" else 2
-        d = dict(name=name, R=w.R, K=w.K, T=w.T, dtype=w.dtype, s=s, W=W, X=X, Wd=to_dev(W),
-                 Xd=to_dev(X))
+        G = w.G()
+        d = dict(name=name, R=w.R, K=w.K, T=w.T, dtype=w.dtype, s=s, W=W, X=X, G=G, Wd=to_dev(W),
+                 Xd=to_dev(X), Gd=to_dev(G))
         vshape, mshape = nm.compressed_shapes(w.R, w.K, n, m, args.layout)
         d["vals"] = torch.empty(vshape, dtype=tdt, device=dev)
         d["meta"] = torch.empty(mshape, dtype=torch.int32, device=dev)
         d["mask"] = torch.empty((w.R, w.K), dtype=torch.bool, device=dev)
         d["dec"] = torch.empty((w.R, w.K), dtype=tdt, device=dev)
         d["Y"] = torch.empty((w.R, w.T), dtype=tdt, device=dev)
+        d["pruned"] = torch.empty((w.R, w.K), dtype=tdt, device=dev)
+        d["grad"] = torch.empty((w.R, w.K), dtype=tdt, device=dev)
         mats.append(d)
     dtype = mats[0]["dtype"]
     if args.copy_calibration:
@@ -202,13 +239,18 @@ def main() -> int:
         elif kind == "decompress":
             rc = L.nm_decompress(d["vals"].data_ptr(), d["meta"].data_ptr(), DT, d["R"], d["K"],
                                  n, m, LAY, d["dec"].data_ptr(), sp)
-        else:
+        elif kind == "spmm":
             rc = L.nm_spmm(d["vals"].data_ptr(), d["meta"].data_ptr(), d["R"], d["K"], n, m, LAY,
                            d["Xd"].data_ptr(), d["T"], DT, d["Y"].data_ptr(), DT, sp)
+        elif kind == "prune":
+            rc = L.nm_prune(d["Wd"].data_ptr(), DT, d["R"], d["K"], n, m, d["pruned"].data_ptr(), sp)
+        else:
+            rc = L.nm_srste_grad(d["Wd"].data_ptr(), d["Gd"].data_ptr(), DT, d["R"], d["K"], n, m,
+                                 nm.SRSTE_DECAY, d["grad"].data_ptr(), sp)
         if rc != 0:
             raise RuntimeError(f"{kind} failed: {nm.status_str(rc)}")
 
-    def step(events=None):
+    def step(events=None, kinds=kinds):
         for d in mats:
             for kind in kinds:
                 if events is not None:
@@ -313,8 +355,41 @@ def main() -> int:
                      "spmm_speedup": round(dense_t / spmm_t, 3),
                      "how": "torch.matmul (hipBLASLt) on the decompressed weight, same dtype"}
 
+    # ---- SR-STE passes on the same weights (not part of the step) ----
+    sr_kinds = ["prune", "srste_grad"]
+    for _ in range(args.warmup):
+        step(kinds=sr_kinds)
+    torch.cuda.synchronize()
+    sr_events = []
+    for _ in range(args.steps):
+        step(sr_events, kinds=sr_kinds)
+    torch.cuda.synchronize()
+    sr_per = {}
+    for name, kind, e0, e1 in sr_events:
+        sr_per.setdefault((name, kind), []).append(e0.elapsed_time(e1) * 1e-3)
+    srste = {"decay": nm.SRSTE_DECAY, "kernels": {}}
+    sr_tot = {k: [0.0, 0.0] for k in sr_kinds}
+    for d in mats:
+        e = d["R"] * d["K"]
+        ab = {"prune": 2 * e * d["s"], "srste_grad": 3 * e * d["s"]}
+        for kind in sr_kinds:
+            t = float(np.mean(sr_per[(d["name"], kind)]))
+            srste["kernels"][f"{d['name']}.{kind}"] = {
+                "us": round(t * 1e6, 2), "alg_bytes": ab[kind], "gbps": round(ab[kind] / t / 1e9, 1),
+                "frac_hbm": round(ab[kind] / t / 1e9 / PEAK_HBM_GBS, 3)}
+            sr_tot[kind][0] += t
+            sr_tot[kind][1] += ab[kind]
+    g_t, g_b = sr_tot["srste_grad"]
+    srste["roofline"] = {"bound": "hbm", "kernel": "nm_srste_grad", "achieved": round(g_b / g_t / 1e9, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(g_b / g_t / 1e9 / PEAK_HBM_GBS, 3),
+                         "alg_bytes_per_elem": 3 * mats[0]["s"]}
+    srste["prune_frac_hbm"] = round(sr_tot["prune"][1] / sr_tot["prune"][0] / 1e9 / PEAK_HBM_GBS, 3)
+    srste["step_us"] = round((g_t + sr_tot["prune"][0]) * 1e6, 1)
+
     cpu = None
     if not args.no_cpu:
+        srste["cpu_baseline"] = srste_cpu_sample(mats, n, m)
         threads = max(1, min(16, os.cpu_count() or 1))
         cpu = cpu_baseline(mats, n, m, threads)
 
@@ -342,6 +417,7 @@ def main() -> int:
         "mask_compress": mask_compress,
         "dense_gemm": dense,
         "kernels": kernels,
+        "srste": srste,
         "context": "pages: up to 2x dense math throughput on A100 sparse Tensor Cores (not a target)",
     }
     print(json.dumps(out), flush=True)
