@@ -15,8 +15,8 @@ CPU oracle timed on the host are reported alongside.
 
 The SR-STE passes of a training step on the same weights (nm_prune, the
 forward's masked weight, and nm_srste_grad, the backward's gradient) are timed
-in a separate pass after the step and reported under "srste" with their HBM
-roofline; they are not part of `value`.
+in a separate pass after the step, each launch after a cache-clearing fill, and
+reported under "srste" with their HBM roofline; they are not part of `value`.
 """
 from __future__ import annotations
 
@@ -65,21 +65,21 @@ def algorithmic_bytes(R, K, T, n, m, s):
     }
 
 
-def profiled_traffic(workload: str):
-    """HBM bytes per nm_spmm dispatch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    summary (already scaled by the copy-kernel calibration), or None when that summary is
-    missing or was taken on a different version of the kernel source."""
+def profiled_traffic(workload: str, kernel: str = "spmm_kernel", source: str = "nm_spmm.hip"):
+    """HBM bytes per dispatch of the kernels whose name contains `kernel`, from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary (already scaled by the copy-kernel calibration),
+    or None when that summary is missing or was taken on a different version of `source`."""
     path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
-    src = os.path.join(ROOT, "masking_sparse_gemm_amd", "csrc", "nm_spmm.hip")
+    src = os.path.join(ROOT, "masking_sparse_gemm_amd", "csrc", source)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         prof = json.load(f)
     with open(src, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != prof.get("nm_spmm_hip_sha256"):
+        if hashlib.sha256(f.read()).hexdigest() != prof.get("sources_sha256", {}).get(source):
             return None
     per = [v["read_bytes"] + v["write_bytes"] for k, v in prof["per_dispatch_bytes"].items()
-           if "spmm_kernel" in k]
+           if kernel in k]
     return sum(per) / len(per) if per else None
 
 
@@ -356,17 +356,28 @@ def main() -> int:
                      "how": "torch.matmul (hipBLASLt) on the decompressed weight, same dtype"}
 
     # ---- SR-STE passes on the same weights (not part of the step) ----
+    # Each timed launch starts cold: a 512 MiB fill (twice the 256 MB Infinity Cache) runs
+    # before it, outside its events, so its inputs come from HBM as in a training step,
+    # where the forward and the backward of a layer are far apart.
     sr_kinds = ["prune", "srste_grad"]
+    flush = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
     for _ in range(args.warmup):
         step(kinds=sr_kinds)
     torch.cuda.synchronize()
-    sr_events = []
-    for _ in range(args.steps):
-        step(sr_events, kinds=sr_kinds)
-    torch.cuda.synchronize()
     sr_per = {}
-    for name, kind, e0, e1 in sr_events:
-        sr_per.setdefault((name, kind), []).append(e0.elapsed_time(e1) * 1e-3)
+    for _ in range(args.steps):
+        for d in mats:
+            for kind in sr_kinds:
+                flush.zero_()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                launch(d, kind)
+                e1.record(stream)
+                sr_per.setdefault((d["name"], kind), []).append((e0, e1))
+    torch.cuda.synchronize()
+    sr_per = {k: [a.elapsed_time(b) * 1e-3 for a, b in v] for k, v in sr_per.items()}
+    del flush
     srste = {"decay": nm.SRSTE_DECAY, "kernels": {}}
     sr_tot = {k: [0.0, 0.0] for k in sr_kinds}
     for d in mats:
@@ -383,7 +394,11 @@ def main() -> int:
     srste["roofline"] = {"bound": "hbm", "kernel": "nm_srste_grad", "achieved": round(g_b / g_t / 1e9, 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(g_b / g_t / 1e9 / PEAK_HBM_GBS, 3),
-                         "alg_bytes_per_elem": 3 * mats[0]["s"]}
+                         "alg_bytes_per_elem": 3 * mats[0]["s"], "traffic": None}
+    g_traffic = profiled_traffic(args.workload, "srste_unit_kernel<2, 2, 4, true>"
+                                 if dtype == "bf16" else "srste_unit_kernel", "nm_srste.hip")
+    if g_traffic is not None:
+        srste["roofline"]["traffic"] = round(g_traffic)
     srste["prune_frac_hbm"] = round(sr_tot["prune"][1] / sr_tot["prune"][0] / 1e9 / PEAK_HBM_GBS, 3)
     srste["step_us"] = round((g_t + sr_tot["prune"][0]) * 1e6, 1)
 

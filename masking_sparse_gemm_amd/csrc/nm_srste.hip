@@ -33,7 +33,7 @@ namespace nm {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnitsPerThread = 4;
+constexpr int kUnitsPerThread = 2;
 
 enum { kF32 = 0, kF16 = 1, kBF16 = 2 };
 
