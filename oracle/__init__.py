@@ -21,6 +21,11 @@ follow the definitions cited in ``nm_oracle.h``:
   "基于直通估计的动态掩码精炼化稀疏(SR-STE)"), the gradient in the printed
   backward's fp32 order; ``round_from_f32`` is its final rounding to the
   element type, exposed for the pins.
+* ``tmask_greedy`` / ``tmask_optimal`` / ``tprune``: transposable N:M masks per
+  M x M block ("[论文解读] Accelerated Sparse Neural Training: ... N:M
+  Transposable Masks", ABSTRACT and "提出的方法"): the greedy 2-approximation
+  the GPU runs, the minimum-cost-flow optimum as a reference, and the forward
+  weight under the greedy mask.  ``compress_t`` is compress of the transpose.
 """
 from __future__ import annotations
 
@@ -73,10 +78,14 @@ def lib():
         L.nmo_prune.argtypes = [vp, i32, i64, i64, i32, i32, vp]
         L.nmo_srste_grad.argtypes = [vp, vp, i32, i64, i64, i32, i32, ctypes.c_float, vp]
         L.nmo_round_from_f32.argtypes = [vp, i32, i64, vp]
+        L.nmo_tmask_greedy.argtypes = [vp, i32, i64, i64, i32, i32, vp]
+        L.nmo_tmask_optimal.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp]
+        L.nmo_tprune.argtypes = [vp, i32, i64, i64, i32, i32, vp]
         L.nmo_to_double.argtypes = [vp, i32, i64]
         L.nmo_to_double.restype = ctypes.c_double
         for f in ("nmo_mask", "nmo_compress", "nmo_decompress", "nmo_spmm", "nmo_spmm_rows",
-                  "nmo_spmm_sample", "nmo_prune", "nmo_srste_grad", "nmo_round_from_f32"):
+                  "nmo_spmm_sample", "nmo_prune", "nmo_srste_grad", "nmo_round_from_f32",
+                  "nmo_tmask_greedy", "nmo_tmask_optimal", "nmo_tprune"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -213,6 +222,44 @@ def round_from_f32(x: np.ndarray, dt) -> np.ndarray:
     out = np.empty(flat.shape[0], dtype=_ELEM[dt])
     _check(lib().nmo_round_from_f32(_ptr(flat), dt, flat.shape[0], _ptr(out)), "round_from_f32")
     return out.reshape(x.shape)
+
+
+def tmask_greedy(W: np.ndarray, dt, n: int, m: int) -> np.ndarray:
+    """uint8 R x K transposable mask by the greedy (1 = kept)."""
+    dt = _code(dt)
+    W = _as_bits(W, dt)
+    R, K = W.shape
+    out = np.empty((R, K), dtype=np.uint8)
+    _check(lib().nmo_tmask_greedy(_ptr(W), dt, R, K, n, m, _ptr(out)), "tmask_greedy")
+    return out
+
+
+def tmask_optimal(W: np.ndarray, dt, n: int, m: int):
+    """(uint8 R x K optimal transposable mask, its kept L1 norm)."""
+    dt = _code(dt)
+    W = _as_bits(W, dt)
+    R, K = W.shape
+    out = np.empty((R, K), dtype=np.uint8)
+    l1 = ctypes.c_double(0.0)
+    _check(lib().nmo_tmask_optimal(_ptr(W), dt, R, K, n, m, _ptr(out), ctypes.byref(l1)),
+           "tmask_optimal")
+    return out, l1.value
+
+
+def tprune(W: np.ndarray, dt, n: int, m: int) -> np.ndarray:
+    """Raw bits: W where the greedy transposable mask keeps it, +0 elsewhere."""
+    dt = _code(dt)
+    W = _as_bits(W, dt)
+    R, K = W.shape
+    out = np.empty((R, K), dtype=_ELEM[dt])
+    _check(lib().nmo_tprune(_ptr(W), dt, R, K, n, m, _ptr(out)), "tprune")
+    return out
+
+
+def compress_t(W: np.ndarray, dt, n: int, m: int):
+    """compress of the transpose: (values K x R*n/m, meta K x words) of W.T."""
+    dt = _code(dt)
+    return compress(np.ascontiguousarray(_as_bits(W, dt).T), dt, n, m)
 
 
 def to_double(a: np.ndarray, dt) -> np.ndarray:

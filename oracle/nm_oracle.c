@@ -484,3 +484,157 @@ int nmo_srste_grad(const void* W, const void* G, int dt, int64_t R, int64_t K, i
   }
   return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Transposable N:M masks ([TRANS] "提出的方法").                              */
+/*                                                                           */
+/* W is cut into m x m blocks (rows and columns aligned at multiples of m).  */
+/* A transposable mask keeps at most n entries in every row and every column */
+/* of every block, so both W and its transpose are N:M along their           */
+/* contiguous dimension and one mask serves the forward and the backward    */
+/* product.  The best such mask maximises the kept L1 norm of each block (a  */
+/* minimum-cost flow problem); the fast method is a greedy 2-approximation.  */
+/* ------------------------------------------------------------------------ */
+
+static int check_tshape(int dt, int64_t R, int64_t K, int n, int m) {
+  int rc = check_args(dt, R, K, n, m);
+  if (rc) return rc;
+  if (R % m != 0) return -4;
+  return 0;
+}
+
+/* Greedy: take the block's entries in descending exact magnitude (equal     */
+/* magnitudes in ascending row-major position inside the block) and keep an  */
+/* entry whenever its row and its column still hold fewer than n kept ones.  */
+static void greedy_block(const void* W, int dt, int64_t K, int64_t r0, int64_t c0, int n, int m,
+                         uint8_t* keep /* m*m, row-major */) {
+  int order[256];
+  big_t mag[256];
+  int cnt = m * m;
+  for (int e = 0; e < cnt; e++) {
+    exact_magnitude(W, dt, (r0 + e / m) * K + c0 + e % m, &mag[e]);
+    order[e] = e;
+  }
+  /* insertion sort: larger magnitude first, lower position first on ties (stable) */
+  for (int i = 1; i < cnt; i++) {
+    int e = order[i], j = i - 1;
+    while (j >= 0 && big_cmp(&mag[order[j]], &mag[e]) < 0) {
+      order[j + 1] = order[j];
+      j--;
+    }
+    order[j + 1] = e;
+  }
+  int rows[16] = {0}, cols[16] = {0};
+  for (int e = 0; e < cnt; e++) keep[e] = 0;
+  for (int i = 0; i < cnt; i++) {
+    int e = order[i], r = e / m, c = e % m;
+    if (rows[r] < n && cols[c] < n) {
+      keep[e] = 1;
+      rows[r]++;
+      cols[c]++;
+    }
+  }
+}
+
+int nmo_tmask_greedy(const void* W, int dt, int64_t R, int64_t K, int n, int m, uint8_t* mask) {
+  int rc = check_tshape(dt, R, K, n, m);
+  if (rc) return rc;
+  uint8_t keep[256];
+  for (int64_t r0 = 0; r0 < R; r0 += m)
+    for (int64_t c0 = 0; c0 < K; c0 += m) {
+      greedy_block(W, dt, K, r0, c0, n, m, keep);
+      for (int e = 0; e < m * m; e++) mask[(r0 + e / m) * K + c0 + e % m] = keep[e];
+    }
+  return 0;
+}
+
+/* The optimum, as a minimum-cost flow: source -> row i (capacity n), row i ->  */
+/* column j (capacity 1, cost -|w_ij|), column j -> sink (capacity n).  Flow is */
+/* pushed one unit at a time along a cheapest source-sink path of the residual  */
+/* graph (Bellman-Ford, since costs are negative), while such a path lowers the */
+/* cost; the row->column arcs that carry flow form the mask.  Costs are doubles */
+/* (|w| of every format is exact in double); the optimum's ties are not fixed.  */
+#define TF_MAXV (2 * 16 + 2)
+int nmo_tmask_optimal(const void* W, int dt, int64_t R, int64_t K, int n, int m, uint8_t* mask,
+                      double* kept_l1) {
+  int rc = check_tshape(dt, R, K, n, m);
+  if (rc) return rc;
+  const int V = 2 * m + 2, S = 2 * m, T = 2 * m + 1;
+  double total = 0.0;
+  for (int64_t r0 = 0; r0 < R; r0 += m)
+    for (int64_t c0 = 0; c0 < K; c0 += m) {
+      double cost[TF_MAXV][TF_MAXV];
+      int cap[TF_MAXV][TF_MAXV];
+      for (int a = 0; a < V; a++)
+        for (int b = 0; b < V; b++) {
+          cost[a][b] = 0.0;
+          cap[a][b] = 0;
+        }
+      for (int i = 0; i < m; i++) {
+        cap[S][i] = n;
+        cap[m + i][T] = n;
+        for (int j = 0; j < m; j++) {
+          double a = fabs(nmo_to_double(W, dt, (r0 + i) * K + c0 + j));
+          if (isnan(a)) a = INFINITY;
+          if (isinf(a)) a = 1e300; /* Inf and NaN outrank every finite value */
+          cap[i][m + j] = 1;
+          cost[i][m + j] = -a;
+          cost[m + j][i] = a; /* residual arc */
+        }
+      }
+      for (;;) {
+        double dist[TF_MAXV];
+        int prev[TF_MAXV];
+        for (int v = 0; v < V; v++) {
+          dist[v] = INFINITY;
+          prev[v] = -1;
+        }
+        dist[S] = 0.0;
+        for (int it = 0; it < V; it++) {
+          int changed = 0;
+          for (int a = 0; a < V; a++) {
+            if (dist[a] == INFINITY) continue;
+            for (int b = 0; b < V; b++)
+              if (cap[a][b] > 0 && dist[a] + cost[a][b] < dist[b]) {
+                dist[b] = dist[a] + cost[a][b];
+                prev[b] = a;
+                changed = 1;
+              }
+          }
+          if (!changed) break;
+        }
+        if (dist[T] == INFINITY || dist[T] >= 0.0) break; /* no improving path left */
+        for (int v = T; v != S; v = prev[v]) {
+          cap[prev[v]][v] -= 1;
+          cap[v][prev[v]] += 1;
+        }
+      }
+      for (int i = 0; i < m; i++)
+        for (int j = 0; j < m; j++) {
+          int used = cap[i][m + j] == 0;
+          mask[(r0 + i) * K + c0 + j] = (uint8_t)used;
+          if (used) total += -cost[i][m + j];
+        }
+    }
+  if (kept_l1) *kept_l1 = total;
+  return 0;
+}
+
+/* Forward weight under the greedy transposable mask: W where kept, +0 where pruned. */
+int nmo_tprune(const void* W, int dt, int64_t R, int64_t K, int n, int m, void* W_out) {
+  int rc = check_tshape(dt, R, K, n, m);
+  if (rc) return rc;
+  uint8_t keep[256];
+  for (int64_t r0 = 0; r0 < R; r0 += m)
+    for (int64_t c0 = 0; c0 < K; c0 += m) {
+      greedy_block(W, dt, K, r0, c0, n, m, keep);
+      for (int e = 0; e < m * m; e++) {
+        int64_t i = (r0 + e / m) * K + c0 + e % m;
+        if (keep[e])
+          copy_elem(W_out, W, dt, i);
+        else
+          zero_elem(W_out, dt, i);
+      }
+    }
+  return 0;
+}

@@ -25,6 +25,12 @@
  *            - section "Tensor Scores 상에서 구조적인 sparse GEMM": sparse (first,
  *              compressed) operand times dense operand gives a dense result.
  *            - section "Step-2: Weight Pruning": drop the two smallest of each four.
+ *   [TRANS]  "[论文解读] Accelerated Sparse Neural Training: A Provable and Efficient
+ *            Method to Find N:M Transposable Masks" (nubint.ai)
+ *            - ABSTRACT and section "提出的方法": a transposable mask makes W and its
+ *              transpose follow the same N:M pattern, chosen per M x M block to
+ *              maximise the kept L1 norm with N per row and column; the optimum is a
+ *              minimum-cost flow, the fast method a greedy 2-approximation.
  *
  * Readings where the pages are silent (each also listed in the design doc):
  *   - N counts KEPT elements; exactly N values are stored per group.
@@ -45,6 +51,11 @@
  *   - SR-STE's gradient is G bit for bit where the weight is kept (the decay
  *     term is zero there); where it is pruned it is fl32(fl32(decay*w) + g),
  *     rounded once more to the element type, in the printed backward's order.
+ *   - Transposable masks: M x M blocks aligned at multiples of M (R and K must be
+ *     multiples of M).  The greedy takes a block's entries by descending exact
+ *     magnitude, equal magnitudes in ascending row-major position, and keeps an
+ *     entry while its row and its column hold fewer than N; rows and columns can
+ *     end with fewer than N kept (at least M-N zeros, the review's own count).
  *
  * Conventions: every matrix is dense row-major; W is R x K with groups along
  * K; values R x (K*N/M); meta R x words_per_row uint32; X K x T; Y R x T.
@@ -99,6 +110,17 @@ int nmo_prune(const void* W, int dt, int64_t R, int64_t K, int n, int m, void* W
  * (SR-STE backward) */
 int nmo_srste_grad(const void* W, const void* G, int dt, int64_t R, int64_t K, int n, int m,
                    float decay, void* G_out);
+
+/* transposable mask by the greedy 2-approximation (R % m == 0, K % m == 0) */
+int nmo_tmask_greedy(const void* W, int dt, int64_t R, int64_t K, int n, int m, uint8_t* mask);
+
+/* transposable mask of maximal kept L1 per block (minimum-cost flow, double costs);
+ * *kept_l1 (if not NULL) receives the kept L1 norm summed over all blocks */
+int nmo_tmask_optimal(const void* W, int dt, int64_t R, int64_t K, int n, int m, uint8_t* mask,
+                      double* kept_l1);
+
+/* W where the greedy transposable mask keeps it, +0 elsewhere */
+int nmo_tprune(const void* W, int dt, int64_t R, int64_t K, int n, int m, void* W_out);
 
 /* out[i] = in[i] rounded to dt (round to nearest, ties to even; fp32 copies) */
 int nmo_round_from_f32(const float* in, int dt, int64_t count, void* out);
