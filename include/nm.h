@@ -54,6 +54,10 @@
  *   "量化友好的SR-STE稀疏化训练", section "基于直通估计的动态掩码精炼化稀疏(SR-STE)"
  *   (the mask is searched again from the weights at every training step; the
  *   backward adds decay * w to the gradient where the mask prunes w).
+ *   "[论文解读] Accelerated Sparse Neural Training: A Provable and Efficient Method
+ *   to Find N:M Transposable Masks", ABSTRACT and section "提出的方法" (one mask per
+ *   M x M block with N kept per row and column serves W and its transpose; a
+ *   greedy 2-approximation finds it in near-linear time).
  */
 #ifndef NM_H
 #define NM_H
@@ -65,7 +69,7 @@
 extern "C" {
 #endif
 
-#define NM_ABI_VERSION 3
+#define NM_ABI_VERSION 4
 
 typedef enum {
   NM_OK = 0,
@@ -165,6 +169,38 @@ nm_status nm_prune(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int 
  * NM_ERR_ALIAS.  W, G and G_out must be 16-byte aligned. */
 nm_status nm_srste_grad(const void* W, const void* G, nm_dtype dt, int64_t R, int64_t K, int n,
                         int m, float decay, void* G_out, nm_stream_t stream);
+
+/* Transposable N:M mask ("Accelerated Sparse Neural Training ... N:M Transposable
+ * Masks", "提出的方法"), greedy 2-approximation: W is cut into m x m blocks (R and K
+ * must be multiples of m, else NM_ERR_SHAPE); in each block the entries are taken by
+ * descending |w| (the nm_mask order: NaN > Inf > finite, equal magnitudes in
+ * ascending row-major position within the block) and an entry is kept while its row
+ * and its column of the block hold fewer than n kept entries.  Every row and column
+ * of a block then keeps at most n (a row and a column can end with fewer), so W and
+ * W^T both have at most n nonzeros in every group of m along their rows.  Writes
+ * mask (R x K, uint8, 1 = kept); mask must not overlap W (NM_ERR_ALIAS). */
+nm_status nm_tmask(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m, uint8_t* mask,
+                   nm_stream_t stream);
+
+/* W_out (R x K, dt) = W where nm_tmask keeps it (bit for bit), +0 elsewhere: the weight
+ * both products of a training step use.  nm_compress of W_out gives the forward
+ * operand and nm_compress_t of W_out the backward one; both keep every nonzero of
+ * W_out.  W_out may be W itself; any other overlap returns NM_ERR_ALIAS. */
+nm_status nm_tprune(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m, void* W_out,
+                    nm_stream_t stream);
+
+/* nm_compress of W's transpose, without forming it: W is R x K row-major; the output
+ * describes the K x R matrix W^T, groups of m running along R (R % m == 0, else
+ * NM_ERR_SHAPE; NM_LAYOUT_BLOCKED needs R % 64 == 0, else NM_ERR_LAYOUT).  values
+ * and meta have the sizes nm_values_bytes(K, R, n, m, dt, layout) and
+ * nm_meta_bytes(K, R, n, m, layout), and the layout of nm_compress for a K x R
+ * matrix, so nm_spmm(values, meta, K, R, ..., dY, T, ...) computes W^T dY, the
+ * backward product ("Tensor Scores 상에서 구조적인 sparse GEMM" with the transposed
+ * operand).  NM_LAYOUT_BLOCKED is the fast path (row-contiguous reads of W, whole
+ * 1 KB blocks written); NM_LAYOUT_ROWS is correct but slower.  values and meta must
+ * not overlap W (NM_ERR_ALIAS). */
+nm_status nm_compress_t(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m,
+                        nm_layout layout, void* values, uint32_t* meta, nm_stream_t stream);
 
 #ifdef __cplusplus
 }

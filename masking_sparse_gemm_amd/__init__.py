@@ -11,6 +11,8 @@ library functions raises.
     Wd = decompress(values, meta, 2, 4, K)    # dense (R, K), +0 where pruned
     Wp = prune(W, 2, 4)                       # SR-STE forward weight: W where kept, +0 else
     srste_grad(W, G, 2, 4, out=G)             # SR-STE backward, in place on G
+    Wt = tprune(W, 2, 4)                      # transposable 2:4 mask applied (4x4 blocks)
+    vt, mt = compress_t(Wt, 2, 4)             # compressed W^T: spmm(vt, mt, dY) = W^T dY
 
 The compressed pair comes in two layouts (defined in include/nm.h): "rows"
 (values (R, K*n/m), meta (R, words)) and "blocked" (blocks of 16 rows x 64
@@ -34,12 +36,12 @@ _TORCH_DT = {v: k for k, v in _DT.items()}
 STATUS = ["ok", "null", "shape", "pattern", "dtype", "align", "unsupported", "device", "layout",
           "alias"]
 LAYOUTS = {"rows": 0, "blocked": 1}
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 # every function the C header declares
 EXPORTS = ("nm_abi_version", "nm_status_str", "nm_values_bytes", "nm_meta_bytes",
            "nm_meta_words_per_row", "nm_mask", "nm_compress", "nm_decompress", "nm_spmm",
-           "nm_prune", "nm_srste_grad")
+           "nm_prune", "nm_srste_grad", "nm_tmask", "nm_tprune", "nm_compress_t")
 SRSTE_DECAY = 0.0002  # the SR-STE page's default decay
 
 
@@ -76,8 +78,11 @@ def lib() -> ctypes.CDLL:
         L.nm_spmm.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, i64, i32, vp, i32, vp]
         L.nm_prune.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp]
         L.nm_srste_grad.argtypes = [vp, vp, i32, i64, i64, i32, i32, ctypes.c_float, vp, vp]
+        L.nm_tmask.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp]
+        L.nm_tprune.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp]
+        L.nm_compress_t.argtypes = [vp, i32, i64, i64, i32, i32, i32, vp, vp, vp]
         for f in ("nm_mask", "nm_compress", "nm_decompress", "nm_spmm", "nm_prune",
-                  "nm_srste_grad"):
+                  "nm_srste_grad", "nm_tmask", "nm_tprune", "nm_compress_t"):
             getattr(L, f).restype = i32
         if L.nm_abi_version() != ABI_VERSION:
             raise ImportError(f"{LIB_PATH} has ABI {L.nm_abi_version()}, expected {ABI_VERSION}: "
@@ -250,3 +255,39 @@ def srste_grad(W: torch.Tensor, G: torch.Tensor, n: int = 2, m: int = 4,
     _check("nm_srste_grad", lib().nm_srste_grad(_ptr(W), _ptr(G), dt, R, K, n, m, float(decay),
                                                 _ptr(out), _stream(W)))
     return out
+
+
+def tmask(W: torch.Tensor, n: int = 2, m: int = 4) -> torch.Tensor:
+    """Bool (R, K): the transposable N:M mask (greedy, per m x m block)."""
+    dt = _dense_input(W, "W")
+    R, K = W.shape
+    out = torch.empty((R, K), dtype=torch.bool, device=W.device)
+    _check("nm_tmask", lib().nm_tmask(_ptr(W), dt, R, K, n, m, _ptr(out), _stream(W)))
+    return out
+
+
+def tprune(W: torch.Tensor, n: int = 2, m: int = 4, out: torch.Tensor | None = None) -> torch.Tensor:
+    """W where the transposable mask keeps it, +0 elsewhere (out may be W)."""
+    dt = _dense_input(W, "W")
+    R, K = W.shape
+    if out is None:
+        out = torch.empty_like(W)
+    else:
+        _same_dense(out, W, "out")
+    _check("nm_tprune", lib().nm_tprune(_ptr(W), dt, R, K, n, m, _ptr(out), _stream(W)))
+    return out
+
+
+def compress_t(W: torch.Tensor, n: int = 2, m: int = 4, layout: str = "rows"):
+    """compress() of W's transpose (a K x R matrix, groups along R) without forming it."""
+    dt = _dense_input(W, "W")
+    R, K = W.shape
+    lay = _layout(layout)
+    if R % m:
+        _check("nm_compress_t", 2)
+    vshape, mshape = compressed_shapes(K, R, n, m, layout)
+    values = torch.empty(vshape, dtype=W.dtype, device=W.device)
+    meta = torch.empty(mshape, dtype=torch.int32, device=W.device)
+    _check("nm_compress_t", lib().nm_compress_t(_ptr(W), dt, R, K, n, m, lay, _ptr(values),
+                                                _ptr(meta), _stream(W)))
+    return values, meta

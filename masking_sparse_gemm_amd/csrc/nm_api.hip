@@ -51,11 +51,12 @@ nm_status check_device() {
   return state == 1 ? NM_OK : NM_ERR_DEVICE;
 }
 
-// Do the byte ranges [a, a + n) and [b, b + n) share a byte?
-bool overlaps(const void* a, const void* b, int64_t bytes) {
+// Do the byte ranges [a, a + a_bytes) and [b, b + b_bytes) share a byte?
+bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
-  return bytes > 0 && x < y + (uintptr_t)bytes && y < x + (uintptr_t)bytes;
+  return a_bytes > 0 && b_bytes > 0 && x < y + (uintptr_t)b_bytes && y < x + (uintptr_t)a_bytes;
 }
+bool overlaps(const void* a, const void* b, int64_t bytes) { return overlaps(a, bytes, b, bytes); }
 
 nm_status from_hip(hipError_t e) { return e == hipSuccess ? NM_OK : NM_ERR_DEVICE; }
 
@@ -180,6 +181,57 @@ nm_status nm_spmm(const void* values, const uint32_t* meta, int64_t R, int64_t K
   if ((st = check_device()) != NM_OK) return st;
   return from_hip(nm::launch_spmm(values, meta, R, K, n, m, layout == NM_LAYOUT_BLOCKED, X, T,
                                   (int)dt, Y, (int)y_dt, static_cast<hipStream_t>(stream)));
+}
+
+nm_status nm_tmask(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m, uint8_t* mask,
+                   nm_stream_t stream) {
+  if (!valid_dtype(dt)) return NM_ERR_DTYPE;
+  nm_status st = check_pattern(n, m);
+  if (st != NM_OK) return st;
+  if ((st = check_shape(R, K, m)) != NM_OK) return st;
+  if (R % m != 0) return NM_ERR_SHAPE;
+  if (missing(W, R * K) || missing(mask, R * K)) return NM_ERR_NULL;
+  if (R * K == 0) return NM_OK;
+  if (overlaps(W, R * K * elem_bytes(dt), mask, R * K)) return NM_ERR_ALIAS;
+  if (!aligned16(W) || !aligned16(mask)) return NM_ERR_ALIGN;
+  if ((st = check_device()) != NM_OK) return st;
+  return from_hip(nm::launch_tmask(W, elem_bytes(dt), R, K, n, m, false, mask,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+nm_status nm_tprune(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m, void* W_out,
+                    nm_stream_t stream) {
+  if (!valid_dtype(dt)) return NM_ERR_DTYPE;
+  nm_status st = check_pattern(n, m);
+  if (st != NM_OK) return st;
+  if ((st = check_shape(R, K, m)) != NM_OK) return st;
+  if (R % m != 0) return NM_ERR_SHAPE;
+  if (missing(W, R * K) || missing(W_out, R * K)) return NM_ERR_NULL;
+  if (R * K == 0) return NM_OK;
+  if (W_out != W && overlaps(W, W_out, R * K * elem_bytes(dt))) return NM_ERR_ALIAS;
+  if (!aligned16(W) || !aligned16(W_out)) return NM_ERR_ALIGN;
+  if ((st = check_device()) != NM_OK) return st;
+  return from_hip(nm::launch_tmask(W, elem_bytes(dt), R, K, n, m, true, W_out,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+nm_status nm_compress_t(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m,
+                        nm_layout layout, void* values, uint32_t* meta, nm_stream_t stream) {
+  if (!valid_dtype(dt)) return NM_ERR_DTYPE;
+  nm_status st = check_pattern(n, m);
+  if (st != NM_OK) return st;
+  if ((st = check_shape(K, R, m)) != NM_OK) return st;  // the transpose is K x R
+  if ((st = check_layout(layout, R)) != NM_OK) return st;
+  if (missing(W, R * K) || missing(values, R * K) || missing(meta, R * K)) return NM_ERR_NULL;
+  if (R * K == 0) return NM_OK;
+  const int64_t wb = R * K * elem_bytes(dt);
+  if (overlaps(W, wb, values, (int64_t)nm_values_bytes(K, R, n, m, dt, layout)) ||
+      overlaps(W, wb, meta, (int64_t)nm_meta_bytes(K, R, n, m, layout)))
+    return NM_ERR_ALIAS;
+  if (!aligned16(W) || !aligned16(values) || !aligned16(meta)) return NM_ERR_ALIGN;
+  if ((st = check_device()) != NM_OK) return st;
+  return from_hip(nm::launch_select_t(W, elem_bytes(dt), R, K, n, m, layout == NM_LAYOUT_BLOCKED,
+                                      values, meta, static_cast<hipStream_t>(stream)));
 }
 
 nm_status nm_prune(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m, void* W_out,

@@ -276,28 +276,17 @@ struct LaneShape {
   static constexpr bool kShuffle = 32 % kBits == 0;           // whole lanes per word
 };
 
+// Selection, value packing and metadata packing of one lane's 16 elements of a block
+// (row l / 4 of the block, elements 16 (l % 4) .. +15 of its step); `live` false writes
+// the zeros of a padding row.  `bits_buf` is the wave's LDS word buffer (used when a
+// lane's metadata bits do not divide 32).
 template <typename E, int N, int M>
-__global__ void __launch_bounds__(kThreads) blocked_select_kernel(const uint32_t* __restrict__ W,
-                                                                  int64_t R, int64_t K,
-                                                                  int64_t blocks,
-                                                                  uint32_t* __restrict__ values,
-                                                                  uint32_t* __restrict__ meta) {
+__device__ __forceinline__ void blocked_emit(const uint32_t (&w)[LaneShape<E, N, M>::kWords],
+                                             bool live, int64_t blk, int lane, uint32_t* bits_buf,
+                                             uint32_t* __restrict__ values,
+                                             uint32_t* __restrict__ meta) {
   using L = LaneShape<E, N, M>;
   constexpr int b = meta_bits(M);
-  __shared__ uint32_t lds_bits[kThreads / 64][L::kShuffle ? 1 : L::kBlockMetaWords];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t blk = (int64_t)blockIdx.x * (kThreads / 64) + wave;
-  if (blk >= blocks) return;  // the whole wave
-  const int64_t steps = K / 64;
-  const int64_t row = 16 * (blk / steps) + (lane >> 2);
-  const bool live = row < R;
-  uint32_t w[L::kWords];
-  if (live) {
-    load_words<L::kWords>(W + (row * K + 64 * (blk % steps) + 16 * (lane & 3)) * sizeof(E) / 4, w);
-  } else {
-#pragma unroll
-    for (int i = 0; i < L::kWords; ++i) w[i] = 0;
-  }
   uint32_t vw[L::kValWords];
 #pragma unroll
   for (int i = 0; i < L::kValWords; ++i) vw[i] = 0;
@@ -329,7 +318,7 @@ __global__ void __launch_bounds__(kThreads) blocked_select_kernel(const uint32_t
     const uint32_t word = or_reduce_lanes<LPW>((uint32_t)bits << ((lane % LPW) * L::kBits));
     if (lane % LPW == 0) mblk[lane / LPW] = word;
   } else {
-    uint32_t* buf = lds_bits[wave];
+    uint32_t* buf = bits_buf;
     for (int i = lane; i < L::kBlockMetaWords; i += 64) buf[i] = 0;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -341,6 +330,145 @@ __global__ void __launch_bounds__(kThreads) blocked_select_kernel(const uint32_t
     __builtin_amdgcn_wave_barrier();
     for (int i = lane; i < L::kBlockMetaWords; i += 64) mblk[i] = buf[i];
   }
+}
+
+template <typename E, int N, int M>
+__global__ void __launch_bounds__(kThreads) blocked_select_kernel(const uint32_t* __restrict__ W,
+                                                                  int64_t R, int64_t K,
+                                                                  int64_t blocks,
+                                                                  uint32_t* __restrict__ values,
+                                                                  uint32_t* __restrict__ meta) {
+  using L = LaneShape<E, N, M>;
+  __shared__ uint32_t lds_bits[kThreads / 64][L::kShuffle ? 1 : L::kBlockMetaWords];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t blk = (int64_t)blockIdx.x * (kThreads / 64) + wave;
+  if (blk >= blocks) return;  // the whole wave
+  const int64_t steps = K / 64;
+  const int64_t row = 16 * (blk / steps) + (lane >> 2);
+  const bool live = row < R;
+  uint32_t w[L::kWords];
+  if (live) {
+    load_words<L::kWords>(W + (row * K + 64 * (blk % steps) + 16 * (lane & 3)) * sizeof(E) / 4, w);
+  } else {
+#pragma unroll
+    for (int i = 0; i < L::kWords; ++i) w[i] = 0;
+  }
+  blocked_emit<E, N, M>(w, live, blk, lane, lds_bits[wave], values, meta);
+}
+
+// The blocked layout of W's TRANSPOSE (K x R, groups of M along R; R % 64 == 0): block
+// (g, s) holds transposed rows 16g .. 16g+15, i.e. columns 16g .. of W, and step s,
+// i.e. rows 64s .. 64s+63 of W.  The wave stages that 64 x 16 tile of W in LDS with
+// row-contiguous loads (4 waves of a workgroup take neighbouring column groups, so
+// together they read whole 128-byte lines), then each lane gathers its 16 elements
+// down one column and proceeds as for W itself.  Columns past K are padding (zeros).
+template <typename E, int N, int M>
+__global__ void __launch_bounds__(kThreads) blocked_select_t_kernel(
+    const E* __restrict__ W, int64_t R, int64_t K, int64_t blocks, uint32_t* __restrict__ values,
+    uint32_t* __restrict__ meta) {
+  using L = LaneShape<E, N, M>;
+  constexpr int kChunkElems = 16 / (int)sizeof(E);      // elements per 16-byte chunk
+  constexpr int kChunksPerRow = 16 / kChunkElems;       // 2 (16-bit) or 4 (fp32)
+  __shared__ uint32_t lds_bits[kThreads / 64][L::kShuffle ? 1 : L::kBlockMetaWords];
+  __shared__ __align__(16) E tile[kThreads / 64][64][16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // workgroup x covers 4 consecutive column groups of one step: blk = g * S + s
+  const int64_t steps = R / 64, groups = (K + 15) / 16;
+  const int64_t s = (int64_t)blockIdx.x % steps;
+  const int64_t g = ((int64_t)blockIdx.x / steps) * (kThreads / 64) + wave;
+  if (g >= groups) return;  // the whole wave
+  const int64_t blk = g * steps + s;
+  const int64_t r0 = 64 * s, c0 = 16 * g;
+  const bool vec_ok = (K * (int64_t)sizeof(E)) % 16 == 0;
+#pragma unroll
+  for (int it = 0; it < kChunksPerRow; ++it) {
+    const int chunk = it * 64 + lane;             // 64 rows x kChunksPerRow chunks
+    const int r = chunk / kChunksPerRow, ch = chunk % kChunksPerRow;
+    const int64_t col = c0 + ch * kChunkElems;
+    const E* src = W + (r0 + r) * K + col;
+    E* dst = &tile[wave][r][ch * kChunkElems];
+    if (vec_ok && col + kChunkElems <= K) {
+      *reinterpret_cast<u32x4_t*>(dst) = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src));
+    } else {
+#pragma unroll
+      for (int e = 0; e < kChunkElems; ++e) dst[e] = (col + e < K) ? src[e] : (E)0;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int col = lane >> 2, q = lane & 3;
+  const bool live = c0 + col < K;
+  uint32_t w[L::kWords];
+#pragma unroll
+  for (int i = 0; i < L::kWords; ++i) w[i] = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t v = (uint32_t)tile[wave][16 * q + i][col];
+    if constexpr (sizeof(E) == 2)
+      w[i / 2] |= v << (16 * (i % 2));
+    else
+      w[i] = v;
+  }
+  blocked_emit<E, N, M>(w, live, blk, lane, lds_bits[wave], values, meta);
+}
+
+// Row layout of W's transpose, slow path: one thread per transposed group (W column k,
+// rows gM .. gM+M-1), consecutive threads along k so that each of the M reads is
+// coalesced; the N values go to row k of the transposed value array.
+template <typename E, int N, int M>
+__global__ void __launch_bounds__(kThreads) group_t_kernel(const E* __restrict__ W, int64_t R,
+                                                           int64_t K, E* __restrict__ values) {
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= R / M * K) return;
+  const int64_t g = idx / K, k = idx % K;
+  uint32_t key[M], v[M];
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    v[i] = W[(g * M + i) * K + k];
+    key[i] = v[i] & Elem<E>::kKeyMask;
+  }
+  int pos[N];
+  kept_positions<N>(keep_bits<N, M>(key), pos);
+  E* dst = values + k * (R / M * N) + g * N;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    uint32_t x = v[0];
+#pragma unroll
+    for (int i = 1; i < M; ++i) x = (pos[j] == i) ? v[i] : x;
+    dst[j] = (E)x;
+  }
+}
+
+// Metadata words of the transposed row layout: one thread per (W column k, word w).
+template <typename E, int N, int M>
+__global__ void __launch_bounds__(kThreads) meta_word_t_kernel(const E* __restrict__ W, int64_t R,
+                                                               int64_t K, int64_t wpr,
+                                                               uint32_t* __restrict__ meta) {
+  constexpr int b = meta_bits(M);
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= K * wpr) return;
+  const int64_t w = idx / K, k = idx % K;
+  const int64_t fields = R / M * N;
+  const int64_t f0 = (32 * w) / b;
+  int64_t f1 = (32 * w + 31) / b;
+  if (f1 > fields - 1) f1 = fields - 1;
+  uint32_t word = 0;
+  for (int64_t g = f0 / N; g <= f1 / N; ++g) {
+    uint32_t key[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) key[i] = (uint32_t)W[(g * M + i) * K + k] & Elem<E>::kKeyMask;
+    int pos[N];
+    kept_positions<N>(keep_bits<N, M>(key), pos);
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int64_t f = g * N + j;
+      if (f < f0 || f > f1) continue;
+      const int64_t off = f * b - 32 * w;
+      word |= off >= 0 ? (uint32_t)pos[j] << off : (uint32_t)pos[j] >> (-off);
+    }
+  }
+  meta[k * wpr + w] = word;
 }
 
 template <typename E, int N, int M>
@@ -554,6 +682,28 @@ hipError_t run_select(const void* W, int64_t R, int64_t K, bool blocked, void* v
 }
 
 template <typename E, int N, int M>
+hipError_t run_select_t(const void* W, int64_t R, int64_t K, bool blocked, void* values,
+                        uint32_t* meta, hipStream_t s) {
+  if (R * K == 0) return hipSuccess;
+  const E* w = static_cast<const E*>(W);
+  if (blocked) {
+    const int64_t steps = R / 64, groups = (K + 15) / 16;
+    const int64_t wg = (groups + kThreads / 64 - 1) / (kThreads / 64) * steps;
+    blocked_select_t_kernel<E, N, M><<<(unsigned)wg, kThreads, 0, s>>>(
+        w, R, K, groups * steps, static_cast<uint32_t*>(values), meta);
+    return hipGetLastError();
+  }
+  group_t_kernel<E, N, M><<<blocks_for(R / M * K, kThreads), kThreads, 0, s>>>(
+      w, R, K, static_cast<E*>(values));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t wpr = ((R / M) * N * meta_bits(M) + 31) / 32;
+  meta_word_t_kernel<E, N, M><<<blocks_for(K * wpr, kThreads), kThreads, 0, s>>>(w, R, K, wpr,
+                                                                                 meta);
+  return hipGetLastError();
+}
+
+template <typename E, int N, int M>
 hipError_t run_decompress(const void* values, const uint32_t* meta, int64_t R, int64_t K,
                           bool blocked, void* out, hipStream_t s) {
   using S = UnitShape<E, M>;
@@ -601,6 +751,13 @@ struct SelectOp {
   }
 };
 template <typename E, int N, int M>
+struct SelectTOp {
+  static hipError_t run(const void* W, int64_t R, int64_t K, bool blocked, void* values,
+                        uint32_t* meta, hipStream_t s) {
+    return run_select_t<E, N, M>(W, R, K, blocked, values, meta, s);
+  }
+};
+template <typename E, int N, int M>
 struct DecompressOp {
   static hipError_t run(const void* values, const uint32_t* meta, int64_t R, int64_t K,
                         bool blocked, void* out, hipStream_t s) {
@@ -616,6 +773,13 @@ hipError_t launch_select(const void* W, int elem_bytes, int64_t R, int64_t K, in
   if (elem_bytes == 2)
     return dispatch_nm<uint16_t, SelectOp>(n, m, W, R, K, blocked, values, meta, mask, s);
   return dispatch_nm<uint32_t, SelectOp>(n, m, W, R, K, blocked, values, meta, mask, s);
+}
+
+hipError_t launch_select_t(const void* W, int elem_bytes, int64_t R, int64_t K, int n, int m,
+                           bool blocked, void* values, uint32_t* meta, hipStream_t s) {
+  if (elem_bytes == 2)
+    return dispatch_nm<uint16_t, SelectTOp>(n, m, W, R, K, blocked, values, meta, s);
+  return dispatch_nm<uint32_t, SelectTOp>(n, m, W, R, K, blocked, values, meta, s);
 }
 
 hipError_t launch_decompress(const void* values, const uint32_t* meta, int elem_bytes, int64_t R,

@@ -20,6 +20,15 @@ hipError_t launch_spmm(const void* values, const uint32_t* meta, int64_t R, int6
                        int m, bool blocked, const void* X, int64_t T, int dt, void* Y, int y_dt,
                        hipStream_t s);
 
+// Compress of W's transpose (the K x R matrix, groups of m along R; R % m == 0, and
+// R % 64 == 0 for the blocked layout).
+hipError_t launch_select_t(const void* W, int elem_bytes, int64_t R, int64_t K, int n, int m,
+                           bool blocked, void* values, uint32_t* meta, hipStream_t s);
+
+// Transposable mask of W (R % m == K % m == 0): mask bytes, or the pruned weight if `prune`.
+hipError_t launch_tmask(const void* W, int elem_bytes, int64_t R, int64_t K, int n, int m,
+                        bool prune, void* out, hipStream_t s);
+
 // SR-STE passes (dt in nm_dtype codes); `out` may be W (prune) or G (grad).
 hipError_t launch_prune(const void* W, int dt, int64_t R, int64_t K, int n, int m, void* out,
                         hipStream_t s);

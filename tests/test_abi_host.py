@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     L = nm.lib()
     for name in header_functions():
         assert hasattr(L, name), name
-    assert L.nm_abi_version() == nm.ABI_VERSION == 3
+    assert L.nm_abi_version() == nm.ABI_VERSION == 4
 
 
 @needs_lib
@@ -199,6 +199,61 @@ def test_prune_argument_errors(case, expect):
     a = dict(W=FAKE, out=FAKE + 0x100000, dt=nm.NM_F16, R=64, K=128, n=2, m=4)
     a.update(case)
     code = L.nm_prune(a["W"], a["dt"], a["R"], a["K"], a["n"], a["m"], a["out"], None)
+    assert nm.STATUS[code] == expect
+
+
+@needs_lib
+@pytest.mark.parametrize("case,expect", [
+    (dict(W=0), "null"),
+    (dict(out=0), "null"),
+    (dict(dt=6), "dtype"),
+    (dict(n=3, m=6), "pattern"),
+    (dict(R=62), "shape"),                           # R % m != 0
+    (dict(K=66, m=4), "shape"),
+    (dict(W=FAKE + 8), "align"),
+    (dict(out=FAKE + 0x100004), "align"),
+])
+def test_tmask_tprune_argument_errors(case, expect):
+    L = nm.lib()
+    a = dict(W=FAKE, out=FAKE + 0x100000, dt=nm.NM_BF16, R=64, K=128, n=2, m=4)
+    a.update(case)
+    for fn in (L.nm_tmask, L.nm_tprune):
+        code = fn(a["W"], a["dt"], a["R"], a["K"], a["n"], a["m"], a["out"], None)
+        assert nm.STATUS[code] == expect, fn.__name__
+
+
+@needs_lib
+def test_tmask_tprune_aliasing():
+    L = nm.lib()
+    # W: 64 x 128 bf16 = 16 KiB at FAKE; the mask is 8 KiB
+    assert nm.STATUS[L.nm_tmask(FAKE, nm.NM_BF16, 64, 128, 2, 4, FAKE + 0x3000, None)] == "alias"
+    # a mask ending exactly where W starts does not overlap it: the (later) alignment
+    # check of a misaligned W reports instead
+    assert nm.STATUS[L.nm_tmask(FAKE + 0x2008, nm.NM_BF16, 64, 128, 2, 4, FAKE + 8, None)] == "align"
+    assert nm.STATUS[L.nm_tprune(FAKE, nm.NM_BF16, 64, 128, 2, 4, FAKE + 0x10, None)] == "alias"
+
+
+@needs_lib
+@pytest.mark.parametrize("case,expect", [
+    (dict(W=0), "null"),
+    (dict(values=0), "null"),
+    (dict(dt=3), "dtype"),
+    (dict(R=66), "shape"),                           # groups run along R
+    (dict(layout=1, R=96), "layout"),                # blocked needs R % 64 == 0
+    (dict(layout=1, K=100), "align"),                # K is free: reaches the alignment check
+    (dict(values=FAKE + 0x1000), "alias"),
+    (dict(meta=FAKE), "alias"),
+    (dict(meta=FAKE + 0x200004), "align"),
+])
+def test_compress_t_argument_errors(case, expect):
+    L = nm.lib()
+    a = dict(W=FAKE, values=FAKE + 0x100000, meta=FAKE + 0x200000, dt=nm.NM_BF16, R=64, K=128,
+             n=2, m=4, layout=0)
+    a.update(case)
+    if case == dict(layout=1, K=100):
+        a["W"] = FAKE + 8
+    code = L.nm_compress_t(a["W"], a["dt"], a["R"], a["K"], a["n"], a["m"], a["layout"],
+                           a["values"], a["meta"], None)
     assert nm.STATUS[code] == expect
 
 
