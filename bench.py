@@ -17,6 +17,9 @@ The SR-STE passes of a training step on the same weights (nm_prune, the
 forward's masked weight, and nm_srste_grad, the backward's gradient) are timed
 in a separate pass after the step, each launch after a cache-clearing fill, and
 reported under "srste" with their HBM roofline; they are not part of `value`.
+So is the transposable-mask path under "transposable": nm_tprune (greedy
+transposable mask applied), nm_compress_t (the compressed transpose) and the
+backward product W^T dY through nm_spmm.
 """
 from __future__ import annotations
 
@@ -214,6 +217,12 @@ def main() -> int:
         d["Y"] = torch.empty((w.R, w.T), dtype=tdt, device=dev)
         d["pruned"] = torch.empty((w.R, w.K), dtype=tdt, device=dev)
         d["grad"] = torch.empty((w.R, w.K), dtype=tdt, device=dev)
+        # transposable-mask path: pruned weight, compressed transpose, backward product
+        d["tpruned"] = torch.empty((w.R, w.K), dtype=tdt, device=dev)
+        vts, mts = nm.compressed_shapes(w.K, w.R, n, m, args.layout)
+        d["vals_t"] = torch.empty(vts, dtype=tdt, device=dev)
+        d["meta_t"] = torch.empty(mts, dtype=torch.int32, device=dev)
+        d["dX"] = torch.empty((w.K, w.T), dtype=tdt, device=dev)
         mats.append(d)
     dtype = mats[0]["dtype"]
     if args.copy_calibration:
@@ -242,6 +251,15 @@ def main() -> int:
         elif kind == "spmm":
             rc = L.nm_spmm(d["vals"].data_ptr(), d["meta"].data_ptr(), d["R"], d["K"], n, m, LAY,
                            d["Xd"].data_ptr(), d["T"], DT, d["Y"].data_ptr(), DT, sp)
+        elif kind == "tprune":
+            rc = L.nm_tprune(d["Wd"].data_ptr(), DT, d["R"], d["K"], n, m, d["tpruned"].data_ptr(),
+                             sp)
+        elif kind == "compress_t":
+            rc = L.nm_compress_t(d["tpruned"].data_ptr(), DT, d["R"], d["K"], n, m, LAY,
+                                 d["vals_t"].data_ptr(), d["meta_t"].data_ptr(), sp)
+        elif kind == "spmm_t":  # dX = W^T dY, with the forward output Y standing in for dY
+            rc = L.nm_spmm(d["vals_t"].data_ptr(), d["meta_t"].data_ptr(), d["K"], d["R"], n, m,
+                           LAY, d["Y"].data_ptr(), d["T"], DT, d["dX"].data_ptr(), DT, sp)
         elif kind == "prune":
             rc = L.nm_prune(d["Wd"].data_ptr(), DT, d["R"], d["K"], n, m, d["pruned"].data_ptr(), sp)
         else:
@@ -402,6 +420,45 @@ def main() -> int:
     srste["prune_frac_hbm"] = round(sr_tot["prune"][1] / sr_tot["prune"][0] / 1e9 / PEAK_HBM_GBS, 3)
     srste["step_us"] = round((g_t + sr_tot["prune"][0]) * 1e6, 1)
 
+    # ---- transposable-mask path on the same weights (not part of the step) ----
+    # tprune and compress_t are timed cold, like the SR-STE passes; the backward product
+    # in the step's manner (its operands fit the Infinity Cache only in part).
+    tr_kinds = ["tprune", "compress_t", "spmm_t"]
+    flush = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        step(kinds=tr_kinds)
+    torch.cuda.synchronize()
+    tr_ev = {}
+    for _ in range(args.steps):
+        for d in mats:
+            for kind in tr_kinds:
+                if kind != "spmm_t":
+                    flush.zero_()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                launch(d, kind)
+                e1.record(stream)
+                tr_ev.setdefault((d["name"], kind), []).append((e0, e1))
+    torch.cuda.synchronize()
+    del flush
+    transposable = {"kernels": {}}
+    for d in mats:
+        e = d["R"] * d["K"]
+        kept = e * n // m
+        meta_t = d["K"] * ((d["R"] // m * n * meta_bits(m) + 31) // 32) * 4
+        for kind in tr_kinds:
+            t = float(np.mean([a.elapsed_time(b) for a, b in tr_ev[(d["name"], kind)]])) * 1e-3
+            entry = {"us": round(t * 1e6, 2)}
+            if kind == "spmm_t":
+                entry["eff_tflops"] = round(2.0 * e * d["T"] / t / 1e12, 1)
+                entry["alg_tflops"] = round(2.0 * kept * d["T"] / t / 1e12, 1)
+            else:
+                ab = 2 * e * d["s"] if kind == "tprune" else e * d["s"] + kept * d["s"] + meta_t
+                entry.update(alg_bytes=ab, gbps=round(ab / t / 1e9, 1),
+                             frac_hbm=round(ab / t / 1e9 / PEAK_HBM_GBS, 3))
+            transposable["kernels"][f"{d['name']}.{kind}"] = entry
+
     cpu = None
     if not args.no_cpu:
         srste["cpu_baseline"] = srste_cpu_sample(mats, n, m)
@@ -433,6 +490,7 @@ def main() -> int:
         "dense_gemm": dense,
         "kernels": kernels,
         "srste": srste,
+        "transposable": transposable,
         "context": "pages: up to 2x dense math throughput on A100 sparse Tensor Cores (not a target)",
     }
     print(json.dumps(out), flush=True)

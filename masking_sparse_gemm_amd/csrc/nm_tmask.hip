@@ -8,9 +8,10 @@
 // 2-approximation of the best (maximal kept L1) such mask: take the block's entries
 // by descending magnitude and keep an entry while its row and column have room.
 //
-// One thread per block.  Consecutive threads take consecutive blocks along K, so row
-// i of every block of a wave is one contiguous run (M elements per lane, 8 to 32
-// bytes), loaded with one or two vector loads.  Each entry gets a composite key, its
+// One thread per block, or per 16-byte-wide run of adjacent blocks (two 4 x 4 blocks of
+// 16-bit values, four 2 x 2): consecutive threads take consecutive blocks along K, so
+// row i of every block of a wave is one contiguous run, loaded and stored with
+// non-temporal vector accesses.  Each entry gets a composite key, its
 // magnitude (sign-cleared bits: NaN > Inf > finite, as for the row mask) above its
 // reversed position inside the block, so that a descending order of keys is the
 // greedy's order with equal magnitudes in ascending row-major position.  A bitonic
@@ -43,15 +44,15 @@ __device__ __forceinline__ void load_row(const E* p, uint32_t (&v)[M]) {
   constexpr int kBytes = M * (int)sizeof(E);
   uint32_t w[kBytes / 4 > 0 ? kBytes / 4 : 1];
   if constexpr (kBytes == 4) {
-    w[0] = *reinterpret_cast<const uint32_t*>(p);
+    w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
   } else if constexpr (kBytes == 8) {
-    const u32x2_t x = *reinterpret_cast<const u32x2_t*>(p);
+    const u32x2_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
     w[0] = x[0];
     w[1] = x[1];
   } else {
 #pragma unroll
     for (int i = 0; i < kBytes / 16; ++i) {
-      const u32x4_t x = reinterpret_cast<const u32x4_t*>(p)[i];
+      const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p) + i);
       w[4 * i] = x[0];
       w[4 * i + 1] = x[1];
       w[4 * i + 2] = x[2];
@@ -77,13 +78,14 @@ __device__ __forceinline__ void store_row(E* p, const uint32_t (&v)[M]) {
       w[j] = v[j];
   }
   if constexpr (kBytes == 4) {
-    *reinterpret_cast<uint32_t*>(p) = w[0];
+    __builtin_nontemporal_store(w[0], reinterpret_cast<uint32_t*>(p));
   } else if constexpr (kBytes == 8) {
-    *reinterpret_cast<u32x2_t*>(p) = u32x2_t{w[0], w[1]};
+    __builtin_nontemporal_store(u32x2_t{w[0], w[1]}, reinterpret_cast<u32x2_t*>(p));
   } else {
 #pragma unroll
     for (int i = 0; i < kBytes / 16; ++i)
-      reinterpret_cast<u32x4_t*>(p)[i] = u32x4_t{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+      __builtin_nontemporal_store(u32x4_t{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]},
+                                  reinterpret_cast<u32x4_t*>(p) + i);
   }
 }
 
@@ -129,68 +131,111 @@ __host__ __device__ __forceinline__ uint64_t greedy_keep(const uint32_t (&v)[M][
       key[e] = ((T)(v[r][c] & Elem<E>::kKeyMask) << kPosBits) | (T)(L - 1 - e);
     }
   if constexpr (L > 1) sort_descending<T, L>(key);
-  uint32_t rows = 0, cols = 0;  // 4-bit counters
-  uint64_t keep = 0;
+  // The low bits of a sorted key give p = L-1-e: row M-1-p/M, column M-1-p%M.  Counters
+  // are kept per reversed row and column (field p/M of `rows`, p%M of `cols`, 4 bits
+  // each), which is the same partition, and the kept set is collected by p and reversed
+  // at the end.  Each field starts at 8 - N, so it reaches 8 (bit 3 set) exactly when
+  // its row or column holds N kept entries: an entry is taken iff neither bit 3 is set.
+  constexpr int kLogM = ilog2(M);
+  constexpr uint32_t kBias = (uint32_t)(8 - N) * (M == 8 ? 0x11111111u : M == 4 ? 0x1111u : 0x11u);
+  uint32_t rows = kBias, cols = kBias;
+  uint64_t keep_rev = 0;
 #pragma unroll
   for (int t = 0; t < L; ++t) {
-    const int e = L - 1 - (int)(key[t] & (T)(L - 1));
-    const int r = e / M, c = e % M;
-    const uint32_t rc = (rows >> (4 * r)) & 15u, cc = (cols >> (4 * c)) & 15u;
-    const bool take = rc < (uint32_t)N && cc < (uint32_t)N;
-    rows += take ? (1u << (4 * r)) : 0u;
-    cols += take ? (1u << (4 * c)) : 0u;
-    keep |= take ? (1ull << e) : 0ull;
+    const uint32_t p = (uint32_t)(key[t] & (T)(L - 1));
+    const uint32_t sh_r = (p >> kLogM) << 2, sh_c = (p & (M - 1)) << 2;
+    const uint32_t full = (rows >> sh_r) | (cols >> sh_c);
+    const uint32_t take = ((full >> 3) & 1u) ^ 1u;
+    rows += take << sh_r;
+    cols += take << sh_c;
+    keep_rev |= (uint64_t)take << p;
   }
-  return keep;
+  if constexpr (L == 64)
+    return __builtin_bitreverse64(keep_rev);
+  else
+    return __builtin_bitreverse32((uint32_t)keep_rev) >> (32 - L);
 }
 
 // kPrune: W_out = W where kept, +0 elsewhere; otherwise mask bytes (1 = kept).
-template <typename E, int N, int M, bool kPrune>
+// A thread takes BPT horizontally adjacent blocks (BPT * M elements of each row, at
+// most 16 bytes), so its loads and stores are as wide as possible and the BPT
+// independent sorts interleave.
+template <typename E, int N, int M, int BPT, bool kPrune>
 __global__ void __launch_bounds__(kThreads) tmask_kernel(const E* __restrict__ W, int64_t K,
-                                                         int64_t block_cols, int64_t blocks,
+                                                         int64_t units_per_row, int64_t units,
                                                          void* __restrict__ out) {
-  const int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (b >= blocks) return;
-  const int64_t r0 = (b / block_cols) * M, c0 = (b % block_cols) * M;
-  uint32_t v[M][M];
+  constexpr int C = BPT * M;  // columns per thread
+  const int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (u >= units) return;
+  const int64_t r0 = (u / units_per_row) * M, c0 = (u % units_per_row) * C;
+  uint32_t row[M][C];
 #pragma unroll
-  for (int r = 0; r < M; ++r) load_row<E, M>(W + (r0 + r) * K + c0, v[r]);
-  const uint64_t keep = greedy_keep<E, N, M>(v);
+  for (int r = 0; r < M; ++r) load_row<E, C>(W + (r0 + r) * K + c0, row[r]);
+  uint64_t keep[BPT];
+#pragma unroll
+  for (int b = 0; b < BPT; ++b) {
+    uint32_t v[M][M];
+#pragma unroll
+    for (int r = 0; r < M; ++r)
+#pragma unroll
+      for (int c = 0; c < M; ++c) v[r][c] = row[r][b * M + c];
+    keep[b] = greedy_keep<E, N, M>(v);
+  }
 #pragma unroll
   for (int r = 0; r < M; ++r) {
     if constexpr (kPrune) {
-      uint32_t o[M];
+      uint32_t o[C];
 #pragma unroll
-      for (int c = 0; c < M; ++c) o[c] = ((keep >> (r * M + c)) & 1u) ? v[r][c] : 0u;
-      store_row<E, M>(static_cast<E*>(out) + (r0 + r) * K + c0, o);
+      for (int b = 0; b < BPT; ++b)
+#pragma unroll
+        for (int c = 0; c < M; ++c)
+          o[b * M + c] = ((keep[b] >> (r * M + c)) & 1u) ? row[r][b * M + c] : 0u;
+      store_row<E, C>(static_cast<E*>(out) + (r0 + r) * K + c0, o);
     } else {
       uint8_t* dst = static_cast<uint8_t*>(out) + (r0 + r) * K + c0;
-      const uint32_t bits = (uint32_t)(keep >> (r * M)) & ((1u << M) - 1u);
-      // byte c = bit c of the row
-      uint64_t bytes = 0;
+      uint64_t bytes = 0;  // byte j = column j of the thread's row
 #pragma unroll
-      for (int c = 0; c < M; ++c) bytes |= (uint64_t)((bits >> c) & 1u) << (8 * c);
-      if constexpr (M == 8)
-        *reinterpret_cast<uint64_t*>(dst) = bytes;
-      else if constexpr (M == 4)
-        *reinterpret_cast<uint32_t*>(dst) = (uint32_t)bytes;
-      else
-        *reinterpret_cast<uint16_t*>(dst) = (uint16_t)bytes;
+      for (int b = 0; b < BPT; ++b)
+#pragma unroll
+        for (int c = 0; c < M; ++c)
+          bytes |= (uint64_t)((keep[b] >> (r * M + c)) & 1u) << (8 * (b * M + c));
+      static_assert(C <= 8, "at most 16 bytes of 16-bit values or 8 fp32 per thread row");
+      if constexpr (C == 8) {
+        __builtin_nontemporal_store(bytes, reinterpret_cast<uint64_t*>(dst));
+      } else if constexpr (C == 4) {
+        __builtin_nontemporal_store((uint32_t)bytes, reinterpret_cast<uint32_t*>(dst));
+      } else {
+        __builtin_nontemporal_store((uint16_t)bytes, reinterpret_cast<uint16_t*>(dst));
+      }
     }
   }
 }
 
+template <typename E, int N, int M, int BPT, bool kPrune>
+hipError_t launch_tmask_bpt(const E* w, int64_t R, int64_t K, void* out, hipStream_t s) {
+  const int64_t per_row = K / (BPT * M), units = (R / M) * per_row;
+  if (units == 0) return hipSuccess;
+  tmask_kernel<E, N, M, BPT, kPrune>
+      <<<(unsigned)((units + kThreads - 1) / kThreads), kThreads, 0, s>>>(w, K, per_row, units, out);
+  return hipGetLastError();
+}
+
+template <typename E, int N, int M, bool kPrune>
+hipError_t launch_tmask_nm(const E* w, int64_t R, int64_t K, void* out, hipStream_t s) {
+  // widest thread: BPT blocks side by side, up to 16 bytes of a row
+  constexpr int kWide = 16 / (M * (int)sizeof(E)) > 1 ? 16 / (M * (int)sizeof(E)) : 1;
+  if constexpr (kWide > 1) {
+    if (K % (kWide * M) == 0) return launch_tmask_bpt<E, N, M, kWide, kPrune>(w, R, K, out, s);
+  }
+  return launch_tmask_bpt<E, N, M, 1, kPrune>(w, R, K, out, s);
+}
+
 template <typename E, bool kPrune>
 hipError_t run_tmask(int n, int m, const void* W, int64_t R, int64_t K, void* out, hipStream_t s) {
-  const int64_t block_cols = K / m, blocks = (R / m) * block_cols;
-  if (blocks == 0) return hipSuccess;
-  const unsigned grid = (unsigned)((blocks + kThreads - 1) / kThreads);
+  if (R == 0 || K == 0) return hipSuccess;
   const E* w = static_cast<const E*>(W);
-#define NM_TMASK_CASE(NN, MM)                                                                  \
-  if (n == NN && m == MM) {                                                                    \
-    tmask_kernel<E, NN, MM, kPrune><<<grid, kThreads, 0, s>>>(w, K, block_cols, blocks, out);  \
-    return hipGetLastError();                                                                  \
-  }
+#define NM_TMASK_CASE(NN, MM) \
+  if (n == NN && m == MM) return launch_tmask_nm<E, NN, MM, kPrune>(w, R, K, out, s);
   NM_TMASK_CASE(1, 2) NM_TMASK_CASE(2, 2)
   NM_TMASK_CASE(1, 4) NM_TMASK_CASE(2, 4) NM_TMASK_CASE(3, 4) NM_TMASK_CASE(4, 4)
   NM_TMASK_CASE(1, 8) NM_TMASK_CASE(2, 8) NM_TMASK_CASE(3, 8) NM_TMASK_CASE(4, 8)
