@@ -358,10 +358,14 @@ __global__ void __launch_bounds__(kThreads) blocked_select_kernel(const uint32_t
 
 // The blocked layout of W's TRANSPOSE (K x R, groups of M along R; R % 64 == 0): block
 // (g, s) holds transposed rows 16g .. 16g+15, i.e. columns 16g .. of W, and step s,
-// i.e. rows 64s .. 64s+63 of W.  The wave stages that 64 x 16 tile of W in LDS with
-// row-contiguous loads (4 waves of a workgroup take neighbouring column groups, so
-// together they read whole 128-byte lines), then each lane gathers its 16 elements
-// down one column and proceeds as for W itself.  Columns past K are padding (zeros).
+// i.e. rows 64s .. 64s+63 of W.  A wave takes column group g and kStepsPerWave
+// consecutive steps: it stages those 64 x 16 tiles of W in LDS with row-contiguous
+// loads, all issued before any is used (the 4 waves of a workgroup take neighbouring
+// column groups, so together they read whole 128-byte lines), then for each tile every
+// lane gathers its 16 elements down one column and proceeds as for W itself.  Columns
+// past K are padding (zeros).
+constexpr int kStepsPerWave = 1;
+
 template <typename E, int N, int M>
 __global__ void __launch_bounds__(kThreads) blocked_select_t_kernel(
     const E* __restrict__ W, int64_t R, int64_t K, int64_t blocks, uint32_t* __restrict__ values,
@@ -370,28 +374,35 @@ __global__ void __launch_bounds__(kThreads) blocked_select_t_kernel(
   constexpr int kChunkElems = 16 / (int)sizeof(E);      // elements per 16-byte chunk
   constexpr int kChunksPerRow = 16 / kChunkElems;       // 2 (16-bit) or 4 (fp32)
   __shared__ uint32_t lds_bits[kThreads / 64][L::kShuffle ? 1 : L::kBlockMetaWords];
-  __shared__ __align__(16) E tile[kThreads / 64][64][16];
+  __shared__ __align__(16) E tile[kThreads / 64][kStepsPerWave][64][16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // workgroup x covers 4 consecutive column groups of one step: blk = g * S + s
   const int64_t steps = R / 64, groups = (K + 15) / 16;
-  const int64_t s = (int64_t)blockIdx.x % steps;
-  const int64_t g = ((int64_t)blockIdx.x / steps) * (kThreads / 64) + wave;
-  if (g >= groups) return;  // the whole wave
-  const int64_t blk = g * steps + s;
-  const int64_t r0 = 64 * s, c0 = 16 * g;
+  // Consecutive workgroups take consecutive steps of the same four column groups, so
+  // each column group's blocks are written front to back.  (Measured: this beats
+  // orders that read the rows of W front to back, which scatter the block writes.)
+  const int64_t wave_steps = (steps + kStepsPerWave - 1) / kStepsPerWave;
+  const int64_t s0 = ((int64_t)blockIdx.x % wave_steps) * kStepsPerWave;
+  const int64_t g = ((int64_t)blockIdx.x / wave_steps) * (kThreads / 64) + wave;
+  if (g >= groups || s0 >= steps) return;  // the whole wave
+  const int64_t c0 = 16 * g;
   const bool vec_ok = (K * (int64_t)sizeof(E)) % 16 == 0;
 #pragma unroll
-  for (int it = 0; it < kChunksPerRow; ++it) {
-    const int chunk = it * 64 + lane;             // 64 rows x kChunksPerRow chunks
-    const int r = chunk / kChunksPerRow, ch = chunk % kChunksPerRow;
-    const int64_t col = c0 + ch * kChunkElems;
-    const E* src = W + (r0 + r) * K + col;
-    E* dst = &tile[wave][r][ch * kChunkElems];
-    if (vec_ok && col + kChunkElems <= K) {
-      *reinterpret_cast<u32x4_t*>(dst) = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src));
-    } else {
+  for (int t = 0; t < kStepsPerWave; ++t) {
+    if (s0 + t >= steps) break;
 #pragma unroll
-      for (int e = 0; e < kChunkElems; ++e) dst[e] = (col + e < K) ? src[e] : (E)0;
+    for (int it = 0; it < kChunksPerRow; ++it) {
+      const int chunk = it * 64 + lane;             // 64 rows x kChunksPerRow chunks
+      const int r = chunk / kChunksPerRow, ch = chunk % kChunksPerRow;
+      const int64_t col = c0 + ch * kChunkElems;
+      const E* src = W + (64 * (s0 + t) + r) * K + col;
+      E* dst = &tile[wave][t][r][ch * kChunkElems];
+      if (vec_ok && col + kChunkElems <= K) {
+        *reinterpret_cast<u32x4_t*>(dst) =
+            __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src));
+      } else {
+#pragma unroll
+        for (int e = 0; e < kChunkElems; ++e) dst[e] = (col + e < K) ? src[e] : (E)0;
+      }
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -399,18 +410,22 @@ __global__ void __launch_bounds__(kThreads) blocked_select_t_kernel(
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const int col = lane >> 2, q = lane & 3;
   const bool live = c0 + col < K;
-  uint32_t w[L::kWords];
 #pragma unroll
-  for (int i = 0; i < L::kWords; ++i) w[i] = 0;
+  for (int t = 0; t < kStepsPerWave; ++t) {
+    if (s0 + t >= steps) break;
+    uint32_t w[L::kWords];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t v = (uint32_t)tile[wave][16 * q + i][col];
-    if constexpr (sizeof(E) == 2)
-      w[i / 2] |= v << (16 * (i % 2));
-    else
-      w[i] = v;
+    for (int i = 0; i < L::kWords; ++i) w[i] = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t v = (uint32_t)tile[wave][t][16 * q + i][col];
+      if constexpr (sizeof(E) == 2)
+        w[i / 2] |= v << (16 * (i % 2));
+      else
+        w[i] = v;
+    }
+    blocked_emit<E, N, M>(w, live, g * steps + s0 + t, lane, lds_bits[wave], values, meta);
   }
-  blocked_emit<E, N, M>(w, live, blk, lane, lds_bits[wave], values, meta);
 }
 
 // Row layout of W's transpose, slow path: one thread per transposed group (W column k,
@@ -688,7 +703,8 @@ hipError_t run_select_t(const void* W, int64_t R, int64_t K, bool blocked, void*
   const E* w = static_cast<const E*>(W);
   if (blocked) {
     const int64_t steps = R / 64, groups = (K + 15) / 16;
-    const int64_t wg = (groups + kThreads / 64 - 1) / (kThreads / 64) * steps;
+    const int64_t wg = (groups + kThreads / 64 - 1) / (kThreads / 64) *
+                       ((steps + kStepsPerWave - 1) / kStepsPerWave);
     blocked_select_t_kernel<E, N, M><<<(unsigned)wg, kThreads, 0, s>>>(
         w, R, K, groups * steps, static_cast<uint32_t*>(values), meta);
     return hipGetLastError();
