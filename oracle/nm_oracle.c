@@ -66,14 +66,22 @@ static void big_from_shifted(big_t* out, uint64_t value, int shift) {
 
 static uint32_t raw_bits(const void* p, int dt, int64_t i) {
   if (dt == NMO_F32) return ((const uint32_t*)p)[i];
+  if (dt == NMO_I8) return ((const uint8_t*)p)[i];
   return ((const uint16_t*)p)[i];
 }
 
-/* exact |w| of element i, as an integer multiple of the smallest subnormal */
+static int elem_size(int dt) { return dt == NMO_F32 ? 4 : dt == NMO_I8 ? 1 : 2; }
+
+/* exact |w| of element i, as an integer multiple of the smallest subnormal (of 1 for int8) */
 static void exact_magnitude(const void* W, int dt, int64_t i, big_t* out) {
   uint32_t bits = raw_bits(W, dt, i);
   uint32_t e, f;
   int p;
+  if (dt == NMO_I8) { /* two's complement: |-128| = 128 */
+    int v = (int)(int8_t)(uint8_t)bits;
+    big_from_shifted(out, (uint64_t)(v < 0 ? -v : v), 0);
+    return;
+  }
   if (dt == NMO_F32) {
     e = (bits >> 23) & 0xFFu;
     f = bits & 0x7FFFFFu;
@@ -95,6 +103,7 @@ static void exact_magnitude(const void* W, int dt, int64_t i, big_t* out) {
 
 double nmo_to_double(const void* p, int dt, int64_t i) {
   uint32_t bits = raw_bits(p, dt, i);
+  if (dt == NMO_I8) return (double)(int8_t)(uint8_t)bits;
   if (dt == NMO_F32) {
     float v;
     memcpy(&v, &bits, 4);
@@ -142,7 +151,7 @@ int64_t nmo_meta_words_per_row(int64_t K, int n, int m) {
 }
 
 static int check_args(int dt, int64_t R, int64_t K, int n, int m) {
-  if (dt != NMO_F32 && dt != NMO_F16 && dt != NMO_BF16) return -1;
+  if (dt != NMO_F32 && dt != NMO_F16 && dt != NMO_BF16 && dt != NMO_I8) return -1;
   if (R < 0 || K < 0) return -2;
   if (nmo_meta_bits(m) < 0 || n < 1 || n > m) return -3;
   if (K % m != 0) return -4;
@@ -235,6 +244,8 @@ int nmo_compress(const void* W, int dt, int64_t R, int64_t K, int n, int m, void
         int64_t dst = r * kv + g * n + j;
         if (dt == NMO_F32)
           ((uint32_t*)values)[dst] = ((const uint32_t*)W)[base + kept[j]];
+        else if (dt == NMO_I8)
+          ((uint8_t*)values)[dst] = ((const uint8_t*)W)[base + kept[j]];
         else
           ((uint16_t*)values)[dst] = ((const uint16_t*)W)[base + kept[j]];
         put_field(mrow, g * n + j, b, (uint32_t)kept[j]);
@@ -252,7 +263,7 @@ int nmo_decompress(const void* values, const uint32_t* meta, int dt, int64_t R, 
   int b = nmo_meta_bits(m);
   int64_t wpr = nmo_meta_words_per_row(K, n, m);
   int64_t kv = K / m * n;
-  int s = dt == NMO_F32 ? 4 : 2;
+  int s = elem_size(dt);
   memset(W_out, 0, (size_t)(R * K * s));
   for (int64_t r = 0; r < R; r++) {
     const uint32_t* mrow = meta + r * wpr;
@@ -262,6 +273,8 @@ int nmo_decompress(const void* values, const uint32_t* meta, int dt, int64_t R, 
         int64_t src = r * kv + g * n + j;
         if (dt == NMO_F32)
           ((uint32_t*)W_out)[pos] = ((const uint32_t*)values)[src];
+        else if (dt == NMO_I8)
+          ((uint8_t*)W_out)[pos] = ((const uint8_t*)values)[src];
         else
           ((uint16_t*)W_out)[pos] = ((const uint16_t*)values)[src];
       }
@@ -440,6 +453,7 @@ static void zero_elem(void* dst, int dt, int64_t i) {
 int nmo_prune(const void* W, int dt, int64_t R, int64_t K, int n, int m, void* W_out) {
   int rc = check_args(dt, R, K, n, m);
   if (rc) return rc;
+  if (dt == NMO_I8) return -1; /* SR-STE trains floating-point weights */
   int kept[16];
   for (int64_t r = 0; r < R; r++) {
     for (int64_t g = 0; g < K / m; g++) {
@@ -462,6 +476,7 @@ int nmo_srste_grad(const void* W, const void* G, int dt, int64_t R, int64_t K, i
                    float decay, void* G_out) {
   int rc = check_args(dt, R, K, n, m);
   if (rc) return rc;
+  if (dt == NMO_I8) return -1;
   int kept[16];
   for (int64_t r = 0; r < R; r++) {
     for (int64_t g = 0; g < K / m; g++) {
@@ -499,6 +514,7 @@ int nmo_srste_grad(const void* W, const void* G, int dt, int64_t R, int64_t K, i
 static int check_tshape(int dt, int64_t R, int64_t K, int n, int m) {
   int rc = check_args(dt, R, K, n, m);
   if (rc) return rc;
+  if (dt == NMO_I8) return -1; /* transposable masks are built for trained float weights */
   if (R % m != 0) return -4;
   return 0;
 }

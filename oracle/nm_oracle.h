@@ -59,8 +59,11 @@
  *
  * Conventions: every matrix is dense row-major; W is R x K with groups along
  * K; values R x (K*N/M); meta R x words_per_row uint32; X K x T; Y R x T.
- * Element types: dt = 0 (fp32), 1 (fp16), 2 (bf16); 16-bit types are passed
- * as raw uint16 bit patterns.  Return value 0 = success, negative = bad args.
+ * Element types: dt = 0 (fp32), 1 (fp16), 2 (bf16), 3 (int8); 16-bit types are
+ * passed as raw uint16 bit patterns, int8 as raw bytes.  int8 (the ASDNN review's
+ * INT8 sparse Tensor Core type, "Tensor Scores 상에서 구조적인 sparse GEMM") takes |w|
+ * as the integer magnitude (|-128| = 128) and is accepted by mask, compress,
+ * decompress and the products, whose double sums are then exact integers.  Return value 0 = success, negative = bad args.
  */
 #ifndef NM_ORACLE_H
 #define NM_ORACLE_H
@@ -73,6 +76,7 @@ extern "C" {
 #define NMO_F32 0
 #define NMO_F16 1
 #define NMO_BF16 2
+#define NMO_I8 3 /* int8 two's complement; products are exact integers */
 
 /* metadata bits per kept value, log2(m); -1 if m is not a power of two in [2,16] */
 int nmo_meta_bits(int m);

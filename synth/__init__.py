@@ -18,7 +18,10 @@ Recipe (published methods, written from their definitions):
 * Outliers: element ``i`` is scaled by a factor when draw ``i`` of a separate
   stream, as a uniform in [0, 1), falls below the outlier probability.
 * Values are produced in float64, rounded to fp32 (round-to-nearest-even),
-  then to bf16 or fp16 (round-to-nearest-even on the fp32 bits).
+  then to bf16 or fp16 (round-to-nearest-even on the fp32 bits).  int8 values
+  are the float64 draws rounded to the nearest integer (ties to even) and
+  clipped to [-128, 127], i.e. a symmetric quantiser with step 1 (the scale is
+  part of the distribution).
 """
 from __future__ import annotations
 
@@ -76,7 +79,10 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
 
 
 def round_to(x64: np.ndarray, dtype: str) -> np.ndarray:
-    """float64 -> fp32 (RNE) -> dtype.  Returns float32 for f32, raw uint16 bits otherwise."""
+    """float64 -> fp32 (RNE) -> dtype.  Returns float32 for f32, raw uint16 bits for the
+    16-bit types, int8 for i8 (nearest integer, clipped)."""
+    if dtype == "i8":
+        return np.clip(np.rint(x64), -128, 127).astype(np.int8)
     x32 = x64.astype(np.float32)
     if dtype == "f32":
         return x32
@@ -96,6 +102,8 @@ def bits_to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
         return a.astype(np.float32).astype(np.float64)
     if dtype == "f16":
         return np.asarray(a, dtype=np.uint16).view(np.float16).astype(np.float64)
+    if dtype == "i8":
+        return np.asarray(a).view(np.int8).astype(np.float64)
     if dtype == "bf16":
         u = np.asarray(a, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
         return u.view(np.float32).astype(np.float64)
@@ -132,7 +140,7 @@ class Dist:
 def generate(dist: Dist, shape: tuple[int, int], dtype: str) -> np.ndarray:
     """Row-major matrix of ``shape``; element (r, c) is draw r*cols + c of ``dist``."""
     n = int(shape[0]) * int(shape[1])
-    out = np.empty(n, dtype=np.float32 if dtype == "f32" else np.uint16)
+    out = np.empty(n, dtype={"f32": np.float32, "i8": np.int8}.get(dtype, np.uint16))
 
     def fill(s: int) -> None:
         c = min(_CHUNK, n - s)
