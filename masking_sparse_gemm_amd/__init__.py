@@ -30,13 +30,15 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libnm.so")
 
-NM_F32, NM_F16, NM_BF16 = 0, 1, 2
-_DT = {torch.float32: NM_F32, torch.float16: NM_F16, torch.bfloat16: NM_BF16}
+NM_F32, NM_F16, NM_BF16, NM_I8, NM_I32 = 0, 1, 2, 3, 4
+_DT = {torch.float32: NM_F32, torch.float16: NM_F16, torch.bfloat16: NM_BF16, torch.int8: NM_I8,
+       torch.int32: NM_I32}
+_FLOAT = (torch.float32, torch.float16, torch.bfloat16)
 _TORCH_DT = {v: k for k, v in _DT.items()}
 STATUS = ["ok", "null", "shape", "pattern", "dtype", "align", "unsupported", "device", "layout",
           "alias"]
 LAYOUTS = {"rows": 0, "blocked": 1}
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 # every function the C header declares
 EXPORTS = ("nm_abi_version", "nm_status_str", "nm_values_bytes", "nm_meta_bytes",
@@ -108,15 +110,15 @@ def _ptr(t: torch.Tensor):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _dense_input(t: torch.Tensor, name: str) -> int:
+def _dense_input(t: torch.Tensor, name: str, int8: bool = True) -> int:
     if t.dim() != 2:
         raise ValueError(f"{name} must be 2-D")
     if not t.is_cuda:
         raise ValueError(f"{name} must be on a GPU")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous (row-major)")
-    if t.dtype not in _DT:
-        raise ValueError(f"{name} must be float32, float16 or bfloat16")
+    if t.dtype not in _FLOAT and not (int8 and t.dtype == torch.int8):
+        raise ValueError(f"{name} must be float32, float16 or bfloat16" + (" or int8" if int8 else ""))
     return _DT[t.dtype]
 
 
@@ -170,8 +172,9 @@ def compress(W: torch.Tensor, n: int = 2, m: int = 4, layout: str = "rows"):
 def _check_compressed(values: torch.Tensor, meta: torch.Tensor, n: int, m: int, K: int,
                       layout: str, rows: int | None) -> tuple[int, int]:
     """(dtype code, R) of a compressed pair, after checking its shapes against K and n:m."""
-    if values.dtype not in _DT or not values.is_cuda or not values.is_contiguous():
-        raise ValueError("values must be a contiguous float32/float16/bfloat16 GPU tensor")
+    ok = values.dtype in _FLOAT or values.dtype == torch.int8
+    if not ok or not values.is_cuda or not values.is_contiguous():
+        raise ValueError("values must be a contiguous float32/float16/bfloat16/int8 GPU tensor")
     if _layout(layout) == 0:
         R = values.shape[0] if values.dim() == 2 else -1
         if rows is not None and rows != R:
@@ -205,13 +208,14 @@ def decompress(values: torch.Tensor, meta: torch.Tensor, n: int, m: int, K: int,
 def spmm(values: torch.Tensor, meta: torch.Tensor, X: torch.Tensor, n: int = 2, m: int = 4,
          out_dtype: torch.dtype | None = None, out: torch.Tensor | None = None,
          layout: str = "rows", rows: int | None = None) -> torch.Tensor:
-    """Y (R, T) = W_sparse @ X with fp32 accumulation; out_dtype is X's dtype or float32."""
+    """Y (R, T) = W_sparse @ X with fp32 accumulation; out_dtype is X's dtype or float32.
+    int8 values and X give the exact int32 product (out_dtype torch.int32)."""
     xdt = _dense_input(X, "X")
     K, T = X.shape
     dt, R = _check_compressed(values, meta, n, m, K, layout, rows)
     if dt != xdt:
         raise ValueError("values and X must have the same dtype")
-    y_dtype = out_dtype or X.dtype
+    y_dtype = out_dtype or (torch.int32 if X.dtype == torch.int8 else X.dtype)
     if out is None:
         out = torch.empty((R, T), dtype=y_dtype, device=X.device)
     elif out.shape != (R, T) or out.dtype != y_dtype or not out.is_contiguous():
@@ -232,7 +236,7 @@ def _same_dense(t: torch.Tensor, like: torch.Tensor, name: str) -> None:
 
 def prune(W: torch.Tensor, n: int = 2, m: int = 4, out: torch.Tensor | None = None) -> torch.Tensor:
     """SR-STE forward weight: W where the N:M mask keeps it, +0 elsewhere (out may be W)."""
-    dt = _dense_input(W, "W")
+    dt = _dense_input(W, "W", int8=False)
     R, K = W.shape
     if out is None:
         out = torch.empty_like(W)
@@ -245,7 +249,7 @@ def prune(W: torch.Tensor, n: int = 2, m: int = 4, out: torch.Tensor | None = No
 def srste_grad(W: torch.Tensor, G: torch.Tensor, n: int = 2, m: int = 4,
                decay: float = SRSTE_DECAY, out: torch.Tensor | None = None) -> torch.Tensor:
     """SR-STE backward: G where W is kept, G + decay*W where pruned (out may be G)."""
-    dt = _dense_input(W, "W")
+    dt = _dense_input(W, "W", int8=False)
     _same_dense(G, W, "G")
     R, K = W.shape
     if out is None:
@@ -259,7 +263,7 @@ def srste_grad(W: torch.Tensor, G: torch.Tensor, n: int = 2, m: int = 4,
 
 def tmask(W: torch.Tensor, n: int = 2, m: int = 4) -> torch.Tensor:
     """Bool (R, K): the transposable N:M mask (greedy, per m x m block)."""
-    dt = _dense_input(W, "W")
+    dt = _dense_input(W, "W", int8=False)
     R, K = W.shape
     out = torch.empty((R, K), dtype=torch.bool, device=W.device)
     _check("nm_tmask", lib().nm_tmask(_ptr(W), dt, R, K, n, m, _ptr(out), _stream(W)))
@@ -268,7 +272,7 @@ def tmask(W: torch.Tensor, n: int = 2, m: int = 4) -> torch.Tensor:
 
 def tprune(W: torch.Tensor, n: int = 2, m: int = 4, out: torch.Tensor | None = None) -> torch.Tensor:
     """W where the transposable mask keeps it, +0 elsewhere (out may be W)."""
-    dt = _dense_input(W, "W")
+    dt = _dense_input(W, "W", int8=False)
     R, K = W.shape
     if out is None:
         out = torch.empty_like(W)
@@ -280,7 +284,7 @@ def tprune(W: torch.Tensor, n: int = 2, m: int = 4, out: torch.Tensor | None = N
 
 def compress_t(W: torch.Tensor, n: int = 2, m: int = 4, layout: str = "rows"):
     """compress() of W's transpose (a K x R matrix, groups along R) without forming it."""
-    dt = _dense_input(W, "W")
+    dt = _dense_input(W, "W", int8=False)
     R, K = W.shape
     lay = _layout(layout)
     if R % m:

@@ -22,9 +22,17 @@ bool missing(const void* p, int64_t count) { return p == nullptr && count > 0; }
 
 int meta_bits_of(int m) { return m == 2 ? 1 : m == 4 ? 2 : m == 8 ? 3 : -1; }
 
-int elem_bytes(nm_dtype dt) { return dt == NM_F32 ? 4 : 2; }
+int elem_bytes(nm_dtype dt) { return dt == NM_F32 ? 4 : dt == NM_I8 ? 1 : 2; }
 
-bool valid_dtype(int dt) { return dt == NM_F32 || dt == NM_F16 || dt == NM_BF16; }
+// Element types of W for the selection and the products; NM_I32 is an output type only.
+bool valid_dtype(int dt) { return dt == NM_F32 || dt == NM_F16 || dt == NM_BF16 || dt == NM_I8; }
+bool float_dtype(int dt) { return dt == NM_F32 || dt == NM_F16 || dt == NM_BF16; }
+
+// The blocked layout stores a lane's 16 elements of a block as whole 32-bit words of values:
+// for int8, 16 N / M bytes must divide by 4.
+bool blocked_pattern_ok(nm_dtype dt, int n, int m) {
+  return dt != NM_I8 || (16 * n / m) % 4 == 0;
+}
 
 nm_status check_pattern(int n, int m) {
   if (meta_bits_of(m) < 0 || n < 1 || n > m) return NM_ERR_PATTERN;
@@ -102,6 +110,7 @@ size_t nm_values_bytes(int64_t R, int64_t K, int n, int m, nm_dtype dt, nm_layou
   if (!valid_dtype(dt) || check_pattern(n, m) != NM_OK || check_shape(R, K, m) != NM_OK ||
       check_layout(layout, K) != NM_OK)
     return 0;
+  if (layout == NM_LAYOUT_BLOCKED && !blocked_pattern_ok(dt, n, m)) return 0;
   return (size_t)(padded_rows(R, layout) * (K / m * n) * elem_bytes(dt));
 }
 
@@ -138,6 +147,7 @@ nm_status nm_compress(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, i
   if (st != NM_OK) return st;
   if ((st = check_shape(R, K, m)) != NM_OK) return st;
   if ((st = check_layout(layout, K)) != NM_OK) return st;
+  if (layout == NM_LAYOUT_BLOCKED && !blocked_pattern_ok(dt, n, m)) return NM_ERR_UNSUPPORTED;
   if (missing(W, R * K) || missing(values, R * K) || missing(meta, R * K)) return NM_ERR_NULL;
   if (R * K == 0) return NM_OK;
   if (!aligned16(W) || !aligned16(values) || !aligned16(meta)) return NM_ERR_ALIGN;
@@ -154,6 +164,7 @@ nm_status nm_decompress(const void* values, const uint32_t* meta, nm_dtype dt, i
   if (st != NM_OK) return st;
   if ((st = check_shape(R, K, m)) != NM_OK) return st;
   if ((st = check_layout(layout, K)) != NM_OK) return st;
+  if (layout == NM_LAYOUT_BLOCKED && !blocked_pattern_ok(dt, n, m)) return NM_ERR_UNSUPPORTED;
   if (missing(values, R * K) || missing(meta, R * K) || missing(W_out, R * K)) return NM_ERR_NULL;
   if (R * K == 0) return NM_OK;
   if (!aligned16(values) || !aligned16(meta) || !aligned16(W_out)) return NM_ERR_ALIGN;
@@ -166,12 +177,17 @@ nm_status nm_decompress(const void* values, const uint32_t* meta, nm_dtype dt, i
 nm_status nm_spmm(const void* values, const uint32_t* meta, int64_t R, int64_t K, int n, int m,
                   nm_layout layout, const void* X, int64_t T, nm_dtype dt, void* Y,
                   nm_dtype y_dt, nm_stream_t stream) {
-  if (!valid_dtype(dt) || !valid_dtype(y_dt) || (y_dt != dt && y_dt != NM_F32))
+  if (dt == NM_I8) {
+    if (y_dt != NM_I32) return NM_ERR_DTYPE;
+  } else if (!float_dtype(dt) || !float_dtype(y_dt) || (y_dt != dt && y_dt != NM_F32)) {
     return NM_ERR_DTYPE;
+  }
   nm_status st = check_pattern(n, m);
   if (st != NM_OK) return st;
   if ((st = check_shape(R, K, m)) != NM_OK) return st;
+  if (dt == NM_I8 && K >= (int64_t)1 << 17) return NM_ERR_SHAPE;  // int32 sums stay exact
   if ((st = check_layout(layout, K)) != NM_OK) return st;
+  if (layout == NM_LAYOUT_BLOCKED && !blocked_pattern_ok(dt, n, m)) return NM_ERR_UNSUPPORTED;
   if (T < 0 || (K > 0 && T > ((int64_t)1 << 40) / K) || (R > 0 && T > ((int64_t)1 << 40) / R))
     return NM_ERR_SHAPE;
   if (missing(values, R * K) || missing(meta, R * K) || missing(X, K * T) || missing(Y, R * T))
@@ -185,7 +201,7 @@ nm_status nm_spmm(const void* values, const uint32_t* meta, int64_t R, int64_t K
 
 nm_status nm_tmask(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m, uint8_t* mask,
                    nm_stream_t stream) {
-  if (!valid_dtype(dt)) return NM_ERR_DTYPE;
+  if (!float_dtype(dt)) return NM_ERR_DTYPE;
   nm_status st = check_pattern(n, m);
   if (st != NM_OK) return st;
   if ((st = check_shape(R, K, m)) != NM_OK) return st;
@@ -201,7 +217,7 @@ nm_status nm_tmask(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int 
 
 nm_status nm_tprune(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m, void* W_out,
                     nm_stream_t stream) {
-  if (!valid_dtype(dt)) return NM_ERR_DTYPE;
+  if (!float_dtype(dt)) return NM_ERR_DTYPE;
   nm_status st = check_pattern(n, m);
   if (st != NM_OK) return st;
   if ((st = check_shape(R, K, m)) != NM_OK) return st;
@@ -217,7 +233,7 @@ nm_status nm_tprune(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int
 
 nm_status nm_compress_t(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m,
                         nm_layout layout, void* values, uint32_t* meta, nm_stream_t stream) {
-  if (!valid_dtype(dt)) return NM_ERR_DTYPE;
+  if (!float_dtype(dt)) return NM_ERR_DTYPE;
   nm_status st = check_pattern(n, m);
   if (st != NM_OK) return st;
   if ((st = check_shape(K, R, m)) != NM_OK) return st;  // the transpose is K x R
@@ -236,7 +252,7 @@ nm_status nm_compress_t(const void* W, nm_dtype dt, int64_t R, int64_t K, int n,
 
 nm_status nm_prune(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m, void* W_out,
                    nm_stream_t stream) {
-  if (!valid_dtype(dt)) return NM_ERR_DTYPE;
+  if (!float_dtype(dt)) return NM_ERR_DTYPE;
   nm_status st = check_pattern(n, m);
   if (st != NM_OK) return st;
   if ((st = check_shape(R, K, m)) != NM_OK) return st;
@@ -251,7 +267,7 @@ nm_status nm_prune(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int 
 
 nm_status nm_srste_grad(const void* W, const void* G, nm_dtype dt, int64_t R, int64_t K, int n,
                         int m, float decay, void* G_out, nm_stream_t stream) {
-  if (!valid_dtype(dt)) return NM_ERR_DTYPE;
+  if (!float_dtype(dt)) return NM_ERR_DTYPE;
   nm_status st = check_pattern(n, m);
   if (st != NM_OK) return st;
   if ((st = check_shape(R, K, m)) != NM_OK) return st;

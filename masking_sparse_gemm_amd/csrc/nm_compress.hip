@@ -73,19 +73,20 @@ struct UnitSelection {
     for (int g = 0; g < S::kGroups; ++g) {
       uint32_t key[M];
 #pragma unroll
-      for (int i = 0; i < M; ++i) key[i] = word_elem<E>(w, g * M + i) & Elem<E>::kKeyMask;
+      for (int i = 0; i < M; ++i) key[i] = Elem<E>::key(word_elem<E>(w, g * M + i));
       keep[g] = keep_bits<N, M>(key);
       kept_positions<N>(keep[g], pos[g]);
     }
   }
   // this unit's metadata: S::kGroups * N fields of b bits, first field in the low bits
-  __device__ __forceinline__ uint32_t meta_bits_of_unit() const {
+  // (up to 48 bits: sixteen int8 elements at 8:8)
+  __device__ __forceinline__ uint64_t meta_bits_of_unit() const {
     constexpr int b = meta_bits(M);
-    uint32_t bits = 0;
+    uint64_t bits = 0;
 #pragma unroll
     for (int g = 0; g < S::kGroups; ++g)
 #pragma unroll
-      for (int j = 0; j < N; ++j) bits |= (uint32_t)pos[g][j] << ((g * N + j) * b);
+      for (int j = 0; j < N; ++j) bits |= (uint64_t)pos[g][j] << ((g * N + j) * b);
     return bits;
   }
 };
@@ -159,19 +160,15 @@ __global__ void __launch_bounds__(kThreads) flat_select_kernel(const uint32_t* _
         for (int g = 0; g < S::kGroups; ++g)
 #pragma unroll
           for (int j = 0; j < N; ++j) {
-            const uint32_t v = group_elem<E, M>(w + g * M * (int)sizeof(E) / 4, sel.pos[g][j]);
-            const int k = g * N + j;  // value index inside the unit
-            if constexpr (sizeof(E) == 2)
-              vw[k / 2] |= v << (16 * (k % 2));
-            else
-              vw[k] = v;
+            const uint32_t v = group_elem_at<E, M>(w, g, sel.pos[g][j]);
+            put_elem<E>(vw, g * N + j, v);  // value index inside the unit
           }
         store_words<kValWords>(values + u * kValWords, vw);
       }
-      const uint32_t bits = live ? sel.meta_bits_of_unit() : 0u;
+      const uint64_t bits = live ? sel.meta_bits_of_unit() : 0u;
       if constexpr (kShuffle) {
         constexpr int L = 32 / kUnitBits;  // lanes per metadata word
-        const uint32_t word = or_reduce_lanes<L>(bits << ((lane % L) * kUnitBits));
+        const uint32_t word = or_reduce_lanes<L>((uint32_t)bits << ((lane % L) * kUnitBits));
         const int64_t widx = u / L;
         if ((lane % L) == 0 && live) meta[widx] = word;
       } else {
@@ -181,8 +178,10 @@ __global__ void __launch_bounds__(kThreads) flat_select_kernel(const uint32_t* _
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         const int bit = lane * kUnitBits;
-        atomicOr(&buf[bit / 32], bits << (bit % 32));
-        if ((bit % 32) + kUnitBits > 32) atomicOr(&buf[bit / 32 + 1], bits >> (32 - bit % 32));
+        const int sh = bit % 32;
+        atomicOr(&buf[bit / 32], (uint32_t)(bits << sh));
+        if (sh + kUnitBits > 32) atomicOr(&buf[bit / 32 + 1], (uint32_t)(bits >> (32 - sh)));
+        if (sh + kUnitBits > 64) atomicOr(&buf[bit / 32 + 2], (uint32_t)(bits >> (64 - sh)));
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         __builtin_amdgcn_wave_barrier();
         const int64_t total_words = units * kUnitBits / 32;
@@ -224,9 +223,10 @@ __global__ void __launch_bounds__(kThreads) flat_decompress_kernel(
       for (int i = 0; i < kValWords; ++i) vw[i] = values[u * kValWords + i];
     }
     const int64_t bit = u * kUnitBits;
-    uint64_t window = meta[bit / 32];
-    if ((bit % 32) + kUnitBits > 32) window |= (uint64_t)meta[bit / 32 + 1] << 32;
-    const uint32_t bits = (uint32_t)(window >> (bit % 32));
+    const int sh = (int)(bit % 32);
+    uint64_t bits = (uint64_t)meta[bit / 32] >> sh;
+    if (sh + kUnitBits > 32) bits |= (uint64_t)meta[bit / 32 + 1] << (32 - sh);
+    if (sh + kUnitBits > 64) bits |= (uint64_t)meta[bit / 32 + 2] << (64 - sh);
     uint32_t ow[S::kWords];
 #pragma unroll
     for (int i = 0; i < S::kWords; ++i) ow[i] = 0;
@@ -241,10 +241,12 @@ __global__ void __launch_bounds__(kThreads) flat_decompress_kernel(
 #pragma unroll
         for (int i = 0; i < M; ++i) {
           const int e = g * M + i;
-          if constexpr (sizeof(E) == 2) {
-            const uint32_t sh = 16 * (e % 2);
-            const uint32_t cur = ow[e / 2];
-            ow[e / 2] = (p == i) ? ((cur & ~(0xFFFFu << sh)) | (v << sh)) : cur;
+          if constexpr (sizeof(E) < 4) {
+            constexpr int kPer = 4 / (int)sizeof(E);
+            constexpr uint32_t kMask = sizeof(E) == 1 ? 0xFFu : 0xFFFFu;
+            const uint32_t sh = 8 * (int)sizeof(E) * (e % kPer);
+            const uint32_t cur = ow[e / kPer];
+            ow[e / kPer] = (p == i) ? ((cur & ~(kMask << sh)) | (v << sh)) : cur;
           } else {
             ow[e] = (p == i) ? v : ow[e];
           }
@@ -295,17 +297,13 @@ __device__ __forceinline__ void blocked_emit(const uint32_t (&w)[LaneShape<E, N,
   for (int gi = 0; gi < L::kGroups; ++gi) {
     uint32_t key[M];
 #pragma unroll
-    for (int i = 0; i < M; ++i) key[i] = word_elem<E>(w, gi * M + i) & Elem<E>::kKeyMask;
+    for (int i = 0; i < M; ++i) key[i] = Elem<E>::key(word_elem<E>(w, gi * M + i));
     int pos[N];
     kept_positions<N>(keep_bits<N, M>(key), pos);
 #pragma unroll
     for (int j = 0; j < N; ++j) {
       const int k = gi * N + j;
-      const uint32_t v = group_elem<E, M>(w + gi * M * (int)sizeof(E) / 4, pos[j]);
-      if constexpr (sizeof(E) == 2)
-        vw[k / 2] |= v << (16 * (k % 2));
-      else
-        vw[k] = v;
+      put_elem<E>(vw, k, group_elem_at<E, M>(w, gi, pos[j]));
       bits |= (uint64_t)pos[j] << (k * b);
     }
   }
@@ -418,11 +416,7 @@ __global__ void __launch_bounds__(kThreads) blocked_select_t_kernel(
     for (int i = 0; i < L::kWords; ++i) w[i] = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const uint32_t v = (uint32_t)tile[wave][t][16 * q + i][col];
-      if constexpr (sizeof(E) == 2)
-        w[i / 2] |= v << (16 * (i % 2));
-      else
-        w[i] = v;
+      put_elem<E>(w, i, (uint32_t)tile[wave][t][16 * q + i][col]);
     }
     blocked_emit<E, N, M>(w, live, g * steps + s0 + t, lane, lds_bits[wave], values, meta);
   }
@@ -441,7 +435,7 @@ __global__ void __launch_bounds__(kThreads) group_t_kernel(const E* __restrict__
 #pragma unroll
   for (int i = 0; i < M; ++i) {
     v[i] = W[(g * M + i) * K + k];
-    key[i] = v[i] & Elem<E>::kKeyMask;
+    key[i] = Elem<E>::key(v[i]);
   }
   int pos[N];
   kept_positions<N>(keep_bits<N, M>(key), pos);
@@ -472,7 +466,7 @@ __global__ void __launch_bounds__(kThreads) meta_word_t_kernel(const E* __restri
   for (int64_t g = f0 / N; g <= f1 / N; ++g) {
     uint32_t key[M];
 #pragma unroll
-    for (int i = 0; i < M; ++i) key[i] = (uint32_t)W[(g * M + i) * K + k] & Elem<E>::kKeyMask;
+    for (int i = 0; i < M; ++i) key[i] = Elem<E>::key((uint32_t)W[(g * M + i) * K + k]);
     int pos[N];
     kept_positions<N>(keep_bits<N, M>(key), pos);
 #pragma unroll
@@ -521,10 +515,12 @@ __global__ void __launch_bounds__(kThreads) blocked_decompress_kernel(
 #pragma unroll
       for (int i = 0; i < M; ++i) {
         const int e = gi * M + i;
-        if constexpr (sizeof(E) == 2) {
-          const uint32_t sh16 = 16 * (e % 2);
-          const uint32_t cur = ow[e / 2];
-          ow[e / 2] = (p == i) ? ((cur & ~(0xFFFFu << sh16)) | (v << sh16)) : cur;
+        if constexpr (sizeof(E) < 4) {
+          constexpr int kPer = 4 / (int)sizeof(E);
+          constexpr uint32_t kMask = sizeof(E) == 1 ? 0xFFu : 0xFFFFu;
+          const uint32_t sh = 8 * (int)sizeof(E) * (e % kPer);
+          const uint32_t cur = ow[e / kPer];
+          ow[e / kPer] = (p == i) ? ((cur & ~(kMask << sh)) | (v << sh)) : cur;
         } else {
           ow[e] = (p == i) ? v : ow[e];
         }
@@ -546,7 +542,7 @@ __device__ __forceinline__ void select_group(const E* W, int64_t base, int (&pos
                                              uint32_t& keep) {
   uint32_t key[M];
 #pragma unroll
-  for (int i = 0; i < M; ++i) key[i] = (uint32_t)W[base + i] & Elem<E>::kKeyMask;
+  for (int i = 0; i < M; ++i) key[i] = Elem<E>::key((uint32_t)W[base + i]);
   keep = keep_bits<N, M>(key);
   kept_positions<N>(keep, pos);
 }
@@ -650,6 +646,13 @@ bool flat_ok(int64_t K) {
   return true;
 }
 
+// Does a lane's share of a block (16 elements) keep a whole number of 32-bit words of
+// values?  Always for 16- and 32-bit elements; for bytes, 16 N / M must divide by 4.
+template <typename E, int N, int M>
+constexpr bool blocked_kernel_exists() {
+  return (16 * N / M * (int)sizeof(E)) % 4 == 0;
+}
+
 template <typename E, int N, int M>
 hipError_t run_select(const void* W, int64_t R, int64_t K, bool blocked, void* values,
                       uint32_t* meta, uint8_t* mask, hipStream_t s) {
@@ -658,10 +661,13 @@ hipError_t run_select(const void* W, int64_t R, int64_t K, bool blocked, void* v
   if (elems == 0) return hipSuccess;
   const bool want_mask = mask != nullptr, want_compress = values != nullptr;
   if (blocked) {  // compress only (the mask is a dense array in either layout)
-    const int64_t blocks = (R + 15) / 16 * (K / 64);
-    blocked_select_kernel<E, N, M><<<blocks_for(blocks, kThreads / 64), kThreads, 0, s>>>(
-        static_cast<const uint32_t*>(W), R, K, blocks, static_cast<uint32_t*>(values), meta);
-    return hipGetLastError();
+    if constexpr (blocked_kernel_exists<E, N, M>()) {
+      const int64_t blocks = (R + 15) / 16 * (K / 64);
+      blocked_select_kernel<E, N, M><<<blocks_for(blocks, kThreads / 64), kThreads, 0, s>>>(
+          static_cast<const uint32_t*>(W), R, K, blocks, static_cast<uint32_t*>(values), meta);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
   }
   if constexpr (flat_kernel_exists<E, N, M>()) {
    if (flat_ok<E, N, M>(K)) {
@@ -726,10 +732,13 @@ hipError_t run_decompress(const void* values, const uint32_t* meta, int64_t R, i
   const int64_t elems = R * K;
   if (elems == 0) return hipSuccess;
   if (blocked) {
-    const int64_t blocks = (R + 15) / 16 * (K / 64);
-    blocked_decompress_kernel<E, N, M><<<blocks_for(blocks, kThreads / 64), kThreads, 0, s>>>(
-        static_cast<const uint32_t*>(values), meta, R, K, blocks, static_cast<uint32_t*>(out));
-    return hipGetLastError();
+    if constexpr (blocked_kernel_exists<E, N, M>()) {
+      const int64_t blocks = (R + 15) / 16 * (K / 64);
+      blocked_decompress_kernel<E, N, M><<<blocks_for(blocks, kThreads / 64), kThreads, 0, s>>>(
+          static_cast<const uint32_t*>(values), meta, R, K, blocks, static_cast<uint32_t*>(out));
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
   }
   if constexpr (flat_kernel_exists<E, N, M>()) {
     if (flat_ok<E, N, M>(K)) {
@@ -786,6 +795,8 @@ struct DecompressOp {
 hipError_t launch_select(const void* W, int elem_bytes, int64_t R, int64_t K, int n, int m,
                          bool blocked, void* values, uint32_t* meta, uint8_t* mask,
                          hipStream_t s) {
+  if (elem_bytes == 1)
+    return dispatch_nm<uint8_t, SelectOp>(n, m, W, R, K, blocked, values, meta, mask, s);
   if (elem_bytes == 2)
     return dispatch_nm<uint16_t, SelectOp>(n, m, W, R, K, blocked, values, meta, mask, s);
   return dispatch_nm<uint32_t, SelectOp>(n, m, W, R, K, blocked, values, meta, mask, s);
@@ -800,6 +811,8 @@ hipError_t launch_select_t(const void* W, int elem_bytes, int64_t R, int64_t K, 
 
 hipError_t launch_decompress(const void* values, const uint32_t* meta, int elem_bytes, int64_t R,
                              int64_t K, int n, int m, bool blocked, void* out, hipStream_t s) {
+  if (elem_bytes == 1)
+    return dispatch_nm<uint8_t, DecompressOp>(n, m, values, meta, R, K, blocked, out, s);
   if (elem_bytes == 2)
     return dispatch_nm<uint16_t, DecompressOp>(n, m, values, meta, R, K, blocked, out, s);
   return dispatch_nm<uint32_t, DecompressOp>(n, m, values, meta, R, K, blocked, out, s);

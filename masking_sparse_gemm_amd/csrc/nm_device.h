@@ -12,7 +12,9 @@
 // Sparse Deep Neural Networks", section "Step-2: Weight Pruning").
 //
 // Magnitudes are compared as integers: the bit pattern with the sign cleared orders
-// exactly as |w| for every finite value and infinity (and puts NaN above Inf).
+// exactly as |w| for every finite value and infinity (and puts NaN above Inf).  int8
+// weights (stored as raw bytes) use the integer magnitude of the two's-complement value,
+// |-128| = 128.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -23,18 +25,28 @@ namespace nm {
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-// Raw storage of one element: uint16_t for bf16 / fp16, uint32_t for fp32.
+// Raw storage of one element: uint8_t for int8, uint16_t for bf16 / fp16, uint32_t for
+// fp32.  key(raw) is the element's magnitude as an unsigned integer.
 template <typename E>
 struct Elem;
+template <>
+struct Elem<uint8_t> {
+  static constexpr int kBytes = 1;
+  __host__ __device__ static constexpr uint32_t key(uint32_t raw) {
+    return (raw & 0x80u) ? 256u - (raw & 0xFFu) : (raw & 0xFFu);
+  }
+};
 template <>
 struct Elem<uint16_t> {
   static constexpr uint32_t kKeyMask = 0x7FFFu;
   static constexpr int kBytes = 2;
+  __host__ __device__ static constexpr uint32_t key(uint32_t raw) { return raw & kKeyMask; }
 };
 template <>
 struct Elem<uint32_t> {
   static constexpr uint32_t kKeyMask = 0x7FFFFFFFu;
   static constexpr int kBytes = 4;
+  __host__ __device__ static constexpr uint32_t key(uint32_t raw) { return raw & kKeyMask; }
 };
 
 constexpr int meta_bits(int m) { return m == 2 ? 1 : m == 4 ? 2 : m == 8 ? 3 : m == 16 ? 4 : 0; }
@@ -97,10 +109,39 @@ __device__ __forceinline__ uint32_t group_elem(const uint32_t* gw, int pos) {
 // Element e of a register array of words.
 template <typename E>
 __device__ __forceinline__ uint32_t word_elem(const uint32_t* w, int e) {
-  if constexpr (sizeof(E) == 2)
+  if constexpr (sizeof(E) == 1)
+    return (w[e >> 2] >> ((e & 3) * 8)) & 0xFFu;
+  else if constexpr (sizeof(E) == 2)
     return (w[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
   else
     return w[e];
+}
+
+// Element `pos` (run-time) of group g (compile-time) of M elements in a register array
+// of words that starts at group 0.
+template <typename E, int M>
+__device__ __forceinline__ uint32_t group_elem_at(const uint32_t* w, int g, int pos) {
+  if constexpr (sizeof(E) == 1) {
+    if constexpr (M >= 4) {
+      const uint32_t word = pick_word<M / 4>(w + g * M / 4, pos >> 2);
+      return (word >> (8 * (pos & 3))) & 0xFFu;
+    } else {  // two groups of two bytes per word
+      return (w[(g * M) / 4] >> (8 * ((g * M) % 4 + pos))) & 0xFFu;
+    }
+  } else {
+    return group_elem<E, M>(w + g * M * (int)sizeof(E) / 4, pos);
+  }
+}
+
+// Set element e of a register array of words to v (v holds only the element's bits).
+template <typename E>
+__device__ __forceinline__ void put_elem(uint32_t* w, int e, uint32_t v) {
+  if constexpr (sizeof(E) == 1)
+    w[e >> 2] |= v << (8 * (e & 3));
+  else if constexpr (sizeof(E) == 2)
+    w[e >> 1] |= v << (16 * (e & 1));
+  else
+    w[e] = v;
 }
 
 }  // namespace nm

@@ -50,7 +50,7 @@ typedef _Float16 f16x16_t __attribute__((ext_vector_type(16)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 
-enum { kF32 = 0, kF16 = 1, kBF16 = 2 };
+enum { kF32 = 0, kF16 = 1, kBF16 = 2, kI8 = 3, kI32 = 4 };
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 __device__ __forceinline__ float f16_to_f32(uint32_t h) {
@@ -1381,20 +1381,39 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
 constexpr int kGT = 64;   // tile rows and columns
 constexpr int kGK = 32;   // K per step (a multiple of every supported M)
 
+// The generic kernel accumulates 16-bit and fp32 inputs in fp32 and int8 inputs in int32
+// (exact for the int8 products: |sum| <= K * 2^14, and the library takes K < 2^17).
+template <int DT>
+struct GenAcc {
+  using T = float;
+};
+template <>
+struct GenAcc<kI8> {
+  using T = int32_t;
+};
+template <int DT>
+__device__ __forceinline__ typename GenAcc<DT>::T load_acc(const void* p, int64_t i) {
+  if constexpr (DT == kI8)
+    return (int32_t) static_cast<const int8_t*>(p)[i];
+  else
+    return load_as_f32<DT>(p, i);
+}
+
 template <int DT, int YT, int N, int M, bool kBlocked>
 __global__ void __launch_bounds__(256) generic_spmm_kernel(const void* __restrict__ values,
                                                            const uint32_t* __restrict__ meta,
                                                            const void* __restrict__ X,
                                                            void* __restrict__ Y, int64_t R,
                                                            int64_t K, int64_t T) {
+  using A = typename GenAcc<DT>::T;
   constexpr int b = meta_bits(M);
-  __shared__ float ws[kGT][kGK + 1];
-  __shared__ float xs[kGK][kGT + 4];
+  __shared__ A ws[kGT][kGK + 1];
+  __shared__ A xs[kGK][kGT + 4];
   const int tid = threadIdx.x;
   const int64_t m0 = (int64_t)blockIdx.y * kGT, t0 = (int64_t)blockIdx.x * kGT;
   const int64_t gpr = K / M, wpr = (gpr * N * b + 31) / 32;
   const int ty = tid / 16, tx = tid % 16;
-  float acc[4][4] = {};
+  A acc[4][4] = {};
 
   for (int64_t k0 = 0; k0 < K; k0 += kGK) {
     // expand the compressed rows of this K step into fp32 (zeros where pruned)
@@ -1402,9 +1421,9 @@ __global__ void __launch_bounds__(256) generic_spmm_kernel(const void* __restric
     for (int i = tid; i < kGT * kGroupsPerRow; i += 256) {
       const int r = i / kGroupsPerRow, gl = i % kGroupsPerRow;
       const int64_t row = m0 + r, g = k0 / M + gl;
-      float o[M];
+      A o[M];
 #pragma unroll
-      for (int e = 0; e < M; ++e) o[e] = 0.f;
+      for (int e = 0; e < M; ++e) o[e] = 0;
       if (row < R && g < gpr) {
 #pragma unroll
         for (int j = 0; j < N; ++j) {
@@ -1423,7 +1442,7 @@ __global__ void __launch_bounds__(256) generic_spmm_kernel(const void* __restric
           uint64_t window = meta[bit / 32];
           if ((bit % 32) + b > 32) window |= (uint64_t)meta[bit / 32 + 1] << 32;
           const int p = (int)((window >> (bit % 32)) & ((1u << b) - 1u));
-          const float v = load_as_f32<DT>(values, vi);
+          const A v = load_acc<DT>(values, vi);
 #pragma unroll
           for (int e = 0; e < M; ++e) o[e] = (p == e) ? v : o[e];
         }
@@ -1434,12 +1453,12 @@ __global__ void __launch_bounds__(256) generic_spmm_kernel(const void* __restric
     for (int i = tid; i < kGK * kGT; i += 256) {
       const int kk = i / kGT, c = i % kGT;
       const int64_t k = k0 + kk, col = t0 + c;
-      xs[kk][c] = (k < K && col < T) ? load_as_f32<DT>(X, k * T + col) : 0.f;
+      xs[kk][c] = (k < K && col < T) ? load_acc<DT>(X, k * T + col) : (A)0;
     }
     __syncthreads();
 #pragma unroll 8
     for (int kk = 0; kk < kGK; ++kk) {
-      float wv[4], xv[4];
+      A wv[4], xv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) wv[i] = ws[ty * 4 + i][kk];
 #pragma unroll
@@ -1447,7 +1466,12 @@ __global__ void __launch_bounds__(256) generic_spmm_kernel(const void* __restric
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(wv[i], xv[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (DT == kI8)
+            acc[i][j] += wv[i] * xv[j];
+          else
+            acc[i][j] = __builtin_fmaf(wv[i], xv[j], acc[i][j]);
+        }
     }
     __syncthreads();
   }
@@ -1458,7 +1482,11 @@ __global__ void __launch_bounds__(256) generic_spmm_kernel(const void* __restric
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t col = t0 + tx * 4 + j;
-      if (col < T) store_from_f32<YT>(Y, row * T + col, acc[i][j]);
+      if (col >= T) continue;
+      if constexpr (YT == kI32)
+        static_cast<int32_t*>(Y)[row * T + col] = acc[i][j];
+      else
+        store_from_f32<YT>(Y, row * T + col, acc[i][j]);
     }
   }
 }
@@ -1650,14 +1678,15 @@ hipError_t launch_spmm(const void* values, const uint32_t* meta, int64_t R, int6
   // the matrix-core kernel addresses A, its metadata and X with 32-bit byte offsets
   const bool tiled_shape = K > 0 && K % kKStep == 0 && T % 8 == 0 && R < (1 << 30) &&
                            T < (1 << 30) && K < (1 << 30);
-  if (dt != kF32 && n == 4 && m == 8 && blocked && tiled_shape) {
+  const bool half = dt == kBF16 || dt == kF16;
+  if (half && n == 4 && m == 8 && blocked && tiled_shape) {
     if (dt == kBF16)
       return y_dt == kF32 ? run_mfma48<true, kF32>(values, meta, R, K, X, T, Y, s)
                           : run_mfma48<true, kBF16>(values, meta, R, K, X, T, Y, s);
     return y_dt == kF32 ? run_mfma48<false, kF32>(values, meta, R, K, X, T, Y, s)
                         : run_mfma48<false, kF16>(values, meta, R, K, X, T, Y, s);
   }
-  if (dt != kF32 && (pat24 || pat12) && tiled_shape) {
+  if (half && (pat24 || pat12) && tiled_shape) {
     const bool yf32 = y_dt == kF32;
 #define NM_S(BF, P12)                                                                       \
   return yf32 ? run_smfmac_layout<BF, P12, kF32>(values, meta, R, K, blocked, X, T, Y, s)   \
@@ -1672,12 +1701,15 @@ hipError_t launch_spmm(const void* values, const uint32_t* meta, int64_t R, int6
   }
   if (K == 0) {
     // empty contraction: Y = 0, written by a fill kernel (safe under stream capture)
-    const int64_t words = R * T * (y_dt == kF32 ? 4 : 2) / 4;
-    const int64_t tail_halves = (R * T * (y_dt == kF32 ? 4 : 2) % 4) / 2;
+    const int ybytes = (y_dt == kF32 || y_dt == kI32) ? 4 : 2;
+    const int64_t words = R * T * ybytes / 4;
+    const int64_t tail_halves = (R * T * ybytes % 4) / 2;
     zero_fill_kernel<<<(unsigned)((words + 255) / 256 + 1), 256, 0, s>>>(
         static_cast<uint32_t*>(Y), words, tail_halves);
     return hipGetLastError();
   }
+  if (dt == kI8)
+    return run_generic_layout<kI8, kI32>(values, meta, R, K, n, m, blocked, X, T, Y, s);
   if (dt == kF32)
     return run_generic_layout<kF32, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s);
   if (dt == kBF16)

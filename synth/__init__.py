@@ -211,6 +211,12 @@ WORKLOADS = {
                                Dist("normal", 1, relu=True)),
     "llama_up": _llama(11008, 4096, "llama_up"),
     "llama_down": _llama(4096, 11008, "llama_down"),
+    # the LLaMA-7B MLP pair quantised to int8: weights and activations ~N(0, 24^2)
+    # rounded to integers (about 1 in 25,000 draws clipped at +-127.5)
+    "llama_up_i8": Workload("llama_up_i8", 11008, 4096, 2048, "i8", Dist("normal", 0, 24.0),
+                            Dist("normal", 1, 24.0), note="LLaMA-7B MLP up-projection, int8"),
+    "llama_down_i8": Workload("llama_down_i8", 4096, 11008, 2048, "i8", Dist("normal", 0, 24.0),
+                              Dist("normal", 1, 24.0), note="LLaMA-7B MLP down-projection, int8"),
     # N:M sweep: fp16 4096 x 4096 ~Laplace(0, 0.05), activations 4096 x 8192 ~N(0,1)
     "sweep_f16": Workload("sweep_f16", 4096, 4096, 8192, "f16", Dist("laplace", 0, 0.05),
                           Dist("normal", 1), patterns=((1, 2), (2, 4), (4, 8))),

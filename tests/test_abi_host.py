@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     L = nm.lib()
     for name in header_functions():
         assert hasattr(L, name), name
-    assert L.nm_abi_version() == nm.ABI_VERSION == 4
+    assert L.nm_abi_version() == nm.ABI_VERSION == 5
 
 
 @needs_lib
@@ -255,6 +255,30 @@ def test_compress_t_argument_errors(case, expect):
     code = L.nm_compress_t(a["W"], a["dt"], a["R"], a["K"], a["n"], a["m"], a["layout"],
                            a["values"], a["meta"], None)
     assert nm.STATUS[code] == expect
+
+
+@needs_lib
+def test_int8_argument_rules():
+    L = nm.lib()
+    I8, I32, BF16, ROWS, BLOCKED = nm.NM_I8, nm.NM_I32, nm.NM_BF16, 0, 1
+    assert L.nm_values_bytes(64, 128, 2, 4, I8, ROWS) == 64 * 64
+    assert L.nm_values_bytes(64, 128, 1, 8, I8, BLOCKED) == 0       # 2 bytes per lane share
+    assert L.nm_values_bytes(64, 128, 2, 8, I8, BLOCKED) == 64 * 32
+    st = lambda code: nm.STATUS[code]
+    # products: int8 in, int32 out, and nothing else mixes with int8
+    spmm = lambda dt, ydt, K=128, layout=ROWS, n=2, m=4: L.nm_spmm(
+        FAKE, FAKE, 64, K, n, m, layout, FAKE, 32, dt, FAKE + 0x100000, ydt, None)
+    assert st(spmm(I8, nm.NM_F32)) == "dtype"
+    assert st(spmm(I8, I8)) == "dtype"
+    assert st(spmm(BF16, I32)) == "dtype"
+    assert st(spmm(I8, I32, K=1 << 17)) == "shape"
+    assert st(spmm(I8, I32, layout=BLOCKED, n=3, m=8)) == "unsupported"
+    assert st(L.nm_compress(FAKE, I8, 64, 128, 1, 8, BLOCKED, FAKE, FAKE, None)) == "unsupported"
+    assert st(L.nm_decompress(FAKE, FAKE, I8, 64, 128, 5, 8, BLOCKED, FAKE, None)) == "unsupported"
+    # the training-side calls need floating-point weights
+    assert st(L.nm_tmask(FAKE, I8, 64, 128, 2, 4, FAKE + 0x100000, None)) == "dtype"
+    assert st(L.nm_prune(FAKE, I8, 64, 128, 2, 4, FAKE + 0x100000, None)) == "dtype"
+    assert st(L.nm_mask(FAKE, I32, 64, 128, 2, 4, FAKE + 0x100000, None)) == "dtype"
 
 
 @needs_lib
