@@ -37,11 +37,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "2:4 spmm effective TFLOP/s + mask/compress GB/s (% of MI355X roofline)"
+METRIC_I8 = "2:4 int8 spmm effective TOP/s + mask/compress GB/s (% of MI355X roofline)"
 PEAK_HBM_GBS = 8000.0
-PEAK_MFMA_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+# dense matrix-core peaks (TFLOP/s; TOP/s for int8)
+PEAK_MFMA_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3, "i8": 5033.2}
 # workload name -> (synthetic matrices, N:M pattern)
 WORKLOADS = {
     "llama_mlp": (["llama_up", "llama_down"], (2, 4)),
+    "llama_mlp_i8": (["llama_up_i8", "llama_down_i8"], (2, 4)),
     "bert_ffn": (["bert_ffn"], (2, 4)),
     "resnet_conv3x3": (["resnet_conv3x3"], (2, 4)),
     "sweep_f16_2_4": (["sweep_f16"], (2, 4)),
@@ -56,15 +59,17 @@ def meta_bits(m: int) -> int:
 
 
 def algorithmic_bytes(R, K, T, n, m, s):
-    """Bytes each kernel must move at minimum (one read of inputs, one write of outputs)."""
+    """Bytes each kernel must move at minimum (one read of inputs, one write of outputs).
+    Y has the input's element size, except int8 (s = 1), whose products are int32."""
     e = R * K
     kept = e * n // m
     meta = R * ((K // m * n * meta_bits(m) + 31) // 32) * 4
+    ys = 4 if s == 1 else s
     return {
         "mask": e * s + e,
         "compress": e * s + kept * s + meta,
         "decompress": kept * s + meta + e * s,
-        "spmm": kept * s + meta + K * T * s + R * T * s,
+        "spmm": kept * s + meta + K * T * s + R * T * ys,
     }
 
 
@@ -158,7 +163,8 @@ def cpu_baseline(mats, n, m, threads: int, budget_s: float = 12.0):
     dt = time.perf_counter() - t0
     sample = ", ".join(f"{k}: rows 0..{v} of {next(w['R'] for w in mats if w['name'] == k)}"
                        for k, v in rows_done.items())
-    return {"value": F / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    unit = "TOP/s" if mats[0]["dtype"] == "i8" else "TFLOP/s"
+    return {"value": F / dt / 1e12, "unit": unit, "cores": threads, "kind": "oracle",
             "seconds": round(dt, 2),
             "sample": f"mask+compress+decompress+product of {sample} (fp64 product, all T columns)"}
 
@@ -198,15 +204,17 @@ def main() -> int:
     for name in names:
         w = synth.WORKLOADS[name]
         W, X = w.W(), w.X()
-        tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
+        tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32,
+               "i8": torch.int8}[w.dtype]
+        ydt = torch.int32 if w.dtype == "i8" else tdt
 
         def to_dev(a, tdt=tdt):
-            if a.dtype == np.float32:
+            if a.dtype in (np.float32, np.int8):
                 return torch.from_numpy(a).to(dev)
             return torch.from_numpy(a.view(np.int16)).view(tdt).to(dev)
 
-        s = 4 if w.dtype == "f32" else 2
-        G = w.G()
+        s = {"f32": 4, "i8": 1}.get(w.dtype, 2)
+        G = w.G() if w.dtype != "i8" else W  # the SR-STE gradient (float weights only)
         d = dict(name=name, R=w.R, K=w.K, T=w.T, dtype=w.dtype, s=s, W=W, X=X, G=G, Wd=to_dev(W),
                  Xd=to_dev(X), Gd=to_dev(G))
         vshape, mshape = nm.compressed_shapes(w.R, w.K, n, m, args.layout)
@@ -214,7 +222,7 @@ def main() -> int:
         d["meta"] = torch.empty(mshape, dtype=torch.int32, device=dev)
         d["mask"] = torch.empty((w.R, w.K), dtype=torch.bool, device=dev)
         d["dec"] = torch.empty((w.R, w.K), dtype=tdt, device=dev)
-        d["Y"] = torch.empty((w.R, w.T), dtype=tdt, device=dev)
+        d["Y"] = torch.empty((w.R, w.T), dtype=ydt, device=dev)
         d["pruned"] = torch.empty((w.R, w.K), dtype=tdt, device=dev)
         d["grad"] = torch.empty((w.R, w.K), dtype=tdt, device=dev)
         # transposable-mask path: pruned weight, compressed transpose, backward product
@@ -222,7 +230,7 @@ def main() -> int:
         vts, mts = nm.compressed_shapes(w.K, w.R, n, m, args.layout)
         d["vals_t"] = torch.empty(vts, dtype=tdt, device=dev)
         d["meta_t"] = torch.empty(mts, dtype=torch.int32, device=dev)
-        d["dX"] = torch.empty((w.K, w.T), dtype=tdt, device=dev)
+        d["dX"] = torch.empty((w.K, w.T), dtype=ydt, device=dev)
         mats.append(d)
     dtype = mats[0]["dtype"]
     if args.copy_calibration:
@@ -235,7 +243,9 @@ def main() -> int:
     L = nm.lib()
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
-    DT = {"f32": 0, "f16": 1, "bf16": 2}[dtype]
+    DT = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3}[dtype]
+    YDT = 4 if dtype == "i8" else DT  # int8 products are exact int32
+    float_path = dtype != "i8"        # SR-STE and transposable masks train float weights
     LAY = nm.LAYOUTS[args.layout]
     kinds = ["mask", "compress", "decompress", "spmm"]
 
@@ -250,7 +260,7 @@ def main() -> int:
                                  n, m, LAY, d["dec"].data_ptr(), sp)
         elif kind == "spmm":
             rc = L.nm_spmm(d["vals"].data_ptr(), d["meta"].data_ptr(), d["R"], d["K"], n, m, LAY,
-                           d["Xd"].data_ptr(), d["T"], DT, d["Y"].data_ptr(), DT, sp)
+                           d["Xd"].data_ptr(), d["T"], DT, d["Y"].data_ptr(), YDT, sp)
         elif kind == "tprune":
             rc = L.nm_tprune(d["Wd"].data_ptr(), DT, d["R"], d["K"], n, m, d["tpruned"].data_ptr(),
                              sp)
@@ -330,7 +340,8 @@ def main() -> int:
     peak = PEAK_MFMA_TFLOPS[dtype]
     roofline = {"bound": "mfma",
                 "kernel": "nm_spmm (structured-sparse matrix cores)" if n * 2 == m else "nm_spmm",
-                "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "achieved": round(achieved, 1), "peak": peak,
+                "unit": "TOP/s" if dtype == "i8" else "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": None,
                 "alg_bytes_per_launch": sum(algorithmic_bytes(d["R"], d["K"], d["T"], n, m,
                                                               d["s"])["spmm"] for d in mats) / len(mats),
@@ -357,13 +368,18 @@ def main() -> int:
             if d["dtype"] == "f32":
                 continue
             A, B = d["dec"], d["Xd"]
-            for _ in range(3):
-                torch.matmul(A, B)
+            # int8: torch._int_mm (int8 x int8 -> int32), where this PyTorch build has it
+            mm = torch._int_mm if d["dtype"] == "i8" else torch.matmul
+            try:
+                for _ in range(3):
+                    mm(A, B)
+            except (RuntimeError, AttributeError):
+                continue
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for _ in range(args.steps):
-                torch.matmul(A, B)
+                mm(A, B)
             e1.record(stream)
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1) / args.steps * 1e-3)
@@ -371,105 +387,109 @@ def main() -> int:
             dense_t = sum(ts)
             dense = {"tflops": round(F_eff / dense_t / 1e12, 1), "us_total": round(dense_t * 1e6, 1),
                      "spmm_speedup": round(dense_t / spmm_t, 3),
-                     "how": "torch.matmul (hipBLASLt) on the decompressed weight, same dtype"}
+                     "how": ("torch._int_mm" if dtype == "i8" else "torch.matmul (hipBLASLt)")
+                            + " on the decompressed weight, same dtype"}
 
-    # ---- SR-STE passes on the same weights (not part of the step) ----
-    # Each timed launch starts cold: a 512 MiB fill (twice the 256 MB Infinity Cache) runs
-    # before it, outside its events, so its inputs come from HBM as in a training step,
-    # where the forward and the backward of a layer are far apart.
-    sr_kinds = ["prune", "srste_grad"]
-    flush = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
-    for _ in range(args.warmup):
-        step(kinds=sr_kinds)
-    torch.cuda.synchronize()
-    sr_per = {}
-    for _ in range(args.steps):
-        for d in mats:
-            for kind in sr_kinds:
-                flush.zero_()
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                launch(d, kind)
-                e1.record(stream)
-                sr_per.setdefault((d["name"], kind), []).append((e0, e1))
-    torch.cuda.synchronize()
-    sr_per = {k: [a.elapsed_time(b) * 1e-3 for a, b in v] for k, v in sr_per.items()}
-    del flush
-    srste = {"decay": nm.SRSTE_DECAY, "kernels": {}}
-    sr_tot = {k: [0.0, 0.0] for k in sr_kinds}
-    for d in mats:
-        e = d["R"] * d["K"]
-        ab = {"prune": 2 * e * d["s"], "srste_grad": 3 * e * d["s"]}
-        for kind in sr_kinds:
-            t = float(np.mean(sr_per[(d["name"], kind)]))
-            srste["kernels"][f"{d['name']}.{kind}"] = {
-                "us": round(t * 1e6, 2), "alg_bytes": ab[kind], "gbps": round(ab[kind] / t / 1e9, 1),
-                "frac_hbm": round(ab[kind] / t / 1e9 / PEAK_HBM_GBS, 3)}
-            sr_tot[kind][0] += t
-            sr_tot[kind][1] += ab[kind]
-    g_t, g_b = sr_tot["srste_grad"]
-    srste["roofline"] = {"bound": "hbm", "kernel": "nm_srste_grad", "achieved": round(g_b / g_t / 1e9, 1),
-                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(g_b / g_t / 1e9 / PEAK_HBM_GBS, 3),
-                         "alg_bytes_per_elem": 3 * mats[0]["s"], "traffic": None}
-    g_traffic = profiled_traffic(args.workload, "srste_unit_kernel<2, 2, 4, true>"
-                                 if dtype == "bf16" else "srste_unit_kernel", "nm_srste.hip")
-    if g_traffic is not None:
-        srste["roofline"]["traffic"] = round(g_traffic)
-    srste["prune_frac_hbm"] = round(sr_tot["prune"][1] / sr_tot["prune"][0] / 1e9 / PEAK_HBM_GBS, 3)
-    srste["step_us"] = round((g_t + sr_tot["prune"][0]) * 1e6, 1)
-
-    # ---- transposable-mask path on the same weights (not part of the step) ----
-    # tprune and compress_t are timed cold, like the SR-STE passes; the backward product
-    # in the step's manner (its operands fit the Infinity Cache only in part).
-    tr_kinds = ["tprune", "compress_t", "spmm_t"]
-    flush = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
-    for _ in range(args.warmup):
-        step(kinds=tr_kinds)
-    torch.cuda.synchronize()
-    tr_ev = {}
-    for _ in range(args.steps):
-        for d in mats:
-            for kind in tr_kinds:
-                if kind != "spmm_t":
+    srste = transposable = None
+    if float_path:
+        # ---- SR-STE passes on the same weights (not part of the step) ----
+        # Each timed launch starts cold: a 512 MiB fill (twice the 256 MB Infinity Cache) runs
+        # before it, outside its events, so its inputs come from HBM as in a training step,
+        # where the forward and the backward of a layer are far apart.
+        sr_kinds = ["prune", "srste_grad"]
+        flush = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
+        for _ in range(args.warmup):
+            step(kinds=sr_kinds)
+        torch.cuda.synchronize()
+        sr_per = {}
+        for _ in range(args.steps):
+            for d in mats:
+                for kind in sr_kinds:
                     flush.zero_()
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                launch(d, kind)
-                e1.record(stream)
-                tr_ev.setdefault((d["name"], kind), []).append((e0, e1))
-    torch.cuda.synchronize()
-    del flush
-    transposable = {"kernels": {}}
-    for d in mats:
-        e = d["R"] * d["K"]
-        kept = e * n // m
-        meta_t = d["K"] * ((d["R"] // m * n * meta_bits(m) + 31) // 32) * 4
-        for kind in tr_kinds:
-            t = float(np.mean([a.elapsed_time(b) for a, b in tr_ev[(d["name"], kind)]])) * 1e-3
-            entry = {"us": round(t * 1e6, 2)}
-            if kind == "spmm_t":
-                entry["eff_tflops"] = round(2.0 * e * d["T"] / t / 1e12, 1)
-                entry["alg_tflops"] = round(2.0 * kept * d["T"] / t / 1e12, 1)
-            else:
-                ab = 2 * e * d["s"] if kind == "tprune" else e * d["s"] + kept * d["s"] + meta_t
-                entry.update(alg_bytes=ab, gbps=round(ab / t / 1e9, 1),
-                             frac_hbm=round(ab / t / 1e9 / PEAK_HBM_GBS, 3))
-            transposable["kernels"][f"{d['name']}.{kind}"] = entry
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    launch(d, kind)
+                    e1.record(stream)
+                    sr_per.setdefault((d["name"], kind), []).append((e0, e1))
+        torch.cuda.synchronize()
+        sr_per = {k: [a.elapsed_time(b) * 1e-3 for a, b in v] for k, v in sr_per.items()}
+        del flush
+        srste = {"decay": nm.SRSTE_DECAY, "kernels": {}}
+        sr_tot = {k: [0.0, 0.0] for k in sr_kinds}
+        for d in mats:
+            e = d["R"] * d["K"]
+            ab = {"prune": 2 * e * d["s"], "srste_grad": 3 * e * d["s"]}
+            for kind in sr_kinds:
+                t = float(np.mean(sr_per[(d["name"], kind)]))
+                srste["kernels"][f"{d['name']}.{kind}"] = {
+                    "us": round(t * 1e6, 2), "alg_bytes": ab[kind], "gbps": round(ab[kind] / t / 1e9, 1),
+                    "frac_hbm": round(ab[kind] / t / 1e9 / PEAK_HBM_GBS, 3)}
+                sr_tot[kind][0] += t
+                sr_tot[kind][1] += ab[kind]
+        g_t, g_b = sr_tot["srste_grad"]
+        srste["roofline"] = {"bound": "hbm", "kernel": "nm_srste_grad", "achieved": round(g_b / g_t / 1e9, 1),
+                             "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": round(g_b / g_t / 1e9 / PEAK_HBM_GBS, 3),
+                             "alg_bytes_per_elem": 3 * mats[0]["s"], "traffic": None}
+        g_traffic = profiled_traffic(args.workload, "srste_unit_kernel<2, 2, 4, true>"
+                                     if dtype == "bf16" else "srste_unit_kernel", "nm_srste.hip")
+        if g_traffic is not None:
+            srste["roofline"]["traffic"] = round(g_traffic)
+        srste["prune_frac_hbm"] = round(sr_tot["prune"][1] / sr_tot["prune"][0] / 1e9 / PEAK_HBM_GBS, 3)
+        srste["step_us"] = round((g_t + sr_tot["prune"][0]) * 1e6, 1)
+
+        # ---- transposable-mask path on the same weights (not part of the step) ----
+        # tprune and compress_t are timed cold, like the SR-STE passes; the backward product
+        # in the step's manner (its operands fit the Infinity Cache only in part).
+        tr_kinds = ["tprune", "compress_t", "spmm_t"]
+        flush = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
+        for _ in range(args.warmup):
+            step(kinds=tr_kinds)
+        torch.cuda.synchronize()
+        tr_ev = {}
+        for _ in range(args.steps):
+            for d in mats:
+                for kind in tr_kinds:
+                    if kind != "spmm_t":
+                        flush.zero_()
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    launch(d, kind)
+                    e1.record(stream)
+                    tr_ev.setdefault((d["name"], kind), []).append((e0, e1))
+        torch.cuda.synchronize()
+        del flush
+        transposable = {"kernels": {}}
+        for d in mats:
+            e = d["R"] * d["K"]
+            kept = e * n // m
+            meta_t = d["K"] * ((d["R"] // m * n * meta_bits(m) + 31) // 32) * 4
+            for kind in tr_kinds:
+                t = float(np.mean([a.elapsed_time(b) for a, b in tr_ev[(d["name"], kind)]])) * 1e-3
+                entry = {"us": round(t * 1e6, 2)}
+                if kind == "spmm_t":
+                    entry["eff_tflops"] = round(2.0 * e * d["T"] / t / 1e12, 1)
+                    entry["alg_tflops"] = round(2.0 * kept * d["T"] / t / 1e12, 1)
+                else:
+                    ab = 2 * e * d["s"] if kind == "tprune" else e * d["s"] + kept * d["s"] + meta_t
+                    entry.update(alg_bytes=ab, gbps=round(ab / t / 1e9, 1),
+                                 frac_hbm=round(ab / t / 1e9 / PEAK_HBM_GBS, 3))
+                transposable["kernels"][f"{d['name']}.{kind}"] = entry
 
     cpu = None
     if not args.no_cpu:
-        srste["cpu_baseline"] = srste_cpu_sample(mats, n, m)
+        if float_path:
+            srste["cpu_baseline"] = srste_cpu_sample(mats, n, m)
         threads = max(1, min(16, os.cpu_count() or 1))
         cpu = cpu_baseline(mats, n, m, threads)
 
     w0 = mats[0]
     out = {
-        "metric": METRIC,
+        "metric": METRIC if float_path else METRIC_I8,
         "value": round(value, 2),
-        "unit": "TFLOP/s",
+        "unit": "TFLOP/s" if float_path else "TOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,

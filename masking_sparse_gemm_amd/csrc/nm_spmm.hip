@@ -620,11 +620,11 @@ __device__ __forceinline__ void widen_frags(AFrags& a) {
 // is either wholly inside the matrix or wholly outside.  A wave's LDS accesses complete in
 // order, so the reads see this slab's writes and the next slab's writes follow the reads.
 constexpr int kEpilogueBytes = 32 * (64 * 4 + 16);
-template <int YT>
-__device__ __forceinline__ void store_block_128x64(const float16v_t (&acc)[4][2], uint8_t* lds,
+template <int YT, typename AccV = float16v_t>
+__device__ __forceinline__ void store_block_128x64(const AccV (&acc)[4][2], uint8_t* lds,
                                                    void* Y, int row0, int col0, int R, int T,
                                                    int lane) {
-  constexpr int kEB = YT == kF32 ? 4 : 2;   // bytes per output
+  constexpr int kEB = (YT == kF32 || YT == kI32) ? 4 : 2;   // bytes per output
   constexpr int kPitch = 64 * kEB + 16;     // LDS row pitch, padded against bank conflicts
   constexpr int kPer16 = 16 / kEB;          // outputs per 16-byte piece
   constexpr int kRowPieces = 64 / kPer16;
@@ -638,8 +638,10 @@ __device__ __forceinline__ void store_block_128x64(const float16v_t (&acc)[4][2]
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         uint8_t* d = lds + (8 * (i / 4) + 4 * q + (i % 4)) * kPitch + (32 * f + l32) * kEB;
-        const float v = acc[fm][f][i];
-        if constexpr (YT == kF32)
+        const auto v = acc[fm][f][i];
+        if constexpr (YT == kI32)
+          *reinterpret_cast<int32_t*>(d) = v;
+        else if constexpr (YT == kF32)
           *reinterpret_cast<float*>(d) = v;
         else if constexpr (YT == kBF16)
           *reinterpret_cast<uint16_t*>(d) = (uint16_t)f32_to_bf16(v);
@@ -1046,6 +1048,230 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
   static_assert(TL::kConsumers * kEpilogueBytes <= kStages * TL::kStageBytes, "epilogue LDS");
   store_block_128x64<YT>(acc, smem + wave * kEpilogueBytes, Y, m0 + wm * TL::kWM,
                          t0 + wn * TL::kWN, R, T, lane);
+}
+
+// ===========================================================================
+// int8 2:4 on v_smfmac_i32_32x32x64_i8 (exact int32 sums).  Lane l of the instruction
+// supplies row l % 32 of A as 16 stored bytes covering logical K [32 (l/32), +32) (8 groups,
+// one 32-bit index word of 2-bit positions), and column l % 32 of B as 32 bytes, K
+// {16 (l/32) + 0..15} and {32 + 16 (l/32) + 0..15}; the accumulator has the dense 32 x 32
+// layout.  B comes out of the row-major X tile with ds_read_b64_tr_b8: inside each 16-lane
+// block, lane i receives byte (i & 7) of the 8-byte chunks addressed by lanes (i >> 3) + 2j
+// (j = 0..7), so with even lanes addressing 8 columns of 8 consecutive K rows and odd
+// lanes the next 8 columns of the same rows, lane i gets 8 consecutive K of column i.
+// One pipeline step is 128 of K: two blocked-layout steps, i.e. one contiguous 1 KB of
+// values and 256 bytes of metadata per 16 rows, and 128 rows of X.  Wave-specialised as
+// smfmac_ws_spmm_kernel: producer waves issue the direct loads (4-stage ring, one barrier
+// per step), each of four consumer waves owns 128 x 64 outputs (4 x 2 fragments).
+// ===========================================================================
+constexpr int kI8KStep = 128;
+
+// Physical 16-byte chunk of logical chunk c in X tile row r (8 chunks per 128-byte row):
+// the eight rows of one transposing read, and the two 16-row halves a wave reads at
+// once, land on different banks.
+__device__ __forceinline__ int xsw_i8(int r) { return ((r >> 1) ^ (r >> 4)) & 7; }
+
+template <int BM, int BN, int CWAVES_M, int CWAVES_N, int PWAVES, int STAGES>
+struct WsI8Tile {
+  static constexpr int kConsumers = CWAVES_M * CWAVES_N;
+  static constexpr int kProducers = PWAVES;
+  static constexpr int kThreads = 64 * (kConsumers + kProducers);
+  static constexpr int kStages = STAGES;
+  static constexpr int kWM = BM / CWAVES_M;
+  static constexpr int kWN = BN / CWAVES_N;
+  static constexpr int kXBytes = kI8KStep * BN;   // 128 K rows of BN bytes
+  static constexpr int kABytes = BM * 64;          // 64 stored bytes per row and step
+  static constexpr int kMBytes = BM * 16;          // 16 metadata bytes per row and step
+  static constexpr int kStageBytes = kXBytes + kABytes + kMBytes;
+  static constexpr int kXLoads = kXBytes / 1024 / kProducers;
+  static constexpr int kALoads = kABytes / 1024 / kProducers;
+  static constexpr int kMLoads = kMBytes / 256 / kProducers;
+  static constexpr int kLoads = kXLoads + kALoads + kMLoads;
+  static_assert(BN == 128, "X rows are 8 swizzled 16-byte chunks");
+  static_assert(kWM == 128 && kWN == 64, "a consumer owns 128 x 64 outputs");
+  static_assert(kXBytes % (1024 * kProducers) == 0 && kABytes % (1024 * kProducers) == 0 &&
+                    kMBytes % (256 * kProducers) == 0,
+                "every producer issues the same number of direct loads per step");
+  static_assert(kStages >= 3 && (kStages - 2) * kLoads <= 63, "vmcnt budget");
+  static_assert(kStages * kStageBytes <= 160 * 1024, "LDS budget");
+};
+
+typedef int int16v_t __attribute__((ext_vector_type(16)));
+typedef int int8v_t __attribute__((ext_vector_type(8)));
+typedef int int4v_t __attribute__((ext_vector_type(4)));
+typedef int int2v_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) int2v_t lds_int2v_t;
+
+template <int YT, int BM, int BN, int CWAVES_M, int CWAVES_N, int PWAVES, int STAGES>
+__global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
+    smfmac_i8_ws_spmm_kernel(const uint8_t* __restrict__ values, const uint32_t* __restrict__ meta,
+                             const uint8_t* __restrict__ X, void* __restrict__ Y, int R, int K,
+                             int T, TileMap map) {
+  using TL = WsI8Tile<BM, BN, CWAVES_M, CWAVES_N, PWAVES, STAGES>;
+  constexpr int kStages = STAGES;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+
+  int tile_m, tile_n;
+  if (!map.tile_of(blockIdx.x, tile_m, tile_n)) return;  // whole workgroup, before any load
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m0 = tile_m * BM, t0 = tile_n * BN;
+  const int nsteps = K / kI8KStep;
+  const int last_step = nsteps - 1;
+  const int steps64 = K / 64;  // blocked-layout steps per row group
+
+  if (wave >= TL::kConsumers) {
+    // ---------------- producer ----------------
+    const int pw = wave - TL::kConsumers;
+    const int last_g = ((R + 15) >> 4) - 1;
+    int64_t x_src[TL::kXLoads];
+    uint32_t x_dst[TL::kXLoads];
+#pragma unroll
+    for (int j = 0; j < TL::kXLoads; ++j) {
+      const int w1k = j * TL::kProducers + pw;  // 1 KB window: 8 rows of the X tile
+      const int slot = w1k * 64 + lane;
+      const int r = slot >> 3, pc = slot & 7;
+      int col = t0 + 16 * (pc ^ xsw_i8(r));
+      col = col < T ? col : 0;  // columns past T: any valid address (outputs past T only)
+      x_src[j] = (int64_t)r * T + col;
+      x_dst[j] = (uint32_t)(w1k * 1024);
+    }
+    int64_t a_src[TL::kALoads], m_src[TL::kMLoads];
+    uint32_t a_dst[TL::kALoads], m_dst[TL::kMLoads];
+#pragma unroll
+    for (int j = 0; j < TL::kALoads; ++j) {
+      const int b16 = j * TL::kProducers + pw;  // row group of the tile
+      int g = (m0 >> 4) + b16;
+      g = g < last_g ? g : last_g;  // rows past the matrix: any valid group
+      a_src[j] = (int64_t)g * steps64 * 512 + 16 * lane;
+      a_dst[j] = (uint32_t)(TL::kXBytes + b16 * 1024);
+    }
+#pragma unroll
+    for (int j = 0; j < TL::kMLoads; ++j) {
+      const int b16 = j * TL::kProducers + pw;
+      int g = (m0 >> 4) + b16;
+      g = g < last_g ? g : last_g;
+      m_src[j] = (int64_t)g * steps64 * 128 + 4 * lane;
+      m_dst[j] = (uint32_t)(TL::kXBytes + TL::kABytes + b16 * 256);
+    }
+    const uint8_t* mg = reinterpret_cast<const uint8_t*>(meta);
+    auto issue_step = [&](int step) {
+      step = step < last_step ? step : last_step;  // past the end: re-read the last step
+      uint8_t* st = smem + (step % kStages) * TL::kStageBytes;
+      const int64_t kx = (int64_t)step * kI8KStep * T;
+#pragma unroll
+      for (int j = 0; j < TL::kXLoads; ++j) global_to_lds<16>(X + x_src[j] + kx, st + x_dst[j]);
+#pragma unroll
+      for (int j = 0; j < TL::kALoads; ++j)
+        global_to_lds<16>(values + a_src[j] + (int64_t)step * 1024, st + a_dst[j]);
+#pragma unroll
+      for (int j = 0; j < TL::kMLoads; ++j)
+        global_to_lds<4>(mg + m_src[j] + (int64_t)step * 256, st + m_dst[j]);
+    };
+#pragma unroll
+    for (int k = 0; k < kStages - 1; ++k) issue_step(k);
+    wait_loads_and_barrier<(kStages - 3) * TL::kLoads>();  // steps 0 and 1 landed
+    for (int s = 0; s < nsteps; ++s) {
+      issue_step(s + kStages - 1);
+      wait_loads_and_barrier<(kStages - 3) * TL::kLoads>();  // step s+2 landed
+    }
+    wait_loads_and_barrier<0>();  // no load in flight when the consumers reuse LDS
+    return;
+  }
+
+  // ---------------- consumer ----------------
+  const int wm = wave / CWAVES_N, wn = wave % CWAVES_N;
+  const int l32 = lane & 31, q = lane >> 5, i16 = lane & 15, blk = lane >> 4;
+  // A and index addresses of fragment fm in half h: row i = wm*128 + 32 fm + l32
+  uint32_t a_off[4], m_off[4];
+#pragma unroll
+  for (int fm = 0; fm < 4; ++fm) {
+    const int i = wm * TL::kWM + 32 * fm + l32;
+    a_off[fm] = (uint32_t)(TL::kXBytes + (i >> 4) * 1024 + (i & 15) * 32 + 16 * q);
+    m_off[fm] = (uint32_t)(TL::kXBytes + TL::kABytes + (i >> 4) * 256 + (i & 15) * 8 + 4 * q);
+  }
+  // B: piece p of fragment f in half h covers K rows 64h + 16q + 8(p & 1) + 32(p >> 1) + 0..7
+  // of columns wn*64 + 32 f + 16 (blk & 1) + 0..15; this lane addresses row + (i16 >> 1),
+  // 8-byte half (i16 & 1) of that 16-column chunk
+  uint32_t b_off[2][2][4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int r = 64 * h + 16 * q + 8 * (p & 1) + 32 * (p >> 1) + (i16 >> 1);
+        const int chunk = (wn * TL::kWN + 32 * f + 16 * (blk & 1)) >> 4;
+        b_off[h][f][p] = (uint32_t)(r * BN + 16 * (chunk ^ xsw_i8(r)) + 8 * (i16 & 1));
+      }
+
+  int16v_t acc[4][2];
+#pragma unroll
+  for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+    for (int f = 0; f < 2; ++f) acc[fm][f] = int16v_t{};
+
+  asm volatile("s_barrier" ::: "memory");  // steps 0 and 1 landed
+  for (int s = 0; s < nsteps; ++s) {
+    const uint8_t* st = smem + (s % kStages) * TL::kStageBytes;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int4v_t a[4];
+      int ix[4];
+#pragma unroll
+      for (int fm = 0; fm < 4; ++fm) {
+        a[fm] = *reinterpret_cast<const int4v_t*>(st + a_off[fm] + 512 * h);
+        ix[fm] = *reinterpret_cast<const int*>(st + m_off[fm] + 128 * h);
+      }
+      int8v_t b[2];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        int2v_t pc[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          pc[p] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_int2v_t*)(st + b_off[h][f][p]));
+        b[f] = int8v_t{pc[0][0], pc[0][1], pc[1][0], pc[1][1],
+                       pc[2][0], pc[2][1], pc[3][0], pc[3][1]};
+      }
+#pragma unroll
+      for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+          acc[fm][f] = __builtin_amdgcn_smfmac_i32_32x32x64_i8(a[fm], b[f], acc[fm][f], ix[fm],
+                                                               0, 0);
+    }
+    asm volatile("s_barrier" ::: "memory");  // step s+2 landed; stage of step s released
+  }
+  asm volatile("s_barrier\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  static_assert(TL::kConsumers * kEpilogueBytes <= kStages * TL::kStageBytes, "epilogue LDS");
+  store_block_128x64<YT, int16v_t>(acc, smem + wave * kEpilogueBytes, Y, m0 + wm * TL::kWM,
+                                   t0 + wn * TL::kWN, R, T, lane);
+}
+
+int xcd_count();
+
+hipError_t run_smfmac_i8(const void* values, const uint32_t* meta, int64_t R, int64_t K,
+                         const void* X, int64_t T, void* Y, hipStream_t s) {
+  constexpr int BM = 256, BN = 128, ST = 4;
+  using TL = WsI8Tile<BM, BN, 2, 2, 4, ST>;
+  auto kernel = smfmac_i8_ws_spmm_kernel<kI32, BM, BN, 2, 2, 4, ST>;
+  const size_t lds = (size_t)ST * TL::kStageBytes;
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
+  TileMap map;
+  map.tiles_m = (int)((R + BM - 1) / BM);
+  map.tiles_n = (int)((T + BN - 1) / BN);
+  map.xcds = xcd_count();
+  map.per_xcd = (map.tiles_m * map.tiles_n + map.xcds - 1) / map.xcds;
+  map.gn = map.tiles_n < 4 ? map.tiles_n : 4;
+  map.gm = 32 / map.gn;
+  kernel<<<map.xcds * map.per_xcd, TL::kThreads, lds, s>>>(
+      static_cast<const uint8_t*>(values), meta, static_cast<const uint8_t*>(X), Y, (int)R,
+      (int)K, (int)T, map);
+  return hipGetLastError();
 }
 
 // ===========================================================================
@@ -1708,8 +1934,14 @@ hipError_t launch_spmm(const void* values, const uint32_t* meta, int64_t R, int6
         static_cast<uint32_t*>(Y), words, tail_halves);
     return hipGetLastError();
   }
-  if (dt == kI8)
+  if (dt == kI8) {
+    // the matrix-core kernel: 2:4, blocked layout, K a multiple of 128 (two blocked steps),
+    // T a multiple of 16 (16-byte X loads), 32-bit byte offsets
+    if (pat24 && blocked && K % kI8KStep == 0 && T % 16 == 0 && R < (1 << 30) &&
+        T < (1 << 30) && K < (1 << 30))
+      return run_smfmac_i8(values, meta, R, K, X, T, Y, s);
     return run_generic_layout<kI8, kI32>(values, meta, R, K, n, m, blocked, X, T, Y, s);
+  }
   if (dt == kF32)
     return run_generic_layout<kF32, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s);
   if (dt == kBF16)
