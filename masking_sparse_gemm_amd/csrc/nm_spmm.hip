@@ -1212,35 +1212,51 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
 #pragma unroll
     for (int f = 0; f < 2; ++f) acc[fm][f] = int16v_t{};
 
+  // Fragments of one half step (64 of K): 4 A fragments with their index words and 2 B
+  // fragments.  The next half step's fragments are read while this one's 8 smfmac run.
+  struct Frags {
+    int4v_t a[4];
+    int ix[4];
+    int8v_t b[2];
+  };
+  auto load_frags = [&](const uint8_t* st, int h) {
+    Frags F;
+#pragma unroll
+    for (int fm = 0; fm < 4; ++fm) {
+      F.a[fm] = *reinterpret_cast<const int4v_t*>(st + a_off[fm] + 512 * h);
+      F.ix[fm] = *reinterpret_cast<const int*>(st + m_off[fm] + 128 * h);
+    }
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      int2v_t pc[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        pc[p] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_int2v_t*)(st + b_off[h][f][p]));
+      F.b[f] = int8v_t{pc[0][0], pc[0][1], pc[1][0], pc[1][1],
+                       pc[2][0], pc[2][1], pc[3][0], pc[3][1]};
+    }
+    return F;
+  };
+  auto mma = [&](const Frags& F) {
+#pragma unroll
+    for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+        acc[fm][f] = __builtin_amdgcn_smfmac_i32_32x32x64_i8(F.a[fm], F.b[f], acc[fm][f],
+                                                             F.ix[fm], 0, 0);
+  };
+
   asm volatile("s_barrier" ::: "memory");  // steps 0 and 1 landed
+  Frags cur = load_frags(smem, 0);
   for (int s = 0; s < nsteps; ++s) {
     const uint8_t* st = smem + (s % kStages) * TL::kStageBytes;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      int4v_t a[4];
-      int ix[4];
-#pragma unroll
-      for (int fm = 0; fm < 4; ++fm) {
-        a[fm] = *reinterpret_cast<const int4v_t*>(st + a_off[fm] + 512 * h);
-        ix[fm] = *reinterpret_cast<const int*>(st + m_off[fm] + 128 * h);
-      }
-      int8v_t b[2];
-#pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        int2v_t pc[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-          pc[p] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_int2v_t*)(st + b_off[h][f][p]));
-        b[f] = int8v_t{pc[0][0], pc[0][1], pc[1][0], pc[1][1],
-                       pc[2][0], pc[2][1], pc[3][0], pc[3][1]};
-      }
-#pragma unroll
-      for (int fm = 0; fm < 4; ++fm)
-#pragma unroll
-        for (int f = 0; f < 2; ++f)
-          acc[fm][f] = __builtin_amdgcn_smfmac_i32_32x32x64_i8(a[fm], b[f], acc[fm][f], ix[fm],
-                                                               0, 0);
-    }
+    const uint8_t* sn = smem + ((s + 1) % kStages) * TL::kStageBytes;
+    Frags nxt = load_frags(st, 1);
+    mma(cur);
+    // step s+1 landed before the previous barrier; after the last step this reads a
+    // stage of re-read data that is never used
+    cur = load_frags(sn, 0);
+    mma(nxt);
     asm volatile("s_barrier" ::: "memory");  // step s+2 landed; stage of step s released
   }
   asm volatile("s_barrier\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
