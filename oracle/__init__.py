@@ -26,6 +26,10 @@ follow the definitions cited in ``nm_oracle.h``:
   Transposable Masks", ABSTRACT and "提出的方法"): the greedy 2-approximation
   the GPU runs, the minimum-cost-flow optimum as a reference, and the forward
   weight under the greedy mask.  ``compress_t`` is compress of the transpose.
+* ``kept_l1`` / ``perm_gains`` / ``perm_search``: channel permutation before
+  masking ("[리뷰] Accelerating Sparse Deep Neural Networks", "Step-2: Weight
+  Pruning", Fig. 6), the kept magnitude of a column permutation and a
+  pairwise-swap search for a better one.
 """
 from __future__ import annotations
 
@@ -81,11 +85,16 @@ def lib():
         L.nmo_tmask_greedy.argtypes = [vp, i32, i64, i64, i32, i32, vp]
         L.nmo_tmask_optimal.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp]
         L.nmo_tprune.argtypes = [vp, i32, i64, i64, i32, i32, vp]
+        L.nmo_kept_l1.argtypes = [vp, i32, i64, i64, i32, i32, vp]
+        L.nmo_kept_l1.restype = ctypes.c_double
+        L.nmo_perm_gains.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, vp]
+        L.nmo_perm_search.argtypes = [vp, i32, i64, i64, i32, i32, i32, vp, vp]
         L.nmo_to_double.argtypes = [vp, i32, i64]
         L.nmo_to_double.restype = ctypes.c_double
         for f in ("nmo_mask", "nmo_compress", "nmo_decompress", "nmo_spmm", "nmo_spmm_rows",
                   "nmo_spmm_sample", "nmo_prune", "nmo_srste_grad", "nmo_round_from_f32",
-                  "nmo_tmask_greedy", "nmo_tmask_optimal", "nmo_tprune"):
+                  "nmo_tmask_greedy", "nmo_tmask_optimal", "nmo_tprune", "nmo_perm_gains",
+                  "nmo_perm_search"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -260,6 +269,51 @@ def compress_t(W: np.ndarray, dt, n: int, m: int):
     """compress of the transpose: (values K x R*n/m, meta K x words) of W.T."""
     dt = _code(dt)
     return compress(np.ascontiguousarray(_as_bits(W, dt).T), dt, n, m)
+
+
+def _perm(perm, K):
+    p = np.arange(K, dtype=np.int32) if perm is None else np.ascontiguousarray(perm, dtype=np.int32)
+    if p.shape != (K,):
+        raise ValueError("perm must have K entries")
+    return p
+
+
+def kept_l1(W: np.ndarray, dt, n: int, m: int, perm=None) -> float:
+    """Kept L1 of the N:M mask of W[:, perm] (perm None = identity)."""
+    dt = _code(dt)
+    W = _as_bits(W, dt)
+    R, K = W.shape
+    p = _perm(perm, K)
+    v = lib().nmo_kept_l1(_ptr(W), dt, R, K, n, m, _ptr(p))
+    if v < 0:
+        raise ValueError("oracle kept_l1 rejected its arguments")
+    return v
+
+
+def perm_gains(W: np.ndarray, dt, n: int, m: int, perm=None):
+    """(gain, pick) tables (G x G, upper triangle filled) of the best swap per group pair."""
+    dt = _code(dt)
+    W = _as_bits(W, dt)
+    R, K = W.shape
+    G = K // m
+    p = _perm(perm, K)
+    gain = np.zeros((G, G), dtype=np.float64)
+    pick = np.zeros((G, G), dtype=np.int32)
+    _check(lib().nmo_perm_gains(_ptr(W), dt, R, K, n, m, _ptr(p), _ptr(gain), _ptr(pick)),
+           "perm_gains")
+    return gain, pick
+
+
+def perm_search(W: np.ndarray, dt, n: int, m: int, max_rounds: int = 1000, perm=None):
+    """(perm, rounds applied) after the swap search, starting from perm (None = identity)."""
+    dt = _code(dt)
+    W = _as_bits(W, dt)
+    R, K = W.shape
+    p = _perm(perm, K).copy()
+    done = ctypes.c_int(0)
+    _check(lib().nmo_perm_search(_ptr(W), dt, R, K, n, m, max_rounds, _ptr(p), ctypes.byref(done)),
+           "perm_search")
+    return p, done.value
 
 
 def to_double(a: np.ndarray, dt) -> np.ndarray:

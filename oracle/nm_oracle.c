@@ -654,3 +654,151 @@ int nmo_tprune(const void* W, int dt, int64_t R, int64_t K, int n, int m, void* 
     }
   return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Channel permutation ([ASDNN] "Step-2: Weight Pruning", Fig. 6): permuting  */
+/* the columns of W before the N:M mask is taken changes which weights share */
+/* a group, and a good permutation keeps a larger total magnitude.  The      */
+/* pages show the effect only; the search here is a reading (see            */
+/* nm_oracle.h): rounds of pairwise column swaps between groups.             */
+/*                                                                           */
+/* perm[i] is the column of W placed at position i; groups are positions    */
+/* g*m .. g*m+m-1.  All sums are in double over ascending rows.              */
+/* ------------------------------------------------------------------------ */
+
+/* sum of the n largest of v[0..m-1] (plain selection sort of a copy) */
+static double top_n_sum(const double* v, int n, int m) {
+  double c[16];
+  for (int i = 0; i < m; i++) c[i] = v[i];
+  double s = 0.0;
+  for (int k = 0; k < n; k++) {
+    int best = k;
+    for (int i = k + 1; i < m; i++)
+      if (c[i] > c[best]) best = i;
+    double t = c[k];
+    c[k] = c[best];
+    c[best] = t;
+    s += c[k];
+  }
+  return s;
+}
+
+static double mag_at(const void* W, int dt, int64_t K, int64_t r, int64_t col) {
+  double x = fabs(nmo_to_double(W, dt, r * K + col));
+  return isnan(x) ? INFINITY : x;
+}
+
+static int check_perm(const int32_t* perm, int64_t K) {
+  for (int64_t i = 0; i < K; i++)
+    if (perm[i] < 0 || perm[i] >= K) return -6;
+  return 0;
+}
+
+double nmo_kept_l1(const void* W, int dt, int64_t R, int64_t K, int n, int m,
+                   const int32_t* perm) {
+  if (check_args(dt, R, K, n, m) || check_perm(perm, K)) return -1.0;
+  double total = 0.0, v[16];
+  for (int64_t r = 0; r < R; r++)
+    for (int64_t g = 0; g < K / m; g++) {
+      for (int i = 0; i < m; i++) v[i] = mag_at(W, dt, K, r, perm[g * m + i]);
+      total += top_n_sum(v, n, m);
+    }
+  return total;
+}
+
+/* For every pair of groups g1 < g2: the change of the kept L1 caused by swapping the     */
+/* column at position a of g1 with the column at position b of g2, summed over all rows,  */
+/* maximised over (a, b) (the first (a, b) in row-major order on ties).  gain[g1*G + g2]  */
+/* and pick[g1*G + g2] = a*m + b; entries with g1 >= g2 are left as they are.            */
+int nmo_perm_gains(const void* W, int dt, int64_t R, int64_t K, int n, int m,
+                   const int32_t* perm, double* gain, int32_t* pick) {
+  int rc = check_args(dt, R, K, n, m);
+  if (rc) return rc;
+  if ((rc = check_perm(perm, K))) return rc;
+  const int64_t G = K / m;
+  double* delta = (double*)malloc(sizeof(double) * (size_t)(m * m));
+  if (!delta) return -5;
+  double u[16], v[16], u2[16], v2[16];
+  for (int64_t g1 = 0; g1 < G; g1++)
+    for (int64_t g2 = g1 + 1; g2 < G; g2++) {
+      for (int s = 0; s < m * m; s++) delta[s] = 0.0;
+      for (int64_t r = 0; r < R; r++) {
+        for (int i = 0; i < m; i++) {
+          u[i] = mag_at(W, dt, K, r, perm[g1 * m + i]);
+          v[i] = mag_at(W, dt, K, r, perm[g2 * m + i]);
+        }
+        const double base = top_n_sum(u, n, m) + top_n_sum(v, n, m);
+        for (int a = 0; a < m; a++)
+          for (int b = 0; b < m; b++) {
+            for (int i = 0; i < m; i++) {
+              u2[i] = u[i];
+              v2[i] = v[i];
+            }
+            u2[a] = v[b];
+            v2[b] = u[a];
+            delta[a * m + b] += top_n_sum(u2, n, m) + top_n_sum(v2, n, m) - base;
+          }
+      }
+      int best = 0;
+      for (int s = 1; s < m * m; s++)
+        if (delta[s] > delta[best]) best = s;
+      gain[g1 * G + g2] = delta[best];
+      pick[g1 * G + g2] = best;
+    }
+  free(delta);
+  return 0;
+}
+
+/* Rounds of swaps: compute every pair's best gain; take the pairs with a positive gain  */
+/* in descending order of gain (ties: smaller g1, then smaller g2) and apply each one    */
+/* whose two groups are still untouched in this round; stop when a round applies none   */
+/* or after max_rounds.  perm is updated in place; *rounds_done counts applied rounds.   */
+int nmo_perm_search(const void* W, int dt, int64_t R, int64_t K, int n, int m, int max_rounds,
+                    int32_t* perm, int* rounds_done) {
+  int rc = check_args(dt, R, K, n, m);
+  if (rc) return rc;
+  if ((rc = check_perm(perm, K))) return rc;
+  const int64_t G = K / m;
+  double* gain = (double*)malloc(sizeof(double) * (size_t)(G * G > 0 ? G * G : 1));
+  int32_t* pick = (int32_t*)malloc(sizeof(int32_t) * (size_t)(G * G > 0 ? G * G : 1));
+  uint8_t* used = (uint8_t*)malloc((size_t)(G > 0 ? G : 1));
+  if (!gain || !pick || !used) {
+    free(gain);
+    free(pick);
+    free(used);
+    return -5;
+  }
+  int done = 0;
+  for (int round = 0; round < max_rounds; round++) {
+    nmo_perm_gains(W, dt, R, K, n, m, perm, gain, pick);
+    for (int64_t g = 0; g < G; g++) used[g] = 0;
+    int applied = 0;
+    for (;;) { /* pick the best remaining pair among untouched groups */
+      int64_t bg1 = -1, bg2 = -1;
+      for (int64_t g1 = 0; g1 < G; g1++) {
+        if (used[g1]) continue;
+        for (int64_t g2 = g1 + 1; g2 < G; g2++) {
+          if (used[g2] || !(gain[g1 * G + g2] > 0.0)) continue;
+          if (bg1 < 0 || gain[g1 * G + g2] > gain[bg1 * G + bg2]) {
+            bg1 = g1;
+            bg2 = g2;
+          }
+        }
+      }
+      if (bg1 < 0) break;
+      const int s = pick[bg1 * G + bg2], a = s / m, b = s % m;
+      const int32_t t = perm[bg1 * m + a];
+      perm[bg1 * m + a] = perm[bg2 * m + b];
+      perm[bg2 * m + b] = t;
+      used[bg1] = used[bg2] = 1;
+      applied++;
+    }
+    if (!applied) break;
+    done++;
+  }
+  free(gain);
+  free(pick);
+  free(used);
+  if (rounds_done) *rounds_done = done;
+  return 0;
+}

@@ -24,7 +24,10 @@
  *              group; 4 fp16 values take 36 bits instead of 64.
  *            - section "Tensor Scores 상에서 구조적인 sparse GEMM": sparse (first,
  *              compressed) operand times dense operand gives a dense result.
- *            - section "Step-2: Weight Pruning": drop the two smallest of each four.
+ *            - section "Step-2: Weight Pruning": drop the two smallest of each four;
+ *              permute the weight's columns first (Fig. 6) so that large values spread
+ *              over the groups and the mask keeps a larger total (83.7 -> 102.9 in the
+ *              figure's example, whose matrix is not given).
  *   [TRANS]  "[论文解读] Accelerated Sparse Neural Training: A Provable and Efficient
  *            Method to Find N:M Transposable Masks" (nubint.ai)
  *            - ABSTRACT and section "提出的方法": a transposable mask makes W and its
@@ -51,6 +54,12 @@
  *   - SR-STE's gradient is G bit for bit where the weight is kept (the decay
  *     term is zero there); where it is pruned it is fl32(fl32(decay*w) + g),
  *     rounded once more to the element type, in the printed backward's order.
+ *   - Channel permutation: the objective is the kept L1 of the N:M mask of W with
+ *     its columns permuted (only group membership matters).  The search, which the
+ *     pages leave open, runs rounds: every pair of groups gets its best single
+ *     column swap (largest kept-L1 gain summed over all rows, first (a, b) on ties);
+ *     positive gains are applied in descending order (ties: smaller group indices),
+ *     each group at most once per round; it stops when a round applies nothing.
  *   - Transposable masks: M x M blocks aligned at multiples of M (R and K must be
  *     multiples of M).  The greedy takes a block's entries by descending exact
  *     magnitude, equal magnitudes in ascending row-major position, and keeps an
@@ -125,6 +134,19 @@ int nmo_tmask_optimal(const void* W, int dt, int64_t R, int64_t K, int n, int m,
 
 /* W where the greedy transposable mask keeps it, +0 elsewhere */
 int nmo_tprune(const void* W, int dt, int64_t R, int64_t K, int n, int m, void* W_out);
+
+/* kept L1 of the N:M mask of W with its columns permuted (perm[i] = column at
+ * position i); -1 for bad arguments */
+double nmo_kept_l1(const void* W, int dt, int64_t R, int64_t K, int n, int m,
+                   const int32_t* perm);
+
+/* best swap gain and choice (a*m + b) for every pair of groups g1 < g2 ((K/m)^2 tables) */
+int nmo_perm_gains(const void* W, int dt, int64_t R, int64_t K, int n, int m,
+                   const int32_t* perm, double* gain, int32_t* pick);
+
+/* rounds of disjoint best swaps, at most max_rounds; perm updated in place */
+int nmo_perm_search(const void* W, int dt, int64_t R, int64_t K, int n, int m, int max_rounds,
+                    int32_t* perm, int* rounds_done);
 
 /* out[i] = in[i] rounded to dt (round to nearest, ties to even; fp32 copies) */
 int nmo_round_from_f32(const float* in, int dt, int64_t count, void* out);
