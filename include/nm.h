@@ -58,6 +58,8 @@
  *   "量化友好的SR-STE稀疏化训练", section "基于直通估计的动态掩码精炼化稀疏(SR-STE)"
  *   (the mask is searched again from the weights at every training step; the
  *   backward adds decay * w to the gradient where the mask prunes w).
+ *   "[리뷰] Accelerating Sparse Deep Neural Networks", section "Step-2: Weight Pruning",
+ *   Fig. 6 (permuting W's columns before the mask keeps a larger total magnitude).
  *   "[论文解读] Accelerated Sparse Neural Training: A Provable and Efficient Method
  *   to Find N:M Transposable Masks", ABSTRACT and section "提出的方法" (one mask per
  *   M x M block with N kept per row and column serves W and its transpose; a
@@ -73,7 +75,7 @@
 extern "C" {
 #endif
 
-#define NM_ABI_VERSION 5
+#define NM_ABI_VERSION 6
 
 typedef enum {
   NM_OK = 0,
@@ -211,6 +213,37 @@ nm_status nm_tprune(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int
  * not overlap W (NM_ERR_ALIAS). */
 nm_status nm_compress_t(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m,
                         nm_layout layout, void* values, uint32_t* meta, nm_stream_t stream);
+
+/* Channel permutation ("Step-2: Weight Pruning", Fig. 6).  For a column permutation perm
+ * (perm[i] = the column of W placed at position i; groups are positions g*m .. g*m+m-1)
+ * the objective is the kept L1 of the N:M mask of W[:, perm]: the sum over rows and
+ * groups of the n largest |w| (NaN counted as the largest).  These calls search for a
+ * better perm by swapping columns between groups.  They take any nm_dtype of W except
+ * NM_I32, need R*K < 2^31, and use a caller-provided device workspace of at least
+ * nm_perm_workspace_bytes(R, K, n, m) bytes (16-byte aligned; contents are scratch). */
+size_t nm_perm_workspace_bytes(int64_t R, int64_t K, int n, int m);
+
+/* One round's evaluation.  perm: DEVICE int32[K], trusted to be a permutation.  For every
+ * pair of groups g1 < g2 (G = K/m), gain[g1*G + g2] receives the largest change of the
+ * kept L1 over the swaps of position a of g1 with position b of g2 (summed over the rows
+ * in fp32), and pick[g1*G + g2] = a*m + b of the first such swap in row-major (a, b)
+ * order; gain and pick are DEVICE arrays of G*G entries whose other entries are left as
+ * they are. */
+nm_status nm_perm_gains(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m,
+                        const int32_t* perm, float* gain, int32_t* pick, void* workspace,
+                        size_t workspace_bytes, nm_stream_t stream);
+
+/* The search: rounds of nm_perm_gains; each round applies the positive gains in
+ * descending order (ties: smaller g1, then smaller g2), skipping a pair when either
+ * group was already changed in that round, and the search stops when a round applies
+ * nothing or after max_rounds rounds.  perm: HOST int32[K], the starting permutation on
+ * entry (it must be one, else NM_ERR_SHAPE) and the result on return; *rounds (if not
+ * NULL) receives the number of rounds that applied a swap.  The call returns when the
+ * search is done (it synchronises `stream`); host scratch of O((K/m)^2) is allocated
+ * for the call's duration. */
+nm_status nm_perm_search(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m,
+                         int max_rounds, int32_t* perm, int* rounds, void* workspace,
+                         size_t workspace_bytes, nm_stream_t stream);
 
 #ifdef __cplusplus
 }

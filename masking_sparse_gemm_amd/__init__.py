@@ -38,12 +38,13 @@ _TORCH_DT = {v: k for k, v in _DT.items()}
 STATUS = ["ok", "null", "shape", "pattern", "dtype", "align", "unsupported", "device", "layout",
           "alias"]
 LAYOUTS = {"rows": 0, "blocked": 1}
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 # every function the C header declares
 EXPORTS = ("nm_abi_version", "nm_status_str", "nm_values_bytes", "nm_meta_bytes",
            "nm_meta_words_per_row", "nm_mask", "nm_compress", "nm_decompress", "nm_spmm",
-           "nm_prune", "nm_srste_grad", "nm_tmask", "nm_tprune", "nm_compress_t")
+           "nm_prune", "nm_srste_grad", "nm_tmask", "nm_tprune", "nm_compress_t",
+           "nm_perm_workspace_bytes", "nm_perm_gains", "nm_perm_search")
 SRSTE_DECAY = 0.0002  # the SR-STE page's default decay
 
 
@@ -83,8 +84,14 @@ def lib() -> ctypes.CDLL:
         L.nm_tmask.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp]
         L.nm_tprune.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp]
         L.nm_compress_t.argtypes = [vp, i32, i64, i64, i32, i32, i32, vp, vp, vp]
+        L.nm_perm_workspace_bytes.argtypes = [i64, i64, i32, i32]
+        L.nm_perm_workspace_bytes.restype = ctypes.c_size_t
+        L.nm_perm_gains.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.nm_perm_search.argtypes = [vp, i32, i64, i64, i32, i32, i32, vp, vp, vp,
+                                     ctypes.c_size_t, vp]
         for f in ("nm_mask", "nm_compress", "nm_decompress", "nm_spmm", "nm_prune",
-                  "nm_srste_grad", "nm_tmask", "nm_tprune", "nm_compress_t"):
+                  "nm_srste_grad", "nm_tmask", "nm_tprune", "nm_compress_t", "nm_perm_gains",
+                  "nm_perm_search"):
             getattr(L, f).restype = i32
         if L.nm_abi_version() != ABI_VERSION:
             raise ImportError(f"{LIB_PATH} has ABI {L.nm_abi_version()}, expected {ABI_VERSION}: "
@@ -295,3 +302,46 @@ def compress_t(W: torch.Tensor, n: int = 2, m: int = 4, layout: str = "rows"):
     _check("nm_compress_t", lib().nm_compress_t(_ptr(W), dt, R, K, n, m, lay, _ptr(values),
                                                 _ptr(meta), _stream(W)))
     return values, meta
+
+
+def _perm_workspace(W: torch.Tensor, n: int, m: int) -> torch.Tensor:
+    R, K = W.shape
+    nbytes = int(lib().nm_perm_workspace_bytes(R, K, n, m))
+    if nbytes == 0 and R * K > 0:
+        _check("nm_perm_workspace_bytes", 2)
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=W.device)
+
+
+def perm_gains(W: torch.Tensor, perm: torch.Tensor, n: int = 2, m: int = 4):
+    """(gain float32 (G, G), pick int32 (G, G)) of the best swap for every pair of column
+    groups g1 < g2 under the permutation perm (int32 (K,) on W's device); other entries 0."""
+    dt = _dense_input(W, "W")
+    R, K = W.shape
+    G = K // m
+    if perm.dtype != torch.int32 or perm.shape != (K,) or perm.device != W.device:
+        raise ValueError("perm must be an int32 (K,) tensor on W's device")
+    gain = torch.zeros((G, G), dtype=torch.float32, device=W.device)
+    pick = torch.zeros((G, G), dtype=torch.int32, device=W.device)
+    ws = _perm_workspace(W, n, m)
+    _check("nm_perm_gains", lib().nm_perm_gains(_ptr(W), dt, R, K, n, m, _ptr(perm.contiguous()),
+                                                _ptr(gain), _ptr(pick), _ptr(ws), ws.numel(),
+                                                _stream(W)))
+    return gain, pick
+
+
+def perm_search(W: torch.Tensor, n: int = 2, m: int = 4, max_rounds: int = 1000, perm=None):
+    """(perm, rounds): a column permutation (CPU int32 (K,)) whose N:M mask keeps at least
+    the kept magnitude of the start (identity by default), by rounds of group swaps."""
+    import numpy as np
+
+    dt = _dense_input(W, "W")
+    R, K = W.shape
+    p = np.arange(K, dtype=np.int32) if perm is None else np.array(perm, dtype=np.int32)
+    if p.shape != (K,):
+        raise ValueError("perm must have K entries")
+    rounds = ctypes.c_int(0)
+    ws = _perm_workspace(W, n, m)
+    _check("nm_perm_search", lib().nm_perm_search(
+        _ptr(W), dt, R, K, n, m, int(max_rounds), p.ctypes.data_as(ctypes.c_void_p),
+        ctypes.byref(rounds), _ptr(ws), ws.numel(), _stream(W)))
+    return torch.from_numpy(p), rounds.value

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libnm.so")
-SOURCES = ["nm_api.hip", "nm_compress.hip", "nm_spmm.hip", "nm_srste.hip", "nm_tmask.hip"]
+SOURCES = ["nm_api.hip", "nm_compress.hip", "nm_spmm.hip", "nm_srste.hip", "nm_tmask.hip", "nm_perm.hip"]
 ARCH = "gfx950"
 
 

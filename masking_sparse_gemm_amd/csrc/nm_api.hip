@@ -5,6 +5,7 @@
 // record of whether the device is a gfx950, filled on first use.
 #include <atomic>
 #include <cstring>
+#include <vector>
 
 #include "../../include/nm.h"
 #include "nm_launch.h"
@@ -279,6 +280,60 @@ nm_status nm_srste_grad(const void* W, const void* G, nm_dtype dt, int64_t R, in
   if ((st = check_device()) != NM_OK) return st;
   return from_hip(nm::launch_srste_grad(W, G, (int)dt, R, K, n, m, decay, G_out,
                                         static_cast<hipStream_t>(stream)));
+}
+
+size_t nm_perm_workspace_bytes(int64_t R, int64_t K, int n, int m) {
+  if (check_pattern(n, m) != NM_OK || check_shape(R, K, m) != NM_OK) return 0;
+  if (R * K >= ((int64_t)1 << 31)) return 0;
+  return nm::perm_workspace_bytes(R, K, m);
+}
+
+namespace {
+nm_status check_perm_args(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m,
+                          const void* workspace, size_t workspace_bytes) {
+  if (!valid_dtype(dt)) return NM_ERR_DTYPE;
+  nm_status st = check_pattern(n, m);
+  if (st != NM_OK) return st;
+  if ((st = check_shape(R, K, m)) != NM_OK) return st;
+  if (R * K >= ((int64_t)1 << 31)) return NM_ERR_SHAPE;  // 32-bit gather indices
+  if (missing(W, R * K) || missing(workspace, R * K)) return NM_ERR_NULL;
+  if (R * K > 0 && workspace_bytes < nm::perm_workspace_bytes(R, K, m)) return NM_ERR_SHAPE;
+  if (!aligned16(W) || !aligned16(workspace)) return NM_ERR_ALIGN;
+  return NM_OK;
+}
+}  // namespace
+
+nm_status nm_perm_gains(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m,
+                        const int32_t* perm, float* gain, int32_t* pick, void* workspace,
+                        size_t workspace_bytes, nm_stream_t stream) {
+  nm_status st = check_perm_args(W, dt, R, K, n, m, workspace, workspace_bytes);
+  if (st != NM_OK) return st;
+  const int64_t G = K / m;
+  if (missing(perm, K) || missing(gain, G * G) || missing(pick, G * G)) return NM_ERR_NULL;
+  if (R * K == 0 || G < 2) return NM_OK;
+  if ((st = check_device()) != NM_OK) return st;
+  return from_hip(nm::launch_perm_gains(W, (int)dt, R, K, n, m, perm, gain, pick, workspace,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+nm_status nm_perm_search(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m,
+                         int max_rounds, int32_t* perm, int* rounds, void* workspace,
+                         size_t workspace_bytes, nm_stream_t stream) {
+  nm_status st = check_perm_args(W, dt, R, K, n, m, workspace, workspace_bytes);
+  if (st != NM_OK) return st;
+  if (missing(perm, K)) return NM_ERR_NULL;
+  if (max_rounds < 0) return NM_ERR_SHAPE;
+  // perm must be a permutation of 0 .. K-1
+  std::vector<uint8_t> seen((size_t)K, 0);
+  for (int64_t i = 0; i < K; ++i) {
+    if (perm[i] < 0 || perm[i] >= K || seen[(size_t)perm[i]]) return NM_ERR_SHAPE;
+    seen[(size_t)perm[i]] = 1;
+  }
+  if (rounds) *rounds = 0;
+  if (R * K == 0 || K / m < 2 || max_rounds == 0) return NM_OK;
+  if ((st = check_device()) != NM_OK) return st;
+  return from_hip(nm::run_perm_search(W, (int)dt, R, K, n, m, max_rounds, perm, rounds,
+                                      workspace, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -29,6 +29,16 @@ hipError_t launch_select_t(const void* W, int elem_bytes, int64_t R, int64_t K, 
 hipError_t launch_tmask(const void* W, int elem_bytes, int64_t R, int64_t K, int n, int m,
                         bool prune, void* out, hipStream_t s);
 
+// Channel permutation (nm_perm.hip): workspace bytes, one round's gains (device perm and
+// outputs), and the whole search (host perm, synchronous on s).
+size_t perm_workspace_bytes(int64_t R, int64_t K, int m);
+hipError_t launch_perm_gains(const void* W, int dt, int64_t R, int64_t K, int n, int m,
+                             const int32_t* perm, float* gain, int32_t* pick, void* workspace,
+                             hipStream_t s);
+hipError_t run_perm_search(const void* W, int dt, int64_t R, int64_t K, int n, int m,
+                           int max_rounds, int32_t* perm_host, int* rounds, void* workspace,
+                           hipStream_t s);
+
 // SR-STE passes (dt in nm_dtype codes); `out` may be W (prune) or G (grad).
 hipError_t launch_prune(const void* W, int dt, int64_t R, int64_t K, int n, int m, void* out,
                         hipStream_t s);

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     L = nm.lib()
     for name in header_functions():
         assert hasattr(L, name), name
-    assert L.nm_abi_version() == nm.ABI_VERSION == 5
+    assert L.nm_abi_version() == nm.ABI_VERSION == 6
 
 
 @needs_lib
@@ -279,6 +279,30 @@ def test_int8_argument_rules():
     assert st(L.nm_tmask(FAKE, I8, 64, 128, 2, 4, FAKE + 0x100000, None)) == "dtype"
     assert st(L.nm_prune(FAKE, I8, 64, 128, 2, 4, FAKE + 0x100000, None)) == "dtype"
     assert st(L.nm_mask(FAKE, I32, 64, 128, 2, 4, FAKE + 0x100000, None)) == "dtype"
+
+
+@needs_lib
+def test_perm_argument_rules():
+    L = nm.lib()
+    st = lambda code: nm.STATUS[code]
+    need = L.nm_perm_workspace_bytes(64, 128, 2, 4)
+    assert need >= 64 * 128 * 4 + 128 * 4 + 2 * 32 * 32 * 4
+    assert L.nm_perm_workspace_bytes(64, 130, 2, 4) == 0
+    gains = lambda **kw: L.nm_perm_gains(kw.get("W", FAKE), kw.get("dt", nm.NM_BF16), 64,
+                                         kw.get("K", 128), 2, 4, FAKE, FAKE, FAKE,
+                                         kw.get("ws", FAKE + 0x100000), kw.get("wsb", need), None)
+    assert st(gains(ws=0)) == "null"
+    assert st(gains(wsb=need - 1)) == "shape"
+    assert st(gains(dt=nm.NM_I32)) == "dtype"
+    assert st(gains(K=126)) == "shape"
+    assert st(gains(W=FAKE + 2)) == "align"
+    perm = (ctypes.c_int32 * 128)(*range(128))
+    perm[5] = 7  # 7 twice: not a permutation
+    assert st(L.nm_perm_search(FAKE, nm.NM_BF16, 64, 128, 2, 4, 10, perm, None, FAKE, need,
+                               None)) == "shape"
+    perm[5] = 5
+    assert st(L.nm_perm_search(FAKE, nm.NM_BF16, 64, 128, 2, 4, -1, perm, None, FAKE, need,
+                               None)) == "shape"
 
 
 @needs_lib
