@@ -19,7 +19,8 @@ in a separate pass after the step, each launch after a cache-clearing fill, and
 reported under "srste" with their HBM roofline; they are not part of `value`.
 So is the transposable-mask path under "transposable": nm_tprune (greedy
 transposable mask applied), nm_compress_t (the compressed transpose) and the
-backward product W^T dY through nm_spmm.
+backward product W^T dY through nm_spmm; and one round of the channel-
+permutation search (nm_perm_gains) under "permutation".
 """
 from __future__ import annotations
 
@@ -39,6 +40,9 @@ sys.path.insert(0, ROOT)
 METRIC = "2:4 spmm effective TFLOP/s + mask/compress GB/s (% of MI355X roofline)"
 METRIC_I8 = "2:4 int8 spmm effective TOP/s + mask/compress GB/s (% of MI355X roofline)"
 PEAK_HBM_GBS = 8000.0
+# fp32 VALU operations: the 157.3 TFLOP/s fp32 vector peak counts an FMA as two flops,
+# i.e. 256 CUs x 128 fp32 lanes per clock x 2.4 GHz = 78.6 T operations per second
+PEAK_VALU_TOPS = 78.64
 # dense matrix-core peaks (TFLOP/s; TOP/s for int8)
 PEAK_MFMA_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3, "i8": 5033.2}
 # workload name -> (synthetic matrices, N:M pattern)
@@ -478,6 +482,45 @@ def main() -> int:
                                  frac_hbm=round(ab / t / 1e9 / PEAK_HBM_GBS, 3))
                 transposable["kernels"][f"{d['name']}.{kind}"] = entry
 
+    # ---- channel permutation: one round of swap-gain evaluation per matrix ----
+    # (compute-bound: pairs of column groups x rows x M^2 swaps, each two max and four adds)
+    permutation = {"kernels": {}}
+    for d in mats:
+        K, G = d["K"], d["K"] // m
+        nbytes = int(L.nm_perm_workspace_bytes(d["R"], K, n, m))
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        pv = torch.arange(K, dtype=torch.int32, device=dev)
+        gain = torch.empty((G, G), dtype=torch.float32, device=dev)
+        pick = torch.empty((G, G), dtype=torch.int32, device=dev)
+
+        def gains_launch(d=d, K=K, ws=ws, pv=pv, gain=gain, pick=pick, nbytes=nbytes):
+            rc = L.nm_perm_gains(d["Wd"].data_ptr(), DT, d["R"], K, n, m, pv.data_ptr(),
+                                 gain.data_ptr(), pick.data_ptr(), ws.data_ptr(), nbytes, sp)
+            if rc != 0:
+                raise RuntimeError(f"nm_perm_gains failed: {nm.status_str(rc)}")
+
+        gains_launch()
+        torch.cuda.synchronize()
+        reps = max(2, min(args.steps, 5))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            gains_launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / reps * 1e-3
+        evals = G * (G - 1) // 2 * d["R"] * m * m
+        ops = evals * 7  # per swap and row: two adds and two max (the kept sums), one add,
+        #                   one subtract (the base) and one accumulate
+        permutation["kernels"][f"{d['name']}.perm_gains"] = {
+            "ms": round(t * 1e3, 3), "pairs": G * (G - 1) // 2, "swap_row_evals": evals,
+            "gops": round(ops / t / 1e9, 1), "frac_alu": round(ops / t / 1e12 / PEAK_VALU_TOPS, 3)}
+        del ws, gain, pick
+    permutation["roofline"] = {
+        "bound": "alu", "unit": "T op/s", "peak": PEAK_VALU_TOPS,
+        "note": "7 fp32 VALU operations per swap and row; peak = the fp32 vector peak "
+                "157.3 TFLOP/s counted as operations (an FMA is two flops): 78.6 T op/s"}
+
     cpu = None
     if not args.no_cpu:
         if float_path:
@@ -511,6 +554,7 @@ def main() -> int:
         "kernels": kernels,
         "srste": srste,
         "transposable": transposable,
+        "permutation": permutation,
         "context": "pages: up to 2x dense math throughput on A100 sparse Tensor Cores (not a target)",
     }
     print(json.dumps(out), flush=True)
