@@ -43,9 +43,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "nm_oracle.c")
 _LIB = os.path.join(_HERE, "libnm_oracle.so")
 
-F32, F16, BF16, I8 = 0, 1, 2, 3
-_DT_CODE = {"f32": F32, "f16": F16, "bf16": BF16, "i8": I8}
-_ELEM = {F32: np.uint32, F16: np.uint16, BF16: np.uint16, I8: np.uint8}
+F32, F16, BF16, I8, FP8 = 0, 1, 2, 3, 4
+_DT_CODE = {"f32": F32, "f16": F16, "bf16": BF16, "i8": I8, "fp8": FP8}
+_ELEM = {F32: np.uint32, F16: np.uint16, BF16: np.uint16, I8: np.uint8, FP8: np.uint8}
 
 
 def build(force: bool = True) -> str:

@@ -66,11 +66,11 @@ static void big_from_shifted(big_t* out, uint64_t value, int shift) {
 
 static uint32_t raw_bits(const void* p, int dt, int64_t i) {
   if (dt == NMO_F32) return ((const uint32_t*)p)[i];
-  if (dt == NMO_I8) return ((const uint8_t*)p)[i];
+  if (dt == NMO_I8 || dt == NMO_FP8) return ((const uint8_t*)p)[i];
   return ((const uint16_t*)p)[i];
 }
 
-static int elem_size(int dt) { return dt == NMO_F32 ? 4 : dt == NMO_I8 ? 1 : 2; }
+static int elem_size(int dt) { return dt == NMO_F32 ? 4 : (dt == NMO_I8 || dt == NMO_FP8) ? 1 : 2; }
 
 /* exact |w| of element i, as an integer multiple of the smallest subnormal (of 1 for int8) */
 static void exact_magnitude(const void* W, int dt, int64_t i, big_t* out) {
@@ -86,6 +86,10 @@ static void exact_magnitude(const void* W, int dt, int64_t i, big_t* out) {
     e = (bits >> 23) & 0xFFu;
     f = bits & 0x7FFFFFu;
     p = 23;
+  } else if (dt == NMO_FP8) { /* OCP E4M3: 1 sign, 4 exponent, 3 fraction bits */
+    e = (bits >> 3) & 0xFu;
+    f = bits & 0x7u;
+    p = 3;
   } else if (dt == NMO_BF16) { /* bf16 = upper half of an fp32 */
     e = (bits >> 7) & 0xFFu;
     f = (bits & 0x7Fu) << 16;
@@ -104,6 +108,18 @@ static void exact_magnitude(const void* W, int dt, int64_t i, big_t* out) {
 double nmo_to_double(const void* p, int dt, int64_t i) {
   uint32_t bits = raw_bits(p, dt, i);
   if (dt == NMO_I8) return (double)(int8_t)(uint8_t)bits;
+  if (dt == NMO_FP8) {
+    /* OCP FP8 E4M3 (bias 7): no infinities; exponent 15 with fraction 7 is NaN */
+    int s8 = (bits >> 7) & 1, e8 = (bits >> 3) & 0xF, f8 = bits & 7;
+    double v8;
+    if (e8 == 0)
+      v8 = ldexp((double)f8, -9);
+    else if (e8 == 15 && f8 == 7)
+      v8 = NAN;
+    else
+      v8 = ldexp((double)(8 + f8), e8 - 10);
+    return s8 ? -v8 : v8;
+  }
   if (dt == NMO_F32) {
     float v;
     memcpy(&v, &bits, 4);
@@ -151,7 +167,8 @@ int64_t nmo_meta_words_per_row(int64_t K, int n, int m) {
 }
 
 static int check_args(int dt, int64_t R, int64_t K, int n, int m) {
-  if (dt != NMO_F32 && dt != NMO_F16 && dt != NMO_BF16 && dt != NMO_I8) return -1;
+  if (dt != NMO_F32 && dt != NMO_F16 && dt != NMO_BF16 && dt != NMO_I8 && dt != NMO_FP8)
+    return -1;
   if (R < 0 || K < 0) return -2;
   if (nmo_meta_bits(m) < 0 || n < 1 || n > m) return -3;
   if (K % m != 0) return -4;
@@ -244,7 +261,7 @@ int nmo_compress(const void* W, int dt, int64_t R, int64_t K, int n, int m, void
         int64_t dst = r * kv + g * n + j;
         if (dt == NMO_F32)
           ((uint32_t*)values)[dst] = ((const uint32_t*)W)[base + kept[j]];
-        else if (dt == NMO_I8)
+        else if (dt == NMO_I8 || dt == NMO_FP8)
           ((uint8_t*)values)[dst] = ((const uint8_t*)W)[base + kept[j]];
         else
           ((uint16_t*)values)[dst] = ((const uint16_t*)W)[base + kept[j]];
@@ -273,7 +290,7 @@ int nmo_decompress(const void* values, const uint32_t* meta, int dt, int64_t R, 
         int64_t src = r * kv + g * n + j;
         if (dt == NMO_F32)
           ((uint32_t*)W_out)[pos] = ((const uint32_t*)values)[src];
-        else if (dt == NMO_I8)
+        else if (dt == NMO_I8 || dt == NMO_FP8)
           ((uint8_t*)W_out)[pos] = ((const uint8_t*)values)[src];
         else
           ((uint16_t*)W_out)[pos] = ((const uint16_t*)values)[src];
@@ -453,7 +470,7 @@ static void zero_elem(void* dst, int dt, int64_t i) {
 int nmo_prune(const void* W, int dt, int64_t R, int64_t K, int n, int m, void* W_out) {
   int rc = check_args(dt, R, K, n, m);
   if (rc) return rc;
-  if (dt == NMO_I8) return -1; /* SR-STE trains floating-point weights */
+  if (dt == NMO_I8 || dt == NMO_FP8) return -1; /* SR-STE trains 16/32-bit weights */
   int kept[16];
   for (int64_t r = 0; r < R; r++) {
     for (int64_t g = 0; g < K / m; g++) {
@@ -476,7 +493,7 @@ int nmo_srste_grad(const void* W, const void* G, int dt, int64_t R, int64_t K, i
                    float decay, void* G_out) {
   int rc = check_args(dt, R, K, n, m);
   if (rc) return rc;
-  if (dt == NMO_I8) return -1;
+  if (dt == NMO_I8 || dt == NMO_FP8) return -1;
   int kept[16];
   for (int64_t r = 0; r < R; r++) {
     for (int64_t g = 0; g < K / m; g++) {
@@ -514,7 +531,7 @@ int nmo_srste_grad(const void* W, const void* G, int dt, int64_t R, int64_t K, i
 static int check_tshape(int dt, int64_t R, int64_t K, int n, int m) {
   int rc = check_args(dt, R, K, n, m);
   if (rc) return rc;
-  if (dt == NMO_I8) return -1; /* transposable masks are built for trained float weights */
+  if (dt == NMO_I8 || dt == NMO_FP8) return -1; /* built for trained 16/32-bit weights */
   if (R % m != 0) return -4;
   return 0;
 }

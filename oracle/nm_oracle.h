@@ -72,7 +72,9 @@
  * passed as raw uint16 bit patterns, int8 as raw bytes.  int8 (the ASDNN review's
  * INT8 sparse Tensor Core type, "Tensor Scores 상에서 구조적인 sparse GEMM") takes |w|
  * as the integer magnitude (|-128| = 128) and is accepted by mask, compress,
- * decompress and the products, whose double sums are then exact integers.  Return value 0 = success, negative = bad args.
+ * decompress and the products, whose double sums are then exact integers.  FP8 (dt 4,
+ * OCP E4M3 bytes) is ranked by its sign-cleared bits like the other floating types
+ * and is accepted by the same four functions.  Return value 0 = success, negative = bad args.
  */
 #ifndef NM_ORACLE_H
 #define NM_ORACLE_H
@@ -86,6 +88,7 @@ extern "C" {
 #define NMO_F16 1
 #define NMO_BF16 2
 #define NMO_I8 3 /* int8 two's complement; products are exact integers */
+#define NMO_FP8 4 /* OCP FP8 E4M3: bias 7, no infinities, S.1111.111 is NaN */
 
 /* metadata bits per kept value, log2(m); -1 if m is not a power of two in [2,16] */
 int nmo_meta_bits(int m);

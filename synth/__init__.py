@@ -78,12 +78,32 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return r.astype(np.uint16)
 
 
+# The 127 non-negative finite OCP FP8 E4M3 values, by code (bias 7, 3 fraction bits).
+_E4M3_CODES = np.arange(127)
+_E4M3_VALUES = np.where(_E4M3_CODES >> 3 == 0, (_E4M3_CODES & 7) * 2.0 ** -9,
+                        (8 + (_E4M3_CODES & 7)) * np.exp2((_E4M3_CODES >> 3) - 10.0))
+
+
+def f32_to_e4m3_bits(x32: np.ndarray) -> np.ndarray:
+    """Nearest E4M3 value (ties to the even code), magnitudes clipped to 448 first."""
+    x = np.asarray(x32, dtype=np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    hi = np.clip(np.searchsorted(_E4M3_VALUES, a), 1, 126)
+    lo = hi - 1
+    dlo, dhi = a - _E4M3_VALUES[lo], _E4M3_VALUES[hi] - a
+    code = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    code = np.where(a >= _E4M3_VALUES[126], 126, code)
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
 def round_to(x64: np.ndarray, dtype: str) -> np.ndarray:
     """float64 -> fp32 (RNE) -> dtype.  Returns float32 for f32, raw uint16 bits for the
     16-bit types, int8 for i8 (nearest integer, clipped)."""
     if dtype == "i8":
         return np.clip(np.rint(x64), -128, 127).astype(np.int8)
     x32 = x64.astype(np.float32)
+    if dtype == "fp8":
+        return f32_to_e4m3_bits(x32)
     if dtype == "f32":
         return x32
     if dtype == "f16":
@@ -104,6 +124,11 @@ def bits_to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
         return np.asarray(a, dtype=np.uint16).view(np.float16).astype(np.float64)
     if dtype == "i8":
         return np.asarray(a).view(np.int8).astype(np.float64)
+    if dtype == "fp8":
+        b = np.asarray(a).view(np.uint8).astype(np.int64)
+        v = _E4M3_VALUES[np.minimum(b & 0x7F, 126)]
+        v = np.where((b & 0x7F) == 0x7F, np.nan, v)
+        return np.where(b & 0x80, -v, v)
     if dtype == "bf16":
         u = np.asarray(a, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
         return u.view(np.float32).astype(np.float64)
@@ -140,7 +165,7 @@ class Dist:
 def generate(dist: Dist, shape: tuple[int, int], dtype: str) -> np.ndarray:
     """Row-major matrix of ``shape``; element (r, c) is draw r*cols + c of ``dist``."""
     n = int(shape[0]) * int(shape[1])
-    out = np.empty(n, dtype={"f32": np.float32, "i8": np.int8}.get(dtype, np.uint16))
+    out = np.empty(n, dtype={"f32": np.float32, "i8": np.int8, "fp8": np.uint8}.get(dtype, np.uint16))
 
     def fill(s: int) -> None:
         c = min(_CHUNK, n - s)
@@ -217,6 +242,11 @@ WORKLOADS = {
                             Dist("normal", 1, 24.0), note="LLaMA-7B MLP up-projection, int8"),
     "llama_down_i8": Workload("llama_down_i8", 4096, 11008, 2048, "i8", Dist("normal", 0, 24.0),
                               Dist("normal", 1, 24.0), note="LLaMA-7B MLP down-projection, int8"),
+    # ... and to OCP FP8 E4M3: weights and activations ~N(0, 1) rounded to E4M3
+    "llama_up_fp8": Workload("llama_up_fp8", 11008, 4096, 2048, "fp8", Dist("normal", 0, 1.0),
+                             Dist("normal", 1, 1.0), note="LLaMA-7B MLP up-projection, fp8"),
+    "llama_down_fp8": Workload("llama_down_fp8", 4096, 11008, 2048, "fp8", Dist("normal", 0, 1.0),
+                               Dist("normal", 1, 1.0), note="LLaMA-7B MLP down-projection, fp8"),
     # N:M sweep: fp16 4096 x 4096 ~Laplace(0, 0.05), activations 4096 x 8192 ~N(0,1)
     "sweep_f16": Workload("sweep_f16", 4096, 4096, 8192, "f16", Dist("laplace", 0, 0.05),
                           Dist("normal", 1), patterns=((1, 2), (2, 4), (4, 8))),
