@@ -39,16 +39,18 @@ sys.path.insert(0, ROOT)
 
 METRIC = "2:4 spmm effective TFLOP/s + mask/compress GB/s (% of MI355X roofline)"
 METRIC_I8 = "2:4 int8 spmm effective TOP/s + mask/compress GB/s (% of MI355X roofline)"
+METRIC_FP8 = "2:4 fp8 spmm effective TFLOP/s + mask/compress GB/s (% of MI355X roofline)"
 PEAK_HBM_GBS = 8000.0
 # fp32 VALU operations: the 157.3 TFLOP/s fp32 vector peak counts an FMA as two flops,
 # i.e. 256 CUs x 128 fp32 lanes per clock x 2.4 GHz = 78.6 T operations per second
 PEAK_VALU_TOPS = 78.64
 # dense matrix-core peaks (TFLOP/s; TOP/s for int8)
-PEAK_MFMA_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3, "i8": 5033.2}
+PEAK_MFMA_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3, "i8": 5033.2, "fp8": 5033.2}
 # workload name -> (synthetic matrices, N:M pattern)
 WORKLOADS = {
     "llama_mlp": (["llama_up", "llama_down"], (2, 4)),
     "llama_mlp_i8": (["llama_up_i8", "llama_down_i8"], (2, 4)),
+    "llama_mlp_fp8": (["llama_up_fp8", "llama_down_fp8"], (2, 4)),
     "bert_ffn": (["bert_ffn"], (2, 4)),
     "resnet_conv3x3": (["resnet_conv3x3"], (2, 4)),
     "sweep_f16_2_4": (["sweep_f16"], (2, 4)),
@@ -62,13 +64,12 @@ def meta_bits(m: int) -> int:
     return {2: 1, 4: 2, 8: 3}[m]
 
 
-def algorithmic_bytes(R, K, T, n, m, s):
-    """Bytes each kernel must move at minimum (one read of inputs, one write of outputs).
-    Y has the input's element size, except int8 (s = 1), whose products are int32."""
+def algorithmic_bytes(R, K, T, n, m, s, ys):
+    """Bytes each kernel must move at minimum (one read of inputs, one write of outputs):
+    elements of s bytes, products of ys bytes (int32 for int8, bf16 for fp8)."""
     e = R * K
     kept = e * n // m
     meta = R * ((K // m * n * meta_bits(m) + 31) // 32) * 4
-    ys = 4 if s == 1 else s
     return {
         "mask": e * s + e,
         "compress": e * s + kept * s + meta,
@@ -209,18 +210,23 @@ def main() -> int:
         w = synth.WORKLOADS[name]
         W, X = w.W(), w.X()
         tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32,
-               "i8": torch.int8}[w.dtype]
-        ydt = torch.int32 if w.dtype == "i8" else tdt
+               "i8": torch.int8, "fp8": torch.float8_e4m3fn}[w.dtype]
+        # int8 products are exact int32; fp8 products are written as bf16
+        ydt = {"i8": torch.int32, "fp8": torch.bfloat16}.get(w.dtype, tdt)
 
         def to_dev(a, tdt=tdt):
             if a.dtype in (np.float32, np.int8):
                 return torch.from_numpy(a).to(dev)
+            if a.dtype == np.uint8:  # fp8 codes
+                return torch.from_numpy(a).to(dev).view(tdt)
             return torch.from_numpy(a.view(np.int16)).view(tdt).to(dev)
 
-        s = {"f32": 4, "i8": 1}.get(w.dtype, 2)
-        G = w.G() if w.dtype != "i8" else W  # the SR-STE gradient (float weights only)
-        d = dict(name=name, R=w.R, K=w.K, T=w.T, dtype=w.dtype, s=s, W=W, X=X, G=G, Wd=to_dev(W),
-                 Xd=to_dev(X), Gd=to_dev(G))
+        s = {"f32": 4, "i8": 1, "fp8": 1}.get(w.dtype, 2)
+        ys = {"i8": 4, "fp8": 2}.get(w.dtype, s)
+        # the SR-STE gradient (16/32-bit float weights only)
+        G = w.G() if w.dtype in ("f32", "f16", "bf16") else W
+        d = dict(name=name, R=w.R, K=w.K, T=w.T, dtype=w.dtype, s=s, ys=ys, W=W, X=X, G=G,
+                 Wd=to_dev(W), Xd=to_dev(X), Gd=to_dev(G))
         vshape, mshape = nm.compressed_shapes(w.R, w.K, n, m, args.layout)
         d["vals"] = torch.empty(vshape, dtype=tdt, device=dev)
         d["meta"] = torch.empty(mshape, dtype=torch.int32, device=dev)
@@ -247,9 +253,10 @@ def main() -> int:
     L = nm.lib()
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
-    DT = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3}[dtype]
-    YDT = 4 if dtype == "i8" else DT  # int8 products are exact int32
-    float_path = dtype != "i8"        # SR-STE and transposable masks train float weights
+    DT = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3, "fp8": 5}[dtype]
+    YDT = {"i8": 4, "fp8": 2}.get(dtype, DT)  # int32 for int8, bf16 for fp8
+    # SR-STE and transposable masks train 16/32-bit float weights
+    float_path = dtype in ("f32", "f16", "bf16")
     LAY = nm.LAYOUTS[args.layout]
     kinds = ["mask", "compress", "decompress", "spmm"]
 
@@ -324,7 +331,7 @@ def main() -> int:
     kernels = {}
     tot = {k: [0.0, 0.0] for k in kinds}  # [seconds per step, algorithmic bytes per step]
     for d in mats:
-        ab = algorithmic_bytes(d["R"], d["K"], d["T"], n, m, d["s"])
+        ab = algorithmic_bytes(d["R"], d["K"], d["T"], n, m, d["s"], d["ys"])
         for kind in kinds:
             t = float(np.mean(per[(d["name"], kind)])) * 1e-3
             entry = {"us": round(t * 1e6, 2), "alg_bytes": ab[kind],
@@ -347,8 +354,8 @@ def main() -> int:
                 "achieved": round(achieved, 1), "peak": peak,
                 "unit": "TOP/s" if dtype == "i8" else "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": None,
-                "alg_bytes_per_launch": sum(algorithmic_bytes(d["R"], d["K"], d["T"], n, m,
-                                                              d["s"])["spmm"] for d in mats) / len(mats),
+                "alg_bytes_per_launch": sum(algorithmic_bytes(d["R"], d["K"], d["T"], n, m, d["s"],
+                                                              d["ys"])["spmm"] for d in mats) / len(mats),
                 "note": "achieved = algorithmic flops 2*R*(K*N/M)*T per launch / mean launch time; "
                         "traffic = profiled HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, "
                         "calibrated on a copy kernel)"}
@@ -372,8 +379,18 @@ def main() -> int:
             if d["dtype"] == "f32":
                 continue
             A, B = d["dec"], d["Xd"]
-            # int8: torch._int_mm (int8 x int8 -> int32), where this PyTorch build has it
-            mm = torch._int_mm if d["dtype"] == "i8" else torch.matmul
+            # int8: torch._int_mm (int8 x int8 -> int32); fp8: torch._scaled_mm (unit scales,
+            # X column-major as it requires, bf16 out), where this PyTorch build has them
+            if d["dtype"] == "i8":
+                mm = torch._int_mm
+            elif d["dtype"] == "fp8":
+                one = torch.ones((), dtype=torch.float32, device=dev)
+                B = B.t().contiguous().t()
+
+                def mm(A, B, one=one):
+                    return torch._scaled_mm(A, B, one, one, out_dtype=torch.bfloat16)
+            else:
+                mm = torch.matmul
             try:
                 for _ in range(3):
                     mm(A, B)
@@ -391,7 +408,8 @@ def main() -> int:
             dense_t = sum(ts)
             dense = {"tflops": round(F_eff / dense_t / 1e12, 1), "us_total": round(dense_t * 1e6, 1),
                      "spmm_speedup": round(dense_t / spmm_t, 3),
-                     "how": ("torch._int_mm" if dtype == "i8" else "torch.matmul (hipBLASLt)")
+                     "how": {"i8": "torch._int_mm", "fp8": "torch._scaled_mm (bf16 out)"}.get(
+                         dtype, "torch.matmul (hipBLASLt)")
                             + " on the decompressed weight, same dtype"}
 
     srste = transposable = None
@@ -530,9 +548,9 @@ def main() -> int:
 
     w0 = mats[0]
     out = {
-        "metric": METRIC if float_path else METRIC_I8,
+        "metric": {"i8": METRIC_I8, "fp8": METRIC_FP8}.get(dtype, METRIC),
         "value": round(value, 2),
-        "unit": "TFLOP/s" if float_path else "TOP/s",
+        "unit": "TOP/s" if dtype == "i8" else "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,

@@ -12,8 +12,8 @@
  * any error nothing is written.  Outputs must not alias inputs.
  *
  * Element types: nm_mask, nm_compress, nm_decompress and nm_spmm take NM_F32, NM_F16,
- * NM_BF16 and NM_I8; the SR-STE and transposable-mask calls take the three floating-point
- * types only.
+ * NM_BF16, NM_I8 and NM_FP8; the SR-STE and transposable-mask calls take the three
+ * 16/32-bit floating-point types only.
  *
  * Dense arrays (row-major, no padding between rows):
  *   W      R x K            elements of `dt`; groups are M consecutive elements along K
@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define NM_ABI_VERSION 6
+#define NM_ABI_VERSION 7
 
 typedef enum {
   NM_OK = 0,
@@ -85,8 +85,8 @@ typedef enum {
   NM_ERR_DTYPE = 4,       /* unknown dtype, y_dt not allowed for dt, or int8 where a
                              floating-point weight is required                       */
   NM_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned                        */
-  NM_ERR_UNSUPPORTED = 6, /* valid arguments this build has no kernel for (int8 in the
-                             blocked layout needs 16 n / m divisible by 4)           */
+  NM_ERR_UNSUPPORTED = 6, /* valid arguments this build has no kernel for (int8 and fp8
+                             in the blocked layout need 16 n / m divisible by 4)     */
   NM_ERR_DEVICE = 7,      /* no usable gfx950 device, or the launch failed           */
   NM_ERR_LAYOUT = 8,      /* unknown layout, or NM_LAYOUT_BLOCKED with K % 64 != 0   */
   NM_ERR_ALIAS = 9        /* an output overlaps an input it may not replace          */
@@ -94,8 +94,11 @@ typedef enum {
 
 /* NM_I8: int8 two's complement ("Tensor Scores 상에서 구조적인 sparse GEMM" lists INT8 among
  * the sparse product's input types), ranked by |w| as an integer (|-128| = 128).
- * NM_I32 is an output type only: the exact int32 result of an int8 product. */
-typedef enum { NM_F32 = 0, NM_F16 = 1, NM_BF16 = 2, NM_I8 = 3, NM_I32 = 4 } nm_dtype;
+ * NM_I32 is an output type only: the exact int32 result of an int8 product.
+ * NM_FP8: OCP FP8 E4M3 bytes (bias 7, no infinities, S.1111.111 is NaN), ranked by the
+ * sign-cleared bits like the other floating types; not one of the pages' types, the
+ * same method one format narrower. */
+typedef enum { NM_F32 = 0, NM_F16 = 1, NM_BF16 = 2, NM_I8 = 3, NM_I32 = 4, NM_FP8 = 5 } nm_dtype;
 
 typedef enum { NM_LAYOUT_ROWS = 0, NM_LAYOUT_BLOCKED = 1 } nm_layout;
 
@@ -152,7 +155,8 @@ nm_status nm_decompress(const void* values, const uint32_t* meta, nm_dtype dt, i
  * R x K matrix that (values, meta) encode, X is K x T, Y is R x T.  Products are
  * accumulated in fp32 and rounded once to y_dt (round to nearest even); y_dt
  * must be dt or NM_F32.  For dt = NM_I8 (W and X int8) y_dt must be NM_I32 and Y is
- * the exact integer product (K < 2^17, else NM_ERR_SHAPE, so no sum can overflow).  The metadata is trusted (well-formedness is the
+ * the exact integer product (K < 2^17, else NM_ERR_SHAPE, so no sum can overflow).
+ * For dt = NM_FP8, y_dt is NM_F32 or NM_BF16 (fp32 accumulation, one rounding).  The metadata is trusted (well-formedness is the
  * caller's responsibility, as for any compressed operand).  Both layouts are
  * accepted; the matrix-core kernels (2:4 and 1:2, 16-bit dt) stream
  * NM_LAYOUT_BLOCKED at full speed and NM_LAYOUT_ROWS at a lower rate. */

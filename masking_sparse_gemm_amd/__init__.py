@@ -30,15 +30,16 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libnm.so")
 
-NM_F32, NM_F16, NM_BF16, NM_I8, NM_I32 = 0, 1, 2, 3, 4
+NM_F32, NM_F16, NM_BF16, NM_I8, NM_I32, NM_FP8 = 0, 1, 2, 3, 4, 5
 _DT = {torch.float32: NM_F32, torch.float16: NM_F16, torch.bfloat16: NM_BF16, torch.int8: NM_I8,
-       torch.int32: NM_I32}
+       torch.int32: NM_I32, torch.float8_e4m3fn: NM_FP8}
+_BYTE = (torch.int8, torch.float8_e4m3fn)  # 1-byte element types (no training-side calls)
 _FLOAT = (torch.float32, torch.float16, torch.bfloat16)
 _TORCH_DT = {v: k for k, v in _DT.items()}
 STATUS = ["ok", "null", "shape", "pattern", "dtype", "align", "unsupported", "device", "layout",
           "alias"]
 LAYOUTS = {"rows": 0, "blocked": 1}
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 # every function the C header declares
 EXPORTS = ("nm_abi_version", "nm_status_str", "nm_values_bytes", "nm_meta_bytes",
@@ -124,8 +125,9 @@ def _dense_input(t: torch.Tensor, name: str, int8: bool = True) -> int:
         raise ValueError(f"{name} must be on a GPU")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous (row-major)")
-    if t.dtype not in _FLOAT and not (int8 and t.dtype == torch.int8):
-        raise ValueError(f"{name} must be float32, float16 or bfloat16" + (" or int8" if int8 else ""))
+    if t.dtype not in _FLOAT and not (int8 and t.dtype in _BYTE):
+        raise ValueError(f"{name} must be float32, float16 or bfloat16" +
+                         (", int8 or float8_e4m3fn" if int8 else ""))
     return _DT[t.dtype]
 
 
@@ -179,9 +181,10 @@ def compress(W: torch.Tensor, n: int = 2, m: int = 4, layout: str = "rows"):
 def _check_compressed(values: torch.Tensor, meta: torch.Tensor, n: int, m: int, K: int,
                       layout: str, rows: int | None) -> tuple[int, int]:
     """(dtype code, R) of a compressed pair, after checking its shapes against K and n:m."""
-    ok = values.dtype in _FLOAT or values.dtype == torch.int8
+    ok = values.dtype in _FLOAT or values.dtype in _BYTE
     if not ok or not values.is_cuda or not values.is_contiguous():
-        raise ValueError("values must be a contiguous float32/float16/bfloat16/int8 GPU tensor")
+        raise ValueError("values must be a contiguous float32/float16/bfloat16/int8/float8 GPU "
+                         "tensor")
     if _layout(layout) == 0:
         R = values.shape[0] if values.dim() == 2 else -1
         if rows is not None and rows != R:
@@ -222,7 +225,8 @@ def spmm(values: torch.Tensor, meta: torch.Tensor, X: torch.Tensor, n: int = 2, 
     dt, R = _check_compressed(values, meta, n, m, K, layout, rows)
     if dt != xdt:
         raise ValueError("values and X must have the same dtype")
-    y_dtype = out_dtype or (torch.int32 if X.dtype == torch.int8 else X.dtype)
+    y_dtype = out_dtype or {torch.int8: torch.int32, torch.float8_e4m3fn: torch.float32}.get(
+        X.dtype, X.dtype)
     if out is None:
         out = torch.empty((R, T), dtype=y_dtype, device=X.device)
     elif out.shape != (R, T) or out.dtype != y_dtype or not out.is_contiguous():

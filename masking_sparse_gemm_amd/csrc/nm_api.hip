@@ -23,16 +23,18 @@ bool missing(const void* p, int64_t count) { return p == nullptr && count > 0; }
 
 int meta_bits_of(int m) { return m == 2 ? 1 : m == 4 ? 2 : m == 8 ? 3 : -1; }
 
-int elem_bytes(nm_dtype dt) { return dt == NM_F32 ? 4 : dt == NM_I8 ? 1 : 2; }
+int elem_bytes(nm_dtype dt) { return dt == NM_F32 ? 4 : (dt == NM_I8 || dt == NM_FP8) ? 1 : 2; }
 
 // Element types of W for the selection and the products; NM_I32 is an output type only.
-bool valid_dtype(int dt) { return dt == NM_F32 || dt == NM_F16 || dt == NM_BF16 || dt == NM_I8; }
+bool valid_dtype(int dt) {
+  return dt == NM_F32 || dt == NM_F16 || dt == NM_BF16 || dt == NM_I8 || dt == NM_FP8;
+}
 bool float_dtype(int dt) { return dt == NM_F32 || dt == NM_F16 || dt == NM_BF16; }
 
 // The blocked layout stores a lane's 16 elements of a block as whole 32-bit words of values:
-// for int8, 16 N / M bytes must divide by 4.
+// for byte elements (int8, fp8), 16 N / M bytes must divide by 4.
 bool blocked_pattern_ok(nm_dtype dt, int n, int m) {
-  return dt != NM_I8 || (16 * n / m) % 4 == 0;
+  return elem_bytes(dt) != 1 || (16 * n / m) % 4 == 0;
 }
 
 nm_status check_pattern(int n, int m) {
@@ -137,7 +139,7 @@ nm_status nm_mask(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m
   if (R * K == 0) return NM_OK;
   if (!aligned16(W) || !aligned16(mask)) return NM_ERR_ALIGN;
   if ((st = check_device()) != NM_OK) return st;
-  return from_hip(nm::launch_select(W, elem_bytes(dt), R, K, n, m, false, nullptr, nullptr, mask,
+  return from_hip(nm::launch_select(W, (int)dt, R, K, n, m, false, nullptr, nullptr, mask,
                                     static_cast<hipStream_t>(stream)));
 }
 
@@ -153,7 +155,7 @@ nm_status nm_compress(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, i
   if (R * K == 0) return NM_OK;
   if (!aligned16(W) || !aligned16(values) || !aligned16(meta)) return NM_ERR_ALIGN;
   if ((st = check_device()) != NM_OK) return st;
-  return from_hip(nm::launch_select(W, elem_bytes(dt), R, K, n, m, layout == NM_LAYOUT_BLOCKED,
+  return from_hip(nm::launch_select(W, (int)dt, R, K, n, m, layout == NM_LAYOUT_BLOCKED,
                                     values, meta, nullptr, static_cast<hipStream_t>(stream)));
 }
 
@@ -180,6 +182,8 @@ nm_status nm_spmm(const void* values, const uint32_t* meta, int64_t R, int64_t K
                   nm_dtype y_dt, nm_stream_t stream) {
   if (dt == NM_I8) {
     if (y_dt != NM_I32) return NM_ERR_DTYPE;
+  } else if (dt == NM_FP8) {
+    if (y_dt != NM_F32 && y_dt != NM_BF16) return NM_ERR_DTYPE;
   } else if (!float_dtype(dt) || !float_dtype(y_dt) || (y_dt != dt && y_dt != NM_F32)) {
     return NM_ERR_DTYPE;
   }

@@ -607,7 +607,7 @@ __global__ void __launch_bounds__(kThreads) group_decompress_kernel(
   const uint32_t* mrow = meta + r * wpr;
   E o[M];
 #pragma unroll
-  for (int i = 0; i < M; ++i) o[i] = 0;
+  for (int i = 0; i < M; ++i) o[i] = E{};
 #pragma unroll
   for (int j = 0; j < N; ++j) {
     const int64_t bit = (g * N + j) * b;
@@ -792,12 +792,15 @@ struct DecompressOp {
 
 }  // namespace
 
-hipError_t launch_select(const void* W, int elem_bytes, int64_t R, int64_t K, int n, int m,
+hipError_t launch_select(const void* W, int dt, int64_t R, int64_t K, int n, int m,
                          bool blocked, void* values, uint32_t* meta, uint8_t* mask,
                          hipStream_t s) {
-  if (elem_bytes == 1)
+  // dt: nm_dtype code (0 fp32, 1 fp16, 2 bf16, 3 int8, 5 fp8)
+  if (dt == 3)
     return dispatch_nm<uint8_t, SelectOp>(n, m, W, R, K, blocked, values, meta, mask, s);
-  if (elem_bytes == 2)
+  if (dt == 5)
+    return dispatch_nm<fp8_t, SelectOp>(n, m, W, R, K, blocked, values, meta, mask, s);
+  if (dt == 1 || dt == 2)
     return dispatch_nm<uint16_t, SelectOp>(n, m, W, R, K, blocked, values, meta, mask, s);
   return dispatch_nm<uint32_t, SelectOp>(n, m, W, R, K, blocked, values, meta, mask, s);
 }

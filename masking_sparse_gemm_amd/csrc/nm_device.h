@@ -25,10 +25,19 @@ namespace nm {
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-// Raw storage of one element: uint8_t for int8, uint16_t for bf16 / fp16, uint32_t for
-// fp32.  key(raw) is the element's magnitude as an unsigned integer.
+// OCP FP8 E4M3 bytes: a type of its own, so that its magnitude key (sign-cleared bits,
+// NaN above 448) is not int8's.
+enum class fp8_t : uint8_t {};
+
+// Raw storage of one element: uint8_t for int8, fp8_t for fp8, uint16_t for bf16 / fp16,
+// uint32_t for fp32.  key(raw) is the element's magnitude as an unsigned integer.
 template <typename E>
 struct Elem;
+template <>
+struct Elem<fp8_t> {
+  static constexpr int kBytes = 1;
+  __host__ __device__ static constexpr uint32_t key(uint32_t raw) { return raw & 0x7Fu; }
+};
 template <>
 struct Elem<uint8_t> {
   static constexpr int kBytes = 1;
@@ -48,6 +57,14 @@ struct Elem<uint32_t> {
   static constexpr int kBytes = 4;
   __host__ __device__ static constexpr uint32_t key(uint32_t raw) { return raw & kKeyMask; }
 };
+
+// OCP FP8 E4M3 byte -> fp32 (exact): bias 7, subnormals f * 2^-9, S.1111.111 is NaN.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, f = b & 7u;
+  float v = e == 0 ? (float)f * 0x1p-9f : __builtin_ldexpf((float)(8u + f), (int)e - 10);
+  v = (e == 15u && f == 7u) ? __builtin_nanf("") : v;
+  return (b & 0x80u) ? -v : v;
+}
 
 constexpr int meta_bits(int m) { return m == 2 ? 1 : m == 4 ? 2 : m == 8 ? 3 : m == 16 ? 4 : 0; }
 

@@ -8,7 +8,8 @@ namespace nm {
 // `blocked` selects NM_LAYOUT_BLOCKED for the compressed pair (K % 64 == 0 checked).
 
 // Mask and/or compress: mask may be null (compress only); values/meta may be null (mask only).
-hipError_t launch_select(const void* W, int elem_bytes, int64_t R, int64_t K, int n, int m,
+// dt is the nm_dtype code of W (its magnitude key depends on it, not only on its size).
+hipError_t launch_select(const void* W, int dt, int64_t R, int64_t K, int n, int m,
                          bool blocked, void* values, uint32_t* meta, uint8_t* mask,
                          hipStream_t s);
 

@@ -37,7 +37,7 @@ constexpr int kThreads = 256;
 constexpr int kPB = 16;        // groups per block side: a workgroup takes 16 x 16 pairs
 constexpr int kRowChunk = 32;  // rows staged in LDS at a time
 
-enum { kF32 = 0, kF16 = 1, kBF16 = 2, kI8 = 3 };
+enum { kF32 = 0, kF16 = 1, kBF16 = 2, kI8 = 3, kFP8 = 5 };
 
 template <int DT>
 __device__ __forceinline__ float magnitude(const void* W, int64_t i) {
@@ -48,6 +48,8 @@ __device__ __forceinline__ float magnitude(const void* W, int64_t i) {
     x = fabsf(__uint_as_float((uint32_t) static_cast<const uint16_t*>(W)[i] << 16));
   } else if constexpr (DT == kF16) {
     x = fabsf((float)__builtin_bit_cast(_Float16, static_cast<const uint16_t*>(W)[i]));
+  } else if constexpr (DT == kFP8) {
+    x = fabsf(e4m3_to_f32(static_cast<const uint8_t*>(W)[i]));
   } else {
     x = fabsf((float) static_cast<const int8_t*>(W)[i]);
   }
@@ -183,6 +185,7 @@ hipError_t launch_permute(const void* W, int dt, int64_t R, int64_t K, const int
     case kF32: return run_permute<kF32>(W, R, K, perm, Wp, s);
     case kF16: return run_permute<kF16>(W, R, K, perm, Wp, s);
     case kBF16: return run_permute<kBF16>(W, R, K, perm, Wp, s);
+    case kFP8: return run_permute<kFP8>(W, R, K, perm, Wp, s);
     default: return run_permute<kI8>(W, R, K, perm, Wp, s);
   }
 }

@@ -50,7 +50,7 @@ typedef _Float16 f16x16_t __attribute__((ext_vector_type(16)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 
-enum { kF32 = 0, kF16 = 1, kBF16 = 2, kI8 = 3, kI32 = 4 };
+enum { kF32 = 0, kF16 = 1, kBF16 = 2, kI8 = 3, kI32 = 4, kFP8 = 5 };
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 __device__ __forceinline__ float f16_to_f32(uint32_t h) {
@@ -66,7 +66,8 @@ __device__ __forceinline__ uint32_t f32_to_f16(float x) {  // hardware conversio
 }
 template <int DT>
 __device__ __forceinline__ float load_as_f32(const void* p, int64_t i) {
-  if constexpr (DT == kF32) return static_cast<const float*>(p)[i];
+  if constexpr (DT == kFP8) return e4m3_to_f32(static_cast<const uint8_t*>(p)[i]);
+  else if constexpr (DT == kF32) return static_cast<const float*>(p)[i];
   else if constexpr (DT == kBF16) return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
   else return f16_to_f32(static_cast<const uint16_t*>(p)[i]);
 }
@@ -1102,7 +1103,7 @@ typedef int int4v_t __attribute__((ext_vector_type(4)));
 typedef int int2v_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) int2v_t lds_int2v_t;
 
-template <int YT, int BM, int BN, int CWAVES_M, int CWAVES_N, int PWAVES, int STAGES>
+template <bool kFp8, int YT, int BM, int BN, int CWAVES_M, int CWAVES_N, int PWAVES, int STAGES>
 __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
     smfmac_i8_ws_spmm_kernel(const uint8_t* __restrict__ values, const uint32_t* __restrict__ meta,
                              const uint8_t* __restrict__ X, void* __restrict__ Y, int R, int K,
@@ -1206,11 +1207,12 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
         b_off[h][f][p] = (uint32_t)(r * BN + 16 * (chunk ^ xsw_i8(r)) + 8 * (i16 & 1));
       }
 
-  int16v_t acc[4][2];
+  using AccV = std::conditional_t<kFp8, float16v_t, int16v_t>;
+  AccV acc[4][2];
 #pragma unroll
   for (int fm = 0; fm < 4; ++fm)
 #pragma unroll
-    for (int f = 0; f < 2; ++f) acc[fm][f] = int16v_t{};
+    for (int f = 0; f < 2; ++f) acc[fm][f] = AccV{};
 
   // Fragments of one half step (64 of K): 4 A fragments with their index words and 2 B
   // fragments.  The next half step's fragments are read while this one's 8 smfmac run.
@@ -1242,8 +1244,12 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
     for (int fm = 0; fm < 4; ++fm)
 #pragma unroll
       for (int f = 0; f < 2; ++f)
-        acc[fm][f] = __builtin_amdgcn_smfmac_i32_32x32x64_i8(F.a[fm], F.b[f], acc[fm][f],
-                                                             F.ix[fm], 0, 0);
+        if constexpr (kFp8)
+          acc[fm][f] = __builtin_amdgcn_smfmac_f32_32x32x64_fp8_fp8(F.a[fm], F.b[f], acc[fm][f],
+                                                                    F.ix[fm], 0, 0);
+        else
+          acc[fm][f] = __builtin_amdgcn_smfmac_i32_32x32x64_i8(F.a[fm], F.b[f], acc[fm][f],
+                                                               F.ix[fm], 0, 0);
   };
 
   asm volatile("s_barrier" ::: "memory");  // steps 0 and 1 landed
@@ -1261,17 +1267,18 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
   }
   asm volatile("s_barrier\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
   static_assert(TL::kConsumers * kEpilogueBytes <= kStages * TL::kStageBytes, "epilogue LDS");
-  store_block_128x64<YT, int16v_t>(acc, smem + wave * kEpilogueBytes, Y, m0 + wm * TL::kWM,
+  store_block_128x64<YT, AccV>(acc, smem + wave * kEpilogueBytes, Y, m0 + wm * TL::kWM,
                                    t0 + wn * TL::kWN, R, T, lane);
 }
 
 int xcd_count();
 
-hipError_t run_smfmac_i8(const void* values, const uint32_t* meta, int64_t R, int64_t K,
-                         const void* X, int64_t T, void* Y, hipStream_t s) {
+template <bool kFp8, int YT>
+hipError_t run_smfmac_8bit(const void* values, const uint32_t* meta, int64_t R, int64_t K,
+                           const void* X, int64_t T, void* Y, hipStream_t s) {
   constexpr int BM = 256, BN = 128, ST = 4;
   using TL = WsI8Tile<BM, BN, 2, 2, 4, ST>;
-  auto kernel = smfmac_i8_ws_spmm_kernel<kI32, BM, BN, 2, 2, 4, ST>;
+  auto kernel = smfmac_i8_ws_spmm_kernel<kFp8, YT, BM, BN, 2, 2, 4, ST>;
   const size_t lds = (size_t)ST * TL::kStageBytes;
   static const hipError_t attr =
       hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
@@ -1955,8 +1962,17 @@ hipError_t launch_spmm(const void* values, const uint32_t* meta, int64_t R, int6
     // T a multiple of 16 (16-byte X loads), 32-bit byte offsets
     if (pat24 && blocked && K % kI8KStep == 0 && T % 16 == 0 && R < (1 << 30) &&
         T < (1 << 30) && K < (1 << 30))
-      return run_smfmac_i8(values, meta, R, K, X, T, Y, s);
+      return run_smfmac_8bit<false, kI32>(values, meta, R, K, X, T, Y, s);
     return run_generic_layout<kI8, kI32>(values, meta, R, K, n, m, blocked, X, T, Y, s);
+  }
+  if (dt == kFP8) {  // the same kernel on the fp8 instruction, fp32 accumulation
+    const bool yf32 = y_dt == kF32;
+    if (pat24 && blocked && K % kI8KStep == 0 && T % 16 == 0 && R < (1 << 30) &&
+        T < (1 << 30) && K < (1 << 30))
+      return yf32 ? run_smfmac_8bit<true, kF32>(values, meta, R, K, X, T, Y, s)
+                  : run_smfmac_8bit<true, kBF16>(values, meta, R, K, X, T, Y, s);
+    return yf32 ? run_generic_layout<kFP8, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s)
+                : run_generic_layout<kFP8, kBF16>(values, meta, R, K, n, m, blocked, X, T, Y, s);
   }
   if (dt == kF32)
     return run_generic_layout<kF32, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s);

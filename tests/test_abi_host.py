@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     L = nm.lib()
     for name in header_functions():
         assert hasattr(L, name), name
-    assert L.nm_abi_version() == nm.ABI_VERSION == 6
+    assert L.nm_abi_version() == nm.ABI_VERSION == 7
 
 
 @needs_lib
@@ -92,7 +92,7 @@ FAKE = 0x10000  # aligned, never dereferenced: validation fails before any devic
 @pytest.mark.parametrize("case,expect", [
     (dict(W=0), "null"),
     (dict(out=0), "null"),
-    (dict(dt=5), "dtype"),
+    (dict(dt=6), "dtype"),
     (dict(n=3, m=3), "pattern"),
     (dict(n=0), "pattern"),
     (dict(n=5), "pattern"),
@@ -279,6 +279,26 @@ def test_int8_argument_rules():
     assert st(L.nm_tmask(FAKE, I8, 64, 128, 2, 4, FAKE + 0x100000, None)) == "dtype"
     assert st(L.nm_prune(FAKE, I8, 64, 128, 2, 4, FAKE + 0x100000, None)) == "dtype"
     assert st(L.nm_mask(FAKE, I32, 64, 128, 2, 4, FAKE + 0x100000, None)) == "dtype"
+
+
+@needs_lib
+def test_fp8_argument_rules():
+    L = nm.lib()
+    F8, ROWS, BLOCKED = nm.NM_FP8, 0, 1
+    st = lambda code: nm.STATUS[code]
+    assert L.nm_values_bytes(64, 128, 2, 4, F8, ROWS) == 64 * 64
+    assert L.nm_values_bytes(64, 128, 1, 8, F8, BLOCKED) == 0
+    assert L.nm_values_bytes(64, 128, 4, 8, F8, BLOCKED) == 64 * 64
+    spmm = lambda ydt, layout=ROWS, n=2, m=4: L.nm_spmm(
+        FAKE, FAKE, 64, 128, n, m, layout, FAKE, 32, F8, FAKE + 0x100000, ydt, None)
+    assert st(spmm(F8)) == "dtype"            # fp8 products come out in fp32 or bf16
+    assert st(spmm(nm.NM_F16)) == "dtype"
+    assert st(spmm(nm.NM_I32)) == "dtype"
+    assert st(spmm(nm.NM_F32, layout=BLOCKED, n=3, m=8)) == "unsupported"
+    assert st(L.nm_compress(FAKE, F8, 64, 128, 1, 8, BLOCKED, FAKE, FAKE, None)) == "unsupported"
+    for call in (L.nm_tmask, L.nm_prune, L.nm_tprune):
+        assert st(call(FAKE, F8, 64, 128, 2, 4, FAKE + 0x100000, None)) == "dtype"
+    assert st(L.nm_mask(FAKE, F8, 64, 130, 2, 4, FAKE + 0x100000, None)) == "shape"
 
 
 @needs_lib
