@@ -74,8 +74,16 @@ struct UnitSelection {
       uint32_t key[M];
 #pragma unroll
       for (int i = 0; i < M; ++i) key[i] = Elem<E>::key(word_elem<E>(w, g * M + i));
-      keep[g] = keep_bits<N, M>(key);
-      kept_positions<N>(keep[g], pos[g]);
+      if constexpr (fast24<E, N, M>()) {
+        int p0, p1;
+        top2_of_4(key[0], key[1], key[2], key[3], p0, p1);
+        pos[g][0] = p0;
+        pos[g][1] = p1;
+        keep[g] = (1u << p0) | (1u << p1);
+      } else {
+        keep[g] = keep_bits<N, M>(key);
+        kept_positions<N>(keep[g], pos[g]);
+      }
     }
   }
   // this unit's metadata: S::kGroups * N fields of b bits, first field in the low bits
@@ -156,13 +164,17 @@ __global__ void __launch_bounds__(kThreads) flat_select_kernel(const uint32_t* _
         uint32_t vw[kValWords];
 #pragma unroll
         for (int i = 0; i < kValWords; ++i) vw[i] = 0;
+        if constexpr (fast24<E, N, M>()) {
+          pack_kept24<E, S::kGroups>(w, sel.pos, vw);
+        } else {
 #pragma unroll
-        for (int g = 0; g < S::kGroups; ++g)
+          for (int g = 0; g < S::kGroups; ++g)
 #pragma unroll
-          for (int j = 0; j < N; ++j) {
-            const uint32_t v = group_elem_at<E, M>(w, g, sel.pos[g][j]);
-            put_elem<E>(vw, g * N + j, v);  // value index inside the unit
-          }
+            for (int j = 0; j < N; ++j) {
+              const uint32_t v = group_elem_at<E, M>(w, g, sel.pos[g][j]);
+              put_elem<E>(vw, g * N + j, v);  // value index inside the unit
+            }
+        }
         store_words<kValWords>(values + u * kValWords, vw);
       }
       const uint64_t bits = live ? sel.meta_bits_of_unit() : 0u;
@@ -293,18 +305,31 @@ __device__ __forceinline__ void blocked_emit(const uint32_t (&w)[LaneShape<E, N,
 #pragma unroll
   for (int i = 0; i < L::kValWords; ++i) vw[i] = 0;
   uint64_t bits = 0;
+  if constexpr (fast24<E, N, M>()) {
+    int pos[L::kGroups][2];
 #pragma unroll
-  for (int gi = 0; gi < L::kGroups; ++gi) {
-    uint32_t key[M];
+    for (int gi = 0; gi < L::kGroups; ++gi) {
+      uint32_t key[4];
 #pragma unroll
-    for (int i = 0; i < M; ++i) key[i] = Elem<E>::key(word_elem<E>(w, gi * M + i));
-    int pos[N];
-    kept_positions<N>(keep_bits<N, M>(key), pos);
+      for (int i = 0; i < 4; ++i) key[i] = Elem<E>::key(word_elem<E>(w, gi * 4 + i));
+      top2_of_4(key[0], key[1], key[2], key[3], pos[gi][0], pos[gi][1]);
+      bits |= (uint64_t)(pos[gi][0] | (pos[gi][1] << 2)) << (4 * gi);
+    }
+    pack_kept24<E, L::kGroups>(w, pos, vw);
+  } else {
 #pragma unroll
-    for (int j = 0; j < N; ++j) {
-      const int k = gi * N + j;
-      put_elem<E>(vw, k, group_elem_at<E, M>(w, gi, pos[j]));
-      bits |= (uint64_t)pos[j] << (k * b);
+    for (int gi = 0; gi < L::kGroups; ++gi) {
+      uint32_t key[M];
+#pragma unroll
+      for (int i = 0; i < M; ++i) key[i] = Elem<E>::key(word_elem<E>(w, gi * M + i));
+      int pos[N];
+      kept_positions<N>(keep_bits<N, M>(key), pos);
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        const int k = gi * N + j;
+        put_elem<E>(vw, k, group_elem_at<E, M>(w, gi, pos[j]));
+        bits |= (uint64_t)pos[j] << (k * b);
+      }
     }
   }
   if (!live) bits = 0;  // padding rows: zero values (w = 0) and zero metadata
@@ -338,15 +363,24 @@ __global__ void __launch_bounds__(kThreads) blocked_select_kernel(const uint32_t
                                                                   uint32_t* __restrict__ meta) {
   using L = LaneShape<E, N, M>;
   __shared__ uint32_t lds_bits[kThreads / 64][L::kShuffle ? 1 : L::kBlockMetaWords];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar math
   const int64_t blk = (int64_t)blockIdx.x * (kThreads / 64) + wave;
   if (blk >= blocks) return;  // the whole wave
   const int64_t steps = K / 64;
-  const int64_t row = 16 * (blk / steps) + (lane >> 2);
+  int64_t rb, st;  // row block and step of this block
+  if (blocks <= 0xFFFFFFFFll) {  // 32-bit division where it fits (every practical size)
+    rb = (uint32_t)blk / (uint32_t)steps;
+    st = (uint32_t)blk - (uint32_t)rb * (uint32_t)steps;
+  } else {
+    rb = blk / steps;
+    st = blk % steps;
+  }
+  const int64_t row = 16 * rb + (lane >> 2);
   const bool live = row < R;
   uint32_t w[L::kWords];
   if (live) {
-    load_words<L::kWords>(W + (row * K + 64 * (blk % steps) + 16 * (lane & 3)) * sizeof(E) / 4, w);
+    load_words<L::kWords>(W + (row * K + 64 * st + 16 * (lane & 3)) * sizeof(E) / 4, w);
   } else {
 #pragma unroll
     for (int i = 0; i < L::kWords; ++i) w[i] = 0;
@@ -378,9 +412,10 @@ __global__ void __launch_bounds__(kThreads) blocked_select_t_kernel(
   // Consecutive workgroups take consecutive steps of the same four column groups, so
   // each column group's blocks are written front to back.  (Measured: this beats
   // orders that read the rows of W front to back, which scatter the block writes.)
-  const int64_t wave_steps = (steps + kStepsPerWave - 1) / kStepsPerWave;
-  const int64_t s0 = ((int64_t)blockIdx.x % wave_steps) * kStepsPerWave;
-  const int64_t g = ((int64_t)blockIdx.x / wave_steps) * (kThreads / 64) + wave;
+  // (blockIdx.x < 2^32, and wave_steps <= blocks fits 32 bits whenever the grid does)
+  const uint32_t wave_steps = (uint32_t)((steps + kStepsPerWave - 1) / kStepsPerWave);
+  const int64_t s0 = (int64_t)(blockIdx.x % wave_steps) * kStepsPerWave;
+  const int64_t g = (int64_t)(blockIdx.x / wave_steps) * (kThreads / 64) + wave;
   if (g >= groups || s0 >= steps) return;  // the whole wave
   const int64_t c0 = 16 * g;
   const bool vec_ok = (K * (int64_t)sizeof(E)) % 16 == 0;
@@ -486,11 +521,20 @@ __global__ void __launch_bounds__(kThreads) blocked_decompress_kernel(
     int64_t blocks, uint32_t* __restrict__ out) {
   using L = LaneShape<E, N, M>;
   constexpr int b = meta_bits(M);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar math
   const int64_t blk = (int64_t)blockIdx.x * (kThreads / 64) + wave;
   if (blk >= blocks) return;
   const int64_t steps = K / 64;
-  const int64_t row = 16 * (blk / steps) + (lane >> 2);
+  int64_t rb, st;  // row block and step of this block
+  if (blocks <= 0xFFFFFFFFll) {
+    rb = (uint32_t)blk / (uint32_t)steps;
+    st = (uint32_t)blk - (uint32_t)rb * (uint32_t)steps;
+  } else {
+    rb = blk / steps;
+    st = blk % steps;
+  }
+  const int64_t row = 16 * rb + (lane >> 2);
   if (row >= R) return;  // padding rows have no output
   const uint32_t* vsrc = values + blk * (64 * L::kValWords) + lane * L::kValWords;
   uint32_t vw[L::kValWords];
@@ -527,7 +571,7 @@ __global__ void __launch_bounds__(kThreads) blocked_decompress_kernel(
       }
     }
   }
-  uint32_t* dst = out + (row * K + 64 * (blk % steps) + 16 * (lane & 3)) * sizeof(E) / 4;
+  uint32_t* dst = out + (row * K + 64 * st + 16 * (lane & 3)) * sizeof(E) / 4;
 #pragma unroll
   for (int i = 0; i < L::kWords / 4; ++i)
     __builtin_nontemporal_store(u32x4_t{ow[4 * i], ow[4 * i + 1], ow[4 * i + 2], ow[4 * i + 3]},

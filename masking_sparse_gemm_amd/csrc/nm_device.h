@@ -42,7 +42,8 @@ template <>
 struct Elem<uint8_t> {
   static constexpr int kBytes = 1;
   __host__ __device__ static constexpr uint32_t key(uint32_t raw) {
-    return (raw & 0x80u) ? 256u - (raw & 0xFFu) : (raw & 0xFFu);
+    const int x = (int)((raw & 0xFFu) ^ 0x80u) - 128;  // the signed value
+    return (uint32_t)(x < 0 ? -x : x);
   }
 };
 template <>
@@ -87,6 +88,45 @@ __device__ __forceinline__ uint32_t keep_bits(const uint32_t (&key)[M]) {
 #pragma unroll
   for (int i = 0; i < M; ++i) keep |= (beaten[i] < N ? 1u : 0u) << i;
   return keep;
+}
+
+// 2:4 for elements of at most 16 bits.  The composite key 4 |w| + (3 - i) is distinct
+// within a group and orders as the rule above (larger magnitude first, then the lower
+// index), so the kept pair is the top two of four distinct integers: eight min / max
+// operations instead of six pairwise counts.  Returns the kept positions p0 < p1.
+__device__ __forceinline__ void top2_of_4(uint32_t k0, uint32_t k1, uint32_t k2, uint32_t k3,
+                                          int& p0, int& p1) {
+  const uint32_t c0 = (k0 << 2) | 3u, c1 = (k1 << 2) | 2u, c2 = (k2 << 2) | 1u, c3 = k3 << 2;
+  const uint32_t a = max(c0, c1), b = min(c0, c1), c = max(c2, c3), d = min(c2, c3);
+  const uint32_t t1 = max(a, c), t2 = max(min(a, c), max(b, d));
+  const uint32_t l1 = t1 & 3u, l2 = t2 & 3u;
+  p0 = (int)(3u - max(l1, l2));
+  p1 = (int)(3u - min(l1, l2));
+}
+
+template <typename E, int N, int M>
+constexpr bool fast24() { return N == 2 && M == 4 && sizeof(E) <= 2; }
+
+// Kept values of consecutive 2:4 groups gathered with byte permutes (fast24 types):
+// 16-bit elements, group g in words 2g, 2g+1 -> word g; 8-bit elements, group g in word
+// g -> half g % 2 of word g / 2.
+template <typename E, int G>
+__device__ __forceinline__ void pack_kept24(const uint32_t* w, const int (&p)[G][2], uint32_t* vw) {
+  if constexpr (sizeof(E) == 2) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const uint32_t sel = (uint32_t)p[g][0] * 0x0202u + (uint32_t)p[g][1] * 0x02020000u + 0x01000100u;
+      vw[g] = __builtin_amdgcn_perm(w[2 * g + 1], w[2 * g], sel);
+    }
+  } else {
+    static_assert(G % 2 == 0, "8-bit groups pair up into words");
+#pragma unroll
+    for (int g = 0; g < G; g += 2) {
+      const uint32_t sel = (uint32_t)p[g][0] | ((uint32_t)p[g][1] << 8) |
+                           ((uint32_t)p[g + 1][0] + 4u) << 16 | ((uint32_t)p[g + 1][1] + 4u) << 24;
+      vw[g / 2] = __builtin_amdgcn_perm(w[g + 1], w[g], sel);
+    }
+  }
 }
 
 // Positions of the N set bits of `keep`, ascending.
