@@ -17,6 +17,8 @@
 // j of group g in b = log2(M) bits at bit f*b of the row, least significant first.
 // The blocked layout stores the same values and bits in blocks of 16 rows x 64
 // columns (include/nm.h); its kernels take one block per wave.
+#include <utility>
+
 #include "nm_device.h"
 #include "nm_launch.h"
 
@@ -515,6 +517,41 @@ __global__ void __launch_bounds__(kThreads) meta_word_t_kernel(const E* __restri
   meta[k * wpr + w] = word;
 }
 
+// Store i of lane q (of a quad holding S 16-byte chunks each, in lane order) writes chunk
+// 4i + q, which lives in lane (4i + q) / S as its chunk (4i + q) % S: fetched with a quad
+// permute (one per source chunk) and a select.
+template <int S, int I>
+__device__ __forceinline__ void store_row_chunk(const uint32_t (&ow)[4 * S], int q, uint32_t* dst) {
+  uint32_t v[4];
+  if constexpr (S == 1) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = ow[j];
+  } else {
+    constexpr int kPerm = ((4 * I + 0) / S) | ((4 * I + 1) / S) << 2 | ((4 * I + 2) / S) << 4 |
+                          ((4 * I + 3) / S) << 6;
+    const int h = (4 * I + q) % S;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t pick = 0;
+#pragma unroll
+      for (int c = 0; c < S; ++c) {
+        const uint32_t moved =
+            (uint32_t)__builtin_amdgcn_mov_dpp((int)ow[4 * c + j], kPerm, 0xF, 0xF, false);
+        pick = (h == c) ? moved : pick;
+      }
+      v[j] = pick;
+    }
+  }
+  __builtin_nontemporal_store(u32x4_t{v[0], v[1], v[2], v[3]},
+                              reinterpret_cast<u32x4_t*>(dst + 16 * I));
+}
+
+template <int S, int... I>
+__device__ __forceinline__ void store_row_chunks(const uint32_t (&ow)[4 * S], int q, uint32_t* dst,
+                                                 std::integer_sequence<int, I...>) {
+  (store_row_chunk<S, I>(ow, q, dst), ...);
+}
+
 template <typename E, int N, int M>
 __global__ void __launch_bounds__(kThreads) blocked_decompress_kernel(
     const uint32_t* __restrict__ values, const uint32_t* __restrict__ meta, int64_t R, int64_t K,
@@ -571,11 +608,14 @@ __global__ void __launch_bounds__(kThreads) blocked_decompress_kernel(
       }
     }
   }
-  uint32_t* dst = out + (row * K + 64 * st + 16 * (lane & 3)) * sizeof(E) / 4;
-#pragma unroll
-  for (int i = 0; i < L::kWords / 4; ++i)
-    __builtin_nontemporal_store(u32x4_t{ow[4 * i], ow[4 * i + 1], ow[4 * i + 2], ow[4 * i + 3]},
-                                reinterpret_cast<u32x4_t*>(dst) + i);
+  // The 4 lanes of a row hold its 16-byte chunks in lane order, kWords / 4 chunks each.
+  // Stored as they are, every store instruction would write one chunk in kWords / 4 of
+  // each row segment, and such scattered 16-byte pieces cost extra HBM write traffic
+  // (measured: 15% over the output's bytes for bf16).  Regroup across the quad first, so
+  // that store i of lane q writes chunk 4i + q: 64 contiguous bytes per row and store.
+  const int q = lane & 3;
+  uint32_t* dst = out + (row * K + 64 * st) * sizeof(E) / 4 + 4 * q;
+  store_row_chunks<L::kWords / 4>(ow, q, dst, std::make_integer_sequence<int, L::kWords / 4>{});
 }
 
 // ---------------------------------------------------------------------------
