@@ -14,10 +14,12 @@
 // non-temporal vector accesses.  Each entry gets a composite key, its
 // magnitude (sign-cleared bits: NaN > Inf > finite, as for the row mask) above its
 // reversed position inside the block, so that a descending order of keys is the
-// greedy's order with equal magnitudes in ascending row-major position.  A bitonic
-// network sorts the M^2 keys in registers (all indices compile-time), then one pass
+// greedy's order with equal magnitudes in ascending row-major position.  An odd-even
+// merge network sorts the M^2 keys in registers (all indices compile-time), then one pass
 // over the sorted keys applies the row and column caps, with the M row counts and M
 // column counts held as 4-bit fields of two registers.
+#include <utility>
+
 #include "nm_device.h"
 #include "nm_launch.h"
 
@@ -89,32 +91,57 @@ __device__ __forceinline__ void store_row(E* p, const uint32_t (&v)[M]) {
   }
 }
 
-// Sort a[0..L) into descending order (bitonic network, L a power of two).
-template <typename T, int L>
-__host__ __device__ __forceinline__ void sort_descending(T (&a)[L]) {
-#pragma unroll
-  for (int k = 2; k <= L; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-#pragma unroll
-      for (int i = 0; i < L; ++i) {
-        const int l = i ^ j;
-        if (l > i) {
-          const T x = a[i], y = a[l];
-          const T hi = x > y ? x : y, lo = x > y ? y : x;
-          // runs with (i & k) == 0 end descending, the others ascending; the last
-          // merge (k == L) makes the whole array descending
-          if ((i & k) == 0) {
-            a[i] = hi;
-            a[l] = lo;
-          } else {
-            a[i] = lo;
-            a[l] = hi;
-          }
-        }
-      }
+// Batcher's odd-even merge sorting network on L = 2^k inputs, as a list of comparator
+// pairs (lo, hi) built at compile time: 5 / 63 / 543 comparators for L = 4 / 16 / 64,
+// against 6 / 80 / 672 for the bitonic network.
+template <int L>
+struct SortNet {
+  int n = 0;
+  int lo[L * L / 2 + 8] = {};
+  int hi[L * L / 2 + 8] = {};
+  constexpr void merge(int base, int m, int r) {
+    const int step = 2 * r;
+    if (step < m) {
+      merge(base, m, step);
+      merge(base + r, m, step);
+      for (int i = base + r; i < base + m - r; i += step) add(i, i + r);
+    } else {
+      add(base, base + r);
     }
   }
+  constexpr void sort(int base, int m) {
+    if (m > 1) {
+      sort(base, m / 2);
+      sort(base + m / 2, m / 2);
+      merge(base, m, 1);
+    }
+  }
+  constexpr void add(int i, int j) {
+    lo[n] = i;
+    hi[n] = j;
+    ++n;
+  }
+  constexpr SortNet() { sort(0, L); }
+};
+
+template <typename T>
+__host__ __device__ __forceinline__ void compare_exchange(T& x, T& y) {
+  const T a = x, b = y;
+  x = a > b ? a : b;
+  y = a > b ? b : a;
+}
+
+template <typename T, int L, int... I>
+__host__ __device__ __forceinline__ void apply_net(T (&a)[L], std::integer_sequence<int, I...>) {
+  constexpr SortNet<L> net{};
+  (compare_exchange(a[net.lo[I]], a[net.hi[I]]), ...);
+}
+
+// Sort a[0..L) into descending order (L a power of two).
+template <typename T, int L>
+__host__ __device__ __forceinline__ void sort_descending(T (&a)[L]) {
+  constexpr int kPairs = SortNet<L>{}.n;
+  apply_net(a, std::make_integer_sequence<int, kPairs>{});
 }
 
 // Greedy keep mask of one block (bit r*M + c = entry (r, c) kept).
@@ -167,7 +194,15 @@ __global__ void __launch_bounds__(kThreads) tmask_kernel(const E* __restrict__ W
   constexpr int C = BPT * M;  // columns per thread
   const int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (u >= units) return;
-  const int64_t r0 = (u / units_per_row) * M, c0 = (u % units_per_row) * C;
+  int64_t ur, uc;  // unit row and column
+  if (units <= 0xFFFFFFFFll) {  // 32-bit division where it fits (every practical size)
+    ur = (uint32_t)u / (uint32_t)units_per_row;
+    uc = (uint32_t)u - (uint32_t)ur * (uint32_t)units_per_row;
+  } else {
+    ur = u / units_per_row;
+    uc = u % units_per_row;
+  }
+  const int64_t r0 = ur * M, c0 = uc * C;
   uint32_t row[M][C];
 #pragma unroll
   for (int r = 0; r < M; ++r) load_row<E, C>(W + (r0 + r) * K + c0, row[r]);
