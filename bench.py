@@ -415,9 +415,10 @@ def main() -> int:
     srste = transposable = None
     if float_path:
         # ---- SR-STE passes on the same weights (not part of the step) ----
-        # Each timed launch starts cold: a 512 MiB fill (twice the 256 MB Infinity Cache) runs
+        # Each timed launch starts cold: a 512 MiB read (twice the 256 MB Infinity Cache) runs
         # before it, outside its events, so its inputs come from HBM as in a training step,
-        # where the forward and the backward of a layer are far apart.
+        # where the forward and the backward of a layer are far apart.  A read, not a fill:
+        # a fill would leave dirty lines whose write-back competes with the timed kernel.
         sr_kinds = ["prune", "srste_grad"]
         flush = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
         for _ in range(args.warmup):
@@ -427,7 +428,7 @@ def main() -> int:
         for _ in range(args.steps):
             for d in mats:
                 for kind in sr_kinds:
-                    flush.zero_()
+                    flush.view(torch.int64).sum()
                     e0 = torch.cuda.Event(enable_timing=True)
                     e1 = torch.cuda.Event(enable_timing=True)
                     e0.record(stream)
@@ -474,7 +475,7 @@ def main() -> int:
             for d in mats:
                 for kind in tr_kinds:
                     if kind != "spmm_t":
-                        flush.zero_()
+                        flush.view(torch.int64).sum()
                     e0 = torch.cuda.Event(enable_timing=True)
                     e1 = torch.cuda.Event(enable_timing=True)
                     e0.record(stream)

@@ -963,6 +963,20 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
       m_src[j] = meta_source<kBlocked, kPat12>(m0, 32 * b32, lane, R, K, nsteps);
       m_dst[j] = (uint32_t)(TL::kXBytes + TL::kABytes + b32 * 256);
     }
+    // Blocked 2:4: the 128 metadata bytes of a 16-row block and step are contiguous, so
+    // each producer fetches four blocks (512 bytes) with one 16-byte-per-lane load on half
+    // its lanes, instead of two 4-byte-per-lane loads; the bytes land where those would.
+    constexpr bool kWideMeta = kBlocked && !kPat12;
+    static_assert(!kWideMeta || TL::kMBytes == 512 * TL::kProducers, "four blocks per producer");
+    int64_t m16_src = 0;
+    uint32_t m16_dst = 0;
+    if constexpr (kWideMeta) {
+      const int last = ((R + 15) >> 4) - 1;
+      int g = (m0 >> 4) + 4 * pw + ((lane & 31) >> 3);
+      g = g < last ? g : last;
+      m16_src = (int64_t)g * nsteps * 128 + 16 * (lane & 7);
+      m16_dst = (uint32_t)(TL::kXBytes + TL::kABytes + pw * 512);
+    }
     auto issue_step = [&](int step) {
       step = step < last_step ? step : last_step;  // past the end: re-read the last step
       uint8_t* st = smem + (step % kStages) * TL::kStageBytes;
@@ -973,15 +987,21 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
       for (int j = 0; j < TL::kXLoads; ++j) global_to_lds<16>(xg + x_src[j] + kx, st + x_dst[j]);
 #pragma unroll
       for (int j = 0; j < TL::kALoads; ++j) global_to_lds<16>(vg + a_src[j] + ka, st + a_dst[j]);
+      if constexpr (kWideMeta) {
+        if (lane < 32) global_to_lds<16>(mg + m16_src + km, st + m16_dst);
+      } else {
 #pragma unroll
-      for (int j = 0; j < TL::kMLoads; ++j) global_to_lds<4>(mg + m_src[j] + km, st + m_dst[j]);
+        for (int j = 0; j < TL::kMLoads; ++j) global_to_lds<4>(mg + m_src[j] + km, st + m_dst[j]);
+      }
     };
+    // direct loads one producer issues per step
+    constexpr int kLoads = TL::kXLoads + TL::kALoads + (kWideMeta ? 1 : TL::kMLoads);
 #pragma unroll
     for (int k = 0; k < kStages - 1; ++k) issue_step(k);
-    wait_loads_and_barrier<(kStages - 3) * TL::kLoads>();  // steps 0 and 1 landed
+    wait_loads_and_barrier<(kStages - 3) * kLoads>();  // steps 0 and 1 landed
     for (int s = 0; s < nsteps; ++s) {
       issue_step(s + kStages - 1);
-      wait_loads_and_barrier<(kStages - 3) * TL::kLoads>();  // step s+2 landed
+      wait_loads_and_barrier<(kStages - 3) * kLoads>();  // step s+2 landed
     }
     // loads past the end have landed before the consumers reuse LDS for the epilogue
     wait_loads_and_barrier<0>();
