@@ -1864,7 +1864,7 @@ struct TileChoice {
   double rate;
 };
 constexpr int kNumTiles = 3;
-constexpr TileChoice kTiles[kNumTiles] = {{256, 256, 1300.0}, {256, 128, 1300.0},
+constexpr TileChoice kTiles[kNumTiles] = {{256, 256, 1300.0}, {256, 128, 1350.0},
                                           {128, 128, 850.0}};
 constexpr double kTileFixedUs = 3.0;
 
