@@ -610,9 +610,8 @@ __global__ void __launch_bounds__(kThreads) blocked_decompress_kernel(
   }
   // The 4 lanes of a row hold its 16-byte chunks in lane order, kWords / 4 chunks each.
   // Stored as they are, every store instruction would write one chunk in kWords / 4 of
-  // each row segment, and such scattered 16-byte pieces cost extra HBM write traffic
-  // (measured: 15% over the output's bytes for bf16).  Regroup across the quad first, so
-  // that store i of lane q writes chunk 4i + q: 64 contiguous bytes per row and store.
+  // each row segment.  Regroup across the quad first, so that store i of lane q writes
+  // chunk 4i + q: 64 contiguous bytes per row and store (measured 8% faster for bf16).
   const int q = lane & 3;
   uint32_t* dst = out + (row * K + 64 * st) * sizeof(E) / 4 + 4 * q;
   store_row_chunks<L::kWords / 4>(ow, q, dst, std::make_integer_sequence<int, L::kWords / 4>{});
