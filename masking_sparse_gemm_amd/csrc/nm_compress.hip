@@ -517,61 +517,12 @@ __global__ void __launch_bounds__(kThreads) meta_word_t_kernel(const E* __restri
   meta[k * wpr + w] = word;
 }
 
-// Store i of lane q (of a quad holding S 16-byte chunks each, in lane order) writes chunk
-// 4i + q, which lives in lane (4i + q) / S as its chunk (4i + q) % S: fetched with a quad
-// permute (one per source chunk) and a select.
-template <int S, int I>
-__device__ __forceinline__ void store_row_chunk(const uint32_t (&ow)[4 * S], int q, uint32_t* dst) {
-  uint32_t v[4];
-  if constexpr (S == 1) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = ow[j];
-  } else {
-    constexpr int kPerm = ((4 * I + 0) / S) | ((4 * I + 1) / S) << 2 | ((4 * I + 2) / S) << 4 |
-                          ((4 * I + 3) / S) << 6;
-    const int h = (4 * I + q) % S;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t pick = 0;
-#pragma unroll
-      for (int c = 0; c < S; ++c) {
-        const uint32_t moved =
-            (uint32_t)__builtin_amdgcn_mov_dpp((int)ow[4 * c + j], kPerm, 0xF, 0xF, false);
-        pick = (h == c) ? moved : pick;
-      }
-      v[j] = pick;
-    }
-  }
-  __builtin_nontemporal_store(u32x4_t{v[0], v[1], v[2], v[3]},
-                              reinterpret_cast<u32x4_t*>(dst + 16 * I));
-}
-
-template <int S, int... I>
-__device__ __forceinline__ void store_row_chunks(const uint32_t (&ow)[4 * S], int q, uint32_t* dst,
-                                                 std::integer_sequence<int, I...>) {
-  (store_row_chunk<S, I>(ow, q, dst), ...);
-}
-
 template <typename E, int N, int M>
-__global__ void __launch_bounds__(kThreads) blocked_decompress_kernel(
-    const uint32_t* __restrict__ values, const uint32_t* __restrict__ meta, int64_t R, int64_t K,
-    int64_t blocks, uint32_t* __restrict__ out) {
+__device__ __forceinline__ void decompress_lane(const uint32_t* __restrict__ values,
+                                                const uint32_t* __restrict__ meta, int64_t blk,
+                                                int lane, uint32_t (&ow)[LaneShape<E, N, M>::kWords]) {
   using L = LaneShape<E, N, M>;
   constexpr int b = meta_bits(M);
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar math
-  const int64_t blk = (int64_t)blockIdx.x * (kThreads / 64) + wave;
-  if (blk >= blocks) return;
-  const int64_t steps = K / 64;
-  int64_t rb, st;  // row block and step of this block
-  if (blocks <= 0xFFFFFFFFll) {
-    rb = (uint32_t)blk / (uint32_t)steps;
-    st = (uint32_t)blk - (uint32_t)rb * (uint32_t)steps;
-  } else {
-    rb = blk / steps;
-    st = blk % steps;
-  }
-  // padding rows (stored as zeros) are decompressed like the others, but not written
   const uint32_t* vsrc = values + blk * (64 * L::kValWords) + lane * L::kValWords;
   uint32_t vw[L::kValWords];
 #pragma unroll
@@ -582,7 +533,6 @@ __global__ void __launch_bounds__(kThreads) blocked_decompress_kernel(
   if (sh + L::kBits > 32) window |= (uint64_t)mblk[wi + 1] << 32;
   uint64_t bits = window >> sh;
   if (sh + L::kBits > 64) bits |= (uint64_t)mblk[wi + 2] << (64 - sh);
-  uint32_t ow[L::kWords];
 #pragma unroll
   for (int i = 0; i < L::kWords; ++i) ow[i] = 0;
 #pragma unroll
@@ -607,27 +557,56 @@ __global__ void __launch_bounds__(kThreads) blocked_decompress_kernel(
       }
     }
   }
-  // The 4 lanes of a row hold its 16-byte chunks in lane order.  Written as they are, a
-  // row's 128-byte line would come from several store instructions; staged through the
-  // wave's LDS slice instead, each store covers whole row segments: lane l writes chunk
-  // l % C of row l / C (C chunks per row), so one instruction writes 64 / C full rows.
-  constexpr int S = L::kWords / 4;  // 16-byte chunks per lane
-  constexpr int C = 4 * S;          // 16-byte chunks per row segment
-  __shared__ __align__(16) uint32_t stage[kThreads / 64][64 * L::kWords];
+}
+
+// kPer consecutive blocks per wave (2 for 1-byte elements when the step count is even, so
+// that a row segment of the two blocks is one 128-byte line).  The 4 lanes of a row hold
+// its 16-byte chunks in lane order; written as they are, a row's 128-byte line would come
+// from several store instructions, which the write counter showed to cost extra HBM write
+// traffic (109 MB for 90 MB of bf16 output).  Each wave therefore stages its blocks in
+// its LDS slice and stores them back row by row: lane l writes chunk l % C of row l / C
+// (C chunks per row segment), one instruction covering 64 / C whole row segments.
+template <typename E, int N, int M, int kPer>
+__global__ void __launch_bounds__(kThreads) blocked_decompress_kernel(
+    const uint32_t* __restrict__ values, const uint32_t* __restrict__ meta, int64_t R, int64_t K,
+    int64_t blocks, uint32_t* __restrict__ out) {
+  using L = LaneShape<E, N, M>;
+  constexpr int S = L::kWords / 4;  // 16-byte chunks per lane and block
+  constexpr int C = 4 * S * kPer;   // 16-byte chunks per row segment
+  __shared__ __align__(16) uint32_t stage[kThreads / 64][64 * L::kWords * kPer];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar math
+  const int64_t blk = ((int64_t)blockIdx.x * (kThreads / 64) + wave) * kPer;
+  if (blk >= blocks) return;
+  const int64_t steps = K / 64;
+  int64_t rb, st;  // row block and (first) step of this wave's blocks
+  if (blocks <= 0xFFFFFFFFll) {
+    rb = (uint32_t)blk / (uint32_t)steps;
+    st = (uint32_t)blk - (uint32_t)rb * (uint32_t)steps;
+  } else {
+    rb = blk / steps;
+    st = blk % steps;
+  }
   uint32_t* sw = stage[wave];
+  const int rr0 = lane >> 2, q = lane & 3;
 #pragma unroll
-  for (int c = 0; c < S; ++c)
-    *reinterpret_cast<u32x4_t*>(sw + lane * L::kWords + 4 * c) =
-        u32x4_t{ow[4 * c], ow[4 * c + 1], ow[4 * c + 2], ow[4 * c + 3]};
+  for (int p = 0; p < kPer; ++p) {
+    uint32_t ow[L::kWords];
+    decompress_lane<E, N, M>(values, meta, blk + p, lane, ow);
+#pragma unroll
+    for (int c = 0; c < S; ++c)
+      *reinterpret_cast<u32x4_t*>(sw + (rr0 * C + p * 4 * S + q * S + c) * 4) =
+          u32x4_t{ow[4 * c], ow[4 * c + 1], ow[4 * c + 2], ow[4 * c + 3]};
+  }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-  for (int i = 0; i < S; ++i) {
+  for (int i = 0; i < S * kPer; ++i) {
     const int rr = i * (64 / C) + lane / C, ch = lane % C;
     const u32x4_t v = *reinterpret_cast<const u32x4_t*>(sw + (rr * C + ch) * 4);
     const int64_t r = 16 * rb + rr;
-    if (r < R)
+    if (r < R)  // padding rows have no output
       __builtin_nontemporal_store(
           v, reinterpret_cast<u32x4_t*>(out + (r * K + 64 * st) * sizeof(E) / 4) + ch);
   }
@@ -833,8 +812,16 @@ hipError_t run_decompress(const void* values, const uint32_t* meta, int64_t R, i
   if (blocked) {
     if constexpr (blocked_kernel_exists<E, N, M>()) {
       const int64_t blocks = (R + 15) / 16 * (K / 64);
-      blocked_decompress_kernel<E, N, M><<<blocks_for(blocks, kThreads / 64), kThreads, 0, s>>>(
-          static_cast<const uint32_t*>(values), meta, R, K, blocks, static_cast<uint32_t*>(out));
+      if (sizeof(E) == 1 && (K / 64) % 2 == 0)
+        blocked_decompress_kernel<E, N, M, 2>
+            <<<blocks_for(blocks / 2, kThreads / 64), kThreads, 0, s>>>(
+                static_cast<const uint32_t*>(values), meta, R, K, blocks,
+                static_cast<uint32_t*>(out));
+      else
+        blocked_decompress_kernel<E, N, M, 1>
+            <<<blocks_for(blocks, kThreads / 64), kThreads, 0, s>>>(
+                static_cast<const uint32_t*>(values), meta, R, K, blocks,
+                static_cast<uint32_t*>(out));
       return hipGetLastError();
     }
     return hipErrorInvalidValue;
