@@ -162,10 +162,18 @@ __global__ void __launch_bounds__(kThreads) gains_kernel(const float* __restrict
     __syncthreads();
   }
   if (active) {
+    // first strict maximum; the value is carried along so that no register array is
+    // indexed at run time (which moved the 64 accumulators of 8-wide groups to scratch
+    // memory)
     int best = 0;
+    float bv = acc[0];
 #pragma unroll
-    for (int i = 1; i < M * M; ++i) best = (acc[i] > acc[best]) ? i : best;
-    gain[g1 * G + g2] = acc[best];
+    for (int i = 1; i < M * M; ++i) {
+      const bool up = acc[i] > bv;
+      best = up ? i : best;
+      bv = up ? acc[i] : bv;
+    }
+    gain[g1 * G + g2] = bv;
     pick[g1 * G + g2] = best;
   }
 }
