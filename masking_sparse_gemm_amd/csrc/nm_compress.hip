@@ -392,70 +392,80 @@ __global__ void __launch_bounds__(kThreads) blocked_select_kernel(const uint32_t
 
 // The blocked layout of W's TRANSPOSE (K x R, groups of M along R; R % 64 == 0): block
 // (g, s) holds transposed rows 16g .. 16g+15, i.e. columns 16g .. of W, and step s,
-// i.e. rows 64s .. 64s+63 of W.  A wave takes column group g and kStepsPerWave
-// consecutive steps: it stages those 64 x 16 tiles of W in LDS with row-contiguous
-// loads, all issued before any is used (the 4 waves of a workgroup take neighbouring
-// column groups, so together they read whole 128-byte lines), then for each tile every
-// lane gathers its 16 elements down one column and proceeds as for W itself.  Columns
-// past K are padding (zeros).
-constexpr int kStepsPerWave = 1;
+// i.e. rows 64s .. 64s+63 of W.  A wave takes a column quad (column groups 4c .. 4c+3,
+// 64 columns of W) and one step: it stages the 64 x 64 tile of W in its LDS slice with
+// whole 128-byte row segments per load instruction, then for each of the four column
+// groups every lane gathers its 16 elements down one column and proceeds as for W
+// itself.  (Quarter-line reads by four waves had fetched 15% more than W's bytes.)  The
+// four waves of a workgroup take four consecutive steps of one quad and consecutive
+// workgroups continue down its steps, so each column group's blocks are written front
+// to back.  Columns past K are padding (zeros).
+template <typename E>
+struct TileT {
+  static constexpr int kChunkElems = 16 / (int)sizeof(E);  // elements per 16-byte chunk
+  static constexpr int kRowChunks = 64 / kChunkElems;      // chunks per 64-column row
+  static constexpr int kRowWords = 16 * kRowChunks / 4;    // LDS words per row
+  // Rows 16q .. 16q+15 start kShift * q words further, so that the column gathers of
+  // the four quarters (lanes with q = 0..3) fall in different banks.
+  static constexpr int kShift = sizeof(E) == 4 ? 16 : 8;
+  static constexpr int kWords = 64 * kRowWords + 3 * kShift;
+  __device__ static constexpr int row_word(int r) { return r * kRowWords + (r >> 4) * kShift; }
+};
 
 template <typename E, int N, int M>
 __global__ void __launch_bounds__(kThreads) blocked_select_t_kernel(
     const E* __restrict__ W, int64_t R, int64_t K, int64_t blocks, uint32_t* __restrict__ values,
     uint32_t* __restrict__ meta) {
   using L = LaneShape<E, N, M>;
-  constexpr int kChunkElems = 16 / (int)sizeof(E);      // elements per 16-byte chunk
-  constexpr int kChunksPerRow = 16 / kChunkElems;       // 2 (16-bit) or 4 (fp32)
+  using TT = TileT<E>;
   __shared__ uint32_t lds_bits[kThreads / 64][L::kShuffle ? 1 : L::kBlockMetaWords];
-  __shared__ __align__(16) E tile[kThreads / 64][kStepsPerWave][64][16];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ __align__(16) uint32_t tile[kThreads / 64][TT::kWords];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t steps = R / 64, groups = (K + 15) / 16;
-  // Consecutive workgroups take consecutive steps of the same four column groups, so
-  // each column group's blocks are written front to back.  (Measured: this beats
-  // orders that read the rows of W front to back, which scatter the block writes.)
-  // (blockIdx.x < 2^32, and wave_steps <= blocks fits 32 bits whenever the grid does)
-  const uint32_t wave_steps = (uint32_t)((steps + kStepsPerWave - 1) / kStepsPerWave);
-  const int64_t s0 = (int64_t)(blockIdx.x % wave_steps) * kStepsPerWave;
-  const int64_t g = (int64_t)(blockIdx.x / wave_steps) * (kThreads / 64) + wave;
-  if (g >= groups || s0 >= steps) return;  // the whole wave
-  const int64_t c0 = 16 * g;
+  // (blockIdx.x < 2^32, and step_quads <= the grid size fits 32 bits)
+  const uint32_t step_quads = (uint32_t)((steps + 3) / 4);
+  const int64_t quad = blockIdx.x / step_quads;
+  const int64_t st = (int64_t)(blockIdx.x % step_quads) * 4 + wave;
+  if (st >= steps) return;  // the whole wave
+  const int64_t c0 = 64 * quad;
   const bool vec_ok = (K * (int64_t)sizeof(E)) % 16 == 0;
+  uint32_t* tw = tile[wave];
 #pragma unroll
-  for (int t = 0; t < kStepsPerWave; ++t) {
-    if (s0 + t >= steps) break;
+  for (int it = 0; it < TT::kRowChunks; ++it) {
+    const int chunk = it * 64 + lane;  // 64 rows x kRowChunks chunks
+    const int r = chunk / TT::kRowChunks, ch = chunk % TT::kRowChunks;
+    const int64_t col = c0 + ch * TT::kChunkElems;
+    const E* src = W + (64 * st + r) * K + col;
+    uint32_t* dst = tw + TT::row_word(r) + 4 * ch;
+    if (vec_ok && col + TT::kChunkElems <= K) {
+      *reinterpret_cast<u32x4_t*>(dst) =
+          __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src));
+    } else {
+      uint32_t v[4] = {0, 0, 0, 0};
 #pragma unroll
-    for (int it = 0; it < kChunksPerRow; ++it) {
-      const int chunk = it * 64 + lane;             // 64 rows x kChunksPerRow chunks
-      const int r = chunk / kChunksPerRow, ch = chunk % kChunksPerRow;
-      const int64_t col = c0 + ch * kChunkElems;
-      const E* src = W + (64 * (s0 + t) + r) * K + col;
-      E* dst = &tile[wave][t][r][ch * kChunkElems];
-      if (vec_ok && col + kChunkElems <= K) {
-        *reinterpret_cast<u32x4_t*>(dst) =
-            __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src));
-      } else {
-#pragma unroll
-        for (int e = 0; e < kChunkElems; ++e) dst[e] = (col + e < K) ? src[e] : (E)0;
-      }
+      for (int e = 0; e < TT::kChunkElems; ++e)
+        put_elem<E>(v, e, (col + e < K) ? (uint32_t)src[e] : 0u);
+      *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{v[0], v[1], v[2], v[3]};
     }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const int col = lane >> 2, q = lane & 3;
-  const bool live = c0 + col < K;
+  const int cl = lane >> 2, q = lane & 3;
+  const E* te = reinterpret_cast<const E*>(tw);
 #pragma unroll
-  for (int t = 0; t < kStepsPerWave; ++t) {
-    if (s0 + t >= steps) break;
+  for (int cg = 0; cg < 4; ++cg) {
+    const int64_t g = 4 * quad + cg;
+    if (g >= groups) break;  // the same for the whole wave
+    const int col = 16 * cg + cl;
     uint32_t w[L::kWords];
 #pragma unroll
     for (int i = 0; i < L::kWords; ++i) w[i] = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      put_elem<E>(w, i, (uint32_t)tile[wave][t][16 * q + i][col]);
-    }
-    blocked_emit<E, N, M>(w, live, g * steps + s0 + t, lane, lds_bits[wave], values, meta);
+    for (int i = 0; i < 16; ++i)
+      put_elem<E>(w, i, (uint32_t)te[TT::row_word(16 * q + i) * (4 / (int)sizeof(E)) + col]);
+    blocked_emit<E, N, M>(w, c0 + col < K, g * steps + st, lane, lds_bits[wave], values, meta);
   }
 }
 
@@ -787,8 +797,7 @@ hipError_t run_select_t(const void* W, int64_t R, int64_t K, bool blocked, void*
   const E* w = static_cast<const E*>(W);
   if (blocked) {
     const int64_t steps = R / 64, groups = (K + 15) / 16;
-    const int64_t wg = (groups + kThreads / 64 - 1) / (kThreads / 64) *
-                       ((steps + kStepsPerWave - 1) / kStepsPerWave);
+    const int64_t wg = (groups + 3) / 4 * ((steps + 3) / 4);  // column quads x step quads
     blocked_select_t_kernel<E, N, M><<<(unsigned)wg, kThreads, 0, s>>>(
         w, R, K, groups * steps, static_cast<uint32_t*>(values), meta);
     return hipGetLastError();
