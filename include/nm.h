@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define NM_ABI_VERSION 7
+#define NM_ABI_VERSION 8
 
 typedef enum {
   NM_OK = 0,
@@ -129,6 +129,18 @@ size_t nm_meta_bytes(int64_t R, int64_t K, int n, int m, nm_layout layout);
  * Returns -1 for invalid arguments. */
 int64_t nm_meta_words_per_row(int64_t K, int n, int m);
 
+/* Debug check of compressed metadata, on the HOST (meta_host is host memory; nothing
+ * runs on the GPU).  The product trusts its metadata ("Tensor Scores 상에서 구조적인
+ * sparse GEMM": the application supplies the compressed operand), so a caller that builds
+ * metadata itself can check it here first.  Well formed means: the n positions of every
+ * group are strictly ascending, and the unused high bits of every NM_LAYOUT_ROWS row are
+ * zero.  Returns -1 if all R rows are well formed; else the row-major index r * (K / m) + g
+ * of the first malformed group (a row with non-zero padding bits counts as malformed at
+ * its last group); -2 for invalid arguments (pattern, shape, layout, or a NULL pointer
+ * with R * K > 0). */
+int64_t nm_check_meta(const uint32_t* meta_host, int64_t R, int64_t K, int n, int m,
+                      nm_layout layout);
+
 /* Magnitude-best N:M mask of W ("NVIDA Apex内的静态掩码稀疏"): in every group of m
  * consecutive elements along K the n positions with the largest sum of |w| are
  * kept; equal sums go to the lexicographically first position tuple (lower
@@ -156,8 +168,9 @@ nm_status nm_decompress(const void* values, const uint32_t* meta, nm_dtype dt, i
  * accumulated in fp32 and rounded once to y_dt (round to nearest even); y_dt
  * must be dt or NM_F32.  For dt = NM_I8 (W and X int8) y_dt must be NM_I32 and Y is
  * the exact integer product (K < 2^17, else NM_ERR_SHAPE, so no sum can overflow).
- * For dt = NM_FP8, y_dt is NM_F32 or NM_BF16 (fp32 accumulation, one rounding).  The metadata is trusted (well-formedness is the
- * caller's responsibility, as for any compressed operand).  Both layouts are
+ * For dt = NM_FP8, y_dt is NM_F32 or NM_BF16 (fp32 accumulation, one rounding).  The
+ * metadata is trusted (well-formedness is the caller's responsibility, as for any
+ * compressed operand; nm_check_meta checks it on the host).  Both layouts are
  * accepted; the matrix-core kernels (2:4 and 1:2, 16-bit dt) stream
  * NM_LAYOUT_BLOCKED at full speed and NM_LAYOUT_ROWS at a lower rate. */
 nm_status nm_spmm(const void* values, const uint32_t* meta, int64_t R, int64_t K, int n, int m,

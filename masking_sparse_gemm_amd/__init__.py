@@ -39,13 +39,13 @@ _TORCH_DT = {v: k for k, v in _DT.items()}
 STATUS = ["ok", "null", "shape", "pattern", "dtype", "align", "unsupported", "device", "layout",
           "alias"]
 LAYOUTS = {"rows": 0, "blocked": 1}
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 # every function the C header declares
 EXPORTS = ("nm_abi_version", "nm_status_str", "nm_values_bytes", "nm_meta_bytes",
            "nm_meta_words_per_row", "nm_mask", "nm_compress", "nm_decompress", "nm_spmm",
            "nm_prune", "nm_srste_grad", "nm_tmask", "nm_tprune", "nm_compress_t",
-           "nm_perm_workspace_bytes", "nm_perm_gains", "nm_perm_search")
+           "nm_perm_workspace_bytes", "nm_perm_gains", "nm_perm_search", "nm_check_meta")
 SRSTE_DECAY = 0.0002  # the SR-STE page's default decay
 
 
@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.nm_meta_bytes.restype = ctypes.c_size_t
         L.nm_meta_words_per_row.argtypes = [i64, i32, i32]
         L.nm_meta_words_per_row.restype = i64
+        L.nm_check_meta.argtypes = [vp, i64, i64, i32, i32, i32]
+        L.nm_check_meta.restype = i64
         L.nm_mask.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp]
         L.nm_compress.argtypes = [vp, i32, i64, i64, i32, i32, i32, vp, vp, vp]
         L.nm_decompress.argtypes = [vp, vp, i32, i64, i64, i32, i32, i32, vp, vp]
@@ -133,6 +135,23 @@ def _dense_input(t: torch.Tensor, name: str, int8: bool = True) -> int:
 
 def meta_words_per_row(K: int, n: int, m: int) -> int:
     return int(lib().nm_meta_words_per_row(K, n, m))
+
+
+def check_meta(meta: torch.Tensor, R: int, K: int, n: int = 2, m: int = 4,
+               layout: str = "rows") -> int:
+    """Host-side check of metadata (copied to host memory first): -1 if every group's
+    positions are strictly ascending and row padding bits are zero, else the row-major
+    index of the first malformed group."""
+    host = meta.detach().to("cpu").contiguous()
+    if host.dtype != torch.int32:
+        raise ValueError("meta must be int32 (holding the uint32 words)")
+    need = int(lib().nm_meta_bytes(R, K, n, m, _layout(layout)))
+    if R * K and host.numel() * 4 < need:
+        raise ValueError(f"meta holds {host.numel() * 4} bytes, {need} needed")
+    res = int(lib().nm_check_meta(ctypes.c_void_p(host.data_ptr()), R, K, n, m, _layout(layout)))
+    if res == -2:
+        raise ValueError("invalid arguments (pattern, shape or layout)")
+    return res
 
 
 def _layout(layout: str) -> int:

@@ -124,6 +124,46 @@ size_t nm_meta_bytes(int64_t R, int64_t K, int n, int m, nm_layout layout) {
   return (size_t)(padded_rows(R, layout) * meta_row_bytes(K, n, m, layout));
 }
 
+int64_t nm_check_meta(const uint32_t* meta_host, int64_t R, int64_t K, int n, int m,
+                      nm_layout layout) {
+  if (check_pattern(n, m) != NM_OK || check_shape(R, K, m) != NM_OK ||
+      check_layout(layout, K) != NM_OK)
+    return -2;
+  if (R * K == 0) return -1;
+  if (meta_host == nullptr) return -2;
+  const int b = meta_bits_of(m);
+  const int64_t G = K / m, row_bits = G * n * b;
+  const uint8_t* bytes = reinterpret_cast<const uint8_t*>(meta_host);
+  const int64_t row_bytes = meta_row_bytes(K, n, m, layout);
+  std::vector<uint8_t> row((size_t)row_bytes + 2);  // + 2: a field read may look past the end
+  for (int64_t r = 0; r < R; ++r) {
+    if (layout == NM_LAYOUT_ROWS) {
+      std::memcpy(row.data(), bytes + r * row_bytes, (size_t)row_bytes);
+    } else {  // the row's slice of every 64-wide step, from block (r / 16, s)
+      const int64_t S = K / 64, B = row_bytes / S;
+      for (int64_t st = 0; st < S; ++st)
+        std::memcpy(row.data() + st * B, bytes + (((r / 16) * S + st) * 16 + r % 16) * B, (size_t)B);
+    }
+    row[row_bytes] = row[row_bytes + 1] = 0;
+    auto field = [&](int64_t f) {  // b bits at bit f * b, least significant first
+      const int64_t bit = f * b;
+      const uint32_t v = row[bit / 8] | (uint32_t)row[bit / 8 + 1] << 8;
+      return (int)((v >> (bit % 8)) & ((1u << b) - 1u));
+    };
+    for (int64_t g = 0; g < G; ++g) {
+      int prev = -1;
+      for (int j = 0; j < n; ++j) {
+        const int p = field(g * n + j);
+        if (p <= prev) return r * G + g;
+        prev = p;
+      }
+    }
+    for (int64_t bit = row_bits; bit < row_bytes * 8; ++bit)
+      if ((row[bit / 8] >> (bit % 8)) & 1u) return r * G + G - 1;
+  }
+  return -1;
+}
+
 int64_t nm_meta_words_per_row(int64_t K, int n, int m) {
   if (check_pattern(n, m) != NM_OK || K < 0 || K % m != 0) return -1;
   return ((K / m) * n * meta_bits_of(m) + 31) / 32;

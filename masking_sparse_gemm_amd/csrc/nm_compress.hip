@@ -414,7 +414,7 @@ struct TileT {
 
 template <typename E, int N, int M>
 __global__ void __launch_bounds__(kThreads) blocked_select_t_kernel(
-    const E* __restrict__ W, int64_t R, int64_t K, int64_t blocks, uint32_t* __restrict__ values,
+    const E* __restrict__ W, int64_t R, int64_t K, uint32_t* __restrict__ values,
     uint32_t* __restrict__ meta) {
   using L = LaneShape<E, N, M>;
   using TT = TileT<E>;
@@ -799,7 +799,7 @@ hipError_t run_select_t(const void* W, int64_t R, int64_t K, bool blocked, void*
     const int64_t steps = R / 64, groups = (K + 15) / 16;
     const int64_t wg = (groups + 3) / 4 * ((steps + 3) / 4);  // column quads x step quads
     blocked_select_t_kernel<E, N, M><<<(unsigned)wg, kThreads, 0, s>>>(
-        w, R, K, groups * steps, static_cast<uint32_t*>(values), meta);
+        w, R, K, static_cast<uint32_t*>(values), meta);
     return hipGetLastError();
   }
   group_t_kernel<E, N, M><<<blocks_for(R / M * K, kThreads), kThreads, 0, s>>>(

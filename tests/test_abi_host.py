@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     L = nm.lib()
     for name in header_functions():
         assert hasattr(L, name), name
-    assert L.nm_abi_version() == nm.ABI_VERSION == 7
+    assert L.nm_abi_version() == nm.ABI_VERSION == 8
 
 
 @needs_lib
