@@ -333,8 +333,10 @@ def main() -> int:
     for d in mats:
         ab = algorithmic_bytes(d["R"], d["K"], d["T"], n, m, d["s"], d["ys"])
         for kind in kinds:
-            t = float(np.mean(per[(d["name"], kind)])) * 1e-3
-            entry = {"us": round(t * 1e6, 2), "alg_bytes": ab[kind],
+            samples = per[(d["name"], kind)]
+            t = float(np.mean(samples)) * 1e-3
+            entry = {"us": round(t * 1e6, 2), "us_median": round(float(np.median(samples)) * 1e3, 2),
+                     "us_min": round(float(np.min(samples)) * 1e3, 2), "alg_bytes": ab[kind],
                      "gbps": round(ab[kind] / t / 1e9, 1)}
             if kind == "spmm":
                 f_alg = 2.0 * d["R"] * d["K"] * d["T"] * n / m
