@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define NM_ABI_VERSION 8
+#define NM_ABI_VERSION 9
 
 typedef enum {
   NM_OK = 0,
@@ -155,6 +155,15 @@ nm_status nm_mask(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m
  * rows of NM_LAYOUT_BLOCKED are written as zeros). */
 nm_status nm_compress(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m,
                       nm_layout layout, void* values, uint32_t* meta, nm_stream_t stream);
+
+/* nm_mask and nm_compress in one pass over W: the mask (R x K, uint8, as nm_mask writes
+ * it) and the compressed pair in `layout` (as nm_compress writes it).  The pages' mask
+ * and compression are one search ("NVIDA Apex内的静态掩码稀疏" keeps the best pattern of
+ * every group; "2:4 Sparsity의 benefits" stores its values and positions), so W is read
+ * once.  No output may overlap W or another output (NM_ERR_ALIAS). */
+nm_status nm_mask_compress(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m,
+                           nm_layout layout, uint8_t* mask, void* values, uint32_t* meta,
+                           nm_stream_t stream);
 
 /* Inverse of nm_compress: W_out (R x K) gets each stored value at its recorded
  * position and +0 (all-zero bits) everywhere else.  The metadata is trusted: a

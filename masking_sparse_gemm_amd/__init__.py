@@ -39,13 +39,14 @@ _TORCH_DT = {v: k for k, v in _DT.items()}
 STATUS = ["ok", "null", "shape", "pattern", "dtype", "align", "unsupported", "device", "layout",
           "alias"]
 LAYOUTS = {"rows": 0, "blocked": 1}
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 # every function the C header declares
 EXPORTS = ("nm_abi_version", "nm_status_str", "nm_values_bytes", "nm_meta_bytes",
            "nm_meta_words_per_row", "nm_mask", "nm_compress", "nm_decompress", "nm_spmm",
            "nm_prune", "nm_srste_grad", "nm_tmask", "nm_tprune", "nm_compress_t",
-           "nm_perm_workspace_bytes", "nm_perm_gains", "nm_perm_search", "nm_check_meta")
+           "nm_perm_workspace_bytes", "nm_perm_gains", "nm_perm_search", "nm_check_meta",
+           "nm_mask_compress")
 SRSTE_DECAY = 0.0002  # the SR-STE page's default decay
 
 
@@ -80,6 +81,7 @@ def lib() -> ctypes.CDLL:
         L.nm_check_meta.restype = i64
         L.nm_mask.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp]
         L.nm_compress.argtypes = [vp, i32, i64, i64, i32, i32, i32, vp, vp, vp]
+        L.nm_mask_compress.argtypes = [vp, i32, i64, i64, i32, i32, i32, vp, vp, vp, vp]
         L.nm_decompress.argtypes = [vp, vp, i32, i64, i64, i32, i32, i32, vp, vp]
         L.nm_spmm.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, i64, i32, vp, i32, vp]
         L.nm_prune.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp]
@@ -195,6 +197,20 @@ def compress(W: torch.Tensor, n: int = 2, m: int = 4, layout: str = "rows"):
     _check("nm_compress", lib().nm_compress(_ptr(W), dt, R, K, n, m, lay, _ptr(values),
                                             _ptr(meta), _stream(W)))
     return values, meta
+
+
+def mask_compress(W: torch.Tensor, n: int = 2, m: int = 4, layout: str = "rows"):
+    """(mask, values, meta) from one pass over W: mask as mask(), the pair as compress()."""
+    dt = _dense_input(W, "W")
+    R, K = W.shape
+    lay = _layout(layout)
+    vshape, mshape = compressed_shapes(R, K, n, m, layout)
+    mask_out = torch.empty((R, K), dtype=torch.bool, device=W.device)
+    values = torch.empty(vshape, dtype=W.dtype, device=W.device)
+    meta = torch.empty(mshape, dtype=torch.int32, device=W.device)
+    _check("nm_mask_compress", lib().nm_mask_compress(_ptr(W), dt, R, K, n, m, lay, _ptr(mask_out),
+                                                      _ptr(values), _ptr(meta), _stream(W)))
+    return mask_out, values, meta
 
 
 def _check_compressed(values: torch.Tensor, meta: torch.Tensor, n: int, m: int, K: int,

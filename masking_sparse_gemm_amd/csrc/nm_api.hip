@@ -199,6 +199,33 @@ nm_status nm_compress(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, i
                                     values, meta, nullptr, static_cast<hipStream_t>(stream)));
 }
 
+nm_status nm_mask_compress(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m,
+                           nm_layout layout, uint8_t* mask, void* values, uint32_t* meta,
+                           nm_stream_t stream) {
+  if (!valid_dtype(dt)) return NM_ERR_DTYPE;
+  nm_status st = check_pattern(n, m);
+  if (st != NM_OK) return st;
+  if ((st = check_shape(R, K, m)) != NM_OK) return st;
+  if ((st = check_layout(layout, K)) != NM_OK) return st;
+  if (layout == NM_LAYOUT_BLOCKED && !blocked_pattern_ok(dt, n, m)) return NM_ERR_UNSUPPORTED;
+  if (missing(W, R * K) || missing(mask, R * K) || missing(values, R * K) ||
+      missing(meta, R * K))
+    return NM_ERR_NULL;
+  if (R * K == 0) return NM_OK;
+  if (!aligned16(W) || !aligned16(mask) || !aligned16(values) || !aligned16(meta))
+    return NM_ERR_ALIGN;
+  const int64_t w_bytes = R * K * elem_bytes(dt), mask_bytes = R * K;
+  const int64_t v_bytes = (int64_t)nm_values_bytes(R, K, n, m, dt, layout);
+  const int64_t m_bytes = (int64_t)nm_meta_bytes(R, K, n, m, layout);
+  if (overlaps(mask, mask_bytes, W, w_bytes) || overlaps(values, v_bytes, W, w_bytes) ||
+      overlaps(meta, m_bytes, W, w_bytes) || overlaps(mask, mask_bytes, values, v_bytes) ||
+      overlaps(mask, mask_bytes, meta, m_bytes) || overlaps(values, v_bytes, meta, m_bytes))
+    return NM_ERR_ALIAS;
+  if ((st = check_device()) != NM_OK) return st;
+  return from_hip(nm::launch_select(W, (int)dt, R, K, n, m, layout == NM_LAYOUT_BLOCKED, values,
+                                    meta, mask, static_cast<hipStream_t>(stream)));
+}
+
 nm_status nm_decompress(const void* values, const uint32_t* meta, nm_dtype dt, int64_t R,
                         int64_t K, int n, int m, nm_layout layout, void* W_out,
                         nm_stream_t stream) {

@@ -295,9 +295,10 @@ struct LaneShape {
 // Selection, value packing and metadata packing of one lane's 16 elements of a block
 // (row l / 4 of the block, elements 16 (l % 4) .. +15 of its step); `live` false writes
 // the zeros of a padding row.  `bits_buf` is the wave's LDS word buffer (used when a
-// lane's metadata bits do not divide 32).
+// lane's metadata bits do not divide 32).  Returns the lane's keep mask (bit e set iff
+// element e of its 16 is kept).
 template <typename E, int N, int M>
-__device__ __forceinline__ void blocked_emit(const uint32_t (&w)[LaneShape<E, N, M>::kWords],
+__device__ __forceinline__ uint32_t blocked_emit(const uint32_t (&w)[LaneShape<E, N, M>::kWords],
                                              bool live, int64_t blk, int lane, uint32_t* bits_buf,
                                              uint32_t* __restrict__ values,
                                              uint32_t* __restrict__ meta) {
@@ -307,6 +308,7 @@ __device__ __forceinline__ void blocked_emit(const uint32_t (&w)[LaneShape<E, N,
 #pragma unroll
   for (int i = 0; i < L::kValWords; ++i) vw[i] = 0;
   uint64_t bits = 0;
+  uint32_t keep16 = 0;
   if constexpr (fast24<E, N, M>()) {
     int pos[L::kGroups][2];
 #pragma unroll
@@ -316,6 +318,7 @@ __device__ __forceinline__ void blocked_emit(const uint32_t (&w)[LaneShape<E, N,
       for (int i = 0; i < 4; ++i) key[i] = Elem<E>::key(word_elem<E>(w, gi * 4 + i));
       top2_of_4(key[0], key[1], key[2], key[3], pos[gi][0], pos[gi][1]);
       bits |= (uint64_t)(pos[gi][0] | (pos[gi][1] << 2)) << (4 * gi);
+      keep16 |= ((1u << pos[gi][0]) | (1u << pos[gi][1])) << (4 * gi);
     }
     pack_kept24<E, L::kGroups>(w, pos, vw);
   } else {
@@ -325,7 +328,9 @@ __device__ __forceinline__ void blocked_emit(const uint32_t (&w)[LaneShape<E, N,
 #pragma unroll
       for (int i = 0; i < M; ++i) key[i] = Elem<E>::key(word_elem<E>(w, gi * M + i));
       int pos[N];
-      kept_positions<N>(keep_bits<N, M>(key), pos);
+      const uint32_t kb = keep_bits<N, M>(key);
+      keep16 |= kb << (M * gi);
+      kept_positions<N>(kb, pos);
 #pragma unroll
       for (int j = 0; j < N; ++j) {
         const int k = gi * N + j;
@@ -355,6 +360,7 @@ __device__ __forceinline__ void blocked_emit(const uint32_t (&w)[LaneShape<E, N,
     __builtin_amdgcn_wave_barrier();
     for (int i = lane; i < L::kBlockMetaWords; i += 64) mblk[i] = buf[i];
   }
+  return keep16;
 }
 
 template <typename E, int N, int M>
@@ -388,6 +394,71 @@ __global__ void __launch_bounds__(kThreads) blocked_select_kernel(const uint32_t
     for (int i = 0; i < L::kWords; ++i) w[i] = 0;
   }
   blocked_emit<E, N, M>(w, live, blk, lane, lds_bits[wave], values, meta);
+}
+
+// Mask, values and metadata in one pass: the compressed pair in the blocked layout and the
+// dense uint8 mask (R x K, row-major).  A wave takes kPer consecutive blocks of one row
+// block (2 when the step count is even), so that it holds 64 kPer mask bytes of each of
+// its 16 rows; they are staged in the wave's LDS slice and stored back as whole row
+// segments (for kPer = 2 each store instruction writes eight full 128-byte lines), since
+// lines assembled from several store instructions cost extra write traffic.
+template <typename E, int N, int M, int kPer>
+__global__ void __launch_bounds__(kThreads) blocked_select_mask_kernel(
+    const uint32_t* __restrict__ W, int64_t R, int64_t K, int64_t blocks,
+    uint32_t* __restrict__ values, uint32_t* __restrict__ meta, uint8_t* __restrict__ mask) {
+  using L = LaneShape<E, N, M>;
+  constexpr int kRowWords = 16 * kPer;  // mask words per row segment
+  __shared__ uint32_t lds_bits[kThreads / 64][L::kShuffle ? 1 : L::kBlockMetaWords];
+  __shared__ __align__(16) uint32_t stage[kThreads / 64][16 * kRowWords];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar math
+  const int64_t blk = ((int64_t)blockIdx.x * (kThreads / 64) + wave) * kPer;
+  if (blk >= blocks) return;  // the whole wave
+  const int64_t steps = K / 64;
+  int64_t rb, st;  // row block and first step of this wave's blocks
+  if (blocks <= 0xFFFFFFFFll) {
+    rb = (uint32_t)blk / (uint32_t)steps;
+    st = (uint32_t)blk - (uint32_t)rb * (uint32_t)steps;
+  } else {
+    rb = blk / steps;
+    st = blk % steps;
+  }
+  const int rr = lane >> 2, q = lane & 3;
+  const int64_t row = 16 * rb + rr;
+  const bool live = row < R;
+  uint32_t w[kPer][L::kWords];
+#pragma unroll
+  for (int p = 0; p < kPer; ++p) {
+    if (live) {
+      load_words<L::kWords>(W + (row * K + 64 * (st + p) + 16 * q) * sizeof(E) / 4, w[p]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < L::kWords; ++i) w[p][i] = 0;
+    }
+  }
+  uint32_t* sw = stage[wave];
+#pragma unroll
+  for (int p = 0; p < kPer; ++p) {
+    const uint32_t keep = blocked_emit<E, N, M>(w[p], live, blk + p, lane, lds_bits[wave],
+                                                values, meta);
+    uint32_t mw[4];  // one byte per element, 1 = kept
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mw[j] = (((keep >> (4 * j)) & 0xFu) * 0x00204081u) & 0x01010101u;
+    *reinterpret_cast<u32x4_t*>(sw + rr * kRowWords + 16 * p + 4 * q) =
+        u32x4_t{mw[0], mw[1], mw[2], mw[3]};
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  constexpr int C = 4 * kPer;  // 16-byte chunks per row segment
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int r2 = i * (64 / C) + lane / C, ch = lane % C;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(sw + (r2 * C + ch) * 4);
+    const int64_t r = 16 * rb + r2;
+    if (r < R)  // padding rows have no mask
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(mask + r * K + 64 * st) + ch);
+  }
 }
 
 // The blocked layout of W's TRANSPOSE (K x R, groups of M along R; R % 64 == 0): block
@@ -748,11 +819,23 @@ hipError_t run_select(const void* W, int64_t R, int64_t K, bool blocked, void* v
   const int64_t elems = R * K;
   if (elems == 0) return hipSuccess;
   const bool want_mask = mask != nullptr, want_compress = values != nullptr;
-  if (blocked) {  // compress only (the mask is a dense array in either layout)
+  if (blocked) {  // compress, with the (dense, row-major) mask in the same pass if asked
     if constexpr (blocked_kernel_exists<E, N, M>()) {
       const int64_t blocks = (R + 15) / 16 * (K / 64);
-      blocked_select_kernel<E, N, M><<<blocks_for(blocks, kThreads / 64), kThreads, 0, s>>>(
-          static_cast<const uint32_t*>(W), R, K, blocks, static_cast<uint32_t*>(values), meta);
+      const uint32_t* w = static_cast<const uint32_t*>(W);
+      uint32_t* v = static_cast<uint32_t*>(values);
+      if (!want_mask) {
+        blocked_select_kernel<E, N, M><<<blocks_for(blocks, kThreads / 64), kThreads, 0, s>>>(
+            w, R, K, blocks, v, meta);
+      } else if ((K / 64) % 2 == 0) {
+        blocked_select_mask_kernel<E, N, M, 2>
+            <<<blocks_for(blocks / 2, kThreads / 64), kThreads, 0, s>>>(w, R, K, blocks, v, meta,
+                                                                        mask);
+      } else {
+        blocked_select_mask_kernel<E, N, M, 1>
+            <<<blocks_for(blocks, kThreads / 64), kThreads, 0, s>>>(w, R, K, blocks, v, meta,
+                                                                    mask);
+      }
       return hipGetLastError();
     }
     return hipErrorInvalidValue;

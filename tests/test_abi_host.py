@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     L = nm.lib()
     for name in header_functions():
         assert hasattr(L, name), name
-    assert L.nm_abi_version() == nm.ABI_VERSION == 8
+    assert L.nm_abi_version() == nm.ABI_VERSION == 9
 
 
 @needs_lib
@@ -358,3 +358,22 @@ def test_binding_has_no_cpu_fallback():
     for f in os.listdir(os.path.join(ROOT, "masking_sparse_gemm_amd", "csrc")):
         text = open(os.path.join(ROOT, "masking_sparse_gemm_amd", "csrc", f)).read()
         assert "nm_oracle" not in text and "nmo_" not in text, f
+
+
+@needs_lib
+def test_mask_compress_argument_rules():
+    L = nm.lib()
+    st = lambda code: nm.STATUS[code]
+    mc = lambda **kw: L.nm_mask_compress(
+        kw.get("W", FAKE), kw.get("dt", nm.NM_BF16), kw.get("R", 64), kw.get("K", 128), 2, 4,
+        kw.get("layout", 0), kw.get("mask", FAKE + 0x100000), kw.get("values", FAKE + 0x200000),
+        kw.get("meta", FAKE + 0x300000), None)
+    assert st(mc(dt=6)) == "dtype"
+    assert st(mc(K=130)) == "shape"
+    assert st(mc(layout=1, K=96)) == "layout"
+    assert st(mc(mask=0)) == "null"
+    assert st(mc(values=FAKE + 0x200008)) == "align"
+    assert st(mc(mask=FAKE)) == "alias"                       # the mask over W
+    assert st(mc(values=FAKE + 0x100000 + 64 * 64)) == "alias"  # values inside the mask
+    assert st(mc(meta=FAKE + 0x200000 + 16)) == "alias"       # meta inside the values
+    assert st(mc(R=0)) == "ok"
