@@ -1,22 +1,28 @@
 // nm_compress.hip -- mask, compress and decompress kernels (gfx950).
 //
-// These passes move bytes and compare integers; they are bound by HBM bandwidth,
-// not by arithmetic.  The fast ("flat") kernels treat W as one stream of 16-byte
-// units: a lane loads one unit (8 x 16-bit or 4 x fp32 elements, or 8 fp32 for
-// M = 8) with a single coalesced 16-byte load, selects its groups in registers,
-// writes its kept values with one 4/8/16-byte store and packs its metadata bits
-// into 32-bit words together with its neighbours: wave shuffles when a whole
-// number of lanes fills a word, a per-wave LDS bit buffer otherwise.  The flat
-// kernels need every row to hold a whole number of units and of metadata words,
-// so that rows concatenate into one stream; any other shape uses the simple
-// per-group / per-word kernels at the bottom, which make no such assumption.
+// These passes move bytes and compare integers; no matrix core is involved.  Their
+// roofline is HBM bandwidth, but the selection is enough vector work to bound them when it
+// is written naively, so it is kept lean (a top-two network for 2:4, byte permutes for the
+// kept values, wave-uniform index math).  The fast ("flat") kernels treat W as one stream
+// of 16-byte units: a lane loads one unit (8 x 16-bit or 4 x fp32 elements, or 8 fp32 for
+// M = 8) with a single coalesced 16-byte load, selects its groups in registers, writes its
+// kept values with one 4/8/16-byte store and packs its metadata bits into 32-bit words
+// together with its neighbours: wave shuffles when a whole number of lanes fills a word, a
+// per-wave LDS bit buffer otherwise.  The flat kernels need every row to hold a whole
+// number of units and of metadata words, so that rows concatenate into one stream; any
+// other shape uses the simple per-group / per-word kernels at the bottom, which make no
+// such assumption.
 //
 // Formats ("[리뷰] Accelerating Sparse Deep Neural Networks", section
 // "2:4 Sparsity의 benefits"): values hold the N kept elements of each group in
 // ascending position order; metadata field f = g*N + j of a row holds position
 // j of group g in b = log2(M) bits at bit f*b of the row, least significant first.
 // The blocked layout stores the same values and bits in blocks of 16 rows x 64
-// columns (include/nm.h); its kernels take one block per wave.
+// columns (include/nm.h).  Its kernels give each wave one block, or two consecutive
+// blocks where a dense row segment would otherwise be half a cache line, and stage dense
+// outputs (mask, decompressed weight) through LDS so that every store instruction writes
+// whole row segments: lines assembled from several store instructions measured extra HBM
+// write traffic.
 #include <utility>
 
 #include "nm_device.h"

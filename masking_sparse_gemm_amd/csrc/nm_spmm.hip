@@ -5,30 +5,33 @@
 // operand and a dense K x T activation matrix as the second; the result is dense.
 //
 // 2:4 and 1:2 with 16-bit inputs run on gfx950's structured-sparse matrix cores
-// (v_smfmac_f32_16x16x64_{bf16,f16}).  That instruction takes, per lane, eight
-// stored values covering sixteen consecutive K positions of one row (four groups
-// of four) plus a 16-bit index whose 2-bit fields give each value's position in
-// its group, least significant field first -- exactly one half-word of this
-// library's 2:4 metadata -- so compressed rows feed the matrix cores with no
-// conversion, and the hardware gathers the matching rows of X.  1:2 metadata (one
-// bit per value) is widened to that nibble form in registers: pairs of 1:2 groups
-// are 2:4 groups with one value in each half.
+// (v_smfmac_f32_32x32x32_{bf16,f16}, and v_smfmac_f32_16x16x64 for small tiles).  The
+// instruction takes, per lane, stored values of one row with an index word whose 2-bit
+// fields give each value's position in its group of four, least significant first --
+// exactly this library's 2:4 metadata -- so compressed rows feed the matrix cores with no
+// conversion and the hardware gathers the matching rows of X.  1:2 metadata (one bit per
+// value) is widened to that nibble form in registers: pairs of 1:2 groups are 2:4 groups
+// with one value in each half.
 //
-// Tiling.  A workgroup owns a BM x BN tile of Y and walks K in steps of 128.  X
-// tiles are staged through LDS (double-buffered, one barrier per step) and read
-// back with ds_read_b64_tr_b16, which hands each lane four consecutive K rows of
-// one column -- the K-major order the matrix-core B operand needs -- from the
-// row-major tile.  Compressed values and metadata go straight from global memory
-// to registers, one step ahead.  Inside a 128-wide K step the contraction order
-// is permuted so that lane group q of the instruction covers K [32q, 32q+32): its
-// stored values are then 32 contiguous bytes and its metadata one 32-bit word
-// whose low and high halves serve the two instructions of the step through the
-// instruction's index-half selector.  The accumulators are fp32; the result is
-// rounded once to the output type (round to nearest even).
-//
-// Every other pattern, fp32, and shapes the tiled kernel does not take (K not a
-// multiple of 128, T not a multiple of 8) use a plain LDS-tiled kernel that
-// expands the compressed rows to fp32 and accumulates with fp32 FMAs.
+// Kernels, chosen per shape by an estimate of rounds of workgroups times tile time:
+//  * smfmac_ws_spmm_kernel (256 x 128 tiles, the large shapes): wave-specialised.  Four
+//    producer waves bring every operand of a 64-wide K step (X rows, compressed values,
+//    metadata) into a 4-stage LDS ring with direct global -> LDS loads; four consumer
+//    waves (128 x 64 outputs each) read fragments from LDS -- X through
+//    ds_read_b64_tr_b16, which hands each lane consecutive K rows of one column, the
+//    K-major order of the B operand -- and issue the smfmac.  One barrier per step.
+//  * smfmac32_spmm_kernel (256 x 256 tiles): the same fragment code with every wave
+//    issuing its own loads, for short K; smfmac_spmm_kernel (128 x 128 tiles,
+//    v_smfmac_f32_16x16x64) for small shapes.
+//  * mfma48_ws_spmm_kernel: 4:8 on the dense matrix cores, each 4:8 group expanded in
+//    registers with byte permutes.
+//  * smfmac_i8_ws_spmm_kernel: 2:4 int8 (exact int32) and fp8 (fp32 accumulation) on
+//    the 32x32x64 8-bit instructions.
+//  * generic_spmm_kernel: every other pattern, fp32, and shapes the tiled kernels do not
+//    take; it expands the compressed rows to fp32 in LDS and accumulates with fp32 FMAs.
+// The blocked layout (include/nm.h) makes every direct load of compressed values or
+// metadata one contiguous run; the row layout is accepted by the same kernels at a lower
+// rate.  Accumulators are fp32 (int32 for int8) and rounded once to the output type.
 #include <atomic>
 #include <cstdlib>
 #include <type_traits>
