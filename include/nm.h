@@ -2,17 +2,18 @@
  * nm.h -- C ABI of libnm: N:M magnitude masking, compression and the
  * compressed-sparse x dense product on AMD Instinct MI355X (gfx950).
  *
- * Plain C; no HIP or PyTorch types appear in the signatures.  Every pointer
- * argument is a DEVICE pointer to memory the caller owns; the library
- * allocates nothing and keeps no state besides a once-initialised record of
- * which devices it has checked.  Calls are asynchronous on `stream` (a
+ * Plain C; no HIP or PyTorch types appear in the signatures.  Pointer arguments
+ * are DEVICE pointers to memory the caller owns, except where a declaration says
+ * host memory (nm_perm_search's permutation, nm_check_meta's metadata); the
+ * library allocates no device memory and keeps no state besides a
+ * once-initialised record of which devices it has checked.  Calls are asynchronous on `stream` (a
  * hipStream_t passed as void*, NULL = the default stream): NM_OK means the
  * work was enqueued, and a fault inside a kernel surfaces at the caller's next
  * synchronisation.  Arguments are validated before anything is launched; on
  * any error nothing is written.  Outputs must not alias inputs.
  *
- * Element types: nm_mask, nm_compress, nm_decompress and nm_spmm take NM_F32, NM_F16,
- * NM_BF16, NM_I8 and NM_FP8; the SR-STE and transposable-mask calls take the three
+ * Element types: nm_mask, nm_compress, nm_mask_compress, nm_decompress and nm_spmm take
+ * NM_F32, NM_F16, NM_BF16, NM_I8 and NM_FP8; the SR-STE and transposable-mask calls take the three
  * 16/32-bit floating-point types only.
  *
  * Dense arrays (row-major, no padding between rows):
