@@ -57,6 +57,7 @@ WORKLOADS = {
     "sweep_f16_1_2": (["sweep_f16"], (1, 2)),
     "sweep_f16_4_8": (["sweep_f16"], (4, 8)),
     "toy_f32": (["toy_f32"], (2, 4)),
+    "sweep_f32_2_4": (["sweep_f32"], (2, 4)),
 }
 
 
@@ -358,7 +359,9 @@ def main() -> int:
     achieved = F_alg / spmm_t / 1e12
     peak = PEAK_MFMA_TFLOPS[dtype]
     roofline = {"bound": "mfma",
-                "kernel": "nm_spmm (structured-sparse matrix cores)" if n * 2 == m else "nm_spmm",
+                "kernel": ("nm_spmm (structured-sparse matrix cores)"
+                           if n * 2 == m and dtype != "f32" else
+                           "nm_spmm (dense matrix cores on expanded tiles)"),
                 "achieved": round(achieved, 1), "peak": peak,
                 "unit": "TOP/s" if dtype == "i8" else "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": None,
@@ -400,8 +403,6 @@ def main() -> int:
         # hipBLASLt through torch.matmul on the decompressed weight, same dtype and shapes
         ts = []
         for d in mats:
-            if d["dtype"] == "f32":
-                continue
             A, B = d["dec"], d["Xd"]
             # int8: torch._int_mm (int8 x int8 -> int32); fp8: torch._scaled_mm (unit scales,
             # X column-major as it requires, bf16 out), where this PyTorch build has them

@@ -27,8 +27,10 @@
 //    registers with byte permutes.
 //  * smfmac_i8_ws_spmm_kernel: 2:4 int8 (exact int32) and fp8 (fp32 accumulation) on
 //    the 32x32x64 8-bit instructions.
-//  * generic_spmm_kernel: every other pattern, fp32, and shapes the tiled kernels do not
-//    take; it expands the compressed rows to fp32 in LDS and accumulates with fp32 FMAs.
+//  * expand_f32_spmm_kernel: fp32, any pattern; the compressed rows are expanded in LDS and
+//    multiplied on the dense fp32 matrix cores (v_mfma_f32_32x32x2_f32).
+//  * generic_spmm_kernel: every other pattern and shapes the tiled kernels do not take; it
+//    expands the compressed rows to fp32 in LDS and accumulates with fp32 FMAs.
 // The blocked layout (include/nm.h) makes every direct load of compressed values or
 // metadata one contiguous run; the row layout is accepted by the same kernels at a lower
 // rate.  Accumulators are fp32 (int32 for int8) and rounded once to the output type.
@@ -50,6 +52,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x16_t __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x16_t __attribute__((ext_vector_type(16)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
 
@@ -1773,6 +1776,206 @@ __global__ void __launch_bounds__(256) generic_spmm_kernel(const void* __restric
   }
 }
 
+// ===========================================================================
+// fp32, any N:M: the compressed rows are expanded in LDS (zeros where pruned, as in the
+// generic kernel) and multiplied on the dense fp32 matrix cores, v_mfma_f32_32x32x2_f32.
+// gfx950 has no structured-sparse fp32 instruction, so this is the dense product of the
+// decompressed tile, reading only the compressed pair.  The fp32 matrix cores need 16x the
+// time of the 16-bit ones per flop, so the loads are a small share of a step and a plain
+// register prefetch hides them: the loads of step s+1 are issued before step s's matrix
+// instructions and written to LDS after them.
+// Workgroup: 128 x 128 outputs, four waves of 64 x 64 (2 x 2 blocks of 32 x 32), K step 32.
+// Instruction i (0..15) of a step pairs K 16q + i in lane half q (the contraction order
+// inside a step is free), so a lane's A operands of the step are one 16-float run of its
+// row, four ds_read_b128, and each B operand is one ds_read_b32.  A rows are padded to 36
+// floats (conflict-free 16-byte reads); X rows 16..31 swap adjacent 32-column blocks, so
+// the two lane halves of a B read hit opposite halves of the 64 banks.
+// ===========================================================================
+constexpr int kEM = 128, kEN = 128, kEK = 32;
+constexpr int kEAS = kEK + 4;
+constexpr int kEStage = kEM * kEAS + kEK * kEN;  // floats per stage
+
+__device__ __forceinline__ int ex_col(int c, int kk) {  // physical column of X tile entry
+  return (((c >> 5) ^ ((kk >> 4) & 1)) << 5) | (c & 31);
+}
+
+template <int YT, int N, int M, bool kBlocked>
+__global__ void __launch_bounds__(256)
+    expand_f32_spmm_kernel(const float* __restrict__ values, const uint32_t* __restrict__ meta,
+                           const float* __restrict__ X, void* __restrict__ Y, int64_t R,
+                           int64_t K, int64_t T, int64_t tiles_n) {
+  constexpr int b = meta_bits(M);
+  constexpr int kGPS = kEK / M;              // groups per row and step
+  constexpr int kItems = kEM * kGPS / 256;   // (row, group) items per thread and step
+  constexpr int64_t V = 64 / M * N;          // blocked layout: values per row per 64 of K
+  static_assert(kItems * 256 == kEM * kGPS, "whole items per thread");
+  extern __shared__ __attribute__((aligned(16))) float ex_smem[];  // two stages of A, X
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * kEM;
+  const int64_t t0 = (int64_t)(blockIdx.x % tiles_n) * kEN;
+  const int64_t gpr = K / M, wpr = (gpr * N * b + 31) / 32;
+
+  // prefetch registers: X pieces, each item's values and the (one or two) metadata words
+  // holding its fields with the fields' bit offset; nothing fetched is used before the
+  // stash, so the loads stay in flight across the step's matrix instructions
+  float4_t xr[4];
+  float vr[kItems][N];
+  uint32_t mw0[kItems], mw1[kItems], msh[kItems];
+  auto fetch = [&](int64_t k0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int idx = j * 256 + tid, kk = idx >> 5, c = 4 * (idx & 31);
+      const int64_t k = k0 + kk, col = t0 + c;
+      xr[j] = (k < K && col < T) ? *reinterpret_cast<const float4_t*>(X + k * T + col)
+                                 : float4_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int it = 0; it < kItems; ++it) {
+      const int i = it * 256 + tid, r = i / kGPS, gl = i % kGPS;
+      const int64_t row = m0 + r, g = k0 / M + gl;
+#pragma unroll
+      for (int j = 0; j < N; ++j) vr[it][j] = 0.f;
+      mw0[it] = mw1[it] = msh[it] = 0u;
+      if (row < R && g < gpr) {
+        // the group's N fields are consecutive in both layouts (a 64-wide step of the blocked
+        // layout holds whole groups): first value index and first metadata bit
+        const int64_t f0 = g * N;
+        int64_t vi, bit;
+        if constexpr (kBlocked) {
+          const int64_t rr = ((row >> 4) * (K / 64) + f0 / V) * 16 + (row & 15);
+          vi = rr * V + f0 % V;
+          bit = (rr * V + f0 % V) * b;
+        } else {
+          vi = row * (gpr * N) + f0;
+          bit = row * wpr * 32 + f0 * b;
+        }
+#pragma unroll
+        for (int j = 0; j < N; ++j) vr[it][j] = values[vi + j];
+        mw0[it] = meta[bit / 32];
+        if ((bit % 32) + N * b > 32) mw1[it] = meta[bit / 32 + 1];
+        msh[it] = (uint32_t)(bit % 32);
+      }
+    }
+  };
+  auto stash = [&](int stage) {
+    float* As = ex_smem + stage * kEStage;
+    float* Xs = As + kEM * kEAS;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int idx = j * 256 + tid, kk = idx >> 5, c = 4 * (idx & 31);
+      *reinterpret_cast<float4_t*>(Xs + kk * kEN + ex_col(c, kk)) = xr[j];
+    }
+#pragma unroll
+    for (int it = 0; it < kItems; ++it) {
+      const int i = it * 256 + tid, r = i / kGPS, gl = i % kGPS;
+      const uint32_t fields = (uint32_t)((((uint64_t)mw1[it] << 32) | mw0[it]) >> msh[it]);
+      float o[M];
+#pragma unroll
+      for (int e = 0; e < M; ++e) o[e] = 0.f;
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        const int p = (int)((fields >> (j * b)) & ((1u << b) - 1u));
+#pragma unroll
+        for (int e = 0; e < M; ++e) o[e] = (p == e) ? vr[it][j] : o[e];
+      }
+      float* dst = As + r * kEAS + gl * M;
+      if constexpr (M == 2) {
+        *reinterpret_cast<float2_t*>(dst) = float2_t{o[0], o[1]};
+      } else {
+#pragma unroll
+        for (int e = 0; e < M; e += 4)
+          *reinterpret_cast<float4_t*>(dst + e) = float4_t{o[e], o[e + 1], o[e + 2], o[e + 3]};
+      }
+    }
+  };
+
+  const int q = lane >> 5, lr = lane & 31, wm = wave >> 1, wn = wave & 1;
+  int a_off[2], b_off[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    a_off[f] = (wm * 64 + f * 32 + lr) * kEAS + 16 * q;
+    b_off[f] = 16 * q * kEN + ex_col(wn * 64 + f * 32 + lr, 16 * q);
+  }
+  float16v_t acc[2][2];
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn) acc[fm][fn] = float16v_t{};
+
+  // one barrier per step: step s+1 is written into the other stage while step s's matrix
+  // instructions run; that stage was last read in step s-1, before the previous barrier
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  int stage = 0;
+  for (int64_t k0 = 0; k0 < K; k0 += kEK) {
+    const bool more = k0 + kEK < K;
+    if (more) fetch(k0 + kEK);
+    const float* As = ex_smem + stage * kEStage;
+    const float* Xs = As + kEM * kEAS;
+    float4_t a[2][4];
+#pragma unroll
+    for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        a[fm][j] = *reinterpret_cast<const float4_t*>(As + a_off[fm] + 4 * j);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float bv[2];
+#pragma unroll
+      for (int fn = 0; fn < 2; ++fn) bv[fn] = Xs[b_off[fn] + i * kEN];
+#pragma unroll
+      for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < 2; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[fm][i >> 2][i & 3], bv[fn],
+                                                             acc[fm][fn], 0, 0, 0);
+    }
+    if (more) stash(stage ^ 1);
+    __syncthreads();
+    stage ^= 1;
+  }
+  // accumulator layout: lane (q, lr) of block (fm, fn) holds column lr and, in register e,
+  // row 8 (e / 4) + 4 q + e % 4
+#pragma unroll
+  for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn) {
+      const int64_t col = t0 + wn * 64 + fn * 32 + lr;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = m0 + wm * 64 + fm * 32 + 8 * (e >> 2) + 4 * q + (e & 3);
+        if (row < R && col < T) store_from_f32<YT>(Y, row * T + col, acc[fm][fn][e]);
+      }
+    }
+}
+
+template <bool kBlocked>
+hipError_t run_expand_f32(const void* values, const uint32_t* meta, int64_t R, int64_t K, int n,
+                          int m, const void* X, int64_t T, void* Y, hipStream_t s) {
+  const int64_t tiles_n = (T + kEN - 1) / kEN, tiles = (R + kEM - 1) / kEM * tiles_n;
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  const float* v = static_cast<const float*>(values);
+  const float* x = static_cast<const float*>(X);
+  constexpr size_t lds = 2 * kEStage * sizeof(float);
+#define NM_E(NN, MM)                                                                       \
+  if (n == NN && m == MM) {                                                                \
+    auto kernel = expand_f32_spmm_kernel<kF32, NN, MM, kBlocked>;                          \
+    static const hipError_t attr =                                                         \
+        hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),                         \
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);         \
+    if (attr != hipSuccess) return attr;                                                   \
+    kernel<<<(unsigned)tiles, 256, lds, s>>>(v, meta, x, Y, R, K, T, tiles_n);             \
+    return hipGetLastError();                                                              \
+  }
+  NM_E(1, 2) NM_E(2, 2)
+  NM_E(1, 4) NM_E(2, 4) NM_E(3, 4) NM_E(4, 4)
+  NM_E(1, 8) NM_E(2, 8) NM_E(3, 8) NM_E(4, 8)
+  NM_E(5, 8) NM_E(6, 8) NM_E(7, 8) NM_E(8, 8)
+#undef NM_E
+  return hipErrorInvalidValue;
+}
+
 __global__ void zero_fill_kernel(uint32_t* __restrict__ p, int64_t words, int64_t tail_halves) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < words) p[i] = 0u;
@@ -1995,8 +2198,13 @@ hipError_t launch_spmm(const void* values, const uint32_t* meta, int64_t R, int6
     return yf32 ? run_generic_layout<kFP8, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s)
                 : run_generic_layout<kFP8, kBF16>(values, meta, R, K, n, m, blocked, X, T, Y, s);
   }
-  if (dt == kF32)
+  if (dt == kF32) {
+    // the matrix-core kernel reads X in 16-byte pieces: rows of whole 16 bytes
+    if (T % 4 == 0)
+      return blocked ? run_expand_f32<true>(values, meta, R, K, n, m, X, T, Y, s)
+                     : run_expand_f32<false>(values, meta, R, K, n, m, X, T, Y, s);
     return run_generic_layout<kF32, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s);
+  }
   if (dt == kBF16)
     return y_dt == kF32
                ? run_generic_layout<kBF16, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s)

@@ -250,4 +250,7 @@ WORKLOADS = {
     # N:M sweep: fp16 4096 x 4096 ~Laplace(0, 0.05), activations 4096 x 8192 ~N(0,1)
     "sweep_f16": Workload("sweep_f16", 4096, 4096, 8192, "f16", Dist("laplace", 0, 0.05),
                           Dist("normal", 1), patterns=((1, 2), (2, 4), (4, 8))),
+    # the same sweep in fp32 (the fp32 product path at a size that fills the device)
+    "sweep_f32": Workload("sweep_f32", 4096, 4096, 8192, "f32", Dist("laplace", 0, 0.05),
+                          Dist("normal", 1), patterns=((1, 2), (2, 4), (4, 8))),
 }

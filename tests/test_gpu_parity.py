@@ -238,11 +238,17 @@ def test_spmm_every_tile_shape(tile, dtype, n, m, layout, monkeypatch):
         check_product(Y, y_ref, s, K // m * n, dtype, "f32", f"tile {tile} {R}x{K}x{T} {layout}")
 
 
-@pytest.mark.parametrize("n,m", [(2, 4), (1, 2), (4, 8), (1, 4)])
+# fp32: T % 4 == 0 takes the matrix-core kernel (any pattern; K tails inside its 32-wide
+# step: K = 200, 72, 8, 40), the rest the generic kernel (T = 13)
+F32_SHAPES = PRODUCT_SHAPES + [(70, 200, 132), (129, 72, 260), (1, 8, 4), (300, 320, 4)]
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (1, 2), (4, 8), (1, 4), (3, 4), (2, 2), (1, 8), (6, 8),
+                                 (8, 8)])
 @pytest.mark.parametrize("layout", ["rows", "blocked"])
 def test_spmm_f32_elementwise(n, m, layout):
     rng = np.random.default_rng(31)
-    for R, K, T in PRODUCT_SHAPES:
+    for R, K, T in F32_SHAPES:
         if K % m or (layout == "blocked" and K % 64):
             continue
         W = rng.standard_normal((R, K)).astype(np.float32)
@@ -253,8 +259,8 @@ def test_spmm_f32_elementwise(n, m, layout):
         check_product(Y, y_ref, s, K // m * n, "f32", "f32", f"{R}x{K}x{T} {layout}")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("n,m", [(2, 4), (1, 2)])
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("n,m", [(2, 4), (1, 2), (3, 8)])
 @pytest.mark.parametrize("layout", ["rows", "blocked"])
 def test_spmm_identity_is_exact(dtype, n, m, layout):
     """X = I: every output is one product by 1, so Y equals the masked weight bitwise."""
@@ -318,7 +324,7 @@ def sample_points(rng, R, T, count=1500):
 
 
 @pytest.mark.parametrize("name", ["toy_f32", "bert_ffn", "resnet_conv3x3", "llama_up", "llama_down",
-                                  "sweep_f16"])
+                                  "sweep_f16", "sweep_f32"])
 def test_spmm_full_workloads_sampled(name):
     """Full-size products, launched exactly as the benchmark launches them; the oracle
     computes sampled outputs one by one."""
