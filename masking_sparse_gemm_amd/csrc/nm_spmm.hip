@@ -1144,7 +1144,8 @@ typedef int int4v_t __attribute__((ext_vector_type(4)));
 typedef int int2v_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) int2v_t lds_int2v_t;
 
-template <bool kFp8, int YT, int BM, int BN, int CWAVES_M, int CWAVES_N, int PWAVES, int STAGES>
+template <bool kFp8, bool kBlocked, int YT, int BM, int BN, int CWAVES_M, int CWAVES_N,
+          int PWAVES, int STAGES>
 __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
     smfmac_i8_ws_spmm_kernel(const uint8_t* __restrict__ values, const uint32_t* __restrict__ meta,
                              const uint8_t* __restrict__ X, void* __restrict__ Y, int R, int K,
@@ -1179,24 +1180,42 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
       x_src[j] = (int64_t)r * T + col;
       x_dst[j] = (uint32_t)(w1k * 1024);
     }
+    // A stage holds, per 16-row group, the values as [64-wide half][row][32 bytes] (1 KB)
+    // and the metadata as [half][row][8 bytes] (256 bytes).  In the blocked layout both are
+    // one contiguous run per group and step; in the row layout lane l fetches row
+    // (l % 32) / 2, half l / 32, 16-byte (values) or 4-byte (metadata) piece l % 2.
     int64_t a_src[TL::kALoads], m_src[TL::kMLoads];
     uint32_t a_dst[TL::kALoads], m_dst[TL::kMLoads];
+    const int lrow = (lane & 31) >> 1, lh = lane >> 5, lp = lane & 1;
 #pragma unroll
     for (int j = 0; j < TL::kALoads; ++j) {
       const int b16 = j * TL::kProducers + pw;  // row group of the tile
-      int g = (m0 >> 4) + b16;
-      g = g < last_g ? g : last_g;  // rows past the matrix: any valid group
-      a_src[j] = (int64_t)g * steps64 * 512 + 16 * lane;
+      if constexpr (kBlocked) {
+        int g = (m0 >> 4) + b16;
+        g = g < last_g ? g : last_g;  // rows past the matrix: any valid group
+        a_src[j] = (int64_t)g * steps64 * 512 + 16 * lane;
+      } else {
+        int row = m0 + 16 * b16 + lrow;
+        row = row < R ? row : R - 1;  // rows past the matrix: any valid row
+        a_src[j] = (int64_t)row * (K / 2) + 32 * lh + 16 * lp;
+      }
       a_dst[j] = (uint32_t)(TL::kXBytes + b16 * 1024);
     }
 #pragma unroll
     for (int j = 0; j < TL::kMLoads; ++j) {
       const int b16 = j * TL::kProducers + pw;
-      int g = (m0 >> 4) + b16;
-      g = g < last_g ? g : last_g;
-      m_src[j] = (int64_t)g * steps64 * 128 + 4 * lane;
+      if constexpr (kBlocked) {
+        int g = (m0 >> 4) + b16;
+        g = g < last_g ? g : last_g;
+        m_src[j] = (int64_t)g * steps64 * 128 + 4 * lane;
+      } else {
+        int row = m0 + 16 * b16 + lrow;
+        row = row < R ? row : R - 1;
+        m_src[j] = (int64_t)row * (K / 8) + 8 * lh + 4 * lp;  // K / 32 words per row
+      }
       m_dst[j] = (uint32_t)(TL::kXBytes + TL::kABytes + b16 * 256);
     }
+    constexpr int64_t kAStep = kBlocked ? 1024 : 64, kMStep = kBlocked ? 256 : 16;
     const uint8_t* mg = reinterpret_cast<const uint8_t*>(meta);
     auto issue_step = [&](int step) {
       step = step < last_step ? step : last_step;  // past the end: re-read the last step
@@ -1206,10 +1225,10 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
       for (int j = 0; j < TL::kXLoads; ++j) global_to_lds<16>(X + x_src[j] + kx, st + x_dst[j]);
 #pragma unroll
       for (int j = 0; j < TL::kALoads; ++j)
-        global_to_lds<16>(values + a_src[j] + (int64_t)step * 1024, st + a_dst[j]);
+        global_to_lds<16>(values + a_src[j] + step * kAStep, st + a_dst[j]);
 #pragma unroll
       for (int j = 0; j < TL::kMLoads; ++j)
-        global_to_lds<4>(mg + m_src[j] + (int64_t)step * 256, st + m_dst[j]);
+        global_to_lds<4>(mg + m_src[j] + step * kMStep, st + m_dst[j]);
     };
 #pragma unroll
     for (int k = 0; k < kStages - 1; ++k) issue_step(k);
@@ -1314,12 +1333,12 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
 
 int xcd_count();
 
-template <bool kFp8, int YT>
+template <bool kFp8, bool kBlocked, int YT>
 hipError_t run_smfmac_8bit(const void* values, const uint32_t* meta, int64_t R, int64_t K,
                            const void* X, int64_t T, void* Y, hipStream_t s) {
   constexpr int BM = 256, BN = 128, ST = 4;
   using TL = WsI8Tile<BM, BN, 2, 2, 4, ST>;
-  auto kernel = smfmac_i8_ws_spmm_kernel<kFp8, YT, BM, BN, 2, 2, 4, ST>;
+  auto kernel = smfmac_i8_ws_spmm_kernel<kFp8, kBlocked, YT, BM, BN, 2, 2, 4, ST>;
   const size_t lds = (size_t)ST * TL::kStageBytes;
   static const hipError_t attr =
       hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
@@ -2181,20 +2200,25 @@ hipError_t launch_spmm(const void* values, const uint32_t* meta, int64_t R, int6
         static_cast<uint32_t*>(Y), words, tail_halves);
     return hipGetLastError();
   }
+  // the 8-bit matrix-core kernel: 2:4, either layout, K a multiple of 128 (two blocked
+  // steps), T a multiple of 16 (16-byte X loads), 32-bit X offsets
+  const bool tiled_8bit = pat24 && K % kI8KStep == 0 && T % 16 == 0 && R < (1 << 30) &&
+                          T < (1 << 30) && K < (1 << 30);
   if (dt == kI8) {
-    // the matrix-core kernel: 2:4, blocked layout, K a multiple of 128 (two blocked steps),
-    // T a multiple of 16 (16-byte X loads), 32-bit byte offsets
-    if (pat24 && blocked && K % kI8KStep == 0 && T % 16 == 0 && R < (1 << 30) &&
-        T < (1 << 30) && K < (1 << 30))
-      return run_smfmac_8bit<false, kI32>(values, meta, R, K, X, T, Y, s);
+    if (tiled_8bit)
+      return blocked ? run_smfmac_8bit<false, true, kI32>(values, meta, R, K, X, T, Y, s)
+                     : run_smfmac_8bit<false, false, kI32>(values, meta, R, K, X, T, Y, s);
     return run_generic_layout<kI8, kI32>(values, meta, R, K, n, m, blocked, X, T, Y, s);
   }
   if (dt == kFP8) {  // the same kernel on the fp8 instruction, fp32 accumulation
     const bool yf32 = y_dt == kF32;
-    if (pat24 && blocked && K % kI8KStep == 0 && T % 16 == 0 && R < (1 << 30) &&
-        T < (1 << 30) && K < (1 << 30))
-      return yf32 ? run_smfmac_8bit<true, kF32>(values, meta, R, K, X, T, Y, s)
-                  : run_smfmac_8bit<true, kBF16>(values, meta, R, K, X, T, Y, s);
+    if (tiled_8bit) {
+      if (blocked)
+        return yf32 ? run_smfmac_8bit<true, true, kF32>(values, meta, R, K, X, T, Y, s)
+                    : run_smfmac_8bit<true, true, kBF16>(values, meta, R, K, X, T, Y, s);
+      return yf32 ? run_smfmac_8bit<true, false, kF32>(values, meta, R, K, X, T, Y, s)
+                  : run_smfmac_8bit<true, false, kBF16>(values, meta, R, K, X, T, Y, s);
+    }
     return yf32 ? run_generic_layout<kFP8, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s)
                 : run_generic_layout<kFP8, kBF16>(values, meta, R, K, n, m, blocked, X, T, Y, s);
   }
