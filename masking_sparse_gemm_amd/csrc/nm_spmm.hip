@@ -25,8 +25,8 @@
 //    v_smfmac_f32_16x16x64) for small shapes.
 //  * mfma48_ws_spmm_kernel: 4:8 on the dense matrix cores, each 4:8 group expanded in
 //    registers with byte permutes.
-//  * smfmac_i8_ws_spmm_kernel: 2:4 int8 (exact int32) and fp8 (fp32 accumulation) on
-//    the 32x32x64 8-bit instructions.
+//  * smfmac_i8_ws_spmm_kernel: 2:4 and 1:2 int8 (exact int32) and fp8 (fp32 accumulation)
+//    on the 32x32x64 8-bit instructions.
 //  * expand_f32_spmm_kernel: fp32, any pattern; the compressed rows are expanded in LDS and
 //    multiplied on the dense fp32 matrix cores (v_mfma_f32_32x32x2_f32).
 //  * generic_spmm_kernel: every other pattern and shapes the tiled kernels do not take; it
@@ -1093,7 +1093,7 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
 }
 
 // ===========================================================================
-// int8 2:4 on v_smfmac_i32_32x32x64_i8 (exact int32 sums).  Lane l of the instruction
+// int8 2:4 and 1:2 on v_smfmac_i32_32x32x64_i8 (exact int32 sums).  Lane l of the instruction
 // supplies row l % 32 of A as 16 stored bytes covering logical K [32 (l/32), +32) (8 groups,
 // one 32-bit index word of 2-bit positions), and column l % 32 of B as 32 bytes, K
 // {16 (l/32) + 0..15} and {32 + 16 (l/32) + 0..15}; the accumulator has the dense 32 x 32
@@ -1102,9 +1102,11 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
 // (j = 0..7), so with even lanes addressing 8 columns of 8 consecutive K rows and odd
 // lanes the next 8 columns of the same rows, lane i gets 8 consecutive K of column i.
 // One pipeline step is 128 of K: two blocked-layout steps, i.e. one contiguous 1 KB of
-// values and 256 bytes of metadata per 16 rows, and 128 rows of X.  Wave-specialised as
+// values and 256 bytes of metadata per 16 rows (128 for 1:2), and 128 rows of X; the row
+// layout lands the same LDS image from 64-byte pieces of each row.  Wave-specialised as
 // smfmac_ws_spmm_kernel: producer waves issue the direct loads (4-stage ring, one barrier
-// per step), each of four consumer waves owns 128 x 64 outputs (4 x 2 fragments).
+// per step), each of four consumer waves owns 128 x 64 outputs (4 x 2 fragments).  The
+// fp8 instantiation (v_smfmac_f32_32x32x64_fp8_fp8) accumulates in fp32.
 // ===========================================================================
 constexpr int kI8KStep = 128;
 
@@ -1144,8 +1146,8 @@ typedef int int4v_t __attribute__((ext_vector_type(4)));
 typedef int int2v_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) int2v_t lds_int2v_t;
 
-template <bool kFp8, bool kBlocked, int YT, int BM, int BN, int CWAVES_M, int CWAVES_N,
-          int PWAVES, int STAGES>
+template <bool kFp8, bool kBlocked, bool kPat12, int YT, int BM, int BN, int CWAVES_M,
+          int CWAVES_N, int PWAVES, int STAGES>
 __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
     smfmac_i8_ws_spmm_kernel(const uint8_t* __restrict__ values, const uint32_t* __restrict__ meta,
                              const uint8_t* __restrict__ X, void* __restrict__ Y, int R, int K,
@@ -1181,9 +1183,10 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
       x_dst[j] = (uint32_t)(w1k * 1024);
     }
     // A stage holds, per 16-row group, the values as [64-wide half][row][32 bytes] (1 KB)
-    // and the metadata as [half][row][8 bytes] (256 bytes).  In the blocked layout both are
-    // one contiguous run per group and step; in the row layout lane l fetches row
-    // (l % 32) / 2, half l / 32, 16-byte (values) or 4-byte (metadata) piece l % 2.
+    // and the metadata as [half][row][8 bytes] (256 bytes; 1:2: [half][row][4 bytes] in its
+    // first 128).  In the blocked layout both are one contiguous run per group and step; in
+    // the row layout lane l fetches row (l % 32) / 2, half l / 32, 16-byte (values) or
+    // 4-byte (metadata) piece l % 2 (1:2 metadata: lanes 0..31, row l % 16, half l / 16).
     int64_t a_src[TL::kALoads], m_src[TL::kMLoads];
     uint32_t a_dst[TL::kALoads], m_dst[TL::kMLoads];
     const int lrow = (lane & 31) >> 1, lh = lane >> 5, lp = lane & 1;
@@ -1207,7 +1210,11 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
       if constexpr (kBlocked) {
         int g = (m0 >> 4) + b16;
         g = g < last_g ? g : last_g;
-        m_src[j] = (int64_t)g * steps64 * 128 + 4 * lane;
+        m_src[j] = (int64_t)g * steps64 * (kPat12 ? 64 : 128) + 4 * lane;
+      } else if constexpr (kPat12) {
+        int row = m0 + 16 * b16 + (lane & 15);
+        row = row < R ? row : R - 1;
+        m_src[j] = (int64_t)row * (K / 16) + 4 * ((lane >> 4) & 1);  // K / 64 words per row
       } else {
         int row = m0 + 16 * b16 + lrow;
         row = row < R ? row : R - 1;
@@ -1215,7 +1222,8 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
       }
       m_dst[j] = (uint32_t)(TL::kXBytes + TL::kABytes + b16 * 256);
     }
-    constexpr int64_t kAStep = kBlocked ? 1024 : 64, kMStep = kBlocked ? 256 : 16;
+    constexpr int64_t kAStep = kBlocked ? 1024 : 64;
+    constexpr int64_t kMStep = kPat12 ? (kBlocked ? 128 : 8) : (kBlocked ? 256 : 16);
     const uint8_t* mg = reinterpret_cast<const uint8_t*>(meta);
     auto issue_step = [&](int step) {
       step = step < last_step ? step : last_step;  // past the end: re-read the last step
@@ -1227,8 +1235,13 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
       for (int j = 0; j < TL::kALoads; ++j)
         global_to_lds<16>(values + a_src[j] + step * kAStep, st + a_dst[j]);
 #pragma unroll
-      for (int j = 0; j < TL::kMLoads; ++j)
-        global_to_lds<4>(mg + m_src[j] + step * kMStep, st + m_dst[j]);
+      for (int j = 0; j < TL::kMLoads; ++j) {
+        if constexpr (kPat12) {  // 128 bytes per group: half the lanes
+          if (lane < 32) global_to_lds<4>(mg + m_src[j] + step * kMStep, st + m_dst[j]);
+        } else {
+          global_to_lds<4>(mg + m_src[j] + step * kMStep, st + m_dst[j]);
+        }
+      }
     };
 #pragma unroll
     for (int k = 0; k < kStages - 1; ++k) issue_step(k);
@@ -1250,7 +1263,8 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
   for (int fm = 0; fm < 4; ++fm) {
     const int i = wm * TL::kWM + 32 * fm + l32;
     a_off[fm] = (uint32_t)(TL::kXBytes + (i >> 4) * 1024 + (i & 15) * 32 + 16 * q);
-    m_off[fm] = (uint32_t)(TL::kXBytes + TL::kABytes + (i >> 4) * 256 + (i & 15) * 8 + 4 * q);
+    m_off[fm] = (uint32_t)(TL::kXBytes + TL::kABytes + (i >> 4) * 256 +
+                           (kPat12 ? (i & 15) * 4 + 2 * q : (i & 15) * 8 + 4 * q));
   }
   // B: piece p of fragment f in half h covers K rows 64h + 16q + 8(p & 1) + 32(p >> 1) + 0..7
   // of columns wn*64 + 32 f + 16 (blk & 1) + 0..15; this lane addresses row + (i16 >> 1),
@@ -1286,7 +1300,19 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
 #pragma unroll
     for (int fm = 0; fm < 4; ++fm) {
       F.a[fm] = *reinterpret_cast<const int4v_t*>(st + a_off[fm] + 512 * h);
-      F.ix[fm] = *reinterpret_cast<const int*>(st + m_off[fm] + 128 * h);
+      if constexpr (kPat12) {
+        // 16 one-bit positions b_j of 1:2 groups j -> the 2:4 index word: value j sits in
+        // group j / 2 of four at position 2 (j % 2) + b_j, i.e. bit j moves to bit 2j and
+        // every odd field gets its bit 1
+        uint32_t x = *reinterpret_cast<const uint16_t*>(st + m_off[fm] + 64 * h);
+        x = (x | (x << 8)) & 0x00FF00FFu;
+        x = (x | (x << 4)) & 0x0F0F0F0Fu;
+        x = (x | (x << 2)) & 0x33333333u;
+        x = (x | (x << 1)) & 0x55555555u;
+        F.ix[fm] = (int)(x | 0x88888888u);
+      } else {
+        F.ix[fm] = *reinterpret_cast<const int*>(st + m_off[fm] + 128 * h);
+      }
     }
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
@@ -1333,12 +1359,12 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
 
 int xcd_count();
 
-template <bool kFp8, bool kBlocked, int YT>
+template <bool kFp8, bool kBlocked, bool kPat12, int YT>
 hipError_t run_smfmac_8bit(const void* values, const uint32_t* meta, int64_t R, int64_t K,
                            const void* X, int64_t T, void* Y, hipStream_t s) {
   constexpr int BM = 256, BN = 128, ST = 4;
   using TL = WsI8Tile<BM, BN, 2, 2, 4, ST>;
-  auto kernel = smfmac_i8_ws_spmm_kernel<kFp8, kBlocked, YT, BM, BN, 2, 2, 4, ST>;
+  auto kernel = smfmac_i8_ws_spmm_kernel<kFp8, kBlocked, kPat12, YT, BM, BN, 2, 2, 4, ST>;
   const size_t lds = (size_t)ST * TL::kStageBytes;
   static const hipError_t attr =
       hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
@@ -2200,25 +2226,26 @@ hipError_t launch_spmm(const void* values, const uint32_t* meta, int64_t R, int6
         static_cast<uint32_t*>(Y), words, tail_halves);
     return hipGetLastError();
   }
-  // the 8-bit matrix-core kernel: 2:4, either layout, K a multiple of 128 (two blocked
-  // steps), T a multiple of 16 (16-byte X loads), 32-bit X offsets
-  const bool tiled_8bit = pat24 && K % kI8KStep == 0 && T % 16 == 0 && R < (1 << 30) &&
-                          T < (1 << 30) && K < (1 << 30);
+  // the 8-bit matrix-core kernel: 2:4 and 1:2, either layout, K a multiple of 128 (two
+  // blocked steps), T a multiple of 16 (16-byte X loads), 32-bit X offsets
+  const bool tiled_8bit = (pat24 || pat12) && K % kI8KStep == 0 && T % 16 == 0 &&
+                          R < (1 << 30) && T < (1 << 30) && K < (1 << 30);
+#define NM_8(FP8, YT)                                                                     \
+  return blocked ? (pat12 ? run_smfmac_8bit<FP8, true, true, YT>(values, meta, R, K, X, T, Y, s)  \
+                          : run_smfmac_8bit<FP8, true, false, YT>(values, meta, R, K, X, T, Y, s)) \
+                 : (pat12 ? run_smfmac_8bit<FP8, false, true, YT>(values, meta, R, K, X, T, Y, s) \
+                          : run_smfmac_8bit<FP8, false, false, YT>(values, meta, R, K, X, T, Y, s));
   if (dt == kI8) {
-    if (tiled_8bit)
-      return blocked ? run_smfmac_8bit<false, true, kI32>(values, meta, R, K, X, T, Y, s)
-                     : run_smfmac_8bit<false, false, kI32>(values, meta, R, K, X, T, Y, s);
+    if (tiled_8bit) { NM_8(false, kI32) }
     return run_generic_layout<kI8, kI32>(values, meta, R, K, n, m, blocked, X, T, Y, s);
   }
   if (dt == kFP8) {  // the same kernel on the fp8 instruction, fp32 accumulation
     const bool yf32 = y_dt == kF32;
     if (tiled_8bit) {
-      if (blocked)
-        return yf32 ? run_smfmac_8bit<true, true, kF32>(values, meta, R, K, X, T, Y, s)
-                    : run_smfmac_8bit<true, true, kBF16>(values, meta, R, K, X, T, Y, s);
-      return yf32 ? run_smfmac_8bit<true, false, kF32>(values, meta, R, K, X, T, Y, s)
-                  : run_smfmac_8bit<true, false, kBF16>(values, meta, R, K, X, T, Y, s);
+      if (yf32) { NM_8(true, kF32) }
+      NM_8(true, kBF16)
     }
+#undef NM_8
     return yf32 ? run_generic_layout<kFP8, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s)
                 : run_generic_layout<kFP8, kBF16>(values, meta, R, K, n, m, blocked, X, T, Y, s);
   }

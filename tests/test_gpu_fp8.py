@@ -152,8 +152,8 @@ def check_product(Y, y_ref, s, kept, y_dtype, label, runs=None):
 
 
 def matrix_core(n, m, layout, K, T):
-    """The fp8 matrix-core kernel's domain (2:4, either layout, K % 128, T % 16)."""
-    return (n, m) == (2, 4) and K % 128 == 0 and T % 16 == 0
+    """The fp8 matrix-core kernel's domain (2:4 or 1:2, either layout, K % 128, T % 16)."""
+    return (n, m) in ((2, 4), (1, 2)) and K % 128 == 0 and T % 16 == 0
 
 
 _VALUE = oracle.to_double(np.arange(256, dtype=np.uint8), "fp8")  # the oracle's decoding
@@ -199,12 +199,13 @@ def test_fp8_product(n, m, layout, y_dtype):
                                    (256, 1024, 256), (40, 128, 1040)])
 @pytest.mark.parametrize("y_dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("layout", ["rows", "blocked"])
-def test_fp8_matrix_core_product(R, K, T, y_dtype, layout):
-    """Shapes the fp8 matrix-core kernel takes (2:4, K % 128 == 0, T % 16 == 0), several
-    tiles with ragged row and column tails."""
+@pytest.mark.parametrize("n,m", [(2, 4), (1, 2)])
+def test_fp8_matrix_core_product(R, K, T, y_dtype, layout, n, m):
+    """Shapes the fp8 matrix-core kernel takes (2:4 or 1:2, K % 128 == 0, T % 16 == 0),
+    several tiles with ragged row and column tails."""
     rng = np.random.default_rng(R + K + T)
-    product_case(fp8_normal(rng, (R, K)), fp8_normal(rng, (K, T)), 2, 4, layout, y_dtype,
-                 f"{R}x{K}x{T} {layout}")
+    product_case(fp8_normal(rng, (R, K)), fp8_normal(rng, (K, T)), n, m, layout, y_dtype,
+                 f"{R}x{K}x{T} {n}:{m} {layout}")
 
 
 def test_fp8_matrix_core_subnormals_and_extremes():

@@ -107,16 +107,17 @@ def test_i8_product_exact(n, m, layout):
 @pytest.mark.parametrize("R,K,T", [(200, 384, 272), (300, 256, 144), (16, 128, 16), (513, 640, 400),
                                    (256, 1024, 256), (40, 128, 1040)])
 @pytest.mark.parametrize("layout", ["rows", "blocked"])
-def test_i8_matrix_core_product_exact(R, K, T, layout):
-    """Shapes the int8 matrix-core kernel takes (2:4, K % 128 == 0, T % 16 == 0), several
-    tiles with ragged row and column tails: exact against the oracle."""
+@pytest.mark.parametrize("n,m", [(2, 4), (1, 2)])
+def test_i8_matrix_core_product_exact(R, K, T, layout, n, m):
+    """Shapes the int8 matrix-core kernel takes (2:4 or 1:2, K % 128 == 0, T % 16 == 0),
+    several tiles with ragged row and column tails: exact against the oracle."""
     rng = np.random.default_rng(R + K + T)
     W = int8_matrix(rng, (R, K))
     X = int8_matrix(rng, (K, T), ties=False)
-    vals_o, meta_o = oracle.compress(W, "i8", 2, 4)
-    v, mt = nm.compress(dev8(W), 2, 4, layout=layout)
-    Y = nm.spmm(v, mt, dev8(X), 2, 4, layout=layout, rows=R)
-    y_ref = oracle.spmm(vals_o, meta_o, R, K, 2, 4, X, "i8")
+    vals_o, meta_o = oracle.compress(W, "i8", n, m)
+    v, mt = nm.compress(dev8(W), n, m, layout=layout)
+    Y = nm.spmm(v, mt, dev8(X), n, m, layout=layout, rows=R)
+    y_ref = oracle.spmm(vals_o, meta_o, R, K, n, m, X, "i8")
     got = Y.cpu().numpy().astype(np.float64)
     bad = got != y_ref
     assert not bad.any(), f"{int(bad.sum())} of {bad.size} differ, first at {np.argwhere(bad)[0]}"
