@@ -23,8 +23,8 @@
 //  * smfmac32_spmm_kernel (256 x 256 tiles): the same fragment code with every wave
 //    issuing its own loads, for short K; smfmac_spmm_kernel (128 x 128 tiles,
 //    v_smfmac_f32_16x16x64) for small shapes.
-//  * mfma48_ws_spmm_kernel: 4:8 on the dense matrix cores, each 4:8 group expanded in
-//    registers with byte permutes.
+//  * mfma48_ws_spmm_kernel: 4:8 (either layout) on the dense matrix cores, each 4:8 group
+//    expanded in registers with byte permutes.
 //  * smfmac_i8_ws_spmm_kernel: 2:4 and 1:2 int8 (exact int32) and fp8 (fp32 accumulation)
 //    on the 32x32x64 8-bit instructions.
 //  * expand_f32_spmm_kernel: fp32, any pattern; the compressed rows are expanded in LDS and
@@ -1438,7 +1438,8 @@ __device__ __forceinline__ float16v_t mfma32x32x16(const u32x4_t& a, const u32x4
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
-template <bool BF16, int YT, int BM, int BN, int CWAVES_M, int CWAVES_N, int PWAVES, int STAGES>
+template <bool BF16, bool kBlocked, int YT, int BM, int BN, int CWAVES_M, int CWAVES_N,
+          int PWAVES, int STAGES>
 __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
     mfma48_ws_spmm_kernel(const uint16_t* __restrict__ values, const uint32_t* __restrict__ meta,
                           const uint16_t* __restrict__ X, void* __restrict__ Y, int R, int K,
@@ -1482,13 +1483,15 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
 #pragma unroll
     for (int j = 0; j < TL::kALoads; ++j) {
       const int b16 = j * TL::kProducers + pw;
-      a_src[j] = values_source<true>(m0, 16 * b16, lane, R, K, nsteps);
+      a_src[j] = values_source<kBlocked>(m0, 16 * b16, lane, R, K, nsteps);
       a_dst[j] = (uint32_t)(TL::kXBytes + b16 * 1024);
     }
-    // metadata: the tile's 16 blocks of 16 rows x 12 bytes (192 bytes each, nsteps * 192
-    // bytes apart) land back to back, so tile row i sits at 12 i; a load covers 256 bytes
-    // of that run, four per lane.  Producer pw loads the bytes of rows 64 pw .. 64 pw + 63
-    // itself, so its own wait covers the rows whose keep masks it builds.
+    // metadata: the tile's rows land back to back, 12 bytes each (tile row i at 12 i); in
+    // the blocked layout that is the tile's 16 blocks of 16 rows x 12 bytes (192 bytes
+    // each, nsteps * 192 bytes apart), in the row layout 12 bytes of each row (3K/16 bytes
+    // apart).  A load covers 256 bytes of the run, four per lane.  Producer pw loads the
+    // bytes of rows 64 pw .. 64 pw + 63 itself, so its own wait covers the rows whose keep
+    // masks it builds.
     static_assert(64 * TL::kMRow == 256 * TL::kMLoads, "a producer's rows are whole loads");
     int64_t m_src[TL::kMLoads];
     uint32_t m_dst[TL::kMLoads];
@@ -1496,17 +1499,23 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
     for (int j = 0; j < TL::kMLoads; ++j) {
       const int w256 = pw * TL::kMLoads + j;
       const int o = w256 * 256 + 4 * lane;
-      int g = m0 / 16 + o / 192;
-      g = g < last_group ? g : last_group;
-      m_src[j] = (int64_t)g * nsteps * 192 + o % 192;
+      if constexpr (kBlocked) {
+        int g = m0 / 16 + o / 192;
+        g = g < last_group ? g : last_group;
+        m_src[j] = (int64_t)g * nsteps * 192 + o % 192;
+      } else {
+        int row = m0 + o / 12;
+        row = row < R ? row : R - 1;  // rows past the matrix: any valid row
+        m_src[j] = (int64_t)row * (3 * (int64_t)K / 16) + o % 12;
+      }
       m_dst[j] = (uint32_t)(TL::kXBytes + TL::kABytes + w256 * 256);
     }
     auto issue_step = [&](int step) {
       step = step < last_step ? step : last_step;
       uint8_t* st = smem + (step % kStages) * TL::kStageBytes;
       const int64_t kx = (int64_t)step * kKStep * T * 2;
-      const int64_t ka = (int64_t)step * 1024;
-      const int64_t km = (int64_t)step * 192;
+      const int64_t ka = (int64_t)step * values_step_bytes<kBlocked>();
+      const int64_t km = (int64_t)step * (kBlocked ? 192 : 12);
 #pragma unroll
       for (int j = 0; j < TL::kXLoads; ++j) global_to_lds<16>(xg + x_src[j] + kx, st + x_dst[j]);
 #pragma unroll
@@ -2159,14 +2168,14 @@ hipError_t run_smfmac(const void* values, const uint32_t* meta, int64_t R, int64
   }
 }
 
-// 4:8, 16-bit, blocked layout: dense matrix cores on expanded groups, 256 x 128 tiles.
-template <bool BF16, int YT>
+// 4:8, 16-bit, either layout: dense matrix cores on expanded groups, 256 x 128 tiles.
+template <bool BF16, bool kBlocked, int YT>
 hipError_t run_mfma48(const void* values, const uint32_t* meta, int64_t R, int64_t K,
                       const void* X, int64_t T, void* Y, hipStream_t s) {
   constexpr int BM = 256, BN = 128, ST = 4;
   using TL = Ws48Tile<BM, BN, 2, 2, 4, ST>;
   const int tiles_m = (int)((R + BM - 1) / BM), tiles_n = (int)((T + BN - 1) / BN);
-  auto kernel = mfma48_ws_spmm_kernel<BF16, YT, BM, BN, 2, 2, 4, ST>;
+  auto kernel = mfma48_ws_spmm_kernel<BF16, kBlocked, YT, BM, BN, 2, 2, 4, ST>;
   const size_t lds = (size_t)ST * TL::kStageBytes + TL::kLutBytes;
   static const hipError_t attr =
       hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
@@ -2197,12 +2206,17 @@ hipError_t launch_spmm(const void* values, const uint32_t* meta, int64_t R, int6
   const bool tiled_shape = K > 0 && K % kKStep == 0 && T % 8 == 0 && R < (1 << 30) &&
                            T < (1 << 30) && K < (1 << 30);
   const bool half = dt == kBF16 || dt == kF16;
-  if (half && n == 4 && m == 8 && blocked && tiled_shape) {
-    if (dt == kBF16)
-      return y_dt == kF32 ? run_mfma48<true, kF32>(values, meta, R, K, X, T, Y, s)
-                          : run_mfma48<true, kBF16>(values, meta, R, K, X, T, Y, s);
-    return y_dt == kF32 ? run_mfma48<false, kF32>(values, meta, R, K, X, T, Y, s)
-                        : run_mfma48<false, kF16>(values, meta, R, K, X, T, Y, s);
+  if (half && n == 4 && m == 8 && tiled_shape) {
+#define NM_48(BF, YT)                                                                   \
+  return blocked ? run_mfma48<BF, true, YT>(values, meta, R, K, X, T, Y, s)             \
+                 : run_mfma48<BF, false, YT>(values, meta, R, K, X, T, Y, s);
+    if (dt == kBF16) {
+      if (y_dt == kF32) { NM_48(true, kF32) }
+      NM_48(true, kBF16)
+    }
+    if (y_dt == kF32) { NM_48(false, kF32) }
+    NM_48(false, kF16)
+#undef NM_48
   }
   if (half && (pat24 || pat12) && tiled_shape) {
     const bool yf32 = y_dt == kF32;
