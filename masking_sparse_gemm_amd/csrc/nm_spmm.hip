@@ -27,8 +27,9 @@
 //    expanded in registers with byte permutes.
 //  * smfmac_i8_ws_spmm_kernel: 2:4 and 1:2 int8 (exact int32) and fp8 (fp32 accumulation)
 //    on the 32x32x64 8-bit instructions.
-//  * expand_f32_spmm_kernel: fp32, any pattern; the compressed rows are expanded in LDS and
-//    multiplied on the dense fp32 matrix cores (v_mfma_f32_32x32x2_f32).
+//  * expand_mfma_spmm_kernel: fp32 (any pattern) and 16-bit patterns without a sparse
+//    kernel; the compressed rows are expanded in LDS and multiplied on the dense matrix
+//    cores (v_mfma_f32_32x32x2_f32, v_mfma_f32_32x32x16_{bf16,f16}).
 //  * generic_spmm_kernel: every other pattern and shapes the tiled kernels do not take; it
 //    expands the compressed rows to fp32 in LDS and accumulates with fp32 FMAs.
 // The blocked layout (include/nm.h) makes every direct load of compressed values or
@@ -1831,39 +1832,49 @@ __global__ void __launch_bounds__(256) generic_spmm_kernel(const void* __restric
 }
 
 // ===========================================================================
-// fp32, any N:M: the compressed rows are expanded in LDS (zeros where pruned, as in the
-// generic kernel) and multiplied on the dense fp32 matrix cores, v_mfma_f32_32x32x2_f32.
-// gfx950 has no structured-sparse fp32 instruction, so this is the dense product of the
-// decompressed tile, reading only the compressed pair.  The fp32 matrix cores need 16x the
-// time of the 16-bit ones per flop, so the loads are a small share of a step and a plain
-// register prefetch hides them: the loads of step s+1 are issued before step s's matrix
-// instructions and written to LDS after them.
-// Workgroup: 128 x 128 outputs, four waves of 64 x 64 (2 x 2 blocks of 32 x 32), K step 32.
-// Instruction i (0..15) of a step pairs K 16q + i in lane half q (the contraction order
-// inside a step is free), so a lane's A operands of the step are one 16-float run of its
-// row, four ds_read_b128, and each B operand is one ds_read_b32.  A rows are padded to 36
-// floats (conflict-free 16-byte reads); X rows 16..31 swap adjacent 32-column blocks, so
-// the two lane halves of a B read hit opposite halves of the 64 banks.
+// Any N:M on the dense matrix cores: the compressed rows are expanded in LDS (zeros where
+// pruned, as in the generic kernel) and multiplied with v_mfma_f32_32x32x2_f32 (fp32) or
+// v_mfma_f32_32x32x16_{bf16,f16} (16-bit patterns without a structured-sparse kernel).
+// This is the dense product of the decompressed tile, reading only the compressed pair, so
+// it can at best match a dense GEMM.  The loads of step s+1 go to registers before step
+// s's matrix instructions and into the other LDS stage after them (one barrier per step).
+// Workgroup: 128 x 128 outputs, four waves of 64 x 64 (2 x 2 blocks of 32 x 32).
+//  * fp32, K step 32: instruction i (0..15) pairs K 16q + i in lane half q (the contraction
+//    order inside a step is free), so a lane's A operands of the step are one 16-float run
+//    of its row and each B operand is one ds_read_b32.  X rows 16..31 swap adjacent
+//    32-column blocks, so the two lane halves of a B read hit opposite halves of the banks.
+//  * 16-bit, K step 64: substep t (0..3) gives lane half q K 32q + 8t + 0..7, one 16-byte
+//    A read of its row; B comes from the row-major X tile through ds_read_b64_tr_b16, X
+//    stored in 32-byte column pairs swizzled by xpair_swizzle as in the 2:4 kernels.
+// A rows are 144 bytes (32 floats or 64 halves, then padding): conflict-free 16-byte reads.
 // ===========================================================================
-constexpr int kEM = 128, kEN = 128, kEK = 32;
-constexpr int kEAS = kEK + 4;
-constexpr int kEStage = kEM * kEAS + kEK * kEN;  // floats per stage
+constexpr int kEM = 128, kEN = 128;
+constexpr int kEARow = 36;                          // 32-bit words per A row in LDS
+constexpr int kEStageWords = kEM * kEARow + 4096;   // A rows + 16 KB of X
 
-__device__ __forceinline__ int ex_col(int c, int kk) {  // physical column of X tile entry
+__device__ __forceinline__ int ex_col(int c, int kk) {  // fp32: physical column of X entry
   return (((c >> 5) ^ ((kk >> 4) & 1)) << 5) | (c & 31);
 }
 
-template <int YT, int N, int M, bool kBlocked>
+template <int DT, int YT, int N, int M, bool kBlocked>
 __global__ void __launch_bounds__(256)
-    expand_f32_spmm_kernel(const float* __restrict__ values, const uint32_t* __restrict__ meta,
-                           const float* __restrict__ X, void* __restrict__ Y, int64_t R,
-                           int64_t K, int64_t T, int64_t tiles_n) {
+    expand_mfma_spmm_kernel(const void* __restrict__ values, const uint32_t* __restrict__ meta,
+                            const void* __restrict__ X, void* __restrict__ Y, int64_t R,
+                            int64_t K, int64_t T, int64_t tiles_n) {
+  constexpr bool kF = DT == kF32;
+  using E = std::conditional_t<kF, float, uint16_t>;
+  constexpr int kEK = kF ? 32 : 64;          // K per step
+  constexpr int kPerChunk = 16 / sizeof(E);  // X elements per 16-byte piece
+  constexpr int kChunksPerRow = kEN / kPerChunk;
   constexpr int b = meta_bits(M);
   constexpr int kGPS = kEK / M;              // groups per row and step
   constexpr int kItems = kEM * kGPS / 256;   // (row, group) items per thread and step
   constexpr int64_t V = 64 / M * N;          // blocked layout: values per row per 64 of K
   static_assert(kItems * 256 == kEM * kGPS, "whole items per thread");
-  extern __shared__ __attribute__((aligned(16))) float ex_smem[];  // two stages of A, X
+  static_assert(kEK * kEN * (int)sizeof(E) == 4096 * 4, "16 KB of X per step");
+  extern __shared__ __attribute__((aligned(16))) uint32_t ex_smem[];  // two stages
+  const E* vals = static_cast<const E*>(values);
+  const E* Xe = static_cast<const E*>(X);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * kEM;
   const int64_t t0 = (int64_t)(blockIdx.x % tiles_n) * kEN;
@@ -1872,23 +1883,24 @@ __global__ void __launch_bounds__(256)
   // prefetch registers: X pieces, each item's values and the (one or two) metadata words
   // holding its fields with the fields' bit offset; nothing fetched is used before the
   // stash, so the loads stay in flight across the step's matrix instructions
-  float4_t xr[4];
-  float vr[kItems][N];
+  u32x4_t xr[4];
+  E vr[kItems][N];
   uint32_t mw0[kItems], mw1[kItems], msh[kItems];
   auto fetch = [&](int64_t k0) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int idx = j * 256 + tid, kk = idx >> 5, c = 4 * (idx & 31);
+      const int idx = j * 256 + tid, kk = idx / kChunksPerRow;
+      const int c = kPerChunk * (idx % kChunksPerRow);
       const int64_t k = k0 + kk, col = t0 + c;
-      xr[j] = (k < K && col < T) ? *reinterpret_cast<const float4_t*>(X + k * T + col)
-                                 : float4_t{0.f, 0.f, 0.f, 0.f};
+      xr[j] = (k < K && col < T) ? *reinterpret_cast<const u32x4_t*>(Xe + k * T + col)
+                                 : u32x4_t{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int it = 0; it < kItems; ++it) {
       const int i = it * 256 + tid, r = i / kGPS, gl = i % kGPS;
       const int64_t row = m0 + r, g = k0 / M + gl;
 #pragma unroll
-      for (int j = 0; j < N; ++j) vr[it][j] = 0.f;
+      for (int j = 0; j < N; ++j) vr[it][j] = E(0);
       mw0[it] = mw1[it] = msh[it] = 0u;
       if (row < R && g < gpr) {
         // the group's N fields are consecutive in both layouts (a 64-wide step of the blocked
@@ -1904,7 +1916,7 @@ __global__ void __launch_bounds__(256)
           bit = row * wpr * 32 + f0 * b;
         }
 #pragma unroll
-        for (int j = 0; j < N; ++j) vr[it][j] = values[vi + j];
+        for (int j = 0; j < N; ++j) vr[it][j] = vals[vi + j];
         mw0[it] = meta[bit / 32];
         if ((bit % 32) + N * b > 32) mw1[it] = meta[bit / 32 + 1];
         msh[it] = (uint32_t)(bit % 32);
@@ -1912,43 +1924,74 @@ __global__ void __launch_bounds__(256)
     }
   };
   auto stash = [&](int stage) {
-    float* As = ex_smem + stage * kEStage;
-    float* Xs = As + kEM * kEAS;
+    uint32_t* As = ex_smem + stage * kEStageWords;
+    uint32_t* Xs = As + kEM * kEARow;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int idx = j * 256 + tid, kk = idx >> 5, c = 4 * (idx & 31);
-      *reinterpret_cast<float4_t*>(Xs + kk * kEN + ex_col(c, kk)) = xr[j];
+      const int idx = j * 256 + tid, kk = idx / kChunksPerRow, pc = idx % kChunksPerRow;
+      int word;
+      if constexpr (kF) {
+        word = kk * kEN + ex_col(4 * pc, kk);
+      } else {
+        word = kk * (kEN / 2) + 4 * (2 * ((pc >> 1) ^ xpair_swizzle(kk)) + (pc & 1));
+      }
+      *reinterpret_cast<u32x4_t*>(Xs + word) = xr[j];
     }
 #pragma unroll
     for (int it = 0; it < kItems; ++it) {
       const int i = it * 256 + tid, r = i / kGPS, gl = i % kGPS;
       const uint32_t fields = (uint32_t)((((uint64_t)mw1[it] << 32) | mw0[it]) >> msh[it]);
-      float o[M];
+      uint32_t o[M];  // element bits, zero where pruned
 #pragma unroll
-      for (int e = 0; e < M; ++e) o[e] = 0.f;
+      for (int e = 0; e < M; ++e) o[e] = 0u;
 #pragma unroll
       for (int j = 0; j < N; ++j) {
         const int p = (int)((fields >> (j * b)) & ((1u << b) - 1u));
+        uint32_t v;
+        if constexpr (kF) v = __float_as_uint(vr[it][j]);
+        else v = vr[it][j];
 #pragma unroll
-        for (int e = 0; e < M; ++e) o[e] = (p == e) ? vr[it][j] : o[e];
+        for (int e = 0; e < M; ++e) o[e] = (p == e) ? v : o[e];
       }
-      float* dst = As + r * kEAS + gl * M;
-      if constexpr (M == 2) {
-        *reinterpret_cast<float2_t*>(dst) = float2_t{o[0], o[1]};
-      } else {
+      if constexpr (kF) {
+        uint32_t* dst = As + r * kEARow + gl * M;
+        if constexpr (M == 2) {
+          *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{o[0], o[1]};
+        } else {
 #pragma unroll
-        for (int e = 0; e < M; e += 4)
-          *reinterpret_cast<float4_t*>(dst + e) = float4_t{o[e], o[e + 1], o[e + 2], o[e + 3]};
+          for (int e = 0; e < M; e += 4)
+            *reinterpret_cast<u32x4_t*>(dst + e) = u32x4_t{o[e], o[e + 1], o[e + 2], o[e + 3]};
+        }
+      } else {
+        uint32_t pk[M / 2];
+#pragma unroll
+        for (int e = 0; e < M / 2; ++e) pk[e] = o[2 * e] | (o[2 * e + 1] << 16);
+        uint32_t* dst = As + r * kEARow + gl * (M / 2);
+        if constexpr (M == 2) {
+          *dst = pk[0];
+        } else if constexpr (M == 4) {
+          *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{pk[0], pk[1]};
+        } else {
+          *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
+        }
       }
     }
   };
 
   const int q = lane >> 5, lr = lane & 31, wm = wave >> 1, wn = wave & 1;
-  int a_off[2], b_off[2];
+  const int l16 = lane & 15, blk = lane >> 4;
+  int a_off[2], b_off[2][2];  // 32-bit words (A, fp32 B) or bytes (16-bit B)
 #pragma unroll
   for (int f = 0; f < 2; ++f) {
-    a_off[f] = (wm * 64 + f * 32 + lr) * kEAS + 16 * q;
-    b_off[f] = 16 * q * kEN + ex_col(wn * 64 + f * 32 + lr, 16 * q);
+    a_off[f] = (wm * 64 + f * 32 + lr) * kEARow + 16 * q;  // K 16q.. (fp32) or 32q.. (16-bit)
+    if constexpr (kF) {
+      b_off[f][0] = 16 * q * kEN + ex_col(wn * 64 + f * 32 + lr, 16 * q);
+      b_off[f][1] = 0;
+    } else {
+      const int rb = 32 * q + (l16 >> 2), lp = (wn * 64 + 32 * f + 16 * (blk & 1)) / 16;
+      b_off[f][0] = rb * (2 * kEN) + ((lp ^ xpair_swizzle(rb)) << 5) + 8 * (l16 & 3);
+      b_off[f][1] = (rb + 4) * (2 * kEN) + ((lp ^ xpair_swizzle(rb + 4)) << 5) + 8 * (l16 & 3);
+    }
   }
   float16v_t acc[2][2];
 #pragma unroll
@@ -1965,25 +2008,50 @@ __global__ void __launch_bounds__(256)
   for (int64_t k0 = 0; k0 < K; k0 += kEK) {
     const bool more = k0 + kEK < K;
     if (more) fetch(k0 + kEK);
-    const float* As = ex_smem + stage * kEStage;
-    const float* Xs = As + kEM * kEAS;
-    float4_t a[2][4];
-#pragma unroll
-    for (int fm = 0; fm < 2; ++fm)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        a[fm][j] = *reinterpret_cast<const float4_t*>(As + a_off[fm] + 4 * j);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float bv[2];
-#pragma unroll
-      for (int fn = 0; fn < 2; ++fn) bv[fn] = Xs[b_off[fn] + i * kEN];
+    const uint32_t* As = ex_smem + stage * kEStageWords;
+    const uint32_t* Xs = As + kEM * kEARow;
+    if constexpr (kF) {
+      float4_t a[2][4];
 #pragma unroll
       for (int fm = 0; fm < 2; ++fm)
 #pragma unroll
-        for (int fn = 0; fn < 2; ++fn)
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[fm][i >> 2][i & 3], bv[fn],
-                                                             acc[fm][fn], 0, 0, 0);
+        for (int j = 0; j < 4; ++j)
+          a[fm][j] = *reinterpret_cast<const float4_t*>(As + a_off[fm] + 4 * j);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float bv[2];
+#pragma unroll
+        for (int fn = 0; fn < 2; ++fn) bv[fn] = __uint_as_float(Xs[b_off[fn][0] + i * kEN]);
+#pragma unroll
+        for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < 2; ++fn)
+            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[fm][i >> 2][i & 3], bv[fn],
+                                                               acc[fm][fn], 0, 0, 0);
+      }
+    } else {
+      const uint8_t* xb = reinterpret_cast<const uint8_t*>(Xs);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        u32x4_t a[2], bb[2];
+#pragma unroll
+        for (int fm = 0; fm < 2; ++fm)
+          a[fm] = *reinterpret_cast<const u32x4_t*>(As + a_off[fm] + 4 * t);
+#pragma unroll
+        for (int fn = 0; fn < 2; ++fn) {
+          const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_short4_t*)(xb + b_off[fn][0] + 8 * t * 2 * kEN));
+          const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_short4_t*)(xb + b_off[fn][1] + 8 * t * 2 * kEN));
+          bb[fn] = __builtin_bit_cast(u32x4_t,
+                                      __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+        for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < 2; ++fn)
+            acc[fm][fn] = mfma32x32x16<DT == kBF16>(a[fm], bb[fn], acc[fm][fn]);
+      }
     }
     if (more) stash(stage ^ 1);
     __syncthreads();
@@ -2004,22 +2072,20 @@ __global__ void __launch_bounds__(256)
     }
 }
 
-template <bool kBlocked>
-hipError_t run_expand_f32(const void* values, const uint32_t* meta, int64_t R, int64_t K, int n,
-                          int m, const void* X, int64_t T, void* Y, hipStream_t s) {
+template <int DT, int YT, bool kBlocked>
+hipError_t run_expand(const void* values, const uint32_t* meta, int64_t R, int64_t K, int n,
+                      int m, const void* X, int64_t T, void* Y, hipStream_t s) {
   const int64_t tiles_n = (T + kEN - 1) / kEN, tiles = (R + kEM - 1) / kEM * tiles_n;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  const float* v = static_cast<const float*>(values);
-  const float* x = static_cast<const float*>(X);
-  constexpr size_t lds = 2 * kEStage * sizeof(float);
+  constexpr size_t lds = 2 * kEStageWords * sizeof(uint32_t);
 #define NM_E(NN, MM)                                                                       \
   if (n == NN && m == MM) {                                                                \
-    auto kernel = expand_f32_spmm_kernel<kF32, NN, MM, kBlocked>;                          \
+    auto kernel = expand_mfma_spmm_kernel<DT, YT, NN, MM, kBlocked>;                       \
     static const hipError_t attr =                                                         \
         hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),                         \
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);         \
     if (attr != hipSuccess) return attr;                                                   \
-    kernel<<<(unsigned)tiles, 256, lds, s>>>(v, meta, x, Y, R, K, T, tiles_n);             \
+    kernel<<<(unsigned)tiles, 256, lds, s>>>(values, meta, X, Y, R, K, T, tiles_n);        \
     return hipGetLastError();                                                              \
   }
   NM_E(1, 2) NM_E(2, 2)
@@ -2028,6 +2094,14 @@ hipError_t run_expand_f32(const void* values, const uint32_t* meta, int64_t R, i
   NM_E(5, 8) NM_E(6, 8) NM_E(7, 8) NM_E(8, 8)
 #undef NM_E
   return hipErrorInvalidValue;
+}
+
+template <int DT, int YT>
+hipError_t run_expand_layout(const void* values, const uint32_t* meta, int64_t R, int64_t K,
+                             int n, int m, bool blocked, const void* X, int64_t T, void* Y,
+                             hipStream_t s) {
+  return blocked ? run_expand<DT, YT, true>(values, meta, R, K, n, m, X, T, Y, s)
+                 : run_expand<DT, YT, false>(values, meta, R, K, n, m, X, T, Y, s);
 }
 
 __global__ void zero_fill_kernel(uint32_t* __restrict__ p, int64_t words, int64_t tail_halves) {
@@ -2263,17 +2337,25 @@ hipError_t launch_spmm(const void* values, const uint32_t* meta, int64_t R, int6
     return yf32 ? run_generic_layout<kFP8, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s)
                 : run_generic_layout<kFP8, kBF16>(values, meta, R, K, n, m, blocked, X, T, Y, s);
   }
+  // the expansion kernel reads X in 16-byte pieces: rows of whole 16 bytes
   if (dt == kF32) {
-    // the matrix-core kernel reads X in 16-byte pieces: rows of whole 16 bytes
     if (T % 4 == 0)
-      return blocked ? run_expand_f32<true>(values, meta, R, K, n, m, X, T, Y, s)
-                     : run_expand_f32<false>(values, meta, R, K, n, m, X, T, Y, s);
+      return run_expand_layout<kF32, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s);
     return run_generic_layout<kF32, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s);
   }
-  if (dt == kBF16)
+  if (dt == kBF16) {
+    if (T % 8 == 0)
+      return y_dt == kF32
+                 ? run_expand_layout<kBF16, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s)
+                 : run_expand_layout<kBF16, kBF16>(values, meta, R, K, n, m, blocked, X, T, Y, s);
     return y_dt == kF32
                ? run_generic_layout<kBF16, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s)
                : run_generic_layout<kBF16, kBF16>(values, meta, R, K, n, m, blocked, X, T, Y, s);
+  }
+  if (T % 8 == 0)
+    return y_dt == kF32
+               ? run_expand_layout<kF16, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s)
+               : run_expand_layout<kF16, kF16>(values, meta, R, K, n, m, blocked, X, T, Y, s);
   return y_dt == kF32
              ? run_generic_layout<kF16, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s)
              : run_generic_layout<kF16, kF16>(values, meta, R, K, n, m, blocked, X, T, Y, s);

@@ -196,14 +196,17 @@ def test_select_empty():
 # sparse x dense product
 # ---------------------------------------------------------------------------
 
-# (R, K, T): several tiles with ragged row and column tails; 2:4 and 1:2 with K a multiple
-# of 64 and T of 8 take the matrix-core kernel, everything else the generic one.
+# (R, K, T): several tiles with ragged row and column tails.  16-bit: 2:4 and 1:2 with K a
+# multiple of 64 and T of 8 take the structured-sparse kernels, 4:8 the expanded-group one,
+# other patterns with T % 8 == 0 the expansion kernel (K = 96 and 40: a K tail inside its
+# 64-wide step); T = 13 takes the generic kernel.
 PRODUCT_SHAPES = [(200, 384, 264), (130, 256, 136), (16, 128, 8), (257, 128, 520), (64, 96, 40),
-                  (33, 40, 13)]
+                  (33, 40, 13), (70, 40, 24)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("n,m", [(2, 4), (1, 2), (4, 8), (3, 4), (1, 8)])
+@pytest.mark.parametrize("n,m", [(2, 4), (1, 2), (4, 8), (3, 4), (1, 8), (1, 4), (2, 8), (6, 8),
+                                 (2, 2)])
 @pytest.mark.parametrize("yf32", [False, True])
 @pytest.mark.parametrize("layout", ["rows", "blocked"])
 def test_spmm_elementwise(dtype, n, m, yf32, layout):
