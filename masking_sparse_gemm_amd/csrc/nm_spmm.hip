@@ -639,9 +639,10 @@ __device__ __forceinline__ void widen_frags(AFrags& a) {
 // f = 0..1 across; lane l holds column 32f + l % 32 and rows 8(i/4) + 4(l/32) + i%4 of
 // fragment fm) to Y as YT.  Each 32-row slab passes through `lds` (this wave's own
 // kEpilogueBytes, row-major) so that Y is written in 16-byte pieces of one row -- eight
-// 16-bit or four fp32 outputs -- instead of one output per store.  T % 8 == 0, so a piece
-// is either wholly inside the matrix or wholly outside.  A wave's LDS accesses complete in
-// order, so the reads see this slab's writes and the next slab's writes follow the reads.
+// 16-bit or four fp32 outputs -- instead of one output per store.  When rows of Y are whole
+// 16-byte pieces a piece is either wholly inside the matrix or wholly outside; for any other
+// T each output of a piece is stored on its own.  A wave's LDS accesses complete in order,
+// so the reads see this slab's writes and the next slab's writes follow the reads.
 constexpr int kEpilogueBytes = 32 * (64 * 4 + 16);
 template <int YT, typename AccV = float16v_t>
 __device__ __forceinline__ void store_block_128x64(const AccV (&acc)[4][2], uint8_t* lds,
@@ -677,8 +678,22 @@ __device__ __forceinline__ void store_block_128x64(const AccV (&acc)[4][2], uint
       const int pc = k * 64 + lane, r = pc / kRowPieces, cp = pc % kRowPieces;
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(lds + r * kPitch + cp * 16);
       const int row = row0 + 32 * fm + r, col = col0 + cp * kPer16;
-      if (row < R && col < T)
-        *reinterpret_cast<u32x4_t*>(y + ((int64_t)row * T + col) * kEB) = v;
+      if (T % kPer16 == 0) {  // rows of Y are whole 16-byte pieces
+        if (row < R && col < T)
+          *reinterpret_cast<u32x4_t*>(y + ((int64_t)row * T + col) * kEB) = v;
+      } else if (row < R) {  // any other T: one store per output, none past the last column
+        const uint32_t w[4] = {v[0], v[1], v[2], v[3]};
+#pragma unroll
+        for (int e = 0; e < kPer16; ++e) {
+          if (col + e < T) {
+            uint8_t* d = y + ((int64_t)row * T + col + e) * kEB;
+            if constexpr (kEB == 4)
+              *reinterpret_cast<uint32_t*>(d) = w[e];
+            else
+              *reinterpret_cast<uint16_t*>(d) = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+          }
+        }
+      }
     }
   }
 }
@@ -916,7 +931,7 @@ struct WsTile {
 };
 
 template <bool BF16, bool kPat12, bool kBlocked, int YT, int BM, int BN, int CWAVES_M,
-          int CWAVES_N, int PWAVES, int STAGES>
+          int CWAVES_N, int PWAVES, int STAGES, int XB = 16>
 __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
     smfmac_ws_spmm_kernel(const uint16_t* __restrict__ values, const uint32_t* __restrict__ meta,
                           const uint16_t* __restrict__ X, void* __restrict__ Y, int R, int K,
@@ -935,24 +950,39 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
   const int nsteps = K / kKStep;
   const int last_step = nsteps - 1;
 
+  // X pieces per lane: 16 bytes when X rows are whole 16-byte pieces (T % 8 == 0), else 4
+  // bytes (T even), which takes four times the load instructions
+  static_assert(XB == 16 || (XB == 4 && BN * 2 == 64 * XB), "4-byte pieces: one row a load");
+  constexpr int kXLoads = TL::kXBytes / (64 * XB) / TL::kProducers;
   if (wave >= TL::kConsumers) {
     // ---------------- producer ----------------
     const int pw = wave - TL::kConsumers;
     const uint8_t* xg = reinterpret_cast<const uint8_t*>(X);
     const uint8_t* vg = reinterpret_cast<const uint8_t*>(values);
     const uint8_t* mg = reinterpret_cast<const uint8_t*>(meta);
-    int64_t x_src[TL::kXLoads];
-    uint32_t x_dst[TL::kXLoads];
+    int64_t x_src[kXLoads];
+    uint32_t x_dst[kXLoads];
 #pragma unroll
-    for (int j = 0; j < TL::kXLoads; ++j) {
-      const int w1k = j * TL::kProducers + pw;  // 1 KB window of the X tile
-      const int slot = w1k * 64 + lane;
-      const int r = slot / TL::kXChunks, pc = slot % TL::kXChunks;
-      const int lc = 2 * ((pc >> 1) ^ xpair_swizzle(r)) + (pc & 1);
-      int col = t0 + 8 * lc;
-      col = col < T ? col : 0;  // columns past T: any valid address (outputs past T only)
-      x_src[j] = ((int64_t)r * T + col) * 2;
-      x_dst[j] = (uint32_t)(w1k * 1024);
+    for (int j = 0; j < kXLoads; ++j) {
+      if constexpr (XB == 16) {
+        const int w1k = j * TL::kProducers + pw;  // 1 KB window of the X tile
+        const int slot = w1k * 64 + lane;
+        const int r = slot / TL::kXChunks, pc = slot % TL::kXChunks;
+        const int lc = 2 * ((pc >> 1) ^ xpair_swizzle(r)) + (pc & 1);
+        int col = t0 + 8 * lc;
+        col = col < T ? col : 0;  // columns past T: any valid address (outputs past T only)
+        x_src[j] = ((int64_t)r * T + col) * 2;
+        x_dst[j] = (uint32_t)(w1k * 1024);
+      } else {
+        // load j fills K row r = j * kProducers + pw: lane l lands at byte 4 l of the row,
+        // physical pair l / 8, which holds logical pair (l / 8) ^ xpair_swizzle(r)
+        const int r = j * TL::kProducers + pw;
+        const int lp = (lane >> 3) ^ xpair_swizzle(r);
+        int col = t0 + 16 * lp + 2 * (lane & 7);
+        col = col < T ? col : 0;  // T even: col even, so every piece is 4-byte aligned
+        x_src[j] = ((int64_t)r * T + col) * 2;
+        x_dst[j] = (uint32_t)(r * BN * 2);
+      }
     }
     int64_t a_src[TL::kALoads];
     uint32_t a_dst[TL::kALoads];
@@ -991,7 +1021,7 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
       const int64_t ka = (int64_t)step * values_step_bytes<kBlocked>();
       const int64_t km = (int64_t)step * meta_step_bytes<kBlocked, kPat12>();
 #pragma unroll
-      for (int j = 0; j < TL::kXLoads; ++j) global_to_lds<16>(xg + x_src[j] + kx, st + x_dst[j]);
+      for (int j = 0; j < kXLoads; ++j) global_to_lds<XB>(xg + x_src[j] + kx, st + x_dst[j]);
 #pragma unroll
       for (int j = 0; j < TL::kALoads; ++j) global_to_lds<16>(vg + a_src[j] + ka, st + a_dst[j]);
       if constexpr (kWideMeta) {
@@ -1002,7 +1032,8 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
       }
     };
     // direct loads one producer issues per step
-    constexpr int kLoads = TL::kXLoads + TL::kALoads + (kWideMeta ? 1 : TL::kMLoads);
+    constexpr int kLoads = kXLoads + TL::kALoads + (kWideMeta ? 1 : TL::kMLoads);
+    static_assert((kStages - 2) * kLoads <= 63, "vmcnt budget");
 #pragma unroll
     for (int k = 0; k < kStages - 1; ++k) issue_step(k);
     wait_loads_and_barrier<(kStages - 3) * kLoads>();  // steps 0 and 1 landed
@@ -1856,7 +1887,7 @@ __device__ __forceinline__ int ex_col(int c, int kk) {  // fp32: physical column
   return (((c >> 5) ^ ((kk >> 4) & 1)) << 5) | (c & 31);
 }
 
-template <int DT, int YT, int N, int M, bool kBlocked>
+template <int DT, int YT, int N, int M, bool kBlocked, bool kVecX>
 __global__ void __launch_bounds__(256)
     expand_mfma_spmm_kernel(const void* __restrict__ values, const uint32_t* __restrict__ meta,
                             const void* __restrict__ X, void* __restrict__ Y, int64_t R,
@@ -1892,8 +1923,23 @@ __global__ void __launch_bounds__(256)
       const int idx = j * 256 + tid, kk = idx / kChunksPerRow;
       const int c = kPerChunk * (idx % kChunksPerRow);
       const int64_t k = k0 + kk, col = t0 + c;
-      xr[j] = (k < K && col < T) ? *reinterpret_cast<const u32x4_t*>(Xe + k * T + col)
-                                 : u32x4_t{0u, 0u, 0u, 0u};
+      if constexpr (kVecX) {  // rows of X are whole 16-byte pieces
+        xr[j] = (k < K && col < T) ? *reinterpret_cast<const u32x4_t*>(Xe + k * T + col)
+                                   : u32x4_t{0u, 0u, 0u, 0u};
+      } else {  // any T: element loads, zeros past the last column
+        uint32_t wv[4] = {0u, 0u, 0u, 0u};
+        if (k < K) {
+          const E* src = Xe + k * T + col;
+#pragma unroll
+          for (int e = 0; e < kPerChunk; ++e) {
+            if (col + e < T) {
+              if constexpr (kF) wv[e] = __float_as_uint(src[e]);
+              else wv[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
+            }
+          }
+        }
+        xr[j] = u32x4_t{wv[0], wv[1], wv[2], wv[3]};
+      }
     }
 #pragma unroll
     for (int it = 0; it < kItems; ++it) {
@@ -2072,7 +2118,7 @@ __global__ void __launch_bounds__(256)
     }
 }
 
-template <int DT, int YT, bool kBlocked>
+template <int DT, int YT, bool kBlocked, bool kVecX>
 hipError_t run_expand(const void* values, const uint32_t* meta, int64_t R, int64_t K, int n,
                       int m, const void* X, int64_t T, void* Y, hipStream_t s) {
   const int64_t tiles_n = (T + kEN - 1) / kEN, tiles = (R + kEM - 1) / kEM * tiles_n;
@@ -2080,7 +2126,7 @@ hipError_t run_expand(const void* values, const uint32_t* meta, int64_t R, int64
   constexpr size_t lds = 2 * kEStageWords * sizeof(uint32_t);
 #define NM_E(NN, MM)                                                                       \
   if (n == NN && m == MM) {                                                                \
-    auto kernel = expand_mfma_spmm_kernel<DT, YT, NN, MM, kBlocked>;                       \
+    auto kernel = expand_mfma_spmm_kernel<DT, YT, NN, MM, kBlocked, kVecX>;                \
     static const hipError_t attr =                                                         \
         hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),                         \
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);         \
@@ -2096,12 +2142,17 @@ hipError_t run_expand(const void* values, const uint32_t* meta, int64_t R, int64
   return hipErrorInvalidValue;
 }
 
+// X rows of whole 16-byte pieces take vector loads, any other T element loads.
 template <int DT, int YT>
 hipError_t run_expand_layout(const void* values, const uint32_t* meta, int64_t R, int64_t K,
                              int n, int m, bool blocked, const void* X, int64_t T, void* Y,
                              hipStream_t s) {
-  return blocked ? run_expand<DT, YT, true>(values, meta, R, K, n, m, X, T, Y, s)
-                 : run_expand<DT, YT, false>(values, meta, R, K, n, m, X, T, Y, s);
+  const bool vec = T % (DT == kF32 ? 4 : 8) == 0;
+  if (vec)
+    return blocked ? run_expand<DT, YT, true, true>(values, meta, R, K, n, m, X, T, Y, s)
+                   : run_expand<DT, YT, false, true>(values, meta, R, K, n, m, X, T, Y, s);
+  return blocked ? run_expand<DT, YT, true, false>(values, meta, R, K, n, m, X, T, Y, s)
+                 : run_expand<DT, YT, false, false>(values, meta, R, K, n, m, X, T, Y, s);
 }
 
 __global__ void zero_fill_kernel(uint32_t* __restrict__ p, int64_t words, int64_t tail_halves) {
@@ -2164,7 +2215,7 @@ using TileOf = std::conditional_t<
                        WsTile<BM, BN, WM_, WN_, PW, ST_>>>;
 
 template <bool BF16, bool kPat12, bool kBlocked, int YT, int KIND, int BM, int BN, int WM_,
-          int WN_, int PW, int ST_>
+          int WN_, int PW, int ST_, int XB = 16>
 hipError_t launch_tile(const void* values, const uint32_t* meta, int64_t R, int64_t K,
                        const void* X, int64_t T, void* Y, hipStream_t s) {
   using TL = TileOf<KIND, BM, BN, WM_, WN_, PW, ST_>;
@@ -2175,7 +2226,7 @@ hipError_t launch_tile(const void* values, const uint32_t* meta, int64_t R, int6
   else if constexpr (KIND == 1)
     kernel = smfmac32_spmm_kernel<BF16, kPat12, kBlocked, YT, BM, BN, WM_, WN_, ST_>;
   else
-    kernel = smfmac_ws_spmm_kernel<BF16, kPat12, kBlocked, YT, BM, BN, WM_, WN_, PW, ST_>;
+    kernel = smfmac_ws_spmm_kernel<BF16, kPat12, kBlocked, YT, BM, BN, WM_, WN_, PW, ST_, XB>;
   const size_t lds = (size_t)ST_ * TL::kStageBytes;
   static const hipError_t attr =
       hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
@@ -2229,6 +2280,9 @@ int pick_tile(int64_t R, int64_t K, int64_t T) {
 template <bool BF16, bool kPat12, bool kBlocked, int YT>
 hipError_t run_smfmac(const void* values, const uint32_t* meta, int64_t R, int64_t K,
                       const void* X, int64_t T, void* Y, hipStream_t s) {
+  if (T % 8 != 0)  // even T: the wave-specialised tile with 4-byte X pieces
+    return launch_tile<BF16, kPat12, kBlocked, YT, 2, 256, 128, 2, 2, 4, 4, 4>(values, meta, R,
+                                                                              K, X, T, Y, s);
   switch (pick_tile(R, K, T)) {
     case 0:
       return launch_tile<BF16, kPat12, kBlocked, YT, 1, 256, 256, 2, 4, 0, 3>(values, meta, R, K,
@@ -2292,7 +2346,10 @@ hipError_t launch_spmm(const void* values, const uint32_t* meta, int64_t R, int6
     NM_48(false, kF16)
 #undef NM_48
   }
-  if (half && (pat24 || pat12) && tiled_shape) {
+  // the structured-sparse kernels also take even T (4-byte X pieces)
+  const bool sparse_shape = K > 0 && K % kKStep == 0 && T % 2 == 0 && R < (1 << 30) &&
+                            T < (1 << 30) && K < (1 << 30);
+  if (half && (pat24 || pat12) && sparse_shape) {
     const bool yf32 = y_dt == kF32;
 #define NM_S(BF, P12)                                                                       \
   return yf32 ? run_smfmac_layout<BF, P12, kF32>(values, meta, R, K, blocked, X, T, Y, s)   \
@@ -2337,28 +2394,16 @@ hipError_t launch_spmm(const void* values, const uint32_t* meta, int64_t R, int6
     return yf32 ? run_generic_layout<kFP8, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s)
                 : run_generic_layout<kFP8, kBF16>(values, meta, R, K, n, m, blocked, X, T, Y, s);
   }
-  // the expansion kernel reads X in 16-byte pieces: rows of whole 16 bytes
-  if (dt == kF32) {
-    if (T % 4 == 0)
-      return run_expand_layout<kF32, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s);
-    return run_generic_layout<kF32, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s);
-  }
-  if (dt == kBF16) {
-    if (T % 8 == 0)
-      return y_dt == kF32
-                 ? run_expand_layout<kBF16, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s)
-                 : run_expand_layout<kBF16, kBF16>(values, meta, R, K, n, m, blocked, X, T, Y, s);
+  // 16-bit and fp32 cases the kernels above do not take: the expansion kernel
+  if (dt == kF32)
+    return run_expand_layout<kF32, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s);
+  if (dt == kBF16)
     return y_dt == kF32
-               ? run_generic_layout<kBF16, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s)
-               : run_generic_layout<kBF16, kBF16>(values, meta, R, K, n, m, blocked, X, T, Y, s);
-  }
-  if (T % 8 == 0)
-    return y_dt == kF32
-               ? run_expand_layout<kF16, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s)
-               : run_expand_layout<kF16, kF16>(values, meta, R, K, n, m, blocked, X, T, Y, s);
+               ? run_expand_layout<kBF16, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s)
+               : run_expand_layout<kBF16, kBF16>(values, meta, R, K, n, m, blocked, X, T, Y, s);
   return y_dt == kF32
-             ? run_generic_layout<kF16, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s)
-             : run_generic_layout<kF16, kF16>(values, meta, R, K, n, m, blocked, X, T, Y, s);
+             ? run_expand_layout<kF16, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s)
+             : run_expand_layout<kF16, kF16>(values, meta, R, K, n, m, blocked, X, T, Y, s);
 }
 
 }  // namespace nm

@@ -198,10 +198,10 @@ def test_select_empty():
 
 # (R, K, T): several tiles with ragged row and column tails.  16-bit: 2:4 and 1:2 with K a
 # multiple of 64 and T of 8 take the structured-sparse kernels, 4:8 the expanded-group one,
-# other patterns with T % 8 == 0 the expansion kernel (K = 96 and 40: a K tail inside its
-# 64-wide step); T = 13 takes the generic kernel.
+# everything else the expansion kernel (K = 96 and 40: a K tail inside its 64-wide step;
+# T = 13, 70 and 261: rows of X that are not whole 16-byte pieces, loaded element-wise).
 PRODUCT_SHAPES = [(200, 384, 264), (130, 256, 136), (16, 128, 8), (257, 128, 520), (64, 96, 40),
-                  (33, 40, 13), (70, 40, 24)]
+                  (33, 40, 13), (70, 40, 24), (130, 256, 70), (129, 128, 261), (300, 192, 262)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
@@ -224,6 +224,21 @@ def test_spmm_elementwise(dtype, n, m, yf32, layout):
         check_product(Y, y_ref, s, K // m * n, dtype, y_dtype, f"{R}x{K}x{T} {n}:{m} {layout}")
 
 
+@pytest.mark.parametrize("dtype,n,m", [("bf16", 2, 4), ("f16", 1, 2)])
+@pytest.mark.parametrize("layout", ["rows", "blocked"])
+def test_spmm_even_ragged_columns(dtype, n, m, layout):
+    """Even T that is not a multiple of 8 (X rows not whole 16-byte pieces): the
+    structured-sparse kernel with 4-byte X pieces, over many tiles, against the oracle."""
+    rng = np.random.default_rng(67)
+    R, K, T = 600, 512, 1022
+    W = encode(rng.standard_normal((R, K)), dtype)
+    X = encode(rng.standard_normal((K, T)), dtype)
+    vals, meta, vals_o, meta_o = compressed(W, dtype, n, m, layout)
+    Y = nm.spmm(vals, meta, dev(X, dtype), n, m, layout=layout, rows=R)
+    y_ref, s = reference_product(vals_o, meta_o, R, K, n, m, X, dtype)
+    check_product(Y, y_ref, s, K // m * n, dtype, dtype, f"{R}x{K}x{T} {layout}")
+
+
 @pytest.mark.parametrize("tile", ["0", "1", "2"])
 @pytest.mark.parametrize("dtype,n,m", [("bf16", 2, 4), ("f16", 1, 2)])
 @pytest.mark.parametrize("layout", ["rows", "blocked"])
@@ -241,8 +256,8 @@ def test_spmm_every_tile_shape(tile, dtype, n, m, layout, monkeypatch):
         check_product(Y, y_ref, s, K // m * n, dtype, "f32", f"tile {tile} {R}x{K}x{T} {layout}")
 
 
-# fp32: T % 4 == 0 takes the matrix-core kernel (any pattern; K tails inside its 32-wide
-# step: K = 200, 72, 8, 40), the rest the generic kernel (T = 13)
+# fp32: the matrix-core expansion kernel for every pattern (K tails inside its 32-wide step:
+# K = 200, 72, 8, 40; T = 13 and 261 load X element-wise)
 F32_SHAPES = PRODUCT_SHAPES + [(70, 200, 132), (129, 72, 260), (1, 8, 4), (300, 320, 4)]
 
 
