@@ -1471,7 +1471,7 @@ __device__ __forceinline__ float16v_t mfma32x32x16(const u32x4_t& a, const u32x4
 }
 
 template <bool BF16, bool kBlocked, int YT, int BM, int BN, int CWAVES_M, int CWAVES_N,
-          int PWAVES, int STAGES>
+          int PWAVES, int STAGES, int XB = 16>
 __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
     mfma48_ws_spmm_kernel(const uint16_t* __restrict__ values, const uint32_t* __restrict__ meta,
                           const uint16_t* __restrict__ X, void* __restrict__ Y, int R, int K,
@@ -1497,18 +1497,33 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
     const uint8_t* xg = reinterpret_cast<const uint8_t*>(X);
     const uint8_t* vg = reinterpret_cast<const uint8_t*>(values);
     const uint8_t* mg = reinterpret_cast<const uint8_t*>(meta);
-    int64_t x_src[TL::kXLoads];
-    uint32_t x_dst[TL::kXLoads];
+    // X pieces of 16 bytes, or of 4 bytes for even T that is not a multiple of 8 (as in
+    // smfmac_ws_spmm_kernel)
+    static_assert(XB == 16 || (XB == 4 && BN * 2 == 64 * XB), "4-byte pieces: one row a load");
+    constexpr int kXLoads = TL::kXBytes / (64 * XB) / TL::kProducers;
+    constexpr int kLoads = kXLoads + TL::kALoads + TL::kMLoads;
+    static_assert((kStages - 2) * kLoads <= 63, "vmcnt budget");
+    int64_t x_src[kXLoads];
+    uint32_t x_dst[kXLoads];
 #pragma unroll
-    for (int j = 0; j < TL::kXLoads; ++j) {
-      const int w1k = j * TL::kProducers + pw;
-      const int slot = w1k * 64 + lane;
-      const int r = slot / TL::kXChunks, pc = slot % TL::kXChunks;
-      const int lc = 2 * ((pc >> 1) ^ xpair_swizzle(r)) + (pc & 1);
-      int col = t0 + 8 * lc;
-      col = col < T ? col : 0;
-      x_src[j] = ((int64_t)r * T + col) * 2;
-      x_dst[j] = (uint32_t)(w1k * 1024);
+    for (int j = 0; j < kXLoads; ++j) {
+      if constexpr (XB == 16) {
+        const int w1k = j * TL::kProducers + pw;
+        const int slot = w1k * 64 + lane;
+        const int r = slot / TL::kXChunks, pc = slot % TL::kXChunks;
+        const int lc = 2 * ((pc >> 1) ^ xpair_swizzle(r)) + (pc & 1);
+        int col = t0 + 8 * lc;
+        col = col < T ? col : 0;
+        x_src[j] = ((int64_t)r * T + col) * 2;
+        x_dst[j] = (uint32_t)(w1k * 1024);
+      } else {
+        const int r = j * TL::kProducers + pw;  // one K row per load
+        const int lp = (lane >> 3) ^ xpair_swizzle(r);
+        int col = t0 + 16 * lp + 2 * (lane & 7);
+        col = col < T ? col : 0;
+        x_src[j] = ((int64_t)r * T + col) * 2;
+        x_dst[j] = (uint32_t)(r * BN * 2);
+      }
     }
     int64_t a_src[TL::kALoads];
     uint32_t a_dst[TL::kALoads];
@@ -1549,7 +1564,7 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
       const int64_t ka = (int64_t)step * values_step_bytes<kBlocked>();
       const int64_t km = (int64_t)step * (kBlocked ? 192 : 12);
 #pragma unroll
-      for (int j = 0; j < TL::kXLoads; ++j) global_to_lds<16>(xg + x_src[j] + kx, st + x_dst[j]);
+      for (int j = 0; j < kXLoads; ++j) global_to_lds<XB>(xg + x_src[j] + kx, st + x_dst[j]);
 #pragma unroll
       for (int j = 0; j < TL::kALoads; ++j) global_to_lds<16>(vg + a_src[j] + ka, st + a_dst[j]);
 #pragma unroll
@@ -1589,13 +1604,13 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
     };
 #pragma unroll
     for (int k = 0; k < kStages - 1; ++k) issue_step(k);
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kStages - 3) * TL::kLoads) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kStages - 3) * kLoads) : "memory");
     build_keep_masks(0);
     build_keep_masks(1);
     asm volatile("s_barrier" ::: "memory");  // steps 0 and 1 landed, their masks built
     for (int s = 0; s < nsteps; ++s) {
       issue_step(s + kStages - 1);
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kStages - 3) * TL::kLoads) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kStages - 3) * kLoads) : "memory");
       build_keep_masks(s + 2);  // past the end: stale data of an unused stage, never read
       asm volatile("s_barrier" ::: "memory");  // step s+2 landed and its masks built
     }
@@ -2297,13 +2312,13 @@ hipError_t run_smfmac(const void* values, const uint32_t* meta, int64_t R, int64
 }
 
 // 4:8, 16-bit, either layout: dense matrix cores on expanded groups, 256 x 128 tiles.
-template <bool BF16, bool kBlocked, int YT>
+template <bool BF16, bool kBlocked, int YT, int XB>
 hipError_t run_mfma48(const void* values, const uint32_t* meta, int64_t R, int64_t K,
                       const void* X, int64_t T, void* Y, hipStream_t s) {
   constexpr int BM = 256, BN = 128, ST = 4;
   using TL = Ws48Tile<BM, BN, 2, 2, 4, ST>;
   const int tiles_m = (int)((R + BM - 1) / BM), tiles_n = (int)((T + BN - 1) / BN);
-  auto kernel = mfma48_ws_spmm_kernel<BF16, kBlocked, YT, BM, BN, 2, 2, 4, ST>;
+  auto kernel = mfma48_ws_spmm_kernel<BF16, kBlocked, YT, BM, BN, 2, 2, 4, ST, XB>;
   const size_t lds = (size_t)ST * TL::kStageBytes + TL::kLutBytes;
   static const hipError_t attr =
       hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
@@ -2330,14 +2345,18 @@ hipError_t launch_spmm(const void* values, const uint32_t* meta, int64_t R, int6
                        hipStream_t s) {
   if (R == 0 || T == 0) return hipSuccess;
   const bool pat24 = (n == 2 && m == 4), pat12 = (n == 1 && m == 2);
-  // the matrix-core kernel addresses A, its metadata and X with 32-bit byte offsets
-  const bool tiled_shape = K > 0 && K % kKStep == 0 && T % 8 == 0 && R < (1 << 30) &&
-                           T < (1 << 30) && K < (1 << 30);
   const bool half = dt == kBF16 || dt == kF16;
-  if (half && n == 4 && m == 8 && tiled_shape) {
+  // the structured-sparse and 4:8 kernels: K in whole 64-wide steps, even T (X in 16-byte
+  // pieces when T % 8 == 0, else 4-byte ones), 32-bit tile coordinates
+  const bool sparse_shape = K > 0 && K % kKStep == 0 && T % 2 == 0 && R < (1 << 30) &&
+                            T < (1 << 30) && K < (1 << 30);
+  if (half && n == 4 && m == 8 && sparse_shape) {
 #define NM_48(BF, YT)                                                                   \
-  return blocked ? run_mfma48<BF, true, YT>(values, meta, R, K, X, T, Y, s)             \
-                 : run_mfma48<BF, false, YT>(values, meta, R, K, X, T, Y, s);
+  if (T % 8 != 0)                                                                       \
+    return blocked ? run_mfma48<BF, true, YT, 4>(values, meta, R, K, X, T, Y, s)        \
+                   : run_mfma48<BF, false, YT, 4>(values, meta, R, K, X, T, Y, s);      \
+  return blocked ? run_mfma48<BF, true, YT, 16>(values, meta, R, K, X, T, Y, s)         \
+                 : run_mfma48<BF, false, YT, 16>(values, meta, R, K, X, T, Y, s);
     if (dt == kBF16) {
       if (y_dt == kF32) { NM_48(true, kF32) }
       NM_48(true, kBF16)
@@ -2346,9 +2365,6 @@ hipError_t launch_spmm(const void* values, const uint32_t* meta, int64_t R, int6
     NM_48(false, kF16)
 #undef NM_48
   }
-  // the structured-sparse kernels also take even T (4-byte X pieces)
-  const bool sparse_shape = K > 0 && K % kKStep == 0 && T % 2 == 0 && R < (1 << 30) &&
-                            T < (1 << 30) && K < (1 << 30);
   if (half && (pat24 || pat12) && sparse_shape) {
     const bool yf32 = y_dt == kF32;
 #define NM_S(BF, P12)                                                                       \

@@ -224,11 +224,12 @@ def test_spmm_elementwise(dtype, n, m, yf32, layout):
         check_product(Y, y_ref, s, K // m * n, dtype, y_dtype, f"{R}x{K}x{T} {n}:{m} {layout}")
 
 
-@pytest.mark.parametrize("dtype,n,m", [("bf16", 2, 4), ("f16", 1, 2)])
+@pytest.mark.parametrize("dtype,n,m", [("bf16", 2, 4), ("f16", 1, 2), ("bf16", 4, 8)])
 @pytest.mark.parametrize("layout", ["rows", "blocked"])
 def test_spmm_even_ragged_columns(dtype, n, m, layout):
     """Even T that is not a multiple of 8 (X rows not whole 16-byte pieces): the
-    structured-sparse kernel with 4-byte X pieces, over many tiles, against the oracle."""
+    structured-sparse and 4:8 kernels with 4-byte X pieces, over many tiles, against the
+    oracle."""
     rng = np.random.default_rng(67)
     R, K, T = 600, 512, 1022
     W = encode(rng.standard_normal((R, K)), dtype)
