@@ -180,9 +180,13 @@ nm_status nm_decompress(const void* values, const uint32_t* meta, nm_dtype dt, i
  * the exact integer product (K < 2^17, else NM_ERR_SHAPE, so no sum can overflow).
  * For dt = NM_FP8, y_dt is NM_F32 or NM_BF16 (fp32 accumulation, one rounding).  The
  * metadata is trusted (well-formedness is the caller's responsibility, as for any
- * compressed operand; nm_check_meta checks it on the host).  Both layouts are
- * accepted; the matrix-core kernels (2:4 and 1:2, 16-bit dt) stream
- * NM_LAYOUT_BLOCKED at full speed and NM_LAYOUT_ROWS at a lower rate. */
+ * compressed operand; nm_check_meta checks it on the host).  Every shape and pattern
+ * is accepted.  Fastest: 2:4 or 1:2 (16-bit on the structured-sparse matrix cores,
+ * int8 and fp8 on their 8-bit form), NM_LAYOUT_BLOCKED (NM_LAYOUT_ROWS runs at a lower
+ * rate), K % 64 == 0 (K % 128 for 8-bit) and T % 8 == 0 (T % 16 for 8-bit); even T
+ * runs on the same 16-bit kernels with narrower X loads; other 16-bit and fp32 cases
+ * run on the dense matrix cores over tiles expanded in LDS, and the rest on a plain
+ * fp32 FMA kernel. */
 nm_status nm_spmm(const void* values, const uint32_t* meta, int64_t R, int64_t K, int n, int m,
                   nm_layout layout, const void* X, int64_t T, nm_dtype dt, void* Y,
                   nm_dtype y_dt, nm_stream_t stream);
