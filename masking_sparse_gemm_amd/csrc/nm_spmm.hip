@@ -27,11 +27,12 @@
 //    expanded in registers with byte permutes.
 //  * smfmac_i8_ws_spmm_kernel: 2:4 and 1:2 int8 (exact int32) and fp8 (fp32 accumulation)
 //    on the 32x32x64 8-bit instructions.
-//  * expand_mfma_spmm_kernel: fp32 (any pattern) and 16-bit patterns without a sparse
-//    kernel; the compressed rows are expanded in LDS and multiplied on the dense matrix
-//    cores (v_mfma_f32_32x32x2_f32, v_mfma_f32_32x32x16_{bf16,f16}).
-//  * generic_spmm_kernel: every other pattern and shapes the tiled kernels do not take; it
-//    expands the compressed rows to fp32 in LDS and accumulates with fp32 FMAs.
+//  * expand_mfma_spmm_kernel: fp32 (any pattern), and 16-bit and fp8 patterns and shapes
+//    the kernels above do not take; the compressed rows are expanded in LDS (fp8 widened
+//    to bf16) and multiplied on the dense matrix cores (v_mfma_f32_32x32x2_f32,
+//    v_mfma_f32_32x32x16_{bf16,f16}).
+//  * generic_spmm_kernel: int8 patterns and shapes the 8-bit kernel does not take; it
+//    expands the compressed rows in LDS and accumulates with VALU multiply-adds.
 // The blocked layout (include/nm.h) makes every direct load of compressed values or
 // metadata one contiguous run; the row layout is accepted by the same kernels at a lower
 // rate.  Accumulators are fp32 (int32 for int8) and rounded once to the output type.
@@ -1880,8 +1881,10 @@ __global__ void __launch_bounds__(256) generic_spmm_kernel(const void* __restric
 // ===========================================================================
 // Any N:M on the dense matrix cores: the compressed rows are expanded in LDS (zeros where
 // pruned, as in the generic kernel) and multiplied with v_mfma_f32_32x32x2_f32 (fp32) or
-// v_mfma_f32_32x32x16_{bf16,f16} (16-bit patterns without a structured-sparse kernel).
-// This is the dense product of the decompressed tile, reading only the compressed pair, so
+// v_mfma_f32_32x32x16_{bf16,f16} (16-bit patterns without a structured-sparse kernel, and
+// fp8, whose values and X are widened exactly to bf16 on the way into LDS: an E4M3 value has
+// at most four significant bits and lies inside bf16's exponent range; products are then
+// exact in fp32 and summed in fp32).  This is the dense product of the decompressed tile, reading only the compressed pair, so
 // it can at best match a dense GEMM.  The loads of step s+1 go to registers before step
 // s's matrix instructions and into the other LDS stage after them (one barrier per step).
 // Workgroup: 128 x 128 outputs, four waves of 64 x 64 (2 x 2 blocks of 32 x 32).
@@ -1908,16 +1911,18 @@ __global__ void __launch_bounds__(256)
                             const void* __restrict__ X, void* __restrict__ Y, int64_t R,
                             int64_t K, int64_t T, int64_t tiles_n) {
   constexpr bool kF = DT == kF32;
-  using E = std::conditional_t<kF, float, uint16_t>;
+  constexpr bool k8 = DT == kFP8;  // fp8: widened to bf16 (exactly) when written to LDS
+  using E = std::conditional_t<kF, float, std::conditional_t<k8, uint8_t, uint16_t>>;
   constexpr int kEK = kF ? 32 : 64;          // K per step
   constexpr int kPerChunk = 16 / sizeof(E);  // X elements per 16-byte piece
   constexpr int kChunksPerRow = kEN / kPerChunk;
+  constexpr int kXPieces = kEK * kEN * (int)sizeof(E) / 16 / 256;  // per thread and step
   constexpr int b = meta_bits(M);
   constexpr int kGPS = kEK / M;              // groups per row and step
   constexpr int kItems = kEM * kGPS / 256;   // (row, group) items per thread and step
   constexpr int64_t V = 64 / M * N;          // blocked layout: values per row per 64 of K
   static_assert(kItems * 256 == kEM * kGPS, "whole items per thread");
-  static_assert(kEK * kEN * (int)sizeof(E) == 4096 * 4, "16 KB of X per step");
+  static_assert(kXPieces * 256 * 16 == kEK * kEN * (int)sizeof(E), "whole X pieces");
   extern __shared__ __attribute__((aligned(16))) uint32_t ex_smem[];  // two stages
   const E* vals = static_cast<const E*>(values);
   const E* Xe = static_cast<const E*>(X);
@@ -1934,7 +1939,7 @@ __global__ void __launch_bounds__(256)
   uint32_t mw0[kItems], mw1[kItems], msh[kItems];
   auto fetch = [&](int64_t k0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kXPieces; ++j) {
       const int idx = j * 256 + tid, kk = idx / kChunksPerRow;
       const int c = kPerChunk * (idx % kChunksPerRow);
       const int64_t k = k0 + kk, col = t0 + c;
@@ -1949,6 +1954,7 @@ __global__ void __launch_bounds__(256)
           for (int e = 0; e < kPerChunk; ++e) {
             if (col + e < T) {
               if constexpr (kF) wv[e] = __float_as_uint(src[e]);
+              else if constexpr (k8) wv[e >> 2] |= (uint32_t)src[e] << (8 * (e & 3));
               else wv[e >> 1] |= (uint32_t)src[e] << (16 * (e & 1));
             }
           }
@@ -1988,15 +1994,27 @@ __global__ void __launch_bounds__(256)
     uint32_t* As = ex_smem + stage * kEStageWords;
     uint32_t* Xs = As + kEM * kEARow;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kXPieces; ++j) {
       const int idx = j * 256 + tid, kk = idx / kChunksPerRow, pc = idx % kChunksPerRow;
-      int word;
       if constexpr (kF) {
-        word = kk * kEN + ex_col(4 * pc, kk);
+        *reinterpret_cast<u32x4_t*>(Xs + kk * kEN + ex_col(4 * pc, kk)) = xr[j];
+      } else if constexpr (k8) {
+        // 16 fp8 columns -> one 32-byte column pair of bf16
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t lo = (xr[j][e >> 1] >> (16 * (e & 1))) & 0xFFu;
+          const uint32_t hi = (xr[j][e >> 1] >> (16 * (e & 1) + 8)) & 0xFFu;
+          h[e] = (__float_as_uint(e4m3_to_f32(lo)) >> 16) |
+                 (__float_as_uint(e4m3_to_f32(hi)) & 0xFFFF0000u);
+        }
+        uint32_t* d = Xs + kk * (kEN / 2) + 8 * (pc ^ xpair_swizzle(kk));
+        *reinterpret_cast<u32x4_t*>(d) = u32x4_t{h[0], h[1], h[2], h[3]};
+        *reinterpret_cast<u32x4_t*>(d + 4) = u32x4_t{h[4], h[5], h[6], h[7]};
       } else {
-        word = kk * (kEN / 2) + 4 * (2 * ((pc >> 1) ^ xpair_swizzle(kk)) + (pc & 1));
+        const int word = kk * (kEN / 2) + 4 * (2 * ((pc >> 1) ^ xpair_swizzle(kk)) + (pc & 1));
+        *reinterpret_cast<u32x4_t*>(Xs + word) = xr[j];
       }
-      *reinterpret_cast<u32x4_t*>(Xs + word) = xr[j];
     }
 #pragma unroll
     for (int it = 0; it < kItems; ++it) {
@@ -2010,6 +2028,7 @@ __global__ void __launch_bounds__(256)
         const int p = (int)((fields >> (j * b)) & ((1u << b) - 1u));
         uint32_t v;
         if constexpr (kF) v = __float_as_uint(vr[it][j]);
+        else if constexpr (k8) v = __float_as_uint(e4m3_to_f32(vr[it][j])) >> 16;
         else v = vr[it][j];
 #pragma unroll
         for (int e = 0; e < M; ++e) o[e] = (p == e) ? v : o[e];
@@ -2111,7 +2130,7 @@ __global__ void __launch_bounds__(256)
         for (int fm = 0; fm < 2; ++fm)
 #pragma unroll
           for (int fn = 0; fn < 2; ++fn)
-            acc[fm][fn] = mfma32x32x16<DT == kBF16>(a[fm], bb[fn], acc[fm][fn]);
+            acc[fm][fn] = mfma32x32x16<DT != kF16>(a[fm], bb[fn], acc[fm][fn]);
       }
     }
     if (more) stash(stage ^ 1);
@@ -2162,7 +2181,7 @@ template <int DT, int YT>
 hipError_t run_expand_layout(const void* values, const uint32_t* meta, int64_t R, int64_t K,
                              int n, int m, bool blocked, const void* X, int64_t T, void* Y,
                              hipStream_t s) {
-  const bool vec = T % (DT == kF32 ? 4 : 8) == 0;
+  const bool vec = T % (DT == kF32 ? 4 : DT == kFP8 ? 16 : 8) == 0;
   if (vec)
     return blocked ? run_expand<DT, YT, true, true>(values, meta, R, K, n, m, X, T, Y, s)
                    : run_expand<DT, YT, false, true>(values, meta, R, K, n, m, X, T, Y, s);
@@ -2407,8 +2426,10 @@ hipError_t launch_spmm(const void* values, const uint32_t* meta, int64_t R, int6
       NM_8(true, kBF16)
     }
 #undef NM_8
-    return yf32 ? run_generic_layout<kFP8, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s)
-                : run_generic_layout<kFP8, kBF16>(values, meta, R, K, n, m, blocked, X, T, Y, s);
+    // other patterns and shapes: the expansion kernel, fp8 widened to bf16 (exact) and
+    // summed in fp32 on the bf16 matrix cores
+    return yf32 ? run_expand_layout<kFP8, kF32>(values, meta, R, K, n, m, blocked, X, T, Y, s)
+                : run_expand_layout<kFP8, kBF16>(values, meta, R, K, n, m, blocked, X, T, Y, s);
   }
   // 16-bit and fp32 cases the kernels above do not take: the expansion kernel
   if (dt == kF32)
