@@ -620,6 +620,30 @@ __device__ __forceinline__ void decompress_lane(const uint32_t* __restrict__ val
   if (sh + L::kBits > 32) window |= (uint64_t)mblk[wi + 1] << 32;
   uint64_t bits = window >> sh;
   if (sh + L::kBits > 64) bits |= (uint64_t)mblk[wi + 2] << (64 - sh);
+  if constexpr (N == 2 && M == 4 && sizeof(E) <= 2) {
+    // 2:4 of 8- or 16-bit elements: each output word is one byte permute of the group's
+    // stored values, selectors 0x0c (a zero byte) except where the two positions point;
+    // the second position is written last, so a repeated position keeps the later value
+#pragma unroll
+    for (int gi = 0; gi < L::kGroups; ++gi) {
+      const uint32_t p0 = (uint32_t)(bits >> (4 * gi)) & 3u;
+      const uint32_t p1 = (uint32_t)(bits >> (4 * gi + 2)) & 3u;
+      if constexpr (sizeof(E) == 1) {  // the group's two values: bytes 2(gi&1), +1 of a word
+        const uint32_t b0 = 2u * (gi & 1);
+        uint32_t sel = 0x0C0C0C0Cu;
+        sel = (sel & ~(0xFFu << (8 * p0))) | (b0 << (8 * p0));
+        sel = (sel & ~(0xFFu << (8 * p1))) | ((b0 + 1u) << (8 * p1));
+        ow[gi] = __builtin_amdgcn_perm(0u, vw[gi >> 1], sel);
+      } else {  // the group's two values are word gi; slot s is bytes 2s, 2s+1 of 8
+        uint64_t sel = 0x0C0C0C0C0C0C0C0Cull;
+        sel = (sel & ~(0xFFFFull << (16 * p0))) | (0x0100ull << (16 * p0));
+        sel = (sel & ~(0xFFFFull << (16 * p1))) | (0x0302ull << (16 * p1));
+        ow[2 * gi] = __builtin_amdgcn_perm(0u, vw[gi], (uint32_t)sel);
+        ow[2 * gi + 1] = __builtin_amdgcn_perm(0u, vw[gi], (uint32_t)(sel >> 32));
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < L::kWords; ++i) ow[i] = 0;
 #pragma unroll
