@@ -218,6 +218,32 @@ __global__ void __launch_bounds__(kThreads) flat_select_kernel(const uint32_t* _
 // ---------------------------------------------------------------------------
 // Flat decompress kernel: one unit of output per lane.
 // ---------------------------------------------------------------------------
+// 2:4 groups of 8- or 16-bit elements (field 2g, 2g+1 of `bits` = the positions of group
+// g): each output word is one byte permute of the group's stored values, with selector
+// 0x0c (a zero byte) except where the two positions point; the second position is
+// written last, so a repeated position keeps the later value.
+template <typename E, int G>
+__device__ __forceinline__ void expand24(uint64_t bits, const uint32_t* vw, uint32_t* ow) {
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) {
+    const uint32_t p0 = (uint32_t)(bits >> (4 * gi)) & 3u;
+    const uint32_t p1 = (uint32_t)(bits >> (4 * gi + 2)) & 3u;
+    if constexpr (sizeof(E) == 1) {  // the group's two values: bytes 2(gi&1), +1 of a word
+      const uint32_t b0 = 2u * (gi & 1);
+      uint32_t sel = 0x0C0C0C0Cu;
+      sel = (sel & ~(0xFFu << (8 * p0))) | (b0 << (8 * p0));
+      sel = (sel & ~(0xFFu << (8 * p1))) | ((b0 + 1u) << (8 * p1));
+      ow[gi] = __builtin_amdgcn_perm(0u, vw[gi >> 1], sel);
+    } else {  // the group's two values are word gi; slot s is bytes 2s, 2s+1 of 8
+      uint64_t sel = 0x0C0C0C0C0C0C0C0Cull;
+      sel = (sel & ~(0xFFFFull << (16 * p0))) | (0x0100ull << (16 * p0));
+      sel = (sel & ~(0xFFFFull << (16 * p1))) | (0x0302ull << (16 * p1));
+      ow[2 * gi] = __builtin_amdgcn_perm(0u, vw[gi], (uint32_t)sel);
+      ow[2 * gi + 1] = __builtin_amdgcn_perm(0u, vw[gi], (uint32_t)(sel >> 32));
+    }
+  }
+}
+
 template <typename E, int N, int M>
 __global__ void __launch_bounds__(kThreads) flat_decompress_kernel(
     const uint32_t* __restrict__ values, const uint32_t* __restrict__ meta, int64_t units,
@@ -250,25 +276,29 @@ __global__ void __launch_bounds__(kThreads) flat_decompress_kernel(
     uint32_t ow[S::kWords];
 #pragma unroll
     for (int i = 0; i < S::kWords; ++i) ow[i] = 0;
+    if constexpr (N == 2 && M == 4 && sizeof(E) <= 2) {
+      expand24<E, S::kGroups>(bits, vw, ow);
+    } else {
 #pragma unroll
-    for (int g = 0; g < S::kGroups; ++g) {
+      for (int g = 0; g < S::kGroups; ++g) {
 #pragma unroll
-      for (int j = 0; j < N; ++j) {
-        const int k = g * N + j;
-        const int p = (bits >> (k * b)) & ((1u << b) - 1u);
-        const uint32_t v = word_elem<E>(vw, k);
-        // out[g*M + p] = v, as selects over the M compile-time positions
+        for (int j = 0; j < N; ++j) {
+          const int k = g * N + j;
+          const int p = (bits >> (k * b)) & ((1u << b) - 1u);
+          const uint32_t v = word_elem<E>(vw, k);
+          // out[g*M + p] = v, as selects over the M compile-time positions
 #pragma unroll
-        for (int i = 0; i < M; ++i) {
-          const int e = g * M + i;
-          if constexpr (sizeof(E) < 4) {
-            constexpr int kPer = 4 / (int)sizeof(E);
-            constexpr uint32_t kMask = sizeof(E) == 1 ? 0xFFu : 0xFFFFu;
-            const uint32_t sh = 8 * (int)sizeof(E) * (e % kPer);
-            const uint32_t cur = ow[e / kPer];
-            ow[e / kPer] = (p == i) ? ((cur & ~(kMask << sh)) | (v << sh)) : cur;
-          } else {
-            ow[e] = (p == i) ? v : ow[e];
+          for (int i = 0; i < M; ++i) {
+            const int e = g * M + i;
+            if constexpr (sizeof(E) < 4) {
+              constexpr int kPer = 4 / (int)sizeof(E);
+              constexpr uint32_t kMask = sizeof(E) == 1 ? 0xFFu : 0xFFFFu;
+              const uint32_t sh = 8 * (int)sizeof(E) * (e % kPer);
+              const uint32_t cur = ow[e / kPer];
+              ow[e / kPer] = (p == i) ? ((cur & ~(kMask << sh)) | (v << sh)) : cur;
+            } else {
+              ow[e] = (p == i) ? v : ow[e];
+            }
           }
         }
       }
@@ -621,27 +651,7 @@ __device__ __forceinline__ void decompress_lane(const uint32_t* __restrict__ val
   uint64_t bits = window >> sh;
   if (sh + L::kBits > 64) bits |= (uint64_t)mblk[wi + 2] << (64 - sh);
   if constexpr (N == 2 && M == 4 && sizeof(E) <= 2) {
-    // 2:4 of 8- or 16-bit elements: each output word is one byte permute of the group's
-    // stored values, selectors 0x0c (a zero byte) except where the two positions point;
-    // the second position is written last, so a repeated position keeps the later value
-#pragma unroll
-    for (int gi = 0; gi < L::kGroups; ++gi) {
-      const uint32_t p0 = (uint32_t)(bits >> (4 * gi)) & 3u;
-      const uint32_t p1 = (uint32_t)(bits >> (4 * gi + 2)) & 3u;
-      if constexpr (sizeof(E) == 1) {  // the group's two values: bytes 2(gi&1), +1 of a word
-        const uint32_t b0 = 2u * (gi & 1);
-        uint32_t sel = 0x0C0C0C0Cu;
-        sel = (sel & ~(0xFFu << (8 * p0))) | (b0 << (8 * p0));
-        sel = (sel & ~(0xFFu << (8 * p1))) | ((b0 + 1u) << (8 * p1));
-        ow[gi] = __builtin_amdgcn_perm(0u, vw[gi >> 1], sel);
-      } else {  // the group's two values are word gi; slot s is bytes 2s, 2s+1 of 8
-        uint64_t sel = 0x0C0C0C0C0C0C0C0Cull;
-        sel = (sel & ~(0xFFFFull << (16 * p0))) | (0x0100ull << (16 * p0));
-        sel = (sel & ~(0xFFFFull << (16 * p1))) | (0x0302ull << (16 * p1));
-        ow[2 * gi] = __builtin_amdgcn_perm(0u, vw[gi], (uint32_t)sel);
-        ow[2 * gi + 1] = __builtin_amdgcn_perm(0u, vw[gi], (uint32_t)(sel >> 32));
-      }
-    }
+    expand24<E, L::kGroups>(bits, vw, ow);
     return;
   }
 #pragma unroll
