@@ -35,7 +35,7 @@
  *              maximise the kept L1 norm with N per row and column; the optimum is a
  *              minimum-cost flow, the fast method a greedy 2-approximation.
  *
- * Readings where the pages are silent (each also listed in the design doc):
+ * Readings where the pages are silent:
  *   - N counts KEPT elements; exactly N values are stored per group.
  *   - Ties between equally good patterns go to the lexicographically first
  *     ascending index tuple (lower index wins).
