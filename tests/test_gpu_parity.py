@@ -201,7 +201,8 @@ def test_select_empty():
 # everything else the expansion kernel (K = 96 and 40: a K tail inside its 64-wide step;
 # T = 13, 70 and 261: rows of X that are not whole 16-byte pieces, loaded element-wise).
 PRODUCT_SHAPES = [(200, 384, 264), (130, 256, 136), (16, 128, 8), (257, 128, 520), (64, 96, 40),
-                  (33, 40, 13), (70, 40, 24), (130, 256, 70), (129, 128, 261), (300, 192, 262)]
+                  (33, 40, 13), (70, 40, 24), (130, 256, 70), (129, 128, 261), (300, 192, 262),
+                  (16, 64, 6), (40, 128, 2), (20, 64, 1)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
