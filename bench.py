@@ -192,7 +192,7 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              "(the kernels shard by rows of W with no exchange, but this build measures one GPU)",
+              "(the kernels shard by rows of W with no exchange, but bench.py measures one GPU)",
               file=sys.stderr)
         return 2
 
