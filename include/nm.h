@@ -184,9 +184,9 @@ nm_status nm_decompress(const void* values, const uint32_t* meta, nm_dtype dt, i
  * is accepted.  Fastest: 2:4 or 1:2 (16-bit on the structured-sparse matrix cores,
  * int8 and fp8 on their 8-bit form), NM_LAYOUT_BLOCKED (NM_LAYOUT_ROWS runs at a lower
  * rate), K % 64 == 0 (K % 128 for 8-bit) and T % 8 == 0 (T % 16 for 8-bit); even T
- * runs on the same 16-bit kernels with narrower X loads; other 16-bit and fp32 cases
- * run on the dense matrix cores over tiles expanded in LDS, and the rest on a plain
- * fp32 FMA kernel. */
+ * runs on the same 16-bit kernels with narrower X loads; every other case runs on the
+ * dense matrix cores over tiles expanded in LDS (8-bit elements widened exactly to bf16;
+ * int8 sums exact). */
 nm_status nm_spmm(const void* values, const uint32_t* meta, int64_t R, int64_t K, int n, int m,
                   nm_layout layout, const void* X, int64_t T, nm_dtype dt, void* Y,
                   nm_dtype y_dt, nm_stream_t stream);

@@ -27,12 +27,11 @@
 //    expanded in registers with byte permutes.
 //  * smfmac_i8_ws_spmm_kernel: 2:4 and 1:2 int8 (exact int32) and fp8 (fp32 accumulation)
 //    on the 32x32x64 8-bit instructions.
-//  * expand_mfma_spmm_kernel: fp32 (any pattern), and 16-bit and fp8 patterns and shapes
-//    the kernels above do not take; the compressed rows are expanded in LDS (fp8 widened
-//    to bf16) and multiplied on the dense matrix cores (v_mfma_f32_32x32x2_f32,
-//    v_mfma_f32_32x32x16_{bf16,f16}).
-//  * generic_spmm_kernel: int8 patterns and shapes the 8-bit kernel does not take; it
-//    expands the compressed rows in LDS and accumulates with VALU multiply-adds.
+//  * expand_mfma_spmm_kernel: every other pattern and shape, any element type; the
+//    compressed rows are expanded in LDS (8-bit elements widened exactly to bf16; int8
+//    sums kept exact in int32) and multiplied on the dense matrix cores
+//    (v_mfma_f32_32x32x2_f32, v_mfma_f32_32x32x16_{bf16,f16}).
+
 // The blocked layout (include/nm.h) makes every direct load of compressed values or
 // metadata one contiguous run; the row layout is accepted by the same kernels at a lower
 // rate.  Accumulators are fp32 (int32 for int8) and rounded once to the output type.
@@ -71,13 +70,6 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float x) {  // round to nearest 
 }
 __device__ __forceinline__ uint32_t f32_to_f16(float x) {  // hardware conversion, RNE
   return __builtin_bit_cast(uint16_t, (_Float16)x);
-}
-template <int DT>
-__device__ __forceinline__ float load_as_f32(const void* p, int64_t i) {
-  if constexpr (DT == kFP8) return e4m3_to_f32(static_cast<const uint8_t*>(p)[i]);
-  else if constexpr (DT == kF32) return static_cast<const float*>(p)[i];
-  else if constexpr (DT == kBF16) return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
-  else return f16_to_f32(static_cast<const uint16_t*>(p)[i]);
 }
 template <int YT>
 __device__ __forceinline__ void store_from_f32(void* p, int64_t i, float v) {
@@ -1763,128 +1755,13 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
 }
 
 // ===========================================================================
-// Shape-agnostic kernel: any N:M, any dtype, any shape with K % M == 0.
-// ===========================================================================
-constexpr int kGT = 64;   // tile rows and columns
-constexpr int kGK = 32;   // K per step (a multiple of every supported M)
-
-// The generic kernel accumulates 16-bit and fp32 inputs in fp32 and int8 inputs in int32
-// (exact for the int8 products: |sum| <= K * 2^14, and the library takes K < 2^17).
-template <int DT>
-struct GenAcc {
-  using T = float;
-};
-template <>
-struct GenAcc<kI8> {
-  using T = int32_t;
-};
-template <int DT>
-__device__ __forceinline__ typename GenAcc<DT>::T load_acc(const void* p, int64_t i) {
-  if constexpr (DT == kI8)
-    return (int32_t) static_cast<const int8_t*>(p)[i];
-  else
-    return load_as_f32<DT>(p, i);
-}
-
-template <int DT, int YT, int N, int M, bool kBlocked>
-__global__ void __launch_bounds__(256) generic_spmm_kernel(const void* __restrict__ values,
-                                                           const uint32_t* __restrict__ meta,
-                                                           const void* __restrict__ X,
-                                                           void* __restrict__ Y, int64_t R,
-                                                           int64_t K, int64_t T) {
-  using A = typename GenAcc<DT>::T;
-  constexpr int b = meta_bits(M);
-  __shared__ A ws[kGT][kGK + 1];
-  __shared__ A xs[kGK][kGT + 4];
-  const int tid = threadIdx.x;
-  const int64_t m0 = (int64_t)blockIdx.y * kGT, t0 = (int64_t)blockIdx.x * kGT;
-  const int64_t gpr = K / M, wpr = (gpr * N * b + 31) / 32;
-  const int ty = tid / 16, tx = tid % 16;
-  A acc[4][4] = {};
-
-  for (int64_t k0 = 0; k0 < K; k0 += kGK) {
-    // expand the compressed rows of this K step into fp32 (zeros where pruned)
-    constexpr int kGroupsPerRow = kGK / M;
-    for (int i = tid; i < kGT * kGroupsPerRow; i += 256) {
-      const int r = i / kGroupsPerRow, gl = i % kGroupsPerRow;
-      const int64_t row = m0 + r, g = k0 / M + gl;
-      A o[M];
-#pragma unroll
-      for (int e = 0; e < M; ++e) o[e] = 0;
-      if (row < R && g < gpr) {
-#pragma unroll
-        for (int j = 0; j < N; ++j) {
-          // field f of the row: value index and metadata bit in the chosen layout
-          const int64_t f = g * N + j;
-          int64_t vi, bit;
-          if constexpr (kBlocked) {
-            constexpr int64_t V = 64 / M * N;  // values per row and 64-wide step
-            const int64_t rr = ((row >> 4) * (K / 64) + f / V) * 16 + (row & 15);
-            vi = rr * V + f % V;
-            bit = rr * V * b + (f % V) * b;
-          } else {
-            vi = row * (gpr * N) + f;
-            bit = row * wpr * 32 + f * b;
-          }
-          uint64_t window = meta[bit / 32];
-          if ((bit % 32) + b > 32) window |= (uint64_t)meta[bit / 32 + 1] << 32;
-          const int p = (int)((window >> (bit % 32)) & ((1u << b) - 1u));
-          const A v = load_acc<DT>(values, vi);
-#pragma unroll
-          for (int e = 0; e < M; ++e) o[e] = (p == e) ? v : o[e];
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < M; ++e) ws[r][gl * M + e] = o[e];
-    }
-    for (int i = tid; i < kGK * kGT; i += 256) {
-      const int kk = i / kGT, c = i % kGT;
-      const int64_t k = k0 + kk, col = t0 + c;
-      xs[kk][c] = (k < K && col < T) ? load_acc<DT>(X, k * T + col) : (A)0;
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < kGK; ++kk) {
-      A wv[4], xv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wv[i] = ws[ty * 4 + i][kk];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) xv[j] = xs[kk][tx * 4 + j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if constexpr (DT == kI8)
-            acc[i][j] += wv[i] * xv[j];
-          else
-            acc[i][j] = __builtin_fmaf(wv[i], xv[j], acc[i][j]);
-        }
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t row = m0 + ty * 4 + i;
-    if (row >= R) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = t0 + tx * 4 + j;
-      if (col >= T) continue;
-      if constexpr (YT == kI32)
-        static_cast<int32_t*>(Y)[row * T + col] = acc[i][j];
-      else
-        store_from_f32<YT>(Y, row * T + col, acc[i][j]);
-    }
-  }
-}
-
-// ===========================================================================
 // Any N:M on the dense matrix cores: the compressed rows are expanded in LDS (zeros where
-// pruned, as in the generic kernel) and multiplied with v_mfma_f32_32x32x2_f32 (fp32) or
+// pruned) and multiplied with v_mfma_f32_32x32x2_f32 (fp32) or
 // v_mfma_f32_32x32x16_{bf16,f16} (16-bit patterns without a structured-sparse kernel, and
-// fp8, whose values and X are widened exactly to bf16 on the way into LDS: an E4M3 value has
-// at most four significant bits and lies inside bf16's exponent range; products are then
-// exact in fp32 and summed in fp32).  This is the dense product of the decompressed tile, reading only the compressed pair, so
+// fp8 and int8, whose values and X are widened exactly to bf16 on the way into LDS: an E4M3
+// value has at most four significant bits and lies inside bf16's exponent range, an int8
+// value is an integer below 2^8; products are then exact in fp32, fp8 sums stay in fp32 and
+// int8 sums move to int32 every 512 of K).  This is the dense product of the decompressed tile, reading only the compressed pair, so
 // it can at best match a dense GEMM.  The loads of step s+1 go to registers before step
 // s's matrix instructions and into the other LDS stage after them (one barrier per step).
 // Workgroup: 128 x 128 outputs, four waves of 64 x 64 (2 x 2 blocks of 32 x 32).
@@ -1911,7 +1788,11 @@ __global__ void __launch_bounds__(256)
                             const void* __restrict__ X, void* __restrict__ Y, int64_t R,
                             int64_t K, int64_t T, int64_t tiles_n) {
   constexpr bool kF = DT == kF32;
-  constexpr bool k8 = DT == kFP8;  // fp8: widened to bf16 (exactly) when written to LDS
+  // fp8 and int8: widened to bf16 (exactly) when written to LDS.  int8 products are summed
+  // exactly: fp32 partial sums of at most 512 products of magnitude <= 2^14 are integers
+  // below 2^24, so every 8 steps (512 of K) they are moved into int32 accumulators.
+  constexpr bool kI = DT == kI8;
+  constexpr bool k8 = DT == kFP8 || kI;
   using E = std::conditional_t<kF, float, std::conditional_t<k8, uint8_t, uint16_t>>;
   constexpr int kEK = kF ? 32 : 64;          // K per step
   constexpr int kPerChunk = 16 / sizeof(E);  // X elements per 16-byte piece
@@ -1926,6 +1807,10 @@ __global__ void __launch_bounds__(256)
   extern __shared__ __attribute__((aligned(16))) uint32_t ex_smem[];  // two stages
   const E* vals = static_cast<const E*>(values);
   const E* Xe = static_cast<const E*>(X);
+  auto widen8 = [](uint32_t code) {  // an 8-bit element as fp32 (exact)
+    if constexpr (kI) return (float)(int8_t)code;
+    else return e4m3_to_f32(code);
+  };
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * kEM;
   const int64_t t0 = (int64_t)(blockIdx.x % tiles_n) * kEN;
@@ -2005,8 +1890,7 @@ __global__ void __launch_bounds__(256)
         for (int e = 0; e < 8; ++e) {
           const uint32_t lo = (xr[j][e >> 1] >> (16 * (e & 1))) & 0xFFu;
           const uint32_t hi = (xr[j][e >> 1] >> (16 * (e & 1) + 8)) & 0xFFu;
-          h[e] = (__float_as_uint(e4m3_to_f32(lo)) >> 16) |
-                 (__float_as_uint(e4m3_to_f32(hi)) & 0xFFFF0000u);
+          h[e] = (__float_as_uint(widen8(lo)) >> 16) | (__float_as_uint(widen8(hi)) & 0xFFFF0000u);
         }
         uint32_t* d = Xs + kk * (kEN / 2) + 8 * (pc ^ xpair_swizzle(kk));
         *reinterpret_cast<u32x4_t*>(d) = u32x4_t{h[0], h[1], h[2], h[3]};
@@ -2028,7 +1912,7 @@ __global__ void __launch_bounds__(256)
         const int p = (int)((fields >> (j * b)) & ((1u << b) - 1u));
         uint32_t v;
         if constexpr (kF) v = __float_as_uint(vr[it][j]);
-        else if constexpr (k8) v = __float_as_uint(e4m3_to_f32(vr[it][j])) >> 16;
+        else if constexpr (k8) v = __float_as_uint(widen8(vr[it][j])) >> 16;
         else v = vr[it][j];
 #pragma unroll
         for (int e = 0; e < M; ++e) o[e] = (p == e) ? v : o[e];
@@ -2078,6 +1962,7 @@ __global__ void __launch_bounds__(256)
   for (int fm = 0; fm < 2; ++fm)
 #pragma unroll
     for (int fn = 0; fn < 2; ++fn) acc[fm][fn] = float16v_t{};
+  int acc_i[kI ? 2 : 1][kI ? 2 : 1][kI ? 16 : 1] = {};  // int8: exact totals
 
   // one barrier per step: step s+1 is written into the other stage while step s's matrix
   // instructions run; that stage was last read in step s-1, before the previous barrier
@@ -2133,6 +2018,18 @@ __global__ void __launch_bounds__(256)
             acc[fm][fn] = mfma32x32x16<DT != kF16>(a[fm], bb[fn], acc[fm][fn]);
       }
     }
+    if constexpr (kI) {
+      if (!more || ((k0 / kEK) & 7) == 7) {  // 512 of K summed exactly in fp32
+#pragma unroll
+        for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < 2; ++fn) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc_i[fm][fn][e] += (int)acc[fm][fn][e];
+            acc[fm][fn] = float16v_t{};
+          }
+      }
+    }
     if (more) stash(stage ^ 1);
     __syncthreads();
     stage ^= 1;
@@ -2147,7 +2044,12 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int64_t row = m0 + wm * 64 + fm * 32 + 8 * (e >> 2) + 4 * q + (e & 3);
-        if (row < R && col < T) store_from_f32<YT>(Y, row * T + col, acc[fm][fn][e]);
+        if (row < R && col < T) {
+          if constexpr (kI)
+            static_cast<int32_t*>(Y)[row * T + col] = acc_i[fm][fn][e];
+          else
+            store_from_f32<YT>(Y, row * T + col, acc[fm][fn][e]);
+        }
       }
     }
 }
@@ -2181,7 +2083,7 @@ template <int DT, int YT>
 hipError_t run_expand_layout(const void* values, const uint32_t* meta, int64_t R, int64_t K,
                              int n, int m, bool blocked, const void* X, int64_t T, void* Y,
                              hipStream_t s) {
-  const bool vec = T % (DT == kF32 ? 4 : DT == kFP8 ? 16 : 8) == 0;
+  const bool vec = T % (DT == kF32 ? 4 : (DT == kFP8 || DT == kI8) ? 16 : 8) == 0;
   if (vec)
     return blocked ? run_expand<DT, YT, true, true>(values, meta, R, K, n, m, X, T, Y, s)
                    : run_expand<DT, YT, false, true>(values, meta, R, K, n, m, X, T, Y, s);
@@ -2193,32 +2095,6 @@ __global__ void zero_fill_kernel(uint32_t* __restrict__ p, int64_t words, int64_
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < words) p[i] = 0u;
   if (i == words && tail_halves) reinterpret_cast<uint16_t*>(p + words)[0] = 0;
-}
-
-template <int DT, int YT, bool kBlocked>
-hipError_t run_generic(const void* values, const uint32_t* meta, int64_t R, int64_t K, int n,
-                       int m, const void* X, int64_t T, void* Y, hipStream_t s) {
-  const dim3 grid((unsigned)((T + kGT - 1) / kGT), (unsigned)((R + kGT - 1) / kGT));
-#define NM_G(NN, MM)                                                                        \
-  if (n == NN && m == MM) {                                                                 \
-    generic_spmm_kernel<DT, YT, NN, MM, kBlocked><<<grid, 256, 0, s>>>(values, meta, X, Y, R, \
-                                                                       K, T);               \
-    return hipGetLastError();                                                               \
-  }
-  NM_G(1, 2) NM_G(2, 2)
-  NM_G(1, 4) NM_G(2, 4) NM_G(3, 4) NM_G(4, 4)
-  NM_G(1, 8) NM_G(2, 8) NM_G(3, 8) NM_G(4, 8)
-  NM_G(5, 8) NM_G(6, 8) NM_G(7, 8) NM_G(8, 8)
-#undef NM_G
-  return hipErrorInvalidValue;
-}
-
-template <int DT, int YT>
-hipError_t run_generic_layout(const void* values, const uint32_t* meta, int64_t R, int64_t K,
-                              int n, int m, bool blocked, const void* X, int64_t T, void* Y,
-                              hipStream_t s) {
-  return blocked ? run_generic<DT, YT, true>(values, meta, R, K, n, m, X, T, Y, s)
-                 : run_generic<DT, YT, false>(values, meta, R, K, n, m, X, T, Y, s);
 }
 
 // XCDs of the current device: MI355X (gfx950) has 8, with 32 compute units each.
@@ -2417,7 +2293,8 @@ hipError_t launch_spmm(const void* values, const uint32_t* meta, int64_t R, int6
                           : run_smfmac_8bit<FP8, false, false, YT>(values, meta, R, K, X, T, Y, s));
   if (dt == kI8) {
     if (tiled_8bit) { NM_8(false, kI32) }
-    return run_generic_layout<kI8, kI32>(values, meta, R, K, n, m, blocked, X, T, Y, s);
+    // other patterns and shapes: the expansion kernel on the bf16 matrix cores, exact
+    return run_expand_layout<kI8, kI32>(values, meta, R, K, n, m, blocked, X, T, Y, s);
   }
   if (dt == kFP8) {  // the same kernel on the fp8 instruction, fp32 accumulation
     const bool yf32 = y_dt == kF32;

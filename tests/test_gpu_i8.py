@@ -93,7 +93,10 @@ def test_i8_product_exact(n, m, layout):
     if layout == "blocked" and not blocked_ok(n, m):
         pytest.skip("pattern not stored in the blocked int8 layout")
     rng = np.random.default_rng(950 + n + m)
-    for R, K, T in [(200, 384, 264), (130, 256, 136), (16, 128, 8), (33, 64, 13), (257, 128, 520)]:
+    # (70, 1280, 48): more than 512 of K, so the expansion kernel's exact fp32 chunks are
+    # moved into int32 several times
+    for R, K, T in [(200, 384, 264), (130, 256, 136), (16, 128, 8), (33, 64, 13), (257, 128, 520),
+                    (70, 1280, 48)]:
         W = int8_matrix(rng, (R, K))
         X = int8_matrix(rng, (K, T), ties=False)
         vals_o, meta_o = oracle.compress(W, "i8", n, m)
@@ -121,6 +124,19 @@ def test_i8_matrix_core_product_exact(R, K, T, layout, n, m):
     got = Y.cpu().numpy().astype(np.float64)
     bad = got != y_ref
     assert not bad.any(), f"{int(bad.sum())} of {bad.size} differ, first at {np.argwhere(bad)[0]}"
+
+
+@pytest.mark.parametrize("n,m", [(4, 8), (1, 4), (3, 4)])
+def test_i8_product_extremes_other_patterns(n, m):
+    """All -128: every output is (K n/m) * 2^14, far past fp32's exact integers, through the
+    expansion kernel's exact int32 totals."""
+    R, K, T = 64, 4096, 64
+    W = np.full((R, K), -128, dtype=np.int8)
+    X = np.full((K, T), -128, dtype=np.int8)
+    for layout in ["rows", "blocked"]:
+        v, mt = nm.compress(dev8(W), n, m, layout=layout)
+        Y = nm.spmm(v, mt, dev8(X), n, m, layout=layout, rows=R)
+        assert bool((Y == K // m * n * 16384).all()), layout
 
 
 def test_i8_product_extremes_and_empty():
