@@ -176,6 +176,71 @@ def cpu_baseline(mats, n, m, threads: int, budget_s: float = 12.0):
             "sample": f"mask+compress+decompress+product of {sample} (fp64 product, all T columns)"}
 
 
+def bf16_sample(a: np.ndarray, dtype: str, count: int = 1 << 20) -> np.ndarray:
+    """bf16 bit patterns of (up to) the first `count` values of a workload array."""
+    a = a.reshape(-1)[:count]
+    if dtype == "bf16":
+        return a.view(np.uint16)
+    if dtype == "f16":
+        a = a.view(np.float16).astype(np.float32)
+    elif dtype in ("i8",):
+        a = a.astype(np.float32)
+    elif dtype != "f32":
+        a = np.zeros(1, dtype=np.float32)
+    return (a.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def matrix_core_ceiling(torch, dev, stream, w_vals, x_vals, waves_per_simd: int = 2):
+    """What the matrix cores sustain alone (libnm_probe): the 2:4 structured-sparse bf16
+    instruction and the dense bf16 one in register-only loops, on three kinds of operands:
+    zeros, small integers, and values drawn from the workload's own weights and
+    activations.  Returns effective (dense-equivalent) TFLOP/s per instruction and kind,
+    and the shader clock the loop ran at (s_memtime over the 100 MHz s_memrealtime)."""
+    import masking_sparse_gemm_amd as nm
+
+    P = nm.probe_lib()
+    props = torch.cuda.get_device_properties(dev)
+    cus = props.multi_processor_count
+    per_lane = 24
+    n_ops = 4 * 64 * per_lane
+    rng = np.random.default_rng(7)
+    kinds = {
+        "zeros": np.zeros(n_ops, dtype=np.uint16),
+        "small_integers": (np.array(rng.integers(-3, 4, n_ops), dtype=np.float32)
+                           .view(np.uint32) >> 16).astype(np.uint16),
+    }
+    # the workload's values: A lanes from W, B lanes from X (bf16 bit patterns)
+    ops = np.empty((4, 64, per_lane), dtype=np.uint16)
+    ops[:, :, :8] = rng.choice(w_vals, size=(4, 64, 8))
+    ops[:, :, 8:] = rng.choice(x_vals, size=(4, 64, 16))
+    kinds["workload"] = ops.reshape(-1)
+    clocks = torch.zeros(4 * cus * waves_per_simd, dtype=torch.int64, device=dev)
+    sink = torch.zeros(cus * waves_per_simd * 256, dtype=torch.float32, device=dev)
+    out = {"waves_per_simd": waves_per_simd, "cus": cus}
+    for kname, arr in kinds.items():
+        dops = torch.from_numpy(arr.view(np.int16)).to(dev)
+        for inst, kind, flops in (("smfmac_32x32x32_bf16", 0, 65536), ("mfma_32x32x16_bf16", 1, 32768)):
+            iters = 4000
+            for _ in range(2):  # warm-up (clock ramp)
+                P.nm_probe_matrix_core(kind, dops.data_ptr(), cus, waves_per_simd, iters,
+                                       clocks.data_ptr(), sink.data_ptr(), stream.cuda_stream)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            rc = P.nm_probe_matrix_core(kind, dops.data_ptr(), cus, waves_per_simd, iters,
+                                        clocks.data_ptr(), sink.data_ptr(), stream.cuda_stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"nm_probe_matrix_core failed ({rc})")
+            t = e0.elapsed_time(e1) * 1e-3
+            insts = cus * waves_per_simd * 4 * iters * 16
+            c = clocks.view(-1, 4).cpu().numpy().astype(np.float64)
+            mhz = float(np.median((c[:, 1] - c[:, 0]) / np.maximum(c[:, 3] - c[:, 2], 1) * 100.0))
+            out[f"{inst}.{kname}"] = {"eff_tflops": round(insts * flops / t / 1e12, 1),
+                                      "clock_mhz": round(mhz, 0), "ms": round(t * 1e3, 3)}
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -186,6 +251,10 @@ def main() -> int:
                     help="storage layout of the compressed weight (include/nm.h)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense GEMM baseline")
+    ap.add_argument("--product-only", action="store_true",
+                    help="time only nm_spmm on the workload's matrices (for profiling runs)")
+    ap.add_argument("--ceiling-only", action="store_true",
+                    help="run only the matrix-core rate probes (libnm_probe)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one 512 MiB device-to-device copy (a kernel of known traffic "
                          "for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -262,6 +331,11 @@ def main() -> int:
     LAY = nm.LAYOUTS[args.layout]
     # the step: mask and compressed pair from one pass over W, decompress, product
     kinds = ["mask_compress", "decompress", "spmm"]
+    if args.ceiling_only:
+        w_vals, x_vals = bf16_sample(mats[0]["W"], dtype), bf16_sample(mats[0]["X"], dtype)
+        print(json.dumps({"matrix_core_ceiling": matrix_core_ceiling(torch, dev, stream, w_vals,
+                                                                     x_vals)}), flush=True)
+        return 0
 
     def launch(d, kind):
         if kind == "mask_compress":
@@ -308,6 +382,29 @@ def main() -> int:
                     events.append((d["name"], kind, e0, e1))
                 else:
                     launch(d, kind)
+
+    if args.product_only:
+        # the compressed pairs once, then only the products: the launches a profiler sees
+        for d in mats:
+            launch(d, "mask_compress")
+        for _ in range(args.warmup):
+            step(kinds=["spmm"])
+        torch.cuda.synchronize()
+        ev = []
+        for _ in range(args.steps):
+            step(ev, kinds=["spmm"])
+        torch.cuda.synchronize()
+        res = {}
+        for name, kind, e0, e1 in ev:
+            res.setdefault(name, []).append(e0.elapsed_time(e1) * 1e3)
+        out = {}
+        for d in mats:
+            t = float(np.mean(res[d["name"]]))
+            out[d["name"]] = {"us": round(t, 2), "us_min": round(float(np.min(res[d["name"]])), 2),
+                              "eff_tflops": round(2.0 * d["R"] * d["K"] * d["T"] / t / 1e6, 1)}
+        print(json.dumps({"workload": args.workload, "pattern": f"{n}:{m}", "layout": args.layout,
+                          "spmm": out}), flush=True)
+        return 0
 
     for _ in range(args.warmup):
         step()

@@ -111,18 +111,22 @@ int nm_abi_version(void);
 /* Static, human-readable name of a status code (never NULL). */
 const char* nm_status_str(nm_status s);
 
-/* Bytes of the value array: R * (K / m * n) * sizeof(dt) for NM_LAYOUT_ROWS,
- * 16 * ceil(R / 16) * (K / m * n) * sizeof(dt) for NM_LAYOUT_BLOCKED; 0 for invalid
- * arguments. */
+/* Bytes of the value array ("2:4 Sparsity의 benefits": the compressed weight keeps
+ * n of every m values, an R x C*n/m array of the weight's type):
+ * R * (K / m * n) * sizeof(dt) for NM_LAYOUT_ROWS, 16 * ceil(R / 16) * (K / m * n) *
+ * sizeof(dt) for NM_LAYOUT_BLOCKED; 0 for invalid arguments. */
 size_t nm_values_bytes(int64_t R, int64_t K, int n, int m, nm_dtype dt, nm_layout layout);
 
-/* Bytes of the metadata array: R * 4 * nm_meta_words_per_row(K, n, m) for
+/* Bytes of the metadata array ("2:4 Sparsity의 benefits": position bits beside the
+ * values): R * 4 * nm_meta_words_per_row(K, n, m) for
  * NM_LAYOUT_ROWS, 16 * ceil(R / 16) * (K / 64) * B for NM_LAYOUT_BLOCKED; 0 for
  * invalid arguments. */
 size_t nm_meta_bytes(int64_t R, int64_t K, int n, int m, nm_layout layout);
 
-/* Metadata words per row: ceil((K / m) * n * b / 32) with b = log2(m) bits per kept
- * value (1 for 1:2, 2 for 2:4, 3 for 4:8).  Field f = g*n + j of a row holds the
+/* Metadata words per row ("2:4 Sparsity의 benefits": 2 bits record the position of
+ * each kept value among its group of 4; the same rule with log2(m) bits is this
+ * library's reading for other m): ceil((K / m) * n * b / 32) with b = log2(m) bits per
+ * kept value (1 for 1:2, 2 for 2:4, 3 for 4:8).  Field f = g*n + j of a row holds the
  * position (0..m-1) of the j-th kept value of group g at bit offset f*b of the
  * row's bitstream, least significant bit first (word f*b/32, bit f*b%32; a 3-bit
  * field may straddle two words).  Every row starts on a word boundary and unused
@@ -166,19 +170,27 @@ nm_status nm_mask_compress(const void* W, nm_dtype dt, int64_t R, int64_t K, int
                            nm_layout layout, uint8_t* mask, void* values, uint32_t* meta,
                            nm_stream_t stream);
 
-/* Inverse of nm_compress: W_out (R x K) gets each stored value at its recorded
- * position and +0 (all-zero bits) everywhere else.  The metadata is trusted: a
+/* Inverse of nm_compress ("2:4 Sparsity의 benefits": the position metadata is what
+ * restores each stored value to its place in the dense row): W_out (R x K) gets each
+ * stored value at its recorded position and +0 (all-zero bits) everywhere else, i.e.
+ * select(mask, W, +0), this library's reading of the pages' masked weight W * mask.  The metadata is trusted: a
  * field that repeats a position within a group leaves the later value there. */
 nm_status nm_decompress(const void* values, const uint32_t* meta, nm_dtype dt, int64_t R,
                         int64_t K, int n, int m, nm_layout layout, void* W_out,
                         nm_stream_t stream);
 
 /* Y = W_sparse * X ("Tensor Scores 상에서 구조적인 sparse GEMM"): W_sparse is the
- * R x K matrix that (values, meta) encode, X is K x T, Y is R x T.  Products are
- * accumulated in fp32 and rounded once to y_dt (round to nearest even); y_dt
+ * R x K matrix that (values, meta) encode, X is K x T, Y is R x T.  Products of 16- and
+ * 32-bit inputs are accumulated in fp32 and rounded once to y_dt (round to nearest even); y_dt
  * must be dt or NM_F32.  For dt = NM_I8 (W and X int8) y_dt must be NM_I32 and Y is
  * the exact integer product (K < 2^17, else NM_ERR_SHAPE, so no sum can overflow).
- * For dt = NM_FP8, y_dt is NM_F32 or NM_BF16 (fp32 accumulation, one rounding).  The
+ * For dt = NM_FP8, y_dt is NM_F32 or NM_BF16.  2:4 and 1:2 fp8 products on the 8-bit
+ * structured-sparse matrix cores do NOT sum every product in fp32: the instruction adds
+ * the products of each run of 16 consecutive K (of the dense row) in fixed point aligned
+ * to the run's largest product, dropping bits below 2^(e - 13) where 2^e bounds that
+ * product, and adds the run sums into fp32 accumulators; the element error is at most
+ * sum over runs of 7 * 2^(e_run - 13) plus the fp32 summation bound of the run sums.
+ * Every other fp8 pattern or shape sums in fp32 (one rounding to y_dt).  The
  * metadata is trusted (well-formedness is the caller's responsibility, as for any
  * compressed operand; nm_check_meta checks it on the host).  Every shape and pattern
  * is accepted.  Fastest: 2:4 or 1:2 (16-bit on the structured-sparse matrix cores,

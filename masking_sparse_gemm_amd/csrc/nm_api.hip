@@ -178,6 +178,7 @@ nm_status nm_mask(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m
   if (missing(W, R * K) || missing(mask, R * K)) return NM_ERR_NULL;
   if (R * K == 0) return NM_OK;
   if (!aligned16(W) || !aligned16(mask)) return NM_ERR_ALIGN;
+  if (overlaps(mask, R * K, W, R * K * elem_bytes(dt))) return NM_ERR_ALIAS;
   if ((st = check_device()) != NM_OK) return st;
   return from_hip(nm::launch_select(W, (int)dt, R, K, n, m, false, nullptr, nullptr, mask,
                                     static_cast<hipStream_t>(stream)));
@@ -194,6 +195,14 @@ nm_status nm_compress(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, i
   if (missing(W, R * K) || missing(values, R * K) || missing(meta, R * K)) return NM_ERR_NULL;
   if (R * K == 0) return NM_OK;
   if (!aligned16(W) || !aligned16(values) || !aligned16(meta)) return NM_ERR_ALIGN;
+  {
+    const int64_t w_bytes = R * K * elem_bytes(dt);
+    const int64_t v_bytes = (int64_t)nm_values_bytes(R, K, n, m, dt, layout);
+    const int64_t m_bytes = (int64_t)nm_meta_bytes(R, K, n, m, layout);
+    if (overlaps(values, v_bytes, W, w_bytes) || overlaps(meta, m_bytes, W, w_bytes) ||
+        overlaps(values, v_bytes, meta, m_bytes))
+      return NM_ERR_ALIAS;
+  }
   if ((st = check_device()) != NM_OK) return st;
   return from_hip(nm::launch_select(W, (int)dt, R, K, n, m, layout == NM_LAYOUT_BLOCKED,
                                     values, meta, nullptr, static_cast<hipStream_t>(stream)));
@@ -238,6 +247,12 @@ nm_status nm_decompress(const void* values, const uint32_t* meta, nm_dtype dt, i
   if (missing(values, R * K) || missing(meta, R * K) || missing(W_out, R * K)) return NM_ERR_NULL;
   if (R * K == 0) return NM_OK;
   if (!aligned16(values) || !aligned16(meta) || !aligned16(W_out)) return NM_ERR_ALIGN;
+  {
+    const int64_t w_bytes = R * K * elem_bytes(dt);
+    if (overlaps(W_out, w_bytes, values, (int64_t)nm_values_bytes(R, K, n, m, dt, layout)) ||
+        overlaps(W_out, w_bytes, meta, (int64_t)nm_meta_bytes(R, K, n, m, layout)))
+      return NM_ERR_ALIAS;
+  }
   if ((st = check_device()) != NM_OK) return st;
   return from_hip(nm::launch_decompress(values, meta, elem_bytes(dt), R, K, n, m,
                                         layout == NM_LAYOUT_BLOCKED, W_out,
@@ -266,6 +281,14 @@ nm_status nm_spmm(const void* values, const uint32_t* meta, int64_t R, int64_t K
     return NM_ERR_NULL;
   if (R * T == 0) return NM_OK;
   if (!aligned16(values) || !aligned16(meta) || !aligned16(X) || !aligned16(Y)) return NM_ERR_ALIGN;
+  {
+    // Y is written while other workgroups still read values, meta and X
+    const int64_t y_bytes = R * T * ((y_dt == NM_F32 || y_dt == NM_I32) ? 4 : 2);
+    if (overlaps(Y, y_bytes, X, K * T * elem_bytes(dt)) ||
+        overlaps(Y, y_bytes, values, (int64_t)nm_values_bytes(R, K, n, m, dt, layout)) ||
+        overlaps(Y, y_bytes, meta, (int64_t)nm_meta_bytes(R, K, n, m, layout)))
+      return NM_ERR_ALIAS;
+  }
   if ((st = check_device()) != NM_OK) return st;
   return from_hip(nm::launch_spmm(values, meta, R, K, n, m, layout == NM_LAYOUT_BLOCKED, X, T,
                                   (int)dt, Y, (int)y_dt, static_cast<hipStream_t>(stream)));

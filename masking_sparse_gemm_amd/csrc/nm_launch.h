@@ -16,10 +16,29 @@ hipError_t launch_select(const void* W, int dt, int64_t R, int64_t K, int n, int
 hipError_t launch_decompress(const void* values, const uint32_t* meta, int elem_bytes, int64_t R,
                              int64_t K, int n, int m, bool blocked, void* out, hipStream_t s);
 
+// XCDs of the current device (8 on MI355X; 1 if unknown), looked up once per device.
+int xcd_count();
+
 // dt / y_dt use the nm_dtype codes: 0 fp32, 1 fp16, 2 bf16.
 hipError_t launch_spmm(const void* values, const uint32_t* meta, int64_t R, int64_t K, int n,
                        int m, bool blocked, const void* X, int64_t T, int dt, void* Y, int y_dt,
                        hipStream_t s);
+
+// The 2:4 16-bit product on 256 x 256 tiles split over the compute units by K steps
+// (nm_spmm_sk.hip), blocked layout, dt / y_dt as for launch_spmm.  sk_shape_ok: the
+// shapes it takes (K % 64 == 0, T % 8 == 0, sizes within its 32-bit offsets);
+// sk_preferred: shapes where it is the fastest kernel.  The workspace (device memory
+// of sk_workspace_bytes(R, T, groups) bytes, 256-byte aligned; none, and NULL may be
+// passed, when every workgroup gets whole tiles) holds one flag and one partial 256 x 256
+// fp32 tile per workgroup; its initial contents do not matter.
+bool sk_shape_ok(int64_t R, int64_t K, int64_t T);
+bool sk_preferred(int64_t R, int64_t K, int64_t T);
+int sk_groups(int64_t R, int64_t K, int64_t T);
+int64_t sk_workspace_bytes(int groups);                    // the largest it may need
+int64_t sk_workspace_bytes(int64_t R, int64_t T, int groups);  // 0: no tile is cut
+hipError_t launch_spmm_sk(const void* values, const uint32_t* meta, int64_t R, int64_t K,
+                          const void* X, int64_t T, int dt, void* Y, int y_dt, void* workspace,
+                          int groups, hipStream_t s);
 
 // Compress of W's transpose (the K x R matrix, groups of m along R; R % m == 0, and
 // R % 64 == 0 for the blocked layout).

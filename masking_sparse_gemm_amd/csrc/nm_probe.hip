@@ -1,0 +1,110 @@
+// nm_probe.hip -- matrix-core rate loops that bound the sparse product on this device
+// (include/nm_probe.h).  Nothing here computes part of the method.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/nm_probe.h"
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x16_t __attribute__((ext_vector_type(16)));
+typedef float float16v_t __attribute__((ext_vector_type(16)));
+typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kSets = 4;
+constexpr int kPerLane = 24;  // 8 A values + 16 B values
+
+// The six legal 2:4 nibbles (i0 | i1 << 2 with i0 < i1), four to a 16-bit index word.
+__device__ __forceinline__ int index_word(int k) {
+  const int nib[6] = {0x4, 0x8, 0xC, 0x9, 0xD, 0xE};
+  return nib[k % 6] | nib[(k + 1) % 6] << 4 | nib[(k + 2) % 6] << 8 | nib[(k + 3) % 6] << 12;
+}
+
+template <int KIND>
+__global__ void __launch_bounds__(256) probe_kernel(const uint16_t* __restrict__ ops, int iters,
+                                                    int64_t* __restrict__ clocks,
+                                                    float* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  bf16x8_t a[kSets];
+  bf16x16_t b[kSets];
+#pragma unroll
+  for (int s = 0; s < kSets; ++s) {
+    const uint16_t* p = ops + ((size_t)s * 64 + lane) * kPerLane;
+    u16x8_t av;
+    u16x16_t bv;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) av[i] = p[i];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) bv[i] = p[8 + i];
+    a[s] = __builtin_bit_cast(bf16x8_t, av);
+    b[s] = __builtin_bit_cast(bf16x16_t, bv);
+  }
+  const int ix0 = index_word(lane), ix1 = index_word(lane + 1), ix2 = index_word(lane + 2),
+            ix3 = index_word(lane + 3);
+  float16v_t c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  const bool timer = threadIdx.x == 0;
+  int64_t t0 = 0, r0 = 0;
+  if (timer) {
+    t0 = (int64_t)__builtin_amdgcn_s_memtime();
+    r0 = (int64_t)__builtin_amdgcn_s_memrealtime();
+  }
+  for (int it = 0; it < iters; ++it) {
+    // 16 instructions: four independent accumulators, each operand set in turn
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int s0 = r, s1 = (r + 1) & 3, s2 = (r + 2) & 3, s3 = (r + 3) & 3;
+      if constexpr (KIND == 0) {
+        c0 = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(a[s0], b[s1], c0, ix0, 0, 0);
+        c1 = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(a[s1], b[s2], c1, ix1, 0, 0);
+        c2 = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(a[s2], b[s3], c2, ix2, 0, 0);
+        c3 = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(a[s3], b[s0], c3, ix3, 0, 0);
+      } else {
+        const bf16x8_t b0 = __builtin_shufflevector(b[s1], b[s1], 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8_t b1 = __builtin_shufflevector(b[s2], b[s2], 8, 9, 10, 11, 12, 13, 14, 15);
+        const bf16x8_t b2 = __builtin_shufflevector(b[s3], b[s3], 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8_t b3 = __builtin_shufflevector(b[s0], b[s0], 8, 9, 10, 11, 12, 13, 14, 15);
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s0], b0, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s1], b1, c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s2], b2, c2, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s3], b3, c3, 0, 0, 0);
+      }
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+  if (timer) {
+    const int64_t t1 = (int64_t)__builtin_amdgcn_s_memtime();
+    const int64_t r1 = (int64_t)__builtin_amdgcn_s_memrealtime();
+    int64_t* c = clocks + 4 * blockIdx.x;
+    c[0] = t0;
+    c[1] = t1;
+    c[2] = r0;
+    c[3] = r1;
+  }
+  sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t nm_probe_operand_bytes(void) { return (int64_t)kSets * 64 * kPerLane * 2; }
+
+int nm_probe_matrix_core(int kind, const void* operands, int cus, int waves_per_simd, int iters,
+                         int64_t* clocks, float* sink, void* stream) {
+  if ((kind != 0 && kind != 1) || operands == nullptr || clocks == nullptr || sink == nullptr ||
+      cus < 1 || cus > 4096 || waves_per_simd < 1 || waves_per_simd > 8 || iters < 1)
+    return 1;
+  // one workgroup of four waves (one per SIMD) per compute unit and wave per SIMD
+  auto k = kind == 0 ? probe_kernel<0> : probe_kernel<1>;
+  hipLaunchKernelGGL(k, dim3(cus * waves_per_simd), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(operands),
+                     iters, clocks, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+}  // extern "C"

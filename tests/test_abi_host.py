@@ -377,3 +377,42 @@ def test_mask_compress_argument_rules():
     assert st(mc(values=FAKE + 0x100000 + 64 * 64)) == "alias"  # values inside the mask
     assert st(mc(meta=FAKE + 0x200000 + 16)) == "alias"       # meta inside the values
     assert st(mc(R=0)) == "ok"
+
+
+@needs_lib
+def test_outputs_overlapping_inputs_are_rejected():
+    """nm_mask, nm_compress, nm_decompress and nm_spmm refuse an output that overlaps an input
+    (other workgroups would still be reading it); disjoint arrays pass every check and reach
+    the device check, which fails on a host without a GPU."""
+    L = nm.lib()
+    MB = 0x100000
+    R, K, T = 64, 128, 32   # bf16: W 16 KiB, mask 8 KiB, values 8 KiB, meta 1 KiB, X 8 KiB, Y 4 KiB
+    BF = nm.NM_BF16
+    st = lambda c: nm.STATUS[c]
+    no_alias = {"device"}   # what a disjoint call returns here
+    # nm_mask: the mask over W
+    assert st(L.nm_mask(FAKE, BF, R, K, 2, 4, FAKE + 0x3000, None)) == "alias"
+    assert st(L.nm_mask(FAKE, BF, R, K, 2, 4, FAKE + MB, None)) in no_alias
+    for layout in (0, 1):
+        # nm_compress: values or meta over W, or over each other
+        comp = lambda W, v, mt: st(L.nm_compress(W, BF, R, K, 2, 4, layout, v, mt, None))
+        assert comp(FAKE, FAKE + 0x1000, FAKE + 2 * MB) == "alias"
+        assert comp(FAKE, FAKE + MB, FAKE + 0x3f00) == "alias"
+        assert comp(FAKE, FAKE + MB, FAKE + MB + 0x1000) == "alias"
+        assert comp(FAKE, FAKE + MB, FAKE + 2 * MB) in no_alias
+        # nm_decompress: W_out over values or over meta
+        dec = lambda v, mt, W: st(L.nm_decompress(v, mt, BF, R, K, 2, 4, layout, W, None))
+        assert dec(FAKE, FAKE + MB, FAKE + 0x1000) == "alias"
+        assert dec(FAKE, FAKE + MB, FAKE + MB - 0x2000) == "alias"
+        assert dec(FAKE, FAKE + MB, FAKE + 2 * MB) in no_alias
+        # nm_spmm: Y over X, values or meta
+        sp = lambda v, mt, X, Y: st(L.nm_spmm(v, mt, R, K, 2, 4, layout, X, T, BF, Y, BF, None))
+        assert sp(FAKE, FAKE + MB, FAKE + 2 * MB, FAKE + 2 * MB + 0x1ff0) == "alias"
+        assert sp(FAKE, FAKE + MB, FAKE + 2 * MB, FAKE + 0x1000) == "alias"
+        assert sp(FAKE, FAKE + MB, FAKE + 2 * MB, FAKE + MB + 0x100) == "alias"
+        assert sp(FAKE, FAKE + MB, FAKE + 2 * MB, FAKE + 3 * MB) in no_alias
+        # Y ending exactly where X starts does not overlap it
+        assert sp(FAKE, FAKE + MB, FAKE + 2 * MB, FAKE + 2 * MB - 0x1000) in no_alias
+    # fp32 output: Y is twice as large
+    assert st(L.nm_spmm(FAKE, FAKE + MB, R, K, 2, 4, 0, FAKE + 2 * MB, T, BF,
+                        FAKE + 2 * MB - 0x1000, nm.NM_F32, None)) == "alias"

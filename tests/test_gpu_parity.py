@@ -241,11 +241,14 @@ def test_spmm_even_ragged_columns(dtype, n, m, layout):
     check_product(Y, y_ref, s, K // m * n, dtype, dtype, f"{R}x{K}x{T} {layout}")
 
 
-@pytest.mark.parametrize("tile", ["0", "1", "2"])
-@pytest.mark.parametrize("dtype,n,m", [("bf16", 2, 4), ("f16", 1, 2)])
+@pytest.mark.parametrize("tile", ["0", "1", "2", "3"])
+@pytest.mark.parametrize("dtype,n,m", [("bf16", 2, 4), ("f16", 1, 2), ("f16", 2, 4)])
 @pytest.mark.parametrize("layout", ["rows", "blocked"])
 def test_spmm_every_tile_shape(tile, dtype, n, m, layout, monkeypatch):
-    """Each matrix-core tile shape, pinned, on shapes with ragged row and column tiles."""
+    """Each matrix-core tile shape, pinned, on shapes with ragged row and column tiles.
+    Tile 3 is the 256 x 256 kernel split over workgroups by K steps (2:4, blocked layout):
+    on these small shapes every workgroup gets one or two steps, so tiles are cut into
+    many parts whose partial sums are exchanged through the workspace."""
     monkeypatch.setenv("NM_SPMM_TILE", tile)
     rng = np.random.default_rng(61)
     for R, K, T in [(300, 192, 264), (520, 128, 136), (16, 64, 8), (33, 640, 392)]:
@@ -256,6 +259,23 @@ def test_spmm_every_tile_shape(tile, dtype, n, m, layout, monkeypatch):
                     rows=R)
         y_ref, s = reference_product(vals_o, meta_o, R, K, n, m, X, dtype)
         check_product(Y, y_ref, s, K // m * n, dtype, "f32", f"tile {tile} {R}x{K}x{T} {layout}")
+
+
+@pytest.mark.parametrize("dtype,ydt", [("bf16", "bf16"), ("f16", "f32")])
+def test_spmm_split_kernel_whole_tiles(dtype, ydt, monkeypatch):
+    """The 256 x 256 split kernel where every workgroup gets whole tiles in step (256 tiles
+    of one or two K steps each, tiles taken in XCD blocks), with ragged edges: every output
+    against the oracle."""
+    monkeypatch.setenv("NM_SPMM_TILE", "3")
+    rng = np.random.default_rng(71)
+    for R, K, T in [(4000, 64, 4088), (2048, 128, 8192)]:
+        W = encode(rng.standard_normal((R, K)), dtype)
+        X = encode(rng.standard_normal((K, T)), dtype)
+        vals, meta, vals_o, meta_o = compressed(W, dtype, 2, 4, "blocked")
+        Y = nm.spmm(vals, meta, dev(X, dtype), 2, 4, out_dtype=TORCH_DT[ydt], layout="blocked",
+                    rows=R)
+        y_ref, s = reference_product(vals_o, meta_o, R, K, 2, 4, X, dtype)
+        check_product(Y, y_ref, s, K // 2, dtype, ydt, f"split whole tiles {R}x{K}x{T}")
 
 
 # fp32: the matrix-core expansion kernel for every pattern (K tails inside its 32-wide step:
@@ -337,9 +357,17 @@ def test_spmm_empty():
 
 
 def sample_points(rng, R, T, count=1500):
-    """Random outputs plus the corners and edges of the matrix (ragged tiles live there)."""
+    """Random outputs, the corners and edges of the matrix (ragged tiles live there), and one
+    random output in every 32 x 32 block (the accumulator fragment of one matrix-core
+    instruction), so every wave's share of every tile is checked."""
     rs = list(rng.integers(0, R, count)) + [0, R - 1, R - 1, 0] + [R - 1] * 64 + list(rng.integers(0, R, 64))
     ts = list(rng.integers(0, T, count)) + [0, T - 1, 0, T - 1] + list(rng.integers(0, T, 64)) + [T - 1] * 64
+    br, bt = np.meshgrid(np.arange(0, R, 32), np.arange(0, T, 32), indexing="ij")
+    br = br.reshape(-1) + rng.integers(0, 32, br.size)
+    bt = bt.reshape(-1) + rng.integers(0, 32, bt.size)
+    keep = (br < R) & (bt < T)
+    rs += list(br[keep])
+    ts += list(bt[keep])
     return np.array(rs, dtype=np.int64), np.array(ts, dtype=np.int64)
 
 
