@@ -13,6 +13,13 @@ flops (2 R K T per matrix) divided by the step time.  Per-kernel figures,
 the roofline of the dominant kernel, the dense GEMM on the same shapes and the
 CPU oracle timed on the host are reported alongside.
 
+Each step kernel is also timed cold (a 512 MiB read, twice the 256 MB Infinity Cache,
+before each launch, outside its events) beside the in-step (warm) timing.  The fp16 N:M
+sweep (4096 x 4096 weights, 8192 activation columns; 1:2, 2:4, 4:8 and mask-only) is
+timed the same way under "sweep_f16", with its product's roofline and the dense GEMM.
+The matrix cores' own rate on the workload's values (libnm_probe) is reported under
+"matrix_core_ceiling".
+
 The SR-STE passes of a training step on the same weights (nm_prune, the
 forward's masked weight, and nm_srste_grad, the backward's gradient) are timed
 in a separate pass after the step, each launch after a cache-clearing fill, and
@@ -41,9 +48,11 @@ METRIC = "2:4 spmm effective TFLOP/s + mask/compress GB/s (% of MI355X roofline)
 METRIC_I8 = "2:4 int8 spmm effective TOP/s + mask/compress GB/s (% of MI355X roofline)"
 METRIC_FP8 = "2:4 fp8 spmm effective TFLOP/s + mask/compress GB/s (% of MI355X roofline)"
 PEAK_HBM_GBS = 8000.0
-# fp32 VALU operations: the 157.3 TFLOP/s fp32 vector peak counts an FMA as two flops,
-# i.e. 256 CUs x 128 fp32 lanes per clock x 2.4 GHz = 78.6 T operations per second
-PEAK_VALU_TOPS = 78.64
+# VALU lane operations the build can issue: packed fp32 is disabled, so a compute unit
+# retires 64 lane-operations per clock (4 SIMDs x 16 lanes; one wave instruction is 64
+# lane-operations over 4 clocks): 256 CUs x 64 x 2.4 GHz = 39.3 T lane-op/s.  (The
+# 157.3 TFLOP/s fp32 vector peak needs packed fp32 FMA: 2 operations per lane and 2 flops each.)
+PEAK_VALU_LANE_TOPS = 39.32
 # dense matrix-core peaks (TFLOP/s; TOP/s for int8)
 PEAK_MFMA_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3, "i8": 5033.2, "fp8": 5033.2}
 # workload name -> (synthetic matrices, N:M pattern)
@@ -59,6 +68,61 @@ WORKLOADS = {
     "toy_f32": (["toy_f32"], (2, 4)),
     "sweep_f32_2_4": (["sweep_f32"], (2, 4)),
 }
+
+
+class HipTimer:
+    """Kernel timing with HIP events created with hipEventDisableSystemFence, through the HIP
+    runtime this process already loaded (PyTorch's).  Recording such an event does not make
+    the queue flush caches to system scope, which costs a few microseconds per record with
+    default events and inflates the time of short kernels; the interval between two records
+    on the launch stream is then the kernels' own time, as a profiler's kernel trace shows."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, stream_handle: int):
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("the HIP runtime is not loaded")
+        import ctypes
+
+        self.ct = ctypes
+        self.hip = ctypes.CDLL(path)
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.stream = ctypes.c_void_p(stream_handle)
+        self.pool = []
+
+    def event(self):
+        e = self.ct.c_void_p()
+        if self.hip.hipEventCreateWithFlags(self.ct.byref(e), self.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+        self.pool.append(e)
+        return e
+
+    def record(self, e):
+        if self.hip.hipEventRecord(e, self.stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, e0, e1) -> float:
+        self.hip.hipEventSynchronize(e1)
+        out = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(out), e0, e1) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(out.value)
+
+    def close(self):
+        for e in self.pool:
+            self.hip.hipEventDestroy(e)
+        self.pool = []
 
 
 def meta_bits(m: int) -> int:
@@ -80,22 +144,95 @@ def algorithmic_bytes(R, K, T, n, m, s, ys):
     }
 
 
-def profiled_traffic(workload: str, kernel: str = "spmm_kernel", source: str = "nm_spmm.hip"):
-    """HBM bytes per dispatch of the kernels whose name contains `kernel`, from the committed
+SPMM_SOURCES = ("nm_spmm.hip", "nm_spmm_sk.hip", "nm_mfma.h")
+
+
+def profile_matches(prof: dict, sources) -> bool:
+    """True when every source file in `sources` is byte-identical to the one the committed
+    profile `prof` was taken on (its "sources_sha256" table)."""
+    for source in sources:
+        src = os.path.join(ROOT, "masking_sparse_gemm_amd", "csrc", source)
+        with open(src, "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != prof.get("sources_sha256", {}).get(source):
+                return False
+    return True
+
+
+def profiled_traffic(workload: str, kernel: str = "spmm_kernel", sources=SPMM_SOURCES):
+    """HBM bytes per dispatch of the kernels whose key contains `kernel`, from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary (already scaled by the copy-kernel calibration),
-    or None when that summary is missing or was taken on a different version of `source`."""
+    or None when that summary is missing or was taken on a different version of any of
+    `sources`."""
     path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
-    src = os.path.join(ROOT, "masking_sparse_gemm_amd", "csrc", source)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         prof = json.load(f)
-    with open(src, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != prof.get("sources_sha256", {}).get(source):
-            return None
+    if not profile_matches(prof, sources):
+        return None
     per = [v["read_bytes"] + v["write_bytes"] for k, v in prof["per_dispatch_bytes"].items()
            if kernel in k]
     return sum(per) / len(per) if per else None
+
+
+def profiled_valu(workload: str, kernel: str = "gains_kernel", sources=("nm_perm.hip",)):
+    """Wave-level VALU instructions per dispatch of `kernel` (SQ_INSTS_VALU) from the committed
+    rocprofv3 summary, keyed by matrix name, or {} when that summary is missing or was taken
+    on a different version of any of `sources`."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_valu.json")
+    if not os.path.exists(path):
+        return {}
+    with open(path) as f:
+        prof = json.load(f)
+    if not profile_matches(prof, sources) or kernel not in prof.get("kernel", ""):
+        return {}
+    return dict(prof.get("valu_insts_per_dispatch", {}))
+
+
+def cpu_info():
+    """Host CPU model and the cores this process may run on (the box allots 16 per GPU)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        visible = len(os.sched_getaffinity(0))
+    except AttributeError:
+        visible = os.cpu_count() or 1
+    return model, visible
+
+
+def cpu_one_core(mats, n, m, rows: int = 64):
+    """The oracle on one thread: mask + compress + decompress + fp64 product of the first
+    `rows` rows of every matrix (all T columns), scaled to the whole workload."""
+    import oracle
+
+    oracle.lib()
+    F = 0.0
+    F_all = 0.0
+    t0 = time.perf_counter()
+    for w in mats:
+        part = np.ascontiguousarray(w["W"][:rows])
+        r = part.shape[0]
+        oracle.mask(part, w["dtype"], n, m)
+        vals, meta = oracle.compress(part, w["dtype"], n, m)
+        oracle.decompress(vals, meta, w["dtype"], r, w["K"], n, m)
+        Y = np.empty((r, w["T"]), dtype=np.float64)
+        oracle.spmm_rows(vals, meta, r, w["K"], n, m, w["X"], w["dtype"], 0, r, Y)
+        F += 2.0 * r * w["K"] * w["T"]
+        F_all += 2.0 * w["R"] * w["K"] * w["T"]
+    dt = time.perf_counter() - t0
+    rate = F / dt
+    unit = "TOP/s" if mats[0]["dtype"] == "i8" else "TFLOP/s"
+    return {"value": rate / 1e12, "unit": unit, "cores": 1, "seconds": round(dt, 2),
+            "sample": f"rows 0..{rows} of each matrix, all T columns",
+            "extrapolated_step_s": round(F_all / rate, 1),
+            "note": "one step of the whole workload on one core, extrapolated from the sample"}
 
 
 def srste_cpu_sample(mats, n, m, budget_s: float = 3.0):
@@ -190,7 +327,7 @@ def bf16_sample(a: np.ndarray, dtype: str, count: int = 1 << 20) -> np.ndarray:
     return (a.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
 
 
-def matrix_core_ceiling(torch, dev, stream, w_vals, x_vals, waves_per_simd: int = 2):
+def matrix_core_ceiling(torch, dev, stream, hipt, w_vals, x_vals, waves_per_simd: int = 2):
     """What the matrix cores sustain alone (libnm_probe): the 2:4 structured-sparse bf16
     instruction and the dense bf16 one in register-only loops, on three kinds of operands:
     zeros, small integers, and values drawn from the workload's own weights and
@@ -224,20 +361,115 @@ def matrix_core_ceiling(torch, dev, stream, w_vals, x_vals, waves_per_simd: int 
             for _ in range(2):  # warm-up (clock ramp)
                 P.nm_probe_matrix_core(kind, dops.data_ptr(), cus, waves_per_simd, iters,
                                        clocks.data_ptr(), sink.data_ptr(), stream.cuda_stream)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
+            e0, e1 = hipt.event(), hipt.event()
+            hipt.record(e0)
             rc = P.nm_probe_matrix_core(kind, dops.data_ptr(), cus, waves_per_simd, iters,
                                         clocks.data_ptr(), sink.data_ptr(), stream.cuda_stream)
-            e1.record(stream)
+            hipt.record(e1)
             torch.cuda.synchronize()
             if rc != 0:
                 raise RuntimeError(f"nm_probe_matrix_core failed ({rc})")
-            t = e0.elapsed_time(e1) * 1e-3
+            t = hipt.ms(e0, e1) * 1e-3
             insts = cus * waves_per_simd * 4 * iters * 16
             c = clocks.view(-1, 4).cpu().numpy().astype(np.float64)
             mhz = float(np.median((c[:, 1] - c[:, 0]) / np.maximum(c[:, 3] - c[:, 2], 1) * 100.0))
             out[f"{inst}.{kname}"] = {"eff_tflops": round(insts * flops / t / 1e12, 1),
                                       "clock_mhz": round(mhz, 0), "ms": round(t * 1e3, 3)}
+    return out
+
+
+def sweep_f16_block(torch, nm, synth, L, dev, stream, hipt, args, flush, cold_times):
+    """The fp16 N:M sweep: W 4096 x 4096 ~Laplace(0, 0.05), X 4096 x 8192 ~N(0, 1).  For each
+    of 1:2, 2:4 and 4:8: the fused mask + compress pass, the mask alone, decompress and the
+    product, warm (back to back) and cold (inputs evicted before each launch), the dense
+    GEMM (hipBLASLt) on the decompressed weight, and the product's matrix-core roofline."""
+    w = synth.WORKLOADS["sweep_f16"]
+    R, K, T = w.R, w.K, w.T
+    W, X = w.W(), w.X()
+    f16 = torch.float16
+    Wd = torch.from_numpy(W.view(np.int16)).view(f16).to(dev)
+    Xd = torch.from_numpy(X.view(np.int16)).view(f16).to(dev)
+    mask = torch.empty((R, K), dtype=torch.bool, device=dev)
+    dec = torch.empty((R, K), dtype=f16, device=dev)
+    Y = torch.empty((R, T), dtype=f16, device=dev)
+    sp = stream.cuda_stream
+    LAY = nm.LAYOUTS[args.layout]
+    out = {"matrix": f"{R}x{K} X {K}x{T}", "dtype": "f16", "layout": args.layout, "patterns": {}}
+    reps = args.steps
+    for (n, m) in w.patterns:
+        vshape, mshape = nm.compressed_shapes(R, K, n, m, args.layout)
+        vals = torch.empty(vshape, dtype=f16, device=dev)
+        meta = torch.empty(mshape, dtype=torch.int32, device=dev)
+        d = {"name": f"{n}:{m}"}
+
+        def launch(d, kind, n=n, m=m, vals=vals, meta=meta):
+            if kind == "mask_compress":
+                rc = L.nm_mask_compress(Wd.data_ptr(), 1, R, K, n, m, LAY, mask.data_ptr(),
+                                        vals.data_ptr(), meta.data_ptr(), sp)
+            elif kind == "mask":
+                rc = L.nm_mask(Wd.data_ptr(), 1, R, K, n, m, mask.data_ptr(), sp)
+            elif kind == "decompress":
+                rc = L.nm_decompress(vals.data_ptr(), meta.data_ptr(), 1, R, K, n, m, LAY,
+                                     dec.data_ptr(), sp)
+            else:
+                rc = L.nm_spmm(vals.data_ptr(), meta.data_ptr(), R, K, n, m, LAY, Xd.data_ptr(), T,
+                               1, Y.data_ptr(), 1, sp)
+            if rc != 0:
+                raise RuntimeError(f"sweep {kind} {n}:{m} failed: {nm.status_str(rc)}")
+
+        kinds = ["mask_compress", "mask", "decompress", "spmm"]
+        for _ in range(max(2, args.warmup)):
+            for k in kinds:
+                launch(d, k)
+        torch.cuda.synchronize()
+        # warm: `reps` launches of one kernel back to back between two events (its inputs stay
+        # in the Infinity Cache); the per-launch mean includes the gaps between launches
+        warm = {}
+        for k in kinds:
+            e0, e1 = hipt.event(), hipt.event()
+            hipt.record(e0)
+            for _ in range(reps):
+                launch(d, k)
+            hipt.record(e1)
+            warm[k] = [hipt.ms(e0, e1) / reps]
+        cold = {k[1]: v for k, v in cold_times([d], kinds, launch, reps).items()}
+        ab = algorithmic_bytes(R, K, T, n, m, 2, 2)
+        entry = {}
+        for k in kinds:
+            t, tc = float(np.mean(warm[k])) * 1e-3, float(np.mean(cold[k])) * 1e-3
+            e = {"us": round(t * 1e6, 2), "us_cold": round(tc * 1e6, 2), "alg_bytes": ab[k]}
+            if k == "spmm":
+                f_eff = 2.0 * R * K * T
+                e.update(eff_tflops=round(f_eff / t / 1e12, 1),
+                         eff_tflops_cold=round(f_eff / tc / 1e12, 1),
+                         alg_tflops=round(f_eff * n / m / t / 1e12, 1),
+                         frac_mfma=round(f_eff * n / m / t / 1e12 / PEAK_MFMA_TFLOPS["f16"], 4),
+                         frac_mfma_cold=round(f_eff * n / m / tc / 1e12 / PEAK_MFMA_TFLOPS["f16"], 4))
+                tr = profiled_traffic("sweep_f16", f"{n}:{m} spmm ")
+                e["traffic"] = None if tr is None else round(tr)
+                e["traffic_over_alg"] = None if tr is None else round(tr / ab[k], 2)
+            else:
+                e.update(gbps=round(ab[k] / t / 1e9, 1), frac_hbm=round(ab[k] / t / 1e9 / PEAK_HBM_GBS, 3),
+                         gbps_cold=round(ab[k] / tc / 1e9, 1),
+                         frac_hbm_cold=round(ab[k] / tc / 1e9 / PEAK_HBM_GBS, 3))
+            entry[k] = e
+        if not args.no_dense:
+            for _ in range(3):
+                torch.matmul(dec, Xd)
+            torch.cuda.synchronize()
+            e0, e1 = hipt.event(), hipt.event()
+            hipt.record(e0)
+            for _ in range(reps):
+                torch.matmul(dec, Xd)
+            hipt.record(e1)
+            torch.cuda.synchronize()
+            td = hipt.ms(e0, e1) / reps * 1e-3
+            entry["dense_gemm"] = {"us": round(td * 1e6, 2),
+                                   "eff_tflops": round(2.0 * R * K * T / td / 1e12, 1),
+                                   "how": "torch.matmul (hipBLASLt) on the decompressed weight"}
+            entry["spmm_speedup"] = round(td / (float(np.mean(warm["spmm"])) * 1e-3), 3)
+        out["patterns"][f"{n}:{m}"] = entry
+        del vals, meta
     return out
 
 
@@ -251,6 +483,8 @@ def main() -> int:
                     help="storage layout of the compressed weight (include/nm.h)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense GEMM baseline")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the fp16 N:M sweep block (1:2, 2:4, 4:8 on 4096 x 4096 x 8192)")
     ap.add_argument("--product-only", action="store_true",
                     help="time only nm_spmm on the workload's matrices (for profiling runs)")
     ap.add_argument("--ceiling-only", action="store_true",
@@ -324,6 +558,7 @@ def main() -> int:
     L = nm.lib()
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
+    hipt = HipTimer(sp)
     DT = {"f32": 0, "f16": 1, "bf16": 2, "i8": 3, "fp8": 5}[dtype]
     YDT = {"i8": 4, "fp8": 2}.get(dtype, DT)  # int32 for int8, bf16 for fp8
     # SR-STE and transposable masks train 16/32-bit float weights
@@ -333,8 +568,8 @@ def main() -> int:
     kinds = ["mask_compress", "decompress", "spmm"]
     if args.ceiling_only:
         w_vals, x_vals = bf16_sample(mats[0]["W"], dtype), bf16_sample(mats[0]["X"], dtype)
-        print(json.dumps({"matrix_core_ceiling": matrix_core_ceiling(torch, dev, stream, w_vals,
-                                                                     x_vals)}), flush=True)
+        print(json.dumps({"matrix_core_ceiling": matrix_core_ceiling(torch, dev, stream, hipt,
+                                                                     w_vals, x_vals)}), flush=True)
         return 0
 
     def launch(d, kind):
@@ -374,11 +609,11 @@ def main() -> int:
         for d in mats:
             for kind in kinds:
                 if events is not None:
-                    e0 = torch.cuda.Event(enable_timing=True)
-                    e1 = torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
+                    e0 = hipt.event()
+                    e1 = hipt.event()
+                    hipt.record(e0)
                     launch(d, kind)
-                    e1.record(stream)
+                    hipt.record(e1)
                     events.append((d["name"], kind, e0, e1))
                 else:
                     launch(d, kind)
@@ -396,7 +631,7 @@ def main() -> int:
         torch.cuda.synchronize()
         res = {}
         for name, kind, e0, e1 in ev:
-            res.setdefault(name, []).append(e0.elapsed_time(e1) * 1e3)
+            res.setdefault(name, []).append(hipt.ms(e0, e1) * 1e3)
         out = {}
         for d in mats:
             t = float(np.mean(res[d["name"]]))
@@ -426,7 +661,29 @@ def main() -> int:
     torch.cuda.synchronize()
     per = {}
     for name, kind, e0, e1 in events:
-        per.setdefault((name, kind), []).append(e0.elapsed_time(e1))
+        per.setdefault((name, kind), []).append(hipt.ms(e0, e1))
+
+    # ---- the same kernels cold: before each launch, outside its events, a 512 MiB read
+    # (twice the 256 MB Infinity Cache) evicts its inputs, so they come from HBM.  A read,
+    # not a fill: a fill would leave dirty lines whose write-back competes with the kernel.
+    flush = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
+
+    def cold_times(mat_list, kind_list, launch_fn, reps):
+        ev = {}
+        for _ in range(reps):
+            for d in mat_list:
+                for kind in kind_list:
+                    flush.view(torch.int64).sum()
+                    e0 = hipt.event()
+                    e1 = hipt.event()
+                    hipt.record(e0)
+                    launch_fn(d, kind)
+                    hipt.record(e1)
+                    ev.setdefault((d["name"], kind), []).append((e0, e1))
+        torch.cuda.synchronize()
+        return {k: [hipt.ms(a, b) for a, b in v] for k, v in ev.items()}
+
+    per_cold = cold_times(mats, kinds, launch, args.steps)
 
     F_eff = sum(2.0 * d["R"] * d["K"] * d["T"] for d in mats)
     F_alg = F_eff * n / m
@@ -434,23 +691,28 @@ def main() -> int:
 
     kernels = {}
     tot = {k: [0.0, 0.0] for k in kinds}  # [seconds per step, algorithmic bytes per step]
+    tot_cold = {k: 0.0 for k in kinds}
     for d in mats:
         ab = algorithmic_bytes(d["R"], d["K"], d["T"], n, m, d["s"], d["ys"])
         for kind in kinds:
             samples = per[(d["name"], kind)]
             t = float(np.mean(samples)) * 1e-3
+            tc = float(np.mean(per_cold[(d["name"], kind)])) * 1e-3
             entry = {"us": round(t * 1e6, 2), "us_median": round(float(np.median(samples)) * 1e3, 2),
-                     "us_min": round(float(np.min(samples)) * 1e3, 2), "alg_bytes": ab[kind],
-                     "gbps": round(ab[kind] / t / 1e9, 1)}
+                     "us_min": round(float(np.min(samples)) * 1e3, 2), "us_cold": round(tc * 1e6, 2),
+                     "alg_bytes": ab[kind], "gbps": round(ab[kind] / t / 1e9, 1)}
             if kind == "spmm":
                 f_alg = 2.0 * d["R"] * d["K"] * d["T"] * n / m
                 entry["eff_tflops"] = round(2.0 * d["R"] * d["K"] * d["T"] / t / 1e12, 1)
                 entry["alg_tflops"] = round(f_alg / t / 1e12, 1)
+                entry["eff_tflops_cold"] = round(2.0 * d["R"] * d["K"] * d["T"] / tc / 1e12, 1)
             else:
                 entry["frac_hbm"] = round(ab[kind] / t / 1e9 / PEAK_HBM_GBS, 3)
+                entry["frac_hbm_cold"] = round(ab[kind] / tc / 1e9 / PEAK_HBM_GBS, 3)
             kernels[f"{d['name']}.{kind}"] = entry
             tot[kind][0] += t
             tot[kind][1] += ab[kind]
+            tot_cold[kind] += tc
 
     spmm_t = tot["spmm"][0]
     achieved = F_alg / spmm_t / 1e12
@@ -470,10 +732,14 @@ def main() -> int:
     traffic = profiled_traffic(args.workload)
     if traffic is not None:
         roofline["traffic"] = round(traffic)
+        roofline["traffic_over_alg"] = round(traffic / roofline["alg_bytes_per_launch"], 2)
 
     mc_bytes, mc_time = tot["mask_compress"][1], tot["mask_compress"][0]
     mask_compress = {"gbps": round(mc_bytes / mc_time / 1e9, 1),
                      "frac_hbm": round(mc_bytes / mc_time / 1e9 / PEAK_HBM_GBS, 3),
+                     "gbps_cold": round(mc_bytes / tot_cold["mask_compress"] / 1e9, 1),
+                     "frac_hbm_cold": round(mc_bytes / tot_cold["mask_compress"] / 1e9
+                                            / PEAK_HBM_GBS, 3),
                      "how": "nm_mask_compress: one pass writes the mask and the compressed pair"}
     # the two separate passes (nm_mask, nm_compress), for reference; not part of the step
     sep = {k: [0.0, 0.0] for k in ("mask", "compress")}
@@ -483,7 +749,7 @@ def main() -> int:
     torch.cuda.synchronize()
     sep_per = {}
     for name, kind, e0, e1 in sep_events:
-        sep_per.setdefault((name, kind), []).append(e0.elapsed_time(e1) * 1e-3)
+        sep_per.setdefault((name, kind), []).append(hipt.ms(e0, e1) * 1e-3)
     for d in mats:
         ab = algorithmic_bytes(d["R"], d["K"], d["T"], n, m, d["s"], d["ys"])
         for kind in ("mask", "compress"):
@@ -519,13 +785,13 @@ def main() -> int:
             except (RuntimeError, AttributeError):
                 continue
             torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
+            e0, e1 = hipt.event(), hipt.event()
+            hipt.record(e0)
             for _ in range(args.steps):
                 mm(A, B)
-            e1.record(stream)
+            hipt.record(e1)
             torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1) / args.steps * 1e-3)
+            ts.append(hipt.ms(e0, e1) / args.steps * 1e-3)
         if ts:
             dense_t = sum(ts)
             dense = {"tflops": round(F_eff / dense_t / 1e12, 1), "us_total": round(dense_t * 1e6, 1),
@@ -533,6 +799,24 @@ def main() -> int:
                      "how": {"i8": "torch._int_mm", "fp8": "torch._scaled_mm (bf16 out)"}.get(
                          dtype, "torch.matmul (hipBLASLt)")
                             + " on the decompressed weight, same dtype"}
+
+    # ---- the matrix cores' own rate on this workload's values (libnm_probe) ----
+    ceiling = None
+    if dtype in ("bf16", "f16"):
+        ceiling = matrix_core_ceiling(torch, dev, stream, hipt, bf16_sample(mats[0]["W"], dtype),
+                                      bf16_sample(mats[0]["X"], dtype))
+        c = ceiling["smfmac_32x32x32_bf16.workload"]
+        roofline["ceiling"] = {
+            "alg_tflops": round(c["eff_tflops"] / 2, 1), "clock_mhz": c["clock_mhz"],
+            "how": "v_smfmac_f32_32x32x32_bf16 alone in a register loop on operands drawn from "
+                   "this workload's W and X (libnm_probe); the device lowers its clock under "
+                   "such load (zeros: %d MHz)" % ceiling["smfmac_32x32x32_bf16.zeros"]["clock_mhz"]}
+        roofline["frac_of_ceiling"] = round(achieved / (c["eff_tflops"] / 2), 4)
+
+    # ---- the fp16 N:M sweep: 4096 x 4096 weights, 8192 activation columns ----
+    sweep = None
+    if args.workload == "llama_mlp" and not args.no_sweep:
+        sweep = sweep_f16_block(torch, nm, synth, L, dev, stream, hipt, args, flush, cold_times)
 
     srste = transposable = None
     if float_path:
@@ -551,14 +835,14 @@ def main() -> int:
             for d in mats:
                 for kind in sr_kinds:
                     flush.view(torch.int64).sum()
-                    e0 = torch.cuda.Event(enable_timing=True)
-                    e1 = torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
+                    e0 = hipt.event()
+                    e1 = hipt.event()
+                    hipt.record(e0)
                     launch(d, kind)
-                    e1.record(stream)
+                    hipt.record(e1)
                     sr_per.setdefault((d["name"], kind), []).append((e0, e1))
         torch.cuda.synchronize()
-        sr_per = {k: [a.elapsed_time(b) * 1e-3 for a, b in v] for k, v in sr_per.items()}
+        sr_per = {k: [hipt.ms(a, b) * 1e-3 for a, b in v] for k, v in sr_per.items()}
         del flush
         srste = {"decay": nm.SRSTE_DECAY, "kernels": {}}
         sr_tot = {k: [0.0, 0.0] for k in sr_kinds}
@@ -578,7 +862,7 @@ def main() -> int:
                              "frac": round(g_b / g_t / 1e9 / PEAK_HBM_GBS, 3),
                              "alg_bytes_per_elem": 3 * mats[0]["s"], "traffic": None}
         g_traffic = profiled_traffic(args.workload, "srste_unit_kernel<2, 2, 4, true>"
-                                     if dtype == "bf16" else "srste_unit_kernel", "nm_srste.hip")
+                                     if dtype == "bf16" else "srste_unit_kernel", ("nm_srste.hip",))
         if g_traffic is not None:
             srste["roofline"]["traffic"] = round(g_traffic)
         srste["prune_frac_hbm"] = round(sr_tot["prune"][1] / sr_tot["prune"][0] / 1e9 / PEAK_HBM_GBS, 3)
@@ -598,11 +882,11 @@ def main() -> int:
                 for kind in tr_kinds:
                     if kind != "spmm_t":
                         flush.view(torch.int64).sum()
-                    e0 = torch.cuda.Event(enable_timing=True)
-                    e1 = torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
+                    e0 = hipt.event()
+                    e1 = hipt.event()
+                    hipt.record(e0)
                     launch(d, kind)
-                    e1.record(stream)
+                    hipt.record(e1)
                     tr_ev.setdefault((d["name"], kind), []).append((e0, e1))
         torch.cuda.synchronize()
         del flush
@@ -612,7 +896,7 @@ def main() -> int:
             kept = e * n // m
             meta_t = d["K"] * ((d["R"] // m * n * meta_bits(m) + 31) // 32) * 4
             for kind in tr_kinds:
-                t = float(np.mean([a.elapsed_time(b) for a, b in tr_ev[(d["name"], kind)]])) * 1e-3
+                t = float(np.mean([hipt.ms(a, b) for a, b in tr_ev[(d["name"], kind)]])) * 1e-3
                 entry = {"us": round(t * 1e6, 2)}
                 if kind == "spmm_t":
                     entry["eff_tflops"] = round(2.0 * e * d["T"] / t / 1e12, 1)
@@ -626,6 +910,7 @@ def main() -> int:
     # ---- channel permutation: one round of swap-gain evaluation per matrix ----
     # (compute-bound: pairs of column groups x rows x M^2 swaps, each two max and four adds)
     permutation = {"kernels": {}}
+    valu = profiled_valu(args.workload)
     for d in mats:
         K, G = d["K"], d["K"] // m
         nbytes = int(L.nm_perm_workspace_bytes(d["R"], K, n, m))
@@ -643,31 +928,40 @@ def main() -> int:
         gains_launch()
         torch.cuda.synchronize()
         reps = max(2, min(args.steps, 5))
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
+        e0, e1 = hipt.event(), hipt.event()
+        hipt.record(e0)
         for _ in range(reps):
             gains_launch()
-        e1.record(stream)
+        hipt.record(e1)
         torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) / reps * 1e-3
+        t = hipt.ms(e0, e1) / reps * 1e-3
         evals = G * (G - 1) // 2 * d["R"] * m * m
-        ops = evals * 7  # per swap and row: two adds and two max (the kept sums), one add,
-        #                   one subtract (the base) and one accumulate
-        permutation["kernels"][f"{d['name']}.perm_gains"] = {
-            "ms": round(t * 1e3, 3), "pairs": G * (G - 1) // 2, "swap_row_evals": evals,
-            "gops": round(ops / t / 1e9, 1), "frac_alu": round(ops / t / 1e12 / PEAK_VALU_TOPS, 3)}
+        entry = {"ms": round(t * 1e3, 3), "pairs": G * (G - 1) // 2, "swap_row_evals": evals,
+                 "swap_row_evals_per_s": round(evals / t / 1e9, 1)}
+        # issued VALU instructions per launch, counted by rocprofv3 (SQ_INSTS_VALU) on the
+        # same kernel and shape; each is 64 lane-operations
+        insts = valu.get(d["name"])
+        if insts is not None:
+            lane_ops = insts * 64.0
+            entry.update(valu_insts=insts, lane_tops=round(lane_ops / t / 1e12, 2),
+                         frac_alu=round(lane_ops / t / 1e12 / PEAK_VALU_LANE_TOPS, 3))
+        permutation["kernels"][f"{d['name']}.perm_gains"] = entry
         del ws, gain, pick
     permutation["roofline"] = {
-        "bound": "alu", "unit": "T op/s", "peak": PEAK_VALU_TOPS,
-        "note": "7 fp32 VALU operations per swap and row; peak = the fp32 vector peak "
-                "157.3 TFLOP/s counted as operations (an FMA is two flops): 78.6 T op/s"}
+        "bound": "alu", "unit": "T lane-op/s", "peak": PEAK_VALU_LANE_TOPS,
+        "note": "achieved = SQ_INSTS_VALU of the launch (committed rocprofv3 profile of the same "
+                "kernel, shape and source) x 64 lanes / launch time; peak = 256 CUs x 64 lanes "
+                "x 2.4 GHz, the rate of unpacked VALU instructions (packed fp32 is disabled)"}
 
     cpu = None
     if not args.no_cpu:
         if float_path:
             srste["cpu_baseline"] = srste_cpu_sample(mats, n, m)
-        threads = max(1, min(16, os.cpu_count() or 1))
+        model, visible = cpu_info()
+        threads = max(1, min(16, visible))  # the host share of one GPU on the box is 16 cores
         cpu = cpu_baseline(mats, n, m, threads)
+        cpu.update(cpu_model=model, cores_visible=visible,
+                   one_core=cpu_one_core(mats, n, m))
 
     w0 = mats[0]
     out = {
@@ -689,6 +983,8 @@ def main() -> int:
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "matrix_core_ceiling": ceiling,
+        "sweep_f16": sweep,
         "spmm_eff_tflops": round(F_eff / spmm_t / 1e12, 1),
         "mask_compress": mask_compress,
         "dense_gemm": dense,
@@ -698,6 +994,7 @@ def main() -> int:
         "permutation": permutation,
         "context": "pages: up to 2x dense math throughput on A100 sparse Tensor Cores (not a target)",
     }
+    hipt.close()
     print(json.dumps(out), flush=True)
     return 0
 
