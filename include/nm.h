@@ -4,9 +4,13 @@
  *
  * Plain C; no HIP or PyTorch types appear in the signatures.  Pointer arguments
  * are DEVICE pointers to memory the caller owns, except where a declaration says
- * host memory (nm_perm_search's permutation, nm_check_meta's metadata); the
- * library allocates no device memory and keeps no state besides a
- * once-initialised record of which devices it has checked.  Calls are asynchronous on `stream` (a
+ * host memory (nm_perm_search's permutation, nm_check_meta's metadata).  The
+ * library's state is a once-initialised record of which devices it has checked and,
+ * per device, the fixed scratch buffer of nm_perm_gains_static.  It allocates no
+ * device memory, with one exception: nm_spmm takes a workspace from the
+ * stream-ordered pool (hipMallocAsync, freed in stream order) when the environment
+ * variable NM_SPMM_TILE=3 forces its split schedule onto a shape whose 256 x 256 tiles
+ * do not divide evenly over the compute units.  Calls are asynchronous on `stream` (a
  * hipStream_t passed as void*, NULL = the default stream): NM_OK means the
  * work was enqueued, and a fault inside a kernel surfaces at the caller's next
  * synchronisation.  Arguments are validated before anything is launched; on
@@ -76,7 +80,7 @@
 extern "C" {
 #endif
 
-#define NM_ABI_VERSION 9
+#define NM_ABI_VERSION 10
 
 typedef enum {
   NM_OK = 0,
@@ -90,7 +94,9 @@ typedef enum {
                              in the blocked layout need 16 n / m divisible by 4)     */
   NM_ERR_DEVICE = 7,      /* no usable gfx950 device, or the launch failed           */
   NM_ERR_LAYOUT = 8,      /* unknown layout, or NM_LAYOUT_BLOCKED with K % 64 != 0   */
-  NM_ERR_ALIAS = 9        /* an output overlaps an input it may not replace          */
+  NM_ERR_ALIAS = 9,       /* an output overlaps an input it may not replace          */
+  NM_ERR_SCRATCH = 10     /* the call needs more than the library's fixed device scratch
+                             buffer (NM_STATIC_SCRATCH_BYTES)                         */
 } nm_status;
 
 /* NM_I8: int8 two's complement ("Tensor Scores 상에서 구조적인 sparse GEMM" lists INT8 among
@@ -275,6 +281,25 @@ size_t nm_perm_workspace_bytes(int64_t R, int64_t K, int n, int m);
 nm_status nm_perm_gains(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m,
                         const int32_t* perm, float* gain, int32_t* pick, void* workspace,
                         size_t workspace_bytes, nm_stream_t stream);
+
+/* Bytes of the fixed device scratch buffer behind nm_perm_gains_static: 64 MiB, held on
+ * every device the library runs on (reserved when the library's device code is loaded
+ * there) until the process ends. */
+#define NM_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* nm_perm_gains without a workspace argument and without any device allocation, for
+ * callers that cannot allocate device memory in the call (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments, checks and
+ * results as nm_perm_gains; the permuted fp32 copy of W is built in the library's
+ * per-device static scratch buffer instead of a workspace, so R*K*4 rounded up to 256
+ * bytes must not exceed NM_STATIC_SCRATCH_BYTES (R*K <= 16,777,216), else NM_ERR_SCRATCH.
+ * The kernels run on the current device, and `stream` must belong to it (else
+ * NM_ERR_DEVICE).  All calls on one device share its buffer, and each call overwrites
+ * it before reading it: calls that overlap in time on one device (on different streams,
+ * or from different host threads) race and must be ordered by the caller. */
+nm_status nm_perm_gains_static(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m,
+                               const int32_t* perm, float* gain, int32_t* pick,
+                               nm_stream_t stream);
 
 /* The search: rounds of nm_perm_gains; each round applies the positive gains in
  * descending order (ties: smaller g1, then smaller g2), skipping a pair when either

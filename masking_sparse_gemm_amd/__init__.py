@@ -37,16 +37,17 @@ _BYTE = (torch.int8, torch.float8_e4m3fn)  # 1-byte element types (no training-s
 _FLOAT = (torch.float32, torch.float16, torch.bfloat16)
 _TORCH_DT = {v: k for k, v in _DT.items()}
 STATUS = ["ok", "null", "shape", "pattern", "dtype", "align", "unsupported", "device", "layout",
-          "alias"]
+          "alias", "scratch"]
 LAYOUTS = {"rows": 0, "blocked": 1}
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 # every function the C header declares
 EXPORTS = ("nm_abi_version", "nm_status_str", "nm_values_bytes", "nm_meta_bytes",
            "nm_meta_words_per_row", "nm_mask", "nm_compress", "nm_decompress", "nm_spmm",
            "nm_prune", "nm_srste_grad", "nm_tmask", "nm_tprune", "nm_compress_t",
            "nm_perm_workspace_bytes", "nm_perm_gains", "nm_perm_search", "nm_check_meta",
-           "nm_mask_compress")
+           "nm_mask_compress", "nm_perm_gains_static")
+STATIC_SCRATCH_BYTES = 64 << 20  # NM_STATIC_SCRATCH_BYTES
 SRSTE_DECAY = 0.0002  # the SR-STE page's default decay
 
 
@@ -94,9 +95,10 @@ def lib() -> ctypes.CDLL:
         L.nm_perm_gains.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.nm_perm_search.argtypes = [vp, i32, i64, i64, i32, i32, i32, vp, vp, vp,
                                      ctypes.c_size_t, vp]
+        L.nm_perm_gains_static.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, vp, vp]
         for f in ("nm_mask", "nm_compress", "nm_decompress", "nm_spmm", "nm_prune",
                   "nm_srste_grad", "nm_tmask", "nm_tprune", "nm_compress_t", "nm_perm_gains",
-                  "nm_perm_search"):
+                  "nm_perm_search", "nm_perm_gains_static"):
             getattr(L, f).restype = i32
         if L.nm_abi_version() != ABI_VERSION:
             raise ImportError(f"{LIB_PATH} has ABI {L.nm_abi_version()}, expected {ABI_VERSION}: "
@@ -390,6 +392,22 @@ def perm_gains(W: torch.Tensor, perm: torch.Tensor, n: int = 2, m: int = 4):
     _check("nm_perm_gains", lib().nm_perm_gains(_ptr(W), dt, R, K, n, m, _ptr(perm.contiguous()),
                                                 _ptr(gain), _ptr(pick), _ptr(ws), ws.numel(),
                                                 _stream(W)))
+    return gain, pick
+
+
+def perm_gains_static(W: torch.Tensor, perm: torch.Tensor, n: int = 2, m: int = 4):
+    """perm_gains through nm_perm_gains_static: the library's fixed device scratch buffer
+    stands in for the workspace (R*K <= 16,777,216), so the C call allocates nothing; the
+    result tensors are allocated here, before the call."""
+    dt = _dense_input(W, "W")
+    R, K = W.shape
+    G = K // m
+    if perm.dtype != torch.int32 or perm.shape != (K,) or perm.device != W.device:
+        raise ValueError("perm must be an int32 (K,) tensor on W's device")
+    gain = torch.zeros((G, G), dtype=torch.float32, device=W.device)
+    pick = torch.zeros((G, G), dtype=torch.int32, device=W.device)
+    _check("nm_perm_gains_static", lib().nm_perm_gains_static(
+        _ptr(W), dt, R, K, n, m, _ptr(perm.contiguous()), _ptr(gain), _ptr(pick), _stream(W)))
     return gain, pick
 
 

@@ -1,10 +1,12 @@
 // nm_api.hip -- the C ABI declared in include/nm.h: argument checks and dispatch.
 //
 // Every check runs on the host before any HIP call, so a rejected call touches
-// neither the device nor the outputs.  The only global state is a per-device
-// record of whether the device is a gfx950, filled on first use.
+// neither the device nor the outputs.  The global state is a per-device record of
+// whether the device is a gfx950, filled on first use, and the per-device address of
+// the static scratch buffer behind nm_perm_gains_static, looked up on first use.
 #include <atomic>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/nm.h"
@@ -105,6 +107,7 @@ const char* nm_status_str(nm_status s) {
     case NM_ERR_DEVICE: return "device error (no gfx950 device, or launch failed)";
     case NM_ERR_LAYOUT: return "bad layout (unknown, or blocked layout with K not a multiple of 64)";
     case NM_ERR_ALIAS: return "an output overlaps an input it may not replace";
+    case NM_ERR_SCRATCH: return "the call needs more than the library's static scratch buffer";
   }
   return "unknown status";
 }
@@ -407,6 +410,66 @@ nm_status nm_perm_gains(const void* W, nm_dtype dt, int64_t R, int64_t K, int n,
   if (R * K == 0 || G < 2) return NM_OK;
   if ((st = check_device()) != NM_OK) return st;
   return from_hip(nm::launch_perm_gains(W, (int)dt, R, K, n, m, perm, gain, pick, workspace,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+// The scratch buffer of nm_perm_gains_static.  Each device holds its own copy at its own
+// address; in host code the name is only the host-side handle of the symbol, so kernels get
+// the device address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[NM_STATIC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on device `dev` (the current device), looked up once per
+// device; nullptr if the lookup fails.
+void* scratch_on(int dev) {
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+nm_status nm_perm_gains_static(const void* W, nm_dtype dt, int64_t R, int64_t K, int n, int m,
+                               const int32_t* perm, float* gain, int32_t* pick,
+                               nm_stream_t stream) {
+  if (!valid_dtype(dt)) return NM_ERR_DTYPE;
+  nm_status st = check_pattern(n, m);
+  if (st != NM_OK) return st;
+  if ((st = check_shape(R, K, m)) != NM_OK) return st;
+  if (R * K >= ((int64_t)1 << 31)) return NM_ERR_SHAPE;  // 32-bit gather indices, as nm_perm_gains
+  const int64_t G = K / m;
+  if (missing(W, R * K) || missing(perm, K) || missing(gain, G * G) || missing(pick, G * G))
+    return NM_ERR_NULL;
+  // the kernels use only the permuted fp32 copy of W: the first part of the workspace
+  if ((size_t)(R * K) * 4 > NM_STATIC_SCRATCH_BYTES) return NM_ERR_SCRATCH;
+  if (!aligned16(W)) return NM_ERR_ALIGN;
+  if (R * K == 0 || G < 2) return NM_OK;
+  if ((st = check_device()) != NM_OK) return st;
+  int dev = 0, sdev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return NM_ERR_DEVICE;
+  if (stream != nullptr &&
+      (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess || sdev != dev))
+    return NM_ERR_DEVICE;
+  void* ws = scratch_on(dev);
+  if (ws == nullptr) return NM_ERR_DEVICE;
+  return from_hip(nm::launch_perm_gains(W, (int)dt, R, K, n, m, perm, gain, pick, ws,
                                         static_cast<hipStream_t>(stream)));
 }
 

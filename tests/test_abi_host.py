@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     L = nm.lib()
     for name in header_functions():
         assert hasattr(L, name), name
-    assert L.nm_abi_version() == nm.ABI_VERSION == 9
+    assert L.nm_abi_version() == nm.ABI_VERSION == 10
 
 
 @needs_lib
@@ -48,7 +48,7 @@ def test_library_has_no_undefined_symbols_of_its_own():
 
 @needs_lib
 def test_status_strings():
-    for code in range(10):
+    for code in range(11):
         s = nm.status_str(code)
         assert s and s != "unknown status"
     assert nm.status_str(99) == "unknown status"
@@ -416,3 +416,30 @@ def test_outputs_overlapping_inputs_are_rejected():
     # fp32 output: Y is twice as large
     assert st(L.nm_spmm(FAKE, FAKE + MB, R, K, 2, 4, 0, FAKE + 2 * MB, T, BF,
                         FAKE + 2 * MB - 0x1000, nm.NM_F32, None)) == "alias"
+
+
+@needs_lib
+def test_perm_gains_static_checks_its_scratch_limit():
+    """nm_perm_gains_static needs R*K*4 bytes of the 64 MiB static scratch buffer: one element
+    more than fits returns NM_ERR_SCRATCH before any device access; a call that fits passes
+    every host check and reaches the device check, which fails on a host without a GPU."""
+    L = nm.lib()
+    st = lambda c: nm.STATUS[c]
+    BF = nm.NM_BF16
+    limit = nm.STATIC_SCRATCH_BYTES // 4          # fp32 elements of the permuted copy
+    K = 4096
+    R_fit = limit // K                            # 4096 x 4096 fills the buffer exactly
+    args = lambda R: (FAKE, BF, R, K, 2, 4, FAKE + 0x4000000 * 3, FAKE + 0x4000000 * 4,
+                      FAKE + 0x4000000 * 5, None)
+    assert st(L.nm_perm_gains_static(*args(R_fit + 1))) == "scratch"
+    assert st(L.nm_perm_gains_static(*args(R_fit))) == "device"
+    assert st(L.nm_perm_gains_static(FAKE, BF, 64, 130, 2, 4, FAKE, FAKE, FAKE, None)) == "shape"
+    assert st(L.nm_perm_gains_static(None, BF, 64, 128, 2, 4, FAKE, FAKE, FAKE, None)) == "null"
+    assert st(L.nm_perm_gains_static(FAKE, BF, 64, 128, 2, 4, None, FAKE, FAKE, None)) == "null"
+    assert st(L.nm_perm_gains_static(FAKE, nm.NM_I32, 64, 128, 2, 4, FAKE, FAKE, FAKE,
+                                     None)) == "dtype"
+    assert st(L.nm_perm_gains_static(FAKE + 8, BF, 64, 128, 2, 4, FAKE, FAKE, FAKE,
+                                     None)) == "align"
+    # empty inputs and a single group are no-ops that touch nothing
+    assert st(L.nm_perm_gains_static(None, BF, 0, 128, 2, 4, FAKE, FAKE, FAKE, None)) == "ok"
+    assert st(L.nm_perm_gains_static(FAKE, BF, 64, 4, 2, 4, FAKE, FAKE, FAKE, None)) == "ok"
