@@ -82,10 +82,20 @@ extern "C" {
 
 #define NM_ABI_VERSION 10
 
-typedef enum {
+/* The enumerations are int-sized in C and C++ alike.  In C++ they are declared with int
+ * as their underlying type, so that an out-of-range value a caller passes (an unknown
+ * dtype, layout or status code) is a valid value the checks reject, not undefined
+ * behaviour. */
+#ifdef __cplusplus
+#define NM_INT_ENUM : int
+#else
+#define NM_INT_ENUM
+#endif
+
+typedef enum NM_INT_ENUM {
   NM_OK = 0,
   NM_ERR_NULL = 1,        /* a required pointer is NULL                              */
-  NM_ERR_SHAPE = 2,       /* negative size, or K not a multiple of M                 */
+  NM_ERR_SHAPE = 2,       /* negative size, K not a multiple of M, or R*K >= 2^36    */
   NM_ERR_PATTERN = 3,     /* N:M outside 1 <= N <= M, M in {2, 4, 8}                 */
   NM_ERR_DTYPE = 4,       /* unknown dtype, y_dt not allowed for dt, or int8 where a
                              floating-point weight is required                       */
@@ -105,9 +115,11 @@ typedef enum {
  * NM_FP8: OCP FP8 E4M3 bytes (bias 7, no infinities, S.1111.111 is NaN), ranked by the
  * sign-cleared bits like the other floating types; not one of the pages' types, the
  * same method one format narrower. */
-typedef enum { NM_F32 = 0, NM_F16 = 1, NM_BF16 = 2, NM_I8 = 3, NM_I32 = 4, NM_FP8 = 5 } nm_dtype;
+typedef enum NM_INT_ENUM {
+  NM_F32 = 0, NM_F16 = 1, NM_BF16 = 2, NM_I8 = 3, NM_I32 = 4, NM_FP8 = 5
+} nm_dtype;
 
-typedef enum { NM_LAYOUT_ROWS = 0, NM_LAYOUT_BLOCKED = 1 } nm_layout;
+typedef enum NM_INT_ENUM { NM_LAYOUT_ROWS = 0, NM_LAYOUT_BLOCKED = 1 } nm_layout;
 
 typedef void* nm_stream_t; /* a hipStream_t; NULL selects the default stream */
 

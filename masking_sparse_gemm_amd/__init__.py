@@ -28,7 +28,8 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libnm.so")
+# NM_LIB_PATH names another build of the same library (the sanitizer test's host-instrumented one)
+LIB_PATH = os.environ.get("NM_LIB_PATH") or os.path.join(HERE, "libnm.so")
 
 NM_F32, NM_F16, NM_BF16, NM_I8, NM_I32, NM_FP8 = 0, 1, 2, 3, 4, 5
 _DT = {torch.float32: NM_F32, torch.float16: NM_F16, torch.bfloat16: NM_BF16, torch.int8: NM_I8,

@@ -46,8 +46,10 @@ nm_status check_pattern(int n, int m) {
 
 nm_status check_shape(int64_t R, int64_t K, int m) {
   if (R < 0 || K < 0 || K % m != 0) return NM_ERR_SHAPE;
-  // element counts must fit the kernels' 64-bit index arithmetic comfortably
-  if (R > 0 && K > ((int64_t)1 << 40) / R) return NM_ERR_SHAPE;
+  // below 2^36 elements (128 GiB of 16-bit W) every launch of the element-wise passes has
+  // fewer than 2^32 work-items: their fast kernels give each work-item at least 16 elements,
+  // and the per-group fallbacks loop over a capped grid
+  if (R > 0 && K >= ((int64_t)1 << 36) / R + ((((int64_t)1 << 36) % R) != 0)) return NM_ERR_SHAPE;
   return NM_OK;
 }
 
@@ -99,7 +101,7 @@ const char* nm_status_str(nm_status s) {
   switch (s) {
     case NM_OK: return "ok";
     case NM_ERR_NULL: return "null pointer";
-    case NM_ERR_SHAPE: return "bad shape (negative size or K not a multiple of M)";
+    case NM_ERR_SHAPE: return "bad shape (negative size, K not a multiple of M, or R*K >= 2^36)";
     case NM_ERR_PATTERN: return "bad N:M pattern (need 1 <= N <= M, M in {2,4,8})";
     case NM_ERR_DTYPE: return "bad dtype (unknown, or output neither input dtype nor fp32)";
     case NM_ERR_ALIGN: return "pointer not 16-byte aligned";

@@ -63,11 +63,16 @@ _lib = None
 
 
 def lib():
+    """The loaded oracle library: libnm_oracle.so, built here when stale, or the build named
+    by NM_ORACLE_LIB (the sanitizer test's instrumented build of the same source)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build(force=True)
-        L = ctypes.CDLL(_LIB)
+        path = os.environ.get("NM_ORACLE_LIB")
+        if not path:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build(force=True)
+            path = _LIB
+        L = ctypes.CDLL(path)
         i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
         L.nmo_meta_bits.argtypes = [i32]
         L.nmo_meta_bits.restype = i32

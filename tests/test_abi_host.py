@@ -443,3 +443,30 @@ def test_perm_gains_static_checks_its_scratch_limit():
     # empty inputs and a single group are no-ops that touch nothing
     assert st(L.nm_perm_gains_static(None, BF, 0, 128, 2, 4, FAKE, FAKE, FAKE, None)) == "ok"
     assert st(L.nm_perm_gains_static(FAKE, BF, 64, 4, 2, 4, FAKE, FAKE, FAKE, None)) == "ok"
+
+
+@needs_lib
+def test_shape_limit_is_2_pow_36_elements():
+    """Below 2^36 elements every launch of the element-wise passes fits the 2^32 work-items
+    of one dispatch; R*K = 2^36 is refused before any device access, one row less passes
+    every host check (and stops at the device check on a host without a GPU)."""
+    L = nm.lib()
+    st = lambda c: nm.STATUS[c]
+    K = 1 << 20
+    R = (1 << 36) // K
+    assert st(L.nm_mask(FAKE, nm.NM_BF16, R, K, 2, 4, FAKE + (1 << 40), None)) == "shape"
+    assert st(L.nm_mask(FAKE, nm.NM_BF16, R - 1, K, 2, 4, FAKE + (1 << 40), None)) == "device"
+    assert st(L.nm_mask(FAKE, nm.NM_BF16, 3, ((1 << 36) + 2) // 3, 2, 2, FAKE + (1 << 40), None)) == "shape"
+    assert L.nm_values_bytes(R, K, 2, 4, nm.NM_BF16, 0) == 0
+    assert L.nm_values_bytes(R - 1, K, 2, 4, nm.NM_BF16, 0) == (R - 1) * K // 2 * 2
+
+
+@needs_lib
+def test_out_of_range_enum_values_are_rejected():
+    """Unknown dtype, layout and status values are ordinary ints to the library (its
+    enumerations have int as their underlying type), refused by the checks."""
+    L = nm.lib()
+    assert nm.STATUS[L.nm_mask(FAKE, 99, 64, 128, 2, 4, FAKE + (1 << 30), None)] == "dtype"
+    assert nm.STATUS[L.nm_mask(FAKE, -1, 64, 128, 2, 4, FAKE + (1 << 30), None)] == "dtype"
+    assert L.nm_values_bytes(64, 128, 2, 4, nm.NM_BF16, 7) == 0
+    assert nm.status_str(-5) == "unknown status" and nm.status_str(1 << 30) == "unknown status"
