@@ -174,3 +174,44 @@ def test_i8_full_workloads(name, layout):
     ts = np.concatenate([rng.integers(0, w.T, 1500), [w.T - 1, w.T - 1]])
     want = oracle.spmm_sample(vals_o, meta_o, w.R, w.K, 2, 4, X, "i8", rs, ts)
     assert np.array_equal(Y[rs, ts].astype(np.float64), want)
+
+
+def crafted_i8_case(n, m, R, K, T, seed):
+    """W, X for test_i8_expansion_exact_past_fp32_integers: large same-sign products almost
+    everywhere, +-1 entries where they are kept or multiplied."""
+    rng = np.random.default_rng(seed)
+    s = rng.choice([-1, 1], size=K)
+    W = np.broadcast_to(s[None, :] * 127, (R, K)).copy()
+    W[(s[None, :] < 0) & (rng.random((R, K)) < 0.3)] = -128
+    # in one group in five, m - n + 1 entries become +-1: the group then keeps n - 1 large
+    # values and one +-1 (the first of the tied small ones)
+    G = K // m
+    for r, g in zip(*np.nonzero(rng.random((R, G)) < 0.2)):
+        pos = g * m + rng.choice(m, size=m - n + 1, replace=False)
+        W[r, pos] = rng.choice([-1, 1], size=pos.size)
+    X = np.broadcast_to(s[:, None] * 127, (K, T)).copy()
+    X[(s[:, None] < 0) & (rng.random((K, T)) < 0.3)] = -128
+    small = rng.random((K, T)) < 0.05
+    X[small] = rng.choice([-1, 1], size=int(small.sum()))
+    return W.astype(np.int8), X.astype(np.int8)
+
+
+@pytest.mark.parametrize("n,m", [(4, 8), (1, 4), (3, 4)])
+@pytest.mark.parametrize("layout", ["rows", "blocked"])
+def test_i8_expansion_exact_past_fp32_integers(n, m, layout):
+    """The expansion kernel's int8 product where rounding would show.  Most kept products
+    are +127^2 .. +128^2 (W's column signs match X's row signs), so each 512-wide run of K
+    sums to within a factor 4 of 2^23 and every total passes 2^24; +-1 entries kept in W
+    and spread through X put odd products of +-1 and +-127 beside them in every 16-wide run.
+    An fp32 total, a run summed past 2^24, or an adder that drops low bits against a large
+    partial sum would lose them; the int32 totals must equal the oracle's exact integers."""
+    R, K, T = 96, 6144, 80
+    W, X = crafted_i8_case(n, m, R, K, T, 4000 + 10 * n + m)
+    vals_o, meta_o = oracle.compress(W, "i8", n, m)
+    y_ref = oracle.spmm(vals_o, meta_o, R, K, n, m, X, "i8")
+    assert np.abs(y_ref).min() > 2 ** 24 and (y_ref % 2 == 1).any()   # the case is what it says
+    v, mt = nm.compress(dev8(W), n, m, layout=layout)
+    Y = nm.spmm(v, mt, dev8(X), n, m, layout=layout, rows=R)
+    got = Y.cpu().numpy().astype(np.float64)
+    bad = got != y_ref
+    assert not bad.any(), f"{int(bad.sum())} of {bad.size} differ, first at {np.argwhere(bad)[0]}"
