@@ -11,7 +11,8 @@
 // per-wave LDS bit buffer otherwise.  The flat kernels need every row to hold a whole
 // number of units and of metadata words, so that rows concatenate into one stream; any
 // other shape uses the simple per-group / per-word kernels at the bottom, which make no
-// such assumption.
+// such assumption and loop over their work with a capped grid (nm_grid.h), so that no
+// accepted shape needs more work-items than one launch may have.
 //
 // Formats ("[리뷰] Accelerating Sparse Deep Neural Networks", section
 // "2:4 Sparsity의 benefits"): values hold the N kept elements of each group in
@@ -26,6 +27,7 @@
 #include <utility>
 
 #include "nm_device.h"
+#include "nm_grid.h"
 #include "nm_launch.h"
 
 namespace nm {
@@ -582,8 +584,9 @@ __global__ void __launch_bounds__(kThreads) blocked_select_t_kernel(
 template <typename E, int N, int M>
 __global__ void __launch_bounds__(kThreads) group_t_kernel(const E* __restrict__ W, int64_t R,
                                                            int64_t K, E* __restrict__ values) {
-  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= R / M * K) return;
+  const int64_t work = R / M * K;
+  for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < work;
+       idx += (int64_t)gridDim.x * kThreads) {
   const int64_t g = idx / K, k = idx % K;
   uint32_t key[M], v[M];
 #pragma unroll
@@ -601,6 +604,7 @@ __global__ void __launch_bounds__(kThreads) group_t_kernel(const E* __restrict__
     for (int i = 1; i < M; ++i) x = (pos[j] == i) ? v[i] : x;
     dst[j] = (E)x;
   }
+  }
 }
 
 // Metadata words of the transposed row layout: one thread per (W column k, word w).
@@ -609,8 +613,8 @@ __global__ void __launch_bounds__(kThreads) meta_word_t_kernel(const E* __restri
                                                                int64_t K, int64_t wpr,
                                                                uint32_t* __restrict__ meta) {
   constexpr int b = meta_bits(M);
-  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= K * wpr) return;
+  for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < K * wpr;
+       idx += (int64_t)gridDim.x * kThreads) {
   const int64_t w = idx / K, k = idx % K;
   const int64_t fields = R / M * N;
   const int64_t f0 = (32 * w) / b;
@@ -632,6 +636,7 @@ __global__ void __launch_bounds__(kThreads) meta_word_t_kernel(const E* __restri
     }
   }
   meta[k * wpr + w] = word;
+  }
 }
 
 template <typename E, int N, int M>
@@ -751,17 +756,18 @@ template <typename E, int N, int M, bool kMask, bool kValues>
 __global__ void __launch_bounds__(kThreads) group_kernel(const E* __restrict__ W, int64_t groups,
                                                          E* __restrict__ values,
                                                          uint8_t* __restrict__ mask) {
-  const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (g >= groups) return;
-  int pos[N];
-  uint32_t keep;
-  select_group<E, N, M>(W, g * M, pos, keep);
-  if constexpr (kMask)
+  for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < groups;
+       g += (int64_t)gridDim.x * kThreads) {
+    int pos[N];
+    uint32_t keep;
+    select_group<E, N, M>(W, g * M, pos, keep);
+    if constexpr (kMask)
 #pragma unroll
-    for (int i = 0; i < M; ++i) mask[g * M + i] = (keep >> i) & 1u;
-  if constexpr (kValues)
+      for (int i = 0; i < M; ++i) mask[g * M + i] = (keep >> i) & 1u;
+    if constexpr (kValues)
 #pragma unroll
-    for (int j = 0; j < N; ++j) values[g * N + j] = W[g * M + pos[j]];
+      for (int j = 0; j < N; ++j) values[g * N + j] = W[g * M + pos[j]];
+  }
 }
 
 // one thread per metadata word
@@ -770,8 +776,8 @@ __global__ void __launch_bounds__(kThreads) meta_word_kernel(const E* __restrict
                                                              int64_t K, int64_t wpr,
                                                              uint32_t* __restrict__ meta) {
   constexpr int b = meta_bits(M);
-  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= R * wpr) return;
+  for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < R * wpr;
+       idx += (int64_t)gridDim.x * kThreads) {
   const int64_t r = idx / wpr, w = idx % wpr;
   const int64_t fields = K / M * N;
   const int64_t f0 = (32 * w) / b;
@@ -791,6 +797,7 @@ __global__ void __launch_bounds__(kThreads) meta_word_kernel(const E* __restrict
     }
   }
   meta[idx] = word;
+  }
 }
 
 // one thread per group of the output
@@ -800,8 +807,8 @@ __global__ void __launch_bounds__(kThreads) group_decompress_kernel(
     int64_t wpr, E* __restrict__ out) {
   constexpr int b = meta_bits(M);
   const int64_t gpr = K / M;
-  const int64_t gi = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (gi >= R * gpr) return;
+  for (int64_t gi = (int64_t)blockIdx.x * kThreads + threadIdx.x; gi < R * gpr;
+       gi += (int64_t)gridDim.x * kThreads) {
   const int64_t r = gi / gpr, g = gi % gpr;
   const uint32_t* mrow = meta + r * wpr;
   E o[M];
@@ -819,6 +826,7 @@ __global__ void __launch_bounds__(kThreads) group_decompress_kernel(
   }
 #pragma unroll
   for (int i = 0; i < M; ++i) out[r * K + g * M + i] = o[i];
+  }
 }
 
 inline unsigned blocks_for(int64_t work, int64_t per_block) {
@@ -896,7 +904,7 @@ hipError_t run_select(const void* W, int64_t R, int64_t K, bool blocked, void* v
    }
   }
   const int64_t groups = elems / M;
-  const unsigned grid = blocks_for(groups, kThreads);
+  const unsigned grid = stride_grid(groups, kThreads);
   const E* w = static_cast<const E*>(W);
   E* v = static_cast<E*>(values);
   if (want_mask && want_compress)
@@ -909,7 +917,7 @@ hipError_t run_select(const void* W, int64_t R, int64_t K, bool blocked, void* v
   if (e != hipSuccess || !want_compress) return e;
   const int64_t wpr = ((K / M) * N * meta_bits(M) + 31) / 32;
   if (R * wpr > 0)
-    meta_word_kernel<E, N, M><<<blocks_for(R * wpr, kThreads), kThreads, 0, s>>>(w, R, K, wpr, meta);
+    meta_word_kernel<E, N, M><<<stride_grid(R * wpr, kThreads), kThreads, 0, s>>>(w, R, K, wpr, meta);
   return hipGetLastError();
 }
 
@@ -925,12 +933,12 @@ hipError_t run_select_t(const void* W, int64_t R, int64_t K, bool blocked, void*
         w, R, K, static_cast<uint32_t*>(values), meta);
     return hipGetLastError();
   }
-  group_t_kernel<E, N, M><<<blocks_for(R / M * K, kThreads), kThreads, 0, s>>>(
+  group_t_kernel<E, N, M><<<stride_grid(R / M * K, kThreads), kThreads, 0, s>>>(
       w, R, K, static_cast<E*>(values));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t wpr = ((R / M) * N * meta_bits(M) + 31) / 32;
-  meta_word_t_kernel<E, N, M><<<blocks_for(K * wpr, kThreads), kThreads, 0, s>>>(w, R, K, wpr,
+  meta_word_t_kernel<E, N, M><<<stride_grid(K * wpr, kThreads), kThreads, 0, s>>>(w, R, K, wpr,
                                                                                  meta);
   return hipGetLastError();
 }
@@ -968,7 +976,7 @@ hipError_t run_decompress(const void* values, const uint32_t* meta, int64_t R, i
     }
   }
   const int64_t wpr = ((K / M) * N * meta_bits(M) + 31) / 32;
-  group_decompress_kernel<E, N, M><<<blocks_for(elems / M, kThreads), kThreads, 0, s>>>(
+  group_decompress_kernel<E, N, M><<<stride_grid(elems / M, kThreads), kThreads, 0, s>>>(
       static_cast<const E*>(values), meta, R, K, wpr, static_cast<E*>(out));
   return hipGetLastError();
 }
