@@ -10,6 +10,9 @@
  * (the device lowers its clock under heavy matrix-core load, more so for values with many
  * toggling bits), so the probe runs the instruction alone on caller-chosen operands.
  *
+ * The VALU loop does the same for the vector ALU, the unit the permutation search's gains
+ * kernel is bound by.
+ *
  * Pointers are DEVICE pointers owned by the caller; calls are asynchronous on `stream`
  * (a hipStream_t as void*, NULL = the default stream).  Returns 0 when the launch was
  * enqueued, 1 for invalid arguments, 2 for a launch error.
@@ -42,6 +45,13 @@ int64_t nm_probe_operand_bytes(void);
  * receives one accumulator sum per lane so the work is not optimised away. */
 int nm_probe_matrix_core(int kind, const void* operands, int cus, int waves_per_simd, int iters,
                          int64_t* clocks, float* sink, void* stream);
+
+/* VALU issue-rate loop, the bound of the permutation gains kernel (fp32 max, min, add and
+ * select on registers).  op 0: v_add_f32, 1: v_max_f32, 2: v_fma_f32 (plain, not packed).
+ * Every lane keeps 16 independent fp32 chains; every wave issues iters x 64 instructions of
+ * that one kind.  Grid, clocks and sink as in nm_probe_matrix_core. */
+int nm_probe_valu(int op, int cus, int waves_per_simd, int iters, int64_t* clocks, float* sink,
+                  void* stream);
 
 #ifdef __cplusplus
 }

@@ -113,8 +113,8 @@ _probe = None
 
 
 def probe_lib() -> ctypes.CDLL:
-    """The loaded libnm_probe.so (include/nm_probe.h): the benchmark's matrix-core rate
-    probes (raises if it is not built)."""
+    """The loaded libnm_probe.so (include/nm_probe.h): the benchmark's matrix-core and VALU
+    rate probes (raises if it is not built)."""
     global _probe
     if _probe is None:
         if not os.path.exists(PROBE_LIB_PATH):
@@ -127,6 +127,9 @@ def probe_lib() -> ctypes.CDLL:
         P.nm_probe_matrix_core.argtypes = [ctypes.c_int, vp, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_int, vp, vp, vp]
         P.nm_probe_matrix_core.restype = ctypes.c_int
+        P.nm_probe_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp,
+                                    vp, vp]
+        P.nm_probe_valu.restype = ctypes.c_int
         _probe = P
     return _probe
 

@@ -88,6 +88,52 @@ __global__ void __launch_bounds__(256) probe_kernel(const uint16_t* __restrict__
   sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// VALU issue-rate loop: 16 independent fp32 chains per lane, 64 wave instructions of one
+// kind per iteration, nothing but registers.  OP 0: v_add_f32, 1: v_max_f32, 2: v_fma_f32.
+template <int OP>
+__global__ void __launch_bounds__(256) valu_probe_kernel(int iters, int64_t* __restrict__ clocks,
+                                                         float* __restrict__ sink) {
+  float a[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) a[i] = (float)(threadIdx.x + i) * 0.25f;
+  const float b = 1.0f / (float)(threadIdx.x + 3);
+  const float c = 0.5f;
+  const bool timer = threadIdx.x == 0;
+  int64_t t0 = 0, r0 = 0;
+  if (timer) {
+    t0 = (int64_t)__builtin_amdgcn_s_memtime();
+    r0 = (int64_t)__builtin_amdgcn_s_memrealtime();
+  }
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if constexpr (OP == 0) {
+          asm volatile("v_add_f32 %0, %0, %1" : "+v"(a[i]) : "v"(b));
+        } else if constexpr (OP == 1) {
+          asm volatile("v_max_f32 %0, %0, %1" : "+v"(a[i]) : "v"(b));
+        } else {
+          asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(a[i]) : "v"(b), "v"(c));
+        }
+      }
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s += a[i];
+  if (timer) {
+    const int64_t t1 = (int64_t)__builtin_amdgcn_s_memtime();
+    const int64_t r1 = (int64_t)__builtin_amdgcn_s_memrealtime();
+    int64_t* cl = clocks + 4 * blockIdx.x;
+    cl[0] = t0;
+    cl[1] = t1;
+    cl[2] = r0;
+    cl[3] = r1;
+  }
+  sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
 }  // namespace
 
 extern "C" {
@@ -104,6 +150,17 @@ int nm_probe_matrix_core(int kind, const void* operands, int cus, int waves_per_
   hipLaunchKernelGGL(k, dim3(cus * waves_per_simd), dim3(256), 0,
                      static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(operands),
                      iters, clocks, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+int nm_probe_valu(int op, int cus, int waves_per_simd, int iters, int64_t* clocks, float* sink,
+                  void* stream) {
+  if (op < 0 || op > 2 || clocks == nullptr || sink == nullptr || cus < 1 || cus > 4096 ||
+      waves_per_simd < 1 || waves_per_simd > 8 || iters < 1)
+    return 1;
+  auto k = op == 0 ? valu_probe_kernel<0> : op == 1 ? valu_probe_kernel<1> : valu_probe_kernel<2>;
+  hipLaunchKernelGGL(k, dim3(cus * waves_per_simd), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), iters, clocks, sink);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
