@@ -13,16 +13,18 @@ flops (2 R K T per matrix) divided by the step time.  Per-kernel figures,
 the roofline of the dominant kernel, the dense GEMM on the same shapes and the
 CPU oracle timed on the host are reported alongside.
 
-Each step kernel is also timed cold (a 512 MiB read, twice the 256 MB Infinity Cache,
-before each launch, outside its events) beside the in-step (warm) timing.  The fp16 N:M
-sweep (4096 x 4096 weights, 8192 activation columns; 1:2, 2:4, 4:8 and mask-only) is
-timed the same way under "sweep_f16", with its product's roofline and the dense GEMM.
-The matrix cores' own rate on the workload's values (libnm_probe) is reported under
-"matrix_core_ceiling".
+Each step kernel is also timed cold beside the in-step (warm) timing: launched on copies
+of its buffers in rotation, enough copies that 512 MiB of other traffic (twice the 256 MB
+Infinity Cache) separates two launches on one copy, rounds of the rotation between two
+events.  The fp16 N:M sweep (4096 x 4096 weights, 8192 activation columns; 1:2, 2:4, 4:8
+and mask-only) is timed warm (back to back) and cold the same way under "sweep_f16",
+with its product's roofline and the dense GEMM.  The matrix cores' own rate on the
+workload's values and the vector ALU's rate (libnm_probe) are reported under
+"matrix_core_ceiling" and in the permutation roofline.
 
 The SR-STE passes of a training step on the same weights (nm_prune, the
 forward's masked weight, and nm_srste_grad, the backward's gradient) are timed
-in a separate pass after the step, each launch after a cache-clearing fill, and
+in a separate pass after the step, each launch after a 512 MiB read, and
 reported under "srste" with their HBM roofline; they are not part of `value`.
 So is the transposable-mask path under "transposable": nm_tprune (greedy
 transposable mask applied), nm_compress_t (the compressed transpose) and the
@@ -48,11 +50,12 @@ METRIC = "2:4 spmm effective TFLOP/s + mask/compress GB/s (% of MI355X roofline)
 METRIC_I8 = "2:4 int8 spmm effective TOP/s + mask/compress GB/s (% of MI355X roofline)"
 METRIC_FP8 = "2:4 fp8 spmm effective TFLOP/s + mask/compress GB/s (% of MI355X roofline)"
 PEAK_HBM_GBS = 8000.0
-# VALU lane operations the build can issue: packed fp32 is disabled, so a compute unit
-# retires 64 lane-operations per clock (4 SIMDs x 16 lanes; one wave instruction is 64
-# lane-operations over 4 clocks): 256 CUs x 64 x 2.4 GHz = 39.3 T lane-op/s.  (The
-# 157.3 TFLOP/s fp32 vector peak needs packed fp32 FMA: 2 operations per lane and 2 flops each.)
-PEAK_VALU_LANE_TOPS = 39.32
+# Vector-ALU peak in lane operations: the published fp32 vector rate, 157.3 TFLOP/s, is
+# 256 CUs x 128 FMA lanes per clock x 2 flops x 2.4 GHz, i.e. 78.6 T lane-op/s.  The VALU
+# probe (libnm_probe) shows plain, unpacked v_add_f32 and v_fma_f32 retiring 112-114 lanes
+# per clock per CU, so this rate needs no packed math (which this build never emits);
+# v_max_f32 retires at half that rate, so a kernel heavy in max/min stays below it.
+PEAK_VALU_LANE_TOPS = 78.64
 # dense matrix-core peaks (TFLOP/s; TOP/s for int8)
 PEAK_MFMA_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3, "i8": 5033.2, "fp8": 5033.2}
 # workload name -> (synthetic matrices, N:M pattern)
@@ -378,11 +381,50 @@ def matrix_core_ceiling(torch, dev, stream, hipt, w_vals, x_vals, waves_per_simd
     return out
 
 
-def sweep_f16_block(torch, nm, synth, L, dev, stream, hipt, args, flush, cold_times):
+def valu_ceiling(torch, dev, stream, hipt):
+    """What the vector ALU sustains alone (libnm_probe): plain (unpacked) v_add_f32,
+    v_max_f32 and v_fma_f32 in register-only loops, 1 to 8 waves per SIMD.  Returns, per
+    instruction, the best rate in T lane-op/s (wave instructions x 64 lanes / s), the lanes
+    retired per clock per CU at the measured shader clock, and that clock."""
+    import masking_sparse_gemm_amd as nm
+
+    P = nm.probe_lib()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = {"cus": cus}
+    clocks = torch.zeros(4 * cus * 8, dtype=torch.int64, device=dev)
+    sink = torch.zeros(cus * 8 * 256, dtype=torch.float32, device=dev)
+    iters = 20000
+    for name, op in (("v_add_f32", 0), ("v_max_f32", 1), ("v_fma_f32", 2)):
+        best = None
+        for wps in (1, 2, 4, 8):
+            P.nm_probe_valu(op, cus, wps, iters, clocks.data_ptr(), sink.data_ptr(), stream.cuda_stream)
+            e0, e1 = hipt.event(), hipt.event()
+            hipt.record(e0)
+            rc = P.nm_probe_valu(op, cus, wps, iters, clocks.data_ptr(), sink.data_ptr(),
+                                 stream.cuda_stream)
+            hipt.record(e1)
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"nm_probe_valu failed ({rc})")
+            t = hipt.ms(e0, e1) * 1e-3
+            lane_ops = cus * wps * 4 * iters * 64 * 64.0
+            c = clocks[: 4 * cus * wps].view(-1, 4).cpu().numpy().astype(np.float64)
+            mhz = float(np.median((c[:, 1] - c[:, 0]) / np.maximum(c[:, 3] - c[:, 2], 1) * 100.0))
+            r = {"waves_per_simd": wps, "lane_tops": round(lane_ops / t / 1e12, 2),
+                 "lanes_per_clock_per_cu": round(lane_ops / t / (mhz * 1e6) / cus, 1),
+                 "clock_mhz": round(mhz, 0), "ms": round(t * 1e3, 3)}
+            if best is None or r["lane_tops"] > best["lane_tops"]:
+                best = r
+        out[name] = best
+    return out
+
+
+def sweep_f16_block(torch, nm, synth, L, dev, stream, hipt, args, cold_times):
     """The fp16 N:M sweep: W 4096 x 4096 ~Laplace(0, 0.05), X 4096 x 8192 ~N(0, 1).  For each
     of 1:2, 2:4 and 4:8: the fused mask + compress pass, the mask alone, decompress and the
-    product, warm (back to back) and cold (inputs evicted before each launch), the dense
-    GEMM (hipBLASLt) on the decompressed weight, and the product's matrix-core roofline."""
+    product, warm (back to back on one buffer set) and cold (rotating buffer copies, so
+    every launch reads from HBM), the dense GEMM (hipBLASLt) on the decompressed weight, and
+    the product's matrix-core roofline."""
     w = synth.WORKLOADS["sweep_f16"]
     R, K, T = w.R, w.K, w.T
     W, X = w.W(), w.X()
@@ -400,20 +442,22 @@ def sweep_f16_block(torch, nm, synth, L, dev, stream, hipt, args, flush, cold_ti
         vshape, mshape = nm.compressed_shapes(R, K, n, m, args.layout)
         vals = torch.empty(vshape, dtype=f16, device=dev)
         meta = torch.empty(mshape, dtype=torch.int32, device=dev)
-        d = {"name": f"{n}:{m}"}
+        d = {"name": f"{n}:{m}", "R": R, "K": K, "T": T, "Wd": Wd, "mask": mask, "vals": vals,
+             "meta": meta, "dec": dec, "Xd": Xd, "Y": Y}
 
-        def launch(d, kind, n=n, m=m, vals=vals, meta=meta):
+        def launch(d, kind, n=n, m=m):
             if kind == "mask_compress":
-                rc = L.nm_mask_compress(Wd.data_ptr(), 1, R, K, n, m, LAY, mask.data_ptr(),
-                                        vals.data_ptr(), meta.data_ptr(), sp)
+                rc = L.nm_mask_compress(d["Wd"].data_ptr(), 1, R, K, n, m, LAY,
+                                        d["mask"].data_ptr(), d["vals"].data_ptr(),
+                                        d["meta"].data_ptr(), sp)
             elif kind == "mask":
-                rc = L.nm_mask(Wd.data_ptr(), 1, R, K, n, m, mask.data_ptr(), sp)
+                rc = L.nm_mask(d["Wd"].data_ptr(), 1, R, K, n, m, d["mask"].data_ptr(), sp)
             elif kind == "decompress":
-                rc = L.nm_decompress(vals.data_ptr(), meta.data_ptr(), 1, R, K, n, m, LAY,
-                                     dec.data_ptr(), sp)
+                rc = L.nm_decompress(d["vals"].data_ptr(), d["meta"].data_ptr(), 1, R, K, n, m,
+                                     LAY, d["dec"].data_ptr(), sp)
             else:
-                rc = L.nm_spmm(vals.data_ptr(), meta.data_ptr(), R, K, n, m, LAY, Xd.data_ptr(), T,
-                               1, Y.data_ptr(), 1, sp)
+                rc = L.nm_spmm(d["vals"].data_ptr(), d["meta"].data_ptr(), R, K, n, m, LAY,
+                               d["Xd"].data_ptr(), T, 1, d["Y"].data_ptr(), 1, sp)
             if rc != 0:
                 raise RuntimeError(f"sweep {kind} {n}:{m} failed: {nm.status_str(rc)}")
 
@@ -569,7 +613,8 @@ def main() -> int:
     if args.ceiling_only:
         w_vals, x_vals = bf16_sample(mats[0]["W"], dtype), bf16_sample(mats[0]["X"], dtype)
         print(json.dumps({"matrix_core_ceiling": matrix_core_ceiling(torch, dev, stream, hipt,
-                                                                     w_vals, x_vals)}), flush=True)
+                                                                     w_vals, x_vals),
+                          "valu_ceiling": valu_ceiling(torch, dev, stream, hipt)}), flush=True)
         return 0
 
     def launch(d, kind):
@@ -663,25 +708,37 @@ def main() -> int:
     for name, kind, e0, e1 in events:
         per.setdefault((name, kind), []).append(hipt.ms(e0, e1))
 
-    # ---- the same kernels cold: before each launch, outside its events, a 512 MiB read
-    # (twice the 256 MB Infinity Cache) evicts its inputs, so they come from HBM.  A read,
-    # not a fill: a fill would leave dirty lines whose write-back competes with the kernel.
-    flush = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
+    # ---- the same kernels cold.  Each (matrix, kernel) is launched on copies of the buffers
+    # it touches, in rotation, with enough copies that at least 512 MiB of other traffic
+    # (twice the 256 MB Infinity Cache) separates two launches on one copy, so every launch
+    # finds its inputs in HBM; `steps` rounds of the rotation run between two events.
+    touch = {"mask_compress": (["Wd"], ["mask", "vals", "meta"]), "mask": (["Wd"], ["mask"]),
+             "compress": (["Wd"], ["vals", "meta"]), "decompress": (["vals", "meta"], ["dec"]),
+             "spmm": (["vals", "meta", "Xd"], ["Y"])}
+    cold_bytes = 1 << 29
 
     def cold_times(mat_list, kind_list, launch_fn, reps):
-        ev = {}
-        for _ in range(reps):
-            for d in mat_list:
-                for kind in kind_list:
-                    flush.view(torch.int64).sum()
-                    e0 = hipt.event()
-                    e1 = hipt.event()
-                    hipt.record(e0)
-                    launch_fn(d, kind)
-                    hipt.record(e1)
-                    ev.setdefault((d["name"], kind), []).append((e0, e1))
-        torch.cuda.synchronize()
-        return {k: [hipt.ms(a, b) for a, b in v] for k, v in ev.items()}
+        res = {}
+        for d in mat_list:
+            for kind in kind_list:
+                ins, outs = touch[kind]
+                nbytes = sum(d[k].numel() * d[k].element_size() for k in ins + outs)
+                sets = -(-cold_bytes // nbytes) + 1
+                copies = [d] + [dict(d, **{k: d[k].clone() for k in ins},
+                                     **{k: torch.empty_like(d[k]) for k in outs})
+                                for _ in range(sets - 1)]
+                for c in copies:  # one untimed round: the first round starts cold as well
+                    launch_fn(c, kind)
+                e0, e1 = hipt.event(), hipt.event()
+                hipt.record(e0)
+                for _ in range(reps):
+                    for c in copies:
+                        launch_fn(c, kind)
+                hipt.record(e1)
+                torch.cuda.synchronize()
+                res[(d["name"], kind)] = [hipt.ms(e0, e1) / (reps * len(copies))]
+                del copies
+        return res
 
     per_cold = cold_times(mats, kinds, launch, args.steps)
 
@@ -763,6 +820,19 @@ def main() -> int:
 
     dense = None
     if not args.no_dense:
+        # the product timed as the dense GEMM is below: `steps` launches back to back on one
+        # matrix between two events, so the ratio compares like with like
+        spmm_b = 0.0
+        for d in mats:
+            launch(d, "spmm")
+            torch.cuda.synchronize()
+            e0, e1 = hipt.event(), hipt.event()
+            hipt.record(e0)
+            for _ in range(args.steps):
+                launch(d, "spmm")
+            hipt.record(e1)
+            torch.cuda.synchronize()
+            spmm_b += hipt.ms(e0, e1) / args.steps * 1e-3
         # hipBLASLt through torch.matmul on the decompressed weight, same dtype and shapes
         ts = []
         for d in mats:
@@ -795,7 +865,9 @@ def main() -> int:
         if ts:
             dense_t = sum(ts)
             dense = {"tflops": round(F_eff / dense_t / 1e12, 1), "us_total": round(dense_t * 1e6, 1),
-                     "spmm_speedup": round(dense_t / spmm_t, 3),
+                     "spmm_us_total": round(spmm_b * 1e6, 1),
+                     "spmm_speedup": round(dense_t / spmm_b, 3),
+                     "spmm_speedup_in_step": round(dense_t / spmm_t, 3),
                      "how": {"i8": "torch._int_mm", "fp8": "torch._scaled_mm (bf16 out)"}.get(
                          dtype, "torch.matmul (hipBLASLt)")
                             + " on the decompressed weight, same dtype"}
@@ -816,7 +888,7 @@ def main() -> int:
     # ---- the fp16 N:M sweep: 4096 x 4096 weights, 8192 activation columns ----
     sweep = None
     if args.workload == "llama_mlp" and not args.no_sweep:
-        sweep = sweep_f16_block(torch, nm, synth, L, dev, stream, hipt, args, flush, cold_times)
+        sweep = sweep_f16_block(torch, nm, synth, L, dev, stream, hipt, args, cold_times)
 
     srste = transposable = None
     if float_path:
@@ -947,11 +1019,14 @@ def main() -> int:
                          frac_alu=round(lane_ops / t / 1e12 / PEAK_VALU_LANE_TOPS, 3))
         permutation["kernels"][f"{d['name']}.perm_gains"] = entry
         del ws, gain, pick
+    vc = valu_ceiling(torch, dev, stream, hipt)
     permutation["roofline"] = {
         "bound": "alu", "unit": "T lane-op/s", "peak": PEAK_VALU_LANE_TOPS,
+        "measured_ceiling": {k: vc[k] for k in ("v_add_f32", "v_max_f32", "v_fma_f32")},
         "note": "achieved = SQ_INSTS_VALU of the launch (committed rocprofv3 profile of the same "
-                "kernel, shape and source) x 64 lanes / launch time; peak = 256 CUs x 64 lanes "
-                "x 2.4 GHz, the rate of unpacked VALU instructions (packed fp32 is disabled)"}
+                "kernel, shape and source) x 64 lanes / launch time; peak = the fp32 vector "
+                "peak in lane operations (157.3 TFLOP/s / 2 flops per FMA); measured_ceiling = "
+                "unpacked 32-bit VALU instructions alone in register loops (libnm_probe)"}
 
     cpu = None
     if not args.no_cpu:

@@ -470,3 +470,20 @@ def test_out_of_range_enum_values_are_rejected():
     assert nm.STATUS[L.nm_mask(FAKE, -1, 64, 128, 2, 4, FAKE + (1 << 30), None)] == "dtype"
     assert L.nm_values_bytes(64, 128, 2, 4, nm.NM_BF16, 7) == 0
     assert nm.status_str(-5) == "unknown status" and nm.status_str(1 << 30) == "unknown status"
+
+
+@pytest.mark.skipif(not os.path.exists(nm.PROBE_LIB_PATH), reason="libnm_probe.so not built")
+def test_probe_library_exports_every_declared_symbol():
+    """libnm_probe.so (the benchmark's rate probes) exports what include/nm_probe.h declares
+    and rejects bad arguments before any launch."""
+    text = open(os.path.join(os.path.dirname(HEADER), "nm_probe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(nm_[a-z_]+)\s*\(", text)))
+    assert names == ["nm_probe_matrix_core", "nm_probe_operand_bytes", "nm_probe_valu"]
+    P = nm.probe_lib()
+    for name in names:
+        assert hasattr(P, name), name
+    assert P.nm_probe_operand_bytes() == 4 * 64 * 24 * 2
+    assert P.nm_probe_matrix_core(2, FAKE, 256, 2, 10, FAKE, FAKE, None) == 1
+    assert P.nm_probe_valu(3, 256, 2, 10, FAKE, FAKE, None) == 1
+    assert P.nm_probe_valu(0, 256, 9, 10, FAKE, FAKE, None) == 1
