@@ -361,21 +361,27 @@ def matrix_core_ceiling(torch, dev, stream, hipt, w_vals, x_vals, waves_per_simd
         dops = torch.from_numpy(arr.view(np.int16)).to(dev)
         for inst, kind, flops in (("smfmac_32x32x32_bf16", 0, 65536), ("mfma_32x32x16_bf16", 1, 32768)):
             iters = 4000
-            for _ in range(2):  # warm-up (clock ramp)
+            for _ in range(3):  # warm-up (clock ramp)
                 P.nm_probe_matrix_core(kind, dops.data_ptr(), cus, waves_per_simd, iters,
                                        clocks.data_ptr(), sink.data_ptr(), stream.cuda_stream)
-            e0, e1 = hipt.event(), hipt.event()
-            hipt.record(e0)
-            rc = P.nm_probe_matrix_core(kind, dops.data_ptr(), cus, waves_per_simd, iters,
-                                        clocks.data_ptr(), sink.data_ptr(), stream.cuda_stream)
-            hipt.record(e1)
-            torch.cuda.synchronize()
-            if rc != 0:
-                raise RuntimeError(f"nm_probe_matrix_core failed ({rc})")
-            t = hipt.ms(e0, e1) * 1e-3
+            best = None
+            for _ in range(3):  # the best of three launches: what the instruction sustains
+                e0, e1 = hipt.event(), hipt.event()
+                hipt.record(e0)
+                rc = P.nm_probe_matrix_core(kind, dops.data_ptr(), cus, waves_per_simd, iters,
+                                            clocks.data_ptr(), sink.data_ptr(), stream.cuda_stream)
+                hipt.record(e1)
+                torch.cuda.synchronize()
+                if rc != 0:
+                    raise RuntimeError(f"nm_probe_matrix_core failed ({rc})")
+                t = hipt.ms(e0, e1) * 1e-3
+                c = clocks.view(-1, 4).cpu().numpy().astype(np.float64)
+                mhz = float(np.median((c[:, 1] - c[:, 0]) / np.maximum(c[:, 3] - c[:, 2], 1)
+                                      * 100.0))
+                if best is None or t < best[0]:
+                    best = (t, mhz)
+            t, mhz = best
             insts = cus * waves_per_simd * 4 * iters * 16
-            c = clocks.view(-1, 4).cpu().numpy().astype(np.float64)
-            mhz = float(np.median((c[:, 1] - c[:, 0]) / np.maximum(c[:, 3] - c[:, 2], 1) * 100.0))
             out[f"{inst}.{kname}"] = {"eff_tflops": round(insts * flops / t / 1e12, 1),
                                       "clock_mhz": round(mhz, 0), "ms": round(t * 1e3, 3)}
     return out
