@@ -6,7 +6,7 @@ matrix of the workload, nm_mask, nm_compress (mask + values + metadata),
 nm_decompress and nm_spmm (Y = W_sparse X).  Inputs are resident in HBM before
 the timed region.  Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload llama_mlp]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 100] [--workload llama_mlp]
 
 `value` is the whole step's effective throughput: dense-equivalent product
 flops (2 R K T per matrix) divided by the step time.  Per-kernel figures,
@@ -526,8 +526,10 @@ def sweep_f16_block(torch, nm, synth, L, dev, stream, hipt, args, cold_times):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # 100 untimed steps (~35 ms of GPU work on the LLaMA pair) bring the device to its steady
+    # clock; after 5, the timed steps still ran ~13% slower than after 100 or 300
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="llama_mlp", choices=sorted(WORKLOADS))
     ap.add_argument("--layout", default="blocked", choices=["blocked", "rows"],
                     help="storage layout of the compressed weight (include/nm.h)")
