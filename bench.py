@@ -53,7 +53,7 @@ PEAK_HBM_GBS = 8000.0
 # Vector-ALU peak in lane operations: the published fp32 vector rate, 157.3 TFLOP/s, is
 # 256 CUs x 128 FMA lanes per clock x 2 flops x 2.4 GHz, i.e. 78.6 T lane-op/s.  The VALU
 # probe (libnm_probe) shows plain, unpacked v_add_f32 and v_fma_f32 retiring 112-114 lanes
-# per clock per CU, so this rate needs no packed math (which this build never emits);
+# per clock per CU, so this rate needs no packed math (which the library is compiled without);
 # v_max_f32 retires at half that rate, so a kernel heavy in max/min stays below it.
 PEAK_VALU_LANE_TOPS = 78.64
 # dense matrix-core peaks (TFLOP/s; TOP/s for int8)

@@ -100,7 +100,7 @@ typedef enum NM_INT_ENUM {
   NM_ERR_DTYPE = 4,       /* unknown dtype, y_dt not allowed for dt, or int8 where a
                              floating-point weight is required                       */
   NM_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned                        */
-  NM_ERR_UNSUPPORTED = 6, /* valid arguments this build has no kernel for (int8 and fp8
+  NM_ERR_UNSUPPORTED = 6, /* valid arguments the library has no kernel for (int8 and fp8 
                              in the blocked layout need 16 n / m divisible by 4)     */
   NM_ERR_DEVICE = 7,      /* no usable gfx950 device, or the launch failed           */
   NM_ERR_LAYOUT = 8,      /* unknown layout, or NM_LAYOUT_BLOCKED with K % 64 != 0   */
