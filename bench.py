@@ -211,31 +211,40 @@ def cpu_info():
 
 
 def cpu_one_core(mats, n, m, rows: int = 64):
-    """The oracle on one thread: mask + compress + decompress + fp64 product of the first
-    `rows` rows of every matrix (all T columns), scaled to the whole workload."""
+    """The oracle on one thread: mask + compress, decompress and the fp64 product of the first
+    `rows` rows of every matrix (all T columns), each phase timed, scaled to the workload."""
     import oracle
 
     oracle.lib()
-    F = 0.0
-    F_all = 0.0
-    t0 = time.perf_counter()
+    F = F_all = B_mc = 0.0
+    t_mc = t_rest = t_mm = 0.0
     for w in mats:
         part = np.ascontiguousarray(w["W"][:rows])
         r = part.shape[0]
+        ta = time.perf_counter()
         oracle.mask(part, w["dtype"], n, m)
         vals, meta = oracle.compress(part, w["dtype"], n, m)
+        tb = time.perf_counter()
         oracle.decompress(vals, meta, w["dtype"], r, w["K"], n, m)
+        tc = time.perf_counter()
         Y = np.empty((r, w["T"]), dtype=np.float64)
         oracle.spmm_rows(vals, meta, r, w["K"], n, m, w["X"], w["dtype"], 0, r, Y)
+        td = time.perf_counter()
+        t_mc += tb - ta
+        t_rest += tc - tb
+        t_mm += td - tc
+        B_mc += algorithmic_bytes(r, w["K"], w["T"], n, m, w["s"], w["ys"])["mask_compress"]
         F += 2.0 * r * w["K"] * w["T"]
         F_all += 2.0 * w["R"] * w["K"] * w["T"]
-    dt = time.perf_counter() - t0
+    dt = t_mc + t_rest + t_mm
     rate = F / dt
     unit = "TOP/s" if mats[0]["dtype"] == "i8" else "TFLOP/s"
     return {"value": rate / 1e12, "unit": unit, "cores": 1, "seconds": round(dt, 2),
             "sample": f"rows 0..{rows} of each matrix, all T columns",
             "extrapolated_step_s": round(F_all / rate, 1),
-            "note": "one step of the whole workload on one core, extrapolated from the sample"}
+            "note": "one step of the whole workload on one core, extrapolated from the sample",
+            "phases": {"mask_compress_gbps": round(B_mc / t_mc / 1e9, 3),
+                       "product_" + unit.replace("/", "_per_"): round(F / t_mm / 1e12, 5)}}
 
 
 def srste_cpu_sample(mats, n, m, budget_s: float = 3.0):
@@ -268,16 +277,19 @@ def srste_cpu_sample(mats, n, m, budget_s: float = 3.0):
 
 
 def cpu_baseline(mats, n, m, threads: int, budget_s: float = 12.0):
-    """The oracle as it stands, on the host: mask + compress + decompress + product of a
-    bounded slice of rows of every matrix, rows spread over `threads` threads."""
+    """The oracle as it stands, on the host: mask + compress, decompress and the product of a
+    bounded slice of rows of every matrix, rows spread over `threads` threads.  Each phase
+    runs over all threads before the next starts, so their rates are reported apart as well
+    (mask + compress in GB/s of its algorithmic bytes, the product in TFLOP/s)."""
     import oracle
 
     oracle.lib()
     F = 0.0
+    B_mc = B_dec = 0.0
+    t_mc = t_dec = t_mm = 0.0
     rows_done = {}
     t0 = time.perf_counter()
     block = 4  # rows per thread per round
-    rounds = 0
     while True:
         for w in mats:
             r0 = rows_done.get(w["name"], 0)
@@ -286,24 +298,46 @@ def cpu_baseline(mats, n, m, threads: int, budget_s: float = 12.0):
                 continue
             Wsl = np.ascontiguousarray(w["W"][r0:r1])
             R = r1 - r0
+            parts = [None] * threads
 
-            def work(k, Wsl=Wsl, R=R, w=w):
-                a = k * R // threads
-                b = (k + 1) * R // threads
-                if b <= a:
-                    return
-                part = np.ascontiguousarray(Wsl[a:b])
-                oracle.mask(part, w["dtype"], n, m)
-                vals, meta = oracle.compress(part, w["dtype"], n, m)
-                oracle.decompress(vals, meta, w["dtype"], b - a, w["K"], n, m)
-                Y = np.empty((b - a, w["T"]), dtype=np.float64)
-                oracle.spmm_rows(vals, meta, b - a, w["K"], n, m, w["X"], w["dtype"], 0, b - a, Y)
+            def split(k, R=R):
+                return k * R // threads, (k + 1) * R // threads
 
+            def mask_compress(k, Wsl=Wsl, w=w):
+                a, b = split(k)
+                if b > a:
+                    part = np.ascontiguousarray(Wsl[a:b])
+                    oracle.mask(part, w["dtype"], n, m)
+                    parts[k] = oracle.compress(part, w["dtype"], n, m)
+
+            def decompress(k, w=w):
+                a, b = split(k)
+                if b > a:
+                    oracle.decompress(parts[k][0], parts[k][1], w["dtype"], b - a, w["K"], n, m)
+
+            def product(k, w=w):
+                a, b = split(k)
+                if b > a:
+                    Y = np.empty((b - a, w["T"]), dtype=np.float64)
+                    oracle.spmm_rows(parts[k][0], parts[k][1], b - a, w["K"], n, m, w["X"],
+                                     w["dtype"], 0, b - a, Y)
+
+            ab = algorithmic_bytes(R, w["K"], w["T"], n, m, w["s"], w["ys"])
             with ThreadPoolExecutor(max_workers=threads) as ex:
-                list(ex.map(work, range(threads)))
+                ta = time.perf_counter()
+                list(ex.map(mask_compress, range(threads)))
+                tb = time.perf_counter()
+                list(ex.map(decompress, range(threads)))
+                tc = time.perf_counter()
+                list(ex.map(product, range(threads)))
+                td = time.perf_counter()
+            t_mc += tb - ta
+            t_dec += tc - tb
+            t_mm += td - tc
+            B_mc += ab["mask_compress"]
+            B_dec += ab["decompress"]
             rows_done[w["name"]] = r1
             F += 2.0 * R * w["K"] * w["T"]
-        rounds += 1
         if time.perf_counter() - t0 >= budget_s or all(rows_done.get(w["name"], 0) >= w["R"]
                                                        for w in mats):
             break
@@ -313,7 +347,10 @@ def cpu_baseline(mats, n, m, threads: int, budget_s: float = 12.0):
     unit = "TOP/s" if mats[0]["dtype"] == "i8" else "TFLOP/s"
     return {"value": F / dt / 1e12, "unit": unit, "cores": threads, "kind": "oracle",
             "seconds": round(dt, 2),
-            "sample": f"mask+compress+decompress+product of {sample} (fp64 product, all T columns)"}
+            "sample": f"mask+compress+decompress+product of {sample} (fp64 product, all T columns)",
+            "phases": {"mask_compress_gbps": round(B_mc / t_mc / 1e9, 3),
+                       "decompress_gbps": round(B_dec / t_dec / 1e9, 3),
+                       "product_" + unit.replace("/", "_per_"): round(F / t_mm / 1e12, 5)}}
 
 
 def bf16_sample(a: np.ndarray, dtype: str, count: int = 1 << 20) -> np.ndarray:
@@ -385,6 +422,45 @@ def matrix_core_ceiling(torch, dev, stream, hipt, w_vals, x_vals, waves_per_simd
             out[f"{inst}.{kname}"] = {"eff_tflops": round(insts * flops / t / 1e12, 1),
                                       "clock_mhz": round(mhz, 0), "ms": round(t * 1e3, 3)}
     return out
+
+
+def hbm_copy(torch, dev, stream, hipt, nbytes: int = 1 << 30, reps: int = 10):
+    """What HBM sustains for a pass that reads and writes each byte once: a plain 16-byte
+    non-temporal copy kernel (libnm_probe) over 1 GiB, far past the 256 MB Infinity Cache."""
+    import masking_sparse_gemm_amd as nm
+
+    P = nm.probe_lib()
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    for _ in range(3):
+        if P.nm_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, stream.cuda_stream) != 0:
+            raise RuntimeError("nm_probe_copy failed")
+    e0, e1 = hipt.event(), hipt.event()
+    hipt.record(e0)
+    for _ in range(reps):
+        P.nm_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, stream.cuda_stream)
+    hipt.record(e1)
+    torch.cuda.synchronize()
+    t = hipt.ms(e0, e1) * 1e-3 / reps
+    # the runtime's own device-to-device copy of the same buffers, for comparison
+    for _ in range(3):
+        dst.copy_(src)
+    e2, e3 = hipt.event(), hipt.event()
+    hipt.record(e2)
+    for _ in range(reps):
+        dst.copy_(src)
+    hipt.record(e3)
+    torch.cuda.synchronize()
+    t_rt = hipt.ms(e2, e3) * 1e-3 / reps
+    del src, dst
+    gbps, gbps_rt = 2.0 * nbytes / t / 1e9, 2.0 * nbytes / t_rt / 1e9
+    return {"gbps": round(max(gbps, gbps_rt), 1),
+            "frac_hbm": round(max(gbps, gbps_rt) / PEAK_HBM_GBS, 3),
+            "probe_gbps": round(gbps, 1), "runtime_copy_gbps": round(gbps_rt, 1),
+            "how": "1 GiB device-to-device copies, read + write bytes: a 16-byte non-temporal "
+                   "copy kernel (libnm_probe) and the runtime's copy (torch copy_); gbps is "
+                   "the faster"}
 
 
 def valu_ceiling(torch, dev, stream, hipt):
@@ -622,7 +698,8 @@ def main() -> int:
         w_vals, x_vals = bf16_sample(mats[0]["W"], dtype), bf16_sample(mats[0]["X"], dtype)
         print(json.dumps({"matrix_core_ceiling": matrix_core_ceiling(torch, dev, stream, hipt,
                                                                      w_vals, x_vals),
-                          "valu_ceiling": valu_ceiling(torch, dev, stream, hipt)}), flush=True)
+                          "valu_ceiling": valu_ceiling(torch, dev, stream, hipt),
+                          "hbm_copy": hbm_copy(torch, dev, stream, hipt)}), flush=True)
         return 0
 
     def launch(d, kind):
@@ -880,6 +957,10 @@ def main() -> int:
                          dtype, "torch.matmul (hipBLASLt)")
                             + " on the decompressed weight, same dtype"}
 
+    # ---- what HBM sustains for a plain copy on this device (libnm_probe) ----
+    copy_rate = hbm_copy(torch, dev, stream, hipt)
+    mask_compress["frac_of_copy"] = round(mask_compress["gbps"] / copy_rate["gbps"], 3)
+
     # ---- the matrix cores' own rate on this workload's values (libnm_probe) ----
     ceiling = None
     if dtype in ("bf16", "f16"):
@@ -1067,6 +1148,7 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
         "matrix_core_ceiling": ceiling,
+        "hbm_copy": copy_rate,
         "sweep_f16": sweep,
         "spmm_eff_tflops": round(F_eff / spmm_t / 1e12, 1),
         "mask_compress": mask_compress,

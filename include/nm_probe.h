@@ -53,6 +53,11 @@ int nm_probe_matrix_core(int kind, const void* operands, int cus, int waves_per_
 int nm_probe_valu(int op, int cus, int waves_per_simd, int iters, int64_t* clocks, float* sink,
                   void* stream);
 
+/* HBM streaming copy: dst[0, bytes) = src[0, bytes) with 16-byte non-temporal loads and
+ * stores per lane (bytes a multiple of 16, both pointers 16-byte aligned, the ranges not
+ * overlapping; else 1).  The rate a pass that reads and writes each byte once can reach. */
+int nm_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

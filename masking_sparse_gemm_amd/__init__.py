@@ -130,6 +130,8 @@ def probe_lib() -> ctypes.CDLL:
         P.nm_probe_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp,
                                     vp, vp]
         P.nm_probe_valu.restype = ctypes.c_int
+        P.nm_probe_copy.argtypes = [vp, vp, ctypes.c_int64, vp]
+        P.nm_probe_copy.restype = ctypes.c_int
         _probe = P
     return _probe
 

@@ -134,6 +134,17 @@ __global__ void __launch_bounds__(256) valu_probe_kernel(int iters, int64_t* __r
   sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// Plain streaming copy, 16 bytes per lane per iteration, non-temporal on both sides: the
+// HBM rate a pass that reads and writes once can reach.  Grid-stride over n16 pieces.
+typedef unsigned int u32x4v_t __attribute__((ext_vector_type(4)));
+
+__global__ void __launch_bounds__(256) copy_probe_kernel(const u32x4v_t* __restrict__ src,
+                                                         u32x4v_t* __restrict__ dst, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
 }  // namespace
 
 extern "C" {
@@ -161,6 +172,20 @@ int nm_probe_valu(int op, int cus, int waves_per_simd, int iters, int64_t* clock
   auto k = op == 0 ? valu_probe_kernel<0> : op == 1 ? valu_probe_kernel<1> : valu_probe_kernel<2>;
   hipLaunchKernelGGL(k, dim3(cus * waves_per_simd), dim3(256), 0,
                      static_cast<hipStream_t>(stream), iters, clocks, sink);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+int nm_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (src == nullptr || dst == nullptr || bytes <= 0 || bytes % 16 != 0 ||
+      (reinterpret_cast<uintptr_t>(src) & 15) != 0 || (reinterpret_cast<uintptr_t>(dst) & 15) != 0)
+    return 1;
+  const int64_t n16 = bytes / 16;
+  // about four pieces per lane, at most 65536 workgroups
+  int64_t blocks = (n16 + 256 * 4 - 1) / (256 * 4);
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(copy_probe_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const u32x4v_t*>(src),
+                     static_cast<u32x4v_t*>(dst), n16);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 

@@ -479,7 +479,8 @@ def test_probe_library_exports_every_declared_symbol():
     text = open(os.path.join(os.path.dirname(HEADER), "nm_probe.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = sorted(set(re.findall(r"\b(nm_[a-z_]+)\s*\(", text)))
-    assert names == ["nm_probe_matrix_core", "nm_probe_operand_bytes", "nm_probe_valu"]
+    assert names == ["nm_probe_copy", "nm_probe_matrix_core", "nm_probe_operand_bytes",
+                     "nm_probe_valu"]
     P = nm.probe_lib()
     for name in names:
         assert hasattr(P, name), name
@@ -487,3 +488,5 @@ def test_probe_library_exports_every_declared_symbol():
     assert P.nm_probe_matrix_core(2, FAKE, 256, 2, 10, FAKE, FAKE, None) == 1
     assert P.nm_probe_valu(3, 256, 2, 10, FAKE, FAKE, None) == 1
     assert P.nm_probe_valu(0, 256, 9, 10, FAKE, FAKE, None) == 1
+    assert P.nm_probe_copy(FAKE, FAKE + 4096, 24, None) == 1      # not a multiple of 16
+    assert P.nm_probe_copy(FAKE + 8, FAKE + 4096, 32, None) == 1  # misaligned

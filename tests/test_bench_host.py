@@ -83,8 +83,24 @@ def test_cpu_one_core_leg_on_a_tiny_workload():
     import synth
 
     w = synth.WORKLOADS["toy_f32"]
-    mats = [{"name": "toy", "R": w.R, "K": w.K, "T": w.T, "W": w.W(), "X": w.X(), "dtype": "f32"}]
+    mats = [{"name": "toy", "R": w.R, "K": w.K, "T": w.T, "W": w.W(), "X": w.X(), "dtype": "f32",
+             "s": 4, "ys": 4}]
     r = bench.cpu_one_core(mats, 2, 4, rows=8)
     assert r["cores"] == 1 and r["value"] > 0 and np.isfinite(r["value"])
+    assert r["phases"]["mask_compress_gbps"] > 0 and r["phases"]["product_TFLOP_per_s"] > 0
     # 8 of 64 rows timed: the whole-workload step is 8x the sample's time
     assert r["extrapolated_step_s"] == pytest.approx(8 * r["seconds"], abs=0.1)
+
+
+def test_cpu_baseline_all_cores_on_a_tiny_workload():
+    import synth
+
+    w = synth.WORKLOADS["toy_f32"]
+    mats = [{"name": "toy", "R": w.R, "K": w.K, "T": w.T, "W": w.W(), "X": w.X(), "dtype": "f32",
+             "s": 4, "ys": 4}]
+    r = bench.cpu_baseline(mats, 2, 4, threads=2, budget_s=0.0)
+    assert r["cores"] == 2 and r["kind"] == "oracle" and r["value"] > 0
+    assert "rows 0..8 of 64" in r["sample"]            # one round: 4 rows per thread
+    ph = r["phases"]
+    assert ph["mask_compress_gbps"] > 0 and ph["decompress_gbps"] > 0
+    assert ph["product_TFLOP_per_s"] > 0
