@@ -1014,7 +1014,8 @@ def main() -> int:
                 t = float(np.mean(sr_per[(d["name"], kind)]))
                 srste["kernels"][f"{d['name']}.{kind}"] = {
                     "us": round(t * 1e6, 2), "alg_bytes": ab[kind], "gbps": round(ab[kind] / t / 1e9, 1),
-                    "frac_hbm": round(ab[kind] / t / 1e9 / PEAK_HBM_GBS, 3)}
+                    "frac_hbm": round(ab[kind] / t / 1e9 / PEAK_HBM_GBS, 3),
+                    "frac_of_copy": round(ab[kind] / t / 1e9 / copy_rate["gbps"], 3)}
                 sr_tot[kind][0] += t
                 sr_tot[kind][1] += ab[kind]
         g_t, g_b = sr_tot["srste_grad"]
@@ -1065,7 +1066,8 @@ def main() -> int:
                 else:
                     ab = 2 * e * d["s"] if kind == "tprune" else e * d["s"] + kept * d["s"] + meta_t
                     entry.update(alg_bytes=ab, gbps=round(ab / t / 1e9, 1),
-                                 frac_hbm=round(ab / t / 1e9 / PEAK_HBM_GBS, 3))
+                                 frac_hbm=round(ab / t / 1e9 / PEAK_HBM_GBS, 3),
+                                 frac_of_copy=round(ab / t / 1e9 / copy_rate["gbps"], 3))
                 transposable["kernels"][f"{d['name']}.{kind}"] = entry
 
     # ---- channel permutation: one round of swap-gain evaluation per matrix ----
