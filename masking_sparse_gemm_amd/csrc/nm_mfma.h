@@ -58,6 +58,28 @@ __device__ __forceinline__ void global_to_lds(const void* src, uint8_t* lds_wave
 #endif
 }
 
+// The same load with the address split into a wave-uniform 64-bit base (scalar
+// registers) and a 32-bit per-lane offset: the saddr form of the instruction, which needs
+// no per-lane 64-bit address arithmetic.  lds is the wave's LDS destination (written to M0;
+// one wait state must separate that write from the load).  Operands are read when the
+// instruction issues, and the load writes only LDS.
+template <int kSize>
+__device__ __forceinline__ void global_to_lds_sv(const void* sbase, uint32_t voff, uint32_t lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  static_assert(kSize == 4 || kSize == 16, "dword or dwordx4");
+  if constexpr (kSize == 16)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds)
+                 : "memory", "m0");
+#endif
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)(p);
 }

@@ -469,28 +469,43 @@ struct AFrags {
   uint32_t ix[4];
 };
 
-// One block: read the next B fragment (rows kb, kb + 4 at b0, b1 and kb + 16, kb + 20 at
-// + kFar); with kReadA also four A fragments (kAStride apart) and their index words
-// (kMStride apart); then the four smfmac of this block on accumulators c[0..3] (AGPRs).
-#define NM_SMFMAC32_OPS(OP)                                                                \
-  OP " %[c0], %[a0], %[b], %[i0]\n\t" OP " %[c1], %[a1], %[b], %[i1]\n\t" OP               \
-     " %[c2], %[a2], %[b], %[i2]\n\t" OP " %[c3], %[a3], %[b], %[i3]\n\t"                  \
-     "s_waitcnt lgkmcnt(0)"
-#define NM_SMFMAC32_BREADS                                                                 \
+// One block: the four smfmac of this block on accumulators c[0..3] (AGPRs), with the LDS
+// reads of the next B fragment (rows kb, kb + 4 at b0, b1 and kb + 16, kb + 20 at + kFar)
+// and, in the A form, of four A fragments (kAStride apart) and their index words (kMStride
+// apart) issued between them.  The first smfmac goes ahead of every read: a wave issues in
+// order, so reads placed first would hold its matrix core idle until the LDS queue had
+// taken them all; issued behind a running smfmac they cost the matrix core nothing.
+#define NM_SMF32(OP, C, A, I) OP " %[" C "], %[" A "], %[b], %[" I "]\n\t"
+#define NM_SMFMAC32_BLOCK(OP)                                                              \
   "s_nop 2\n\t"                                                                            \
+  NM_SMF32(OP, "c0", "a0", "i0")                                                           \
+  "ds_read_b64_tr_b16 %[n0], %[b0]\n\t"                                                    \
+  "ds_read_b64_tr_b16 %[n1], %[b1]\n\t"                                                    \
+  NM_SMF32(OP, "c1", "a1", "i1")                                                           \
+  "ds_read_b64_tr_b16 %[n2], %[b0] offset:%[far]\n\t"                                      \
+  "ds_read_b64_tr_b16 %[n3], %[b1] offset:%[far]\n\t"                                      \
+  NM_SMF32(OP, "c2", "a2", "i2")                                                           \
+  NM_SMF32(OP, "c3", "a3", "i3")                                                           \
+  "s_waitcnt lgkmcnt(0)"
+#define NM_SMFMAC32_BLOCK_A(OP, MREAD)                                                     \
+  "s_nop 2\n\t"                                                                            \
+  NM_SMF32(OP, "c0", "a0", "i0")                                                           \
   "ds_read_b64_tr_b16 %[n0], %[b0]\n\t"                                                    \
   "ds_read_b64_tr_b16 %[n1], %[b1]\n\t"                                                    \
   "ds_read_b64_tr_b16 %[n2], %[b0] offset:%[far]\n\t"                                      \
-  "ds_read_b64_tr_b16 %[n3], %[b1] offset:%[far]\n\t"
-#define NM_SMFMAC32_AREADS(MREAD)                                                          \
+  "ds_read_b64_tr_b16 %[n3], %[b1] offset:%[far]\n\t"                                      \
+  NM_SMF32(OP, "c1", "a1", "i1")                                                           \
   "ds_read_b128 %[na0], %[aa]\n\t"                                                         \
   "ds_read_b128 %[na1], %[aa] offset:%[as1]\n\t"                                           \
   "ds_read_b128 %[na2], %[aa] offset:%[as2]\n\t"                                           \
   "ds_read_b128 %[na3], %[aa] offset:%[as3]\n\t"                                           \
+  NM_SMF32(OP, "c2", "a2", "i2")                                                           \
   MREAD " %[ni0], %[ma]\n\t"                                                               \
   MREAD " %[ni1], %[ma] offset:%[ms1]\n\t"                                                 \
   MREAD " %[ni2], %[ma] offset:%[ms2]\n\t"                                                 \
-  MREAD " %[ni3], %[ma] offset:%[ms3]\n\t"
+  MREAD " %[ni3], %[ma] offset:%[ms3]\n\t"                                                 \
+  NM_SMF32(OP, "c3", "a3", "i3")                                                           \
+  "s_waitcnt lgkmcnt(0)"
 #define NM_SMFMAC32_BOUTS                                                                  \
   [n0] "=&v"(n[0]), [n1] "=&v"(n[1]), [n2] "=&v"(n[2]), [n3] "=&v"(n[3])
 #define NM_SMFMAC32_COUTS                                                                  \
@@ -506,12 +521,12 @@ __device__ __forceinline__ void smfmac32_block(float16v_t& c0, float16v_t& c1, f
                                                const short16_t& b, const short16_t& keep,
                                                uint32_t b0, uint32_t b1, short4_t (&n)[4]) {
   if constexpr (BF16)
-    asm volatile(NM_SMFMAC32_BREADS NM_SMFMAC32_OPS("v_smfmac_f32_32x32x32_bf16")
+    asm volatile(NM_SMFMAC32_BLOCK("v_smfmac_f32_32x32x32_bf16")
                  : NM_SMFMAC32_BOUTS, NM_SMFMAC32_COUTS
                  : NM_SMFMAC32_INS
                  : "memory");
   else
-    asm volatile(NM_SMFMAC32_BREADS NM_SMFMAC32_OPS("v_smfmac_f32_32x32x32_f16")
+    asm volatile(NM_SMFMAC32_BLOCK("v_smfmac_f32_32x32x32_f16")
                  : NM_SMFMAC32_BOUTS, NM_SMFMAC32_COUTS
                  : NM_SMFMAC32_INS
                  : "memory");
@@ -524,7 +539,7 @@ __device__ __forceinline__ void smfmac32_block_a(float16v_t& c0, float16v_t& c1,
                                                  uint32_t b0, uint32_t b1, short4_t (&n)[4],
                                                  uint32_t aa, uint32_t ma, AFrags& na) {
 #define NM_SMFMAC32_A(OP, MREAD)                                                           \
-  asm volatile(NM_SMFMAC32_BREADS NM_SMFMAC32_AREADS(MREAD) NM_SMFMAC32_OPS(OP)            \
+  asm volatile(NM_SMFMAC32_BLOCK_A(OP, MREAD)                                           \
                : NM_SMFMAC32_BOUTS, [na0] "=&v"(na.v[0]), [na1] "=&v"(na.v[1]),            \
                  [na2] "=&v"(na.v[2]), [na3] "=&v"(na.v[3]), [ni0] "=&v"(na.ix[0]),        \
                  [ni1] "=&v"(na.ix[1]), [ni2] "=&v"(na.ix[2]), [ni3] "=&v"(na.ix[3]),      \
@@ -546,9 +561,62 @@ __device__ __forceinline__ void smfmac32_block_a(float16v_t& c0, float16v_t& c1,
   }
 #undef NM_SMFMAC32_A
 }
-#undef NM_SMFMAC32_OPS
-#undef NM_SMFMAC32_BREADS
-#undef NM_SMFMAC32_AREADS
+// The same four smfmac with an even share of the next reads: the next B fragment and half
+// of the next A fragments with their index words (two fragments, kAStride apart, into
+// na0 / na1; index words kMStride apart into ni0 / ni1), 4.25 KB per wave, so that every
+// block of a step reads the same amount from LDS (a SIMD's LDS port moves about 64 bytes
+// a clock, and the four smfmac of a block take 128 clocks).  All reads follow the first
+// smfmac.  An A half is written one block after the last smfmac that read it was issued:
+// each smfmac of a SIMD starts only when the one before it has finished, so the reads,
+// which issue behind this block's first smfmac, land after the previous block's smfmac
+// have read their operands.
+#define NM_SMFMAC32_BLOCK_H(OP, MREAD)                                                     \
+  "s_nop 2\n\t"                                                                            \
+  NM_SMF32(OP, "c0", "a0", "i0")                                                           \
+  "ds_read_b64_tr_b16 %[n0], %[b0]\n\t"                                                    \
+  "ds_read_b64_tr_b16 %[n1], %[b1]\n\t"                                                    \
+  "ds_read_b64_tr_b16 %[n2], %[b0] offset:%[far]\n\t"                                      \
+  "ds_read_b64_tr_b16 %[n3], %[b1] offset:%[far]\n\t"                                      \
+  "ds_read_b128 %[na0], %[aa]\n\t"                                                         \
+  "ds_read_b128 %[na1], %[aa] offset:%[as1]\n\t"                                           \
+  MREAD " %[ni0], %[ma]\n\t"                                                               \
+  MREAD " %[ni1], %[ma] offset:%[ms1]\n\t"                                                 \
+  NM_SMF32(OP, "c1", "a1", "i1")                                                           \
+  NM_SMF32(OP, "c2", "a2", "i2")                                                           \
+  NM_SMF32(OP, "c3", "a3", "i3")                                                           \
+  "s_waitcnt lgkmcnt(0)"
+
+template <bool BF16, bool kPat12, int kFar, int kAStride, int kMStride>
+__device__ __forceinline__ void smfmac32_block_h(float16v_t& c0, float16v_t& c1, float16v_t& c2,
+                                                 float16v_t& c3, const AFrags& a,
+                                                 const short16_t& b, const short16_t& keep,
+                                                 uint32_t b0, uint32_t b1, short4_t (&n)[4],
+                                                 uint32_t aa, uint32_t ma, u32x4_t& na0,
+                                                 u32x4_t& na1, uint32_t& ni0, uint32_t& ni1) {
+#define NM_SMFMAC32_H(OP, MREAD)                                                           \
+  asm volatile(NM_SMFMAC32_BLOCK_H(OP, MREAD)                                              \
+               : NM_SMFMAC32_BOUTS, [na0] "=&v"(na0), [na1] "=&v"(na1), [ni0] "=&v"(ni0),  \
+                 [ni1] "=&v"(ni1), NM_SMFMAC32_COUTS                                       \
+               : NM_SMFMAC32_INS, [aa] "v"(aa), [ma] "v"(ma), [as1] "n"(kAStride),         \
+                 [ms1] "n"(kMStride)                                                       \
+               : "memory")
+  if constexpr (BF16) {
+    if constexpr (kPat12)
+      NM_SMFMAC32_H("v_smfmac_f32_32x32x32_bf16", "ds_read_u8");
+    else
+      NM_SMFMAC32_H("v_smfmac_f32_32x32x32_bf16", "ds_read_u16");
+  } else {
+    if constexpr (kPat12)
+      NM_SMFMAC32_H("v_smfmac_f32_32x32x32_f16", "ds_read_u8");
+    else
+      NM_SMFMAC32_H("v_smfmac_f32_32x32x32_f16", "ds_read_u16");
+  }
+#undef NM_SMFMAC32_H
+}
+#undef NM_SMF32
+#undef NM_SMFMAC32_BLOCK_H
+#undef NM_SMFMAC32_BLOCK
+#undef NM_SMFMAC32_BLOCK_A
 #undef NM_SMFMAC32_BOUTS
 #undef NM_SMFMAC32_COUTS
 #undef NM_SMFMAC32_INS
@@ -825,41 +893,83 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
   constexpr int kXLoads = TL::kXBytes / (64 * XB) / TL::kProducers;
   if (wave >= TL::kConsumers) {
     // ---------------- producer ----------------
+    // Every direct load reads at a wave-uniform base (scalar registers, advanced by one
+    // step's bytes per step) plus a 32-bit per-lane offset that stays fixed for the whole
+    // loop, so the loop issues its loads with no vector address arithmetic.  The per-lane
+    // offsets stay below 2^32 because R, K and T are below 2^28 (the launcher's guard).
+    static_assert(BN == 128 && TL::kProducers % 4 == 0, "X load windows of four K rows");
     const int pw = wave - TL::kConsumers;
     const uint8_t* xg = reinterpret_cast<const uint8_t*>(X);
     const uint8_t* vg = reinterpret_cast<const uint8_t*>(values);
     const uint8_t* mg = reinterpret_cast<const uint8_t*>(meta);
-    int64_t x_src[kXLoads];
-    uint32_t x_dst[kXLoads];
+    const uint8_t* x_base[kXLoads];
+    uint32_t x_off, x_dst[kXLoads];
+    if constexpr (XB == 16) {
+      // load j fills the 1 KB window w1k = j * kProducers + pw of the X tile: K rows
+      // 4 w1k .. 4 w1k + 3, lane l taking row 4 w1k + l / 16 and physical chunk l % 16;
+      // the row swizzle depends on r & 3 = (l / 16) & 3 only, so the lane offset is the
+      // same for every j
+      const int r = lane >> 4, pc = lane & 15;
+      const int lc = 2 * ((pc >> 1) ^ xpair_swizzle(r)) + (pc & 1);
+      int col = t0 + 8 * lc;
+      col = col < T ? col : 0;  // columns past T: any valid address (outputs past T only)
+      x_off = (uint32_t)(((int64_t)r * T + col) * 2);
 #pragma unroll
-    for (int j = 0; j < kXLoads; ++j) {
-      if constexpr (XB == 16) {
-        const int w1k = j * TL::kProducers + pw;  // 1 KB window of the X tile
-        const int slot = w1k * 64 + lane;
-        const int r = slot / TL::kXChunks, pc = slot % TL::kXChunks;
-        const int lc = 2 * ((pc >> 1) ^ xpair_swizzle(r)) + (pc & 1);
-        int col = t0 + 8 * lc;
-        col = col < T ? col : 0;  // columns past T: any valid address (outputs past T only)
-        x_src[j] = ((int64_t)r * T + col) * 2;
+      for (int j = 0; j < kXLoads; ++j) {
+        const int w1k = j * TL::kProducers + pw;
+        x_base[j] = xg + (int64_t)(4 * w1k) * T * 2;
         x_dst[j] = (uint32_t)(w1k * 1024);
-      } else {
-        // load j fills K row r = j * kProducers + pw: lane l lands at byte 4 l of the row,
-        // physical pair l / 8, which holds logical pair (l / 8) ^ xpair_swizzle(r)
+      }
+    } else {
+      // load j fills K row r = j * kProducers + pw: lane l lands at byte 4 l of the row,
+      // physical pair l / 8, which holds logical pair (l / 8) ^ xpair_swizzle(r); r & 3 is
+      // pw & 3 for every j
+      const int lp = (lane >> 3) ^ xpair_swizzle(pw);
+      int col = t0 + 16 * lp + 2 * (lane & 7);
+      col = col < T ? col : 0;  // T even: col even, so every piece is 4-byte aligned
+      x_off = (uint32_t)(col * 2);
+#pragma unroll
+      for (int j = 0; j < kXLoads; ++j) {
         const int r = j * TL::kProducers + pw;
-        const int lp = (lane >> 3) ^ xpair_swizzle(r);
-        int col = t0 + 16 * lp + 2 * (lane & 7);
-        col = col < T ? col : 0;  // T even: col even, so every piece is 4-byte aligned
-        x_src[j] = ((int64_t)r * T + col) * 2;
+        x_base[j] = xg + (int64_t)r * T * 2;
         x_dst[j] = (uint32_t)(r * BN * 2);
       }
     }
-    int64_t a_src[TL::kALoads];
-    uint32_t a_dst[TL::kALoads];
+    // compressed values: load j fills the 16 tile rows of block b16 = j * kProducers + pw
+    // (the blocked layout's 1 KB block of those rows and the step; the row layout's
+    // 64-byte pieces of each row); lane l takes row l / 4 of them and the chunk that lands
+    // at physical chunk l % 4, logical chunk (l % 4) ^ ((l / 16) & 3)
+    const uint8_t* a_base[TL::kALoads];
+    uint32_t a_off, a_dst[TL::kALoads];
+    {
+      const int lc = (lane & 3) ^ ((lane >> 4) & 3);
+      const int last = ((R + 15) >> 4) - 1;
+      a_off = (uint32_t)((kBlocked ? (lane >> 2) * 64 : 0) + 16 * lc);
+#pragma unroll
+      for (int j = 0; j < TL::kALoads; ++j) {
+        const int b16 = j * TL::kProducers + pw;
+        if constexpr (kBlocked) {
+          int g = (m0 >> 4) + b16;
+          g = g < last ? g : last;  // rows past the matrix: any valid block
+          a_base[j] = vg + (int64_t)g * nsteps * 1024;
+        } else {
+          a_base[j] = vg;  // row layout: the row is per lane (a_row below)
+        }
+        a_dst[j] = (uint32_t)(TL::kXBytes + b16 * 1024);
+      }
+    }
+    // row layout: each lane's row, clamped to the matrix (its offset from W's start does
+    // not fit the 32-bit lane offset, so it is kept as a 64-bit per-lane address)
+    int64_t a_row[TL::kALoads];
 #pragma unroll
     for (int j = 0; j < TL::kALoads; ++j) {
-      const int b16 = j * TL::kProducers + pw;
-      a_src[j] = values_source<kBlocked>(m0, 16 * b16, lane, R, K, nsteps);
-      a_dst[j] = (uint32_t)(TL::kXBytes + b16 * 1024);
+      if constexpr (!kBlocked) {
+        int row = m0 + 16 * (j * TL::kProducers + pw) + (lane >> 2);
+        row = row < R ? row : R - 1;
+        a_row[j] = (int64_t)row * K;
+      } else {
+        a_row[j] = 0;
+      }
     }
     int64_t m_src[TL::kMLoads];
     uint32_t m_dst[TL::kMLoads];
@@ -874,27 +984,36 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
     // its lanes, instead of two 4-byte-per-lane loads; the bytes land where those would.
     constexpr bool kWideMeta = kBlocked && !kPat12;
     static_assert(!kWideMeta || TL::kMBytes == 512 * TL::kProducers, "four blocks per producer");
-    int64_t m16_src = 0;
-    uint32_t m16_dst = 0;
+    const uint8_t* m16_base = mg;
+    uint32_t m16_off = 0, m16_dst = 0;
     if constexpr (kWideMeta) {
       const int last = ((R + 15) >> 4) - 1;
+      int g0 = (m0 >> 4) + 4 * pw;
+      g0 = g0 < last ? g0 : last;
       int g = (m0 >> 4) + 4 * pw + ((lane & 31) >> 3);
       g = g < last ? g : last;
-      m16_src = (int64_t)g * nsteps * 128 + 16 * (lane & 7);
+      m16_base = mg + (int64_t)g0 * nsteps * 128;
+      m16_off = (uint32_t)((g - g0) * nsteps * 128 + 16 * (lane & 7));
       m16_dst = (uint32_t)(TL::kXBytes + TL::kABytes + pw * 512);
     }
     auto issue_step = [&](int step) {
       step = step < last_step ? step : last_step;  // past the end: re-read the last step
       uint8_t* st = smem + (step % kStages) * TL::kStageBytes;
+      const uint32_t sta = lds_addr(st);
       const int64_t kx = (int64_t)step * kKStep * T * 2;
       const int64_t ka = (int64_t)step * values_step_bytes<kBlocked>();
       const int64_t km = (int64_t)step * meta_step_bytes<kBlocked, kPat12>();
 #pragma unroll
-      for (int j = 0; j < kXLoads; ++j) global_to_lds<XB>(xg + x_src[j] + kx, st + x_dst[j]);
+      for (int j = 0; j < kXLoads; ++j) global_to_lds_sv<XB>(x_base[j] + kx, x_off, sta + x_dst[j]);
 #pragma unroll
-      for (int j = 0; j < TL::kALoads; ++j) global_to_lds<16>(vg + a_src[j] + ka, st + a_dst[j]);
+      for (int j = 0; j < TL::kALoads; ++j) {
+        if constexpr (kBlocked)
+          global_to_lds_sv<16>(a_base[j] + ka, a_off, sta + a_dst[j]);
+        else
+          global_to_lds<16>(vg + a_row[j] + ka + a_off, st + a_dst[j]);
+      }
       if constexpr (kWideMeta) {
-        if (lane < 32) global_to_lds<16>(mg + m16_src + km, st + m16_dst);
+        if (lane < 32) global_to_lds_sv<16>(m16_base + km, m16_off, sta + m16_dst);
       } else {
 #pragma unroll
         for (int j = 0; j < TL::kMLoads; ++j) global_to_lds<4>(mg + m_src[j] + km, st + m_dst[j]);
@@ -962,24 +1081,31 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
   }
   for (int s = 0; s < nsteps; ++s) {
     const uint32_t st = stage_of(s), sn = stage_of(s + 1);
-    smfmac32_block<BF16, kFar>(acc[0][0], acc[1][0], acc[2][0], acc[3][0], a0, b, bk,
-                               st + b_rd[1][0], st + b_rd[1][1], n);
+    // blocks 0 and 1 (substep 0, on a0) read substep 1's A into a1, half each; blocks 2
+    // and 3 (substep 1, on a1) read the next step's substep-0 A into a0
+    smfmac32_block_h<BF16, kPat12, kFar, kAS, kMS>(
+        acc[0][0], acc[1][0], acc[2][0], acc[3][0], a0, b, bk, st + b_rd[1][0],
+        st + b_rd[1][1], n, st + a_rd1, st + m_rd1, a1.v[0], a1.v[1], a1.ix[0], a1.ix[1]);
     bk = b;
     b = join_b(n);
-    smfmac32_block_a<BF16, kPat12, kFar, kAS, kMS>(
+    smfmac32_block_h<BF16, kPat12, kFar, kAS, kMS>(
         acc[0][1], acc[1][1], acc[2][1], acc[3][1], a0, b, bk, st + b_rd[0][0] + kSub,
-        st + b_rd[0][1] + kSub, n, st + a_rd1, st + m_rd1, a1);
+        st + b_rd[0][1] + kSub, n, st + a_rd1 + 2 * kAS, st + m_rd1 + 2 * kMS, a1.v[2],
+        a1.v[3], a1.ix[2], a1.ix[3]);
     bk = b;
     b = join_b(n);
     widen_frags<kPat12>(a1);
-    smfmac32_block<BF16, kFar>(acc[0][0], acc[1][0], acc[2][0], acc[3][0], a1, b, bk,
-                               st + b_rd[1][0] + kSub, st + b_rd[1][1] + kSub, n);
+    smfmac32_block_h<BF16, kPat12, kFar, kAS, kMS>(
+        acc[0][0], acc[1][0], acc[2][0], acc[3][0], a1, b, bk, st + b_rd[1][0] + kSub,
+        st + b_rd[1][1] + kSub, n, sn + a_rd0, sn + m_rd0, a0.v[0], a0.v[1], a0.ix[0],
+        a0.ix[1]);
     bk = b;
     b = join_b(n);
     // the last step reads a stage that holds no useful data; the values are never used
-    smfmac32_block_a<BF16, kPat12, kFar, kAS, kMS>(
+    smfmac32_block_h<BF16, kPat12, kFar, kAS, kMS>(
         acc[0][1], acc[1][1], acc[2][1], acc[3][1], a1, b, bk, sn + b_rd[0][0],
-        sn + b_rd[0][1], n, sn + a_rd0, sn + m_rd0, a0);
+        sn + b_rd[0][1], n, sn + a_rd0 + 2 * kAS, sn + m_rd0 + 2 * kMS, a0.v[2], a0.v[3],
+        a0.ix[2], a0.ix[3]);
     bk = b;
     b = join_b(n);
     widen_frags<kPat12>(a0);
@@ -2120,9 +2246,10 @@ hipError_t launch_spmm(const void* values, const uint32_t* meta, int64_t R, int6
   const bool pat24 = (n == 2 && m == 4), pat12 = (n == 1 && m == 2);
   const bool half = dt == kBF16 || dt == kF16;
   // the structured-sparse and 4:8 kernels: K in whole 64-wide steps, even T (X in 16-byte
-  // pieces when T % 8 == 0, else 4-byte ones), 32-bit tile coordinates
+  // pieces when T % 8 == 0, else 4-byte ones), 32-bit tile coordinates, and K and T below
+  // 2^28 (the wave-specialised kernels' per-lane load offsets are 32-bit)
   const bool sparse_shape = K > 0 && K % kKStep == 0 && T % 2 == 0 && R < (1 << 30) &&
-                            T < (1 << 30) && K < (1 << 30);
+                            T < (1 << 28) && K < (1 << 28);
   if (half && n == 4 && m == 8 && sparse_shape) {
 #define NM_48(BF, YT)                                                                   \
   if (T % 8 != 0)                                                                       \
