@@ -827,6 +827,153 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
                          t0 + wn * TL::kWN, R, T, lane);
 }
 
+// The 2:4 consumer's whole K loop as one asm statement, so that LDS reads can stay in
+// flight across blocks (the compiler would take an asm statement's outputs as written when
+// the statement ends).  Fragments live in fixed registers: A of substep 0 (a0) in
+// v64..v83, of substep 1 (a1) in v84..v103, the four B fragments of a step in v104..v127
+// and v40..v47, addresses in v48..v59.  Per step, block j issues its reads right behind
+// its first smfmac, one block ahead of their use:
+//   block 0 (a0 x B0): a1 fragments 0-1 and B2;   block 1 (a0 x B1): B3, a1 fragments 2-3;
+//   block 2 (a1 x B2): next B0, next a0 0-1;       block 3 (a1 x B3): next B1, next a0 2-3.
+// Each set is 8 LDS instructions, issued two behind each smfmac of the block so that the
+// matrix core never waits on a run of LDS issue.  LDS reads complete in order, so
+// "lgkmcnt(8)" before a block's first smfmac (blocks 0, 2) completes the set issued two
+// blocks earlier, and "lgkmcnt(4)" before its third smfmac (four of its own reads issued)
+// the set issued one block earlier.  A register is rewritten only by reads issued behind a
+// later smfmac than every smfmac that reads it.  Reads of the next step's stage may be in flight at the step's barrier; the
+// released stage (this step's) has no read in flight by then.  Everything has landed when
+// the statement ends.
+#define NM_WS24_LOOP(OP) \
+  "s_waitcnt lgkmcnt(0)\n\t" \
+  "s_mov_b32 %[sn], %[base]\n\t" \
+  "v_add_u32 v54, %[sn], %[b00]\n\t" \
+  "v_add_u32 v55, %[sn], %[b01]\n\t" \
+  "v_add_u32 v56, %[sn], %[ar0]\n\t" \
+  "v_add_u32 v57, %[sn], %[mr0]\n\t" \
+  "v_add_u32 v58, %[sn], %[b10]\n\t" \
+  "v_add_u32 v59, %[sn], %[b11]\n\t" \
+  "ds_read_b64_tr_b16 v[104:105], v54\n\t" \
+  "ds_read_b64_tr_b16 v[106:107], v55\n\t" \
+  "ds_read_b64_tr_b16 v[108:109], v54 offset:%[far]\n\t" \
+  "ds_read_b64_tr_b16 v[110:111], v55 offset:%[far]\n\t" \
+  "ds_read_b128 v[64:67], v56\n\t" \
+  "ds_read_b128 v[68:71], v56 offset:%[as1]\n\t" \
+  "ds_read_u16 v80, v57\n\t" \
+  "ds_read_u16 v81, v57 offset:%[ms1]\n\t" \
+  "ds_read_b64_tr_b16 v[112:113], v58\n\t" \
+  "ds_read_b64_tr_b16 v[114:115], v59\n\t" \
+  "ds_read_b64_tr_b16 v[116:117], v58 offset:%[far]\n\t" \
+  "ds_read_b64_tr_b16 v[118:119], v59 offset:%[far]\n\t" \
+  "ds_read_b128 v[72:75], v56 offset:%[as2]\n\t" \
+  "ds_read_b128 v[76:79], v56 offset:%[as3]\n\t" \
+  "ds_read_u16 v82, v57 offset:%[ms2]\n\t" \
+  "ds_read_u16 v83, v57 offset:%[ms3]\n\t" \
+  "s_mov_b32 %[st], %[base]\n\t" \
+  "s_add_u32 %[sn], %[base], %[stride]\n\t" \
+  "s_mov_b32 %[cnt], %[ns]\n\t" \
+  "L_ws24_%=:\n\t" \
+  "v_add_u32 v48, %[st], %[ar1]\n\t" \
+  "v_add_u32 v49, %[st], %[mr1]\n\t" \
+  "v_add_u32 v50, %[st], %[b00]\n\t" \
+  "v_add_u32 v51, %[st], %[b01]\n\t" \
+  "s_waitcnt lgkmcnt(8)\n\t" \
+  OP " %[c00], v[64:67], v[104:111], v80\n\t" \
+  "ds_read_b128 v[84:87], v48\n\t" \
+  "ds_read_b128 v[88:91], v48 offset:%[as1]\n\t" \
+  OP " %[c10], v[68:71], v[104:111], v81\n\t" \
+  "ds_read_u16 v100, v49\n\t" \
+  "ds_read_u16 v101, v49 offset:%[ms1]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  OP " %[c20], v[72:75], v[104:111], v82\n\t" \
+  "ds_read_b64_tr_b16 v[120:121], v50 offset:%[sub]\n\t" \
+  "ds_read_b64_tr_b16 v[122:123], v51 offset:%[sub]\n\t" \
+  OP " %[c30], v[76:79], v[104:111], v83\n\t" \
+  "ds_read_b64_tr_b16 v[124:125], v50 offset:%[subfar]\n\t" \
+  "ds_read_b64_tr_b16 v[126:127], v51 offset:%[subfar]\n\t" \
+  "v_add_u32 v52, %[st], %[b10]\n\t" \
+  "v_add_u32 v53, %[st], %[b11]\n\t" \
+  OP " %[c01], v[64:67], v[112:119], v80\n\t" \
+  "ds_read_b64_tr_b16 v[40:41], v52 offset:%[sub]\n\t" \
+  "ds_read_b64_tr_b16 v[42:43], v53 offset:%[sub]\n\t" \
+  OP " %[c11], v[68:71], v[112:119], v81\n\t" \
+  "ds_read_b64_tr_b16 v[44:45], v52 offset:%[subfar]\n\t" \
+  "ds_read_b64_tr_b16 v[46:47], v53 offset:%[subfar]\n\t" \
+  OP " %[c21], v[72:75], v[112:119], v82\n\t" \
+  "ds_read_b128 v[92:95], v48 offset:%[as2]\n\t" \
+  "ds_read_b128 v[96:99], v48 offset:%[as3]\n\t" \
+  OP " %[c31], v[76:79], v[112:119], v83\n\t" \
+  "ds_read_u16 v102, v49 offset:%[ms2]\n\t" \
+  "ds_read_u16 v103, v49 offset:%[ms3]\n\t" \
+  "v_add_u32 v54, %[sn], %[b00]\n\t" \
+  "v_add_u32 v55, %[sn], %[b01]\n\t" \
+  "v_add_u32 v56, %[sn], %[ar0]\n\t" \
+  "v_add_u32 v57, %[sn], %[mr0]\n\t" \
+  "v_add_u32 v58, %[sn], %[b10]\n\t" \
+  "v_add_u32 v59, %[sn], %[b11]\n\t" \
+  "s_waitcnt lgkmcnt(8)\n\t" \
+  OP " %[c00], v[84:87], v[120:127], v100\n\t" \
+  "ds_read_b64_tr_b16 v[104:105], v54\n\t" \
+  "ds_read_b64_tr_b16 v[106:107], v55\n\t" \
+  OP " %[c10], v[88:91], v[120:127], v101\n\t" \
+  "ds_read_b64_tr_b16 v[108:109], v54 offset:%[far]\n\t" \
+  "ds_read_b64_tr_b16 v[110:111], v55 offset:%[far]\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  OP " %[c20], v[92:95], v[120:127], v102\n\t" \
+  "ds_read_b128 v[64:67], v56\n\t" \
+  "ds_read_b128 v[68:71], v56 offset:%[as1]\n\t" \
+  OP " %[c30], v[96:99], v[120:127], v103\n\t" \
+  "ds_read_u16 v80, v57\n\t" \
+  "ds_read_u16 v81, v57 offset:%[ms1]\n\t" \
+  OP " %[c01], v[84:87], v[40:47], v100\n\t" \
+  "ds_read_b64_tr_b16 v[112:113], v58\n\t" \
+  "ds_read_b64_tr_b16 v[114:115], v59\n\t" \
+  OP " %[c11], v[88:91], v[40:47], v101\n\t" \
+  "ds_read_b64_tr_b16 v[116:117], v58 offset:%[far]\n\t" \
+  "ds_read_b64_tr_b16 v[118:119], v59 offset:%[far]\n\t" \
+  OP " %[c21], v[92:95], v[40:47], v102\n\t" \
+  "ds_read_b128 v[72:75], v56 offset:%[as2]\n\t" \
+  "ds_read_b128 v[76:79], v56 offset:%[as3]\n\t" \
+  OP " %[c31], v[96:99], v[40:47], v103\n\t" \
+  "ds_read_u16 v82, v57 offset:%[ms2]\n\t" \
+  "ds_read_u16 v83, v57 offset:%[ms3]\n\t" \
+  "s_barrier\n\t" \
+  "s_mov_b32 %[st], %[sn]\n\t" \
+  "s_add_u32 %[sn], %[sn], %[stride]\n\t" \
+  "s_cmp_eq_u32 %[sn], %[end]\n\t" \
+  "s_cselect_b32 %[sn], %[base], %[sn]\n\t" \
+  "s_sub_u32 %[cnt], %[cnt], 1\n\t" \
+  "s_cmp_lg_u32 %[cnt], 0\n\t" \
+  "s_cbranch_scc1 L_ws24_%=\n\t" \
+  "s_waitcnt lgkmcnt(0)\n\t"
+
+template <bool BF16, int kStageBytes, int kStages, int kFar, int kSub, int kAS, int kMS>
+__device__ __forceinline__ void ws24_consumer_loop(float16v_t (&acc)[4][2], uint32_t base,
+                                                   int nsteps, uint32_t ar0, uint32_t ar1,
+                                                   uint32_t mr0, uint32_t mr1, uint32_t b00,
+                                                   uint32_t b01, uint32_t b10, uint32_t b11) {
+  uint32_t st, sn, cnt;
+  const uint32_t end = base + (uint32_t)(kStages * kStageBytes);
+#define NM_WS24_ASM(OPC)                                                                  \
+  asm volatile(NM_WS24_LOOP(OPC)                                                          \
+               : [c00] "+a"(acc[0][0]), [c10] "+a"(acc[1][0]), [c20] "+a"(acc[2][0]),     \
+                 [c30] "+a"(acc[3][0]), [c01] "+a"(acc[0][1]), [c11] "+a"(acc[1][1]),     \
+                 [c21] "+a"(acc[2][1]), [c31] "+a"(acc[3][1]), [st] "=&s"(st),            \
+                 [sn] "=&s"(sn), [cnt] "=&s"(cnt)                                         \
+               : [base] "s"(base), [end] "s"(end), [ns] "s"(nsteps), [ar0] "v"(ar0),       \
+                 [ar1] "v"(ar1), [mr0] "v"(mr0), [mr1] "v"(mr1), [b00] "v"(b00),          \
+                 [b01] "v"(b01), [b10] "v"(b10), [b11] "v"(b11), [stride] "n"(kStageBytes), \
+                 [far] "n"(kFar), [sub] "n"(kSub), [subfar] "n"(kSub + kFar),             \
+                 [as1] "n"(kAS), [as2] "n"(2 * kAS), [as3] "n"(3 * kAS), [ms1] "n"(kMS),  \
+                 [ms2] "n"(2 * kMS), [ms3] "n"(3 * kMS)                                   \
+               : "memory", "scc", "v40", "v41", "v42", "v43", "v44", "v45", "v46", "v47", "v48", "v49", "v50", "v51", "v52", "v53", "v54", "v55", "v56", "v57", "v58", "v59", "v64", "v65", "v66", "v67", "v68", "v69", "v70", "v71", "v72", "v73", "v74", "v75", "v76", "v77", "v78", "v79", "v80", "v81", "v82", "v83", "v84", "v85", "v86", "v87", "v88", "v89", "v90", "v91", "v92", "v93", "v94", "v95", "v96", "v97", "v98", "v99", "v100", "v101", "v102", "v103", "v104", "v105", "v106", "v107", "v108", "v109", "v110", "v111", "v112", "v113", "v114", "v115", "v116", "v117", "v118", "v119", "v120", "v121", "v122", "v123", "v124", "v125", "v126", "v127")
+  if constexpr (BF16)
+    NM_WS24_ASM("v_smfmac_f32_32x32x32_bf16");
+  else
+    NM_WS24_ASM("v_smfmac_f32_32x32x32_f16");
+#undef NM_WS24_ASM
+}
+#undef NM_WS24_LOOP
+
 // ===========================================================================
 // Wave-specialised form of the 32x32x32 kernel.  Each SIMD runs one consumer wave (LDS
 // fragment reads and smfmac blocks, exactly as in smfmac32_spmm_kernel) and one producer
@@ -1068,48 +1215,54 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
   auto stage_of = [&](int step) {
     return smem_base + (uint32_t)((step % kStages) * TL::kStageBytes);
   };
-  AFrags a0, a1;
-  short16_t b, bk = short16_t{};
-  short4_t n[4];
   asm volatile("s_barrier" ::: "memory");  // steps 0 and 1 landed
-  {
-    const uint32_t st = stage_of(0);
-    lds_a_fragments4<kPat12, kAS, kMS>(st + a_rd0, st + m_rd0, a0.v[0], a0.v[1], a0.v[2],
-                                       a0.v[3], a0.ix[0], a0.ix[1], a0.ix[2], a0.ix[3]);
-    b = lds_b_fragment<kFar>(st + b_rd[0][0], st + b_rd[0][1]);
-    widen_frags<kPat12>(a0);
-  }
-  for (int s = 0; s < nsteps; ++s) {
-    const uint32_t st = stage_of(s), sn = stage_of(s + 1);
-    // blocks 0 and 1 (substep 0, on a0) read substep 1's A into a1, half each; blocks 2
-    // and 3 (substep 1, on a1) read the next step's substep-0 A into a0
-    smfmac32_block_h<BF16, kPat12, kFar, kAS, kMS>(
-        acc[0][0], acc[1][0], acc[2][0], acc[3][0], a0, b, bk, st + b_rd[1][0],
-        st + b_rd[1][1], n, st + a_rd1, st + m_rd1, a1.v[0], a1.v[1], a1.ix[0], a1.ix[1]);
-    bk = b;
-    b = join_b(n);
-    smfmac32_block_h<BF16, kPat12, kFar, kAS, kMS>(
-        acc[0][1], acc[1][1], acc[2][1], acc[3][1], a0, b, bk, st + b_rd[0][0] + kSub,
-        st + b_rd[0][1] + kSub, n, st + a_rd1 + 2 * kAS, st + m_rd1 + 2 * kMS, a1.v[2],
-        a1.v[3], a1.ix[2], a1.ix[3]);
-    bk = b;
-    b = join_b(n);
-    widen_frags<kPat12>(a1);
-    smfmac32_block_h<BF16, kPat12, kFar, kAS, kMS>(
-        acc[0][0], acc[1][0], acc[2][0], acc[3][0], a1, b, bk, st + b_rd[1][0] + kSub,
-        st + b_rd[1][1] + kSub, n, sn + a_rd0, sn + m_rd0, a0.v[0], a0.v[1], a0.ix[0],
-        a0.ix[1]);
-    bk = b;
-    b = join_b(n);
-    // the last step reads a stage that holds no useful data; the values are never used
-    smfmac32_block_h<BF16, kPat12, kFar, kAS, kMS>(
-        acc[0][1], acc[1][1], acc[2][1], acc[3][1], a1, b, bk, sn + b_rd[0][0],
-        sn + b_rd[0][1], n, sn + a_rd0 + 2 * kAS, sn + m_rd0 + 2 * kMS, a0.v[2], a0.v[3],
-        a0.ix[2], a0.ix[3]);
-    bk = b;
-    b = join_b(n);
-    widen_frags<kPat12>(a0);
-    asm volatile("s_barrier" ::: "memory");  // step s+2 landed; stage of step s released
+  if constexpr (!kPat12) {
+    ws24_consumer_loop<BF16, TL::kStageBytes, kStages, kFar, kSub, kAS, kMS>(
+        acc, smem_base, nsteps, a_rd0, a_rd1, m_rd0, m_rd1, b_rd[0][0], b_rd[0][1],
+        b_rd[1][0], b_rd[1][1]);
+  } else {  // 1:2: index bytes widened in registers between blocks
+    AFrags a0, a1;
+    short16_t b, bk = short16_t{};
+    short4_t n[4];
+    {
+      const uint32_t st = stage_of(0);
+      lds_a_fragments4<kPat12, kAS, kMS>(st + a_rd0, st + m_rd0, a0.v[0], a0.v[1], a0.v[2],
+                                         a0.v[3], a0.ix[0], a0.ix[1], a0.ix[2], a0.ix[3]);
+      b = lds_b_fragment<kFar>(st + b_rd[0][0], st + b_rd[0][1]);
+      widen_frags<kPat12>(a0);
+    }
+    for (int s = 0; s < nsteps; ++s) {
+      const uint32_t st = stage_of(s), sn = stage_of(s + 1);
+      // blocks 0 and 1 (substep 0, on a0) read substep 1's A into a1, half each; blocks 2
+      // and 3 (substep 1, on a1) read the next step's substep-0 A into a0
+      smfmac32_block_h<BF16, kPat12, kFar, kAS, kMS>(
+          acc[0][0], acc[1][0], acc[2][0], acc[3][0], a0, b, bk, st + b_rd[1][0],
+          st + b_rd[1][1], n, st + a_rd1, st + m_rd1, a1.v[0], a1.v[1], a1.ix[0], a1.ix[1]);
+      bk = b;
+      b = join_b(n);
+      smfmac32_block_h<BF16, kPat12, kFar, kAS, kMS>(
+          acc[0][1], acc[1][1], acc[2][1], acc[3][1], a0, b, bk, st + b_rd[0][0] + kSub,
+          st + b_rd[0][1] + kSub, n, st + a_rd1 + 2 * kAS, st + m_rd1 + 2 * kMS, a1.v[2],
+          a1.v[3], a1.ix[2], a1.ix[3]);
+      bk = b;
+      b = join_b(n);
+      widen_frags<kPat12>(a1);
+      smfmac32_block_h<BF16, kPat12, kFar, kAS, kMS>(
+          acc[0][0], acc[1][0], acc[2][0], acc[3][0], a1, b, bk, st + b_rd[1][0] + kSub,
+          st + b_rd[1][1] + kSub, n, sn + a_rd0, sn + m_rd0, a0.v[0], a0.v[1], a0.ix[0],
+          a0.ix[1]);
+      bk = b;
+      b = join_b(n);
+      // the last step reads a stage that holds no useful data; the values are never used
+      smfmac32_block_h<BF16, kPat12, kFar, kAS, kMS>(
+          acc[0][1], acc[1][1], acc[2][1], acc[3][1], a1, b, bk, sn + b_rd[0][0],
+          sn + b_rd[0][1], n, sn + a_rd0 + 2 * kAS, sn + m_rd0 + 2 * kMS, a0.v[2], a0.v[3],
+          a0.ix[2], a0.ix[3]);
+      bk = b;
+      b = join_b(n);
+      widen_frags<kPat12>(a0);
+      asm volatile("s_barrier" ::: "memory");  // step s+2 landed; stage of step s released
+    }
   }
   // the producers' last loads have landed (final barrier), and the last smfmac results
   // get time to land before plain instructions read the accumulators
