@@ -27,7 +27,8 @@ hipError_t launch_spmm(const void* values, const uint32_t* meta, int64_t R, int6
 // The 2:4 16-bit product on 256 x 256 tiles split over the compute units by K steps
 // (nm_spmm_sk.hip), blocked layout, dt / y_dt as for launch_spmm.  sk_shape_ok: the
 // shapes it takes (K % 64 == 0, T % 8 == 0, sizes within its 32-bit offsets);
-// sk_preferred: shapes where it is the fastest kernel.  The workspace (device memory
+// sk_preferred: shapes where it is taken without NM_SPMM_TILE=3 (none at present: the
+// wave-specialised kernel is faster on every measured shape).  The workspace (device memory
 // of sk_workspace_bytes(R, T, groups) bytes, 256-byte aligned; none, and NULL may be
 // passed, when every workgroup gets whole tiles) holds one flag and one partial 256 x 256
 // fp32 tile per workgroup; its initial contents do not matter.

@@ -80,6 +80,25 @@ __device__ __forceinline__ void global_to_lds_sv(const void* sbase, uint32_t vof
 #endif
 }
 
+// The same with a per-lane 64-bit address (the instruction's "off" form), for sources whose
+// per-lane offsets do not fit 32 bits.
+template <int kSize>
+__device__ __forceinline__ void global_to_lds_v(const void* src, uint32_t lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  static_assert(kSize == 4 || kSize == 16, "dword or dwordx4");
+  if constexpr (kSize == 16)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(src), "s"(lds)
+                 : "memory", "m0");
+#endif
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)(p);
 }

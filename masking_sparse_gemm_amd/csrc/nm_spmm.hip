@@ -561,60 +561,7 @@ __device__ __forceinline__ void smfmac32_block_a(float16v_t& c0, float16v_t& c1,
   }
 #undef NM_SMFMAC32_A
 }
-// The same four smfmac with an even share of the next reads: the next B fragment and half
-// of the next A fragments with their index words (two fragments, kAStride apart, into
-// na0 / na1; index words kMStride apart into ni0 / ni1), 4.25 KB per wave, so that every
-// block of a step reads the same amount from LDS (a SIMD's LDS port moves about 64 bytes
-// a clock, and the four smfmac of a block take 128 clocks).  All reads follow the first
-// smfmac.  An A half is written one block after the last smfmac that read it was issued:
-// each smfmac of a SIMD starts only when the one before it has finished, so the reads,
-// which issue behind this block's first smfmac, land after the previous block's smfmac
-// have read their operands.
-#define NM_SMFMAC32_BLOCK_H(OP, MREAD)                                                     \
-  "s_nop 2\n\t"                                                                            \
-  NM_SMF32(OP, "c0", "a0", "i0")                                                           \
-  "ds_read_b64_tr_b16 %[n0], %[b0]\n\t"                                                    \
-  "ds_read_b64_tr_b16 %[n1], %[b1]\n\t"                                                    \
-  "ds_read_b64_tr_b16 %[n2], %[b0] offset:%[far]\n\t"                                      \
-  "ds_read_b64_tr_b16 %[n3], %[b1] offset:%[far]\n\t"                                      \
-  "ds_read_b128 %[na0], %[aa]\n\t"                                                         \
-  "ds_read_b128 %[na1], %[aa] offset:%[as1]\n\t"                                           \
-  MREAD " %[ni0], %[ma]\n\t"                                                               \
-  MREAD " %[ni1], %[ma] offset:%[ms1]\n\t"                                                 \
-  NM_SMF32(OP, "c1", "a1", "i1")                                                           \
-  NM_SMF32(OP, "c2", "a2", "i2")                                                           \
-  NM_SMF32(OP, "c3", "a3", "i3")                                                           \
-  "s_waitcnt lgkmcnt(0)"
-
-template <bool BF16, bool kPat12, int kFar, int kAStride, int kMStride>
-__device__ __forceinline__ void smfmac32_block_h(float16v_t& c0, float16v_t& c1, float16v_t& c2,
-                                                 float16v_t& c3, const AFrags& a,
-                                                 const short16_t& b, const short16_t& keep,
-                                                 uint32_t b0, uint32_t b1, short4_t (&n)[4],
-                                                 uint32_t aa, uint32_t ma, u32x4_t& na0,
-                                                 u32x4_t& na1, uint32_t& ni0, uint32_t& ni1) {
-#define NM_SMFMAC32_H(OP, MREAD)                                                           \
-  asm volatile(NM_SMFMAC32_BLOCK_H(OP, MREAD)                                              \
-               : NM_SMFMAC32_BOUTS, [na0] "=&v"(na0), [na1] "=&v"(na1), [ni0] "=&v"(ni0),  \
-                 [ni1] "=&v"(ni1), NM_SMFMAC32_COUTS                                       \
-               : NM_SMFMAC32_INS, [aa] "v"(aa), [ma] "v"(ma), [as1] "n"(kAStride),         \
-                 [ms1] "n"(kMStride)                                                       \
-               : "memory")
-  if constexpr (BF16) {
-    if constexpr (kPat12)
-      NM_SMFMAC32_H("v_smfmac_f32_32x32x32_bf16", "ds_read_u8");
-    else
-      NM_SMFMAC32_H("v_smfmac_f32_32x32x32_bf16", "ds_read_u16");
-  } else {
-    if constexpr (kPat12)
-      NM_SMFMAC32_H("v_smfmac_f32_32x32x32_f16", "ds_read_u8");
-    else
-      NM_SMFMAC32_H("v_smfmac_f32_32x32x32_f16", "ds_read_u16");
-  }
-#undef NM_SMFMAC32_H
-}
 #undef NM_SMF32
-#undef NM_SMFMAC32_BLOCK_H
 #undef NM_SMFMAC32_BLOCK
 #undef NM_SMFMAC32_BLOCK_A
 #undef NM_SMFMAC32_BOUTS
@@ -1144,9 +1091,10 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
       m16_dst = (uint32_t)(TL::kXBytes + TL::kABytes + pw * 512);
     }
     auto issue_step = [&](int step) {
-      step = step < last_step ? step : last_step;  // past the end: re-read the last step
-      uint8_t* st = smem + (step % kStages) * TL::kStageBytes;
-      const uint32_t sta = lds_addr(st);
+      // the step's own ring slot; past the end the loads re-read the last step's data into
+      // it (a slot no wave reads any more), so every step issues the same loads
+      const uint32_t sta = lds_addr(smem + (step % kStages) * TL::kStageBytes);
+      step = step < last_step ? step : last_step;
       const int64_t kx = (int64_t)step * kKStep * T * 2;
       const int64_t ka = (int64_t)step * values_step_bytes<kBlocked>();
       const int64_t km = (int64_t)step * meta_step_bytes<kBlocked, kPat12>();
@@ -1157,24 +1105,48 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
         if constexpr (kBlocked)
           global_to_lds_sv<16>(a_base[j] + ka, a_off, sta + a_dst[j]);
         else
-          global_to_lds<16>(vg + a_row[j] + ka + a_off, st + a_dst[j]);
+          global_to_lds_v<16>(vg + a_row[j] + ka + a_off, sta + a_dst[j]);
       }
       if constexpr (kWideMeta) {
         if (lane < 32) global_to_lds_sv<16>(m16_base + km, m16_off, sta + m16_dst);
       } else {
 #pragma unroll
-        for (int j = 0; j < TL::kMLoads; ++j) global_to_lds<4>(mg + m_src[j] + km, st + m_dst[j]);
+        for (int j = 0; j < TL::kMLoads; ++j) global_to_lds_v<4>(mg + m_src[j] + km, sta + m_dst[j]);
+      }
+    };
+    // 1:2: once a step has landed, each producer rewrites the metadata rows it loaded
+    // (four bytes per row, one bit per stored value) in place as the 2:4 instruction's
+    // index units (four 16-bit units per row), so the consumers read both patterns alike.
+    auto widen_step = [&](int step) {
+      if constexpr (kPat12) {
+        const int row = 32 * ((lane >> 5) * TL::kProducers + pw) + (lane & 31);
+        const uint32_t a = lds_addr(smem + (step % kStages) * TL::kStageBytes + TL::kXBytes +
+                                    TL::kABytes) + (uint32_t)(row * 8);
+        uint32_t raw;
+        asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(raw) : "v"(a) : "memory");
+        const uint32_t w0 = widen_1_2(raw) | (widen_1_2(raw >> 8) << 16);
+        const uint32_t w1 = widen_1_2(raw >> 16) | (widen_1_2(raw >> 24) << 16);
+        asm volatile("ds_write_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                     :
+                     : "v"(a), "v"(u32x2_t{w0, w1})
+                     : "memory");
       }
     };
     // direct loads one producer issues per step
     constexpr int kLoads = kXLoads + TL::kALoads + (kWideMeta ? 1 : TL::kMLoads);
     static_assert((kStages - 2) * kLoads <= 63, "vmcnt budget");
+    static_assert(!kPat12 || TL::kMLoads * 32 * TL::kProducers == BM, "a metadata row per lane");
 #pragma unroll
     for (int k = 0; k < kStages - 1; ++k) issue_step(k);
-    wait_loads_and_barrier<(kStages - 3) * kLoads>();  // steps 0 and 1 landed
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kStages - 3) * kLoads) : "memory");
+    widen_step(0);  // steps 0 and 1 landed
+    widen_step(1);
+    asm volatile("s_barrier" ::: "memory");
     for (int s = 0; s < nsteps; ++s) {
       issue_step(s + kStages - 1);
-      wait_loads_and_barrier<(kStages - 3) * kLoads>();  // step s+2 landed
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kStages - 3) * kLoads) : "memory");
+      widen_step(s + 2);  // step s+2 landed
+      asm volatile("s_barrier" ::: "memory");
     }
     // loads past the end have landed before the consumers reuse LDS for the epilogue
     wait_loads_and_barrier<0>();
@@ -1188,9 +1160,9 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
   const int aswz = (ia >> 2) & 3;
   const uint32_t a_rd0 = (uint32_t)(TL::kXBytes + ia * 64 + (((0 + q) ^ aswz) << 4));
   const uint32_t a_rd1 = (uint32_t)(TL::kXBytes + ia * 64 + (((2 + q) ^ aswz) << 4));
-  constexpr int kMT = kPat12 ? 2 : 4;
-  const uint32_t m_rd0 = (uint32_t)(TL::kXBytes + TL::kABytes + ia * 8 + (kPat12 ? q : 2 * q));
-  const uint32_t m_rd1 = m_rd0 + kMT;
+  // index units of the 2:4 instruction (1:2 rows are widened to them by the producers)
+  const uint32_t m_rd0 = (uint32_t)(TL::kXBytes + TL::kABytes + ia * 8 + 2 * q);
+  const uint32_t m_rd1 = m_rd0 + 4;
   const int rb = 8 * q + (l16 >> 2);
   uint32_t b_rd[2][2];
 #pragma unroll
@@ -1212,58 +1184,10 @@ __global__ void __launch_bounds__(64 * (CWAVES_M * CWAVES_N + PWAVES))
     for (int f = 0; f < 2; ++f) acc[fm][f] = float16v_t{};
 
   const uint32_t smem_base = lds_addr(smem);
-  auto stage_of = [&](int step) {
-    return smem_base + (uint32_t)((step % kStages) * TL::kStageBytes);
-  };
   asm volatile("s_barrier" ::: "memory");  // steps 0 and 1 landed
-  if constexpr (!kPat12) {
-    ws24_consumer_loop<BF16, TL::kStageBytes, kStages, kFar, kSub, kAS, kMS>(
-        acc, smem_base, nsteps, a_rd0, a_rd1, m_rd0, m_rd1, b_rd[0][0], b_rd[0][1],
-        b_rd[1][0], b_rd[1][1]);
-  } else {  // 1:2: index bytes widened in registers between blocks
-    AFrags a0, a1;
-    short16_t b, bk = short16_t{};
-    short4_t n[4];
-    {
-      const uint32_t st = stage_of(0);
-      lds_a_fragments4<kPat12, kAS, kMS>(st + a_rd0, st + m_rd0, a0.v[0], a0.v[1], a0.v[2],
-                                         a0.v[3], a0.ix[0], a0.ix[1], a0.ix[2], a0.ix[3]);
-      b = lds_b_fragment<kFar>(st + b_rd[0][0], st + b_rd[0][1]);
-      widen_frags<kPat12>(a0);
-    }
-    for (int s = 0; s < nsteps; ++s) {
-      const uint32_t st = stage_of(s), sn = stage_of(s + 1);
-      // blocks 0 and 1 (substep 0, on a0) read substep 1's A into a1, half each; blocks 2
-      // and 3 (substep 1, on a1) read the next step's substep-0 A into a0
-      smfmac32_block_h<BF16, kPat12, kFar, kAS, kMS>(
-          acc[0][0], acc[1][0], acc[2][0], acc[3][0], a0, b, bk, st + b_rd[1][0],
-          st + b_rd[1][1], n, st + a_rd1, st + m_rd1, a1.v[0], a1.v[1], a1.ix[0], a1.ix[1]);
-      bk = b;
-      b = join_b(n);
-      smfmac32_block_h<BF16, kPat12, kFar, kAS, kMS>(
-          acc[0][1], acc[1][1], acc[2][1], acc[3][1], a0, b, bk, st + b_rd[0][0] + kSub,
-          st + b_rd[0][1] + kSub, n, st + a_rd1 + 2 * kAS, st + m_rd1 + 2 * kMS, a1.v[2],
-          a1.v[3], a1.ix[2], a1.ix[3]);
-      bk = b;
-      b = join_b(n);
-      widen_frags<kPat12>(a1);
-      smfmac32_block_h<BF16, kPat12, kFar, kAS, kMS>(
-          acc[0][0], acc[1][0], acc[2][0], acc[3][0], a1, b, bk, st + b_rd[1][0] + kSub,
-          st + b_rd[1][1] + kSub, n, sn + a_rd0, sn + m_rd0, a0.v[0], a0.v[1], a0.ix[0],
-          a0.ix[1]);
-      bk = b;
-      b = join_b(n);
-      // the last step reads a stage that holds no useful data; the values are never used
-      smfmac32_block_h<BF16, kPat12, kFar, kAS, kMS>(
-          acc[0][1], acc[1][1], acc[2][1], acc[3][1], a1, b, bk, sn + b_rd[0][0],
-          sn + b_rd[0][1], n, sn + a_rd0 + 2 * kAS, sn + m_rd0 + 2 * kMS, a0.v[2], a0.v[3],
-          a0.ix[2], a0.ix[3]);
-      bk = b;
-      b = join_b(n);
-      widen_frags<kPat12>(a0);
-      asm volatile("s_barrier" ::: "memory");  // step s+2 landed; stage of step s released
-    }
-  }
+  ws24_consumer_loop<BF16, TL::kStageBytes, kStages, kFar, kSub, kAS, kMS>(
+      acc, smem_base, nsteps, a_rd0, a_rd1, m_rd0, m_rd1, b_rd[0][0], b_rd[0][1], b_rd[1][0],
+      b_rd[1][1]);
   // the producers' last loads have landed (final barrier), and the last smfmac results
   // get time to land before plain instructions read the accumulators
   asm volatile("s_barrier\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
@@ -2299,9 +2223,9 @@ struct TileChoice {
   double rate;
 };
 constexpr int kNumTiles = 3;
-constexpr TileChoice kTiles[kNumTiles] = {{256, 256, 1300.0}, {256, 128, 1350.0},
-                                          {128, 128, 850.0}};
-constexpr double kTileFixedUs = 3.0;
+constexpr TileChoice kTiles[kNumTiles] = {{256, 256, 1720.0}, {256, 128, 1900.0},
+                                          {128, 128, 1150.0}};
+constexpr double kTileFixedUs = 5.0;
 
 int pick_tile(int64_t R, int64_t K, int64_t T) {
   // NM_SPMM_TILE=0/1/2 pins one shape (used by the tests to cover every shape)

@@ -632,15 +632,15 @@ bool sk_shape_ok(int64_t R, int64_t K, int64_t T) {
 }
 
 bool sk_preferred(int64_t R, int64_t K, int64_t T) {
-  // the kernel's 256 x 256 tiles come out ahead of the 256 x 128 wave-specialised kernel
-  // when every compute unit gets the same whole number of tiles (no partial tiles to
-  // exchange, all workgroups in step) over a long enough K loop; on shapes that would
-  // need tiles cut between workgroups the exchange of partial sums and the workgroups'
-  // scattered K positions cost more than they save (measured on the LLaMA-7B MLP shapes)
-  if (!sk_shape_ok(R, K, T) || K / kKStep < 16) return false;
-  const int64_t tiles = ((R + kSkBM - 1) / kSkBM) * ((T + kSkBN - 1) / kSkBN);
-  const int g = sk_groups(R, K, T);
-  return tiles >= g && tiles % g == 0;
+  // Never taken on its own: the 256 x 128 wave-specialised kernel, whose consumers keep
+  // their LDS reads in flight across blocks, now runs every measured shape faster (the
+  // fp16 4096 x 4096 x 8192 2:4 product, 512 tiles of this kernel on 256 compute units:
+  // 146 against 160 us; the LLaMA-7B MLP shapes, where tiles would have to be cut between
+  // workgroups: 107 / 92 against 167 / 143 us).  NM_SPMM_TILE=3 still selects it.
+  (void)R;
+  (void)K;
+  (void)T;
+  return false;
 }
 
 hipError_t launch_spmm_sk(const void* values, const uint32_t* meta, int64_t R, int64_t K,
