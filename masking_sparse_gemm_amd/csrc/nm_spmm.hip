@@ -778,7 +778,10 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 // flight across blocks (the compiler would take an asm statement's outputs as written when
 // the statement ends).  Fragments live in fixed registers: A of substep 0 (a0) in
 // v64..v83, of substep 1 (a1) in v84..v103, the four B fragments of a step in v104..v127
-// and v40..v47, addresses in v48..v59.  Per step, block j issues its reads right behind
+// and v40..v47.  The loop is unrolled over the four ring slots: v48..v63 hold each lane
+// offset plus the LDS address of slots 0-1 and of slots 2-3, and a read adds (slot & 1)
+// stages and its own offset as the instruction's immediate, so a step does no address
+// arithmetic.  Per step, block j issues its reads right behind
 // its first smfmac, one block ahead of their use:
 //   block 0 (a0 x B0): a1 fragments 0-1 and B2;   block 1 (a0 x B1): B3, a1 fragments 2-3;
 //   block 2 (a1 x B2): next B0, next a0 0-1;       block 3 (a1 x B3): next B1, next a0 2-3.
@@ -792,105 +795,269 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 // the statement ends.
 #define NM_WS24_LOOP(OP) \
   "s_waitcnt lgkmcnt(0)\n\t" \
-  "s_mov_b32 %[sn], %[base]\n\t" \
-  "v_add_u32 v54, %[sn], %[b00]\n\t" \
-  "v_add_u32 v55, %[sn], %[b01]\n\t" \
-  "v_add_u32 v56, %[sn], %[ar0]\n\t" \
-  "v_add_u32 v57, %[sn], %[mr0]\n\t" \
-  "v_add_u32 v58, %[sn], %[b10]\n\t" \
-  "v_add_u32 v59, %[sn], %[b11]\n\t" \
-  "ds_read_b64_tr_b16 v[104:105], v54\n\t" \
-  "ds_read_b64_tr_b16 v[106:107], v55\n\t" \
-  "ds_read_b64_tr_b16 v[108:109], v54 offset:%[far]\n\t" \
-  "ds_read_b64_tr_b16 v[110:111], v55 offset:%[far]\n\t" \
-  "ds_read_b128 v[64:67], v56\n\t" \
-  "ds_read_b128 v[68:71], v56 offset:%[as1]\n\t" \
-  "ds_read_u16 v80, v57\n\t" \
-  "ds_read_u16 v81, v57 offset:%[ms1]\n\t" \
-  "ds_read_b64_tr_b16 v[112:113], v58\n\t" \
-  "ds_read_b64_tr_b16 v[114:115], v59\n\t" \
-  "ds_read_b64_tr_b16 v[116:117], v58 offset:%[far]\n\t" \
-  "ds_read_b64_tr_b16 v[118:119], v59 offset:%[far]\n\t" \
-  "ds_read_b128 v[72:75], v56 offset:%[as2]\n\t" \
-  "ds_read_b128 v[76:79], v56 offset:%[as3]\n\t" \
-  "ds_read_u16 v82, v57 offset:%[ms2]\n\t" \
-  "ds_read_u16 v83, v57 offset:%[ms3]\n\t" \
-  "s_mov_b32 %[st], %[base]\n\t" \
-  "s_add_u32 %[sn], %[base], %[stride]\n\t" \
+  "v_add_u32 v48, %[base], %[ar0]\n\t" \
+  "v_add_u32 v49, %[basehi], %[ar0]\n\t" \
+  "v_add_u32 v50, %[base], %[ar1]\n\t" \
+  "v_add_u32 v51, %[basehi], %[ar1]\n\t" \
+  "v_add_u32 v52, %[base], %[mr0]\n\t" \
+  "v_add_u32 v53, %[basehi], %[mr0]\n\t" \
+  "v_add_u32 v54, %[base], %[mr1]\n\t" \
+  "v_add_u32 v55, %[basehi], %[mr1]\n\t" \
+  "v_add_u32 v56, %[base], %[b00]\n\t" \
+  "v_add_u32 v57, %[basehi], %[b00]\n\t" \
+  "v_add_u32 v58, %[base], %[b01]\n\t" \
+  "v_add_u32 v59, %[basehi], %[b01]\n\t" \
+  "v_add_u32 v60, %[base], %[b10]\n\t" \
+  "v_add_u32 v61, %[basehi], %[b10]\n\t" \
+  "v_add_u32 v62, %[base], %[b11]\n\t" \
+  "v_add_u32 v63, %[basehi], %[b11]\n\t" \
+  "ds_read_b64_tr_b16 v[104:105], v56\n\t" \
+  "ds_read_b64_tr_b16 v[106:107], v58\n\t" \
+  "ds_read_b64_tr_b16 v[108:109], v56 offset:4096\n\t" \
+  "ds_read_b64_tr_b16 v[110:111], v58 offset:4096\n\t" \
+  "ds_read_b128 v[64:67], v48\n\t" \
+  "ds_read_b128 v[68:71], v48 offset:2048\n\t" \
+  "ds_read_u16 v80, v52\n\t" \
+  "ds_read_u16 v81, v52 offset:256\n\t" \
+  "ds_read_b64_tr_b16 v[112:113], v60\n\t" \
+  "ds_read_b64_tr_b16 v[114:115], v62\n\t" \
+  "ds_read_b64_tr_b16 v[116:117], v60 offset:4096\n\t" \
+  "ds_read_b64_tr_b16 v[118:119], v62 offset:4096\n\t" \
+  "ds_read_b128 v[72:75], v48 offset:4096\n\t" \
+  "ds_read_b128 v[76:79], v48 offset:6144\n\t" \
+  "ds_read_u16 v82, v52 offset:512\n\t" \
+  "ds_read_u16 v83, v52 offset:768\n\t" \
   "s_mov_b32 %[cnt], %[ns]\n\t" \
-  "L_ws24_%=:\n\t" \
-  "v_add_u32 v48, %[st], %[ar1]\n\t" \
-  "v_add_u32 v49, %[st], %[mr1]\n\t" \
-  "v_add_u32 v50, %[st], %[b00]\n\t" \
-  "v_add_u32 v51, %[st], %[b01]\n\t" \
+  "L_ws24_s0_%=:\n\t" \
   "s_waitcnt lgkmcnt(8)\n\t" \
   OP " %[c00], v[64:67], v[104:111], v80\n\t" \
-  "ds_read_b128 v[84:87], v48\n\t" \
-  "ds_read_b128 v[88:91], v48 offset:%[as1]\n\t" \
+  "ds_read_b128 v[84:87], v50\n\t" \
+  "ds_read_b128 v[88:91], v50 offset:2048\n\t" \
   OP " %[c10], v[68:71], v[104:111], v81\n\t" \
-  "ds_read_u16 v100, v49\n\t" \
-  "ds_read_u16 v101, v49 offset:%[ms1]\n\t" \
+  "ds_read_u16 v100, v54\n\t" \
+  "ds_read_u16 v101, v54 offset:256\n\t" \
   "s_waitcnt lgkmcnt(4)\n\t" \
   OP " %[c20], v[72:75], v[104:111], v82\n\t" \
-  "ds_read_b64_tr_b16 v[120:121], v50 offset:%[sub]\n\t" \
-  "ds_read_b64_tr_b16 v[122:123], v51 offset:%[sub]\n\t" \
+  "ds_read_b64_tr_b16 v[120:121], v56 offset:8192\n\t" \
+  "ds_read_b64_tr_b16 v[122:123], v58 offset:8192\n\t" \
   OP " %[c30], v[76:79], v[104:111], v83\n\t" \
-  "ds_read_b64_tr_b16 v[124:125], v50 offset:%[subfar]\n\t" \
-  "ds_read_b64_tr_b16 v[126:127], v51 offset:%[subfar]\n\t" \
-  "v_add_u32 v52, %[st], %[b10]\n\t" \
-  "v_add_u32 v53, %[st], %[b11]\n\t" \
+  "ds_read_b64_tr_b16 v[124:125], v56 offset:12288\n\t" \
+  "ds_read_b64_tr_b16 v[126:127], v58 offset:12288\n\t" \
   OP " %[c01], v[64:67], v[112:119], v80\n\t" \
-  "ds_read_b64_tr_b16 v[40:41], v52 offset:%[sub]\n\t" \
-  "ds_read_b64_tr_b16 v[42:43], v53 offset:%[sub]\n\t" \
+  "ds_read_b64_tr_b16 v[40:41], v60 offset:8192\n\t" \
+  "ds_read_b64_tr_b16 v[42:43], v62 offset:8192\n\t" \
   OP " %[c11], v[68:71], v[112:119], v81\n\t" \
-  "ds_read_b64_tr_b16 v[44:45], v52 offset:%[subfar]\n\t" \
-  "ds_read_b64_tr_b16 v[46:47], v53 offset:%[subfar]\n\t" \
+  "ds_read_b64_tr_b16 v[44:45], v60 offset:12288\n\t" \
+  "ds_read_b64_tr_b16 v[46:47], v62 offset:12288\n\t" \
   OP " %[c21], v[72:75], v[112:119], v82\n\t" \
-  "ds_read_b128 v[92:95], v48 offset:%[as2]\n\t" \
-  "ds_read_b128 v[96:99], v48 offset:%[as3]\n\t" \
+  "ds_read_b128 v[92:95], v50 offset:4096\n\t" \
+  "ds_read_b128 v[96:99], v50 offset:6144\n\t" \
   OP " %[c31], v[76:79], v[112:119], v83\n\t" \
-  "ds_read_u16 v102, v49 offset:%[ms2]\n\t" \
-  "ds_read_u16 v103, v49 offset:%[ms3]\n\t" \
-  "v_add_u32 v54, %[sn], %[b00]\n\t" \
-  "v_add_u32 v55, %[sn], %[b01]\n\t" \
-  "v_add_u32 v56, %[sn], %[ar0]\n\t" \
-  "v_add_u32 v57, %[sn], %[mr0]\n\t" \
-  "v_add_u32 v58, %[sn], %[b10]\n\t" \
-  "v_add_u32 v59, %[sn], %[b11]\n\t" \
+  "ds_read_u16 v102, v54 offset:512\n\t" \
+  "ds_read_u16 v103, v54 offset:768\n\t" \
   "s_waitcnt lgkmcnt(8)\n\t" \
   OP " %[c00], v[84:87], v[120:127], v100\n\t" \
-  "ds_read_b64_tr_b16 v[104:105], v54\n\t" \
-  "ds_read_b64_tr_b16 v[106:107], v55\n\t" \
+  "ds_read_b64_tr_b16 v[104:105], v56 offset:34816\n\t" \
+  "ds_read_b64_tr_b16 v[106:107], v58 offset:34816\n\t" \
   OP " %[c10], v[88:91], v[120:127], v101\n\t" \
-  "ds_read_b64_tr_b16 v[108:109], v54 offset:%[far]\n\t" \
-  "ds_read_b64_tr_b16 v[110:111], v55 offset:%[far]\n\t" \
+  "ds_read_b64_tr_b16 v[108:109], v56 offset:38912\n\t" \
+  "ds_read_b64_tr_b16 v[110:111], v58 offset:38912\n\t" \
   "s_waitcnt lgkmcnt(4)\n\t" \
   OP " %[c20], v[92:95], v[120:127], v102\n\t" \
-  "ds_read_b128 v[64:67], v56\n\t" \
-  "ds_read_b128 v[68:71], v56 offset:%[as1]\n\t" \
+  "ds_read_b128 v[64:67], v48 offset:34816\n\t" \
+  "ds_read_b128 v[68:71], v48 offset:36864\n\t" \
   OP " %[c30], v[96:99], v[120:127], v103\n\t" \
-  "ds_read_u16 v80, v57\n\t" \
-  "ds_read_u16 v81, v57 offset:%[ms1]\n\t" \
+  "ds_read_u16 v80, v52 offset:34816\n\t" \
+  "ds_read_u16 v81, v52 offset:35072\n\t" \
   OP " %[c01], v[84:87], v[40:47], v100\n\t" \
-  "ds_read_b64_tr_b16 v[112:113], v58\n\t" \
-  "ds_read_b64_tr_b16 v[114:115], v59\n\t" \
+  "ds_read_b64_tr_b16 v[112:113], v60 offset:34816\n\t" \
+  "ds_read_b64_tr_b16 v[114:115], v62 offset:34816\n\t" \
   OP " %[c11], v[88:91], v[40:47], v101\n\t" \
-  "ds_read_b64_tr_b16 v[116:117], v58 offset:%[far]\n\t" \
-  "ds_read_b64_tr_b16 v[118:119], v59 offset:%[far]\n\t" \
+  "ds_read_b64_tr_b16 v[116:117], v60 offset:38912\n\t" \
+  "ds_read_b64_tr_b16 v[118:119], v62 offset:38912\n\t" \
   OP " %[c21], v[92:95], v[40:47], v102\n\t" \
-  "ds_read_b128 v[72:75], v56 offset:%[as2]\n\t" \
-  "ds_read_b128 v[76:79], v56 offset:%[as3]\n\t" \
+  "ds_read_b128 v[72:75], v48 offset:38912\n\t" \
+  "ds_read_b128 v[76:79], v48 offset:40960\n\t" \
   OP " %[c31], v[96:99], v[40:47], v103\n\t" \
-  "ds_read_u16 v82, v57 offset:%[ms2]\n\t" \
-  "ds_read_u16 v83, v57 offset:%[ms3]\n\t" \
+  "ds_read_u16 v82, v52 offset:35328\n\t" \
+  "ds_read_u16 v83, v52 offset:35584\n\t" \
   "s_barrier\n\t" \
-  "s_mov_b32 %[st], %[sn]\n\t" \
-  "s_add_u32 %[sn], %[sn], %[stride]\n\t" \
-  "s_cmp_eq_u32 %[sn], %[end]\n\t" \
-  "s_cselect_b32 %[sn], %[base], %[sn]\n\t" \
   "s_sub_u32 %[cnt], %[cnt], 1\n\t" \
-  "s_cmp_lg_u32 %[cnt], 0\n\t" \
-  "s_cbranch_scc1 L_ws24_%=\n\t" \
+  "s_cmp_eq_u32 %[cnt], 0\n\t" \
+  "s_cbranch_scc1 L_ws24_end_%=\n\t" \
+  "L_ws24_s1_%=:\n\t" \
+  "s_waitcnt lgkmcnt(8)\n\t" \
+  OP " %[c00], v[64:67], v[104:111], v80\n\t" \
+  "ds_read_b128 v[84:87], v50 offset:34816\n\t" \
+  "ds_read_b128 v[88:91], v50 offset:36864\n\t" \
+  OP " %[c10], v[68:71], v[104:111], v81\n\t" \
+  "ds_read_u16 v100, v54 offset:34816\n\t" \
+  "ds_read_u16 v101, v54 offset:35072\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  OP " %[c20], v[72:75], v[104:111], v82\n\t" \
+  "ds_read_b64_tr_b16 v[120:121], v56 offset:43008\n\t" \
+  "ds_read_b64_tr_b16 v[122:123], v58 offset:43008\n\t" \
+  OP " %[c30], v[76:79], v[104:111], v83\n\t" \
+  "ds_read_b64_tr_b16 v[124:125], v56 offset:47104\n\t" \
+  "ds_read_b64_tr_b16 v[126:127], v58 offset:47104\n\t" \
+  OP " %[c01], v[64:67], v[112:119], v80\n\t" \
+  "ds_read_b64_tr_b16 v[40:41], v60 offset:43008\n\t" \
+  "ds_read_b64_tr_b16 v[42:43], v62 offset:43008\n\t" \
+  OP " %[c11], v[68:71], v[112:119], v81\n\t" \
+  "ds_read_b64_tr_b16 v[44:45], v60 offset:47104\n\t" \
+  "ds_read_b64_tr_b16 v[46:47], v62 offset:47104\n\t" \
+  OP " %[c21], v[72:75], v[112:119], v82\n\t" \
+  "ds_read_b128 v[92:95], v50 offset:38912\n\t" \
+  "ds_read_b128 v[96:99], v50 offset:40960\n\t" \
+  OP " %[c31], v[76:79], v[112:119], v83\n\t" \
+  "ds_read_u16 v102, v54 offset:35328\n\t" \
+  "ds_read_u16 v103, v54 offset:35584\n\t" \
+  "s_waitcnt lgkmcnt(8)\n\t" \
+  OP " %[c00], v[84:87], v[120:127], v100\n\t" \
+  "ds_read_b64_tr_b16 v[104:105], v57\n\t" \
+  "ds_read_b64_tr_b16 v[106:107], v59\n\t" \
+  OP " %[c10], v[88:91], v[120:127], v101\n\t" \
+  "ds_read_b64_tr_b16 v[108:109], v57 offset:4096\n\t" \
+  "ds_read_b64_tr_b16 v[110:111], v59 offset:4096\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  OP " %[c20], v[92:95], v[120:127], v102\n\t" \
+  "ds_read_b128 v[64:67], v49\n\t" \
+  "ds_read_b128 v[68:71], v49 offset:2048\n\t" \
+  OP " %[c30], v[96:99], v[120:127], v103\n\t" \
+  "ds_read_u16 v80, v53\n\t" \
+  "ds_read_u16 v81, v53 offset:256\n\t" \
+  OP " %[c01], v[84:87], v[40:47], v100\n\t" \
+  "ds_read_b64_tr_b16 v[112:113], v61\n\t" \
+  "ds_read_b64_tr_b16 v[114:115], v63\n\t" \
+  OP " %[c11], v[88:91], v[40:47], v101\n\t" \
+  "ds_read_b64_tr_b16 v[116:117], v61 offset:4096\n\t" \
+  "ds_read_b64_tr_b16 v[118:119], v63 offset:4096\n\t" \
+  OP " %[c21], v[92:95], v[40:47], v102\n\t" \
+  "ds_read_b128 v[72:75], v49 offset:4096\n\t" \
+  "ds_read_b128 v[76:79], v49 offset:6144\n\t" \
+  OP " %[c31], v[96:99], v[40:47], v103\n\t" \
+  "ds_read_u16 v82, v53 offset:512\n\t" \
+  "ds_read_u16 v83, v53 offset:768\n\t" \
+  "s_barrier\n\t" \
+  "s_sub_u32 %[cnt], %[cnt], 1\n\t" \
+  "s_cmp_eq_u32 %[cnt], 0\n\t" \
+  "s_cbranch_scc1 L_ws24_end_%=\n\t" \
+  "L_ws24_s2_%=:\n\t" \
+  "s_waitcnt lgkmcnt(8)\n\t" \
+  OP " %[c00], v[64:67], v[104:111], v80\n\t" \
+  "ds_read_b128 v[84:87], v51\n\t" \
+  "ds_read_b128 v[88:91], v51 offset:2048\n\t" \
+  OP " %[c10], v[68:71], v[104:111], v81\n\t" \
+  "ds_read_u16 v100, v55\n\t" \
+  "ds_read_u16 v101, v55 offset:256\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  OP " %[c20], v[72:75], v[104:111], v82\n\t" \
+  "ds_read_b64_tr_b16 v[120:121], v57 offset:8192\n\t" \
+  "ds_read_b64_tr_b16 v[122:123], v59 offset:8192\n\t" \
+  OP " %[c30], v[76:79], v[104:111], v83\n\t" \
+  "ds_read_b64_tr_b16 v[124:125], v57 offset:12288\n\t" \
+  "ds_read_b64_tr_b16 v[126:127], v59 offset:12288\n\t" \
+  OP " %[c01], v[64:67], v[112:119], v80\n\t" \
+  "ds_read_b64_tr_b16 v[40:41], v61 offset:8192\n\t" \
+  "ds_read_b64_tr_b16 v[42:43], v63 offset:8192\n\t" \
+  OP " %[c11], v[68:71], v[112:119], v81\n\t" \
+  "ds_read_b64_tr_b16 v[44:45], v61 offset:12288\n\t" \
+  "ds_read_b64_tr_b16 v[46:47], v63 offset:12288\n\t" \
+  OP " %[c21], v[72:75], v[112:119], v82\n\t" \
+  "ds_read_b128 v[92:95], v51 offset:4096\n\t" \
+  "ds_read_b128 v[96:99], v51 offset:6144\n\t" \
+  OP " %[c31], v[76:79], v[112:119], v83\n\t" \
+  "ds_read_u16 v102, v55 offset:512\n\t" \
+  "ds_read_u16 v103, v55 offset:768\n\t" \
+  "s_waitcnt lgkmcnt(8)\n\t" \
+  OP " %[c00], v[84:87], v[120:127], v100\n\t" \
+  "ds_read_b64_tr_b16 v[104:105], v57 offset:34816\n\t" \
+  "ds_read_b64_tr_b16 v[106:107], v59 offset:34816\n\t" \
+  OP " %[c10], v[88:91], v[120:127], v101\n\t" \
+  "ds_read_b64_tr_b16 v[108:109], v57 offset:38912\n\t" \
+  "ds_read_b64_tr_b16 v[110:111], v59 offset:38912\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  OP " %[c20], v[92:95], v[120:127], v102\n\t" \
+  "ds_read_b128 v[64:67], v49 offset:34816\n\t" \
+  "ds_read_b128 v[68:71], v49 offset:36864\n\t" \
+  OP " %[c30], v[96:99], v[120:127], v103\n\t" \
+  "ds_read_u16 v80, v53 offset:34816\n\t" \
+  "ds_read_u16 v81, v53 offset:35072\n\t" \
+  OP " %[c01], v[84:87], v[40:47], v100\n\t" \
+  "ds_read_b64_tr_b16 v[112:113], v61 offset:34816\n\t" \
+  "ds_read_b64_tr_b16 v[114:115], v63 offset:34816\n\t" \
+  OP " %[c11], v[88:91], v[40:47], v101\n\t" \
+  "ds_read_b64_tr_b16 v[116:117], v61 offset:38912\n\t" \
+  "ds_read_b64_tr_b16 v[118:119], v63 offset:38912\n\t" \
+  OP " %[c21], v[92:95], v[40:47], v102\n\t" \
+  "ds_read_b128 v[72:75], v49 offset:38912\n\t" \
+  "ds_read_b128 v[76:79], v49 offset:40960\n\t" \
+  OP " %[c31], v[96:99], v[40:47], v103\n\t" \
+  "ds_read_u16 v82, v53 offset:35328\n\t" \
+  "ds_read_u16 v83, v53 offset:35584\n\t" \
+  "s_barrier\n\t" \
+  "s_sub_u32 %[cnt], %[cnt], 1\n\t" \
+  "s_cmp_eq_u32 %[cnt], 0\n\t" \
+  "s_cbranch_scc1 L_ws24_end_%=\n\t" \
+  "L_ws24_s3_%=:\n\t" \
+  "s_waitcnt lgkmcnt(8)\n\t" \
+  OP " %[c00], v[64:67], v[104:111], v80\n\t" \
+  "ds_read_b128 v[84:87], v51 offset:34816\n\t" \
+  "ds_read_b128 v[88:91], v51 offset:36864\n\t" \
+  OP " %[c10], v[68:71], v[104:111], v81\n\t" \
+  "ds_read_u16 v100, v55 offset:34816\n\t" \
+  "ds_read_u16 v101, v55 offset:35072\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  OP " %[c20], v[72:75], v[104:111], v82\n\t" \
+  "ds_read_b64_tr_b16 v[120:121], v57 offset:43008\n\t" \
+  "ds_read_b64_tr_b16 v[122:123], v59 offset:43008\n\t" \
+  OP " %[c30], v[76:79], v[104:111], v83\n\t" \
+  "ds_read_b64_tr_b16 v[124:125], v57 offset:47104\n\t" \
+  "ds_read_b64_tr_b16 v[126:127], v59 offset:47104\n\t" \
+  OP " %[c01], v[64:67], v[112:119], v80\n\t" \
+  "ds_read_b64_tr_b16 v[40:41], v61 offset:43008\n\t" \
+  "ds_read_b64_tr_b16 v[42:43], v63 offset:43008\n\t" \
+  OP " %[c11], v[68:71], v[112:119], v81\n\t" \
+  "ds_read_b64_tr_b16 v[44:45], v61 offset:47104\n\t" \
+  "ds_read_b64_tr_b16 v[46:47], v63 offset:47104\n\t" \
+  OP " %[c21], v[72:75], v[112:119], v82\n\t" \
+  "ds_read_b128 v[92:95], v51 offset:38912\n\t" \
+  "ds_read_b128 v[96:99], v51 offset:40960\n\t" \
+  OP " %[c31], v[76:79], v[112:119], v83\n\t" \
+  "ds_read_u16 v102, v55 offset:35328\n\t" \
+  "ds_read_u16 v103, v55 offset:35584\n\t" \
+  "s_waitcnt lgkmcnt(8)\n\t" \
+  OP " %[c00], v[84:87], v[120:127], v100\n\t" \
+  "ds_read_b64_tr_b16 v[104:105], v56\n\t" \
+  "ds_read_b64_tr_b16 v[106:107], v58\n\t" \
+  OP " %[c10], v[88:91], v[120:127], v101\n\t" \
+  "ds_read_b64_tr_b16 v[108:109], v56 offset:4096\n\t" \
+  "ds_read_b64_tr_b16 v[110:111], v58 offset:4096\n\t" \
+  "s_waitcnt lgkmcnt(4)\n\t" \
+  OP " %[c20], v[92:95], v[120:127], v102\n\t" \
+  "ds_read_b128 v[64:67], v48\n\t" \
+  "ds_read_b128 v[68:71], v48 offset:2048\n\t" \
+  OP " %[c30], v[96:99], v[120:127], v103\n\t" \
+  "ds_read_u16 v80, v52\n\t" \
+  "ds_read_u16 v81, v52 offset:256\n\t" \
+  OP " %[c01], v[84:87], v[40:47], v100\n\t" \
+  "ds_read_b64_tr_b16 v[112:113], v60\n\t" \
+  "ds_read_b64_tr_b16 v[114:115], v62\n\t" \
+  OP " %[c11], v[88:91], v[40:47], v101\n\t" \
+  "ds_read_b64_tr_b16 v[116:117], v60 offset:4096\n\t" \
+  "ds_read_b64_tr_b16 v[118:119], v62 offset:4096\n\t" \
+  OP " %[c21], v[92:95], v[40:47], v102\n\t" \
+  "ds_read_b128 v[72:75], v48 offset:4096\n\t" \
+  "ds_read_b128 v[76:79], v48 offset:6144\n\t" \
+  OP " %[c31], v[96:99], v[40:47], v103\n\t" \
+  "ds_read_u16 v82, v52 offset:512\n\t" \
+  "ds_read_u16 v83, v52 offset:768\n\t" \
+  "s_barrier\n\t" \
+  "s_sub_u32 %[cnt], %[cnt], 1\n\t" \
+  "s_cmp_eq_u32 %[cnt], 0\n\t" \
+  "s_cbranch_scc1 L_ws24_end_%=\n\t" \
+  "s_branch L_ws24_s0_%=\n\t" \
+  "L_ws24_end_%=:\n\t" \
   "s_waitcnt lgkmcnt(0)\n\t"
 
 template <bool BF16, int kStageBytes, int kStages, int kFar, int kSub, int kAS, int kMS>
@@ -898,21 +1065,21 @@ __device__ __forceinline__ void ws24_consumer_loop(float16v_t (&acc)[4][2], uint
                                                    int nsteps, uint32_t ar0, uint32_t ar1,
                                                    uint32_t mr0, uint32_t mr1, uint32_t b00,
                                                    uint32_t b01, uint32_t b10, uint32_t b11) {
-  uint32_t st, sn, cnt;
-  const uint32_t end = base + (uint32_t)(kStages * kStageBytes);
+  // the loop text carries these as numbers (256 x 128 tiles, 64-wide steps, four slots)
+  static_assert(kStageBytes == 34816 && kStages == 4 && kFar == 4096 && kSub == 8192 &&
+                    kAS == 2048 && kMS == 256,
+                "layout constants of the generated loop");
+  uint32_t cnt;
+  const uint32_t basehi = base + (uint32_t)(2 * kStageBytes);
 #define NM_WS24_ASM(OPC)                                                                  \
   asm volatile(NM_WS24_LOOP(OPC)                                                          \
                : [c00] "+a"(acc[0][0]), [c10] "+a"(acc[1][0]), [c20] "+a"(acc[2][0]),     \
                  [c30] "+a"(acc[3][0]), [c01] "+a"(acc[0][1]), [c11] "+a"(acc[1][1]),     \
-                 [c21] "+a"(acc[2][1]), [c31] "+a"(acc[3][1]), [st] "=&s"(st),            \
-                 [sn] "=&s"(sn), [cnt] "=&s"(cnt)                                         \
-               : [base] "s"(base), [end] "s"(end), [ns] "s"(nsteps), [ar0] "v"(ar0),       \
+                 [c21] "+a"(acc[2][1]), [c31] "+a"(acc[3][1]), [cnt] "=&s"(cnt)           \
+               : [base] "s"(base), [basehi] "s"(basehi), [ns] "s"(nsteps), [ar0] "v"(ar0), \
                  [ar1] "v"(ar1), [mr0] "v"(mr0), [mr1] "v"(mr1), [b00] "v"(b00),          \
-                 [b01] "v"(b01), [b10] "v"(b10), [b11] "v"(b11), [stride] "n"(kStageBytes), \
-                 [far] "n"(kFar), [sub] "n"(kSub), [subfar] "n"(kSub + kFar),             \
-                 [as1] "n"(kAS), [as2] "n"(2 * kAS), [as3] "n"(3 * kAS), [ms1] "n"(kMS),  \
-                 [ms2] "n"(2 * kMS), [ms3] "n"(3 * kMS)                                   \
-               : "memory", "scc", "v40", "v41", "v42", "v43", "v44", "v45", "v46", "v47", "v48", "v49", "v50", "v51", "v52", "v53", "v54", "v55", "v56", "v57", "v58", "v59", "v64", "v65", "v66", "v67", "v68", "v69", "v70", "v71", "v72", "v73", "v74", "v75", "v76", "v77", "v78", "v79", "v80", "v81", "v82", "v83", "v84", "v85", "v86", "v87", "v88", "v89", "v90", "v91", "v92", "v93", "v94", "v95", "v96", "v97", "v98", "v99", "v100", "v101", "v102", "v103", "v104", "v105", "v106", "v107", "v108", "v109", "v110", "v111", "v112", "v113", "v114", "v115", "v116", "v117", "v118", "v119", "v120", "v121", "v122", "v123", "v124", "v125", "v126", "v127")
+                 [b01] "v"(b01), [b10] "v"(b10), [b11] "v"(b11)                           \
+               : "memory", "scc", "v40", "v41", "v42", "v43", "v44", "v45", "v46", "v47", "v48", "v49", "v50", "v51", "v52", "v53", "v54", "v55", "v56", "v57", "v58", "v59", "v60", "v61", "v62", "v63", "v64", "v65", "v66", "v67", "v68", "v69", "v70", "v71", "v72", "v73", "v74", "v75", "v76", "v77", "v78", "v79", "v80", "v81", "v82", "v83", "v84", "v85", "v86", "v87", "v88", "v89", "v90", "v91", "v92", "v93", "v94", "v95", "v96", "v97", "v98", "v99", "v100", "v101", "v102", "v103", "v104", "v105", "v106", "v107", "v108", "v109", "v110", "v111", "v112", "v113", "v114", "v115", "v116", "v117", "v118", "v119", "v120", "v121", "v122", "v123", "v124", "v125", "v126", "v127")
   if constexpr (BF16)
     NM_WS24_ASM("v_smfmac_f32_32x32x32_bf16");
   else
