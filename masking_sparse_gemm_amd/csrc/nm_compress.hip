@@ -91,7 +91,7 @@ struct UnitSelection {
         pos[g][1] = p1;
         keep[g] = (1u << p0) | (1u << p1);
       } else {
-        keep[g] = keep_bits<N, M>(key);
+        keep[g] = group_keep<E, N, M>(key);
         kept_positions<N>(keep[g], pos[g]);
       }
     }
@@ -328,6 +328,7 @@ struct LaneShape {
   static constexpr int kBits = kVals * meta_bits(M);          // metadata bits per lane
   static constexpr int kBlockMetaWords = 64 * kBits / 32;
   static constexpr bool kShuffle = 32 % kBits == 0;           // whole lanes per word
+  static constexpr bool kLdsBits = !kShuffle && kBits != 24;  // packed in an LDS buffer
 };
 
 // Selection, value packing and metadata packing of one lane's 16 elements of a block
@@ -366,7 +367,7 @@ __device__ __forceinline__ uint32_t blocked_emit(const uint32_t (&w)[LaneShape<E
 #pragma unroll
       for (int i = 0; i < M; ++i) key[i] = Elem<E>::key(word_elem<E>(w, gi * M + i));
       int pos[N];
-      const uint32_t kb = keep_bits<N, M>(key);
+      const uint32_t kb = group_keep<E, N, M>(key);
       keep16 |= kb << (M * gi);
       kept_positions<N>(kb, pos);
 #pragma unroll
@@ -385,6 +386,14 @@ __device__ __forceinline__ uint32_t blocked_emit(const uint32_t (&w)[LaneShape<E
     constexpr int LPW = 32 / L::kBits;  // lanes per metadata word
     const uint32_t word = or_reduce_lanes<LPW>((uint32_t)bits << ((lane % LPW) * L::kBits));
     if (lane % LPW == 0) mblk[lane / LPW] = word;
+  } else if constexpr (L::kBits == 24) {
+    // 4:8 (eight 3-bit fields a lane): four lanes' 24-bit runs make three whole words.
+    // Lane 4j + i (i < 3) writes word 3j + i: its own bits from bit 8i on, and the next
+    // lane's bits above them.
+    const uint32_t own = (uint32_t)bits;
+    const uint32_t next = __shfl_down(own, 1);
+    const int i = lane & 3;
+    if (i < 3) mblk[3 * (lane >> 2) + i] = (own >> (8 * i)) | (next << (24 - 8 * i));
   } else {
     uint32_t* buf = bits_buf;
     for (int i = lane; i < L::kBlockMetaWords; i += 64) buf[i] = 0;
@@ -408,7 +417,7 @@ __global__ void __launch_bounds__(kThreads) blocked_select_kernel(const uint32_t
                                                                   uint32_t* __restrict__ values,
                                                                   uint32_t* __restrict__ meta) {
   using L = LaneShape<E, N, M>;
-  __shared__ uint32_t lds_bits[kThreads / 64][L::kShuffle ? 1 : L::kBlockMetaWords];
+  __shared__ uint32_t lds_bits[kThreads / 64][L::kLdsBits ? L::kBlockMetaWords : 1];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar math
   const int64_t blk = (int64_t)blockIdx.x * (kThreads / 64) + wave;
@@ -446,7 +455,7 @@ __global__ void __launch_bounds__(kThreads) blocked_select_mask_kernel(
     uint32_t* __restrict__ values, uint32_t* __restrict__ meta, uint8_t* __restrict__ mask) {
   using L = LaneShape<E, N, M>;
   constexpr int kRowWords = 16 * kPer;  // mask words per row segment
-  __shared__ uint32_t lds_bits[kThreads / 64][L::kShuffle ? 1 : L::kBlockMetaWords];
+  __shared__ uint32_t lds_bits[kThreads / 64][L::kLdsBits ? L::kBlockMetaWords : 1];
   __shared__ __align__(16) uint32_t stage[kThreads / 64][16 * kRowWords];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar math
@@ -527,7 +536,7 @@ __global__ void __launch_bounds__(kThreads) blocked_select_t_kernel(
     uint32_t* __restrict__ meta) {
   using L = LaneShape<E, N, M>;
   using TT = TileT<E>;
-  __shared__ uint32_t lds_bits[kThreads / 64][L::kShuffle ? 1 : L::kBlockMetaWords];
+  __shared__ uint32_t lds_bits[kThreads / 64][L::kLdsBits ? L::kBlockMetaWords : 1];
   __shared__ __align__(16) uint32_t tile[kThreads / 64][TT::kWords];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -595,7 +604,7 @@ __global__ void __launch_bounds__(kThreads) group_t_kernel(const E* __restrict__
     key[i] = Elem<E>::key(v[i]);
   }
   int pos[N];
-  kept_positions<N>(keep_bits<N, M>(key), pos);
+  kept_positions<N>(group_keep<E, N, M>(key), pos);
   E* dst = values + k * (R / M * N) + g * N;
 #pragma unroll
   for (int j = 0; j < N; ++j) {
@@ -626,7 +635,7 @@ __global__ void __launch_bounds__(kThreads) meta_word_t_kernel(const E* __restri
 #pragma unroll
     for (int i = 0; i < M; ++i) key[i] = Elem<E>::key((uint32_t)W[(g * M + i) * K + k]);
     int pos[N];
-    kept_positions<N>(keep_bits<N, M>(key), pos);
+    kept_positions<N>(group_keep<E, N, M>(key), pos);
 #pragma unroll
     for (int j = 0; j < N; ++j) {
       const int64_t f = g * N + j;
@@ -747,7 +756,7 @@ __device__ __forceinline__ void select_group(const E* W, int64_t base, int (&pos
   uint32_t key[M];
 #pragma unroll
   for (int i = 0; i < M; ++i) key[i] = Elem<E>::key((uint32_t)W[base + i]);
-  keep = keep_bits<N, M>(key);
+  keep = group_keep<E, N, M>(key);
   kept_positions<N>(keep, pos);
 }
 

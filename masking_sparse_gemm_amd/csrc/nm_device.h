@@ -104,8 +104,55 @@ __device__ __forceinline__ void top2_of_4(uint32_t k0, uint32_t k1, uint32_t k2,
   p1 = (int)(3u - min(l1, l2));
 }
 
+// 4:8 for elements of at most 16 bits.  The composite key 8 |w| + (7 - i) is again
+// distinct within a group and orders as the rule above, so the kept set is the top four
+// of eight distinct integers.  Each half of four is sorted (five compare-exchanges), the
+// first half descending and the second ascending; the eight then form a bitonic sequence,
+// whose element-wise maxima of the two halves are its four largest values.  That is 24
+// min / max operations instead of 28 pairwise counts.  Returns the keep mask (bit i set iff
+// element i is kept).
+__host__ __device__ __forceinline__ uint32_t top4_of_8(const uint32_t (&key)[8]) {
+  uint32_t a[4], b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = (key[i] << 3) | (7u - i);
+    b[i] = (key[4 + i] << 3) | (3u - i);
+  }
+  constexpr int kNet[5][2] = {{0, 1}, {2, 3}, {0, 2}, {1, 3}, {1, 2}};  // sorts four
+#pragma unroll
+  for (int c = 0; c < 5; ++c) {
+    const int i = kNet[c][0], j = kNet[c][1];
+    const uint32_t ahi = a[i] > a[j] ? a[i] : a[j], alo = a[i] > a[j] ? a[j] : a[i];
+    const uint32_t bhi = b[i] > b[j] ? b[i] : b[j], blo = b[i] > b[j] ? b[j] : b[i];
+    a[i] = ahi;  // descending
+    a[j] = alo;
+    b[i] = blo;  // ascending
+    b[j] = bhi;
+  }
+  uint32_t keep = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t t = a[i] > b[i] ? a[i] : b[i];
+    keep |= 0x80u >> (t & 7u);
+  }
+  return keep;
+}
+
 template <typename E, int N, int M>
 constexpr bool fast24() { return N == 2 && M == 4 && sizeof(E) <= 2; }
+
+template <typename E, int N, int M>
+constexpr bool fast48() { return N == 4 && M == 8 && sizeof(E) <= 2; }
+
+// Keep mask of one group: the network above for 4:8 on elements of at most 16 bits, the
+// count rule otherwise.
+template <typename E, int N, int M>
+__device__ __forceinline__ uint32_t group_keep(const uint32_t (&key)[M]) {
+  if constexpr (fast48<E, N, M>())
+    return top4_of_8(key);
+  else
+    return keep_bits<N, M>(key);
+}
 
 // Kept values of consecutive 2:4 groups gathered with byte permutes (fast24 types):
 // 16-bit elements, group g in words 2g, 2g+1 -> word g; 8-bit elements, group g in word

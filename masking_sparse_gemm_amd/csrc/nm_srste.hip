@@ -85,7 +85,7 @@ __device__ __forceinline__ uint32_t unit_keep(const uint32_t (&w)[NW]) {
     uint32_t key[M];
 #pragma unroll
     for (int i = 0; i < M; ++i) key[i] = word_elem<E>(w, g * M + i) & Elem<E>::kKeyMask;
-    keep |= keep_bits<N, M>(key) << (g * M);
+    keep |= group_keep<E, N, M>(key) << (g * M);
   }
   return keep;
 }
@@ -196,7 +196,7 @@ __global__ void __launch_bounds__(kThreads) srste_group_kernel(const void* W, co
     key[i] = wv[i] & Elem<E>::kKeyMask;
     if constexpr (kGrad) gv[i] = static_cast<const E*>(G)[base + i];
   }
-  const uint32_t keep = keep_bits<N, M>(key);
+  const uint32_t keep = group_keep<E, N, M>(key);
   E* o = static_cast<E*>(out) + base;
 #pragma unroll
   for (int i = 0; i < M; ++i) {
