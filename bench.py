@@ -501,6 +501,41 @@ def valu_ceiling(torch, dev, stream, hipt):
     return out
 
 
+def load_path_ceiling(nm, mats, stream, hipt, launch, reps):
+    """What the product's direct global -> LDS loads take alone (libnm_probe's load-path
+    probe: the same loads, ring, waits, barriers and tile mapping as the 2:4 product on its
+    256 x 128 tiles, with idle waves in place of the matrix work), timed as `reps` launches
+    back to back on each matrix's own inputs, beside the product timed the same way."""
+    import torch
+
+    P = nm.probe_lib()
+    sp = stream.cuda_stream
+    out = {"us": {}, "spmm_us": {}}
+    for d in mats:
+        def probe(d=d):
+            rc = P.nm_probe_load_path(d["vals"].data_ptr(), d["meta"].data_ptr(),
+                                      d["Xd"].data_ptr(), d["R"], d["K"], d["T"], sp)
+            if rc != 0:
+                raise RuntimeError(f"nm_probe_load_path failed ({rc})")
+        for name, fn in (("us", probe), ("spmm_us", lambda d=d: launch(d, "spmm"))):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = hipt.event(), hipt.event()
+            hipt.record(e0)
+            for _ in range(reps):
+                fn()
+            hipt.record(e1)
+            torch.cuda.synchronize()
+            out[name][d["name"]] = round(hipt.ms(e0, e1) / reps * 1e3, 2)
+    out["how"] = ("the product's direct loads alone (libnm_probe): X rows, compressed values and "
+                  "metadata of every 64-wide K step into the same 4-stage LDS ring with the same "
+                  "waits, barriers and XCD tile mapping, idle waves in place of the matrix work; "
+                  "launches back to back, the product timed the same way beside it (spmm_us); "
+                  "alg_tflops = the product's algorithmic flops over the probe's time")
+    return out
+
+
 def sweep_f16_block(torch, nm, synth, L, dev, stream, hipt, args, cold_times):
     """The fp16 N:M sweep: W 4096 x 4096 ~Laplace(0, 0.05), X 4096 x 8192 ~N(0, 1).  For each
     of 1:2, 2:4 and 4:8: the fused mask + compress pass, the mask alone, decompress and the
@@ -973,6 +1008,16 @@ def main() -> int:
                    "this workload's W and X (libnm_probe); the device lowers its clock under "
                    "such load (zeros: %d MHz)" % ceiling["smfmac_32x32x32_bf16.zeros"]["clock_mhz"]}
         roofline["frac_of_ceiling"] = round(achieved / (c["eff_tflops"] / 2), 4)
+
+    # ---- the product's direct loads alone (libnm_probe): its load-path bound ----
+    if dtype in ("bf16", "f16") and (n, m) == (2, 4) and args.layout == "blocked" and \
+            all(d["T"] % 8 == 0 and d["K"] % 64 == 0 for d in mats):
+        lp = load_path_ceiling(nm, mats, stream, hipt, launch, args.steps)
+        lp["alg_tflops"] = round(F_alg / (sum(lp["us"].values()) * 1e-6) / 1e12, 1)
+        lp["frac_of_peak"] = round(lp["alg_tflops"] / peak, 4)
+        roofline["load_path_ceiling"] = lp
+        roofline["frac_of_load_path"] = round(sum(lp["us"].values())
+                                              / sum(lp["spmm_us"].values()), 4)
 
     # ---- the fp16 N:M sweep: 4096 x 4096 weights, 8192 activation columns ----
     sweep = None

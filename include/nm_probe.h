@@ -11,7 +11,7 @@
  * toggling bits), so the probe runs the instruction alone on caller-chosen operands.
  *
  * The VALU loop does the same for the vector ALU, the unit the permutation search's gains
- * kernel is bound by.
+ * kernel is bound by, and the load-path probe replays the product's direct loads alone.
  *
  * Pointers are DEVICE pointers owned by the caller; calls are asynchronous on `stream`
  * (a hipStream_t as void*, NULL = the default stream).  Returns 0 when the launch was
@@ -57,6 +57,18 @@ int nm_probe_valu(int op, int cus, int waves_per_simd, int iters, int64_t* clock
  * stores per lane (bytes a multiple of 16, both pointers 16-byte aligned, the ranges not
  * overlapping; else 1).  The rate a pass that reads and writes each byte once can reach. */
 int nm_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
+/* The direct-load stream of the 2:4 16-bit product on its 256 x 128 tiles, alone: the
+ * same global -> LDS loads (X rows, compressed values and metadata in the blocked layout,
+ * 34,816 bytes per 64-wide K step and tile), the same 4-stage LDS ring, wait counts,
+ * barrier per step and workgroup -> tile mapping as the product's producer waves, with
+ * idle waves in place of the consumers; nothing is computed or written.  values and meta
+ * are a 2:4 16-bit compressed pair of an R x K weight in NM_LAYOUT_BLOCKED (as nm_compress
+ * writes it), X is K x T 16-bit: the product's inputs.  Requires K % 64 == 0, T % 8 == 0,
+ * 16-byte aligned pointers, R < 2^28, K < 2^22, T < 2^24 (else 1).  Its time is what the
+ * product's loads take without its matrix work: a bound on the product from above. */
+int nm_probe_load_path(const void* values, const void* meta, const void* X, int64_t R,
+                       int64_t K, int64_t T, void* stream);
 
 #ifdef __cplusplus
 }

@@ -113,8 +113,8 @@ _probe = None
 
 
 def probe_lib() -> ctypes.CDLL:
-    """The loaded libnm_probe.so (include/nm_probe.h): the benchmark's matrix-core and VALU
-    rate probes (raises if it is not built)."""
+    """The loaded libnm_probe.so (include/nm_probe.h): the benchmark's matrix-core, VALU,
+    copy and load-path probes (raises if it is not built)."""
     global _probe
     if _probe is None:
         if not os.path.exists(PROBE_LIB_PATH):
@@ -132,6 +132,9 @@ def probe_lib() -> ctypes.CDLL:
         P.nm_probe_valu.restype = ctypes.c_int
         P.nm_probe_copy.argtypes = [vp, vp, ctypes.c_int64, vp]
         P.nm_probe_copy.restype = ctypes.c_int
+        P.nm_probe_load_path.argtypes = [vp, vp, vp, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_int64, vp]
+        P.nm_probe_load_path.restype = ctypes.c_int
         _probe = P
     return _probe
 

@@ -1,10 +1,11 @@
-// nm_probe.hip -- matrix-core rate loops that bound the sparse product on this device
+// nm_probe.hip -- rate loops that bound the sparse product on this device
 // (include/nm_probe.h).  Nothing here computes part of the method.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 
 #include "../../include/nm_probe.h"
+#include "nm_mfma.h"
 
 namespace {
 
@@ -145,6 +146,109 @@ __global__ void __launch_bounds__(256) copy_probe_kernel(const u32x4v_t* __restr
     __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
+// ---------------------------------------------------------------------------------------
+// The direct-load stream of the 2:4 16-bit product on 256 x 128 tiles (blocked layout,
+// T % 8 == 0) with nothing else: per 64-wide K step and tile, 16 KB of X rows, 16 KB of
+// compressed values and 2 KB of metadata land in a 4-stage LDS ring, issued by four
+// producer waves with the same addresses, wait counts and one barrier per step as the
+// product's producers, while four idle waves pass the same barriers in place of the
+// consumers (so one workgroup holds a compute unit's LDS, as the product's does).  Its time
+// is what the product's loads take alone.
+// ---------------------------------------------------------------------------------------
+constexpr int kLpBM = 256, kLpBN = 128, kLpStages = 4, kLpProducers = 4;
+constexpr int kLpXBytes = nm::kKStep * kLpBN * 2;  // 64 K rows of 128 columns
+constexpr int kLpABytes = kLpBM * 64;               // 32 kept values a row
+constexpr int kLpMBytes = kLpBM * 8;                // 64 metadata bits a row
+constexpr int kLpStageBytes = kLpXBytes + kLpABytes + kLpMBytes;
+constexpr int kLpXLoads = kLpXBytes / 1024 / kLpProducers;
+constexpr int kLpALoads = kLpABytes / 1024 / kLpProducers;
+constexpr int kLpLoads = kLpXLoads + kLpALoads + 1;
+
+// Workgroup -> tile: workgroup b runs on XCD b % xcds; each XCD takes a contiguous range
+// of the tile order, which walks gm x gn groups of tiles (the product's mapping).
+struct LpMap {
+  int tiles_m, tiles_n, xcds, per_xcd, gm, gn;
+  __device__ bool tile_of(int b, int& tm, int& tn) const {
+    const int t = (b % xcds) * per_xcd + b / xcds;
+    if (t >= tiles_m * tiles_n) return false;
+    const int g_m = t / (gm * tiles_n);
+    const int rows = min(gm, tiles_m - g_m * gm);
+    const int u = t - g_m * gm * tiles_n;
+    const int g_n = u / (rows * gn);
+    const int v = u - g_n * rows * gn;
+    tm = g_m * gm + v % rows;
+    tn = g_n * gn + v / rows;
+    return true;
+  }
+};
+
+__global__ void __launch_bounds__(512) load_path_probe_kernel(const uint8_t* __restrict__ values,
+                                                              const uint8_t* __restrict__ meta,
+                                                              const uint8_t* __restrict__ X,
+                                                              int R, int K, int T, LpMap map) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  int tile_m, tile_n;
+  if (!map.tile_of(blockIdx.x, tile_m, tile_n)) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int m0 = tile_m * kLpBM, t0 = tile_n * kLpBN;
+  const int nsteps = K / nm::kKStep;
+  if (wave < 4) {  // in place of the consumers: the same barriers, nothing else
+    for (int s = 0; s < nsteps + 2; ++s) asm volatile("s_barrier" ::: "memory");
+    return;
+  }
+  const int pw = wave - 4;
+  const int last_step = nsteps - 1;
+  // X: load j fills 1 KB window w = 4 j + pw of the stage (K rows 4w .. 4w+3); lane l takes
+  // row 4w + l / 16 and the 16-byte piece that lands at physical piece l % 16
+  const int r = lane >> 4, pc = lane & 15;
+  const int lc = 2 * ((pc >> 1) ^ nm::xpair_swizzle(r)) + (pc & 1);
+  int col = t0 + 8 * lc;
+  col = col < T ? col : 0;
+  const uint32_t x_off = (uint32_t)(((int64_t)r * T + col) * 2);
+  // values: load j fills the 1 KB block of tile rows 16 (4 j + pw) .. +15 for the step
+  const int last = ((R + 15) >> 4) - 1;
+  const uint32_t a_off = (uint32_t)((lane >> 2) * 64 + 16 * ((lane & 3) ^ ((lane >> 4) & 3)));
+  // metadata: four 128-byte blocks per producer, one 16-byte piece on each of 32 lanes
+  int g0 = (m0 >> 4) + 4 * pw;
+  g0 = g0 < last ? g0 : last;
+  int g = (m0 >> 4) + 4 * pw + ((lane & 31) >> 3);
+  g = g < last ? g : last;
+  const uint8_t* m16_base = meta + (int64_t)g0 * nsteps * 128;
+  const uint32_t m16_off = (uint32_t)((g - g0) * nsteps * 128 + 16 * (lane & 7));
+  auto issue_step = [&](int step) {
+    const uint32_t sta = nm::lds_addr(smem + (step % kLpStages) * kLpStageBytes);
+    step = step < last_step ? step : last_step;
+    const int64_t kx = (int64_t)step * nm::kKStep * T * 2;
+#pragma unroll
+    for (int j = 0; j < kLpXLoads; ++j) {
+      const int w = j * kLpProducers + pw;
+      nm::global_to_lds_sv<16>(X + (int64_t)(4 * w) * T * 2 + kx, x_off, sta + (uint32_t)(w * 1024));
+    }
+#pragma unroll
+    for (int j = 0; j < kLpALoads; ++j) {
+      const int b16 = j * kLpProducers + pw;
+      int gb = (m0 >> 4) + b16;
+      gb = gb < last ? gb : last;
+      nm::global_to_lds_sv<16>(values + (int64_t)gb * nsteps * 1024 + (int64_t)step * 1024, a_off,
+                               sta + (uint32_t)(kLpXBytes + b16 * 1024));
+    }
+    if (lane < 32)
+      nm::global_to_lds_sv<16>(m16_base + (int64_t)step * 128, m16_off,
+                               sta + (uint32_t)(kLpXBytes + kLpABytes + pw * 512));
+  };
+#pragma unroll
+  for (int k = 0; k < kLpStages - 1; ++k) issue_step(k);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kLpStages - 3) * kLpLoads) : "memory");
+  asm volatile("s_barrier" ::: "memory");
+  for (int s = 0; s < nsteps; ++s) {
+    issue_step(s + kLpStages - 1);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kLpStages - 3) * kLpLoads) : "memory");
+    asm volatile("s_barrier" ::: "memory");
+  }
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 }  // namespace
 
 extern "C" {
@@ -186,6 +290,36 @@ int nm_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
   hipLaunchKernelGGL(copy_probe_kernel, dim3((unsigned)blocks), dim3(256), 0,
                      static_cast<hipStream_t>(stream), static_cast<const u32x4v_t*>(src),
                      static_cast<u32x4v_t*>(dst), n16);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+int nm_probe_load_path(const void* values, const void* meta, const void* X, int64_t R,
+                       int64_t K, int64_t T, void* stream) {
+  const auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; };
+  if (values == nullptr || meta == nullptr || X == nullptr || misaligned(values) ||
+      misaligned(meta) || misaligned(X) || R <= 0 || K <= 0 || T <= 0 || K % 64 != 0 ||
+      T % 8 != 0 || R >= (1 << 28) || K >= (1 << 22) || T >= (1 << 24))
+    return 1;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 2;
+  LpMap map;
+  map.tiles_m = (int)((R + kLpBM - 1) / kLpBM);
+  map.tiles_n = (int)((T + kLpBN - 1) / kLpBN);
+  map.xcds = cus % 8 == 0 ? 8 : 1;
+  map.per_xcd = (map.tiles_m * map.tiles_n + map.xcds - 1) / map.xcds;
+  map.gn = map.tiles_n < 4 ? map.tiles_n : 4;
+  map.gm = 32 / map.gn;
+  const int lds = kLpStages * kLpStageBytes;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(load_path_probe_kernel),
+      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return 2;
+  hipLaunchKernelGGL(load_path_probe_kernel, dim3(map.xcds * map.per_xcd), dim3(512), lds,
+                     static_cast<hipStream_t>(stream), static_cast<const uint8_t*>(values),
+                     static_cast<const uint8_t*>(meta), static_cast<const uint8_t*>(X), (int)R,
+                     (int)K, (int)T, map);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 

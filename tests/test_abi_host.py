@@ -479,8 +479,8 @@ def test_probe_library_exports_every_declared_symbol():
     text = open(os.path.join(os.path.dirname(HEADER), "nm_probe.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = sorted(set(re.findall(r"\b(nm_[a-z_]+)\s*\(", text)))
-    assert names == ["nm_probe_copy", "nm_probe_matrix_core", "nm_probe_operand_bytes",
-                     "nm_probe_valu"]
+    assert names == ["nm_probe_copy", "nm_probe_load_path", "nm_probe_matrix_core",
+                     "nm_probe_operand_bytes", "nm_probe_valu"]
     P = nm.probe_lib()
     for name in names:
         assert hasattr(P, name), name
@@ -490,3 +490,10 @@ def test_probe_library_exports_every_declared_symbol():
     assert P.nm_probe_valu(0, 256, 9, 10, FAKE, FAKE, None) == 1
     assert P.nm_probe_copy(FAKE, FAKE + 4096, 24, None) == 1      # not a multiple of 16
     assert P.nm_probe_copy(FAKE + 8, FAKE + 4096, 32, None) == 1  # misaligned
+    # the load-path probe: shapes the product's 256 x 128 loads take, 16-byte alignment
+    assert P.nm_probe_load_path(FAKE, FAKE, FAKE, 256, 100, 128, None) == 1  # K % 64
+    assert P.nm_probe_load_path(FAKE, FAKE, FAKE, 256, 128, 12, None) == 1   # T % 8
+    assert P.nm_probe_load_path(FAKE, FAKE, FAKE, 0, 128, 128, None) == 1    # empty
+    assert P.nm_probe_load_path(FAKE + 4, FAKE, FAKE, 256, 128, 128, None) == 1
+    assert P.nm_probe_load_path(None, FAKE, FAKE, 256, 128, 128, None) == 1
+    assert P.nm_probe_load_path(FAKE, FAKE, FAKE, 1 << 28, 128, 128, None) == 1

@@ -402,3 +402,24 @@ def test_spmm_full_workloads_sampled(name):
             if name == "toy_f32":  # small enough to compare every output
                 y_full, s_full = reference_product(vals_o, meta_o, w.R, w.K, n, m, X, w.dtype)
                 check_product(Y, y_full, s_full, w.K // m * n, w.dtype, w.dtype, "toy full")
+
+
+def test_load_path_probe_runs_on_product_inputs():
+    """The benchmark's load-path probe (libnm_probe: the product's direct loads alone) runs
+    to completion on the product's own inputs, ragged tiles included, and writes nothing
+    to them."""
+    if not os.path.exists(nm.PROBE_LIB_PATH):
+        pytest.skip("libnm_probe.so not built")
+    P = nm.probe_lib()
+    for i, (R, K, T) in enumerate([(512, 256, 256), (300, 192, 136), (16, 64, 8)]):
+        print(f"[load-path probe] {R}x{K}x{T}", flush=True)
+        W = synth.generate(synth.Dist("normal", 91 + 2 * i, 0.02), (R, K), "bf16")
+        X = synth.generate(synth.Dist("normal", 92 + 2 * i), (K, T), "bf16")
+        vals, meta = nm.compress(dev(W, "bf16"), 2, 4, layout="blocked")
+        Xd = dev(X, "bf16")
+        before = [host_bits(t) for t in (vals, meta, Xd)]
+        assert P.nm_probe_load_path(vals.data_ptr(), meta.data_ptr(), Xd.data_ptr(), R, K, T,
+                                    None) == 0
+        torch.cuda.synchronize()
+        for b, t in zip(before, (vals, meta, Xd)):
+            assert np.array_equal(b, host_bits(t))
