@@ -651,7 +651,8 @@ def main() -> int:
     ap.add_argument("--product-only", action="store_true",
                     help="time only nm_spmm on the workload's matrices (for profiling runs)")
     ap.add_argument("--ceiling-only", action="store_true",
-                    help="run only the matrix-core rate probes (libnm_probe)")
+                    help="run only the rate probes (libnm_probe): matrix cores, vector ALU, "
+                         "HBM copy and the product's load path")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one 512 MiB device-to-device copy (a kernel of known traffic "
                          "for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -729,14 +730,6 @@ def main() -> int:
     LAY = nm.LAYOUTS[args.layout]
     # the step: mask and compressed pair from one pass over W, decompress, product
     kinds = ["mask_compress", "decompress", "spmm"]
-    if args.ceiling_only:
-        w_vals, x_vals = bf16_sample(mats[0]["W"], dtype), bf16_sample(mats[0]["X"], dtype)
-        print(json.dumps({"matrix_core_ceiling": matrix_core_ceiling(torch, dev, stream, hipt,
-                                                                     w_vals, x_vals),
-                          "valu_ceiling": valu_ceiling(torch, dev, stream, hipt),
-                          "hbm_copy": hbm_copy(torch, dev, stream, hipt)}), flush=True)
-        return 0
-
     def launch(d, kind):
         if kind == "mask_compress":
             rc = L.nm_mask_compress(d["Wd"].data_ptr(), DT, d["R"], d["K"], n, m, LAY,
@@ -782,6 +775,23 @@ def main() -> int:
                     events.append((d["name"], kind, e0, e1))
                 else:
                     launch(d, kind)
+
+    if args.ceiling_only:
+        w_vals, x_vals = bf16_sample(mats[0]["W"], dtype), bf16_sample(mats[0]["X"], dtype)
+        out = {"matrix_core_ceiling": matrix_core_ceiling(torch, dev, stream, hipt, w_vals, x_vals),
+               "valu_ceiling": valu_ceiling(torch, dev, stream, hipt),
+               "hbm_copy": hbm_copy(torch, dev, stream, hipt)}
+        if dtype in ("bf16", "f16") and (n, m) == (2, 4) and args.layout == "blocked" and \
+                all(d["T"] % 8 == 0 and d["K"] % 64 == 0 for d in mats):
+            for d in mats:
+                launch(d, "mask_compress")
+            lp = load_path_ceiling(nm, mats, stream, hipt, launch, args.steps)
+            f_alg = sum(2.0 * d["R"] * d["K"] * d["T"] for d in mats) * n / m
+            lp["alg_tflops"] = round(f_alg / (sum(lp["us"].values()) * 1e-6) / 1e12, 1)
+            lp["frac_of_peak"] = round(lp["alg_tflops"] / PEAK_MFMA_TFLOPS[dtype], 4)
+            out["load_path_ceiling"] = lp
+        print(json.dumps(out), flush=True)
+        return 0
 
     if args.product_only:
         # the compressed pairs once, then only the products: the launches a profiler sees
