@@ -246,6 +246,32 @@ __device__ __forceinline__ void expand24(uint64_t bits, const uint32_t* vw, uint
   }
 }
 
+// 4:8 groups of 16-bit elements (fields 4g .. 4g+3 of `bits`, 3 bits each, the positions of
+// group g's four values, which sit in words 2g and 2g+1): byte i of `slot` records 1 + the
+// value written to position i (0: none), the fields taken in order so that a repeated
+// position keeps the later value; each output word (positions 2w, 2w+1) is then one byte
+// permute of the two value words, value j being bytes 2j, 2j+1 and selector 0x0c a zero byte.
+template <int G>
+__device__ __forceinline__ void expand48_16(uint64_t bits, const uint32_t* vw, uint32_t* ow) {
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) {
+    uint64_t slot = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t sh = 8u * ((uint32_t)(bits >> (3 * (4 * gi + j))) & 7u);
+      slot = (slot & ~(0xFFull << sh)) | ((uint64_t)(j + 1) << sh);
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t lo = (uint32_t)(slot >> (16 * w)) & 0xFFu;
+      const uint32_t hi = (uint32_t)(slot >> (16 * w + 8)) & 0xFFu;
+      const uint32_t s_lo = lo ? 0x0202u * lo - 0x0102u : 0x0C0Cu;
+      const uint32_t s_hi = hi ? 0x0202u * hi - 0x0102u : 0x0C0Cu;
+      ow[4 * gi + w] = __builtin_amdgcn_perm(vw[2 * gi + 1], vw[2 * gi], s_lo | (s_hi << 16));
+    }
+  }
+}
+
 template <typename E, int N, int M>
 __global__ void __launch_bounds__(kThreads) flat_decompress_kernel(
     const uint32_t* __restrict__ values, const uint32_t* __restrict__ meta, int64_t units,
@@ -666,6 +692,10 @@ __device__ __forceinline__ void decompress_lane(const uint32_t* __restrict__ val
   if (sh + L::kBits > 64) bits |= (uint64_t)mblk[wi + 2] << (64 - sh);
   if constexpr (N == 2 && M == 4 && sizeof(E) <= 2) {
     expand24<E, L::kGroups>(bits, vw, ow);
+    return;
+  }
+  if constexpr (N == 4 && M == 8 && sizeof(E) == 2) {
+    expand48_16<L::kGroups>(bits, vw, ow);
     return;
   }
 #pragma unroll
