@@ -423,3 +423,25 @@ def test_load_path_probe_runs_on_product_inputs():
         torch.cuda.synchronize()
         for b, t in zip(before, (vals, meta, Xd)):
             assert np.array_equal(b, host_bits(t))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("n,m", [(1, 2), (2, 4), (4, 8), (3, 8)])
+def test_decompress_trusts_metadata_later_value_wins(dtype, n, m):
+    """Decompress trusts its metadata (include/nm.h): with arbitrary fields, repeated and
+    descending positions included, value j of a group goes to its field's position in the
+    order j = 0 .. n-1, so a repeated position keeps the later value and unnamed positions
+    are +0.  Bitwise against the oracle, which writes them in that order, in both layouts."""
+    rng = np.random.default_rng(700 + 10 * n + m)
+    R, K = 40, 256  # whole metadata words per row for every pattern here; a ragged row block
+    words = K // m * n * {2: 1, 4: 2, 8: 3}[m] // 32
+    bits_t = np.uint32 if dtype == "f32" else np.uint16
+    vals_o = rng.integers(0, np.iinfo(bits_t).max, size=(R, K // m * n), dtype=np.uint64).astype(bits_t)
+    meta_o = rng.integers(0, 1 << 32, size=(R, words), dtype=np.uint64).astype(np.uint32)
+    dec_o = oracle.decompress(vals_o, meta_o, dtype, R, K, n, m)
+    dec = nm.decompress(dev(vals_o, dtype), torch.from_numpy(meta_o.view(np.int32)).cuda(), n, m, K)
+    assert np.array_equal(host_bits(dec), as_bits(dec_o)), "rows"
+    vb, mb = blocked_from_rows(vals_o, meta_o, R, K, n, m)
+    decb = nm.decompress(dev(vb, dtype), torch.from_numpy(mb.view(np.int32)).cuda(), n, m, K,
+                         layout="blocked", rows=R)
+    assert np.array_equal(host_bits(decb), as_bits(dec_o)), "blocked"
